@@ -1,0 +1,288 @@
+"""Pins for the float64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: central
+finite differences of the loss L = sum <dO, o> + <dht, S_T>, the literal
+matrix form of the recurrence, hand-derived closed forms (one token; beta = 0,
+where the rule reduces to gated linear attention), an independent chunked
+algorithm, the suffix-sum example worked on the FlashKDA backward page, and
+invariants (L2-norm gradient orthogonality, scale invariance, linearity,
+per-channel gate with constant channels = scalar gate, varlen = separate runs).
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.chunked as chunked
+from chunked_gated_delta_bwd_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _np_inputs(gate, lengths, H=2, K=4, V=4, seed=0, h0=0.4, dht=0.3, scale=None):
+    """Float64 numpy inputs (FD needs exact double perturbations)."""
+    sp = synth.Spec("t", gate, "f32", H=H, K=K, V=V, lengths=lengths, h0_std=h0, dht_std=dht,
+                    seed=seed, scale=scale)
+    inp = synth.generate(sp)
+    out = dict(inp)
+    for key in ("q", "k", "v", "dO", "b", "g", "A_log", "dt_bias", "h0", "dht"):
+        if inp.get(key) is not None:
+            out[key] = inp[key].double().numpy().copy()
+    out["cu_seqlens"] = inp["cu_seqlens"].numpy().copy()
+    return out
+
+
+def _loss(inp):
+    r = oracle.run(inp, backward=False, nthreads=1)
+    L = float((np.asarray(inp["dO"]) * r["o"]).sum())
+    if inp.get("dht") is not None:
+        L += float((np.asarray(inp["dht"]) * r["ht"]).sum())
+    return L
+
+
+GRAD_OF = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "b": "db", "h0": "dh0",
+           "A_log": "dA_log", "dt_bias": "ddt_bias"}
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("lengths,chunk", [([1], 4), ([5, 11], 4), ([70], 64), ([3, 0, 9], 4)])
+def test_finite_differences_all_inputs(gate, lengths, chunk):
+    inp = _np_inputs(gate, lengths, K=4, V=4, seed=11 + len(lengths))
+    g = oracle.run(inp, backward=True, chunk=chunk, nthreads=1)
+    eps = 1e-6
+    for name, gname in GRAD_OF.items():
+        if inp.get(name) is None or gname not in g:
+            continue
+        x = inp[name]
+        num = np.zeros_like(x)
+        flat = x.reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + eps
+            lp = _loss(inp)
+            flat[i] = old - eps
+            lm = _loss(inp)
+            flat[i] = old
+            num.reshape(-1)[i] = (lp - lm) / (2 * eps)
+        ana = g[gname].reshape(num.shape)
+        err = np.abs(num - ana).max() / max(1e-3, np.abs(num).max())
+        assert err < 1e-7, (name, err)
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_forward_matches_literal_matrix_form(gate):
+    """S_t = S_{t-1} Diag(e^lam)(I - beta kn kn^T) + beta v kn^T, o_t = scale S_t qn_t."""
+    inp = _np_inputs(gate, [9, 4], H=2, K=5, V=3, seed=3)
+    r = oracle.run(inp, backward=False)
+    H, K = inp["H"], inp["K"]
+    cu = inp["cu_seqlens"]
+    for n in range(inp["N"]):
+        for h in range(H):
+            S = inp["h0"][n, h].copy()
+            for t in range(cu[n], cu[n + 1]):
+                q, k, v = inp["q"][0, t, h], inp["k"][0, t, h], inp["v"][0, t, h]
+                qn = q / np.sqrt(q @ q + 1e-6)
+                kn = k / np.sqrt(k @ k + 1e-6)
+                beta = 1 / (1 + np.exp(-inp["b"][0, t, h]))
+                if gate == 0:
+                    lam = np.full(K, inp["g"][0, t, h])
+                else:
+                    x = inp["g"][0, t, h] + inp["dt_bias"][h]
+                    lam = -np.exp(inp["A_log"][h]) * np.log1p(np.exp(x))
+                S = S @ np.diag(np.exp(lam)) @ (np.eye(K) - beta * np.outer(kn, kn)) + beta * np.outer(v, kn)
+                np.testing.assert_allclose(r["o"][0, t, h], inp["scale"] * S @ qn, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(r["ht"][n, h], S, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_single_token_closed_form(gate):
+    inp = _np_inputs(gate, [1], H=1, K=5, V=4, seed=5)
+    r = oracle.run(inp)
+    q, k, v, dO = inp["q"][0, 0, 0], inp["k"][0, 0, 0], inp["v"][0, 0, 0], inp["dO"][0, 0, 0]
+    h0, dht, sc = inp["h0"][0, 0], inp["dht"][0, 0], inp["scale"]
+    rq, rk = 1 / np.sqrt(q @ q + 1e-6), 1 / np.sqrt(k @ k + 1e-6)
+    qn, kn = q * rq, k * rk
+    beta = 1 / (1 + np.exp(-inp["b"][0, 0, 0]))
+    if gate == 0:
+        lam = np.full(5, inp["g"][0, 0, 0])
+    else:
+        x = inp["g"][0, 0, 0] + inp["dt_bias"][0]
+        lam = -np.exp(inp["A_log"][0]) * np.log1p(np.exp(x))
+    D = np.diag(np.exp(lam))
+    S1 = h0 @ D @ (np.eye(5) - beta * np.outer(kn, kn)) + beta * np.outer(v, kn)
+    G = sc * np.outer(dO, qn) + dht                      # dL/dS_1
+    dqn = sc * S1.T @ dO
+    dh0 = G @ (np.eye(5) - beta * np.outer(kn, kn)) @ D
+    dv = beta * G @ kn
+    e = h0 @ D @ kn
+    dbeta = (v - e) @ G @ kn
+    dkn = -beta * ((h0 @ D).T @ G @ kn + G.T @ h0 @ D @ kn) + beta * G.T @ v
+    dlam = np.exp(lam) * np.einsum("ij,ij->j", h0, G - beta * np.outer(G @ kn, kn))
+    np.testing.assert_allclose(r["o"][0, 0, 0], sc * S1 @ qn, rtol=1e-12)
+    np.testing.assert_allclose(r["dh0"][0, 0], dh0, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(r["dv"][0, 0, 0], dv, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(r["dq"][0, 0, 0], rq * (dqn - qn * (qn @ dqn)), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(r["dk"][0, 0, 0], rk * (dkn - kn * (kn @ dkn)), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(r["db"][0, 0, 0], dbeta * beta * (1 - beta), rtol=1e-10, atol=1e-14)
+    if gate == 0:
+        np.testing.assert_allclose(r["dg"][0, 0, 0], dlam.sum(), rtol=1e-10, atol=1e-14)
+    else:
+        x = inp["g"][0, 0, 0] + inp["dt_bias"][0]
+        sig = 1 / (1 + np.exp(-x))
+        np.testing.assert_allclose(r["dg"][0, 0, 0], dlam * (-np.exp(inp["A_log"][0]) * sig), rtol=1e-10, atol=1e-14)
+        np.testing.assert_allclose(r["dA_log"][0], (dlam * lam).sum(), rtol=1e-10, atol=1e-14)
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_beta_zero_reduces_to_gated_linear_attention(gate):
+    """beta = 0 (logit -inf): no writes; readout, dq, dlam, dh0 and dbeta in closed form."""
+    inp = _np_inputs(gate, [13], H=1, K=4, V=3, seed=9)
+    inp["b"] = np.full_like(inp["b"], -np.inf)
+    r = oracle.run(inp, exports=True, chunk=4)
+    T, sc = 13, inp["scale"]
+    h0, dht = inp["h0"][0, 0], inp["dht"][0, 0]
+    q, k, v, dO = inp["q"][0, :, 0], inp["k"][0, :, 0], inp["v"][0, :, 0], inp["dO"][0, :, 0]
+    rq = 1 / np.sqrt((q * q).sum(1) + 1e-6)
+    qn = q * rq[:, None]
+    kn = k / np.sqrt((k * k).sum(1) + 1e-6)[:, None]
+    if gate == 0:
+        lam = np.repeat(inp["g"][0, :, 0][:, None], 4, axis=1)
+    else:
+        lam = -np.exp(inp["A_log"][0]) * np.log1p(np.exp(inp["g"][0, :, 0] + inp["dt_bias"][0]))
+    Lam = np.cumsum(lam, axis=0)                          # global cumsum
+    o = sc * np.einsum("ij,tj,tj->ti", h0, np.exp(Lam), qn)
+    np.testing.assert_allclose(r["o"][0, :, 0], o, rtol=1e-12, atol=1e-14)
+    assert np.all(r["dk"] == 0) and np.all(r["dv"] == 0)
+    dh0 = dht * np.exp(Lam[-1])[None, :] + sc * np.einsum("ti,tj->ij", dO, qn * np.exp(Lam))
+    np.testing.assert_allclose(r["dh0"][0, 0], dh0, rtol=1e-11, atol=1e-14)
+    dqn = sc * np.exp(Lam) * (dO @ h0)
+    dq = rq[:, None] * (dqn - qn * (qn * dqn).sum(1, keepdims=True))
+    np.testing.assert_allclose(r["dq"][0, :, 0], dq, rtol=1e-10, atol=1e-14)
+    # dL/dLam_t[j] = scale (h0^T dO_t)_j e^Lam_t qn_t ; + terminal term at t = T
+    dLam = sc * (dO @ h0) * np.exp(Lam) * qn
+    dLam[-1] += np.exp(Lam[-1]) * (dht * h0).sum(0)
+    dlam = np.flip(np.cumsum(np.flip(dLam, 0), 0), 0)
+    if gate == 0:
+        np.testing.assert_allclose(r["dg"][0, :, 0], dlam.sum(1), rtol=1e-10, atol=1e-13)
+    else:
+        np.testing.assert_allclose(r["dlam"][0, :, 0], dlam, rtol=1e-10, atol=1e-13)
+    # first-order effect of beta: a gated-linear-attention write of (v - e) kn^T
+    dbeta = np.zeros(T)
+    for s in range(T):
+        dS = dht * np.exp(Lam[-1] - Lam[s])[None, :]
+        for t in range(s, T):
+            dS = dS + sc * np.outer(dO[t], qn[t] * np.exp(Lam[t] - Lam[s]))
+        e = h0 @ (np.exp(Lam[s]) * kn[s])
+        dbeta[s] = (dS @ kn[s]) @ (v[s] - e)
+    np.testing.assert_allclose(r["dbeta"][0, :, 0], dbeta, rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("chunk", [4, 16, 64])
+def test_chunked_algorithm_matches_recurrence(gate, chunk):
+    inp = _np_inputs(gate, [70, 1, 33, 0, 64], H=2, K=8, V=6, seed=21)
+    a = oracle.run(inp, exports=True, chunk=chunk)
+    b = chunked.run(inp, chunk=chunk)
+    keys = ["o", "ht", "u", "dq", "dk", "dv", "dg", "db", "dh0"] + (["dA_log", "ddt_bias"] if gate else [])
+    for key in keys:
+        scale = max(1.0, np.abs(a[key]).max())
+        assert np.abs(a[key] - b[key]).max() / scale < 1e-12, key
+    assert np.abs(a["S_chunk"] - b["S_chunk"]).max() < 1e-12
+    assert np.abs(a["dS_chunk"] - b["dS_chunk"]).max() < 1e-12
+
+
+def test_reverse_cumsum_worked_example():
+    with open(os.path.join(GOLDEN, "reverse_cumsum_worked_example.json")) as f:
+        ex = json.load(f)
+    got = chunked.reverse_cumsum_with_total(np.array(ex["dgc"]), 0.0)
+    np.testing.assert_array_equal(got, np.array(ex["expected_suffix_sums"]))
+    # the chunk total adds the same amount to every row
+    got2 = chunked.reverse_cumsum_with_total(np.array(ex["dgc"]), 1.5)
+    np.testing.assert_array_equal(got2, np.array(ex["expected_suffix_sums"]) + 1.5)
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_l2_gradient_orthogonal_and_scale_invariant(gate):
+    inp = _np_inputs(gate, [20], H=2, K=8, V=8, seed=4)
+    r = oracle.run(inp)
+    q, dq = inp["q"], r["dq"]
+    # <q, dq> = rho <q, dqn> * 1e-6 rho^2: zero up to the eps inside the root
+    dots = np.abs((q * dq).sum(-1))
+    assert np.all(dots <= 1e-6 * np.linalg.norm(dq, axis=-1) * np.linalg.norm(q, axis=-1) + 1e-15)
+    inp2 = dict(inp)
+    inp2["q"] = inp["q"] * 3.0
+    r2 = oracle.run(inp2)
+    # exact up to the eps inside the root: a relative effect of about 1e-6 / |q|^2
+    assert np.abs(r2["o"] - r["o"]).max() <= 1e-6 * np.abs(r["o"]).max()
+    assert np.abs(r2["dq"] * 3.0 - r["dq"]).max() <= 1e-6 * np.abs(r["dq"]).max()
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_gradients_linear_in_upstream(gate):
+    inp = _np_inputs(gate, [17, 6], H=2, K=4, V=5, seed=8)
+    rng = np.random.default_rng(0)
+    dO2 = rng.standard_normal(inp["dO"].shape)
+    dht2 = rng.standard_normal(inp["dht"].shape)
+    a = oracle.run(inp)
+    b = oracle.run(inp, dO=dO2, dht=dht2)
+    c = oracle.run(inp, dO=2.0 * inp["dO"] - dO2, dht=2.0 * inp["dht"] - dht2)
+    for key in ("dq", "dk", "dv", "dg", "db", "dh0") + (("dA_log", "ddt_bias") if gate else ()):
+        np.testing.assert_allclose(c[key], 2.0 * a[key] - b[key], rtol=1e-9, atol=1e-11)
+
+
+def test_channel_constant_gate_equals_scalar_gate():
+    kda = _np_inputs(1, [19, 7], H=2, K=6, V=5, seed=12)
+    # constant across channels: g_raw[t,h,:] = c_th, dt_bias[h,:] = d_h
+    kda["g"] = np.repeat(kda["g"][..., :1], 6, axis=-1)
+    kda["dt_bias"] = np.repeat(kda["dt_bias"][:, :1], 6, axis=-1)
+    lam = -np.exp(kda["A_log"])[None, None, :] * np.log1p(np.exp(kda["g"][..., 0] + kda["dt_bias"][None, None, :, 0]))
+    gdn = dict(kda)
+    gdn["gate"] = 0
+    gdn["g"] = lam
+    gdn["A_log"] = gdn["dt_bias"] = None
+    a = oracle.run(kda, exports=True)
+    b = oracle.run(gdn, exports=True)
+    for key in ("o", "ht", "dq", "dk", "dv", "db", "dh0"):
+        np.testing.assert_allclose(a[key], b[key], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(a["dlam"].sum(-1), b["dg"], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_varlen_pack_equals_separate_runs(gate):
+    lengths = [9, 0, 21, 1]
+    inp = _np_inputs(gate, lengths, H=2, K=4, V=4, seed=13)
+    packed = oracle.run(inp)
+    cu = inp["cu_seqlens"]
+    dA = 0.0
+    ddt = 0.0
+    for n, L in enumerate(lengths):
+        sub = dict(inp)
+        for key in ("q", "k", "v", "dO", "b", "g"):
+            sub[key] = inp[key][:, cu[n]:cu[n + 1]]
+        sub["h0"], sub["dht"] = inp["h0"][n:n + 1], inp["dht"][n:n + 1]
+        sub["cu_seqlens"] = np.array([0, L], dtype=np.int64)
+        sub["N"], sub["T"] = 1, L
+        r = oracle.run(sub)
+        for key in ("o", "dq", "dk", "dv", "dg", "db"):
+            np.testing.assert_allclose(packed[key][:, cu[n]:cu[n + 1]], r[key], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(packed["dh0"][n], r["dh0"][0], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(packed["ht"][n], r["ht"][0], rtol=1e-13, atol=1e-15)
+        if gate:
+            dA = dA + r["dA_log"]
+            ddt = ddt + r["ddt_bias"]
+        if L == 0:  # empty sequence: state passes through, gradient too
+            np.testing.assert_array_equal(r["ht"][0], inp["h0"][n])
+            np.testing.assert_array_equal(r["dh0"][0], inp["dht"][n])
+    if gate:
+        np.testing.assert_allclose(packed["dA_log"], dA, rtol=1e-12)
+        np.testing.assert_allclose(packed["ddt_bias"], ddt, rtol=1e-12)
+
+
+def test_oracle_rejects_bad_arguments():
+    inp = _np_inputs(1, [4], H=1, K=4, V=4, seed=1)
+    inp["A_log"] = None
+    with pytest.raises(RuntimeError):
+        oracle.run(inp)
