@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked gated delta-rule backward on one MI355X.
+
+One step = one whole backward (forward recompute + backward, all kernels, the
+fused entry point gdr_fwd_bwd) over the headline workload: GDN scalar gate,
+B=1, T=32768, H=16, Dk=Dv=128, bf16 inputs, h0/dht ~ N(0, 0.1), synthetic
+seeded inputs already resident in HBM.  Prints one JSON line.
+
+Besides the whole-step time it times every kernel alone (HIP events on the
+stream the library launches on), reports the roofline fraction of the dominant
+kernel from its algorithmic FLOPs or bytes, and times the float64 CPU oracle on
+a bounded sample of the same workload (the first --cpu-tokens tokens, all heads).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from chunked_gated_delta_bwd_amd import binding as B  # noqa: E402
+from chunked_gated_delta_bwd_amd import synth  # noqa: E402
+
+METRIC = "gated-delta-rule bwd tokens/s + ms/bwd at T=32k,H=16,D=128 bf16; MFMA %"
+C = 64
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def algorithmic_work(inp, stage: str):
+    """(flops, bytes) one launch of `stage` must do on this problem.
+
+    FLOPs are the chunked method's own contractions per (chunk, head), counting
+    triangular products at half size; bytes are the HBM traffic the stage
+    cannot avoid (inputs read, outputs written, its workspace in and out).
+    """
+    H, D = inp["H"], inp["K"]
+    NC = sum((L + C - 1) // C for L in inp["lengths"])
+    tokens = inp["B"] * inp["T"]
+    ch = NC * H
+    gk = D if inp["gate"] == 1 else 1
+    io = 2 if inp["dtype"] == "bf16" else 4
+    f_prep = 4 * C * C * D + C ** 3 // 3
+    f_fwd = 4 * C * D * D
+    f_bwd = 6 * C * D * D + C * C * D
+    f_grads = 6 * C * D * D + 9 * C * C * D
+    if stage == "prep":
+        b = tokens * H * (3 * D * io + (1 + gk) * io) + ch * (C * gk * 4 + 2 * C * 4 + 2 * C * C * 2 + 2 * C * D * 2)
+        return ch * f_prep, b
+    if stage == "chain_fwd":
+        return ch * f_fwd, ch * (C * D * 2 * 2 + D * D * 2 + C * D * 2) + tokens * H * D * io
+    if stage == "chain_bwd":
+        return ch * f_bwd, ch * (C * D * 2 + C * C * 2 + D * D * 2 + C * D * 2) + tokens * H * 3 * D * io
+    if stage == "chain_both":
+        a, b = algorithmic_work(inp, "chain_fwd"), algorithmic_work(inp, "chain_bwd")
+        return a[0] + b[0], a[1] + b[1]
+    if stage == "grads":
+        b = ch * (2 * D * D * 2 + 2 * C * D * 2 + C * C * 2 + 2 * C * D * 4 + C * gk * 4 + C * 4) + tokens * H * 5 * D * io
+        return ch * f_grads, b
+    if stage == "finish":
+        # read q, k, dqn, dkn, rho, dGamma, dbeta, b (and g_raw for KDA); write dq, dk, dg, db
+        b = tokens * H * (2 * D * io + 2 * D * 4 + 8 + gk * 4 + 4 + io + 2 * D * io + gk * io + io)
+        if inp["gate"] == 1:
+            b += tokens * H * D * io
+        return 0, b
+    raise KeyError(stage)
+
+
+def time_it(fn, iters: int) -> float:
+    """Average milliseconds per call, HIP events on the current stream."""
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def cpu_baseline(inp, tokens: int):
+    """The float64 oracle on the first `tokens` tokens of the workload (all heads)."""
+    import oracle  # test infrastructure: only this leg of the benchmark uses it
+
+    sub = dict(inp)
+    for key in ("q", "k", "v", "dO", "g", "b"):
+        sub[key] = inp[key][:, :tokens].contiguous()
+    sub["T"] = tokens
+    if inp["N"] == inp["B"]:      # dense: the first tokens of every batch row
+        sub["lengths"] = [tokens] * inp["B"]
+        sub["cu_seqlens"] = torch.arange(inp["B"] + 1, dtype=torch.int64) * tokens
+    else:                         # packed: cut the packed axis, sequences keep their own states
+        cu = torch.clamp(inp["cu_seqlens"], max=tokens)
+        sub["cu_seqlens"] = cu
+        sub["lengths"] = [int(x) for x in (cu[1:] - cu[:-1])]
+    threads = oracle.default_threads()
+    oracle.run(sub, nthreads=threads)  # build/load outside the timed call
+    t0 = time.perf_counter()
+    oracle.run(sub, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"first {tokens} of {inp['T']} tokens, all {inp['H']} heads of the same workload; "
+                      f"float64 token recurrence + adjoint, {threads} threads over (sequence, head)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=synth.HEADLINE, choices=synth.WORKLOADS)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--stage-iters", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU path is not built",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    B.load_library()
+
+    spec = synth.workload(args.workload)
+    inp = synth.generate(spec)
+    dev = B.to_device(inp)
+    prob = B.Problem.from_inputs(inp)
+    ws = B.alloc_workspace(prob)
+    out = B.alloc_outputs(inp, dev)
+    N, H, K, V = inp["N"], inp["H"], inp["K"], inp["V"]
+    ht = torch.empty((N, H, V, K), dtype=torch.float32, device="cuda")
+
+    def step():
+        B.gdr_fwd_bwd(prob, dev, dev["dO"], dev["dht"], ws, out, ht=ht)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_it(step, args.steps)
+    tokens = inp["B"] * inp["T"]
+
+    # every kernel alone (the workspace already holds what earlier stages leave)
+    kernels = {}
+    for stage, name in B.STAGE_NAMES.items():
+        fn = lambda s=stage: B.gdr_run_stage(prob, dev, dev["dO"], dev["dht"], ws, out, s, ht=ht)  # noqa: E731
+        fn()
+        t = time_it(fn, args.stage_iters)
+        flops, nbytes = algorithmic_work(inp, name)
+        kernels[name] = {"ms": round(t, 4),
+                         "tflops": round(flops / t / 1e9, 2) if flops else 0.0,
+                         "mfma_frac": round(flops / t / 1e9 / PEAK_BF16_TFLOPS, 4) if flops else 0.0,
+                         "gbs": round(nbytes / t / 1e6, 1),
+                         "hbm_frac": round(nbytes / t / 1e6 / PEAK_HBM_GBS, 4)}
+    path = ("prep", "chain_both", "grads", "finish")
+    dom = max(path, key=lambda n: kernels[n]["ms"])
+    flops, nbytes = algorithmic_work(inp, dom)
+    if dom == "finish":
+        achieved = nbytes / (kernels[dom]["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / (kernels[dom]["ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = dom
+    roof["work_per_launch"] = flops if dom != "finish" else nbytes
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if inp["dtype"] == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": inp["B"], "T": inp["T"], "H": H, "D": K,
+                   "gate": "scalar" if inp["gate"] == 0 else "channel", "chunk": C},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_tokens, inp["T"]))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

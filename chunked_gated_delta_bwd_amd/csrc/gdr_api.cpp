@@ -1,0 +1,313 @@
+// Host side of the C ABI declared in include/gdr.h: argument validation,
+// workspace layout, the chunk and sequence tables, and the launch sequence.
+// Nothing here allocates or synchronises; everything is enqueued on the
+// caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "gdr_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdr_status fail(gdr_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates the shape and computes the chunk count.
+gdr_status check_shape(const gdr_shape* s, int64_t* NC_out) {
+  if (!s) return fail(GDR_EINVAL, "shape is NULL");
+  if (s->gate != GDR_GATE_SCALAR && s->gate != GDR_GATE_CHANNEL)
+    return fail(GDR_EINVAL, "unknown gate %d", s->gate);
+  if (s->dtype != GDR_BF16 && s->dtype != GDR_F32) return fail(GDR_EINVAL, "unknown dtype %d", s->dtype);
+  if (s->Dk != s->Dv) return fail(GDR_EUNSUPPORTED, "Dk (%d) != Dv (%d)", s->Dk, s->Dv);
+  if (s->Dk != 64 && s->Dk != 128) return fail(GDR_EUNSUPPORTED, "head dim %d not in {64, 128}", s->Dk);
+  if (s->H < 1 || s->B < 1 || s->T < 0 || s->N < 0) return fail(GDR_EINVAL, "bad B/T/H/N");
+  int64_t NC = 0;
+  if (s->cu_seqlens_host == nullptr) {
+    if (s->N != s->B) return fail(GDR_EINVAL, "dense shape needs N == B (N=%d, B=%d)", s->N, s->B);
+    NC = int64_t(s->B) * ((int64_t(s->T) + gdr::kChunk - 1) / gdr::kChunk);
+  } else {
+    if (s->B != 1) return fail(GDR_EINVAL, "varlen shape needs B == 1");
+    if (s->N < 1) return fail(GDR_EINVAL, "varlen shape needs N >= 1");
+    const int64_t* cu = s->cu_seqlens_host;
+    if (cu[0] != 0) return fail(GDR_EINVAL, "cu_seqlens[0] = %lld, expected 0", (long long)cu[0]);
+    for (int n = 0; n < s->N; ++n) {
+      if (cu[n + 1] < cu[n]) return fail(GDR_EINVAL, "cu_seqlens decreases at %d", n);
+      NC += (cu[n + 1] - cu[n] + gdr::kChunk - 1) / gdr::kChunk;
+    }
+    if (cu[s->N] != s->T)
+      return fail(GDR_EINVAL, "cu_seqlens[N] = %lld != T = %d", (long long)cu[s->N], s->T);
+  }
+  const int64_t tokens = int64_t(s->B) * s->T;
+  if (tokens * s->H * s->Dk >= (int64_t(1) << 40) || NC * s->H * gdr::kChunk >= (int64_t(1) << 31))
+    return fail(GDR_EUNSUPPORTED, "problem too large for 32-bit chunk indexing");
+  *NC_out = NC;
+  return GDR_OK;
+}
+
+gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
+  gdr::WsLayout L;
+  L.NC = NC;
+  const size_t H = s->H, K = s->Dk, V = s->Dv, C = gdr::kChunk, N = s->N;
+  const size_t gk = s->gate == GDR_GATE_CHANNEL ? K : 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  L.ctab = take(NC * sizeof(gdr::ChunkEntry));
+  L.stab = take(N * sizeof(gdr::SeqEntry));
+  L.gam = take(H * NC * C * gk * 4);
+  L.rho = take(H * NC * 2 * C * 4);
+  L.A = take(H * NC * C * C * 2);
+  L.P = take(H * NC * C * C * 2);
+  L.W = take(H * NC * C * K * 2);
+  L.Up = take(H * NC * C * V * 2);
+  L.U = take(H * NC * C * V * 2);
+  L.S = take(H * NC * V * K * 2);
+  L.dS = take(H * NC * V * K * 2);
+  L.dU = take(H * NC * C * V * 2);
+  L.dqn = take(H * NC * C * K * 4);
+  L.dkn = take(H * NC * C * K * 4);
+  L.dgam = take(H * NC * C * gk * 4);
+  L.dgamc = take(H * NC * gk * 4);
+  L.dbeta = take(H * NC * C * 4);
+  L.total = off;
+  return L;
+}
+
+gdr_status check_inputs(const gdr_shape* s, const gdr_inputs* in) {
+  if (!in) return fail(GDR_EINVAL, "inputs is NULL");
+  const void* req[] = {in->q, in->k, in->v, in->g, in->beta_logit};
+  const char* names[] = {"q", "k", "v", "g", "beta_logit"};
+  for (int i = 0; i < 5; ++i) {
+    if (!req[i]) return fail(GDR_EINVAL, "input %s is NULL", names[i]);
+    if (!aligned16(req[i])) return fail(GDR_EINVAL, "input %s is not 16-byte aligned", names[i]);
+  }
+  if (in->h0 && !aligned16(in->h0)) return fail(GDR_EINVAL, "h0 is not 16-byte aligned");
+  if (s->gate == GDR_GATE_CHANNEL) {
+    if (!in->A_log || !in->dt_bias) return fail(GDR_EINVAL, "per-channel gate needs A_log and dt_bias");
+    if (!aligned16(in->A_log) || !aligned16(in->dt_bias))
+      return fail(GDR_EINVAL, "A_log/dt_bias not 16-byte aligned");
+  } else if (in->A_log || in->dt_bias) {
+    return fail(GDR_EINVAL, "scalar gate takes no A_log/dt_bias");
+  }
+  return GDR_OK;
+}
+
+gdr_status check_grads(const gdr_shape* s, const void* dO, const float* dht, const gdr_grads* gr) {
+  if (!dO) return fail(GDR_EINVAL, "dO is NULL");
+  if (!aligned16(dO)) return fail(GDR_EINVAL, "dO is not 16-byte aligned");
+  if (dht && !aligned16(dht)) return fail(GDR_EINVAL, "dht is not 16-byte aligned");
+  if (!gr) return fail(GDR_EINVAL, "grads is NULL");
+  const void* req[] = {gr->dq, gr->dk, gr->dv, gr->dg, gr->dbeta};
+  const char* names[] = {"dq", "dk", "dv", "dg", "dbeta"};
+  for (int i = 0; i < 5; ++i) {
+    if (!req[i]) return fail(GDR_EINVAL, "output %s is NULL", names[i]);
+    if (!aligned16(req[i])) return fail(GDR_EINVAL, "output %s is not 16-byte aligned", names[i]);
+  }
+  if (gr->dh0 && !aligned16(gr->dh0)) return fail(GDR_EINVAL, "dh0 is not 16-byte aligned");
+  if (s->gate == GDR_GATE_CHANNEL) {
+    if (!gr->dA_log || !gr->ddt_bias) return fail(GDR_EINVAL, "per-channel gate needs dA_log and ddt_bias outputs");
+    if (!aligned16(gr->dA_log) || !aligned16(gr->ddt_bias))
+      return fail(GDR_EINVAL, "dA_log/ddt_bias not 16-byte aligned");
+  } else if (gr->dA_log || gr->ddt_bias) {
+    return fail(GDR_EINVAL, "scalar gate has no dA_log/ddt_bias outputs");
+  }
+  return GDR_OK;
+}
+
+gdr_status check_ws(const gdr::WsLayout& L, const void* ws, size_t ws_bytes) {
+  if (ws_bytes < L.total) return fail(GDR_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+  if (!ws && L.total) return fail(GDR_EINVAL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(GDR_EINVAL, "workspace is not 256-byte aligned");
+  return GDR_OK;
+}
+
+// Builds the chunk and sequence tables on the host and enqueues their upload.
+// Both live back to back at the start of the workspace (one copy).
+gdr_status upload_tables(const gdr_shape* s, const gdr::WsLayout& L, void* ws, hipStream_t stream) {
+  const int N = s->N;
+  std::vector<unsigned char> host(L.stab + size_t(N) * sizeof(gdr::SeqEntry));
+  auto* ct = reinterpret_cast<gdr::ChunkEntry*>(host.data() + L.ctab);
+  auto* st = reinterpret_cast<gdr::SeqEntry*>(host.data() + L.stab);
+  int64_t c = 0;
+  for (int n = 0; n < N; ++n) {
+    const int64_t b = s->cu_seqlens_host ? s->cu_seqlens_host[n] : int64_t(n) * s->T;
+    const int64_t e = s->cu_seqlens_host ? s->cu_seqlens_host[n + 1] : int64_t(n + 1) * s->T;
+    const int len = int(e - b);
+    const int nck = (len + gdr::kChunk - 1) / gdr::kChunk;
+    st[n] = gdr::SeqEntry{n, len, int32_t(c), nck};
+    for (int i = 0; i < nck; ++i, ++c) {
+      const int rows = std::min(gdr::kChunk, len - i * gdr::kChunk);
+      ct[c] = gdr::ChunkEntry{int32_t(b + int64_t(i) * gdr::kChunk), rows, n, i};
+    }
+  }
+  std::stable_sort(st, st + N, [](const gdr::SeqEntry& x, const gdr::SeqEntry& y) { return x.len > y.len; });
+  if (host.empty()) return GDR_OK;
+  // Pageable source: the runtime stages it before returning, so `host` may die afterwards.
+  hipError_t e = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice,
+                                reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDR_EHIP, "hipMemcpyAsync(tables): %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_inputs* in, void* ws) {
+  gdr::Params p;
+  std::memset(&p, 0, sizeof(p));
+  p.H = s->H; p.K = s->Dk; p.V = s->Dv; p.N = s->N; p.NC = int32_t(L.NC); p.T = s->B * s->T;
+  p.gate = s->gate; p.dtype = s->dtype; p.scale = s->scale;
+  p.q = in->q; p.k = in->k; p.v = in->v; p.g = in->g; p.b = in->beta_logit;
+  p.A_log = in->A_log; p.dt_bias = in->dt_bias; p.h0 = in->h0;
+  char* w = static_cast<char*>(ws);
+  p.ctab = reinterpret_cast<const gdr::ChunkEntry*>(w + L.ctab);
+  p.stab = reinterpret_cast<const gdr::SeqEntry*>(w + L.stab);
+  p.gam = reinterpret_cast<float*>(w + L.gam);
+  p.rho = reinterpret_cast<float*>(w + L.rho);
+  p.A = reinterpret_cast<uint16_t*>(w + L.A);
+  p.P = reinterpret_cast<uint16_t*>(w + L.P);
+  p.W = reinterpret_cast<uint16_t*>(w + L.W);
+  p.Up = reinterpret_cast<uint16_t*>(w + L.Up);
+  p.U = reinterpret_cast<uint16_t*>(w + L.U);
+  p.S = reinterpret_cast<uint16_t*>(w + L.S);
+  p.dS = reinterpret_cast<uint16_t*>(w + L.dS);
+  p.dU = reinterpret_cast<uint16_t*>(w + L.dU);
+  p.dqn = reinterpret_cast<float*>(w + L.dqn);
+  p.dkn = reinterpret_cast<float*>(w + L.dkn);
+  p.dgam = reinterpret_cast<float*>(w + L.dgam);
+  p.dgamc = reinterpret_cast<float*>(w + L.dgamc);
+  p.dbeta = reinterpret_cast<float*>(w + L.dbeta);
+  return p;
+}
+
+gdr_status hip_status(int err, const char* what) {
+  if (err == 0) return GDR_OK;
+  return fail(GDR_EHIP, "%s: %s", what, gdr::hip_error_string(err));
+}
+
+void set_grads(gdr::Params& p, const void* dO, const float* dht, const gdr_grads* gr) {
+  p.dO = dO; p.dht = dht;
+  p.dq = gr->dq; p.dk = gr->dk; p.dv = gr->dv; p.dg = gr->dg; p.db = gr->dbeta;
+  p.dh0 = gr->dh0; p.dA_log = gr->dA_log; p.ddt_bias = gr->ddt_bias;
+}
+
+enum Stage { kFwd = 1, kBwd = 2, kFused = 3 };
+
+// `only` >= 0 restricts the launch sequence to one GDR_STAGE_* kernel.
+gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* dO, const float* dht,
+               void* ws, size_t ws_bytes, const gdr_grads* gr, float* ht, void* stream, int only = -1) {
+  int64_t NC = 0;
+  gdr_status st = check_shape(s, &NC);
+  if (st != GDR_OK) return st;
+  if ((st = check_inputs(s, in)) != GDR_OK) return st;
+  if (stage != kFwd && (st = check_grads(s, dO, dht, gr)) != GDR_OK) return st;
+  if (ht && !aligned16(ht)) return fail(GDR_EINVAL, "ht is not 16-byte aligned");
+  const gdr::WsLayout L = layout(s, NC);
+  if ((st = check_ws(L, ws, ws_bytes)) != GDR_OK) return st;
+
+  if (s->gate == GDR_GATE_CHANNEL)
+    return fail(GDR_EUNSUPPORTED, "per-channel gate kernels are not available in this build");
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if ((st = upload_tables(s, L, ws, hs)) != GDR_OK) return st;
+  gdr::Params p = make_params(s, L, in, ws);
+  p.ht = ht;
+  if (stage != kFwd) set_grads(p, dO, dht, gr);
+
+  if (only >= 0) {
+    switch (only) {
+      case GDR_STAGE_PREP: return NC > 0 ? hip_status(gdr::launch_prep(p, stream), "prep kernel") : GDR_OK;
+      case GDR_STAGE_CHAIN_FWD: return hip_status(gdr::launch_chain(p, gdr::kChainFwd, stream), "chain kernel");
+      case GDR_STAGE_CHAIN_BWD: return hip_status(gdr::launch_chain(p, gdr::kChainBwd, stream), "chain kernel");
+      case GDR_STAGE_CHAIN_BOTH: return hip_status(gdr::launch_chain(p, gdr::kChainBoth, stream), "chain kernel");
+      case GDR_STAGE_GRADS: return NC > 0 ? hip_status(gdr::launch_grads(p, stream), "gradient kernel") : GDR_OK;
+      case GDR_STAGE_FINISH:
+        return NC > 0 ? hip_status(gdr::launch_finish(p, stream), "prepare-backward kernel") : GDR_OK;
+      default: return fail(GDR_EINVAL, "unknown stage %d", only);
+    }
+  }
+  if (stage != kBwd && NC > 0) {
+    if ((st = hip_status(gdr::launch_prep(p, stream), "prep kernel")) != GDR_OK) return st;
+  }
+  if (stage != kFwd && s->gate == GDR_GATE_CHANNEL) {
+    if ((st = hip_status(gdr::launch_zero_params(p, stream), "zero kernel")) != GDR_OK) return st;
+  }
+  const int mode = stage == kFwd ? gdr::kChainFwd : stage == kBwd ? gdr::kChainBwd : gdr::kChainBoth;
+  if ((st = hip_status(gdr::launch_chain(p, mode, stream), "chain kernel")) != GDR_OK) return st;
+  if (stage != kFwd && NC > 0) {
+    if ((st = hip_status(gdr::launch_grads(p, stream), "gradient kernel")) != GDR_OK) return st;
+    if ((st = hip_status(gdr::launch_finish(p, stream), "prepare-backward kernel")) != GDR_OK) return st;
+  }
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_workspace_bytes(const gdr_shape* shape, size_t* bytes) {
+  int64_t NC = 0;
+  gdr_status st = check_shape(shape, &NC);
+  if (st != GDR_OK) return st;
+  if (!bytes) return fail(GDR_EINVAL, "bytes is NULL");
+  *bytes = layout(shape, NC).total;
+  return GDR_OK;
+}
+
+gdr_status gdr_fwd_recompute(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes, float* ht,
+                             void* stream) {
+  return run(kFwd, shape, in, nullptr, nullptr, ws, ws_bytes, nullptr, ht, stream);
+}
+
+gdr_status gdr_bwd(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht, void* ws,
+                   size_t ws_bytes, gdr_grads* grads, void* stream) {
+  return run(kBwd, shape, in, dO, dht, ws, ws_bytes, grads, nullptr, stream);
+}
+
+gdr_status gdr_fwd_bwd(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht, void* ws,
+                       size_t ws_bytes, gdr_grads* grads, float* ht, void* stream) {
+  return run(kFused, shape, in, dO, dht, ws, ws_bytes, grads, ht, stream);
+}
+
+gdr_status gdr_run_stage(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht, void* ws,
+                         size_t ws_bytes, gdr_grads* grads, float* ht, int32_t stage, void* stream) {
+  if (stage < GDR_STAGE_PREP || stage > GDR_STAGE_FINISH) return fail(GDR_EINVAL, "unknown stage %d", stage);
+  return run(kFused, shape, in, dO, dht, ws, ws_bytes, grads, ht, stream, stage);
+}
+
+gdr_status gdr_workspace_region(const gdr_shape* shape, int32_t which, size_t* offset, size_t* bytes) {
+  int64_t NC = 0;
+  gdr_status st = check_shape(shape, &NC);
+  if (st != GDR_OK) return st;
+  if (!offset || !bytes) return fail(GDR_EINVAL, "offset/bytes is NULL");
+  const gdr::WsLayout L = layout(shape, NC);
+  const size_t H = shape->H, K = shape->Dk, V = shape->Dv, C = gdr::kChunk;
+  const size_t gk = shape->gate == GDR_GATE_CHANNEL ? K : 1;
+  switch (which) {
+    case GDR_WS_STATE: *offset = L.S; *bytes = H * NC * V * K * 2; break;
+    case GDR_WS_DSTATE: *offset = L.dS; *bytes = H * NC * V * K * 2; break;
+    case GDR_WS_U: *offset = L.U; *bytes = H * NC * C * V * 2; break;
+    case GDR_WS_A: *offset = L.A; *bytes = H * NC * C * C * 2; break;
+    case GDR_WS_GAMMA: *offset = L.gam; *bytes = H * NC * C * gk * 4; break;
+    default: return fail(GDR_EINVAL, "unknown workspace region %d", which);
+  }
+  return GDR_OK;
+}
+
+const char* gdr_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// Device helpers for gfx950: bf16 conversion, MFMA 16x16x32 bf16 fragments,
+// LDS transpose reads, typed global loads/stores and wave reductions.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 lane layout (wave64, lane l, g = l/16, j = l%16):
+//   A operand: A[m = j][k = 8g .. 8g+7]      (8 bf16 per lane)
+//   B operand: B[k = 8g .. 8g+7][n = j]
+//   C/D:       C[m = 4g + i][n = j], i = 0..3 (4 fp32 per lane)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) short lds_short;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Fragment of a tile stored T[row][k] (k contiguous, pitch P elements):
+// lane gets T[r0 + j][k0 + 8g .. 8g+7].  Serves as the A operand (m = row) or
+// as the B operand when B[k][n] = T[n][k].
+__device__ __forceinline__ bf16x8 frag_rk(const bf16* T, int P, int r0, int k0) {
+  const int l = lane_id();
+  return *reinterpret_cast<const bf16x8*>(T + (r0 + (l & 15)) * P + k0 + 8 * (l >> 4));
+}
+
+// Fragment of a tile stored T[k][col] (col contiguous, pitch P elements):
+// lane gets T[k0 + 8g .. 8g+7][c0 + j], gathered by two ds_read_b64_tr_b16.
+// Within each 16-lane group, lane i of the transposed read receives element
+// i%4 of the 64-bit chunk addressed by lane 4r + i/4 (r = result slot), so lane
+// q addresses row k0 + 8g + q/4, columns c0 + 4(q%4) .. +3.
+__device__ __forceinline__ bf16x8 frag_kc(const bf16* T, int P, int c0, int k0) {
+  const int l = lane_id();
+  const int g = l >> 4, q = l & 15;
+  const bf16* p0 = T + (k0 + 8 * g + (q >> 2)) * P + c0 + 4 * (q & 3);
+  const bf16* p1 = p0 + 4 * P;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(p0)));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(p1)));
+  // whole-vector bit casts: extracting 16-bit lanes one at a time through a
+  // scalar bf16 bit cast miscompiles on this toolchain (element 0 is splat)
+  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+  const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+  return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (bf16)x); }
+
+// Four fp32 -> four bf16 packed into 8 bytes.
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  uint2 r;
+  r.x = uint32_t(f32_to_bf16_bits(a)) | (uint32_t(f32_to_bf16_bits(b)) << 16);
+  r.y = uint32_t(f32_to_bf16_bits(c)) | (uint32_t(f32_to_bf16_bits(d)) << 16);
+  return r;
+}
+
+// ---- typed token-tensor access (storage bf16 or fp32, math in fp32) ----
+template <typename T> struct IO;
+
+template <> struct IO<bf16> {
+  static __device__ __forceinline__ void load8(const void* base, int64_t off, float (&x)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void load4(const void* base, int64_t off, float (&x)[4]) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
+    x[0] = __uint_as_float(u.x << 16);
+    x[1] = __uint_as_float(u.x & 0xffff0000u);
+    x[2] = __uint_as_float(u.y << 16);
+    x[3] = __uint_as_float(u.y & 0xffff0000u);
+  }
+  static __device__ __forceinline__ float load1(const void* base, int64_t off) {
+    return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[off]);
+  }
+  static __device__ __forceinline__ void store8(void* base, int64_t off, const float (&x)[8]) {
+    uint4 u;
+    const uint2 a = pack4_bf16(x[0], x[1], x[2], x[3]);
+    const uint2 b = pack4_bf16(x[4], x[5], x[6], x[7]);
+    u.x = a.x; u.y = a.y; u.z = b.x; u.w = b.y;
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = u;
+  }
+  static __device__ __forceinline__ void store4(void* base, int64_t off, float a, float b, float c, float d) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) = pack4_bf16(a, b, c, d);
+  }
+  static __device__ __forceinline__ void store1(void* base, int64_t off, float x) {
+    static_cast<uint16_t*>(base)[off] = f32_to_bf16_bits(x);
+  }
+};
+
+template <> struct IO<float> {
+  static __device__ __forceinline__ void load8(const void* base, int64_t off, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  static __device__ __forceinline__ void load4(const void* base, int64_t off, float (&x)[4]) {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  }
+  static __device__ __forceinline__ float load1(const void* base, int64_t off) {
+    return static_cast<const float*>(base)[off];
+  }
+  static __device__ __forceinline__ void store8(void* base, int64_t off, const float (&x)[8]) {
+    float* p = static_cast<float*>(base) + off;
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+  static __device__ __forceinline__ void store4(void* base, int64_t off, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + off) = make_float4(a, b, c, d);
+  }
+  static __device__ __forceinline__ void store1(void* base, int64_t off, float x) {
+    static_cast<float*>(base)[off] = x;
+  }
+};
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = WIDTH / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// softplus(x) = max(x, 0) + log1p(exp(-|x|)), stable for every x
+__device__ __forceinline__ float softplusf(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
+
+}  // namespace gdr

@@ -1,0 +1,85 @@
+// Internal declarations shared by the host API (gdr_api.cpp) and the kernels
+// (gdr_kernels.hip): workspace layout, the chunk/sequence tables and the
+// parameter block every kernel receives by value.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdr.h"
+
+namespace gdr {
+
+constexpr int kChunk = 64;     // tokens per chunk
+constexpr int kThreads = 256;  // threads per workgroup in every kernel (4 wave64s)
+
+// One row per chunk (global chunk index c).
+struct ChunkEntry {
+  int32_t t_start;   // first token (packed token axis)
+  int32_t len;       // valid rows, 1..64
+  int32_t seq;       // sequence index
+  int32_t idx;       // chunk index inside its sequence
+};
+
+// One row per sequence, ordered longest first so the serial kernels start the
+// longest chains first.
+struct SeqEntry {
+  int32_t seq;       // sequence index (addresses h0/dht/dh0/ht)
+  int32_t len;       // tokens
+  int32_t c0;        // global index of its first chunk
+  int32_t nchunks;   // ceil(len / 64)
+};
+
+// Byte offsets of every workspace region (all 256-byte aligned).
+struct WsLayout {
+  int64_t NC = 0;    // total chunks
+  size_t ctab = 0, stab = 0;
+  size_t gam = 0;    // fp32 [H][NC][64] or [H][NC][64][K]: in-chunk cumsum of the log decay
+  size_t rho = 0;    // fp32 [H][NC][2][64]: 1/|q|, 1/|k| per row
+  size_t A = 0;      // bf16 [H][NC][64][64]: UT/WY inverse
+  size_t P = 0;      // bf16 [H][NC][64][64]: scale * (Qn Kn^T o E), lower incl. diagonal
+  size_t W = 0;      // bf16 [H][NC][64][K]:  A diag(beta) Kbar
+  size_t Up = 0;     // bf16 [H][NC][64][V]:  U' = A diag(beta) V
+  size_t U = 0;      // bf16 [H][NC][64][V]:  v_new = U' - W S^T (forward state pass)
+  size_t S = 0;      // bf16 [H][NC][V][K]:   state at chunk start
+  size_t dS = 0;     // bf16 [H][NC][V][K]:   gradient w.r.t. the state at chunk end
+  size_t dU = 0;     // bf16 [H][NC][64][V]:  gradient w.r.t. v_new
+  size_t dqn = 0;    // fp32 [H][NC][64][K]
+  size_t dkn = 0;    // fp32 [H][NC][64][K]
+  size_t dgam = 0;   // fp32 [H][NC][64] or [H][NC][64][K]
+  size_t dgamc = 0;  // fp32 [H][NC] or [H][NC][K]
+  size_t dbeta = 0;  // fp32 [H][NC][64]: gradient w.r.t. beta (sigmoid space)
+  size_t total = 0;
+};
+
+struct Params {
+  int32_t H, K, V, N, NC, T;     // T = total tokens
+  int32_t gate, dtype;
+  float scale;
+  // inputs
+  const void *q, *k, *v, *g, *b, *dO;
+  const float *A_log, *dt_bias, *h0, *dht;
+  // outputs
+  void *dq, *dk, *dv, *dg, *db;
+  float *dh0, *dA_log, *ddt_bias, *ht;
+  // workspace
+  const ChunkEntry* ctab;
+  const SeqEntry* stab;
+  float* gam;
+  float* rho;
+  uint16_t *A, *P, *W, *Up, *U, *S, *dS, *dU;   // bf16 bit patterns
+  float *dqn, *dkn, *dgam, *dgamc, *dbeta;
+};
+
+// Chain-kernel roles.
+enum ChainMode { kChainFwd = 1, kChainBwd = 2, kChainBoth = 3 };
+
+// Kernel launchers (gdr_kernels.hip).  Return a hipError_t as int.
+int launch_prep(const Params& p, void* stream);
+int launch_chain(const Params& p, int mode, void* stream);
+int launch_grads(const Params& p, void* stream);
+int launch_finish(const Params& p, void* stream);
+int launch_zero_params(const Params& p, void* stream);
+const char* hip_error_string(int err);
+
+}  // namespace gdr

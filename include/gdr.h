@@ -1,0 +1,148 @@
+/*
+ * gdr.h -- C ABI of the chunked gated delta-rule backward for AMD MI355X (gfx950).
+ *
+ * The op.  Per sequence n and head h, with Dv x Dk state S and tokens t:
+ *   qn = q / sqrt(|q|^2 + 1e-6), kn likewise, beta = sigmoid(b),
+ *   lambda_t = g_t                                   (GDR_GATE_SCALAR, GDN)
+ *   lambda_t = -exp(A_log[h]) * softplus(g_t + dt_bias[h])  (GDR_GATE_CHANNEL, KDA)
+ *   S_t = S_{t-1} Diag(exp(lambda_t)) (I - beta_t kn_t kn_t^T) + beta_t v_t kn_t^T,
+ *   o_t = scale * S_t qn_t,  S_0 = h0 (or 0).
+ * The backward returns the gradients of L = sum_t <dO_t, o_t> + <dht, S_T> with
+ * respect to q, k, v, g, the beta logit, h0, A_log and dt_bias.
+ *
+ * Citations (the pages describing the method):
+ *  - FlashQLA GDN backward overview (lqnn.cn/news/272630), section 1: entry
+ *    conventions -- dh0 returned in fp32 while dq/dk/dv are stored in bf16,
+ *    dht optional (absent = zero); section 2: the state gradient recursion runs
+ *    strictly from the last chunk to the first; section 3: the recursion
+ *    dh <- g_last*dh + R^T dO + X^T Y with X = A_beta K.
+ *  - FlashKDA backward "K1" page (yuyanqi.com), listing and sections 1-6: the
+ *    prepare stage (L2-norm backward, reverse cumsum of the gate gradient plus
+ *    the chunk-total term, gate backward, per-head parameter sums by atomics,
+ *    beta-logit backward, tail-row masking).
+ *
+ * Memory and streams.  Every pointer is caller-owned.  Token tensors are
+ * row-major [B, T, H, D] (dense) or [1, T_total, H, D] (varlen, B == 1 and
+ * T == T_total); per-token scalars are [B, T, H]; states are [N, H, Dv, Dk]
+ * fp32.  Device pointers must be 16-byte aligned.  The library never allocates,
+ * frees or synchronises: all work is enqueued on `stream` (a hipStream_t; NULL
+ * = the null stream).  The workspace carries state from gdr_fwd_recompute to
+ * gdr_bwd; its layout is internal (gdr_workspace_region exposes it for tests).
+ * Outputs are overwritten, never accumulated.
+ *
+ * Errors.  All argument checks run before anything is enqueued; a non-OK status
+ * means nothing was launched, except GDR_EHIP (a HIP call failed while
+ * enqueueing).  gdr_last_error() returns a thread-local message for the last
+ * non-OK status of the calling thread.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDR_OK = 0,
+  GDR_EINVAL = 1,        /* bad argument: null/misaligned pointer, bad cu_seqlens, gate/param mismatch */
+  GDR_EUNSUPPORTED = 2,  /* Dk != Dv, D not in {64, 128}, or a size beyond the int32 index range */
+  GDR_EWORKSPACE = 3,    /* workspace smaller than gdr_workspace_bytes() */
+  GDR_EHIP = 4           /* a HIP runtime call failed while enqueueing */
+} gdr_status;
+
+typedef enum { GDR_GATE_SCALAR = 0, GDR_GATE_CHANNEL = 1 } gdr_gate;
+typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
+
+typedef struct {
+  int32_t B, T, H, Dk, Dv;          /* dense: [B,T,H,D]; varlen: B == 1, T == total tokens */
+  int32_t N;                        /* sequences: == B when dense, == len(cu_seqlens) - 1 when varlen */
+  const int64_t* cu_seqlens_host;   /* host array [N+1], non-decreasing, [0] == 0, [N] == T; NULL = dense.
+                                       Read during the call only. */
+  int32_t gate;                     /* gdr_gate */
+  int32_t dtype;                    /* gdr_dtype of q, k, v, g, b, dO and of dq, dk, dv, dg, dbeta */
+  float scale;                      /* readout scale (usually 1/sqrt(Dk)) */
+} gdr_shape;
+
+typedef struct {                    /* device pointers */
+  const void *q, *k;                /* [B,T,H,Dk] dtype */
+  const void *v;                    /* [B,T,H,Dv] dtype */
+  const void *g;                    /* SCALAR: [B,T,H] log decay; CHANNEL: [B,T,H,Dk] raw gate; dtype */
+  const void *beta_logit;           /* [B,T,H] dtype (pre-sigmoid) */
+  const float *A_log;               /* CHANNEL: [H]; SCALAR: must be NULL */
+  const float *dt_bias;             /* CHANNEL: [H,Dk]; SCALAR: must be NULL */
+  const float *h0;                  /* [N,H,Dv,Dk] or NULL (zero initial state) */
+} gdr_inputs;
+
+typedef struct {                    /* device pointers, all overwritten */
+  void *dq, *dk;                    /* [B,T,H,Dk] dtype */
+  void *dv;                         /* [B,T,H,Dv] dtype */
+  void *dg;                         /* SCALAR: [B,T,H]; CHANNEL: [B,T,H,Dk] (w.r.t. the raw gate); dtype */
+  void *dbeta;                      /* [B,T,H] dtype, w.r.t. the logit */
+  float *dh0;                       /* [N,H,Dv,Dk] or NULL (not returned) */
+  float *dA_log, *ddt_bias;         /* CHANNEL: [H], [H,Dk] required; SCALAR: must be NULL */
+} gdr_grads;
+
+/* Bytes of workspace the three compute calls need for this shape. */
+gdr_status gdr_workspace_bytes(const gdr_shape* shape, size_t* bytes);
+
+/* Forward recompute: per-chunk prologue (normalisation, beta, in-chunk gate
+ * cumsum, the UT/WY inverse A = (I + StrictLower(diag(beta) (K K^T o decay)))^-1
+ * and W = A diag(beta) K e^Gamma, U' = A diag(beta) V), then the serial state
+ * pass storing the state at the start of every chunk and v_new = U' - W S^T.
+ * Optional outputs: ht = final state per sequence ([N,H,Dv,Dk] fp32, NULL to
+ * skip).  Leaves what gdr_bwd needs in `ws`; every stage only reads inputs and
+ * what earlier stages wrote, so any call may be repeated. */
+gdr_status gdr_fwd_recompute(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes,
+                             float* ht, void* stream);
+
+/* Backward, after gdr_fwd_recompute on the same shape, inputs and workspace:
+ * reverse-chunk state-gradient recursion (dh0), chunk-parallel gradients, and
+ * the prepare-backward stage.  dO: [B,T,H,Dv] dtype; dht: [N,H,Dv,Dk] fp32 or
+ * NULL (zero). */
+gdr_status gdr_bwd(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht,
+                   void* ws, size_t ws_bytes, gdr_grads* grads, void* stream);
+
+/* The whole backward in one call: the same kernels as gdr_fwd_recompute
+ * followed by gdr_bwd, except that the forward state pass and the reverse
+ * state-gradient recursion (which do not depend on each other) run side by
+ * side in one launch.  Same results; ht may be NULL. */
+gdr_status gdr_fwd_bwd(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht,
+                       void* ws, size_t ws_bytes, gdr_grads* grads, float* ht, void* stream);
+
+/* Workspace regions, for tests that inspect intermediates.  Layouts (NC =
+ * total chunks of 64 tokens over all sequences, chunk c of sequence n numbered
+ * after all chunks of sequences < n; rows past a sequence's end are padding):
+ *   GDR_WS_STATE   bf16 [H][NC][Dv][Dk]  state at the start of each chunk
+ *   GDR_WS_DSTATE  bf16 [H][NC][Dv][Dk]  gradient w.r.t. the state at the end of each chunk
+ *   GDR_WS_U       bf16 [H][NC][64][Dv]  v_new = U' - W S^T
+ *   GDR_WS_A       bf16 [H][NC][64][64]  the UT/WY inverse
+ *   GDR_WS_GAMMA   fp32 [H][NC][64] (SCALAR) or [H][NC][64][Dk] (CHANNEL): in-chunk gate cumsum
+ */
+enum { GDR_WS_STATE = 0, GDR_WS_DSTATE = 1, GDR_WS_U = 2, GDR_WS_A = 3, GDR_WS_GAMMA = 4 };
+gdr_status gdr_workspace_region(const gdr_shape* shape, int32_t which, size_t* offset, size_t* bytes);
+
+/* One stage of gdr_fwd_bwd enqueued alone, for benchmarks and kernel profiles
+ * (same arguments as gdr_fwd_bwd; the workspace must already hold what the
+ * earlier stages leave there, e.g. after one gdr_fwd_bwd call).  Stages:
+ *   GDR_STAGE_PREP        per-chunk prologue and UT/WY inverse (one launch)
+ *   GDR_STAGE_CHAIN_FWD   forward state pass alone
+ *   GDR_STAGE_CHAIN_BWD   reverse state-gradient recursion alone
+ *   GDR_STAGE_CHAIN_BOTH  both recursions in one launch, as gdr_fwd_bwd runs them
+ *   GDR_STAGE_GRADS       chunk-parallel gradients
+ *   GDR_STAGE_FINISH      prepare-backward (norm, sigmoid, gate, parameter sums) */
+enum { GDR_STAGE_PREP = 0, GDR_STAGE_CHAIN_FWD = 1, GDR_STAGE_CHAIN_BWD = 2, GDR_STAGE_CHAIN_BOTH = 3,
+       GDR_STAGE_GRADS = 4, GDR_STAGE_FINISH = 5 };
+gdr_status gdr_run_stage(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht,
+                         void* ws, size_t ws_bytes, gdr_grads* grads, float* ht, int32_t stage, void* stream);
+
+/* Thread-local text for the last non-OK status returned to this thread. */
+const char* gdr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

@@ -1,0 +1,92 @@
+"""Shared helpers for the GPU tests: run the HIP path through the C ABI and
+compare with the float64 oracle on the same input bytes."""
+
+from __future__ import annotations
+
+import sys
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+import torch
+
+from chunked_gated_delta_bwd_amd import binding as B
+
+# Tolerances (normalised error |X - ref|_F / |ref|_F, float64): per-token
+# gradients in bf16 storage, and the fp32 state-gradient / parameter outputs.
+TOL_BF16 = 2e-2
+TOL_FP32 = 1e-3
+TOKEN_GRADS = ("dq", "dk", "dv", "dg", "db")
+FP32_GRADS = ("dh0", "dA_log", "ddt_bias")
+
+
+def nerr(x: np.ndarray, ref: np.ndarray) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(x - ref)
+    return float(num / den) if den > 0 else float(num)
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_run(inp: Dict, mode: str = "fused", exports: bool = False) -> Dict[str, np.ndarray]:
+    """Runs the backward on cuda:0 through the C ABI; float64 host copies."""
+    dev = B.to_device(inp)
+    prob = B.Problem.from_inputs(inp)
+    ws = B.alloc_workspace(prob)
+    out = B.alloc_outputs(inp, dev)
+    N, H, K, V = inp["N"], inp["H"], inp["K"], inp["V"]
+    ht = torch.empty((N, H, V, K), dtype=torch.float32, device="cuda")
+    if mode == "fused":
+        B.gdr_fwd_bwd(prob, dev, dev["dO"], dev["dht"], ws, out, ht=ht)
+    elif mode == "split":
+        B.gdr_fwd_recompute(prob, dev, ws, ht=ht)
+        B.gdr_bwd(prob, dev, dev["dO"], dev["dht"], ws, out)
+    else:
+        raise ValueError(mode)
+    torch.cuda.synchronize()
+    res = {k: v.double().cpu().numpy() for k, v in out.items() if v is not None}
+    res["ht"] = ht.double().cpu().numpy()
+    if exports:
+        NC = sum((L + 63) // 64 for L in inp["lengths"])
+        for name, which, shape in (("S_chunk", B.GDR_WS_STATE, (H, NC, V, K)),
+                                   ("dS_chunk", B.GDR_WS_DSTATE, (H, NC, V, K))):
+            off, n = B.gdr_workspace_region(prob, which)
+            res[name] = ws[off:off + n].view(torch.bfloat16).view(shape).double().cpu().numpy()
+    return res
+
+
+def subset_heads(inp: Dict, heads: Iterable[int]) -> Dict:
+    """The same problem restricted to some heads (heads never interact)."""
+    heads = list(heads)
+    idx = torch.tensor(heads, dtype=torch.long)
+    out = dict(inp)
+    for key in ("q", "k", "v", "dO", "g", "b"):
+        out[key] = inp[key].index_select(2, idx).contiguous()
+    for key in ("h0", "dht"):
+        if inp.get(key) is not None:
+            out[key] = inp[key].index_select(1, idx).contiguous()
+    for key in ("A_log", "dt_bias"):
+        if inp.get(key) is not None:
+            out[key] = inp[key].index_select(0, idx).contiguous()
+    out["H"] = len(heads)
+    return out
+
+
+def compare(got: Dict, ref: Dict, keys, tol: float, label: str, head_index: Optional[list] = None) -> Dict:
+    errs = {}
+    for key in keys:
+        if key not in ref:
+            continue
+        x = got[key]
+        if head_index is not None:
+            axis = 0 if key in ("dA_log", "ddt_bias") else (1 if key in ("dh0", "ht") else 2)
+            x = np.take(x, head_index, axis=axis)
+        errs[key] = nerr(x, ref[key])
+    log(f"[{label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{label}: {bad} above {tol}"
+    return errs

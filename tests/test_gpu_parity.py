@@ -1,0 +1,92 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle on the
+same seeded input bytes.  Normalised errors |X - ref| / |ref| must stay within
+2e-2 for the per-token gradients (stored in bf16) and 1e-3 for dh0, dA_log and
+ddt_bias (fp32).  Small problems are compared in full; full-size workloads are
+compared on sampled heads (heads are independent, so the oracle runs the exact
+same computation for them)."""
+
+import pytest
+import torch
+
+import oracle
+from chunked_gated_delta_bwd_amd import synth
+from gpu_common import (FP32_GRADS, TOKEN_GRADS, TOL_BF16, TOL_FP32, compare, gpu_run, log,
+                        subset_heads)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _check(inp, got, label, heads=None):
+    sub = inp if heads is None else subset_heads(inp, heads)
+    ref = oracle.run(sub)
+    compare(got, ref, TOKEN_GRADS, TOL_BF16, label + " grads", heads)
+    compare(got, ref, FP32_GRADS, TOL_FP32, label + " fp32", heads)
+    compare(got, ref, ("ht",), TOL_FP32 * 5, label + " ht", heads)
+
+
+SMALL = [
+    ("gdn_f32_t128_h2_d64", synth.workload("gdn_f32_t128_h2_d64")),
+    ("gdn_bf16_varlen_edges_d128",
+     synth.Spec("e", 0, "bf16", H=3, K=128, V=128, lengths=[1, 63, 64, 65, 0, 200], h0_std=0.1,
+                dht_std=0.1, seed=31)),
+    ("gdn_f32_b2_t100_d64", synth.Spec("f", 0, "f32", H=2, K=64, V=64, B=2, T=100, seed=32)),
+    ("gdn_bf16_b1_t300_d64_h0", synth.Spec("g", 0, "bf16", H=4, K=64, V=64, B=1, T=300, h0_std=0.5,
+                                           dht_std=0.5, seed=33)),
+]
+
+
+@pytest.mark.parametrize("name,spec", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_small_against_oracle(name, spec, mode):
+    log(f"case {name} mode {mode}")
+    inp = synth.generate(spec)
+    got = gpu_run(inp, mode=mode)
+    _check(inp, got, f"{name}/{mode}")
+
+
+def test_chunk_boundary_states():
+    """Stage check: states at chunk starts and state gradients at chunk ends."""
+    spec = synth.Spec("s", 0, "bf16", H=2, K=128, V=128, lengths=[130, 64, 5], h0_std=0.2, dht_std=0.2,
+                      seed=34)
+    inp = synth.generate(spec)
+    got = gpu_run(inp, exports=True)
+    ref = oracle.run(inp, exports=True)
+    compare(got, ref, ("S_chunk", "dS_chunk"), 1e-2, "chunk states")
+
+
+def test_fused_and_split_agree():
+    inp = synth.generate(synth.Spec("a", 0, "bf16", H=4, K=128, V=128, B=1, T=512, h0_std=0.1,
+                                    dht_std=0.1, seed=35))
+    a = gpu_run(inp, mode="fused")
+    b = gpu_run(inp, mode="split")
+    for key in TOKEN_GRADS + ("dh0", "ht"):
+        assert (a[key] == b[key]).all(), key
+
+
+def test_repeat_is_deterministic():
+    inp = synth.generate(synth.Spec("r", 0, "bf16", H=2, K=128, V=128, B=2, T=256, seed=36))
+    a = gpu_run(inp)
+    b = gpu_run(inp)
+    for key in TOKEN_GRADS + ("dh0",):
+        assert (a[key] == b[key]).all(), key
+
+
+def test_workload_b2_t4096_h16():
+    inp = synth.generate(synth.workload("gdn_bf16_b2_t4096_h16_d128"))
+    got = gpu_run(inp)
+    _check(inp, got, "gdn_bf16_b2_t4096_h16_d128")
+
+
+def test_workload_varlen12_h32_sampled_heads():
+    inp = synth.generate(synth.workload("gdn_varlen12_bf16_t32768_h32_d128"))
+    assert any(L % 64 for L in inp["lengths"])
+    got = gpu_run(inp)
+    _check(inp, got, "gdn_varlen12_h32", heads=[0, 17, 31])
+
+
+@pytest.mark.parametrize("H", [16, 32])
+def test_workload_t32768_sampled_heads(H):
+    inp = synth.generate(synth.workload(f"gdn_bf16_t32768_h{H}_d128"))
+    got = gpu_run(inp)
+    _check(inp, got, f"gdn_t32768_h{H}", heads=[0, H - 1])
