@@ -152,7 +152,7 @@ gdr_status upload_tables(const gdr_shape* s, const gdr::WsLayout& L, void* ws, h
     const int64_t e = s->cu_seqlens_host ? s->cu_seqlens_host[n + 1] : int64_t(n + 1) * s->T;
     const int len = int(e - b);
     const int nck = (len + gdr::kChunk - 1) / gdr::kChunk;
-    st[n] = gdr::SeqEntry{n, len, int32_t(c), nck};
+    st[n] = gdr::SeqEntry{n, len, int32_t(c), nck, int32_t(b), {0, 0, 0}};
     for (int i = 0; i < nck; ++i, ++c) {
       const int rows = std::min(gdr::kChunk, len - i * gdr::kChunk);
       ct[c] = gdr::ChunkEntry{int32_t(b + int64_t(i) * gdr::kChunk), rows, n, i};

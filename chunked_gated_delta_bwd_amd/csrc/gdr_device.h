@@ -73,6 +73,29 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
 template <typename T> struct IO;
 
 template <> struct IO<bf16> {
+  // raw (still packed) register images, so that a prefetch keeps loads in
+  // flight and unpacks only where the data is consumed
+  typedef u32x4 Raw8;
+  typedef unsigned int __attribute__((ext_vector_type(2))) Raw4;
+  static __device__ __forceinline__ Raw8 load_raw8(const void* base, int64_t off) {
+    return *reinterpret_cast<const Raw8*>(static_cast<const uint16_t*>(base) + off);
+  }
+  static __device__ __forceinline__ Raw4 load_raw4(const void* base, int64_t off) {
+    return *reinterpret_cast<const Raw4*>(static_cast<const uint16_t*>(base) + off);
+  }
+  static __device__ __forceinline__ void unpack8(const Raw8& u, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(u[i] << 16);
+      x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void unpack4(const Raw4& u, float (&x)[4]) {
+    x[0] = __uint_as_float(u[0] << 16);
+    x[1] = __uint_as_float(u[0] & 0xffff0000u);
+    x[2] = __uint_as_float(u[1] << 16);
+    x[3] = __uint_as_float(u[1] & 0xffff0000u);
+  }
   static __device__ __forceinline__ void load8(const void* base, int64_t off, float (&x)[8]) {
     const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -108,6 +131,26 @@ template <> struct IO<bf16> {
 };
 
 template <> struct IO<float> {
+  struct Raw8 { f32x4 a, b; };
+  typedef f32x4 Raw4;
+  static __device__ __forceinline__ Raw8 load_raw8(const void* base, int64_t off) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + off);
+    return Raw8{p[0], p[1]};
+  }
+  static __device__ __forceinline__ Raw4 load_raw4(const void* base, int64_t off) {
+    return *reinterpret_cast<const Raw4*>(static_cast<const float*>(base) + off);
+  }
+  static __device__ __forceinline__ void unpack8(const Raw8& u, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = u.a[i];
+      x[4 + i] = u.b[i];
+    }
+  }
+  static __device__ __forceinline__ void unpack4(const Raw4& u, float (&x)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = u[i];
+  }
   static __device__ __forceinline__ void load8(const void* base, int64_t off, float (&x)[8]) {
     const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
     const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off + 4);

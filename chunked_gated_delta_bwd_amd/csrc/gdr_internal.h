@@ -28,6 +28,8 @@ struct SeqEntry {
   int32_t len;       // tokens
   int32_t c0;        // global index of its first chunk
   int32_t nchunks;   // ceil(len / 64)
+  int32_t t_start;   // first token (packed token axis)
+  int32_t pad[3];
 };
 
 // Byte offsets of every workspace region (all 256-byte aligned).

@@ -80,14 +80,20 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     float qv[8], kv[8];
-    if (r < len) {
-      const int64_t off = tok(t0 + r, H, h) * D + c0;
+    {
+      // unconditional loads from a clamped row, masked afterwards (no branch
+      // around the loads, so they are not serialised)
+      const int64_t off = tok(t0 + min(r, len - 1), H, h) * D + c0;
       IO<TIO>::load8(p.q, off, qv);
       IO<TIO>::load8(p.k, off, kv);
       IO<TIO>::load8(p.v, off, v_r[ps]);
-    } else {
+      const float m = r < len ? 1.f : 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qv[e] = kv[e] = v_r[ps][e] = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        qv[e] *= m;
+        kv[e] *= m;
+        v_r[ps][e] *= m;
+      }
     }
     float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -111,12 +117,10 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   }
   // --- beta and the in-chunk cumsum of the log decay (wave 0) ---
   if (w == 0) {
-    float lam = 0.f, bt = 0.f;
-    if (l < len) {
-      const int64_t o = tok(t0 + l, H, h);
-      lam = IO<TIO>::load1(p.g, o);
-      bt = sigmoidf(IO<TIO>::load1(p.b, o));
-    }
+    const int64_t o = tok(t0 + min(l, len - 1), H, h);
+    const float m = l < len ? 1.f : 0.f;
+    float lam = m * IO<TIO>::load1(p.g, o);
+    const float bt = m * sigmoidf(IO<TIO>::load1(p.b, o));
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
       const float y = __shfl_up(lam, m, 64);
@@ -234,10 +238,164 @@ struct ChainSmem {
   static constexpr size_t bytes = fwd > bwd ? fwd : bwd;
 };
 
+// Each recursion keeps two register sets of prefetched chunk data (raw, not
+// unpacked): the set stashed into LDS at step k was loaded at step k-2, so every
+// load has two full steps to arrive while vmcnt waits only for the older set.
+template <int D, typename TIO>
+struct FwdPrefetch {
+  using Dm = Dims<D>;
+  u32x4 w[Dm::NPASS];
+  typename IO<TIO>::Raw8 k[Dm::NPASS];
+  float rk[Dm::NPASS], g[Dm::NPASS], m[Dm::NPASS], gC;
+  uint16_t u[4];
+};
+
+template <int D, typename TIO>
+struct BwdPrefetch {
+  using Dm = Dims<D>;
+  u32x4 w[Dm::NPASS], pm[2];
+  typename IO<TIO>::Raw8 k[Dm::NPASS], q[Dm::NPASS];
+  typename IO<TIO>::Raw4 dO;
+  float rk[Dm::NPASS], g[Dm::NPASS], m[Dm::NPASS], gC, rq_do, g_do, m_do;
+};
+
+// Loads of one chunk into registers: unconditional (rows past the sequence end
+// read its last row and are masked at the stash) and with no arithmetic on the
+// loaded values, so nothing waits for them before the stash.
+template <int D, typename TIO>
+__device__ __forceinline__ void fwd_load(FwdPrefetch<D, TIO>& f, const Params& p, const SeqEntry& se, int h,
+                                         int v0, int c) {
+  using Dm = Dims<D>;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int64_t ch = int64_t(h) * p.NC + c;
+  const int ct0 = se.t_start + (c - se.c0) * C;
+  const int clen = min(C, se.len - (c - se.c0) * C);
+#pragma unroll
+  for (int ps = 0; ps < Dm::NPASS; ++ps) {
+    const int r = ps * Dm::RPP + tid / Dm::TPR, c0 = (tid % Dm::TPR) * 8;
+    f.w[ps] = *reinterpret_cast<const u32x4*>(p.W + (ch * C + r) * D + c0);
+    f.k[ps] = IO<TIO>::load_raw8(p.k, tok(ct0 + min(r, clen - 1), p.H, h) * D + c0);
+    f.m[ps] = r < clen ? 1.f : 0.f;
+    f.rk[ps] = p.rho[ch * 2 * C + C + r];
+    f.g[ps] = p.gam[ch * C + r];
+  }
+  f.gC = p.gam[ch * C + C - 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.u[i] = p.Up[(ch * C + 16 * w + 4 * (l >> 4) + i) * D + v0 + (l & 15)];
+}
+
+// Khat = kn e^(GamC - Gam) and W into LDS buffer `buf`; U' into registers.
+template <int D, typename TIO>
+__device__ __forceinline__ void fwd_stash(const FwdPrefetch<D, TIO>& f, bf16* Ws, bf16* Kh, float* dec,
+                                          float (&up)[4]) {
+  using Dm = Dims<D>;
+  constexpr int PD = Dm::PD;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int ps = 0; ps < Dm::NPASS; ++ps) {
+    const int r = ps * Dm::RPP + tid / Dm::TPR, c0 = (tid % Dm::TPR) * 8;
+    *reinterpret_cast<u32x4*>(Ws + r * PD + c0) = f.w[ps];
+    const float s = f.m[ps] * f.rk[ps] * fast_exp(f.gC - f.g[ps]);
+    float kx[8];
+    IO<TIO>::unpack8(f.k[ps], kx);
+    bf16x8 kb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kb[e] = to_bf16(kx[e] * s);
+    *reinterpret_cast<bf16x8*>(Kh + r * PD + c0) = kb;
+  }
+  if (tid == 0) *dec = fast_exp(f.gC);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) up[i] = bf16_bits_to_f32(f.u[i]);
+}
+
+template <int D, typename TIO>
+__device__ __forceinline__ void bwd_load(BwdPrefetch<D, TIO>& f, const Params& p, const SeqEntry& se, int h,
+                                         int v0, int c) {
+  using Dm = Dims<D>;
+  const int tid = threadIdx.x;
+  const int64_t ch = int64_t(h) * p.NC + c;
+  const int ct0 = se.t_start + (c - se.c0) * C;
+  const int clen = min(C, se.len - (c - se.c0) * C);
+#pragma unroll
+  for (int ps = 0; ps < Dm::NPASS; ++ps) {
+    const int r = ps * Dm::RPP + tid / Dm::TPR, c0 = (tid % Dm::TPR) * 8;
+    f.w[ps] = *reinterpret_cast<const u32x4*>(p.W + (ch * C + r) * D + c0);
+    const int64_t o = tok(ct0 + min(r, clen - 1), p.H, h) * D + c0;
+    f.k[ps] = IO<TIO>::load_raw8(p.k, o);
+    f.q[ps] = IO<TIO>::load_raw8(p.q, o);
+    f.m[ps] = r < clen ? 1.f : 0.f;
+    f.rk[ps] = p.rho[ch * 2 * C + C + r];
+    f.g[ps] = p.gam[ch * C + r];
+  }
+  f.gC = p.gam[ch * C + C - 1];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int pc = tid + x * kThreads;   // 16-byte piece of the 64x64 P tile
+    f.pm[x] = *reinterpret_cast<const u32x4*>(p.P + (ch * C + pc / 8) * C + (pc % 8) * 8);
+  }
+  const int r = tid / 4, c0 = (tid % 4) * 4;
+  f.dO = IO<TIO>::load_raw4(p.dO, tok(ct0 + min(r, clen - 1), p.H, h) * D + v0 + c0);
+  f.m_do = r < clen ? 1.f : 0.f;
+  f.rq_do = p.rho[ch * 2 * C + r];
+  f.g_do = p.gam[ch * C + r];
+}
+
+// Khat, raw q (exact in bf16; high/low parts for fp32 inputs), W, P, the raw dO
+// slice and the scaled slice f*dO (f_r = scale rho_r e^Gam_r) split into bf16
+// high + low parts.  The Qbar^T dO term is then q^T (f dO) with no rounding of
+// Qbar: it dominates dh0.
+template <int D, typename TIO, bool QLO>
+__device__ __forceinline__ void bwd_stash(const BwdPrefetch<D, TIO>& f, float scale, bf16* Kh, bf16* Qb, bf16* Ql,
+                                          bf16* Ws, bf16* Ps, bf16* dOr, bf16* dFh, bf16* dFl, float* dec) {
+  using Dm = Dims<D>;
+  constexpr int PD = Dm::PD, PO = 24;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int ps = 0; ps < Dm::NPASS; ++ps) {
+    const int r = ps * Dm::RPP + tid / Dm::TPR, c0 = (tid % Dm::TPR) * 8;
+    *reinterpret_cast<u32x4*>(Ws + r * PD + c0) = f.w[ps];
+    const float fk = f.m[ps] * f.rk[ps] * fast_exp(f.gC - f.g[ps]);
+    float kx[8], qx[8];
+    IO<TIO>::unpack8(f.k[ps], kx);
+    IO<TIO>::unpack8(f.q[ps], qx);
+    bf16x8 kb, qb, ql;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float qv = qx[e] * f.m[ps];
+      kb[e] = to_bf16(kx[e] * fk);
+      qb[e] = to_bf16(qv);
+      if constexpr (QLO) ql[e] = to_bf16(qv - float(qb[e]));
+    }
+    *reinterpret_cast<bf16x8*>(Kh + r * PD + c0) = kb;
+    *reinterpret_cast<bf16x8*>(Qb + r * PD + c0) = qb;
+    if constexpr (QLO) *reinterpret_cast<bf16x8*>(Ql + r * PD + c0) = ql;
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int pc = tid + x * kThreads;
+    *reinterpret_cast<u32x4*>(Ps + (pc / 8) * PC + (pc % 8) * 8) = f.pm[x];
+  }
+  const int r = tid / 4, c0 = (tid % 4) * 4;
+  const float fs = f.m_do * scale * f.rq_do * fast_exp(f.g_do);
+  float dx[4], fh[4], fl[4];
+  IO<TIO>::unpack4(f.dO, dx);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x = dx[e] * fs;
+    fh[e] = float(to_bf16(x));
+    fl[e] = x - fh[e];
+    dx[e] *= f.m_do;
+  }
+  st_bf16x4(dOr + r * PO + c0, dx[0], dx[1], dx[2], dx[3]);
+  st_bf16x4(dFh + r * PO + c0, fh[0], fh[1], fh[2], fh[3]);
+  st_bf16x4(dFl + r * PO + c0, fl[0], fl[1], fl[2], fl[3]);
+  if (tid == 0) *dec = fast_exp(f.gC);
+}
+
 template <int D, typename TIO>
 __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, int h, int sl) {
   using Dm = Dims<D>;
-  constexpr int PD = Dm::PD, TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS, NJW = Dm::NJW;
+  constexpr int PD = Dm::PD, NJW = Dm::NJW;
   // double-buffered tiles: buffer b of X starts at X0 + b * C * PD
   bf16* const Ws0 = reinterpret_cast<bf16*>(smem);
   bf16* const Kh0 = Ws0 + 2 * C * PD;
@@ -245,11 +403,12 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
   bf16* Ut = Ss + 16 * PD;       // U[r][v] stored as Ut[v][r]
   float* dec = reinterpret_cast<float*>(Ut + 16 * PC);
 
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  const int l = lane_id(), w = wave_id();
   const int g = l >> 4, jj = l & 15;
   const int H = p.H;
   const SeqEntry se = p.stab[si];
   const int v0 = 16 * sl;
+  const int nck = se.nchunks;
 
   f32x4 acc[NJW];
 #pragma unroll
@@ -263,95 +422,60 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     }
   }
 
-  // register prefetch of one chunk
-  u32x4 pw[NPASS];
-  float pk[NPASS][8], prk[NPASS], pg[NPASS], pgC;
-  uint16_t pu[4];
-  auto load = [&](int c) __attribute__((always_inline)) {
+  FwdPrefetch<D, TIO> A, Bp;
+  float up[4];
+  // one chunk k (0-based in this sequence) on LDS buffer `buf`; `nx` holds chunk
+  // k+1 (stashed into the other buffer here) and is refilled with chunk k+3
+  auto step = [&](int k, int buf, FwdPrefetch<D, TIO>& nx) __attribute__((always_inline)) {
+    const int c = se.c0 + k;
     const int64_t ch = int64_t(h) * p.NC + c;
-    const ChunkEntry ce = p.ctab[c];
+    // S_k: to LDS (operand of U) and to the workspace
 #pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
-      pw[ps] = *reinterpret_cast<const u32x4*>(p.W + (ch * C + r) * D + c0);
-      if (r < ce.len) {
-        IO<TIO>::load8(p.k, tok(ce.t_start + r, H, h) * D + c0, pk[ps]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pk[ps][e] = 0.f;
-      }
-      prk[ps] = p.rho[ch * 2 * C + C + r];
-      pg[ps] = p.gam[ch * C + r];
+    for (int x = 0; x < NJW; ++x) {
+      const int j = 16 * (w * NJW + x) + 4 * g;
+      st_bf16x4(Ss + jj * PD + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+      st_bf16x4(p.S + (ch * D + v0 + jj) * D + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
     }
-    pgC = p.gam[ch * C + C - 1];
+    __syncthreads();
+    // U = U' - W S^T for rows 16w.., columns of this slice
+    const bf16* Wb = Ws0 + buf * C * PD;
+    const bf16* Khb = Kh0 + buf * C * PD;
+    f32x4 au = zero4();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pu[i] = p.Up[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj];
-  };
-  auto stash = [&](int buf) __attribute__((always_inline)) {
+    for (int k0 = 0; k0 < D; k0 += 32) au = mma(frag_rk(Wb, PD, 16 * w, k0), frag_rk(Ss, PD, 0, k0), au);
+    float u[4];
 #pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
-      *reinterpret_cast<u32x4*>(Ws0 + buf * C * PD + r * PD + c0) = pw[ps];
-      const float f = prk[ps] * fast_exp(pgC - pg[ps]);
-      bf16x8 kb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kb[e] = to_bf16(pk[ps][e] * f);
-      *reinterpret_cast<bf16x8*>(Kh0 + buf * C * PD + r * PD + c0) = kb;
+    for (int i = 0; i < 4; ++i) {
+      u[i] = up[i] - au[i];
+      p.U[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj] = f32_to_bf16_bits(u[i]);
     }
-    if (tid == 0) dec[buf] = fast_exp(pgC);
+    st_bf16x4(Ut + jj * PC + 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
+    if (k + 1 < nck) fwd_stash<D, TIO>(nx, Ws0 + (buf ^ 1) * C * PD, Kh0 + (buf ^ 1) * C * PD, dec + (buf ^ 1), up);
+    // unconditional (clamped to the last chunk): a branch here would make the
+    // compiler wait for the loaded registers at the join
+    fwd_load<D, TIO>(nx, p, se, h, v0, se.c0 + min(k + 3, nck - 1));
+    __syncthreads();
+    // S_{k+1}^T = S_k^T e^GamC + Khat^T U
+    const float d = dec[buf];
+#pragma unroll
+    for (int x = 0; x < NJW; ++x) {
+      const int jb = w * NJW + x;
+      f32x4 a = acc[x] * d;
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc(Khb, PD, 16 * jb, k0), frag_rk(Ut, PC, 0, k0), a);
+      acc[x] = a;
+    }
   };
 
-  const int nck = se.nchunks;
   if (nck > 0) {
-    float up[4];
-    load(se.c0);
-    stash(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) up[i] = bf16_bits_to_f32(pu[i]);
+    fwd_load<D, TIO>(A, p, se, h, v0, se.c0);
+    fwd_load<D, TIO>(Bp, p, se, h, v0, se.c0 + min(1, nck - 1));
+    fwd_stash<D, TIO>(A, Ws0, Kh0, dec, up);
+    fwd_load<D, TIO>(A, p, se, h, v0, se.c0 + min(2, nck - 1));
     __syncthreads();
-    for (int n = 0; n < nck; ++n) {
-      const int buf = n & 1;
-      const int c = se.c0 + n;
-      const int64_t ch = int64_t(h) * p.NC + c;
-      const bool has_next = n + 1 < nck;
-      if (has_next) load(c + 1);
-      // S_n: to LDS (operand of U) and to the workspace
-#pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        const int j = 16 * (w * NJW + x) + 4 * g;
-        st_bf16x4(Ss + jj * PD + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-        st_bf16x4(p.S + (ch * D + v0 + jj) * D + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-      }
-      __syncthreads();
-      // U = U' - W S^T for rows 16w.., columns of this slice
-      f32x4 au = zero4();
-      const bf16* Wb = Ws0 + buf * C * PD;
-      const bf16* Khb = Kh0 + buf * C * PD;
-#pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) au = mma(frag_rk(Wb, PD, 16 * w, k0), frag_rk(Ss, PD, 0, k0), au);
-      float u[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u[i] = up[i] - au[i];
-        p.U[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj] = f32_to_bf16_bits(u[i]);
-      }
-      st_bf16x4(Ut + jj * PC + 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
-      if (has_next) {
-        stash(buf ^ 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) up[i] = bf16_bits_to_f32(pu[i]);
-      }
-      __syncthreads();
-      // S_{n+1}^T = S_n^T e^GamC + Khat^T U
-      const float d = dec[buf];
-#pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        const int jb = w * NJW + x;
-        f32x4 a = acc[x] * d;
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc(Khb, PD, 16 * jb, k0), frag_rk(Ut, PC, 0, k0), a);
-        acc[x] = a;
-      }
+    for (int k = 0; k < nck; k += 2) {
+      step(k, 0, Bp);
+      if (k + 1 < nck) step(k + 1, 1, A);
     }
   }
   if (p.ht) {
@@ -367,13 +491,10 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
 template <int D, typename TIO>
 __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, int h, int sl) {
   using Dm = Dims<D>;
-  constexpr int PD = Dm::PD, TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS, NJW = Dm::NJW;
+  constexpr int PD = Dm::PD, NJW = Dm::NJW;
   constexpr int PO = ChainSmem<D, TIO>::PO;
   constexpr bool QLO = ChainSmem<D, TIO>::kQlo;
   // Double-buffered tiles: buffer b of X starts at X0 + b * (tile size).
-  // The Qbar^T dO term is formed as q^T (diag(f) dO), f_r = scale rho_r e^Gam_r:
-  // q is exact in bf16 and the small scaled dO slice is split into bf16 hi + lo,
-  // so this term (the dominant one in dh0) carries no bf16 rounding.
   bf16* const Kh0 = reinterpret_cast<bf16*>(smem);
   bf16* const Qb0 = Kh0 + 2 * C * PD;   // raw q (high part for fp32 inputs)
   bf16* const Ws0 = Qb0 + 2 * C * PD;
@@ -386,11 +507,13 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
   bf16* dUt = dSl + 16 * PD;     // -dU stored as [v][r]
   float* dec = reinterpret_cast<float*>(dUt + 16 * PC);
 
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  const int l = lane_id(), w = wave_id();
   const int g = l >> 4, jj = l & 15;
   const int H = p.H;
   const SeqEntry se = p.stab[si];
   const int v0 = 16 * sl;
+  const int nck = se.nchunks;
+  const float scale = p.scale;
 
   f32x4 acc[NJW];
 #pragma unroll
@@ -404,137 +527,73 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     }
   }
 
-  u32x4 pw[NPASS], pp[2];
-  float pk[NPASS][8], pq[NPASS][8], prk[NPASS], pg[NPASS], pgC, pdo[4], pfr;
-  auto load = [&](int c) __attribute__((always_inline)) {
-    const int64_t ch = int64_t(h) * p.NC + c;
-    const ChunkEntry ce = p.ctab[c];
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
-      pw[ps] = *reinterpret_cast<const u32x4*>(p.W + (ch * C + r) * D + c0);
-      if (r < ce.len) {
-        const int64_t o = tok(ce.t_start + r, H, h) * D + c0;
-        IO<TIO>::load8(p.k, o, pk[ps]);
-        IO<TIO>::load8(p.q, o, pq[ps]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pk[ps][e] = pq[ps][e] = 0.f;
-      }
-      prk[ps] = p.rho[ch * 2 * C + C + r];
-      pg[ps] = p.gam[ch * C + r];
-    }
-    pgC = p.gam[ch * C + C - 1];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int pc = tid + x * kThreads;   // 16-byte piece of the 64x64 P tile
-      pp[x] = *reinterpret_cast<const u32x4*>(p.P + (ch * C + pc / 8) * C + (pc % 8) * 8);
-    }
-    {
-      const int r = tid / 4, c0 = (tid % 4) * 4;
-      if (r < ce.len) {
-        IO<TIO>::load4(p.dO, tok(ce.t_start + r, H, h) * D + v0 + c0, pdo);
-        pfr = p.scale * p.rho[ch * 2 * C + r] * fast_exp(p.gam[ch * C + r]);
-      } else {
-        pdo[0] = pdo[1] = pdo[2] = pdo[3] = 0.f;
-        pfr = 0.f;
-      }
-    }
+  auto stash = [&](const BwdPrefetch<D, TIO>& f, int buf) __attribute__((always_inline)) {
+    bwd_stash<D, TIO, QLO>(f, scale, Kh0 + buf * C * PD, Qb0 + buf * C * PD, Ql0 + buf * C * PD,
+                           Ws0 + buf * C * PD, Ps0 + buf * C * PC, dO0 + buf * C * PO, dFh0 + buf * C * PO,
+                           dFl0 + buf * C * PO, dec + buf);
   };
-  auto stash = [&](int buf) __attribute__((always_inline)) {
+  // chunks are walked last to first: step k handles chunk c0 + nck - 1 - k
+  BwdPrefetch<D, TIO> A, Bp;
+  auto step = [&](int k, int buf, BwdPrefetch<D, TIO>& nx) __attribute__((always_inline)) {
+    const int c = se.c0 + nck - 1 - k;
+    const int64_t ch = int64_t(h) * p.NC + c;
+    // dS_{n+1}: to LDS (operand of dU) and to the workspace
 #pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
-      *reinterpret_cast<u32x4*>(Ws0 + buf * C * PD + r * PD + c0) = pw[ps];
-      const float fk = prk[ps] * fast_exp(pgC - pg[ps]);
-      bf16x8 kb, qb, ql;
+    for (int x = 0; x < NJW; ++x) {
+      const int j = 16 * (w * NJW + x) + 4 * g;
+      st_bf16x4(dSl + jj * PD + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+      st_bf16x4(p.dS + (ch * D + v0 + jj) * D + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+    }
+    __syncthreads();
+    const bf16* Khb = Kh0 + buf * C * PD;
+    const bf16* Qbb = Qb0 + buf * C * PD;
+    const bf16* Wb = Ws0 + buf * C * PD;
+    const bf16* Pb = Ps0 + buf * C * PC;
+    const bf16* dOb = dO0 + buf * C * PO;
+    const bf16* dFh = dFh0 + buf * C * PO;
+    const bf16* dFl = dFl0 + buf * C * PO;
+    const bf16* Qlb = Ql0 + buf * C * PD;
+    // dU = P^T dO + Khat dS^T for rows 16w.., columns of this slice
+    f32x4 ad = zero4();
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kb[e] = to_bf16(pk[ps][e] * fk);
-        qb[e] = to_bf16(pq[ps][e]);
-        if constexpr (QLO) ql[e] = to_bf16(pq[ps][e] - float(qb[e]));
+    for (int k0 = 0; k0 < C; k0 += 32) ad = mma(frag_kc(Pb, PC, 16 * w, k0), frag_kc(dOb, PO, 0, k0), ad);
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 32) ad = mma(frag_rk(Khb, PD, 16 * w, k0), frag_rk(dSl, PD, 0, k0), ad);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p.dU[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj] = f32_to_bf16_bits(ad[i]);
+    st_bf16x4(dUt + jj * PC + 16 * w + 4 * g, -ad[0], -ad[1], -ad[2], -ad[3]);
+    if (k + 1 < nck) stash(nx, buf ^ 1);
+    bwd_load<D, TIO>(nx, p, se, h, v0, se.c0 + max(nck - 4 - k, 0));  // chunk k+3, clamped
+    __syncthreads();
+    // dS_n^T = dS_{n+1}^T e^GamC + q^T (f dO) - W^T dU
+    const float d = dec[buf];
+#pragma unroll
+    for (int x = 0; x < NJW; ++x) {
+      const int jb = w * NJW + x;
+      f32x4 a = acc[x] * d;
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 32) {
+        const bf16x8 aq = frag_kc(Qbb, PD, 16 * jb, k0);
+        const bf16x8 bh = frag_kc(dFh, PO, 0, k0);
+        a = mma(aq, bh, a);
+        a = mma(aq, frag_kc(dFl, PO, 0, k0), a);
+        if constexpr (QLO) a = mma(frag_kc(Qlb, PD, 16 * jb, k0), bh, a);
+        a = mma(frag_kc(Wb, PD, 16 * jb, k0), frag_rk(dUt, PC, 0, k0), a);
       }
-      *reinterpret_cast<bf16x8*>(Kh0 + buf * C * PD + r * PD + c0) = kb;
-      *reinterpret_cast<bf16x8*>(Qb0 + buf * C * PD + r * PD + c0) = qb;
-      if constexpr (QLO) *reinterpret_cast<bf16x8*>(Ql0 + buf * C * PD + r * PD + c0) = ql;
+      acc[x] = a;
     }
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int pc = tid + x * kThreads;
-      *reinterpret_cast<u32x4*>(Ps0 + buf * C * PC + (pc / 8) * PC + (pc % 8) * 8) = pp[x];
-    }
-    {
-      const int r = tid / 4, c0 = (tid % 4) * 4;
-      st_bf16x4(dO0 + buf * C * PO + r * PO + c0, pdo[0], pdo[1], pdo[2], pdo[3]);
-      float fh[4], fl[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = pdo[e] * pfr;
-        fh[e] = float(to_bf16(x));
-        fl[e] = x - fh[e];
-      }
-      st_bf16x4(dFh0 + buf * C * PO + r * PO + c0, fh[0], fh[1], fh[2], fh[3]);
-      st_bf16x4(dFl0 + buf * C * PO + r * PO + c0, fl[0], fl[1], fl[2], fl[3]);
-    }
-    if (tid == 0) dec[buf] = fast_exp(pgC);
   };
 
-  const int nck = se.nchunks;
   if (nck > 0) {
-    load(se.c0 + nck - 1);
-    stash(0);
+    const int cl = se.c0 + nck - 1;
+    bwd_load<D, TIO>(A, p, se, h, v0, cl);
+    bwd_load<D, TIO>(Bp, p, se, h, v0, max(cl - 1, se.c0));
+    stash(A, 0);
+    bwd_load<D, TIO>(A, p, se, h, v0, max(cl - 2, se.c0));
     __syncthreads();
-    for (int it = 0; it < nck; ++it) {
-      const int n = nck - 1 - it;
-      const int buf = it & 1;
-      const int c = se.c0 + n;
-      const int64_t ch = int64_t(h) * p.NC + c;
-      const bool has_next = n > 0;
-      if (has_next) load(c - 1);
-      // dS_{n+1}: to LDS (operand of dU) and to the workspace
-#pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        const int j = 16 * (w * NJW + x) + 4 * g;
-        st_bf16x4(dSl + jj * PD + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-        st_bf16x4(p.dS + (ch * D + v0 + jj) * D + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-      }
-      __syncthreads();
-      // dU = P^T dO + Khat dS^T for rows 16w.., columns of this slice
-      const bf16* Khb = Kh0 + buf * C * PD;
-      const bf16* Qbb = Qb0 + buf * C * PD;
-      const bf16* Wb = Ws0 + buf * C * PD;
-      const bf16* Pb = Ps0 + buf * C * PC;
-      const bf16* dOb = dO0 + buf * C * PO;
-      const bf16* dFh = dFh0 + buf * C * PO;
-      const bf16* dFl = dFl0 + buf * C * PO;
-      const bf16* Qlb = Ql0 + buf * C * PD;
-      f32x4 ad = zero4();
-#pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 32) ad = mma(frag_kc(Pb, PC, 16 * w, k0), frag_kc(dOb, PO, 0, k0), ad);
-#pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) ad = mma(frag_rk(Khb, PD, 16 * w, k0), frag_rk(dSl, PD, 0, k0), ad);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p.dU[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj] = f32_to_bf16_bits(ad[i]);
-      st_bf16x4(dUt + jj * PC + 16 * w + 4 * g, -ad[0], -ad[1], -ad[2], -ad[3]);
-      if (has_next) stash(buf ^ 1);
-      __syncthreads();
-      // dS_n^T = dS_{n+1}^T e^GamC + Qbar^T dO - W^T dU
-      const float d = dec[buf];
-#pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        const int jb = w * NJW + x;
-        f32x4 a = acc[x] * d;
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) {
-          const bf16x8 aq = frag_kc(Qbb, PD, 16 * jb, k0);
-          const bf16x8 bh = frag_kc(dFh, PO, 0, k0);
-          a = mma(aq, bh, a);
-          a = mma(aq, frag_kc(dFl, PO, 0, k0), a);
-          if constexpr (QLO) a = mma(frag_kc(Qlb, PD, 16 * jb, k0), bh, a);
-          a = mma(frag_kc(Wb, PD, 16 * jb, k0), frag_rk(dUt, PC, 0, k0), a);
-        }
-        acc[x] = a;
-      }
+    for (int k = 0; k < nck; k += 2) {
+      step(k, 0, Bp);
+      if (k + 1 < nck) step(k + 1, 1, A);
     }
   }
   if (p.dh0) {
@@ -612,7 +671,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     gam_s[tid] = p.gam[ch * C + tid];
     rq_s[tid] = p.rho[ch * 2 * C + tid];
     rk_s[tid] = p.rho[ch * 2 * C + C + tid];
-    beta_s[tid] = tid < len ? sigmoidf(IO<TIO>::load1(p.b, tok(t0 + tid, H, h))) : 0.f;
+    beta_s[tid] = (tid < len ? 1.f : 0.f) * sigmoidf(IO<TIO>::load1(p.b, tok(t0 + min(tid, len - 1), H, h)));
 #pragma unroll
     for (int x = 0; x < 4; ++x) colsum_s[x][tid] = 0.f;
   }
@@ -622,15 +681,11 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     *reinterpret_cast<uint4*>(dUs + r * PD + c0) = *reinterpret_cast<const uint4*>(p.dU + (ch * C + r) * D + c0);
     *reinterpret_cast<uint4*>(Us + r * PD + c0) = *reinterpret_cast<const uint4*>(p.U + (ch * C + r) * D + c0);
     float x[8];
-    if (r < len) {
-      IO<TIO>::load8(p.dO, tok(t0 + r, H, h) * D + c0, x);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    }
+    IO<TIO>::load8(p.dO, tok(t0 + min(r, len - 1), H, h) * D + c0, x);
+    const float m = r < len ? 1.f : 0.f;
     bf16x8 xb;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xb[e] = to_bf16(x[e]);
+    for (int e = 0; e < 8; ++e) xb[e] = to_bf16(x[e] * m);
     *reinterpret_cast<bf16x8*>(dOs + r * PD + c0) = xb;
   }
 #pragma unroll
@@ -652,13 +707,12 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc(dUs, PD, 16 * vb, k0), frag_kc(As, PC, 16 * w, k0), a);
     const int v = 16 * vb + 4 * g;
     st_bf16x4(dYs + r * PD + v, a[0], a[1], a[2], a[3]);
-    if (r < len) {
-      const int64_t o = tok(t0 + r, H, h) * D + v;
-      IO<TIO>::store4(p.dv, o, br * a[0], br * a[1], br * a[2], br * a[3]);
-      float vv[4];
-      IO<TIO>::load4(p.v, o, vv);
-      dbeta_row += a[0] * vv[0] + a[1] * vv[1] + a[2] * vv[2] + a[3] * vv[3];
-    }
+    // rows past the end: dY is exactly zero there, so the clamped v row adds nothing
+    const int64_t o = tok(t0 + min(r, len - 1), H, h) * D + v;
+    float vv[4];
+    IO<TIO>::load4(p.v, o, vv);
+    dbeta_row += a[0] * vv[0] + a[1] * vv[1] + a[2] * vv[2] + a[3] * vv[3];
+    if (r < len) IO<TIO>::store4(p.dv, o, br * a[0], br * a[1], br * a[2], br * a[3]);
   }
   __syncthreads();
   // ---- load S (RS) and dS (RdS), both [v][j] ----
@@ -705,19 +759,16 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   for (int ps = 0; ps < NPASS; ++ps) {
     const int rr = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     float qv[8], kv[8];
-    if (rr < len) {
-      const int64_t o = tok(t0 + rr, H, h) * D + c0;
-      IO<TIO>::load8(p.q, o, qv);
-      IO<TIO>::load8(p.k, o, kv);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[e] = kv[e] = 0.f;
-    }
+    const int64_t o = tok(t0 + min(rr, len - 1), H, h) * D + c0;
+    IO<TIO>::load8(p.q, o, qv);
+    IO<TIO>::load8(p.k, o, kv);
+    const float m = rr < len ? 1.f : 0.f;
+    const float fq = m * rq_s[rr], fk = m * rk_s[rr];
     bf16x8 qb, kb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      qb[e] = to_bf16(qv[e] * rq_s[rr]);
-      kb[e] = to_bf16(kv[e] * rk_s[rr]);
+      qb[e] = to_bf16(qv[e] * fq);
+      kb[e] = to_bf16(kv[e] * fk);
     }
     *reinterpret_cast<bf16x8*>(Qn + rr * PD + c0) = qb;
     *reinterpret_cast<bf16x8*>(Kn + rr * PD + c0) = kb;
@@ -850,19 +901,17 @@ __global__ __launch_bounds__(kThreads) void k_finish_gdn(const Params p) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     const bool ok = r < len;
     float q[8], k[8], dq[8], dk[8];
-    const int64_t o = tok(t0 + (ok ? r : 0), H, h) * D + c0;
-    const float rq = p.rho[ch * 2 * C + r], rk = p.rho[ch * 2 * C + C + r];
-    if (ok) {
-      IO<TIO>::load8(p.q, o, q);
-      IO<TIO>::load8(p.k, o, k);
+    const int64_t o = tok(t0 + min(r, len - 1), H, h) * D + c0;
+    const float m = ok ? 1.f : 0.f;
+    const float rq = m * p.rho[ch * 2 * C + r], rk = m * p.rho[ch * 2 * C + C + r];
+    IO<TIO>::load8(p.q, o, q);
+    IO<TIO>::load8(p.k, o, k);
+    {
       const float4* a = reinterpret_cast<const float4*>(p.dqn + (ch * C + r) * D + c0);
       const float4* b = reinterpret_cast<const float4*>(p.dkn + (ch * C + r) * D + c0);
       const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
       dq[0] = a0.x; dq[1] = a0.y; dq[2] = a0.z; dq[3] = a0.w; dq[4] = a1.x; dq[5] = a1.y; dq[6] = a1.z; dq[7] = a1.w;
       dk[0] = b0.x; dk[1] = b0.y; dk[2] = b0.z; dk[3] = b0.w; dk[4] = b1.x; dk[5] = b1.y; dk[6] = b1.z; dk[7] = b1.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = k[e] = dq[e] = dk[e] = 0.f;
     }
     float pq = 0.f, pk = 0.f;
 #pragma unroll
@@ -893,11 +942,12 @@ __global__ __launch_bounds__(kThreads) void k_finish_gdn(const Params p) {
       const float y = __shfl_down(x, m, 64);
       if (l + m < 64) x += y;
     }
+    const int64_t o = tok(t0 + min(l, len - 1), H, h);
+    const float bt = sigmoidf(IO<TIO>::load1(p.b, o));
+    const float dgc = p.dgamc[ch], dbs = p.dbeta[ch * C + l];
     if (l < len) {
-      const int64_t o = tok(t0 + l, H, h);
-      IO<TIO>::store1(p.dg, o, x + p.dgamc[ch]);
-      const float bt = sigmoidf(IO<TIO>::load1(p.b, o));
-      IO<TIO>::store1(p.db, o, p.dbeta[ch * C + l] * bt * (1.f - bt));
+      IO<TIO>::store1(p.dg, o, x + dgc);
+      IO<TIO>::store1(p.db, o, dbs * bt * (1.f - bt));
     }
   }
 }
