@@ -30,6 +30,23 @@ from chunked_gated_delta_bwd_amd import binding as B  # noqa: E402
 from chunked_gated_delta_bwd_amd import synth  # noqa: E402
 
 METRIC = "gated-delta-rule bwd tokens/s + ms/bwd at T=32k,H=16,D=128 bf16; MFMA %"
+KERNEL_SOURCE = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc", "gdr_kernels.hip")
+# HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by a
+# 1 GiB copy; profiles/gdn_t32768_h16_d128.md), valid only for the kernel
+# source they were taken on: (workload, stage, sha256 prefix) -> bytes.
+MEASURED_TRAFFIC = {
+    ("gdn_bf16_t32768_h16_d128", "prep", "1ebc4b235775"): 0.845e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "1ebc4b235775"): 1.822e9,
+    ("gdn_bf16_t32768_h16_d128", "grads", "1ebc4b235775"): 2.132e9,
+    ("gdn_bf16_t32768_h16_d128", "finish", "1ebc4b235775"): 1.136e9,
+}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:12]
 C = 64
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -122,6 +139,10 @@ def main() -> int:
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--stage-iters", type=int, default=10)
+    ap.add_argument("--all-stages", action="store_true",
+                    help="also time the forward and reverse recursions alone (two more chain launches)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device copy, the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU path is not built",
@@ -131,6 +152,15 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     B.load_library()
+    if args.copy_calibration:
+        # a plain copy of exactly 1 GiB (read 1 GiB, write 1 GiB): its FETCH_SIZE /
+        # WRITE_SIZE counters give the scale for the kernels' counter readings
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     spec = synth.workload(args.workload)
     inp = synth.generate(spec)
@@ -152,7 +182,11 @@ def main() -> int:
 
     # every kernel alone (the workspace already holds what earlier stages leave)
     kernels = {}
-    for stage, name in B.STAGE_NAMES.items():
+    stages = [B.GDR_STAGE_PREP, B.GDR_STAGE_CHAIN_BOTH, B.GDR_STAGE_GRADS, B.GDR_STAGE_FINISH]
+    if args.all_stages:
+        stages += [B.GDR_STAGE_CHAIN_FWD, B.GDR_STAGE_CHAIN_BWD]
+    for stage in stages:
+        name = B.STAGE_NAMES[stage]
         fn = lambda s=stage: B.gdr_run_stage(prob, dev, dev["dO"], dev["dht"], ws, out, s, ht=ht)  # noqa: E731
         fn()
         t = time_it(fn, args.stage_iters)
@@ -173,6 +207,7 @@ def main() -> int:
         achieved = flops / (kernels[dom]["ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof["traffic"] = MEASURED_TRAFFIC.get((args.workload, dom, kernel_source_hash()))
     roof["kernel"] = dom
     roof["work_per_launch"] = flops if dom != "finish" else nbytes
 
