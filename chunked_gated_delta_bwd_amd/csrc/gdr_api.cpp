@@ -87,6 +87,10 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.dgam = take(H * NC * C * gk * 4);
   L.dgamc = take(H * NC * gk * 4);
   L.dbeta = take(H * NC * C * 4);
+  const size_t kda = s->gate == GDR_GATE_CHANNEL ? 1 : 0;
+  L.Kh = take(kda * H * NC * C * K * 2);
+  L.Qh = take(kda * H * NC * C * K * 2);
+  L.Ql = take(kda * H * NC * C * K * 2);
   L.total = off;
   return L;
 }
@@ -192,6 +196,9 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   p.dgam = reinterpret_cast<float*>(w + L.dgam);
   p.dgamc = reinterpret_cast<float*>(w + L.dgamc);
   p.dbeta = reinterpret_cast<float*>(w + L.dbeta);
+  p.Kh = reinterpret_cast<uint16_t*>(w + L.Kh);
+  p.Qh = reinterpret_cast<uint16_t*>(w + L.Qh);
+  p.Ql = reinterpret_cast<uint16_t*>(w + L.Ql);
   return p;
 }
 
@@ -221,7 +228,7 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
   if ((st = check_ws(L, ws, ws_bytes)) != GDR_OK) return st;
 
   if (s->gate == GDR_GATE_CHANNEL)
-    return fail(GDR_EUNSUPPORTED, "per-channel gate kernels are not available in this build");
+    return fail(GDR_EUNSUPPORTED, "the per-channel gate is not implemented yet");
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if ((st = upload_tables(s, L, ws, hs)) != GDR_OK) return st;
   gdr::Params p = make_params(s, L, in, ws);

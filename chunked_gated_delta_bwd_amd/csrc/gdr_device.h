@@ -185,6 +185,29 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// ---- tile geometry shared by the kernels ----
+constexpr int C = 64;       // tokens per chunk
+constexpr int PC = C + 8;   // LDS pitch of 64-wide bf16 tiles (elements)
+
+template <int D>
+struct Dims {
+  static constexpr int PD = D + 8;             // LDS pitch of D-wide bf16 tiles
+  static constexpr int TPR = D / 8;            // threads per row in row sweeps (8 elements each)
+  static constexpr int RPP = 256 / TPR;        // rows per pass for 256 threads
+  static constexpr int NPASS = C / RPP;        // passes over the 64 rows
+  static constexpr int NJB = D / 16;           // 16-wide blocks along D
+  static constexpr int NJW = NJB / 4;          // D-blocks per compute wave in the chain kernels
+};
+
+__device__ __forceinline__ int64_t tok(int t, int H, int h) { return int64_t(t) * H + h; }
+
+__device__ __forceinline__ void st_bf16x4(bf16* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(dst) = pack4_bf16(a, b, c, d);
+}
+__device__ __forceinline__ void st_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(dst) = pack4_bf16(a, b, c, d);
+}
+
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
 // softplus(x) = max(x, 0) + log1p(exp(-|x|)), stable for every x

@@ -51,6 +51,10 @@ struct WsLayout {
   size_t dgam = 0;   // fp32 [H][NC][64] or [H][NC][64][K]
   size_t dgamc = 0;  // fp32 [H][NC] or [H][NC][K]
   size_t dbeta = 0;  // fp32 [H][NC][64]: gradient w.r.t. beta (sigmoid space)
+  // per-channel gate only: the recursions' operand tiles formed by the prologue
+  size_t Kh = 0;     // bf16 [H][NC][64][K]: Khat = kn e^(GamC - Gam)
+  size_t Qh = 0;     // bf16 [H][NC][64][K]: Qbar = scale qn e^Gam, high part
+  size_t Ql = 0;     // bf16 [H][NC][64][K]: Qbar low part
   size_t total = 0;
 };
 
@@ -70,6 +74,7 @@ struct Params {
   float* gam;
   float* rho;
   uint16_t *A, *P, *W, *Up, *U, *S, *dS, *dU;   // bf16 bit patterns
+  uint16_t *Kh, *Qh, *Ql;                        // per-channel gate only
   float *dqn, *dkn, *dgam, *dgamc, *dbeta;
 };
 

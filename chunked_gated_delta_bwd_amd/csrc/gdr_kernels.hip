@@ -30,27 +30,8 @@
 
 namespace gdr {
 
-constexpr int C = kChunk;
-constexpr int PC = C + 8;   // LDS pitch of 64-wide bf16 tiles (elements)
-
-template <int D>
-struct Dims {
-  static constexpr int PD = D + 8;             // LDS pitch of D-wide bf16 tiles
-  static constexpr int TPR = D / 8;            // threads per row in row sweeps (8 elements each)
-  static constexpr int RPP = kThreads / TPR;   // rows per pass
-  static constexpr int NPASS = C / RPP;        // passes over the 64 rows
-  static constexpr int NJB = D / 16;           // 16-wide blocks along D
-  static constexpr int NJW = NJB / 4;          // D-blocks per wave in the chain kernels
-};
-
-__device__ __forceinline__ int64_t tok(int t, int H, int h) { return int64_t(t) * H + h; }
-
-__device__ __forceinline__ void st_bf16x4(bf16* dst, float a, float b, float c, float d) {
-  *reinterpret_cast<uint2*>(dst) = pack4_bf16(a, b, c, d);
-}
-__device__ __forceinline__ void st_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
-  *reinterpret_cast<uint2*>(dst) = pack4_bf16(a, b, c, d);
-}
+static_assert(C == kChunk, "chunk size");
+static_assert(Dims<128>::RPP * Dims<128>::TPR == kThreads, "row sweep covers the workgroup");
 
 // ===========================================================================
 // k_prep (scalar gate)
@@ -220,416 +201,6 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
       st_bf16x4(p.Up + (ch * C + r) * D + j0, aU[0], aU[1], aU[2], aU[3]);
     }
   }
-}
-
-// ===========================================================================
-// k_chain: serial recursions over the chunks of one (sequence, head, V slice)
-// ===========================================================================
-template <int D, typename TIO>
-struct ChainSmem {
-  using Dm = Dims<D>;
-  static constexpr int PD = Dm::PD, PO = 24;
-  static constexpr size_t tile = size_t(C) * PD * 2;
-  // fp32 inputs are not exact in bf16: q also gets a low-order tile (where it fits)
-  static constexpr bool kQlo = std::is_same<TIO, float>::value && D == 64;
-  static constexpr size_t fwd = 4 * tile + 16 * PD * 2 + 16 * PC * 2 + 2 * 4;
-  static constexpr size_t bwd = (kQlo ? 8 : 6) * tile + 2 * C * PC * 2 + 3 * 2 * C * PO * 2 + 16 * PD * 2 +
-                                16 * PC * 2 + 2 * 4;
-  static constexpr size_t bytes = fwd > bwd ? fwd : bwd;
-};
-
-// Each recursion keeps two register sets of prefetched chunk data (raw, not
-// unpacked): the set stashed into LDS at step k was loaded at step k-2, so every
-// load has two full steps to arrive while vmcnt waits only for the older set.
-template <int D, typename TIO>
-struct FwdPrefetch {
-  using Dm = Dims<D>;
-  u32x4 w[Dm::NPASS];
-  typename IO<TIO>::Raw8 k[Dm::NPASS];
-  float rk[Dm::NPASS], g[Dm::NPASS], m[Dm::NPASS], gC;
-  uint16_t u[4];
-};
-
-template <int D, typename TIO>
-struct BwdPrefetch {
-  using Dm = Dims<D>;
-  u32x4 w[Dm::NPASS], pm[2];
-  typename IO<TIO>::Raw8 k[Dm::NPASS], q[Dm::NPASS];
-  typename IO<TIO>::Raw4 dO;
-  float rk[Dm::NPASS], g[Dm::NPASS], m[Dm::NPASS], gC, rq_do, g_do, m_do;
-};
-
-// Loads of one chunk into registers: unconditional (rows past the sequence end
-// read its last row and are masked at the stash) and with no arithmetic on the
-// loaded values, so nothing waits for them before the stash.
-template <int D, typename TIO>
-__device__ __forceinline__ void fwd_load(FwdPrefetch<D, TIO>& f, const Params& p, const SeqEntry& se, int h,
-                                         int v0, int c) {
-  using Dm = Dims<D>;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int64_t ch = int64_t(h) * p.NC + c;
-  const int ct0 = se.t_start + (c - se.c0) * C;
-  const int clen = min(C, se.len - (c - se.c0) * C);
-#pragma unroll
-  for (int ps = 0; ps < Dm::NPASS; ++ps) {
-    const int r = ps * Dm::RPP + tid / Dm::TPR, c0 = (tid % Dm::TPR) * 8;
-    f.w[ps] = *reinterpret_cast<const u32x4*>(p.W + (ch * C + r) * D + c0);
-    f.k[ps] = IO<TIO>::load_raw8(p.k, tok(ct0 + min(r, clen - 1), p.H, h) * D + c0);
-    f.m[ps] = r < clen ? 1.f : 0.f;
-    f.rk[ps] = p.rho[ch * 2 * C + C + r];
-    f.g[ps] = p.gam[ch * C + r];
-  }
-  f.gC = p.gam[ch * C + C - 1];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.u[i] = p.Up[(ch * C + 16 * w + 4 * (l >> 4) + i) * D + v0 + (l & 15)];
-}
-
-// Khat = kn e^(GamC - Gam) and W into LDS buffer `buf`; U' into registers.
-template <int D, typename TIO>
-__device__ __forceinline__ void fwd_stash(const FwdPrefetch<D, TIO>& f, bf16* Ws, bf16* Kh, float* dec,
-                                          float (&up)[4]) {
-  using Dm = Dims<D>;
-  constexpr int PD = Dm::PD;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int ps = 0; ps < Dm::NPASS; ++ps) {
-    const int r = ps * Dm::RPP + tid / Dm::TPR, c0 = (tid % Dm::TPR) * 8;
-    *reinterpret_cast<u32x4*>(Ws + r * PD + c0) = f.w[ps];
-    const float s = f.m[ps] * f.rk[ps] * fast_exp(f.gC - f.g[ps]);
-    float kx[8];
-    IO<TIO>::unpack8(f.k[ps], kx);
-    bf16x8 kb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kb[e] = to_bf16(kx[e] * s);
-    *reinterpret_cast<bf16x8*>(Kh + r * PD + c0) = kb;
-  }
-  if (tid == 0) *dec = fast_exp(f.gC);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) up[i] = bf16_bits_to_f32(f.u[i]);
-}
-
-template <int D, typename TIO>
-__device__ __forceinline__ void bwd_load(BwdPrefetch<D, TIO>& f, const Params& p, const SeqEntry& se, int h,
-                                         int v0, int c) {
-  using Dm = Dims<D>;
-  const int tid = threadIdx.x;
-  const int64_t ch = int64_t(h) * p.NC + c;
-  const int ct0 = se.t_start + (c - se.c0) * C;
-  const int clen = min(C, se.len - (c - se.c0) * C);
-#pragma unroll
-  for (int ps = 0; ps < Dm::NPASS; ++ps) {
-    const int r = ps * Dm::RPP + tid / Dm::TPR, c0 = (tid % Dm::TPR) * 8;
-    f.w[ps] = *reinterpret_cast<const u32x4*>(p.W + (ch * C + r) * D + c0);
-    const int64_t o = tok(ct0 + min(r, clen - 1), p.H, h) * D + c0;
-    f.k[ps] = IO<TIO>::load_raw8(p.k, o);
-    f.q[ps] = IO<TIO>::load_raw8(p.q, o);
-    f.m[ps] = r < clen ? 1.f : 0.f;
-    f.rk[ps] = p.rho[ch * 2 * C + C + r];
-    f.g[ps] = p.gam[ch * C + r];
-  }
-  f.gC = p.gam[ch * C + C - 1];
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int pc = tid + x * kThreads;   // 16-byte piece of the 64x64 P tile
-    f.pm[x] = *reinterpret_cast<const u32x4*>(p.P + (ch * C + pc / 8) * C + (pc % 8) * 8);
-  }
-  const int r = tid / 4, c0 = (tid % 4) * 4;
-  f.dO = IO<TIO>::load_raw4(p.dO, tok(ct0 + min(r, clen - 1), p.H, h) * D + v0 + c0);
-  f.m_do = r < clen ? 1.f : 0.f;
-  f.rq_do = p.rho[ch * 2 * C + r];
-  f.g_do = p.gam[ch * C + r];
-}
-
-// Khat, raw q (exact in bf16; high/low parts for fp32 inputs), W, P, the raw dO
-// slice and the scaled slice f*dO (f_r = scale rho_r e^Gam_r) split into bf16
-// high + low parts.  The Qbar^T dO term is then q^T (f dO) with no rounding of
-// Qbar: it dominates dh0.
-template <int D, typename TIO, bool QLO>
-__device__ __forceinline__ void bwd_stash(const BwdPrefetch<D, TIO>& f, float scale, bf16* Kh, bf16* Qb, bf16* Ql,
-                                          bf16* Ws, bf16* Ps, bf16* dOr, bf16* dFh, bf16* dFl, float* dec) {
-  using Dm = Dims<D>;
-  constexpr int PD = Dm::PD, PO = 24;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int ps = 0; ps < Dm::NPASS; ++ps) {
-    const int r = ps * Dm::RPP + tid / Dm::TPR, c0 = (tid % Dm::TPR) * 8;
-    *reinterpret_cast<u32x4*>(Ws + r * PD + c0) = f.w[ps];
-    const float fk = f.m[ps] * f.rk[ps] * fast_exp(f.gC - f.g[ps]);
-    float kx[8], qx[8];
-    IO<TIO>::unpack8(f.k[ps], kx);
-    IO<TIO>::unpack8(f.q[ps], qx);
-    bf16x8 kb, qb, ql;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float qv = qx[e] * f.m[ps];
-      kb[e] = to_bf16(kx[e] * fk);
-      qb[e] = to_bf16(qv);
-      if constexpr (QLO) ql[e] = to_bf16(qv - float(qb[e]));
-    }
-    *reinterpret_cast<bf16x8*>(Kh + r * PD + c0) = kb;
-    *reinterpret_cast<bf16x8*>(Qb + r * PD + c0) = qb;
-    if constexpr (QLO) *reinterpret_cast<bf16x8*>(Ql + r * PD + c0) = ql;
-  }
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int pc = tid + x * kThreads;
-    *reinterpret_cast<u32x4*>(Ps + (pc / 8) * PC + (pc % 8) * 8) = f.pm[x];
-  }
-  const int r = tid / 4, c0 = (tid % 4) * 4;
-  const float fs = f.m_do * scale * f.rq_do * fast_exp(f.g_do);
-  float dx[4], fh[4], fl[4];
-  IO<TIO>::unpack4(f.dO, dx);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float x = dx[e] * fs;
-    fh[e] = float(to_bf16(x));
-    fl[e] = x - fh[e];
-    dx[e] *= f.m_do;
-  }
-  st_bf16x4(dOr + r * PO + c0, dx[0], dx[1], dx[2], dx[3]);
-  st_bf16x4(dFh + r * PO + c0, fh[0], fh[1], fh[2], fh[3]);
-  st_bf16x4(dFl + r * PO + c0, fl[0], fl[1], fl[2], fl[3]);
-  if (tid == 0) *dec = fast_exp(f.gC);
-}
-
-template <int D, typename TIO>
-__device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, int h, int sl) {
-  using Dm = Dims<D>;
-  constexpr int PD = Dm::PD, NJW = Dm::NJW;
-  // double-buffered tiles: buffer b of X starts at X0 + b * C * PD
-  bf16* const Ws0 = reinterpret_cast<bf16*>(smem);
-  bf16* const Kh0 = Ws0 + 2 * C * PD;
-  bf16* Ss = Kh0 + 2 * C * PD;   // S[v][j], 16 rows
-  bf16* Ut = Ss + 16 * PD;       // U[r][v] stored as Ut[v][r]
-  float* dec = reinterpret_cast<float*>(Ut + 16 * PC);
-
-  const int l = lane_id(), w = wave_id();
-  const int g = l >> 4, jj = l & 15;
-  const int H = p.H;
-  const SeqEntry se = p.stab[si];
-  const int v0 = 16 * sl;
-  const int nck = se.nchunks;
-
-  f32x4 acc[NJW];
-#pragma unroll
-  for (int x = 0; x < NJW; ++x) {
-    const int j = 16 * (w * NJW + x) + 4 * g;
-    if (p.h0) {
-      const float4 t = *reinterpret_cast<const float4*>(p.h0 + ((int64_t(se.seq) * H + h) * D + v0 + jj) * D + j);
-      acc[x] = f32x4{t.x, t.y, t.z, t.w};
-    } else {
-      acc[x] = zero4();
-    }
-  }
-
-  FwdPrefetch<D, TIO> A, Bp;
-  float up[4];
-  // one chunk k (0-based in this sequence) on LDS buffer `buf`; `nx` holds chunk
-  // k+1 (stashed into the other buffer here) and is refilled with chunk k+3
-  auto step = [&](int k, int buf, FwdPrefetch<D, TIO>& nx) __attribute__((always_inline)) {
-    const int c = se.c0 + k;
-    const int64_t ch = int64_t(h) * p.NC + c;
-    // S_k: to LDS (operand of U) and to the workspace
-#pragma unroll
-    for (int x = 0; x < NJW; ++x) {
-      const int j = 16 * (w * NJW + x) + 4 * g;
-      st_bf16x4(Ss + jj * PD + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-      st_bf16x4(p.S + (ch * D + v0 + jj) * D + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-    }
-    __syncthreads();
-    // U = U' - W S^T for rows 16w.., columns of this slice
-    const bf16* Wb = Ws0 + buf * C * PD;
-    const bf16* Khb = Kh0 + buf * C * PD;
-    f32x4 au = zero4();
-#pragma unroll
-    for (int k0 = 0; k0 < D; k0 += 32) au = mma(frag_rk(Wb, PD, 16 * w, k0), frag_rk(Ss, PD, 0, k0), au);
-    float u[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u[i] = up[i] - au[i];
-      p.U[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj] = f32_to_bf16_bits(u[i]);
-    }
-    st_bf16x4(Ut + jj * PC + 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
-    if (k + 1 < nck) fwd_stash<D, TIO>(nx, Ws0 + (buf ^ 1) * C * PD, Kh0 + (buf ^ 1) * C * PD, dec + (buf ^ 1), up);
-    // unconditional (clamped to the last chunk): a branch here would make the
-    // compiler wait for the loaded registers at the join
-    fwd_load<D, TIO>(nx, p, se, h, v0, se.c0 + min(k + 3, nck - 1));
-    __syncthreads();
-    // S_{k+1}^T = S_k^T e^GamC + Khat^T U
-    const float d = dec[buf];
-#pragma unroll
-    for (int x = 0; x < NJW; ++x) {
-      const int jb = w * NJW + x;
-      f32x4 a = acc[x] * d;
-#pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc(Khb, PD, 16 * jb, k0), frag_rk(Ut, PC, 0, k0), a);
-      acc[x] = a;
-    }
-  };
-
-  if (nck > 0) {
-    fwd_load<D, TIO>(A, p, se, h, v0, se.c0);
-    fwd_load<D, TIO>(Bp, p, se, h, v0, se.c0 + min(1, nck - 1));
-    fwd_stash<D, TIO>(A, Ws0, Kh0, dec, up);
-    fwd_load<D, TIO>(A, p, se, h, v0, se.c0 + min(2, nck - 1));
-    __syncthreads();
-    for (int k = 0; k < nck; k += 2) {
-      step(k, 0, Bp);
-      if (k + 1 < nck) step(k + 1, 1, A);
-    }
-  }
-  if (p.ht) {
-#pragma unroll
-    for (int x = 0; x < NJW; ++x) {
-      const int j = 16 * (w * NJW + x) + 4 * g;
-      *reinterpret_cast<float4*>(p.ht + ((int64_t(se.seq) * H + h) * D + v0 + jj) * D + j) =
-          make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-    }
-  }
-}
-
-template <int D, typename TIO>
-__device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, int h, int sl) {
-  using Dm = Dims<D>;
-  constexpr int PD = Dm::PD, NJW = Dm::NJW;
-  constexpr int PO = ChainSmem<D, TIO>::PO;
-  constexpr bool QLO = ChainSmem<D, TIO>::kQlo;
-  // Double-buffered tiles: buffer b of X starts at X0 + b * (tile size).
-  bf16* const Kh0 = reinterpret_cast<bf16*>(smem);
-  bf16* const Qb0 = Kh0 + 2 * C * PD;   // raw q (high part for fp32 inputs)
-  bf16* const Ws0 = Qb0 + 2 * C * PD;
-  bf16* const Ql0 = Ws0 + 2 * C * PD;   // low part of q (fp32 inputs only)
-  bf16* const Ps0 = Ql0 + (QLO ? 2 * C * PD : 0);
-  bf16* const dO0 = Ps0 + 2 * C * PC;   // raw dO slice
-  bf16* const dFh0 = dO0 + 2 * C * PO;  // f * dO, high part
-  bf16* const dFl0 = dFh0 + 2 * C * PO; // f * dO, low part
-  bf16* dSl = dFl0 + 2 * C * PO;  // dS[v][j], 16 rows
-  bf16* dUt = dSl + 16 * PD;     // -dU stored as [v][r]
-  float* dec = reinterpret_cast<float*>(dUt + 16 * PC);
-
-  const int l = lane_id(), w = wave_id();
-  const int g = l >> 4, jj = l & 15;
-  const int H = p.H;
-  const SeqEntry se = p.stab[si];
-  const int v0 = 16 * sl;
-  const int nck = se.nchunks;
-  const float scale = p.scale;
-
-  f32x4 acc[NJW];
-#pragma unroll
-  for (int x = 0; x < NJW; ++x) {
-    const int j = 16 * (w * NJW + x) + 4 * g;
-    if (p.dht) {
-      const float4 t = *reinterpret_cast<const float4*>(p.dht + ((int64_t(se.seq) * H + h) * D + v0 + jj) * D + j);
-      acc[x] = f32x4{t.x, t.y, t.z, t.w};
-    } else {
-      acc[x] = zero4();
-    }
-  }
-
-  auto stash = [&](const BwdPrefetch<D, TIO>& f, int buf) __attribute__((always_inline)) {
-    bwd_stash<D, TIO, QLO>(f, scale, Kh0 + buf * C * PD, Qb0 + buf * C * PD, Ql0 + buf * C * PD,
-                           Ws0 + buf * C * PD, Ps0 + buf * C * PC, dO0 + buf * C * PO, dFh0 + buf * C * PO,
-                           dFl0 + buf * C * PO, dec + buf);
-  };
-  // chunks are walked last to first: step k handles chunk c0 + nck - 1 - k
-  BwdPrefetch<D, TIO> A, Bp;
-  auto step = [&](int k, int buf, BwdPrefetch<D, TIO>& nx) __attribute__((always_inline)) {
-    const int c = se.c0 + nck - 1 - k;
-    const int64_t ch = int64_t(h) * p.NC + c;
-    // dS_{n+1}: to LDS (operand of dU) and to the workspace
-#pragma unroll
-    for (int x = 0; x < NJW; ++x) {
-      const int j = 16 * (w * NJW + x) + 4 * g;
-      st_bf16x4(dSl + jj * PD + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-      st_bf16x4(p.dS + (ch * D + v0 + jj) * D + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-    }
-    __syncthreads();
-    const bf16* Khb = Kh0 + buf * C * PD;
-    const bf16* Qbb = Qb0 + buf * C * PD;
-    const bf16* Wb = Ws0 + buf * C * PD;
-    const bf16* Pb = Ps0 + buf * C * PC;
-    const bf16* dOb = dO0 + buf * C * PO;
-    const bf16* dFh = dFh0 + buf * C * PO;
-    const bf16* dFl = dFl0 + buf * C * PO;
-    const bf16* Qlb = Ql0 + buf * C * PD;
-    // dU = P^T dO + Khat dS^T for rows 16w.., columns of this slice
-    f32x4 ad = zero4();
-#pragma unroll
-    for (int k0 = 0; k0 < C; k0 += 32) ad = mma(frag_kc(Pb, PC, 16 * w, k0), frag_kc(dOb, PO, 0, k0), ad);
-#pragma unroll
-    for (int k0 = 0; k0 < D; k0 += 32) ad = mma(frag_rk(Khb, PD, 16 * w, k0), frag_rk(dSl, PD, 0, k0), ad);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p.dU[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj] = f32_to_bf16_bits(ad[i]);
-    st_bf16x4(dUt + jj * PC + 16 * w + 4 * g, -ad[0], -ad[1], -ad[2], -ad[3]);
-    if (k + 1 < nck) stash(nx, buf ^ 1);
-    bwd_load<D, TIO>(nx, p, se, h, v0, se.c0 + max(nck - 4 - k, 0));  // chunk k+3, clamped
-    __syncthreads();
-    // dS_n^T = dS_{n+1}^T e^GamC + q^T (f dO) - W^T dU
-    const float d = dec[buf];
-#pragma unroll
-    for (int x = 0; x < NJW; ++x) {
-      const int jb = w * NJW + x;
-      f32x4 a = acc[x] * d;
-#pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 32) {
-        const bf16x8 aq = frag_kc(Qbb, PD, 16 * jb, k0);
-        const bf16x8 bh = frag_kc(dFh, PO, 0, k0);
-        a = mma(aq, bh, a);
-        a = mma(aq, frag_kc(dFl, PO, 0, k0), a);
-        if constexpr (QLO) a = mma(frag_kc(Qlb, PD, 16 * jb, k0), bh, a);
-        a = mma(frag_kc(Wb, PD, 16 * jb, k0), frag_rk(dUt, PC, 0, k0), a);
-      }
-      acc[x] = a;
-    }
-  };
-
-  if (nck > 0) {
-    const int cl = se.c0 + nck - 1;
-    bwd_load<D, TIO>(A, p, se, h, v0, cl);
-    bwd_load<D, TIO>(Bp, p, se, h, v0, max(cl - 1, se.c0));
-    stash(A, 0);
-    bwd_load<D, TIO>(A, p, se, h, v0, max(cl - 2, se.c0));
-    __syncthreads();
-    for (int k = 0; k < nck; k += 2) {
-      step(k, 0, Bp);
-      if (k + 1 < nck) step(k + 1, 1, A);
-    }
-  }
-  if (p.dh0) {
-#pragma unroll
-    for (int x = 0; x < NJW; ++x) {
-      const int j = 16 * (w * NJW + x) + 4 * g;
-      *reinterpret_cast<float4*>(p.dh0 + ((int64_t(se.seq) * H + h) * D + v0 + jj) * D + j) =
-          make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-    }
-  }
-}
-
-// blockIdx -> (work group of one (sequence, head), V slice): the slices of one
-// (sequence, head) share its chunk tiles, so they are placed on the same XCD
-// (workgroups are dealt round-robin over the 8 XCDs).
-template <int D, typename TIO>
-__global__ __launch_bounds__(kThreads) void k_chain(const Params p, int mode, int nb_role) {
-  __shared__ __attribute__((aligned(16))) char smem[ChainSmem<D, TIO>::bytes];
-  int b = blockIdx.x;
-  int role;
-  if (mode == kChainBoth) {
-    role = b < nb_role ? 0 : 1;
-    if (role) b -= nb_role;
-  } else {
-    role = mode == kChainFwd ? 0 : 1;
-  }
-  constexpr int ns = D / 16;
-  const int xcd = b % 8, y = b / 8;
-  const int sl = y % ns;
-  const int gidx = (y / ns) * 8 + xcd;
-  if (gidx >= p.N * p.H) return;
-  const int si = gidx / p.H, h = gidx % p.H;
-  if (role == 0)
-    chain_fwd<D, TIO>(p, smem, si, h, sl);
-  else
-    chain_bwd<D, TIO>(p, smem, si, h, sl);
 }
 
 // ===========================================================================
@@ -995,27 +566,11 @@ struct RunFinish {
   }
 };
 
-int g_chain_mode = 0;
-template <int D, typename TIO>
-struct RunChain {
-  static void run(const Params& p, hipStream_t s) {
-    constexpr int ns = D / 16;
-    const int groups = p.N * p.H;
-    const int nb = ((groups + 7) / 8) * 8 * ns;
-    const int nroles = g_chain_mode == kChainBoth ? 2 : 1;
-    k_chain<D, TIO><<<dim3(nb * nroles), kThreads, 0, s>>>(p, g_chain_mode, nb);
-  }
-};
-
 }  // namespace
 
 int launch_prep(const Params& p, void* stream) { return dispatch<RunPrep>(p, stream); }
 int launch_grads(const Params& p, void* stream) { return dispatch<RunGrads>(p, stream); }
 int launch_finish(const Params& p, void* stream) { return dispatch<RunFinish>(p, stream); }
-int launch_chain(const Params& p, int mode, void* stream) {
-  g_chain_mode = mode;
-  return dispatch<RunChain>(p, stream);
-}
 int launch_zero_params(const Params& p, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
