@@ -74,6 +74,8 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.stab = take(N * sizeof(gdr::SeqEntry));
   L.gam = take(H * NC * C * gk * 4);
   L.rho = take(H * NC * 2 * C * 4);
+  L.fac = take(H * NC * 2 * C * 4);
+  L.edec = take(H * NC * gk * 4);
   L.A = take(H * NC * C * C * 2);
   L.P = take(H * NC * C * C * 2);
   L.W = take(H * NC * C * K * 2);
@@ -87,10 +89,10 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.dgam = take(H * NC * C * gk * 4);
   L.dgamc = take(H * NC * gk * 4);
   L.dbeta = take(H * NC * C * 4);
-  const size_t kda = s->gate == GDR_GATE_CHANNEL ? 1 : 0;
-  L.Kh = take(kda * H * NC * C * K * 2);
-  L.Qh = take(kda * H * NC * C * K * 2);
-  L.Ql = take(kda * H * NC * C * K * 2);
+  const size_t mat = (s->gate == GDR_GATE_CHANNEL || s->dtype == GDR_F32) ? 1 : 0;
+  L.Kh = take(mat * H * NC * C * K * 2);
+  L.Qh = take(mat * H * NC * C * K * 2);
+  L.Ql = take(mat * H * NC * C * K * 2);
   L.total = off;
   return L;
 }
@@ -183,6 +185,8 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   p.stab = reinterpret_cast<const gdr::SeqEntry*>(w + L.stab);
   p.gam = reinterpret_cast<float*>(w + L.gam);
   p.rho = reinterpret_cast<float*>(w + L.rho);
+  p.fac = reinterpret_cast<float*>(w + L.fac);
+  p.edec = reinterpret_cast<float*>(w + L.edec);
   p.A = reinterpret_cast<uint16_t*>(w + L.A);
   p.P = reinterpret_cast<uint16_t*>(w + L.P);
   p.W = reinterpret_cast<uint16_t*>(w + L.W);

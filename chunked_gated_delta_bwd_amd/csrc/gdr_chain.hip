@@ -11,21 +11,29 @@
 // runs both in one grid.  The fp32 state / state gradient of a slice lives in
 // registers for the whole sequence.
 //
-// Workgroups are 512 threads: waves 0-3 compute, waves 4-7 load and stage the
-// chunk tiles ("producers"), so the compute waves never wait on global loads.
-// Every chunk step has two barriers, B1 and B2.  A tile is written in the window
-// where no compute wave reads it, so the large tiles need one LDS buffer each:
-//   reverse: Khat, P (read in the first window) are staged after B2 of the
-//            previous step; Qbar (hi + lo) and W (read after B2) are staged
-//            between B1 and B2 of their own step; dO is double-buffered.
-//   forward: W and U' (first window) after B2 of the previous step; Khat and
-//            the decay (second window) between B1 and B2.
-// Producers keep two register sets of raw prefetched chunk data (chunk k in set
-// k % 2) and issue every load unconditionally (clamped to the last chunk), so the
-// compiler never has to wait for a load before its data is staged.
+// Workgroups have nine waves with fixed jobs:
+//   waves 0-3  compute: the MFMA products of one chunk step, two barriers a step;
+//   wave  4    converter: loads the small per-chunk data into registers one step
+//              ahead (the dO slice, row factors, the chunk decay) and writes it
+//              to LDS in the form the MFMAs take (bf16, high + low parts);
+//   waves 5-8  movers: copy the chunk tiles global -> LDS with direct-to-LDS
+//              loads (no registers, no ALU), two chunks ahead.
+// Every big tile has two LDS buffers (chunk k in buffer k % 2).  A tile read
+// in the first window of a step (between its barriers B1 and B2) is refilled
+// after B2, a tile read in the second window after the next B1, so each load
+// has one and a half steps to land; the movers wait for their own loads with
+// vmcnt before the barrier that publishes them.
 //
-// Qbar^T dO carries the dominant part of dh0, so Qbar is split into bf16 high and
-// low parts (two MFMAs); for fp32 inputs dO is split too.
+// Tiles are stored unpadded with an XOR swizzle of their 16-byte pieces (one
+// direct-to-LDS load writes 1 KB contiguously, so the swizzle is applied by
+// choosing which global piece each lane fetches).
+//
+// The scalar gate with bf16 inputs reads the raw q and k rows and applies the
+// row factors of Qbar = q (scale e^Gam / |q|) and Khat = k (e^(GamC - Gam) / |k|)
+// to the small operands instead (dO rows, U rows, dU rows); the per-channel
+// gate and fp32 inputs take the Khat / Qbar tiles the prologue kernel formed.
+// Qbar^T dO carries the dominant part of dh0, so that product is taken in two
+// bf16 parts (Qbar high + low, or the scaled dO high + low).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -35,59 +43,131 @@
 
 namespace gdr {
 
-constexpr int kChainThreads = 512;
-constexpr int kChainCompute = 256;   // threads of the compute waves (0-3)
+constexpr int kChainWaves = 9;
+constexpr int kChainThreads = 64 * kChainWaves;
+constexpr int kConvWave = 4;
+constexpr int kMoveWave0 = 5;
 
-template <int D>
-struct ChainLayout {
-  static constexpr int PD = D + 8, PO = 24;
-  // reverse role, bf16 element offsets
-  static constexpr int bKh = 0;
-  static constexpr int bP = bKh + C * PD;
-  static constexpr int bQh = bP + C * PC;
-  static constexpr int bQl = bQh + C * PD;
-  static constexpr int bW = bQl + C * PD;
-  static constexpr int bdOh = bW + C * PD;     // two buffers
-  static constexpr int bdOl = bdOh + 2 * C * PO;  // two buffers
-  static constexpr int bdS = bdOl + 2 * C * PO;
-  static constexpr int bdU = bdS + 16 * PD;
-  static constexpr int bEnd = bdU + 16 * PC;   // then 2 x D fp32 decay values
-  static constexpr size_t bBytes = size_t(bEnd) * 2 + 2 * D * 4;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// ---------------------------------------------------------------------------
+// swizzled LDS tiles
+// ---------------------------------------------------------------------------
+// Piece p (16 bytes) of row r of a W-column bf16 tile sits at piece p ^ swz<W>(r):
+// 16 consecutive rows at one piece (row fragments) and 4 consecutive rows at two
+// adjacent pieces (transposed reads) land on distinct banks.
+template <int W>
+__device__ __forceinline__ int swz(int r);
+template <>
+__device__ __forceinline__ int swz<128>(int r) {
+  return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1);
+}
+template <>
+__device__ __forceinline__ int swz<64>(int r) {
+  return 4 * ((r >> 1) & 1) + 2 * ((r & 1) ^ ((r >> 3) & 1)) + ((r >> 2) & 1);
+}
+template <>
+__device__ __forceinline__ int swz<16>(int) {
+  return 0;
+}
+
+// byte offset of element (r, c) of a swizzled W-column bf16 tile
+template <int W>
+__device__ __forceinline__ int soff(int r, int c) {
+  return r * (2 * W) + (((c >> 3) ^ swz<W>(r)) << 4) + ((c & 7) << 1);
+}
+
+// T[r0 + j][k0 + 8g .. 8g+7] (see frag_rk)
+template <int W>
+__device__ __forceinline__ bf16x8 frag_rk_s(const char* T, int r0, int k0) {
+  const int l = lane_id();
+  return *reinterpret_cast<const bf16x8*>(T + soff<W>(r0 + (l & 15), k0 + 8 * (l >> 4)));
+}
+
+// T[k0 + 8g .. 8g+7][c0 + j] by transposed reads (see frag_kc)
+template <int W>
+__device__ __forceinline__ bf16x8 frag_kc_s(const char* T, int c0, int k0) {
+  const int l = lane_id();
+  const int g = l >> 4, q = l & 15;
+  const int r = k0 + 8 * g + (q >> 2), c = c0 + 4 * (q & 3);
+  const char* p0 = T + soff<W>(r, c);
+  const char* p1 = T + soff<W>(r + 4, c);
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(p0)));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(p1)));
+  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+  const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+  return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int W>
+__device__ __forceinline__ void st4_s(char* T, int r, int c, float a, float b, float d, float e) {
+  *reinterpret_cast<uint2*>(T + soff<W>(r, c)) = pack4_bf16(a, b, d, e);
+}
+
+// one 16-byte direct-to-LDS load per lane: lane l's bytes land at lds + 16 l
+__device__ __forceinline__ void dma16(const void* src, char* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)((lds_char_t*)lds), 16, 0, 0);
+}
+
+// Workgroup barrier that orders LDS traffic only: each wave's LDS reads and
+// writes complete first (lgkmcnt), while its global stores and loads stay in
+// flight (a __syncthreads fence would drain them every chunk step; the movers
+// wait for exactly the loads a barrier publishes).  The signal fences keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void chain_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt vmcnt(N), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// ---------------------------------------------------------------------------
+// LDS plan
+// ---------------------------------------------------------------------------
+template <int D, typename TIO, int GATE>
+struct ChainCfg {
+  static constexpr bool MAT = GATE == 1 || std::is_same<TIO, float>::value;  // materialised Khat / Qbar
+  static constexpr bool RAW = !MAT;
+  static constexpr bool LO = std::is_same<TIO, float>::value;                // dO needs a low part
+  static constexpr int DG = GATE == 1 ? D : 4;     // decay floats per chunk (scalar padded)
+  static constexpr int TB = C * D * 2;             // one 64 x D bf16 tile
+  static constexpr int PB = C * C * 2;             // the 64 x 64 P tile
+  static constexpr int XB = C * 16 * 2;            // a 64 x 16 slice
+  static constexpr int NJ = TB / 4096;             // 1 KB loads per mover wave per 64 x D tile
+  // reverse role, byte offsets; the tile buffers first
+  static constexpr int bK = 0, bQh = TB, bQl = 2 * TB, bW = (MAT ? 3 : 2) * TB, bP = bW + TB;
+  static constexpr int bufB = bP + PB;
+  static constexpr bool kX2 = RAW || LO, kX3 = RAW;
+  static constexpr int bX1 = 2 * bufB;                       // dO, bf16 (high part)
+  static constexpr int bX2 = bX1 + 2 * XB;                   // RAW: fq dO high; LO: dO low
+  static constexpr int bX3 = bX2 + (kX2 ? 2 * XB : 0);       // RAW: fq dO low
+  static constexpr int bFk = bX3 + (kX3 ? 2 * XB : 0);       // RAW: fk per row
+  static constexpr int bDec = bFk + (RAW ? 2 * C * 4 : 0);
+  static constexpr int bdS = bDec + 2 * DG * 4;              // 16 x D state-gradient slice
+  static constexpr int bdU = bdS + 16 * D * 2;               // 16 x 64: -dU^T
+  static constexpr int bEnd = bdU + 16 * C * 2;
   // forward role
-  static constexpr int fW = 0;
-  static constexpr int fKh = fW + C * PD;
-  static constexpr int fUq = fKh + C * PD;     // U' slice as [v][r]
-  static constexpr int fS = fUq + 16 * PC;
-  static constexpr int fU = fS + 16 * PD;
-  static constexpr int fEnd = fU + 16 * PC;    // then D fp32 decay values
-  static constexpr size_t fBytes = size_t(fEnd) * 2 + D * 4;
-  static constexpr size_t bytes = bBytes > fBytes ? bBytes : fBytes;
-};
-
-// ---------------------------------------------------------------------------
-// producer register sets
-// ---------------------------------------------------------------------------
-template <int D, typename TIO, int GATE>
-struct FwdSet {
-  using Dm = Dims<D>;
-  u32x4 w[Dm::NPASS];
-  typename IO<TIO>::Raw8 k[Dm::NPASS];   // scalar gate: raw k (Khat formed at the stash)
-  u32x4 kh[Dm::NPASS];                   // per-channel gate: Khat tile from the prologue kernel
-  float rk[Dm::NPASS], g[Dm::NPASS], m[Dm::NPASS], gC;
-  f32x4 gCv[2];                          // per-channel gate: GamC of this thread's 8 columns
-  uint2 up;                              // U' slice: 4 values of one row
-};
-
-template <int D, typename TIO, int GATE>
-struct BwdSet {
-  using Dm = Dims<D>;
-  u32x4 w[Dm::NPASS], pm[2];
-  typename IO<TIO>::Raw8 k[Dm::NPASS], q[Dm::NPASS];   // scalar gate
-  u32x4 kh[Dm::NPASS], qh[Dm::NPASS], ql[Dm::NPASS];   // per-channel gate
-  float rk[Dm::NPASS], rq[Dm::NPASS], g[Dm::NPASS], m[Dm::NPASS], gC;
-  f32x4 gCv[2];
-  typename IO<TIO>::Raw4 dO;
-  float m_do;
+  static constexpr int fW = 0, fK = TB, fUp = 2 * TB, bufF = fUp + XB;
+  static constexpr int fFk = 2 * bufF;
+  static constexpr int fDec = fFk + (RAW ? 2 * C * 4 : 0);
+  static constexpr int fS = fDec + 2 * DG * 4;               // 16 x D state slice
+  static constexpr int fU = fS + 16 * D * 2;                 // 16 x 64: U^T (row-scaled for RAW)
+  static constexpr int fEnd = fU + 16 * C * 2;
+  static constexpr int bytes = bEnd > fEnd ? bEnd : fEnd;
+  // mover loads per wave per chunk, first-window set A and second-window set B
+  static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 : 2) * NJ;
+  static constexpr int fwdA = NJ + 1, fwdB = NJ;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert(bwdA + bwdB < 64 && fwdA + fwdB < 64, "vmcnt range");
 };
 
 struct ChunkGeo {
@@ -103,198 +183,226 @@ __device__ __forceinline__ ChunkGeo geo(const Params& p, const SeqEntry& se, int
   return r;
 }
 
-// ---- forward role ----
+// ---------------------------------------------------------------------------
+// movers (waves 5-8): mover wave mw fills bytes [mw T/4, (mw+1) T/4) of a tile T
+// ---------------------------------------------------------------------------
+template <int D>
+struct MoverLane {
+  int rD[4], pD[4], tD[4];   // 64 x D tile, load j: row, swizzled piece byte offset, in-tile offset
+  int tP[2];                 // P tile, load j: in-tile offset
+  int up;                    // 64 x 16 slice of a 64 x D tile (lanes 0-31): row * 2D + piece * 16
+  __device__ __forceinline__ void init(int mw, int l) {
+    constexpr int RB = 2 * D, TB = C * RB, NJ = TB / 4096;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pos = mw * (TB / 4) + (j < NJ ? j : 0) * 1024 + 16 * l;
+      const int row = pos / RB, lp = ((pos % RB) >> 4) ^ swz<D>(row);
+      rD[j] = row;
+      pD[j] = lp << 4;
+      tD[j] = row * RB + (lp << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pos = mw * 2048 + j * 1024 + 16 * l;
+      const int row = pos >> 7, lp = ((pos & 127) >> 4) ^ swz<64>(row);
+      tP[j] = row * 128 + (lp << 4);
+    }
+    const int pos = mw * 512 + 16 * (l & 31);
+    up = (pos >> 5) * RB + (((pos & 31) >> 4) << 4);
+  }
+};
+
+// a 64 x D tile stored contiguously at `src` (workspace layout [64][D])
+template <int D>
+__device__ __forceinline__ void move_tile(const MoverLane<D>& ml, const void* src, char* dst, int mw) {
+  constexpr int TB = C * D * 2, NJ = TB / 4096;
+  const char* s = static_cast<const char*>(src);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) dma16(s + ml.tD[j], dst + mw * (TB / 4) + j * 1024);
+}
+
+// a 64 x D tile of raw token rows (q or k of head h), rows past the end clamped
+template <int D>
+__device__ __forceinline__ void move_rows(const MoverLane<D>& ml, const void* base, const Params& p, const ChunkGeo& cg,
+                                          int h, char* dst, int mw) {
+  constexpr int TB = C * D * 2, NJ = TB / 4096;
+  const char* s = static_cast<const char*>(base) + int64_t(h) * D * 2;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t t = cg.t0 + min(ml.rD[j], cg.len - 1);
+    dma16(s + t * (int64_t(p.H) * D * 2) + ml.pD[j], dst + mw * (TB / 4) + j * 1024);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void move_p(const MoverLane<D>& ml, const void* src, char* dst, int mw) {
+  const char* s = static_cast<const char*>(src);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) dma16(s + ml.tP[j], dst + mw * 2048 + j * 1024);
+}
+
+// reverse role: set A (Khat or k, P), set B (Qbar high [+ low] or q, W)
 template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void fwd_load(FwdSet<D, TIO, GATE>& f, const Params& p, const SeqEntry& se, int h,
-                                         int v0, int c, int pt) {
-  using Dm = Dims<D>;
+__device__ __forceinline__ void move_bwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
+                                           char* buf, int mw) {
+  using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
-#pragma unroll
-  for (int ps = 0; ps < Dm::NPASS; ++ps) {
-    const int r = ps * Dm::RPP + pt / Dm::TPR, c0 = (pt % Dm::TPR) * 8;
-    f.w[ps] = *reinterpret_cast<const u32x4*>(p.W + (cg.ch * C + r) * D + c0);
-    if constexpr (GATE == 0) {
-      f.k[ps] = IO<TIO>::load_raw8(p.k, tok(cg.t0 + min(r, cg.len - 1), p.H, h) * D + c0);
-      f.m[ps] = r < cg.len ? 1.f : 0.f;
-      f.rk[ps] = p.rho[cg.ch * 2 * C + C + r];
-      f.g[ps] = p.gam[cg.ch * C + r];
-    } else {
-      f.kh[ps] = *reinterpret_cast<const u32x4*>(p.Kh + (cg.ch * C + r) * D + c0);
-    }
-  }
-  const int c0 = (pt % Dm::TPR) * 8;
-  if constexpr (GATE == 0) {
-    f.gC = p.gam[cg.ch * C + C - 1];
-  } else {
-    const f32x4* gc = reinterpret_cast<const f32x4*>(p.gam + (cg.ch * C + C - 1) * D + c0);
-    f.gCv[0] = gc[0];
-    f.gCv[1] = gc[1];
-  }
-  const int r = pt / 4, cc = (pt % 4) * 4;
-  f.up = *reinterpret_cast<const uint2*>(p.Up + (cg.ch * C + r) * D + v0 + cc);
+  if constexpr (Cf::RAW)
+    move_rows<D>(ml, p.k, p, cg, h, buf + Cf::bK, mw);
+  else
+    move_tile<D>(ml, p.Kh + cg.ch * C * D, buf + Cf::bK, mw);
+  move_p<D>(ml, p.P + cg.ch * C * C, buf + Cf::bP, mw);
 }
 
-// window before B1 (after B2 of the previous step): W and U' of the chunk
 template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void fwd_stash_w(const FwdSet<D, TIO, GATE>& f, bf16* L, int pt) {
-  using Dm = Dims<D>;
-  using Ly = ChainLayout<D>;
-  constexpr int PD = Dm::PD;
-#pragma unroll
-  for (int ps = 0; ps < Dm::NPASS; ++ps) {
-    const int r = ps * Dm::RPP + pt / Dm::TPR, c0 = (pt % Dm::TPR) * 8;
-    *reinterpret_cast<u32x4*>(L + Ly::fW + r * PD + c0) = f.w[ps];
-  }
-  const int r = pt / 4, cc = (pt % 4) * 4;
-  uint16_t* uq = reinterpret_cast<uint16_t*>(L + Ly::fUq);
-  uq[(cc + 0) * PC + r] = uint16_t(f.up.x & 0xffffu);
-  uq[(cc + 1) * PC + r] = uint16_t(f.up.x >> 16);
-  uq[(cc + 2) * PC + r] = uint16_t(f.up.y & 0xffffu);
-  uq[(cc + 3) * PC + r] = uint16_t(f.up.y >> 16);
-}
-
-// window between B1 and B2: Khat and the per-column decay of the chunk
-template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void fwd_stash_k(const FwdSet<D, TIO, GATE>& f, bf16* L, float* dec, int pt) {
-  using Dm = Dims<D>;
-  using Ly = ChainLayout<D>;
-  constexpr int PD = Dm::PD;
-#pragma unroll
-  for (int ps = 0; ps < Dm::NPASS; ++ps) {
-    const int r = ps * Dm::RPP + pt / Dm::TPR, c0 = (pt % Dm::TPR) * 8;
-    if constexpr (GATE == 0) {
-      const float s = f.m[ps] * f.rk[ps] * fast_exp(f.gC - f.g[ps]);
-      float kx[8];
-      IO<TIO>::unpack8(f.k[ps], kx);
-      bf16x8 kb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kb[e] = to_bf16(kx[e] * s);
-      *reinterpret_cast<bf16x8*>(L + Ly::fKh + r * PD + c0) = kb;
-    } else {
-      *reinterpret_cast<u32x4*>(L + Ly::fKh + r * PD + c0) = f.kh[ps];
-    }
-  }
-  if (pt < Dm::TPR) {
-    const int c0 = pt * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dec[c0 + e] = fast_exp(GATE == 0 ? f.gC : f.gCv[e / 4][e % 4]);
-  }
-}
-
-// ---- reverse role ----
-template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void bwd_load(BwdSet<D, TIO, GATE>& f, const Params& p, const SeqEntry& se, int h,
-                                         int v0, int c, int pt) {
-  using Dm = Dims<D>;
+__device__ __forceinline__ void move_bwd_b(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
+                                           char* buf, int mw) {
+  using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
-#pragma unroll
-  for (int ps = 0; ps < Dm::NPASS; ++ps) {
-    const int r = ps * Dm::RPP + pt / Dm::TPR, c0 = (pt % Dm::TPR) * 8;
-    f.w[ps] = *reinterpret_cast<const u32x4*>(p.W + (cg.ch * C + r) * D + c0);
-    if constexpr (GATE == 0) {
-      const int64_t o = tok(cg.t0 + min(r, cg.len - 1), p.H, h) * D + c0;
-      f.k[ps] = IO<TIO>::load_raw8(p.k, o);
-      f.q[ps] = IO<TIO>::load_raw8(p.q, o);
-      f.m[ps] = r < cg.len ? 1.f : 0.f;
-      f.rk[ps] = p.rho[cg.ch * 2 * C + C + r];
-      f.rq[ps] = p.rho[cg.ch * 2 * C + r];
-      f.g[ps] = p.gam[cg.ch * C + r];
-    } else {
-      const int64_t o = (cg.ch * C + r) * D + c0;
-      f.kh[ps] = *reinterpret_cast<const u32x4*>(p.Kh + o);
-      f.qh[ps] = *reinterpret_cast<const u32x4*>(p.Qh + o);
-      f.ql[ps] = *reinterpret_cast<const u32x4*>(p.Ql + o);
-    }
-  }
-  const int c0 = (pt % Dm::TPR) * 8;
-  if constexpr (GATE == 0) {
-    f.gC = p.gam[cg.ch * C + C - 1];
+  if constexpr (Cf::RAW) {
+    move_rows<D>(ml, p.q, p, cg, h, buf + Cf::bQh, mw);
   } else {
-    const f32x4* gc = reinterpret_cast<const f32x4*>(p.gam + (cg.ch * C + C - 1) * D + c0);
-    f.gCv[0] = gc[0];
-    f.gCv[1] = gc[1];
+    move_tile<D>(ml, p.Qh + cg.ch * C * D, buf + Cf::bQh, mw);
+    move_tile<D>(ml, p.Ql + cg.ch * C * D, buf + Cf::bQl, mw);
   }
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int pc = pt + x * 256;   // 16-byte piece of the 64x64 P tile
-    f.pm[x] = *reinterpret_cast<const u32x4*>(p.P + (cg.ch * C + pc / 8) * C + (pc % 8) * 8);
-  }
-  const int r = pt / 4, cc = (pt % 4) * 4;
-  f.dO = IO<TIO>::load_raw4(p.dO, tok(cg.t0 + min(r, cg.len - 1), p.H, h) * D + v0 + cc);
-  f.m_do = r < cg.len ? 1.f : 0.f;
+  move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::bW, mw);
 }
 
-// window between B1 and B2: Qbar (hi + lo) and W of the chunk
+// forward role: set A (W, the U' slice), set B (Khat or k)
 template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void bwd_stash_q(const BwdSet<D, TIO, GATE>& f, bf16* L, float scale, int pt) {
-  using Dm = Dims<D>;
-  using Ly = ChainLayout<D>;
-  constexpr int PD = Dm::PD;
+__device__ __forceinline__ void move_fwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
+                                           int v0, char* buf, int mw) {
+  using Cf = ChainCfg<D, TIO, GATE>;
+  const ChunkGeo cg = geo(p, se, h, c);
+  move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::fW, mw);
+  if (lane_id() < 32) dma16(reinterpret_cast<const char*>(p.Up + cg.ch * C * D + v0) + ml.up, buf + Cf::fUp + mw * 512);
+}
+
+template <int D, typename TIO, int GATE>
+__device__ __forceinline__ void move_fwd_b(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
+                                           char* buf, int mw) {
+  using Cf = ChainCfg<D, TIO, GATE>;
+  const ChunkGeo cg = geo(p, se, h, c);
+  if constexpr (Cf::RAW)
+    move_rows<D>(ml, p.k, p, cg, h, buf + Cf::fK, mw);
+  else
+    move_tile<D>(ml, p.Kh + cg.ch * C * D, buf + Cf::fK, mw);
+}
+
+// ---------------------------------------------------------------------------
+// converter (wave 4): lane l owns row l of the chunk
+// ---------------------------------------------------------------------------
+template <int D, typename TIO, int GATE>
+struct ConvRegs {
+  static constexpr int ND = GATE == 1 ? D / 64 : 1;
+  typename IO<TIO>::Raw8 d0, d1;   // 16 dO values of row l (reverse role)
+  float m, fq, fk;
+  float dec[ND];
+
+  __device__ __forceinline__ void load(const Params& p, const SeqEntry& se, int h, int c, int v0, bool with_dO) {
+    using Cf = ChainCfg<D, TIO, GATE>;
+    const int l = lane_id();
+    const ChunkGeo cg = geo(p, se, h, c);
+    if (with_dO) {
+      const int64_t o = tok(cg.t0 + min(l, cg.len - 1), p.H, h) * D + v0;
+      d0 = IO<TIO>::load_raw8(p.dO, o);
+      d1 = IO<TIO>::load_raw8(p.dO, o + 8);
+    }
+    m = l < cg.len ? 1.f : 0.f;
+    if constexpr (Cf::RAW) {
+      fq = p.fac[cg.ch * 2 * C + l];
+      fk = p.fac[cg.ch * 2 * C + C + l];
+    }
+    if constexpr (GATE == 1) {
 #pragma unroll
-  for (int ps = 0; ps < Dm::NPASS; ++ps) {
-    const int r = ps * Dm::RPP + pt / Dm::TPR, c0 = (pt % Dm::TPR) * 8;
-    *reinterpret_cast<u32x4*>(L + Ly::bW + r * PD + c0) = f.w[ps];
-    if constexpr (GATE == 0) {
-      const float s = f.m[ps] * scale * f.rq[ps] * fast_exp(f.g[ps]);
-      float qx[8];
-      IO<TIO>::unpack8(f.q[ps], qx);
-      bf16x8 qh, ql;
+      for (int i = 0; i < ND; ++i) dec[i] = p.edec[cg.ch * D + ND * l + i];
+    } else {
+      dec[0] = p.edec[cg.ch];
+    }
+  }
+
+  // reverse role: dO (high [, low]) or for RAW dO and fq dO (high, low), fk, decay
+  __device__ __forceinline__ void store_bwd(char* smem, int buf) const {
+    using Cf = ChainCfg<D, TIO, GATE>;
+    const int l = lane_id();
+    float x[16];
+    {
+      float a[8], b[8];
+      IO<TIO>::unpack8(d0, a);
+      IO<TIO>::unpack8(d1, b);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = qx[e] * s;
-        qh[e] = to_bf16(x);
-        ql[e] = to_bf16(x - float(qh[e]));
+        x[e] = m * a[e];
+        x[8 + e] = m * b[e];
       }
-      *reinterpret_cast<bf16x8*>(L + Ly::bQh + r * PD + c0) = qh;
-      *reinterpret_cast<bf16x8*>(L + Ly::bQl + r * PD + c0) = ql;
-    } else {
-      *reinterpret_cast<u32x4*>(L + Ly::bQh + r * PD + c0) = f.qh[ps];
-      *reinterpret_cast<u32x4*>(L + Ly::bQl + r * PD + c0) = f.ql[ps];
     }
+    bf16x8 h0, h1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h0[e] = to_bf16(x[e]);
+      h1[e] = to_bf16(x[8 + e]);
+    }
+    char* r1 = smem + Cf::bX1 + buf * Cf::XB + l * 32;
+    *reinterpret_cast<bf16x8*>(r1) = h0;
+    *reinterpret_cast<bf16x8*>(r1 + 16) = h1;
+    if constexpr (Cf::RAW) {
+      bf16x8 a0, a1, b0, b1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y0 = fq * x[e], y1 = fq * x[8 + e];
+        a0[e] = to_bf16(y0);
+        a1[e] = to_bf16(y1);
+        b0[e] = to_bf16(y0 - float(a0[e]));
+        b1[e] = to_bf16(y1 - float(a1[e]));
+      }
+      char* r2 = smem + Cf::bX2 + buf * Cf::XB + l * 32;
+      char* r3 = smem + Cf::bX3 + buf * Cf::XB + l * 32;
+      *reinterpret_cast<bf16x8*>(r2) = a0;
+      *reinterpret_cast<bf16x8*>(r2 + 16) = a1;
+      *reinterpret_cast<bf16x8*>(r3) = b0;
+      *reinterpret_cast<bf16x8*>(r3 + 16) = b1;
+      reinterpret_cast<float*>(smem + Cf::bFk)[buf * C + l] = fk;
+    } else if constexpr (Cf::LO) {
+      bf16x8 b0, b1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        b0[e] = to_bf16(x[e] - float(h0[e]));
+        b1[e] = to_bf16(x[8 + e] - float(h1[e]));
+      }
+      char* r2 = smem + Cf::bX2 + buf * Cf::XB + l * 32;
+      *reinterpret_cast<bf16x8*>(r2) = b0;
+      *reinterpret_cast<bf16x8*>(r2 + 16) = b1;
+    }
+    store_dec(reinterpret_cast<float*>(smem + Cf::bDec) + buf * Cf::DG);
   }
-}
 
-// window after B2: Khat, P, dO (buffer `buf`) and the decay (buffer `buf`) of the chunk
-template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void bwd_stash_k(const BwdSet<D, TIO, GATE>& f, bf16* L, float* dec, int buf, int pt) {
-  using Dm = Dims<D>;
-  using Ly = ChainLayout<D>;
-  constexpr int PD = Dm::PD, PO = Ly::PO;
+  // forward role: fk and the decay
+  __device__ __forceinline__ void store_fwd(char* smem, int buf) const {
+    using Cf = ChainCfg<D, TIO, GATE>;
+    if constexpr (Cf::RAW) reinterpret_cast<float*>(smem + Cf::fFk)[buf * C + lane_id()] = fk;
+    store_dec(reinterpret_cast<float*>(smem + Cf::fDec) + buf * Cf::DG);
+  }
+
+  __device__ __forceinline__ void store_dec(float* dst) const {
+    const int l = lane_id();
+    if constexpr (GATE == 1) {
 #pragma unroll
-  for (int ps = 0; ps < Dm::NPASS; ++ps) {
-    const int r = ps * Dm::RPP + pt / Dm::TPR, c0 = (pt % Dm::TPR) * 8;
-    if constexpr (GATE == 0) {
-      const float s = f.m[ps] * f.rk[ps] * fast_exp(f.gC - f.g[ps]);
-      float kx[8];
-      IO<TIO>::unpack8(f.k[ps], kx);
-      bf16x8 kb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kb[e] = to_bf16(kx[e] * s);
-      *reinterpret_cast<bf16x8*>(L + Ly::bKh + r * PD + c0) = kb;
+      for (int i = 0; i < ND; ++i) dst[ND * l + i] = dec[i];
     } else {
-      *reinterpret_cast<u32x4*>(L + Ly::bKh + r * PD + c0) = f.kh[ps];
+      if (l == 0) dst[0] = dec[0];
     }
   }
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int pc = pt + x * 256;
-    *reinterpret_cast<u32x4*>(L + Ly::bP + (pc / 8) * PC + (pc % 8) * 8) = f.pm[x];
-  }
-  const int r = pt / 4, cc = (pt % 4) * 4;
-  float dx[4], hi[4], lo[4];
-  IO<TIO>::unpack4(f.dO, dx);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    dx[e] *= f.m_do;
-    hi[e] = float(to_bf16(dx[e]));
-    lo[e] = dx[e] - hi[e];   // zero for bf16 inputs
-  }
-  st_bf16x4(L + Ly::bdOh + buf * C * PO + r * PO + cc, hi[0], hi[1], hi[2], hi[3]);
-  st_bf16x4(L + Ly::bdOl + buf * C * PO + r * PO + cc, lo[0], lo[1], lo[2], lo[3]);
-  if (pt < Dm::TPR) {
-    const int c0 = pt * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dec[buf * D + c0 + e] = fast_exp(GATE == 0 ? f.gC : f.gCv[e / 4][e % 4]);
+};
+
+// the decay of this lane's four accumulator rows j = 16 jb + 4 g .. +3
+template <int D, int GATE>
+__device__ __forceinline__ f32x4 decay4(const float* dec, int jb, int g) {
+  if constexpr (GATE == 1) {
+    const float4 d = *reinterpret_cast<const float4*>(dec + 16 * jb + 4 * g);
+    return f32x4{d.x, d.y, d.z, d.w};
+  } else {
+    const float d = dec[0];
+    return f32x4{d, d, d, d};
   }
 }
 
@@ -304,219 +412,242 @@ __device__ __forceinline__ void bwd_stash_k(const BwdSet<D, TIO, GATE>& f, bf16*
 template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, int h, int sl) {
   using Dm = Dims<D>;
-  using Ly = ChainLayout<D>;
-  constexpr int PD = Dm::PD, NJW = Dm::NJW;
-  bf16* const L = reinterpret_cast<bf16*>(smem);
-  float* const dec = reinterpret_cast<float*>(smem + size_t(Ly::fEnd) * 2);
-  const bf16* Wl = L + Ly::fW;
-  const bf16* Khl = L + Ly::fKh;
-  const bf16* Uq = L + Ly::fUq;
-  bf16* Ss = L + Ly::fS;
-  bf16* Ut = L + Ly::fU;
-
-  const int tid = threadIdx.x;
-  const bool compute = tid < kChainCompute;
-  const int pt = tid - kChainCompute;   // producer thread index (valid when !compute)
-  const int l = lane_id(), w = wave_id();
+  using Cf = ChainCfg<D, TIO, GATE>;
+  constexpr int NJW = Dm::NJW;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = lane_id();
   const int g = l >> 4, jj = l & 15;
   const SeqEntry se = p.stab[si];
   const int v0 = 16 * sl;
   const int nck = se.nchunks;
 
-  f32x4 acc[NJW];
+  if (wv < 4) {
+    const int w = wv;
+    f32x4 acc[NJW];
 #pragma unroll
-  for (int x = 0; x < NJW; ++x) acc[x] = zero4();
-  if (compute && p.h0) {
+    for (int x = 0; x < NJW; ++x) acc[x] = zero4();
+    if (p.h0) {
 #pragma unroll
-    for (int x = 0; x < NJW; ++x) {
-      const int j = 16 * (w * NJW + x) + 4 * g;
-      const float4 t = *reinterpret_cast<const float4*>(p.h0 + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j);
-      acc[x] = f32x4{t.x, t.y, t.z, t.w};
+      for (int x = 0; x < NJW; ++x) {
+        const int j = 16 * (w * NJW + x) + 4 * g;
+        const float4 t = *reinterpret_cast<const float4*>(p.h0 + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j);
+        acc[x] = f32x4{t.x, t.y, t.z, t.w};
+      }
     }
-  }
-
-  // The two roles run separate loops (live ranges do not overlap); each executes
-  // exactly two workgroup barriers per chunk step.
-  if (compute) {
+    char* Ss = smem + Cf::fS;
+    char* Ut = smem + Cf::fU;
     for (int k = 0; k < nck; ++k) {
+      const int buf = k & 1;
+      const char* Fb = smem + buf * Cf::bufF;
       const int64_t ch = int64_t(h) * p.NC + se.c0 + k;
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
-        st_bf16x4(Ss + jj * PD + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+        st4_s<D>(Ss, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
         st_bf16x4(p.S + (ch * D + v0 + jj) * D + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
       }
-      __syncthreads();   // B1
+      chain_barrier();   // B1
       // U = U' - W S^T, rows 16w.., columns of this slice
       f32x4 au = zero4();
 #pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) au = mma(frag_rk(Wl, PD, 16 * w, k0), frag_rk(Ss, PD, 0, k0), au);
-      const uint2 up = *reinterpret_cast<const uint2*>(Uq + jj * PC + 16 * w + 4 * g);
+      for (int k0 = 0; k0 < D; k0 += 32) au = mma(frag_rk_s<D>(Fb + Cf::fW, 16 * w, k0), frag_rk_s<D>(Ss, 0, k0), au);
+      const uint16_t* Up = reinterpret_cast<const uint16_t*>(Fb + Cf::fUp);
       float u[4];
-      u[0] = __uint_as_float(up.x << 16) - au[0];
-      u[1] = __uint_as_float(up.x & 0xffff0000u) - au[1];
-      u[2] = __uint_as_float(up.y << 16) - au[2];
-      u[3] = __uint_as_float(up.y & 0xffff0000u) - au[3];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]) - au[i];
 #pragma unroll
       for (int i = 0; i < 4; ++i) p.U[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj] = f32_to_bf16_bits(u[i]);
-      st_bf16x4(Ut + jj * PC + 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
-      __syncthreads();   // B2
-      // S_{k+1}^T = S_k^T Diag(e^GamC) + Khat^T U
+      if constexpr (Cf::RAW) {
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(smem + Cf::fFk) + buf * C +
+                                                          16 * w + 4 * g);
+        u[0] *= f.x;
+        u[1] *= f.y;
+        u[2] *= f.z;
+        u[3] *= f.w;
+      }
+      st4_s<C>(Ut, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
+      chain_barrier();   // B2
+      // S_{k+1}^T = Diag(e^GamC) S_k^T + Khat^T U
+      const float* dec = reinterpret_cast<const float*>(smem + Cf::fDec) + buf * Cf::DG;
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int jb = w * NJW + x;
-        const float4 d = *reinterpret_cast<const float4*>(dec + 16 * jb + 4 * g);
-        f32x4 a = acc[x] * f32x4{d.x, d.y, d.z, d.w};
+        f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
 #pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc(Khl, PD, 16 * jb, k0), frag_rk(Ut, PC, 0, k0), a);
+        for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc_s<D>(Fb + Cf::fK, 16 * jb, k0), frag_rk_s<C>(Ut, 0, k0), a);
         acc[x] = a;
       }
     }
-  } else if (nck > 0) {
-    // three register sets: chunk k lives in set k % 3 from its load (step k - 3)
-    // until its last stash (step k), so every load has two steps to arrive
-    FwdSet<D, TIO, GATE> s0, s1, s2;
-    auto step = [&](int k, FwdSet<D, TIO, GATE>& cur, FwdSet<D, TIO, GATE>& nxt) __attribute__((always_inline)) {
-      __syncthreads();   // B1
-      fwd_stash_k<D, TIO, GATE>(cur, L, dec, pt);
-      __syncthreads();   // B2
-      if (k + 1 < nck) fwd_stash_w<D, TIO, GATE>(nxt, L, pt);
-      fwd_load<D, TIO, GATE>(cur, p, se, h, v0, se.c0 + min(k + 3, nck - 1), pt);
-    };
-    fwd_load<D, TIO, GATE>(s0, p, se, h, v0, se.c0, pt);
-    fwd_load<D, TIO, GATE>(s1, p, se, h, v0, se.c0 + min(1, nck - 1), pt);
-    fwd_load<D, TIO, GATE>(s2, p, se, h, v0, se.c0 + min(2, nck - 1), pt);
-    fwd_stash_w<D, TIO, GATE>(s0, L, pt);
-    for (int k = 0; k < nck; k += 3) {
-      step(k, s0, s1);
-      if (k + 1 < nck) step(k + 1, s1, s2);
-      if (k + 2 < nck) step(k + 2, s2, s0);
-    }
-  }
-  if (compute && p.ht) {
+    if (p.ht) {
 #pragma unroll
-    for (int x = 0; x < NJW; ++x) {
-      const int j = 16 * (w * NJW + x) + 4 * g;
-      *reinterpret_cast<float4*>(p.ht + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j) =
-          make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+      for (int x = 0; x < NJW; ++x) {
+        const int j = 16 * (w * NJW + x) + 4 * g;
+        *reinterpret_cast<float4*>(p.ht + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j) =
+            make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+      }
     }
+  } else if (wv == kConvWave) {
+    if (nck == 0) return;
+    ConvRegs<D, TIO, GATE> R;
+    auto chunk = [&](int k) { return se.c0 + min(k, nck - 1); };
+    R.load(p, se, h, chunk(0), v0, false);
+    R.store_fwd(smem, 0);
+    R.load(p, se, h, chunk(1), v0, false);
+    for (int k = 0; k < nck; ++k) {
+      chain_barrier();   // B1
+      chain_barrier();   // B2
+      R.store_fwd(smem, (k + 1) & 1);
+      R.load(p, se, h, chunk(k + 2), v0, false);
+    }
+    wait_vm<0>();
+  } else {
+    if (nck == 0) return;
+    const int mw = wv - kMoveWave0;
+    MoverLane<D> ml;
+    ml.init(mw, l);
+    auto chunk = [&](int k) { return se.c0 + min(k, nck - 1); };
+    move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), v0, smem, mw);
+    move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
+    move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), v0, smem + Cf::bufF, mw);
+    wait_vm<Cf::fwdB + Cf::fwdA>();
+    for (int k = 0; k < nck; ++k) {
+      chain_barrier();   // B1
+      move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
+      wait_vm<Cf::fwdA + Cf::fwdB>();
+      chain_barrier();   // B2
+      move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0, smem + (k & 1) * Cf::bufF, mw);
+      wait_vm<Cf::fwdB + Cf::fwdA>();
+    }
+    wait_vm<0>();
   }
 }
 
 template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, int h, int sl) {
   using Dm = Dims<D>;
-  using Ly = ChainLayout<D>;
-  constexpr int PD = Dm::PD, NJW = Dm::NJW, PO = Ly::PO;
-  constexpr bool kLo = std::is_same<TIO, float>::value;   // fp32 dO is not exact in bf16
-  bf16* const L = reinterpret_cast<bf16*>(smem);
-  float* const dec = reinterpret_cast<float*>(smem + size_t(Ly::bEnd) * 2);
-  const bf16* Khl = L + Ly::bKh;
-  const bf16* Pl = L + Ly::bP;
-  const bf16* Qhl = L + Ly::bQh;
-  const bf16* Qll = L + Ly::bQl;
-  const bf16* Wl = L + Ly::bW;
-  bf16* dSl = L + Ly::bdS;
-  bf16* dUt = L + Ly::bdU;
-
-  const int tid = threadIdx.x;
-  const bool compute = tid < kChainCompute;
-  const int pt = tid - kChainCompute;
-  const int l = lane_id(), w = wave_id();
+  using Cf = ChainCfg<D, TIO, GATE>;
+  constexpr int NJW = Dm::NJW;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = lane_id();
   const int g = l >> 4, jj = l & 15;
   const SeqEntry se = p.stab[si];
   const int v0 = 16 * sl;
   const int nck = se.nchunks;
-  const float scale = p.scale;
+  // step k walks chunk c0 + nck - 1 - k (last to first), clamped past the end
+  auto chunk = [&](int k) { return se.c0 + nck - 1 - min(k, nck - 1); };
 
-  f32x4 acc[NJW];
+  if (wv < 4) {
+    const int w = wv;
+    f32x4 acc[NJW];
 #pragma unroll
-  for (int x = 0; x < NJW; ++x) acc[x] = zero4();
-  if (compute && p.dht) {
-#pragma unroll
-    for (int x = 0; x < NJW; ++x) {
-      const int j = 16 * (w * NJW + x) + 4 * g;
-      const float4 t = *reinterpret_cast<const float4*>(p.dht + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j);
-      acc[x] = f32x4{t.x, t.y, t.z, t.w};
-    }
-  }
-
-  // step k walks chunk c0 + nck - 1 - k (last to first); the two roles run
-  // separate loops, each with exactly two workgroup barriers per step
-  auto chunk_of = [&](int k) { return se.c0 + nck - 1 - min(k, nck - 1); };
-  if (compute) {
-    for (int k = 0; k < nck; ++k) {
-      const int buf = k & 1;
-      const int64_t ch = int64_t(h) * p.NC + chunk_of(k);
-      const bf16* dOh = L + Ly::bdOh + buf * C * PO;
-      const bf16* dOl = L + Ly::bdOl + buf * C * PO;
+    for (int x = 0; x < NJW; ++x) acc[x] = zero4();
+    if (p.dht) {
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
-        st_bf16x4(dSl + jj * PD + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+        const float4 t = *reinterpret_cast<const float4*>(p.dht + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j);
+        acc[x] = f32x4{t.x, t.y, t.z, t.w};
+      }
+    }
+    char* dSl = smem + Cf::bdS;
+    char* dUt = smem + Cf::bdU;
+    for (int k = 0; k < nck; ++k) {
+      const int buf = k & 1;
+      const char* Bb = smem + buf * Cf::bufB;
+      const char* X1 = smem + Cf::bX1 + buf * Cf::XB;
+      const char* X2 = smem + Cf::bX2 + buf * Cf::XB;
+      const char* X3 = smem + Cf::bX3 + buf * Cf::XB;
+      const int64_t ch = int64_t(h) * p.NC + chunk(k);
+#pragma unroll
+      for (int x = 0; x < NJW; ++x) {
+        const int j = 16 * (w * NJW + x) + 4 * g;
+        st4_s<D>(dSl, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
         st_bf16x4(p.dS + (ch * D + v0 + jj) * D + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
       }
-      __syncthreads();   // B1
+      chain_barrier();   // B1
       // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice
-      f32x4 ad = zero4();
+      f32x4 ad = zero4(), ak = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < C; k0 += 32) {
-        const bf16x8 pa = frag_kc(Pl, PC, 16 * w, k0);
-        ad = mma(pa, frag_kc(dOh, PO, 0, k0), ad);
-        if constexpr (kLo) ad = mma(pa, frag_kc(dOl, PO, 0, k0), ad);
+        const bf16x8 pa = frag_kc_s<C>(Bb + Cf::bP, 16 * w, k0);
+        ad = mma(pa, frag_kc_s<16>(X1, 0, k0), ad);
+        if constexpr (Cf::LO) ad = mma(pa, frag_kc_s<16>(X2, 0, k0), ad);
       }
 #pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) ad = mma(frag_rk(Khl, PD, 16 * w, k0), frag_rk(dSl, PD, 0, k0), ad);
+      for (int k0 = 0; k0 < D; k0 += 32) ak = mma(frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0), frag_rk_s<D>(dSl, 0, k0), ak);
+      if constexpr (Cf::RAW) {
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(smem + Cf::bFk) + buf * C +
+                                                          16 * w + 4 * g);
+        ad += ak * f32x4{f.x, f.y, f.z, f.w};
+      } else {
+        ad += ak;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) p.dU[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj] = f32_to_bf16_bits(ad[i]);
-      st_bf16x4(dUt + jj * PC + 16 * w + 4 * g, -ad[0], -ad[1], -ad[2], -ad[3]);
-      __syncthreads();   // B2
-      // dS_n^T = dS_{n+1}^T Diag(e^GamC) + Qbar^T dO - W^T dU
+      st4_s<C>(dUt, jj, 16 * w + 4 * g, -ad[0], -ad[1], -ad[2], -ad[3]);
+      chain_barrier();   // B2
+      // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU
+      const float* dec = reinterpret_cast<const float*>(smem + Cf::bDec) + buf * Cf::DG;
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int jb = w * NJW + x;
-        const float4 d = *reinterpret_cast<const float4*>(dec + buf * D + 16 * jb + 4 * g);
-        f32x4 a = acc[x] * f32x4{d.x, d.y, d.z, d.w};
+        f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += 32) {
-          const bf16x8 qh = frag_kc(Qhl, PD, 16 * jb, k0);
-          const bf16x8 bh = frag_kc(dOh, PO, 0, k0);
-          a = mma(qh, bh, a);
-          a = mma(frag_kc(Qll, PD, 16 * jb, k0), bh, a);
-          if constexpr (kLo) a = mma(qh, frag_kc(dOl, PO, 0, k0), a);
-          a = mma(frag_kc(Wl, PD, 16 * jb, k0), frag_rk(dUt, PC, 0, k0), a);
+          const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, k0);
+          if constexpr (Cf::RAW) {
+            a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
+            a = mma(qa, frag_kc_s<16>(X3, 0, k0), a);
+          } else {
+            const bf16x8 bh = frag_kc_s<16>(X1, 0, k0);
+            a = mma(qa, bh, a);
+            a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, k0), bh, a);
+            if constexpr (Cf::LO) a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
+          }
+          a = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C>(dUt, 0, k0), a);
         }
         acc[x] = a;
       }
     }
-  } else if (nck > 0) {
-    // three register sets: chunk k lives in set k % 3 from its load (step k - 3)
-    // until its last stash (step k), so every load has two steps to arrive
-    BwdSet<D, TIO, GATE> s0, s1, s2;
-    auto step = [&](int k, BwdSet<D, TIO, GATE>& cur, BwdSet<D, TIO, GATE>& nxt) __attribute__((always_inline)) {
-      __syncthreads();   // B1
-      bwd_stash_q<D, TIO, GATE>(cur, L, scale, pt);
-      __syncthreads();   // B2
-      if (k + 1 < nck) bwd_stash_k<D, TIO, GATE>(nxt, L, dec, (k + 1) & 1, pt);
-      bwd_load<D, TIO, GATE>(cur, p, se, h, v0, chunk_of(k + 3), pt);
-    };
-    bwd_load<D, TIO, GATE>(s0, p, se, h, v0, chunk_of(0), pt);
-    bwd_load<D, TIO, GATE>(s1, p, se, h, v0, chunk_of(1), pt);
-    bwd_load<D, TIO, GATE>(s2, p, se, h, v0, chunk_of(2), pt);
-    bwd_stash_k<D, TIO, GATE>(s0, L, dec, 0, pt);
-    for (int k = 0; k < nck; k += 3) {
-      step(k, s0, s1);
-      if (k + 1 < nck) step(k + 1, s1, s2);
-      if (k + 2 < nck) step(k + 2, s2, s0);
-    }
-  }
-  if (compute && p.dh0) {
+    if (p.dh0) {
 #pragma unroll
-    for (int x = 0; x < NJW; ++x) {
-      const int j = 16 * (w * NJW + x) + 4 * g;
-      *reinterpret_cast<float4*>(p.dh0 + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j) =
-          make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+      for (int x = 0; x < NJW; ++x) {
+        const int j = 16 * (w * NJW + x) + 4 * g;
+        *reinterpret_cast<float4*>(p.dh0 + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j) =
+            make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+      }
     }
+  } else if (wv == kConvWave) {
+    if (nck == 0) return;
+    ConvRegs<D, TIO, GATE> R;
+    R.load(p, se, h, chunk(0), v0, true);
+    R.store_bwd(smem, 0);
+    R.load(p, se, h, chunk(1), v0, true);
+    for (int k = 0; k < nck; ++k) {
+      chain_barrier();   // B1
+      chain_barrier();   // B2
+      R.store_bwd(smem, (k + 1) & 1);
+      R.load(p, se, h, chunk(k + 2), v0, true);
+    }
+    wait_vm<0>();
+  } else {
+    if (nck == 0) return;
+    const int mw = wv - kMoveWave0;
+    MoverLane<D> ml;
+    ml.init(mw, l);
+    move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
+    move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
+    move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), smem + Cf::bufB, mw);
+    wait_vm<Cf::bwdB + Cf::bwdA>();
+    for (int k = 0; k < nck; ++k) {
+      chain_barrier();   // B1
+      move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
+      wait_vm<Cf::bwdA + Cf::bwdB>();
+      chain_barrier();   // B2
+      move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
+      wait_vm<Cf::bwdB + Cf::bwdA>();
+    }
+    wait_vm<0>();
   }
 }
 
@@ -525,7 +656,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
 // dealt round-robin over the 8 XCDs).
 template <int D, typename TIO, int GATE>
 __global__ __launch_bounds__(kChainThreads) void k_chain(const Params p, int mode, int nb_role) {
-  __shared__ __attribute__((aligned(16))) char smem[ChainLayout<D>::bytes];
+  __shared__ __attribute__((aligned(1024))) char smem[ChainCfg<D, TIO, GATE>::bytes];
   int b = blockIdx.x;
   int role;
   if (mode == kChainBoth) {

@@ -38,6 +38,9 @@ struct WsLayout {
   size_t ctab = 0, stab = 0;
   size_t gam = 0;    // fp32 [H][NC][64] or [H][NC][64][K]: in-chunk cumsum of the log decay
   size_t rho = 0;    // fp32 [H][NC][2][64]: 1/|q|, 1/|k| per row
+  size_t fac = 0;    // fp32 [H][NC][2][64]: scalar gate row factors of the recursions,
+                     //   fq = scale e^Gam / |q|, fk = e^(GamC - Gam) / |k| (zero past the end)
+  size_t edec = 0;   // fp32 [H][NC] or [H][NC][K]: chunk decay e^GamC
   size_t A = 0;      // bf16 [H][NC][64][64]: UT/WY inverse
   size_t P = 0;      // bf16 [H][NC][64][64]: scale * (Qn Kn^T o E), lower incl. diagonal
   size_t W = 0;      // bf16 [H][NC][64][K]:  A diag(beta) Kbar
@@ -51,7 +54,8 @@ struct WsLayout {
   size_t dgam = 0;   // fp32 [H][NC][64] or [H][NC][64][K]
   size_t dgamc = 0;  // fp32 [H][NC] or [H][NC][K]
   size_t dbeta = 0;  // fp32 [H][NC][64]: gradient w.r.t. beta (sigmoid space)
-  // per-channel gate only: the recursions' operand tiles formed by the prologue
+  // per-channel gate or fp32 inputs: the recursions' operand tiles formed by the
+  // prologue (the scalar gate with bf16 inputs applies row factors instead)
   size_t Kh = 0;     // bf16 [H][NC][64][K]: Khat = kn e^(GamC - Gam)
   size_t Qh = 0;     // bf16 [H][NC][64][K]: Qbar = scale qn e^Gam, high part
   size_t Ql = 0;     // bf16 [H][NC][64][K]: Qbar low part
@@ -73,8 +77,9 @@ struct Params {
   const SeqEntry* stab;
   float* gam;
   float* rho;
+  float *fac, *edec;
   uint16_t *A, *P, *W, *Up, *U, *S, *dS, *dU;   // bf16 bit patterns
-  uint16_t *Kh, *Qh, *Ql;                        // per-channel gate only
+  uint16_t *Kh, *Qh, *Ql;                        // materialised operand tiles (see WsLayout)
   float *dqn, *dkn, *dgam, *dgamc, *dbeta;
 };
 

@@ -46,7 +46,10 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   __shared__ __attribute__((aligned(16))) bf16 Vs[C * PD];
   __shared__ __attribute__((aligned(16))) bf16 As[C * PC];
   __shared__ __attribute__((aligned(16))) float Lf[C * PL];
-  __shared__ float gam_s[C], beta_s[C];
+  __shared__ float gam_s[C], beta_s[C], rq_s[C], rk_s[C];
+  // fp32 inputs: the recursions take materialised Khat / Qbar tiles (Qbar split
+  // into bf16 high and low parts); bf16 inputs use the raw rows and row factors
+  constexpr bool kMat = std::is_same<TIO, float>::value;
 
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkEntry ce = p.ctab[c];
@@ -57,6 +60,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
 
   // --- rows: L2 norms; qn, kn to LDS; kn and v kept in registers ---
   float kn_r[NPASS][8], v_r[NPASS][8];
+  float qn_r[kMat ? NPASS : 1][8];
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
@@ -86,6 +90,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       kn_r[ps][e] = kv[e] * rk;
+      if constexpr (kMat) qn_r[ps][e] = qv[e] * rq;
       qb[e] = to_bf16(qv[e] * rq);
       kb[e] = to_bf16(kn_r[ps][e]);
     }
@@ -94,6 +99,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
     if (tid % TPR == 0) {
       p.rho[ch * 2 * C + r] = rq;
       p.rho[ch * 2 * C + C + r] = rk;
+      rq_s[r] = rq;
+      rk_s[r] = rk;
     }
   }
   // --- beta and the in-chunk cumsum of the log decay (wave 0) ---
@@ -112,6 +119,34 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
     p.gam[ch * C + l] = lam;
   }
   __syncthreads();
+
+  // --- operands of the two recursions: row factors, chunk decay, and for fp32
+  // inputs the Khat and Qbar (high + low) tiles ---
+  if (tid < C) {
+    const float m = tid < len ? 1.f : 0.f, gC = gam_s[C - 1], gr = gam_s[tid];
+    p.fac[ch * 2 * C + tid] = m * p.scale * rq_s[tid] * fast_exp(gr);
+    p.fac[ch * 2 * C + C + tid] = m * rk_s[tid] * fast_exp(gC - gr);
+    if (tid == 0) p.edec[ch] = fast_exp(gC);
+  }
+  if constexpr (kMat) {
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
+      const float fk = fast_exp(gam_s[C - 1] - gam_s[r]), fq = p.scale * fast_exp(gam_s[r]);
+      bf16x8 kh, qh, ql;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = qn_r[ps][e] * fq;
+        kh[e] = to_bf16(kn_r[ps][e] * fk);
+        qh[e] = to_bf16(x);
+        ql[e] = to_bf16(x - float(qh[e]));
+      }
+      const int64_t o = (ch * C + r) * D + c0;
+      *reinterpret_cast<bf16x8*>(p.Kh + o) = kh;
+      *reinterpret_cast<bf16x8*>(p.Qh + o) = qh;
+      *reinterpret_cast<bf16x8*>(p.Ql + o) = ql;
+    }
+  }
 
   // --- M and P, transposed tiles so that each lane owns 4 consecutive s ---
   {
