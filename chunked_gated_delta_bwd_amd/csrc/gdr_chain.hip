@@ -13,16 +13,21 @@
 //
 // Workgroups have nine waves with fixed jobs:
 //   waves 0-3  compute: the MFMA products of one chunk step, two barriers a step;
-//   wave  4    converter: loads the small per-chunk data into registers one step
-//              ahead (the dO slice, row factors, the chunk decay) and writes it
-//              to LDS in the form the MFMAs take (bf16, high + low parts);
-//   waves 5-8  movers: copy the chunk tiles global -> LDS with direct-to-LDS
-//              loads (no registers, no ALU), two chunks ahead.
-// Every big tile has two LDS buffers (chunk k in buffer k % 2).  A tile read
-// in the first window of a step (between its barriers B1 and B2) is refilled
-// after B2, a tile read in the second window after the next B1, so each load
-// has one and a half steps to land; the movers wait for their own loads with
-// vmcnt before the barrier that publishes them.
+//              their results for later kernels (S, U or dS, dU of the chunk) go
+//              to LDS only;
+//   wave  4    converter: writes those slices from LDS to global memory with
+//              16-byte stores, and turns the chunk's dO slice into the bf16 form
+//              the MFMAs take (fq dO in high + low parts for the scalar gate with
+//              bf16 inputs; fp32 inputs: dO high + low, loaded into registers one
+//              step ahead);
+//   waves 5-8  movers: copy the chunk tiles and the small per-chunk data (dO
+//              slice, row factors, decay) global -> LDS with direct-to-LDS loads
+//              (no registers, no ALU), up to two chunks ahead.
+// Every big tile has two LDS buffers (chunk k in buffer k % 2), the small data
+// three rotating slots.  A tile read in the first window of a step (between its
+// barriers B1 and B2) is refilled after B2, a tile read in the second window
+// after the next B1, so each load has one and a half steps to land; the movers
+// wait for their own loads with vmcnt before the barrier that publishes them.
 //
 // Tiles are stored unpadded with an XOR swizzle of their 16-byte pieces (one
 // direct-to-LDS load writes 1 KB contiguously, so the swizzle is applied by
@@ -135,39 +140,46 @@ __device__ __forceinline__ void wait_vm() {
 // ---------------------------------------------------------------------------
 template <int D, typename TIO, int GATE>
 struct ChainCfg {
-  static constexpr bool MAT = GATE == 1 || std::is_same<TIO, float>::value;  // materialised Khat / Qbar
-  static constexpr bool RAW = !MAT;
-  static constexpr bool LO = std::is_same<TIO, float>::value;                // dO needs a low part
-  static constexpr int DG = GATE == 1 ? D : 4;     // decay floats per chunk (scalar padded)
+  static constexpr bool LO = std::is_same<TIO, float>::value;  // fp32 inputs: dO split in two parts
+  static constexpr bool MAT = GATE == 1 || LO;                 // materialised Khat / Qbar tiles
+  static constexpr bool RAW = !MAT;                            // raw q, k rows and row factors
+  static constexpr int DG = GATE == 1 ? D : 16;    // decay floats per slot (scalar: a 4-float copy per mover)
   static constexpr int TB = C * D * 2;             // one 64 x D bf16 tile
   static constexpr int PB = C * C * 2;             // the 64 x 64 P tile
-  static constexpr int XB = C * 16 * 2;            // a 64 x 16 slice
+  static constexpr int XB = C * 16 * 2;            // a 64 x 16 bf16 slice
   static constexpr int NJ = TB / 4096;             // 1 KB loads per mover wave per 64 x D tile
+  // small per-chunk data, three rotating slots: the raw dO slice (bf16 inputs),
+  // the row factors fq, fk (raw mode) and the decay
+  static constexpr int sDO = 0;
+  static constexpr int sFac = sDO + (LO ? 0 : XB);
+  static constexpr int sDec = sFac + (RAW ? 2 * C * 4 : 0);
+  static constexpr int SLOT = sDec + DG * 4;
   // reverse role, byte offsets; the tile buffers first
   static constexpr int bK = 0, bQh = TB, bQl = 2 * TB, bW = (MAT ? 3 : 2) * TB, bP = bW + TB;
   static constexpr int bufB = bP + PB;
-  static constexpr bool kX2 = RAW || LO, kX3 = RAW;
-  static constexpr int bX1 = 2 * bufB;                       // dO, bf16 (high part)
-  static constexpr int bX2 = bX1 + 2 * XB;                   // RAW: fq dO high; LO: dO low
-  static constexpr int bX3 = bX2 + (kX2 ? 2 * XB : 0);       // RAW: fq dO low
-  static constexpr int bFk = bX3 + (kX3 ? 2 * XB : 0);       // RAW: fk per row
-  static constexpr int bDec = bFk + (RAW ? 2 * C * 4 : 0);
-  static constexpr int bdS = bDec + 2 * DG * 4;              // 16 x D state-gradient slice
-  static constexpr int bdU = bdS + 16 * D * 2;               // 16 x 64: -dU^T
+  static constexpr int bX1 = 2 * bufB;                             // LO: dO high part
+  static constexpr int bX2 = bX1 + (LO ? 2 * XB : 0);              // RAW: fq dO high; LO: dO low
+  static constexpr int bX3 = bX2 + ((RAW || LO) ? 2 * XB : 0);     // RAW: fq dO low
+  static constexpr int bSlot = bX3 + (RAW ? 2 * XB : 0);
+  static constexpr int bdS = bSlot + 3 * SLOT;                     // 16 x D state-gradient slice
+  static constexpr int bdU = bdS + 16 * D * 2;                     // 16 x 64: dU^T
   static constexpr int bEnd = bdU + 16 * C * 2;
   // forward role
   static constexpr int fW = 0, fK = TB, fUp = 2 * TB, bufF = fUp + XB;
-  static constexpr int fFk = 2 * bufF;
-  static constexpr int fDec = fFk + (RAW ? 2 * C * 4 : 0);
-  static constexpr int fS = fDec + 2 * DG * 4;               // 16 x D state slice
-  static constexpr int fU = fS + 16 * D * 2;                 // 16 x 64: U^T (row-scaled for RAW)
-  static constexpr int fEnd = fU + 16 * C * 2;
+  static constexpr int fSlot = 2 * bufF;
+  static constexpr int fS = fSlot + 3 * SLOT;                      // 16 x D state slice
+  static constexpr int fU = fS + 16 * D * 2;                       // 16 x 64: U^T as the MFMA takes it
+  static constexpr int fUo = fU + 16 * C * 2;                      // RAW: unscaled U^T, to be stored
+  static constexpr int fEnd = fUo + (RAW ? 16 * C * 2 : 0);
   static constexpr int bytes = bEnd > fEnd ? bEnd : fEnd;
-  // mover loads per wave per chunk, first-window set A and second-window set B
-  static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 : 2) * NJ;
-  static constexpr int fwdA = NJ + 1, fwdB = NJ;
+  // mover loads per wave per chunk: first-window set A, second-window set B
+  // (set B carries the small data of the chunk after its own)
+  static constexpr int nSb = LO ? 0 : (RAW ? 3 : 2);   // dO, fac, decay
+  static constexpr int nSf = LO ? 0 : (RAW ? 2 : 1);   // fac, decay
+  static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 : 2) * NJ + nSb;
+  static constexpr int fwdA = NJ + 1, fwdB = NJ + nSf;
   static_assert(bytes <= 160 * 1024, "LDS budget");
-  static_assert(bwdA + bwdB < 64 && fwdA + fwdB < 64, "vmcnt range");
+  static_assert(2 * bwdA + bwdB < 64 && 2 * fwdA + fwdB < 64, "vmcnt range");
 };
 
 struct ChunkGeo {
@@ -241,6 +253,33 @@ __device__ __forceinline__ void move_p(const MoverLane<D>& ml, const void* src, 
   for (int j = 0; j < 2; ++j) dma16(s + ml.tP[j], dst + mw * 2048 + j * 1024);
 }
 
+// small data of chunk c into a slot: the dO slice (reverse role), fq / fk, decay.
+// Every mover wave issues the same number of loads (partial-wave loads).
+template <int D, typename TIO, int GATE>
+__device__ __forceinline__ void move_small(const Params& p, const SeqEntry& se, int h, int c, int v0, char* slot,
+                                           int mw, bool with_dO) {
+  using Cf = ChainCfg<D, TIO, GATE>;
+  if constexpr (!Cf::LO) {
+    const ChunkGeo cg = geo(p, se, h, c);
+    const int l = lane_id();
+    if (with_dO && l < 32) {
+      // rows 16 mw .. 16 mw + 15 of the 64 x 16 slice, two pieces a row
+      const int row = 16 * mw + (l >> 1);
+      const char* src = reinterpret_cast<const char*>(p.dO) +
+                        (tok(cg.t0 + min(row, cg.len - 1), p.H, h) * D + v0) * 2 + (l & 1) * 16;
+      dma16(src, slot + Cf::sDO + mw * 512);
+    }
+    if constexpr (Cf::RAW) {
+      if (l < 8) dma16(reinterpret_cast<const char*>(p.fac + cg.ch * 2 * C) + mw * 128 + l * 16, slot + Cf::sFac + mw * 128);
+    }
+    if constexpr (GATE == 1) {
+      if (l < D / 16) dma16(reinterpret_cast<const char*>(p.edec + cg.ch * D) + mw * D + l * 16, slot + Cf::sDec + mw * D);
+    } else {
+      if (l == 0) dma16(p.edec + cg.ch * 4, slot + Cf::sDec + mw * 16);
+    }
+  }
+}
+
 // reverse role: set A (Khat or k, P), set B (Qbar high [+ low] or q, W)
 template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void move_bwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
@@ -290,17 +329,33 @@ __device__ __forceinline__ void move_fwd_b(const MoverLane<D>& ml, const Params&
 }
 
 // ---------------------------------------------------------------------------
-// converter (wave 4): lane l owns row l of the chunk
+// converter (wave 4)
 // ---------------------------------------------------------------------------
+// Copies a 16-row slice tile (W columns, swizzled in LDS) to 16 contiguous global
+// rows with 16-byte stores.
+template <int W>
+__device__ __forceinline__ void store_slice(const char* T, uint16_t* dst) {
+  constexpr int BYTES = 16 * W * 2;
+  const int l = lane_id();
+#pragma unroll
+  for (int i = 0; i < BYTES / 1024; ++i) {
+    const int pos = i * 1024 + 16 * l;
+    const int row = pos / (2 * W), piece = (pos % (2 * W)) >> 4;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(T + soff<W>(row, piece * 8));
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst) + pos) = v;
+  }
+}
+
+// fp32 inputs: the converter loads the chunk's dO rows and decay into registers
+// one step ahead and writes dO high / low parts and the decay to LDS
 template <int D, typename TIO, int GATE>
-struct ConvRegs {
+struct LoRegs {
   static constexpr int ND = GATE == 1 ? D / 64 : 1;
-  typename IO<TIO>::Raw8 d0, d1;   // 16 dO values of row l (reverse role)
-  float m, fq, fk;
+  typename IO<TIO>::Raw8 d0, d1;   // 16 dO values of row l
+  float m;
   float dec[ND];
 
   __device__ __forceinline__ void load(const Params& p, const SeqEntry& se, int h, int c, int v0, bool with_dO) {
-    using Cf = ChainCfg<D, TIO, GATE>;
     const int l = lane_id();
     const ChunkGeo cg = geo(p, se, h, c);
     if (with_dO) {
@@ -309,78 +364,32 @@ struct ConvRegs {
       d1 = IO<TIO>::load_raw8(p.dO, o + 8);
     }
     m = l < cg.len ? 1.f : 0.f;
-    if constexpr (Cf::RAW) {
-      fq = p.fac[cg.ch * 2 * C + l];
-      fk = p.fac[cg.ch * 2 * C + C + l];
-    }
     if constexpr (GATE == 1) {
 #pragma unroll
       for (int i = 0; i < ND; ++i) dec[i] = p.edec[cg.ch * D + ND * l + i];
     } else {
-      dec[0] = p.edec[cg.ch];
+      dec[0] = p.edec[cg.ch * 4];
     }
   }
 
-  // reverse role: dO (high [, low]) or for RAW dO and fq dO (high, low), fk, decay
-  __device__ __forceinline__ void store_bwd(char* smem, int buf) const {
-    using Cf = ChainCfg<D, TIO, GATE>;
+  __device__ __forceinline__ void store_dO(char* x1, char* x2) const {
     const int l = lane_id();
-    float x[16];
-    {
-      float a[8], b[8];
-      IO<TIO>::unpack8(d0, a);
-      IO<TIO>::unpack8(d1, b);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = m * a[e];
-        x[8 + e] = m * b[e];
-      }
-    }
-    bf16x8 h0, h1;
+    float a[8], b[8];
+    IO<TIO>::unpack8(d0, a);
+    IO<TIO>::unpack8(d1, b);
+    bf16x8 h0, h1, l0, l1;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      h0[e] = to_bf16(x[e]);
-      h1[e] = to_bf16(x[8 + e]);
+      const float xa = m * a[e], xb = m * b[e];
+      h0[e] = to_bf16(xa);
+      h1[e] = to_bf16(xb);
+      l0[e] = to_bf16(xa - float(h0[e]));
+      l1[e] = to_bf16(xb - float(h1[e]));
     }
-    char* r1 = smem + Cf::bX1 + buf * Cf::XB + l * 32;
-    *reinterpret_cast<bf16x8*>(r1) = h0;
-    *reinterpret_cast<bf16x8*>(r1 + 16) = h1;
-    if constexpr (Cf::RAW) {
-      bf16x8 a0, a1, b0, b1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float y0 = fq * x[e], y1 = fq * x[8 + e];
-        a0[e] = to_bf16(y0);
-        a1[e] = to_bf16(y1);
-        b0[e] = to_bf16(y0 - float(a0[e]));
-        b1[e] = to_bf16(y1 - float(a1[e]));
-      }
-      char* r2 = smem + Cf::bX2 + buf * Cf::XB + l * 32;
-      char* r3 = smem + Cf::bX3 + buf * Cf::XB + l * 32;
-      *reinterpret_cast<bf16x8*>(r2) = a0;
-      *reinterpret_cast<bf16x8*>(r2 + 16) = a1;
-      *reinterpret_cast<bf16x8*>(r3) = b0;
-      *reinterpret_cast<bf16x8*>(r3 + 16) = b1;
-      reinterpret_cast<float*>(smem + Cf::bFk)[buf * C + l] = fk;
-    } else if constexpr (Cf::LO) {
-      bf16x8 b0, b1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        b0[e] = to_bf16(x[e] - float(h0[e]));
-        b1[e] = to_bf16(x[8 + e] - float(h1[e]));
-      }
-      char* r2 = smem + Cf::bX2 + buf * Cf::XB + l * 32;
-      *reinterpret_cast<bf16x8*>(r2) = b0;
-      *reinterpret_cast<bf16x8*>(r2 + 16) = b1;
-    }
-    store_dec(reinterpret_cast<float*>(smem + Cf::bDec) + buf * Cf::DG);
-  }
-
-  // forward role: fk and the decay
-  __device__ __forceinline__ void store_fwd(char* smem, int buf) const {
-    using Cf = ChainCfg<D, TIO, GATE>;
-    if constexpr (Cf::RAW) reinterpret_cast<float*>(smem + Cf::fFk)[buf * C + lane_id()] = fk;
-    store_dec(reinterpret_cast<float*>(smem + Cf::fDec) + buf * Cf::DG);
+    *reinterpret_cast<bf16x8*>(x1 + l * 32) = h0;
+    *reinterpret_cast<bf16x8*>(x1 + l * 32 + 16) = h1;
+    *reinterpret_cast<bf16x8*>(x2 + l * 32) = l0;
+    *reinterpret_cast<bf16x8*>(x2 + l * 32 + 16) = l1;
   }
 
   __device__ __forceinline__ void store_dec(float* dst) const {
@@ -393,6 +402,32 @@ struct ConvRegs {
     }
   }
 };
+
+// raw mode: fq dO split into bf16 high and low parts, from the slot's dO slice
+template <int D, typename TIO, int GATE>
+__device__ __forceinline__ void convert_raw(const char* slot, char* x2, char* x3) {
+  using Cf = ChainCfg<D, TIO, GATE>;
+  const int l = lane_id();
+  const u32x4 r0 = *reinterpret_cast<const u32x4*>(slot + Cf::sDO + l * 32);
+  const u32x4 r1 = *reinterpret_cast<const u32x4*>(slot + Cf::sDO + l * 32 + 16);
+  const float fq = reinterpret_cast<const float*>(slot + Cf::sFac)[l];
+  float a[8], b[8];
+  IO<bf16>::unpack8(r0, a);
+  IO<bf16>::unpack8(r1, b);
+  bf16x8 h0, h1, l0, l1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float ya = fq * a[e], yb = fq * b[e];
+    h0[e] = to_bf16(ya);
+    h1[e] = to_bf16(yb);
+    l0[e] = to_bf16(ya - float(h0[e]));
+    l1[e] = to_bf16(yb - float(h1[e]));
+  }
+  *reinterpret_cast<bf16x8*>(x2 + l * 32) = h0;
+  *reinterpret_cast<bf16x8*>(x2 + l * 32 + 16) = h1;
+  *reinterpret_cast<bf16x8*>(x3 + l * 32) = l0;
+  *reinterpret_cast<bf16x8*>(x3 + l * 32 + 16) = l1;
+}
 
 // the decay of this lane's four accumulator rows j = 16 jb + 4 g .. +3
 template <int D, int GATE>
@@ -420,6 +455,11 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
   const SeqEntry se = p.stab[si];
   const int v0 = 16 * sl;
   const int nck = se.nchunks;
+  char* Ss = smem + Cf::fS;
+  char* Ut = smem + Cf::fU;
+  char* Uo = smem + (Cf::RAW ? Cf::fUo : Cf::fU);
+  auto chunk = [&](int k) { return se.c0 + min(k, nck - 1); };
+  auto slot = [&](int k) { return smem + Cf::fSlot + (k % 3) * Cf::SLOT; };
 
   if (wv < 4) {
     const int w = wv;
@@ -434,17 +474,14 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
         acc[x] = f32x4{t.x, t.y, t.z, t.w};
       }
     }
-    char* Ss = smem + Cf::fS;
-    char* Ut = smem + Cf::fU;
+    if (nck > 0) chain_barrier();   // B0
     for (int k = 0; k < nck; ++k) {
-      const int buf = k & 1;
-      const char* Fb = smem + buf * Cf::bufF;
-      const int64_t ch = int64_t(h) * p.NC + se.c0 + k;
+      const char* Fb = smem + (k & 1) * Cf::bufF;
+      const char* sl_k = slot(k);
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
         st4_s<D>(Ss, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-        st_bf16x4(p.S + (ch * D + v0 + jj) * D + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
       }
       chain_barrier();   // B1
       // U = U' - W S^T, rows 16w.., columns of this slice
@@ -455,10 +492,9 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       float u[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) u[i] = bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]) - au[i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p.U[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj] = f32_to_bf16_bits(u[i]);
       if constexpr (Cf::RAW) {
-        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(smem + Cf::fFk) + buf * C +
+        st4_s<C>(Uo, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C +
                                                           16 * w + 4 * g);
         u[0] *= f.x;
         u[1] *= f.y;
@@ -468,7 +504,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       st4_s<C>(Ut, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
       chain_barrier();   // B2
       // S_{k+1}^T = Diag(e^GamC) S_k^T + Khat^T U
-      const float* dec = reinterpret_cast<const float*>(smem + Cf::fDec) + buf * Cf::DG;
+      const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int jb = w * NJW + x;
@@ -488,16 +524,23 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     }
   } else if (wv == kConvWave) {
     if (nck == 0) return;
-    ConvRegs<D, TIO, GATE> R;
-    auto chunk = [&](int k) { return se.c0 + min(k, nck - 1); };
-    R.load(p, se, h, chunk(0), v0, false);
-    R.store_fwd(smem, 0);
-    R.load(p, se, h, chunk(1), v0, false);
+    LoRegs<D, TIO, GATE> R;
+    if constexpr (Cf::LO) {
+      R.load(p, se, h, chunk(0), v0, false);
+      R.store_dec(reinterpret_cast<float*>(slot(0) + Cf::sDec));
+      R.load(p, se, h, chunk(1), v0, false);
+    }
+    chain_barrier();   // B0
     for (int k = 0; k < nck; ++k) {
+      const int64_t ch = int64_t(h) * p.NC + chunk(k);
       chain_barrier();   // B1
+      store_slice<D>(Ss, p.S + (ch * D + v0) * D);
       chain_barrier();   // B2
-      R.store_fwd(smem, (k + 1) & 1);
-      R.load(p, se, h, chunk(k + 2), v0, false);
+      store_slice<C>(Uo, p.U + (ch * D + v0) * C);
+      if constexpr (Cf::LO) {
+        R.store_dec(reinterpret_cast<float*>(slot(k + 1) + Cf::sDec));
+        R.load(p, se, h, chunk(k + 2), v0, false);
+      }
     }
     wait_vm<0>();
   } else {
@@ -505,14 +548,18 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     const int mw = wv - kMoveWave0;
     MoverLane<D> ml;
     ml.init(mw, l);
-    auto chunk = [&](int k) { return se.c0 + min(k, nck - 1); };
+    move_small<D, TIO, GATE>(p, se, h, chunk(0), v0, slot(0), mw, false);
     move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), v0, smem, mw);
     move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
+    move_small<D, TIO, GATE>(p, se, h, chunk(1), v0, slot(1), mw, false);
     move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), v0, smem + Cf::bufF, mw);
+    wait_vm<Cf::fwdA + Cf::fwdB + Cf::fwdA>();
+    chain_barrier();   // B0
     wait_vm<Cf::fwdB + Cf::fwdA>();
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
+      move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0, slot(k + 2), mw, false);
       wait_vm<Cf::fwdA + Cf::fwdB>();
       chain_barrier();   // B2
       move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0, smem + (k & 1) * Cf::bufF, mw);
@@ -533,8 +580,11 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
   const SeqEntry se = p.stab[si];
   const int v0 = 16 * sl;
   const int nck = se.nchunks;
+  char* dSl = smem + Cf::bdS;
+  char* dUt = smem + Cf::bdU;
   // step k walks chunk c0 + nck - 1 - k (last to first), clamped past the end
   auto chunk = [&](int k) { return se.c0 + nck - 1 - min(k, nck - 1); };
+  auto slot = [&](int k) { return smem + Cf::bSlot + (k % 3) * Cf::SLOT; };
 
   if (wv < 4) {
     const int w = wv;
@@ -549,20 +599,18 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         acc[x] = f32x4{t.x, t.y, t.z, t.w};
       }
     }
-    char* dSl = smem + Cf::bdS;
-    char* dUt = smem + Cf::bdU;
+    if (nck > 0) chain_barrier();   // B0
     for (int k = 0; k < nck; ++k) {
       const int buf = k & 1;
       const char* Bb = smem + buf * Cf::bufB;
-      const char* X1 = smem + Cf::bX1 + buf * Cf::XB;
+      const char* sl_k = slot(k);
+      const char* X1 = Cf::LO ? smem + Cf::bX1 + buf * Cf::XB : sl_k + Cf::sDO;
       const char* X2 = smem + Cf::bX2 + buf * Cf::XB;
       const char* X3 = smem + Cf::bX3 + buf * Cf::XB;
-      const int64_t ch = int64_t(h) * p.NC + chunk(k);
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
         st4_s<D>(dSl, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-        st_bf16x4(p.dS + (ch * D + v0 + jj) * D + j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
       }
       chain_barrier();   // B1
       // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice
@@ -576,22 +624,20 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
 #pragma unroll
       for (int k0 = 0; k0 < D; k0 += 32) ak = mma(frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0), frag_rk_s<D>(dSl, 0, k0), ak);
       if constexpr (Cf::RAW) {
-        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(smem + Cf::bFk) + buf * C +
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C +
                                                           16 * w + 4 * g);
         ad += ak * f32x4{f.x, f.y, f.z, f.w};
       } else {
         ad += ak;
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p.dU[(ch * C + 16 * w + 4 * g + i) * D + v0 + jj] = f32_to_bf16_bits(ad[i]);
-      st4_s<C>(dUt, jj, 16 * w + 4 * g, -ad[0], -ad[1], -ad[2], -ad[3]);
+      st4_s<C>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
       chain_barrier();   // B2
       // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU
-      const float* dec = reinterpret_cast<const float*>(smem + Cf::bDec) + buf * Cf::DG;
+      const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int jb = w * NJW + x;
-        f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
+        f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g), aw = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += 32) {
           const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, k0);
@@ -604,9 +650,9 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
             a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, k0), bh, a);
             if constexpr (Cf::LO) a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
           }
-          a = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C>(dUt, 0, k0), a);
+          aw = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C>(dUt, 0, k0), aw);
         }
-        acc[x] = a;
+        acc[x] = a - aw;
       }
     }
     if (p.dh0) {
@@ -619,15 +665,29 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     }
   } else if (wv == kConvWave) {
     if (nck == 0) return;
-    ConvRegs<D, TIO, GATE> R;
-    R.load(p, se, h, chunk(0), v0, true);
-    R.store_bwd(smem, 0);
-    R.load(p, se, h, chunk(1), v0, true);
+    LoRegs<D, TIO, GATE> R;
+    if constexpr (Cf::LO) {
+      R.load(p, se, h, chunk(0), v0, true);
+      R.store_dO(smem + Cf::bX1, smem + Cf::bX2);
+      R.store_dec(reinterpret_cast<float*>(slot(0) + Cf::sDec));
+      R.load(p, se, h, chunk(1), v0, true);
+    }
+    chain_barrier();   // B0
+    if constexpr (Cf::RAW) convert_raw<D, TIO, GATE>(slot(0), smem + Cf::bX2, smem + Cf::bX3);
     for (int k = 0; k < nck; ++k) {
+      const int64_t ch = int64_t(h) * p.NC + chunk(k);
+      const int nb = (k + 1) & 1;
       chain_barrier();   // B1
+      store_slice<D>(dSl, p.dS + (ch * D + v0) * D);
       chain_barrier();   // B2
-      R.store_bwd(smem, (k + 1) & 1);
-      R.load(p, se, h, chunk(k + 2), v0, true);
+      store_slice<C>(dUt, p.dU + (ch * D + v0) * C);
+      if constexpr (Cf::RAW) {
+        convert_raw<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + nb * Cf::XB, smem + Cf::bX3 + nb * Cf::XB);
+      } else if constexpr (Cf::LO) {
+        R.store_dO(smem + Cf::bX1 + nb * Cf::XB, smem + Cf::bX2 + nb * Cf::XB);
+        R.store_dec(reinterpret_cast<float*>(slot(k + 1) + Cf::sDec));
+        R.load(p, se, h, chunk(k + 2), v0, true);
+      }
     }
     wait_vm<0>();
   } else {
@@ -635,13 +695,18 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     const int mw = wv - kMoveWave0;
     MoverLane<D> ml;
     ml.init(mw, l);
+    move_small<D, TIO, GATE>(p, se, h, chunk(0), v0, slot(0), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
     move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
+    move_small<D, TIO, GATE>(p, se, h, chunk(1), v0, slot(1), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), smem + Cf::bufB, mw);
+    wait_vm<Cf::bwdA + Cf::bwdB + Cf::bwdA>();
+    chain_barrier();   // B0
     wait_vm<Cf::bwdB + Cf::bwdA>();
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
+      move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0, slot(k + 2), mw, true);
       wait_vm<Cf::bwdA + Cf::bwdB>();
       chain_barrier();   // B2
       move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);

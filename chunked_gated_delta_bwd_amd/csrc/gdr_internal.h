@@ -40,15 +40,15 @@ struct WsLayout {
   size_t rho = 0;    // fp32 [H][NC][2][64]: 1/|q|, 1/|k| per row
   size_t fac = 0;    // fp32 [H][NC][2][64]: scalar gate row factors of the recursions,
                      //   fq = scale e^Gam / |q|, fk = e^(GamC - Gam) / |k| (zero past the end)
-  size_t edec = 0;   // fp32 [H][NC] or [H][NC][K]: chunk decay e^GamC
+  size_t edec = 0;   // fp32 [H][NC][4] (value, 3 pad) or [H][NC][K]: chunk decay e^GamC
   size_t A = 0;      // bf16 [H][NC][64][64]: UT/WY inverse
   size_t P = 0;      // bf16 [H][NC][64][64]: scale * (Qn Kn^T o E), lower incl. diagonal
   size_t W = 0;      // bf16 [H][NC][64][K]:  A diag(beta) Kbar
   size_t Up = 0;     // bf16 [H][NC][64][V]:  U' = A diag(beta) V
-  size_t U = 0;      // bf16 [H][NC][64][V]:  v_new = U' - W S^T (forward state pass)
+  size_t U = 0;      // bf16 [H][NC][V][64]:  v_new = U' - W S^T (forward state pass), transposed
   size_t S = 0;      // bf16 [H][NC][V][K]:   state at chunk start
   size_t dS = 0;     // bf16 [H][NC][V][K]:   gradient w.r.t. the state at chunk end
-  size_t dU = 0;     // bf16 [H][NC][64][V]:  gradient w.r.t. v_new
+  size_t dU = 0;     // bf16 [H][NC][V][64]:  gradient w.r.t. v_new, transposed
   size_t dqn = 0;    // fp32 [H][NC][64][K]
   size_t dkn = 0;    // fp32 [H][NC][64][K]
   size_t dgam = 0;   // fp32 [H][NC][64] or [H][NC][64][K]

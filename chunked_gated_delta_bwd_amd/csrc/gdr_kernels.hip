@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
     const float m = tid < len ? 1.f : 0.f, gC = gam_s[C - 1], gr = gam_s[tid];
     p.fac[ch * 2 * C + tid] = m * p.scale * rq_s[tid] * fast_exp(gr);
     p.fac[ch * 2 * C + C + tid] = m * rk_s[tid] * fast_exp(gC - gr);
-    if (tid == 0) p.edec[ch] = fast_exp(gC);
+    if (tid == 0) p.edec[ch * 4] = fast_exp(gC);
   }
   if constexpr (kMat) {
 #pragma unroll
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   __shared__ __attribute__((aligned(16))) bf16 RS[GradSmem<D>::rs];
   __shared__ __attribute__((aligned(16))) bf16 RdS[GradSmem<D>::rds];
   __shared__ __attribute__((aligned(16))) bf16 dOs[C * PD];
-  __shared__ __attribute__((aligned(16))) bf16 Us[C * PD];
+  __shared__ __attribute__((aligned(16))) bf16 UsT[D * PC];   // U^T: [v][r]
   __shared__ __attribute__((aligned(16))) bf16 dYs[C * PD];
   __shared__ float gam_s[C], beta_s[C], rq_s[C], rk_s[C];
   // fixed-order partial sums (deterministic): column sums of the pairwise dGamma
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   const int H = p.H;
   const float scale = p.scale;
 
-  bf16* dUs = RS;     // phase 1
+  bf16* dUsT = RS;    // phase 1: dU^T [v][r]
   bf16* As = RdS;     // phase 1
   if (tid < C) {
     gam_s[tid] = p.gam[ch * C + tid];
@@ -281,11 +281,15 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) colsum_s[x][tid] = 0.f;
   }
+  // U and dU are stored transposed, [v][r]
+  for (int pc = tid; pc < D * C / 8; pc += kThreads) {
+    const int v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
+    *reinterpret_cast<uint4*>(dUsT + v * PC + c0) = *reinterpret_cast<const uint4*>(p.dU + (ch * D + v) * C + c0);
+    *reinterpret_cast<uint4*>(UsT + v * PC + c0) = *reinterpret_cast<const uint4*>(p.U + (ch * D + v) * C + c0);
+  }
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
-    *reinterpret_cast<uint4*>(dUs + r * PD + c0) = *reinterpret_cast<const uint4*>(p.dU + (ch * C + r) * D + c0);
-    *reinterpret_cast<uint4*>(Us + r * PD + c0) = *reinterpret_cast<const uint4*>(p.U + (ch * C + r) * D + c0);
     float x[8];
     IO<TIO>::load8(p.dO, tok(t0 + min(r, len - 1), H, h) * D + c0, x);
     const float m = r < len ? 1.f : 0.f;
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   for (int vb = 0; vb < NJB; ++vb) {
     f32x4 a = zero4();
 #pragma unroll
-    for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc(dUs, PD, 16 * vb, k0), frag_kc(As, PC, 16 * w, k0), a);
+    for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_rk(dUsT, PC, 16 * vb, k0), frag_kc(As, PC, 16 * w, k0), a);
     const int v = 16 * vb + 4 * g;
     st_bf16x4(dYs + r * PD + v, a[0], a[1], a[2], a[3]);
     // rows past the end: dY is exactly zero there, so the clamped v row adds nothing
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
       const bf16x8 aD = frag_kc(RdS, PD, 16 * jb, k0);
       aZ[jb] = mma(aS, frag_rk(dYs, PD, 16 * w, k0), aZ[jb]);
       aQ[jb] = mma(aS, frag_rk(dOs, PD, 16 * w, k0), aQ[jb]);
-      aK[jb] = mma(aD, frag_rk(Us, PD, 16 * w, k0), aK[jb]);
+      aK[jb] = mma(aD, frag_kc(UsT, PC, 16 * w, k0), aK[jb]);
     }
   }
   // state term of dGamma_C: sum_{v,j} dS * S
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
       f32x4 G1 = zero4(), G2 = zero4(), Mr = zero4(), Pr = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < D; k0 += 32) {
-        const bf16x8 aU = frag_rk(Us, PD, 16 * sb, k0);
+        const bf16x8 aU = frag_kc(UsT, PC, 16 * sb, k0);
         G1 = mma(aU, frag_rk(dOs, PD, 16 * w, k0), G1);
         G2 = mma(aU, frag_rk(dYs, PD, 16 * w, k0), G2);
         const bf16x8 aK = frag_rk(Kn, PD, 16 * sb, k0);

@@ -117,7 +117,7 @@ gdr_status gdr_fwd_bwd(const gdr_shape* shape, const gdr_inputs* in, const void*
  * after all chunks of sequences < n; rows past a sequence's end are padding):
  *   GDR_WS_STATE   bf16 [H][NC][Dv][Dk]  state at the start of each chunk
  *   GDR_WS_DSTATE  bf16 [H][NC][Dv][Dk]  gradient w.r.t. the state at the end of each chunk
- *   GDR_WS_U       bf16 [H][NC][64][Dv]  v_new = U' - W S^T
+ *   GDR_WS_U       bf16 [H][NC][Dv][64]  v_new = U' - W S^T, transposed (column v of the chunk is contiguous)
  *   GDR_WS_A       bf16 [H][NC][64][64]  the UT/WY inverse
  *   GDR_WS_GAMMA   fp32 [H][NC][64] (SCALAR) or [H][NC][64][Dk] (CHANNEL): in-chunk gate cumsum
  */
