@@ -60,45 +60,51 @@ typedef __attribute__((address_space(1))) void gbl_void_t;
 // ---------------------------------------------------------------------------
 // swizzled LDS tiles
 // ---------------------------------------------------------------------------
-// Piece p (16 bytes) of row r of a W-column bf16 tile sits at piece p ^ swz<W>(r):
-// 16 consecutive rows at one piece (row fragments) and 4 consecutive rows at two
-// adjacent pieces (transposed reads) land on distinct banks.
+// Piece p (16 bytes) of row r of a W-column bf16 tile sits at piece p ^ swz(r).
+// The functions were chosen by measuring LDS bank conflicts on gfx950:
+//   W = 128: (r ^ 2r) mod 16 is conflict-free for both row-fragment reads (16
+//            rows at one piece, ds_read_b128) and transposed reads (rows
+//            r..r+3 and r+8..r+11 at two adjacent pieces, ds_read_b64_tr_b16);
+//   W = 64, kind 0: conflict-free transposed reads (the P tile, 64-wide tiles);
+//   W = 64, kind 1: r mod 8, conflict-free row-fragment reads (16-row tiles);
+//   W = 16: no swizzle, but rows 8-11 and 12-15 of every 16 swap places, so
+//            that the two 16-lane halves of a transposed read hit different banks.
+template <int W, int KIND>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (W == 128) return (r ^ (r << 1)) & 15;
+  else if constexpr (W == 64 && KIND == 0) return 4 * ((r >> 1) & 1) + 2 * ((r & 1) ^ ((r >> 3) & 1)) + ((r >> 2) & 1);
+  else if constexpr (W == 64) return r & 7;
+  else return 0;
+}
+
+// physical row of logical row r (only 16-wide tiles permute rows)
 template <int W>
-__device__ __forceinline__ int swz(int r);
-template <>
-__device__ __forceinline__ int swz<128>(int r) {
-  return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1);
-}
-template <>
-__device__ __forceinline__ int swz<64>(int r) {
-  return 4 * ((r >> 1) & 1) + 2 * ((r & 1) ^ ((r >> 3) & 1)) + ((r >> 2) & 1);
-}
-template <>
-__device__ __forceinline__ int swz<16>(int) {
-  return 0;
+__device__ __forceinline__ int prow(int r) {
+  if constexpr (W == 16) return r ^ (((r >> 3) & 1) << 2);
+  else return r;
 }
 
 // byte offset of element (r, c) of a swizzled W-column bf16 tile
-template <int W>
+template <int W, int KIND = 0>
 __device__ __forceinline__ int soff(int r, int c) {
-  return r * (2 * W) + (((c >> 3) ^ swz<W>(r)) << 4) + ((c & 7) << 1);
+  return prow<W>(r) * (2 * W) + (((c >> 3) ^ swz<W, KIND>(r)) << 4) + ((c & 7) << 1);
 }
 
 // T[r0 + j][k0 + 8g .. 8g+7] (see frag_rk)
-template <int W>
+template <int W, int KIND = 0>
 __device__ __forceinline__ bf16x8 frag_rk_s(const char* T, int r0, int k0) {
   const int l = lane_id();
-  return *reinterpret_cast<const bf16x8*>(T + soff<W>(r0 + (l & 15), k0 + 8 * (l >> 4)));
+  return *reinterpret_cast<const bf16x8*>(T + soff<W, KIND>(r0 + (l & 15), k0 + 8 * (l >> 4)));
 }
 
 // T[k0 + 8g .. 8g+7][c0 + j] by transposed reads (see frag_kc)
-template <int W>
+template <int W, int KIND = 0>
 __device__ __forceinline__ bf16x8 frag_kc_s(const char* T, int c0, int k0) {
   const int l = lane_id();
   const int g = l >> 4, q = l & 15;
   const int r = k0 + 8 * g + (q >> 2), c = c0 + 4 * (q & 3);
-  const char* p0 = T + soff<W>(r, c);
-  const char* p1 = T + soff<W>(r + 4, c);
+  const char* p0 = T + soff<W, KIND>(r, c);
+  const char* p1 = T + soff<W, KIND>(r + 4, c);
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(p0)));
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(p1)));
   const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
@@ -106,14 +112,19 @@ __device__ __forceinline__ bf16x8 frag_kc_s(const char* T, int c0, int k0) {
   return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <int W>
+template <int W, int KIND = 0>
 __device__ __forceinline__ void st4_s(char* T, int r, int c, float a, float b, float d, float e) {
-  *reinterpret_cast<uint2*>(T + soff<W>(r, c)) = pack4_bf16(a, b, d, e);
+  *reinterpret_cast<uint2*>(T + soff<W, KIND>(r, c)) = pack4_bf16(a, b, d, e);
 }
 
 // one 16-byte direct-to-LDS load per lane: lane l's bytes land at lds + 16 l
 __device__ __forceinline__ void dma16(const void* src, char* lds) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)((lds_char_t*)lds), 16, 0, 0);
+}
+
+// a 4-byte direct-to-LDS load: used to pull a cache line into L2 ahead of time
+__device__ __forceinline__ void dma4(const void* src, char* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)((lds_char_t*)lds), 4, 0, 0);
 }
 
 // Workgroup barrier that orders LDS traffic only: each wave's LDS reads and
@@ -163,14 +174,16 @@ struct ChainCfg {
   static constexpr int bSlot = bX3 + (RAW ? 2 * XB : 0);
   static constexpr int bdS = bSlot + 3 * SLOT;                     // 16 x D state-gradient slice
   static constexpr int bdU = bdS + 16 * D * 2;                     // 16 x 64: dU^T
-  static constexpr int bEnd = bdU + 16 * C * 2;
+  static constexpr int bPF = bdU + 16 * C * 2;                     // 256 B sink of the L2 prefetches
+  static constexpr int bEnd = bPF + 256;
   // forward role
   static constexpr int fW = 0, fK = TB, fUp = 2 * TB, bufF = fUp + XB;
   static constexpr int fSlot = 2 * bufF;
   static constexpr int fS = fSlot + 3 * SLOT;                      // 16 x D state slice
   static constexpr int fU = fS + 16 * D * 2;                       // 16 x 64: U^T as the MFMA takes it
   static constexpr int fUo = fU + 16 * C * 2;                      // RAW: unscaled U^T, to be stored
-  static constexpr int fEnd = fUo + (RAW ? 16 * C * 2 : 0);
+  static constexpr int fPF = fUo + (RAW ? 16 * C * 2 : 0);
+  static constexpr int fEnd = fPF + 256;
   static constexpr int bytes = bEnd > fEnd ? bEnd : fEnd;
   // mover loads per wave per chunk: first-window set A, second-window set B
   // (set B carries the small data of the chunk after its own)
@@ -179,7 +192,7 @@ struct ChainCfg {
   static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 : 2) * NJ + nSb;
   static constexpr int fwdA = NJ + 1, fwdB = NJ + nSf;
   static_assert(bytes <= 160 * 1024, "LDS budget");
-  static_assert(2 * bwdA + bwdB < 64 && 2 * fwdA + fwdB < 64, "vmcnt range");
+  static_assert(2 * bwdA + bwdB + 3 < 64 && 2 * fwdA + fwdB + 3 < 64, "vmcnt range");
 };
 
 struct ChunkGeo {
@@ -208,7 +221,7 @@ struct MoverLane {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int pos = mw * (TB / 4) + (j < NJ ? j : 0) * 1024 + 16 * l;
-      const int row = pos / RB, lp = ((pos % RB) >> 4) ^ swz<D>(row);
+      const int row = pos / RB, lp = ((pos % RB) >> 4) ^ swz<D, 0>(row);
       rD[j] = row;
       pD[j] = lp << 4;
       tD[j] = row * RB + (lp << 4);
@@ -216,7 +229,7 @@ struct MoverLane {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int pos = mw * 2048 + j * 1024 + 16 * l;
-      const int row = pos >> 7, lp = ((pos & 127) >> 4) ^ swz<64>(row);
+      const int row = pos >> 7, lp = ((pos & 127) >> 4) ^ swz<64, 0>(row);
       tP[j] = row * 128 + (lp << 4);
     }
     const int pos = mw * 512 + 16 * (l & 31);
@@ -264,7 +277,7 @@ __device__ __forceinline__ void move_small(const Params& p, const SeqEntry& se, 
     const int l = lane_id();
     if (with_dO && l < 32) {
       // rows 16 mw .. 16 mw + 15 of the 64 x 16 slice, two pieces a row
-      const int row = 16 * mw + (l >> 1);
+      const int row = prow<16>(16 * mw + (l >> 1));   // logical row landing at physical row 16 mw + l/2
       const char* src = reinterpret_cast<const char*>(p.dO) +
                         (tok(cg.t0 + min(row, cg.len - 1), p.H, h) * D + v0) * 2 + (l & 1) * 16;
       dma16(src, slot + Cf::sDO + mw * 512);
@@ -328,12 +341,73 @@ __device__ __forceinline__ void move_fwd_b(const MoverLane<D>& ml, const Params&
     move_tile<D>(ml, p.Kh + cg.ch * C * D, buf + Cf::fK, mw);
 }
 
+// L2 prefetch of chunk c, three steps beyond the direct-to-LDS loads: the V
+// slices of one (sequence, head) read the same tiles, so slice sl touches only
+// rows [sl R, (sl+1) R) of them (R = 64 / slices), mover wave mw a quarter of
+// those, one 4-byte load per 64-byte sector into a sink that is never read.
+template <int D, typename TIO, int GATE, bool BWD>
+__device__ __forceinline__ void prefetch_chunk(const Params& p, const SeqEntry& se, int h, int c, int sl, int mw,
+                                               char* sink) {
+  using Cf = ChainCfg<D, TIO, GATE>;
+  constexpr int ns = D / 16, R = C / ns, RW = R / 4;
+  constexpr int LB = 64;                                   // bytes per prefetch load
+  constexpr int LPR = (2 * D) / LB;                        // loads per row of a 64 x D bf16 tile
+  constexpr int DOL = int(D * sizeof(TIO)) / LB;           // loads per dO row of one head
+  constexpr int NP = 128 / LB;                             // loads per P row
+  constexpr int NT = BWD ? (Cf::MAT ? 4 : 3) : 2;          // tiles with D-wide rows
+  constexpr int N1 = NT * RW * LPR, N2 = N1 + (BWD ? RW * NP : 0), N3 = N2 + (BWD ? RW * DOL : RW * LPR);
+  static_assert(N3 + 512 / LB <= 64, "one prefetch load per wave");
+  const ChunkGeo cg = geo(p, se, h, c);
+  const int l = lane_id(), r0 = sl * R + mw * RW;
+  const char* a = nullptr;
+  auto tok_row = [&](const void* base, int row, int bytes_per_elem) {
+    return static_cast<const char*>(base) +
+           (tok(cg.t0 + min(row, cg.len - 1), p.H, h) * D) * bytes_per_elem;
+  };
+  auto tile_row = [&](const uint16_t* base, int row) {
+    return reinterpret_cast<const char*>(base + (cg.ch * C + row) * D);
+  };
+  if (l < N1) {
+    const int t = l / (RW * LPR), rem = l % (RW * LPR), row = r0 + rem / LPR, line = rem % LPR;
+    const char* rb;
+    if constexpr (BWD) {
+      if constexpr (Cf::RAW)
+        rb = t == 0 ? tok_row(p.k, row, 2) : t == 1 ? tok_row(p.q, row, 2) : tile_row(p.W, row);
+      else
+        rb = t == 0 ? tile_row(p.Kh, row) : t == 1 ? tile_row(p.Qh, row) : t == 2 ? tile_row(p.Ql, row) : tile_row(p.W, row);
+    } else {
+      if constexpr (Cf::RAW)
+        rb = t == 0 ? tile_row(p.W, row) : tok_row(p.k, row, 2);
+      else
+        rb = t == 0 ? tile_row(p.W, row) : tile_row(p.Kh, row);
+    }
+    a = rb + line * LB;
+  } else if (l < N2) {
+    a = reinterpret_cast<const char*>(p.P + (cg.ch * C + r0 + (l - N1) / NP) * C) + ((l - N1) % NP) * LB;
+  } else if (l < N3) {
+    if constexpr (BWD) {
+      const int i = l - N2;
+      a = tok_row(p.dO, r0 + i / DOL, int(sizeof(TIO))) + (i % DOL) * LB;
+    } else {
+      const int i = l - N2;
+      a = tile_row(p.Up, r0 + i / LPR) + (i % LPR) * LB;
+    }
+  } else if (sl == 0 && mw == 0 && l < N3 + 512 / LB) {
+    const int i = l - N3;
+    if constexpr (GATE == 1)
+      a = reinterpret_cast<const char*>(p.edec + cg.ch * D) + (i * LB) % (D * 4);
+    else
+      a = reinterpret_cast<const char*>(p.fac + cg.ch * 2 * C) + i * LB;
+  }
+  if (a) dma4(a, sink);
+}
+
 // ---------------------------------------------------------------------------
 // converter (wave 4)
 // ---------------------------------------------------------------------------
 // Copies a 16-row slice tile (W columns, swizzled in LDS) to 16 contiguous global
 // rows with 16-byte stores.
-template <int W>
+template <int W, int KIND = 0>
 __device__ __forceinline__ void store_slice(const char* T, uint16_t* dst) {
   constexpr int BYTES = 16 * W * 2;
   const int l = lane_id();
@@ -341,7 +415,7 @@ __device__ __forceinline__ void store_slice(const char* T, uint16_t* dst) {
   for (int i = 0; i < BYTES / 1024; ++i) {
     const int pos = i * 1024 + 16 * l;
     const int row = pos / (2 * W), piece = (pos % (2 * W)) >> 4;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(T + soff<W>(row, piece * 8));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(T + soff<W, KIND>(row, piece * 8));
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst) + pos) = v;
   }
 }
@@ -386,10 +460,11 @@ struct LoRegs {
       l0[e] = to_bf16(xa - float(h0[e]));
       l1[e] = to_bf16(xb - float(h1[e]));
     }
-    *reinterpret_cast<bf16x8*>(x1 + l * 32) = h0;
-    *reinterpret_cast<bf16x8*>(x1 + l * 32 + 16) = h1;
-    *reinterpret_cast<bf16x8*>(x2 + l * 32) = l0;
-    *reinterpret_cast<bf16x8*>(x2 + l * 32 + 16) = l1;
+    const int o = prow<16>(l) * 32;
+    *reinterpret_cast<bf16x8*>(x1 + o) = h0;
+    *reinterpret_cast<bf16x8*>(x1 + o + 16) = h1;
+    *reinterpret_cast<bf16x8*>(x2 + o) = l0;
+    *reinterpret_cast<bf16x8*>(x2 + o + 16) = l1;
   }
 
   __device__ __forceinline__ void store_dec(float* dst) const {
@@ -408,8 +483,9 @@ template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void convert_raw(const char* slot, char* x2, char* x3) {
   using Cf = ChainCfg<D, TIO, GATE>;
   const int l = lane_id();
-  const u32x4 r0 = *reinterpret_cast<const u32x4*>(slot + Cf::sDO + l * 32);
-  const u32x4 r1 = *reinterpret_cast<const u32x4*>(slot + Cf::sDO + l * 32 + 16);
+  const int o = prow<16>(l) * 32;
+  const u32x4 r0 = *reinterpret_cast<const u32x4*>(slot + Cf::sDO + o);
+  const u32x4 r1 = *reinterpret_cast<const u32x4*>(slot + Cf::sDO + o + 16);
   const float fq = reinterpret_cast<const float*>(slot + Cf::sFac)[l];
   float a[8], b[8];
   IO<bf16>::unpack8(r0, a);
@@ -423,10 +499,10 @@ __device__ __forceinline__ void convert_raw(const char* slot, char* x2, char* x3
     l0[e] = to_bf16(ya - float(h0[e]));
     l1[e] = to_bf16(yb - float(h1[e]));
   }
-  *reinterpret_cast<bf16x8*>(x2 + l * 32) = h0;
-  *reinterpret_cast<bf16x8*>(x2 + l * 32 + 16) = h1;
-  *reinterpret_cast<bf16x8*>(x3 + l * 32) = l0;
-  *reinterpret_cast<bf16x8*>(x3 + l * 32 + 16) = l1;
+  *reinterpret_cast<bf16x8*>(x2 + o) = h0;
+  *reinterpret_cast<bf16x8*>(x2 + o + 16) = h1;
+  *reinterpret_cast<bf16x8*>(x3 + o) = l0;
+  *reinterpret_cast<bf16x8*>(x3 + o + 16) = l1;
 }
 
 // the decay of this lane's four accumulator rows j = 16 jb + 4 g .. +3
@@ -493,7 +569,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) u[i] = bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]) - au[i];
       if constexpr (Cf::RAW) {
-        st4_s<C>(Uo, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
+        st4_s<C, 1>(Uo, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
         const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C +
                                                           16 * w + 4 * g);
         u[0] *= f.x;
@@ -501,7 +577,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
         u[2] *= f.z;
         u[3] *= f.w;
       }
-      st4_s<C>(Ut, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
+      st4_s<C, 1>(Ut, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
       chain_barrier();   // B2
       // S_{k+1}^T = Diag(e^GamC) S_k^T + Khat^T U
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
@@ -510,7 +586,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
         const int jb = w * NJW + x;
         f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
 #pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc_s<D>(Fb + Cf::fK, 16 * jb, k0), frag_rk_s<C>(Ut, 0, k0), a);
+        for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc_s<D>(Fb + Cf::fK, 16 * jb, k0), frag_rk_s<C, 1>(Ut, 0, k0), a);
         acc[x] = a;
       }
     }
@@ -536,7 +612,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       chain_barrier();   // B1
       store_slice<D>(Ss, p.S + (ch * D + v0) * D);
       chain_barrier();   // B2
-      store_slice<C>(Uo, p.U + (ch * D + v0) * C);
+      store_slice<C, 1>(Uo, p.U + (ch * D + v0) * C);
       if constexpr (Cf::LO) {
         R.store_dec(reinterpret_cast<float*>(slot(k + 1) + Cf::sDec));
         R.load(p, se, h, chunk(k + 2), v0, false);
@@ -553,17 +629,19 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
     move_small<D, TIO, GATE>(p, se, h, chunk(1), v0, slot(1), mw, false);
     move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), v0, smem + Cf::bufF, mw);
-    wait_vm<Cf::fwdA + Cf::fwdB + Cf::fwdA>();
+    for (int c = 2; c < 5; ++c) prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(c), sl, mw, smem + Cf::fPF);
+    wait_vm<Cf::fwdA + Cf::fwdB + Cf::fwdA + 3>();
     chain_barrier();   // B0
-    wait_vm<Cf::fwdB + Cf::fwdA>();
+    wait_vm<Cf::fwdB + Cf::fwdA + 3>();
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
       move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0, slot(k + 2), mw, false);
-      wait_vm<Cf::fwdA + Cf::fwdB>();
+      wait_vm<Cf::fwdA + 1 + Cf::fwdB>();
       chain_barrier();   // B2
       move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0, smem + (k & 1) * Cf::bufF, mw);
-      wait_vm<Cf::fwdB + Cf::fwdA>();
+      prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(k + 5), sl, mw, smem + Cf::fPF);
+      wait_vm<Cf::fwdB + Cf::fwdA + 2>();
     }
     wait_vm<0>();
   }
@@ -630,7 +708,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       } else {
         ad += ak;
       }
-      st4_s<C>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
+      st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
       chain_barrier();   // B2
       // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
@@ -650,7 +728,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
             a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, k0), bh, a);
             if constexpr (Cf::LO) a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
           }
-          aw = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C>(dUt, 0, k0), aw);
+          aw = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C, 1>(dUt, 0, k0), aw);
         }
         acc[x] = a - aw;
       }
@@ -680,7 +758,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       chain_barrier();   // B1
       store_slice<D>(dSl, p.dS + (ch * D + v0) * D);
       chain_barrier();   // B2
-      store_slice<C>(dUt, p.dU + (ch * D + v0) * C);
+      store_slice<C, 1>(dUt, p.dU + (ch * D + v0) * C);
       if constexpr (Cf::RAW) {
         convert_raw<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + nb * Cf::XB, smem + Cf::bX3 + nb * Cf::XB);
       } else if constexpr (Cf::LO) {
@@ -700,17 +778,19 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
     move_small<D, TIO, GATE>(p, se, h, chunk(1), v0, slot(1), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), smem + Cf::bufB, mw);
-    wait_vm<Cf::bwdA + Cf::bwdB + Cf::bwdA>();
+    for (int c = 2; c < 5; ++c) prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(c), sl, mw, smem + Cf::bPF);
+    wait_vm<Cf::bwdA + Cf::bwdB + Cf::bwdA + 3>();
     chain_barrier();   // B0
-    wait_vm<Cf::bwdB + Cf::bwdA>();
+    wait_vm<Cf::bwdB + Cf::bwdA + 3>();
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
       move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0, slot(k + 2), mw, true);
-      wait_vm<Cf::bwdA + Cf::bwdB>();
+      wait_vm<Cf::bwdA + 1 + Cf::bwdB>();
       chain_barrier();   // B2
       move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
-      wait_vm<Cf::bwdB + Cf::bwdA>();
+      prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(k + 5), sl, mw, smem + Cf::bPF);
+      wait_vm<Cf::bwdB + Cf::bwdA + 2>();
     }
     wait_vm<0>();
   }
