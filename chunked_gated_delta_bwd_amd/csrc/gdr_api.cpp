@@ -93,6 +93,14 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.Kh = take(mat * H * NC * C * K * 2);
   L.Qh = take(mat * H * NC * C * K * 2);
   L.Ql = take(mat * H * NC * C * K * 2);
+  const size_t kda = s->gate == GDR_GATE_CHANNEL ? 1 : 0;
+  L.Mk = take(kda * H * NC * C * C * 2);
+  L.pdA = take(kda * H * NC * 4);
+  L.pddt = take(kda * H * NC * K * 4);
+  L.Uplo = take(kda * H * NC * C * V * 2);
+  L.Ulo = take(kda * H * NC * C * V * 2);
+  L.Slo = take(kda * H * NC * V * K * 2);
+  L.dSlo = take(kda * H * NC * V * K * 2);
   L.total = off;
   return L;
 }
@@ -203,6 +211,13 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   p.Kh = reinterpret_cast<uint16_t*>(w + L.Kh);
   p.Qh = reinterpret_cast<uint16_t*>(w + L.Qh);
   p.Ql = reinterpret_cast<uint16_t*>(w + L.Ql);
+  p.Mk = reinterpret_cast<uint16_t*>(w + L.Mk);
+  p.pdA = reinterpret_cast<float*>(w + L.pdA);
+  p.pddt = reinterpret_cast<float*>(w + L.pddt);
+  p.Uplo = reinterpret_cast<uint16_t*>(w + L.Uplo);
+  p.Ulo = reinterpret_cast<uint16_t*>(w + L.Ulo);
+  p.Slo = reinterpret_cast<uint16_t*>(w + L.Slo);
+  p.dSlo = reinterpret_cast<uint16_t*>(w + L.dSlo);
   return p;
 }
 
@@ -231,37 +246,46 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
   const gdr::WsLayout L = layout(s, NC);
   if ((st = check_ws(L, ws, ws_bytes)) != GDR_OK) return st;
 
-  if (s->gate == GDR_GATE_CHANNEL)
-    return fail(GDR_EUNSUPPORTED, "the per-channel gate is not implemented yet");
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if ((st = upload_tables(s, L, ws, hs)) != GDR_OK) return st;
   gdr::Params p = make_params(s, L, in, ws);
   p.ht = ht;
   if (stage != kFwd) set_grads(p, dO, dht, gr);
 
+  const bool kda = s->gate == GDR_GATE_CHANNEL;
+  auto prep = [&]() { return kda ? gdr::launch_kda(p, 0, stream) : gdr::launch_prep(p, stream); };
+  auto grads = [&]() { return kda ? gdr::launch_kda(p, 1, stream) : gdr::launch_grads(p, stream); };
+  auto finish = [&]() {
+    if (!kda) return gdr::launch_finish(p, stream);
+    const int e = gdr::launch_kda(p, 2, stream);
+    return e ? e : gdr::launch_kda(p, 3, stream);
+  };
   if (only >= 0) {
     switch (only) {
-      case GDR_STAGE_PREP: return NC > 0 ? hip_status(gdr::launch_prep(p, stream), "prep kernel") : GDR_OK;
+      case GDR_STAGE_PREP: return NC > 0 ? hip_status(prep(), "prep kernel") : GDR_OK;
       case GDR_STAGE_CHAIN_FWD: return hip_status(gdr::launch_chain(p, gdr::kChainFwd, stream), "chain kernel");
       case GDR_STAGE_CHAIN_BWD: return hip_status(gdr::launch_chain(p, gdr::kChainBwd, stream), "chain kernel");
       case GDR_STAGE_CHAIN_BOTH: return hip_status(gdr::launch_chain(p, gdr::kChainBoth, stream), "chain kernel");
-      case GDR_STAGE_GRADS: return NC > 0 ? hip_status(gdr::launch_grads(p, stream), "gradient kernel") : GDR_OK;
+      case GDR_STAGE_GRADS: return NC > 0 ? hip_status(grads(), "gradient kernel") : GDR_OK;
       case GDR_STAGE_FINISH:
-        return NC > 0 ? hip_status(gdr::launch_finish(p, stream), "prepare-backward kernel") : GDR_OK;
+        if (NC > 0) return hip_status(finish(), "prepare-backward kernel");
+        return kda ? hip_status(gdr::launch_zero_params(p, stream), "zero kernel") : GDR_OK;
       default: return fail(GDR_EINVAL, "unknown stage %d", only);
     }
   }
   if (stage != kBwd && NC > 0) {
-    if ((st = hip_status(gdr::launch_prep(p, stream), "prep kernel")) != GDR_OK) return st;
-  }
-  if (stage != kFwd && s->gate == GDR_GATE_CHANNEL) {
-    if ((st = hip_status(gdr::launch_zero_params(p, stream), "zero kernel")) != GDR_OK) return st;
+    if ((st = hip_status(prep(), "prep kernel")) != GDR_OK) return st;
   }
   const int mode = stage == kFwd ? gdr::kChainFwd : stage == kBwd ? gdr::kChainBwd : gdr::kChainBoth;
   if ((st = hip_status(gdr::launch_chain(p, mode, stream), "chain kernel")) != GDR_OK) return st;
-  if (stage != kFwd && NC > 0) {
-    if ((st = hip_status(gdr::launch_grads(p, stream), "gradient kernel")) != GDR_OK) return st;
-    if ((st = hip_status(gdr::launch_finish(p, stream), "prepare-backward kernel")) != GDR_OK) return st;
+  if (stage != kFwd) {
+    if (NC > 0) {
+      if ((st = hip_status(grads(), "gradient kernel")) != GDR_OK) return st;
+      if ((st = hip_status(finish(), "prepare-backward kernel")) != GDR_OK) return st;
+    } else if (kda) {
+      // no tokens: the per-head parameter gradients are zero
+      if ((st = hip_status(gdr::launch_zero_params(p, stream), "zero kernel")) != GDR_OK) return st;
+    }
   }
   return GDR_OK;
 }

@@ -117,6 +117,9 @@ __device__ __forceinline__ void st4_s(char* T, int r, int c, float a, float b, f
   *reinterpret_cast<uint2*>(T + soff<W, KIND>(r, c)) = pack4_bf16(a, b, d, e);
 }
 
+// x - bf16(x): the low part of a two-part bf16 value
+__device__ __forceinline__ float lo_part(float x) { return x - float(to_bf16(x)); }
+
 // one 16-byte direct-to-LDS load per lane: lane l's bytes land at lds + 16 l
 __device__ __forceinline__ void dma16(const void* src, char* lds) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)((lds_char_t*)lds), 16, 0, 0);
@@ -154,6 +157,7 @@ struct ChainCfg {
   static constexpr bool LO = std::is_same<TIO, float>::value;  // fp32 inputs: dO split in two parts
   static constexpr bool MAT = GATE == 1 || LO;                 // materialised Khat / Qbar tiles
   static constexpr bool RAW = !MAT;                            // raw q, k rows and row factors
+  static constexpr bool SPLIT = GATE == 1;   // U', U, S, dS also carried as bf16 high + low parts
   static constexpr int DG = GATE == 1 ? D : 16;    // decay floats per slot (scalar: a 4-float copy per mover)
   static constexpr int TB = C * D * 2;             // one 64 x D bf16 tile
   static constexpr int PB = C * C * 2;             // the 64 x 64 P tile
@@ -177,12 +181,14 @@ struct ChainCfg {
   static constexpr int bPF = bdU + 16 * C * 2;                     // 256 B sink of the L2 prefetches
   static constexpr int bEnd = bPF + 256;
   // forward role
-  static constexpr int fW = 0, fK = TB, fUp = 2 * TB, bufF = fUp + XB;
+  static constexpr int fW = 0, fK = TB, fUp = 2 * TB, fUpl = fUp + XB, bufF = fUpl + (SPLIT ? XB : 0);
   static constexpr int fSlot = 2 * bufF;
   static constexpr int fS = fSlot + 3 * SLOT;                      // 16 x D state slice
   static constexpr int fU = fS + 16 * D * 2;                       // 16 x 64: U^T as the MFMA takes it
   static constexpr int fUo = fU + 16 * C * 2;                      // RAW: unscaled U^T, to be stored
-  static constexpr int fPF = fUo + (RAW ? 16 * C * 2 : 0);
+  static constexpr int fUl = fUo + (RAW ? 16 * C * 2 : 0);         // SPLIT: low part of U^T
+  static constexpr int fSl = fUl + (SPLIT ? 16 * C * 2 : 0);       // SPLIT: low part of the state slice
+  static constexpr int fPF = fSl + (SPLIT ? 16 * D * 2 : 0);
   static constexpr int fEnd = fPF + 256;
   static constexpr int bytes = bEnd > fEnd ? bEnd : fEnd;
   // mover loads per wave per chunk: first-window set A, second-window set B
@@ -190,7 +196,7 @@ struct ChainCfg {
   static constexpr int nSb = LO ? 0 : (RAW ? 3 : 2);   // dO, fac, decay
   static constexpr int nSf = LO ? 0 : (RAW ? 2 : 1);   // fac, decay
   static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 : 2) * NJ + nSb;
-  static constexpr int fwdA = NJ + 1, fwdB = NJ + nSf;
+  static constexpr int fwdA = NJ + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(2 * bwdA + bwdB + 3 < 64 && 2 * fwdA + fwdB + 3 < 64, "vmcnt range");
 };
@@ -328,6 +334,10 @@ __device__ __forceinline__ void move_fwd_a(const MoverLane<D>& ml, const Params&
   const ChunkGeo cg = geo(p, se, h, c);
   move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::fW, mw);
   if (lane_id() < 32) dma16(reinterpret_cast<const char*>(p.Up + cg.ch * C * D + v0) + ml.up, buf + Cf::fUp + mw * 512);
+  if constexpr (Cf::SPLIT) {
+    if (lane_id() < 32)
+      dma16(reinterpret_cast<const char*>(p.Uplo + cg.ch * C * D + v0) + ml.up, buf + Cf::fUpl + mw * 512);
+  }
 }
 
 template <int D, typename TIO, int GATE>
@@ -558,6 +568,9 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
         st4_s<D>(Ss, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+        if constexpr (Cf::SPLIT)
+          st4_s<D>(smem + Cf::fSl, jj, j, lo_part(acc[x][0]), lo_part(acc[x][1]), lo_part(acc[x][2]),
+                   lo_part(acc[x][3]));
       }
       chain_barrier();   // B1
       // U = U' - W S^T, rows 16w.., columns of this slice
@@ -568,6 +581,12 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       float u[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) u[i] = bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]) - au[i];
+      if constexpr (Cf::SPLIT) {
+        const uint16_t* Upl = reinterpret_cast<const uint16_t*>(Fb + Cf::fUpl);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] += bf16_bits_to_f32(Upl[(16 * w + 4 * g + i) * 16 + jj]);
+        st4_s<C, 1>(smem + Cf::fUl, jj, 16 * w + 4 * g, lo_part(u[0]), lo_part(u[1]), lo_part(u[2]), lo_part(u[3]));
+      }
       if constexpr (Cf::RAW) {
         st4_s<C, 1>(Uo, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
         const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C +
@@ -611,8 +630,10 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       const int64_t ch = int64_t(h) * p.NC + chunk(k);
       chain_barrier();   // B1
       store_slice<D>(Ss, p.S + (ch * D + v0) * D);
+      if constexpr (Cf::SPLIT) store_slice<D>(smem + Cf::fSl, p.Slo + (ch * D + v0) * D);
       chain_barrier();   // B2
       store_slice<C, 1>(Uo, p.U + (ch * D + v0) * C);
+      if constexpr (Cf::SPLIT) store_slice<C, 1>(smem + Cf::fUl, p.Ulo + (ch * D + v0) * C);
       if constexpr (Cf::LO) {
         R.store_dec(reinterpret_cast<float*>(slot(k + 1) + Cf::sDec));
         R.load(p, se, h, chunk(k + 2), v0, false);
@@ -689,6 +710,9 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
         st4_s<D>(dSl, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+        if constexpr (Cf::SPLIT)   // no LDS left for a low tile: stored directly
+          st_bf16x4(p.dSlo + (int64_t(h) * p.NC + chunk(k)) * D * D + (v0 + jj) * D + j, lo_part(acc[x][0]),
+                    lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
       }
       chain_barrier();   // B1
       // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice

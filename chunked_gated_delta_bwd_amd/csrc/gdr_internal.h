@@ -59,6 +59,16 @@ struct WsLayout {
   size_t Kh = 0;     // bf16 [H][NC][64][K]: Khat = kn e^(GamC - Gam)
   size_t Qh = 0;     // bf16 [H][NC][64][K]: Qbar = scale qn e^Gam, high part
   size_t Ql = 0;     // bf16 [H][NC][64][K]: Qbar low part
+  // per-channel gate only
+  size_t Mk = 0;     // bf16 [H][NC][64][64]: M = Kn Kn^T weighted by the per-channel decay
+  size_t pdA = 0;    // fp32 [H][NC]:    per-chunk partial sums of dA_log
+  size_t pddt = 0;   // fp32 [H][NC][K]: per-chunk partial sums of ddt_bias
+  // per-channel gate only: low bf16 parts (x = hi + lo) of U', U, S and dS, for
+  // the gate gradient, whose per-head sums cancel strongly
+  size_t Uplo = 0;   // bf16 [H][NC][64][V]
+  size_t Ulo = 0;    // bf16 [H][NC][V][64]
+  size_t Slo = 0;    // bf16 [H][NC][V][K]
+  size_t dSlo = 0;   // bf16 [H][NC][V][K]
   size_t total = 0;
 };
 
@@ -80,6 +90,9 @@ struct Params {
   float *fac, *edec;
   uint16_t *A, *P, *W, *Up, *U, *S, *dS, *dU;   // bf16 bit patterns
   uint16_t *Kh, *Qh, *Ql;                        // materialised operand tiles (see WsLayout)
+  uint16_t* Mk;                                  // per-channel gate only
+  float *pdA, *pddt;
+  uint16_t *Uplo, *Ulo, *Slo, *dSlo;             // per-channel gate only: low parts
   float *dqn, *dkn, *dgam, *dgamc, *dbeta;
 };
 
@@ -92,6 +105,9 @@ int launch_chain(const Params& p, int mode, void* stream);
 int launch_grads(const Params& p, void* stream);
 int launch_finish(const Params& p, void* stream);
 int launch_zero_params(const Params& p, void* stream);
+// Per-channel gate kernels (gdr_kda.hip): stage 0 prologue, 1 gradients,
+// 2 prepare-backward, 3 dA_log / ddt_bias reduction.
+int launch_kda(const Params& p, int stage, void* stream);
 const char* hip_error_string(int err);
 
 }  // namespace gdr

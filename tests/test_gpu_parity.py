@@ -90,3 +90,57 @@ def test_workload_t32768_sampled_heads(H):
     inp = synth.generate(synth.workload(f"gdn_bf16_t32768_h{H}_d128"))
     got = gpu_run(inp)
     _check(inp, got, f"gdn_t32768_h{H}", heads=[0, H - 1])
+
+
+# ---------------------------------------------------------------------------
+# per-channel gate (KDA)
+# ---------------------------------------------------------------------------
+SMALL_KDA = [
+    ("kda_f32_t128_h2_d64", synth.Spec("kf", 1, "f32", H=2, K=64, V=64, B=1, T=128, seed=41)),
+    ("kda_bf16_varlen_edges_d128",
+     synth.Spec("ke", 1, "bf16", H=3, K=128, V=128, lengths=[1, 63, 64, 65, 0, 200], h0_std=0.1,
+                dht_std=0.1, seed=42)),
+    ("kda_f32_b2_t100_d128", synth.Spec("kg", 1, "f32", H=2, K=128, V=128, B=2, T=100, h0_std=0.2,
+                                        dht_std=0.2, seed=43)),
+    ("kda_bf16_b1_t300_d64", synth.Spec("kh", 1, "bf16", H=4, K=64, V=64, B=1, T=300, h0_std=0.5,
+                                        dht_std=0.5, seed=44)),
+]
+
+
+@pytest.mark.parametrize("name,spec", SMALL_KDA, ids=[s[0] for s in SMALL_KDA])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_kda_small_against_oracle(name, spec, mode):
+    log(f"case {name} mode {mode}")
+    inp = synth.generate(spec)
+    got = gpu_run(inp, mode=mode)
+    _check(inp, got, f"{name}/{mode}")
+
+
+def test_kda_chunk_boundary_states():
+    spec = synth.Spec("ks", 1, "bf16", H=2, K=128, V=128, lengths=[130, 64, 5], h0_std=0.2, dht_std=0.2,
+                      seed=45)
+    inp = synth.generate(spec)
+    got = gpu_run(inp, exports=True)
+    ref = oracle.run(inp, exports=True)
+    compare(got, ref, ("S_chunk", "dS_chunk"), 1e-2, "kda chunk states")
+
+
+def test_kda_repeat_is_deterministic():
+    inp = synth.generate(synth.Spec("kr", 1, "bf16", H=2, K=128, V=128, B=2, T=256, seed=46))
+    a = gpu_run(inp)
+    b = gpu_run(inp)
+    for key in TOKEN_GRADS + FP32_GRADS:
+        assert (a[key] == b[key]).all(), key
+
+
+def test_kda_workload_t8192_h16():
+    inp = synth.generate(synth.workload("kda_bf16_t8192_h16_d128"))
+    got = gpu_run(inp)
+    _check(inp, got, "kda_bf16_t8192_h16_d128")
+
+
+@pytest.mark.parametrize("H", [16, 32])
+def test_kda_workload_t32768_sampled_heads(H):
+    inp = synth.generate(synth.workload(f"kda_bf16_t32768_h{H}_d128"))
+    got = gpu_run(inp)
+    _check(inp, got, f"kda_t32768_h{H}", heads=[0, H - 1])
