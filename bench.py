@@ -30,23 +30,28 @@ from chunked_gated_delta_bwd_amd import binding as B  # noqa: E402
 from chunked_gated_delta_bwd_amd import synth  # noqa: E402
 
 METRIC = "gated-delta-rule bwd tokens/s + ms/bwd at T=32k,H=16,D=128 bf16; MFMA %"
-KERNEL_SOURCE = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc", "gdr_kernels.hip")
+CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 # HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by a
 # 1 GiB copy; profiles/gdn_t32768_h16_d128.md), valid only for the kernel
-# source they were taken on: (workload, stage, sha256 prefix) -> bytes.
+# sources they were taken on: (workload, stage, sha256 prefix) -> bytes.
 MEASURED_TRAFFIC = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "1ebc4b235775"): 0.845e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "1ebc4b235775"): 1.822e9,
-    ("gdn_bf16_t32768_h16_d128", "grads", "1ebc4b235775"): 2.132e9,
-    ("gdn_bf16_t32768_h16_d128", "finish", "1ebc4b235775"): 1.136e9,
+    ("gdn_bf16_t32768_h16_d128", "prep", "3583a19fdd6c"): 0.850e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "3583a19fdd6c"): 1.824e9,
+    ("gdn_bf16_t32768_h16_d128", "grads", "3583a19fdd6c"): 2.123e9,
+    ("gdn_bf16_t32768_h16_d128", "finish", "3583a19fdd6c"): 1.136e9,
 }
 
 
 def kernel_source_hash() -> str:
+    """sha256 prefix over every kernel source (sorted by name)."""
     import hashlib
 
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:12]
+    hsh = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                hsh.update(name.encode() + b"\0" + f.read())
+    return hsh.hexdigest()[:12]
 C = 64
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -136,7 +141,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=synth.HEADLINE, choices=synth.WORKLOADS)
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--stage-iters", type=int, default=10)
     ap.add_argument("--all-stages", action="store_true",
@@ -208,6 +213,7 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
     roof["traffic"] = MEASURED_TRAFFIC.get((args.workload, dom, kernel_source_hash()))
+    roof["source_hash"] = kernel_source_hash()
     roof["kernel"] = dom
     roof["work_per_launch"] = flops if dom != "finish" else nbytes
 
