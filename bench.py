@@ -35,10 +35,6 @@ CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 # 1 GiB copy; profiles/gdn_t32768_h16_d128.md), valid only for the kernel
 # sources they were taken on: (workload, stage, sha256 prefix) -> bytes.
 MEASURED_TRAFFIC = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "3583a19fdd6c"): 0.850e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "3583a19fdd6c"): 1.824e9,
-    ("gdn_bf16_t32768_h16_d128", "grads", "3583a19fdd6c"): 2.123e9,
-    ("gdn_bf16_t32768_h16_d128", "finish", "3583a19fdd6c"): 1.136e9,
 }
 
 
@@ -85,7 +81,13 @@ def algorithmic_work(inp, stage: str):
         a, b = algorithmic_work(inp, "chain_fwd"), algorithmic_work(inp, "chain_bwd")
         return a[0] + b[0], a[1] + b[1]
     if stage == "grads":
-        b = ch * (2 * D * D * 2 + 2 * C * D * 2 + C * C * 2 + 2 * C * D * 4 + C * gk * 4 + C * 4) + tokens * H * 5 * D * io
+        if inp["gate"] == 0:
+            # fused with the prepare-backward: S, dS, U, dU, A, Gamma, (1/|q|, 1/|k|, beta)
+            # per chunk; q, k, v, dO read and dq, dk, dv, dg, db written per token
+            b = ch * (2 * D * D * 2 + 2 * C * D * 2 + C * C * 2 + C * 4 + 3 * C * 4) + tokens * H * (7 * D * io + 2 * io)
+        else:
+            b = (ch * (2 * D * D * 2 + 2 * C * D * 2 + C * C * 2 + 2 * C * D * 4 + C * gk * 4 + C * 4)
+                 + tokens * H * 5 * D * io)
         return ch * f_grads, b
     if stage == "finish":
         # read q, k, dqn, dkn, rho, dGamma, dbeta, b (and g_raw for KDA); write dq, dk, dg, db
@@ -187,7 +189,11 @@ def main() -> int:
 
     # every kernel alone (the workspace already holds what earlier stages leave)
     kernels = {}
-    stages = [B.GDR_STAGE_PREP, B.GDR_STAGE_CHAIN_BOTH, B.GDR_STAGE_GRADS, B.GDR_STAGE_FINISH]
+    # the scalar gate's prepare-backward runs inside its gradient kernel
+    path = ("prep", "chain_both", "grads") + (("finish",) if inp["gate"] == 1 else ())
+    stages = [B.GDR_STAGE_PREP, B.GDR_STAGE_CHAIN_BOTH, B.GDR_STAGE_GRADS]
+    if inp["gate"] == 1:
+        stages.append(B.GDR_STAGE_FINISH)
     if args.all_stages:
         stages += [B.GDR_STAGE_CHAIN_FWD, B.GDR_STAGE_CHAIN_BWD]
     for stage in stages:
@@ -201,7 +207,6 @@ def main() -> int:
                          "mfma_frac": round(flops / t / 1e9 / PEAK_BF16_TFLOPS, 4) if flops else 0.0,
                          "gbs": round(nbytes / t / 1e6, 1),
                          "hbm_frac": round(nbytes / t / 1e6 / PEAK_HBM_GBS, 4)}
-    path = ("prep", "chain_both", "grads", "finish")
     dom = max(path, key=lambda n: kernels[n]["ms"])
     flops, nbytes = algorithmic_work(inp, dom)
     if dom == "finish":

@@ -73,7 +73,7 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.ctab = take(NC * sizeof(gdr::ChunkEntry));
   L.stab = take(N * sizeof(gdr::SeqEntry));
   L.gam = take(H * NC * C * gk * 4);
-  L.rho = take(H * NC * 2 * C * 4);
+  L.rho = take(H * NC * 3 * C * 4);
   L.fac = take(H * NC * 2 * C * 4);
   L.edec = take(H * NC * (gk == 1 ? 4 : gk) * 4);
   L.A = take(H * NC * C * C * 2);
@@ -84,11 +84,13 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.S = take(H * NC * V * K * 2);
   L.dS = take(H * NC * V * K * 2);
   L.dU = take(H * NC * C * V * 2);
-  L.dqn = take(H * NC * C * K * 4);
-  L.dkn = take(H * NC * C * K * 4);
-  L.dgam = take(H * NC * C * gk * 4);
-  L.dgamc = take(H * NC * gk * 4);
-  L.dbeta = take(H * NC * C * 4);
+  // handed from the gradient kernel to the prepare-backward (per-channel gate only)
+  const size_t sep = s->gate == GDR_GATE_CHANNEL ? 1 : 0;
+  L.dqn = take(sep * H * NC * C * K * 4);
+  L.dkn = take(sep * H * NC * C * K * 4);
+  L.dgam = take(sep * H * NC * C * gk * 4);
+  L.dgamc = take(sep * H * NC * gk * 4);
+  L.dbeta = take(sep * H * NC * C * 4);
   const size_t mat = (s->gate == GDR_GATE_CHANNEL || s->dtype == GDR_F32) ? 1 : 0;
   L.Kh = take(mat * H * NC * C * K * 2);
   L.Qh = take(mat * H * NC * C * K * 2);
@@ -255,8 +257,9 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
   const bool kda = s->gate == GDR_GATE_CHANNEL;
   auto prep = [&]() { return kda ? gdr::launch_kda(p, 0, stream) : gdr::launch_prep(p, stream); };
   auto grads = [&]() { return kda ? gdr::launch_kda(p, 1, stream) : gdr::launch_grads(p, stream); };
+  // the scalar gate's prepare-backward is fused into its gradient kernel
   auto finish = [&]() {
-    if (!kda) return gdr::launch_finish(p, stream);
+    if (!kda) return 0;
     const int e = gdr::launch_kda(p, 2, stream);
     return e ? e : gdr::launch_kda(p, 3, stream);
   };

@@ -75,6 +75,7 @@ template <typename T> struct IO;
 template <> struct IO<bf16> {
   // raw (still packed) register images, so that a prefetch keeps loads in
   // flight and unpacks only where the data is consumed
+  static constexpr int kRaw8Loads = 1;   // global load instructions per Raw8
   typedef u32x4 Raw8;
   typedef unsigned int __attribute__((ext_vector_type(2))) Raw4;
   static __device__ __forceinline__ Raw8 load_raw8(const void* base, int64_t off) {
@@ -131,6 +132,7 @@ template <> struct IO<bf16> {
 };
 
 template <> struct IO<float> {
+  static constexpr int kRaw8Loads = 2;
   struct Raw8 { f32x4 a, b; };
   typedef f32x4 Raw4;
   static __device__ __forceinline__ Raw8 load_raw8(const void* base, int64_t off) {

@@ -37,7 +37,7 @@ struct WsLayout {
   int64_t NC = 0;    // total chunks
   size_t ctab = 0, stab = 0;
   size_t gam = 0;    // fp32 [H][NC][64] or [H][NC][64][K]: in-chunk cumsum of the log decay
-  size_t rho = 0;    // fp32 [H][NC][2][64]: 1/|q|, 1/|k| per row
+  size_t rho = 0;    // fp32 [H][NC][3][64]: 1/|q|, 1/|k|, beta per row (beta 0 past the end)
   size_t fac = 0;    // fp32 [H][NC][2][64]: scalar gate row factors of the recursions,
                      //   fq = scale e^Gam / |q|, fk = e^(GamC - Gam) / |k| (zero past the end)
   size_t edec = 0;   // fp32 [H][NC][4] (value, 3 pad) or [H][NC][K]: chunk decay e^GamC
@@ -103,7 +103,6 @@ enum ChainMode { kChainFwd = 1, kChainBwd = 2, kChainBoth = 3 };
 int launch_prep(const Params& p, void* stream);
 int launch_chain(const Params& p, int mode, void* stream);
 int launch_grads(const Params& p, void* stream);
-int launch_finish(const Params& p, void* stream);
 int launch_zero_params(const Params& p, void* stream);
 // Per-channel gate kernels (gdr_kda.hip): stage 0 prologue, 1 gradients,
 // 2 prepare-backward, 3 dA_log / ddt_bias reduction.

@@ -125,8 +125,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
     *reinterpret_cast<bf16x8*>(Qs + r * PD + c0) = qb;
     *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
     if (tid % TPR == 0) {
-      p.rho[ch * 2 * C + r] = rq;
-      p.rho[ch * 2 * C + C + r] = rk;
+      p.rho[ch * 3 * C + r] = rq;
+      p.rho[ch * 3 * C + C + r] = rk;
     }
   }
   // --- gate and its per-channel cumsum (thread = channel), beta (last wave) ---
@@ -143,7 +143,9 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
     }
   } else if (tid >= kThreads - C) {
     const int r = tid - (kThreads - C);
-    beta_s[r] = (r < len ? 1.f : 0.f) * sigmoidf(IO<TIO>::load1(p.b, tok(t0 + min(r, len - 1), H, h)));
+    const float bt = (r < len ? 1.f : 0.f) * sigmoidf(IO<TIO>::load1(p.b, tok(t0 + min(r, len - 1), H, h)));
+    beta_s[r] = bt;
+    p.rho[ch * 3 * C + 2 * C + r] = bt;
   }
   __syncthreads();
 
@@ -395,9 +397,9 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   float* Gs = reinterpret_cast<float*>(dPl + C * PC); // phase 4: Gamma [r][c]
 
   if (tid < C) {
-    rq_s[tid] = p.rho[ch * 2 * C + tid];
-    rk_s[tid] = p.rho[ch * 2 * C + C + tid];
-    beta_s[tid] = (tid < len ? 1.f : 0.f) * sigmoidf(IO<TIO>::load1(p.b, tok(t0 + min(tid, len - 1), H, h)));
+    rq_s[tid] = p.rho[ch * 3 * C + tid];
+    rk_s[tid] = p.rho[ch * 3 * C + C + tid];
+    beta_s[tid] = p.rho[ch * 3 * C + 2 * C + tid];
   }
   for (int pc = tid; pc < D * C / 8; pc += kThreads) {
     const int v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
@@ -738,7 +740,7 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
     float q[8], k[8], dq[8], dk[8];
     const int64_t o = tok(t0 + min(r, len - 1), H, h) * D + c0;
     const float m = ok ? 1.f : 0.f;
-    const float rq = m * p.rho[ch * 2 * C + r], rk = m * p.rho[ch * 2 * C + C + r];
+    const float rq = m * p.rho[ch * 3 * C + r], rk = m * p.rho[ch * 3 * C + C + r];
     IO<TIO>::load8(p.q, o, q);
     IO<TIO>::load8(p.k, o, k);
     {

@@ -1,21 +1,15 @@
-// HIP kernels for gfx950: the chunked gated delta-rule forward recompute and
-// backward.  Four launches per backward:
+// HIP kernels for gfx950, scalar gate (GDN): the chunk-parallel parts of the
+// chunked gated delta-rule forward recompute and backward.  Three launches per
+// backward (the per-channel gate has its own kernels in gdr_kda.hip):
 //
 //   k_prep    one workgroup per (chunk, head): L2 norms, beta, in-chunk gate
 //             cumsum Gamma, M = Kn Kn^T o E and P = scale Qn Kn^T o E on MFMA,
 //             the UT/WY inverse A = (I + StrictLower(diag(beta) M))^-1, and
 //             W = A diag(beta) Kbar, U' = A diag(beta) V on MFMA.
-//   k_chain   the two serial chunk recursions, one workgroup per
-//             (sequence, head, 16-wide V slice) per direction: the forward state
-//             pass S_{n+1} = S_n Diag(e^GamC) + (U' - W S_n^T)^T Khat and the
-//             reverse state-gradient pass dS_n = dS_{n+1} Diag(e^GamC) +
-//             dO^T Qbar - dU^T W with dU = P^T dO + Khat dS_{n+1}^T.  Neither
-//             depends on the other, so the fused entry point runs both side by
-//             side in one grid.  The fp32 accumulators stay in registers.
-//   k_grads   one workgroup per (chunk, head): the chunk-local gradients on MFMA.
-//   k_finish  one workgroup per (chunk, head), bandwidth bound: L2-norm and
-//             sigmoid backward, reverse cumsum of the gate gradient plus the
-//             chunk-total term.
+//   k_chain   (gdr_chain.hip) the two serial chunk recursions.
+//   k_grads   one workgroup per (chunk, head): the chunk-local gradients on MFMA,
+//             and in its tail the prepare-backward: L2-norm and sigmoid backward,
+//             reverse cumsum of the gate gradient plus the chunk-total term.
 //
 // The recursion is the one the FlashQLA overview describes (state gradient
 // strictly from the last chunk to the first, dh <- g_last dh + R^T dO + X^T Y
@@ -27,6 +21,7 @@
 
 #include "gdr_device.h"
 #include "gdr_internal.h"
+#include "gdr_lds.h"
 
 namespace gdr {
 
@@ -97,8 +92,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
     *reinterpret_cast<bf16x8*>(Qs + r * PD + c0) = qb;
     *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
     if (tid % TPR == 0) {
-      p.rho[ch * 2 * C + r] = rq;
-      p.rho[ch * 2 * C + C + r] = rk;
+      p.rho[ch * 3 * C + r] = rq;
+      p.rho[ch * 3 * C + C + r] = rk;
       rq_s[r] = rq;
       rk_s[r] = rk;
     }
@@ -117,6 +112,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
     gam_s[l] = lam;
     beta_s[l] = bt;
     p.gam[ch * C + l] = lam;
+    p.rho[ch * 3 * C + 2 * C + l] = bt;
   }
   __syncthreads();
 
@@ -239,102 +235,161 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
 }
 
 // ===========================================================================
-// k_grads (scalar gate): chunk-local gradients
+// k_grads_gdn (scalar gate): chunk-local gradients, fused with the
+// prepare-backward (L2-norm and sigmoid backward, the gate's reverse cumsum)
 // ===========================================================================
-template <int D>
-struct GradSmem {
-  static constexpr int PD = Dims<D>::PD;
-  static constexpr int rs = 2 * C * PD;                                  // elements
-  static constexpr int rds = (D * PD > 2 * C * PC) ? D * PD : 2 * C * PC;  // elements
+// The tiles a chunk needs (dU^T, A, U^T, dO, v, S, dS) are copied global -> LDS
+// with direct-to-LDS loads issued as the workgroup starts, in two groups: phase 1
+// waits for the first only, so the state tiles arrive while it runs.  Raw q and
+// k rows are copied the same way at the start of phase 2, into the space phase 1
+// has freed.  Each tile is its own LDS object, so the compiler can tell that a
+// read of one tile does not depend on the copies into another.
+//
+// A wave with direct-to-LDS loads in flight must not consume an ordinary
+// register load: the compiler then waits for every load in flight.  With bf16
+// inputs the kernel therefore reads nothing from global memory into registers
+// until all copies have landed; fp32 inputs (rounded to bf16 on the way into
+// LDS) are loaded into registers and lose that overlap.
+template <int D, typename TIO>
+struct GradLds {
+  static constexpr bool kDma = !std::is_same<TIO, float>::value;
+  static constexpr int TS = D * D * 2;   // S, dS tiles [v][j]
+  static constexpr int TU = D * C * 2;   // dU^T, U^T tiles [v][r]
+  static constexpr int TR = C * D * 2;   // row tiles [r][*]: dO, dY, v, q, k, Kn, Qn
+  static constexpr int TA = C * C * 2;   // A, dME, dPE
+  // the S tile later holds Kn and Qn, the dS tile dME and dPE
+  static constexpr int TSx = TS > 2 * TR ? TS : 2 * TR;
+  static constexpr int TdSx = TS > 2 * TA ? TS : 2 * TA;
+  // loads per wave of the first group (tiles + one row of per-row scalars) and
+  // of the second (S, dS)
+  static constexpr int G1 = (2 * TU + TA + (kDma ? 2 * TR : 0)) / 1024 / 4 + 1;
+  static constexpr int G2 = 2 * TS / 1024 / 4;
+  static_assert(TU == TR, "raw q rows reuse the dU^T tile");
 };
 
 template <int D, typename TIO>
 __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   using Dm = Dims<D>;
-  constexpr int PD = Dm::PD, TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS, NJB = Dm::NJB;
-  __shared__ __attribute__((aligned(16))) bf16 RS[GradSmem<D>::rs];
-  __shared__ __attribute__((aligned(16))) bf16 RdS[GradSmem<D>::rds];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[C * PD];
-  __shared__ __attribute__((aligned(16))) bf16 UsT[D * PC];   // U^T: [v][r]
-  __shared__ __attribute__((aligned(16))) bf16 dYs[C * PD];
-  __shared__ float gam_s[C], beta_s[C], rq_s[C], rk_s[C];
+  using Ly = GradLds<D, TIO>;
+  constexpr bool kDma = Ly::kDma;
+  constexpr int TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS, NJB = Dm::NJB;
+  __shared__ __attribute__((aligned(1024))) char Sx[Ly::TSx];         // S; phases 3-4: Kn, Qn
+  __shared__ __attribute__((aligned(1024))) char dSx[Ly::TdSx];       // dS; phases 3-4: dME, dPE
+  __shared__ __attribute__((aligned(1024))) char dUT[Ly::TU];         // phase 1: dU^T; then raw q
+  __shared__ __attribute__((aligned(1024))) char At[Ly::TA];
+  __shared__ __attribute__((aligned(1024))) char UT[Ly::TU];
+  __shared__ __attribute__((aligned(1024))) char dOt[Ly::TR];
+  __shared__ __attribute__((aligned(1024))) char dYt[Ly::TR];
+  __shared__ __attribute__((aligned(1024))) char Vt[kDma ? Ly::TR : 16];   // phase 1: v; then raw k
+  // per-row scalars: Gamma, 1/|q|, 1/|k|, beta (0 past the end)
+  __shared__ __attribute__((aligned(256))) float sc_s[4][C];
   // fixed-order partial sums (deterministic): column sums of the pairwise dGamma
-  // term per wave, row sums per row, and two per-wave chunk scalars
-  __shared__ float colsum_s[4][C], rowsum_s[C], red_s[4][2];
+  // term per wave, row sums and dbeta per row, two per-wave chunk scalars
+  __shared__ float colsum_s[4][C], rowsum_s[C], dbeta_s[C], red_s[4][2];
+  const float* const gam_s = sc_s[0];
+  const float* const rq_s = sc_s[1];
+  const float* const rk_s = sc_s[2];
+  const float* const beta_s = sc_s[3];
 
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  const int tid = threadIdx.x, l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = l >> 4, jj = l & 15;
   const int64_t ch = int64_t(h) * p.NC + c;
   const int H = p.H;
   const float scale = p.scale;
+  char* const Kn = Sx;
+  char* const Qn = Sx + Ly::TR;
+  char* const dME = dSx;
+  char* const dPE = dSx + Ly::TA;
+  const int r = 16 * w + jj;
+  const int64_t trow = tok(t0 + min(r, len - 1), H, h) * D;
+  auto u16 = [](const uint16_t* x) { return reinterpret_cast<const char*>(x); };
+  auto row_of = [&](const void* x, int rr) {
+    return reinterpret_cast<const char*>(x) + tok(t0 + min(rr, len - 1), H, h) * D * 2;
+  };
 
-  bf16* dUsT = RS;    // phase 1: dU^T [v][r]
-  bf16* As = RdS;     // phase 1
+  // ---- first group: per-row scalars, phase-1 tiles, dO (and v) ----
+  dma4(w == 0 ? static_cast<const void*>(p.gam + ch * C + l) : static_cast<const void*>(p.rho + (ch * 3 + w - 1) * C + l),
+       reinterpret_cast<char*>(sc_s[w]));
+  dma_tile<C, 1, D, 4>(dUT, [&](int v) { return u16(p.dU + (ch * D + v) * C); }, w);
+  dma_tile<C, 0, C, 4>(At, [&](int rr) { return u16(p.A + (ch * C + rr) * C); }, w);
+  dma_tile<C, 0, D, 4>(UT, [&](int v) { return u16(p.U + (ch * D + v) * C); }, w);
+  if constexpr (kDma) {
+    dma_tile<D, 0, C, 4>(dOt, [&](int rr) { return row_of(p.dO, rr); }, w);
+    dma_tile<D, 0, C, 4>(Vt, [&](int rr) { return row_of(p.v, rr); }, w);
+  }
+  // ---- second group: S, dS ----
+  dma_tile<D, 0, D, 4>(Sx, [&](int v) { return u16(p.S + (ch * D + v) * D); }, w);
+  dma_tile<D, 0, D, 4>(dSx, [&](int v) { return u16(p.dS + (ch * D + v) * D); }, w);
+
+  // fp32 inputs: dO rounded into its tile, v and raw q, k rows kept in registers
+  typename IO<TIO>::Raw4 vraw[kDma ? 1 : NJB];
+  typename IO<TIO>::Raw8 qraw[kDma ? 1 : NPASS], kraw[kDma ? 1 : NPASS];
+  if constexpr (!kDma) {
+#pragma unroll
+    for (int vb = 0; vb < NJB; ++vb) vraw[vb] = IO<TIO>::load_raw4(p.v, trow + 16 * vb + 4 * g);
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int rr = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
+      const int64_t o = tok(t0 + min(rr, len - 1), H, h) * D + c0;
+      qraw[ps] = IO<TIO>::load_raw8(p.q, o);
+      kraw[ps] = IO<TIO>::load_raw8(p.k, o);
+      float x[8];
+      IO<TIO>::load8(p.dO, o, x);
+      bf16x8 xb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[e] = to_bf16(x[e]);
+      *reinterpret_cast<bf16x8*>(dOt + soff<D>(rr, c0)) = xb;
+    }
+  }
   if (tid < C) {
-    gam_s[tid] = p.gam[ch * C + tid];
-    rq_s[tid] = p.rho[ch * 2 * C + tid];
-    rk_s[tid] = p.rho[ch * 2 * C + C + tid];
-    beta_s[tid] = (tid < len ? 1.f : 0.f) * sigmoidf(IO<TIO>::load1(p.b, tok(t0 + min(tid, len - 1), H, h)));
 #pragma unroll
     for (int x = 0; x < 4; ++x) colsum_s[x][tid] = 0.f;
   }
-  // U and dU are stored transposed, [v][r]
-  for (int pc = tid; pc < D * C / 8; pc += kThreads) {
-    const int v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
-    *reinterpret_cast<uint4*>(dUsT + v * PC + c0) = *reinterpret_cast<const uint4*>(p.dU + (ch * D + v) * C + c0);
-    *reinterpret_cast<uint4*>(UsT + v * PC + c0) = *reinterpret_cast<const uint4*>(p.U + (ch * D + v) * C + c0);
-  }
-#pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
-    float x[8];
-    IO<TIO>::load8(p.dO, tok(t0 + min(r, len - 1), H, h) * D + c0, x);
-    const float m = r < len ? 1.f : 0.f;
-    bf16x8 xb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) xb[e] = to_bf16(x[e] * m);
-    *reinterpret_cast<bf16x8*>(dOs + r * PD + c0) = xb;
-  }
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int pc = tid + x * kThreads;
-    *reinterpret_cast<uint4*>(As + (pc / 8) * PC + (pc % 8) * 8) =
-        *reinterpret_cast<const uint4*>(p.A + (ch * C + pc / 8) * C + (pc % 8) * 8);
-  }
-  __syncthreads();
+  if constexpr (kDma) wait_vm<Ly::G2>();   // the first group has landed
+  else wait_vm<0>();
+  chain_barrier();   // B_a
 
   // ---- phase 1: dY = A^T dU (lane owns dY[r][v .. v+3], r = 16w + jj); dv; sum dY*v ----
-  const int r = 16 * w + jj;
   const float br = beta_s[r];
   float dbeta_row = 0.f, dgam_row = 0.f;
+  f32x4 dvv[NJB];
 #pragma unroll
   for (int vb = 0; vb < NJB; ++vb) {
     f32x4 a = zero4();
 #pragma unroll
-    for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_rk(dUsT, PC, 16 * vb, k0), frag_kc(As, PC, 16 * w, k0), a);
+    for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_rk_s<C, 1>(dUT, 16 * vb, k0), frag_kc_s<C, 0>(At, 16 * w, k0), a);
     const int v = 16 * vb + 4 * g;
-    st_bf16x4(dYs + r * PD + v, a[0], a[1], a[2], a[3]);
+    st4_s<D>(dYt, r, v, a[0], a[1], a[2], a[3]);
     // rows past the end: dY is exactly zero there, so the clamped v row adds nothing
-    const int64_t o = tok(t0 + min(r, len - 1), H, h) * D + v;
     float vv[4];
-    IO<TIO>::load4(p.v, o, vv);
-    dbeta_row += a[0] * vv[0] + a[1] * vv[1] + a[2] * vv[2] + a[3] * vv[3];
-    if (r < len) IO<TIO>::store4(p.dv, o, br * a[0], br * a[1], br * a[2], br * a[3]);
-  }
-  __syncthreads();
-  // ---- load S (RS) and dS (RdS), both [v][j] ----
-  {
-    constexpr int PIECES = D * D / 8;
-    for (int pc = tid; pc < PIECES; pc += kThreads) {
-      const int row = pc / (D / 8), col = (pc % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(RS + row * PD + col) = *reinterpret_cast<const uint4*>(p.S + (ch * D + row) * D + col);
-      *reinterpret_cast<uint4*>(RdS + row * PD + col) = *reinterpret_cast<const uint4*>(p.dS + (ch * D + row) * D + col);
+    if constexpr (kDma) {
+      const bf16x4 vb4 = *reinterpret_cast<const bf16x4*>(Vt + soff<D>(r, v));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] = float(vb4[i]);
+    } else {
+      IO<TIO>::unpack4(vraw[vb], vv);
     }
+    dbeta_row += a[0] * vv[0] + a[1] * vv[1] + a[2] * vv[2] + a[3] * vv[3];
+    dvv[vb] = a;
   }
-  __syncthreads();
+  wait_vm<0>();
+  chain_barrier();   // B_b: S, dS and all of dY in LDS; dU^T, A and v are no longer read
+
+  // ---- raw q, k rows (bf16 inputs) into the freed dU^T and v tiles; dv ----
+  if constexpr (kDma) {
+    dma_tile<D, 0, C, 4>(dUT, [&](int rr) { return row_of(p.q, rr); }, w);
+    dma_tile<D, 0, C, 4>(Vt, [&](int rr) { return row_of(p.k, rr); }, w);
+  }
+  if (r < len) {
+#pragma unroll
+    for (int vb = 0; vb < NJB; ++vb)
+      IO<TIO>::store4(p.dv, trow + 16 * vb + 4 * g, br * dvv[vb][0], br * dvv[vb][1], br * dvv[vb][2], br * dvv[vb][3]);
+  }
+
   // ---- phase 2: Z = dY S, dQbar = dO S, dKhat = U dS (transposed tiles) ----
   f32x4 aZ[NJB], aQ[NJB], aK[NJB];
 #pragma unroll
@@ -342,36 +397,38 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     aZ[jb] = aQ[jb] = aK[jb] = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += 32) {
-      const bf16x8 aS = frag_kc(RS, PD, 16 * jb, k0);
-      const bf16x8 aD = frag_kc(RdS, PD, 16 * jb, k0);
-      aZ[jb] = mma(aS, frag_rk(dYs, PD, 16 * w, k0), aZ[jb]);
-      aQ[jb] = mma(aS, frag_rk(dOs, PD, 16 * w, k0), aQ[jb]);
-      aK[jb] = mma(aD, frag_kc(UsT, PC, 16 * w, k0), aK[jb]);
+      const bf16x8 aS = frag_kc_s<D>(Sx, 16 * jb, k0);
+      aZ[jb] = mma(aS, frag_rk_s<D>(dYt, 16 * w, k0), aZ[jb]);
+      aQ[jb] = mma(aS, frag_rk_s<D>(dOt, 16 * w, k0), aQ[jb]);
+      aK[jb] = mma(frag_kc_s<D>(dSx, 16 * jb, k0), frag_kc_s<C, 0>(UT, 16 * w, k0), aK[jb]);
     }
   }
   // state term of dGamma_C: sum_{v,j} dS * S
   float sdot = 0.f;
-  {
-    constexpr int PIECES = D * D / 8;
-    for (int pc = tid; pc < PIECES; pc += kThreads) {
-      const int row = pc / (D / 8), col = (pc % (D / 8)) * 8;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(RS + row * PD + col);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(RdS + row * PD + col);
+  for (int pc = tid; pc < D * D / 8; pc += kThreads) {
+    const int row = pc / (D / 8), col = (pc % (D / 8)) * 8;
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Sx + soff<D>(row, col));
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dSx + soff<D>(row, col));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sdot += float(a[e]) * float(b[e]);
-    }
+    for (int e = 0; e < 8; ++e) sdot += float(a[e]) * float(b[e]);
   }
-  __syncthreads();
-  // ---- load Kn, Qn (RS rows 0..63 and 64..127) ----
-  bf16* Kn = RS;
-  bf16* Qn = RS + C * PD;
+  wait_vm<0>();
+  chain_barrier();   // B_c: S and dS are no longer read; raw q, k in LDS
+
+  // ---- Kn, Qn (over S) ----
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int rr = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     float qv[8], kv[8];
-    const int64_t o = tok(t0 + min(rr, len - 1), H, h) * D + c0;
-    IO<TIO>::load8(p.q, o, qv);
-    IO<TIO>::load8(p.k, o, kv);
+    if constexpr (kDma) {
+      const bf16x8 qb8 = *reinterpret_cast<const bf16x8*>(dUT + soff<D>(rr, c0));
+      const bf16x8 kb8 = *reinterpret_cast<const bf16x8*>(Vt + soff<D>(rr, c0));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { qv[e] = float(qb8[e]); kv[e] = float(kb8[e]); }
+    } else {
+      IO<TIO>::unpack8(qraw[ps], qv);
+      IO<TIO>::unpack8(kraw[ps], kv);
+    }
     const float m = rr < len ? 1.f : 0.f;
     const float fq = m * rq_s[rr], fk = m * rk_s[rr];
     bf16x8 qb, kb;
@@ -380,14 +437,35 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
       qb[e] = to_bf16(qv[e] * fq);
       kb[e] = to_bf16(kv[e] * fk);
     }
-    *reinterpret_cast<bf16x8*>(Qn + rr * PD + c0) = qb;
-    *reinterpret_cast<bf16x8*>(Kn + rr * PD + c0) = kb;
+    *reinterpret_cast<bf16x8*>(Qn + soff<D>(rr, c0)) = qb;
+    *reinterpret_cast<bf16x8*>(Kn + soff<D>(rr, c0)) = kb;
   }
-  __syncthreads();
-  // ---- phase 3: M, P, dP, dL (transposed tiles: lane owns X[r][s .. s+3]) ----
-  bf16* dMEs = RdS;
-  bf16* dPEs = RdS + C * PC;
+  chain_barrier();   // B_d
+
+  // ---- fold the state-side terms (lane owns (r, j .. j+3)) ----
   const float gr = gam_s[r];
+  const float eg = fast_exp(gr), eh = fast_exp(gam_s[C - 1] - gr);
+  float dgc_loc = 0.f;
+  f32x4 dkn[NJB], dqn[NJB];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) {
+    const int j = 16 * jb + 4 * g;
+    const bf16x4 kb = *reinterpret_cast<const bf16x4*>(Kn + soff<D>(r, j));
+    const bf16x4 qb = *reinterpret_cast<const bf16x4*>(Qn + soff<D>(r, j));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float kn = float(kb[i]), qn = float(qb[i]);
+      const float z = aZ[jb][i], dkh = aK[jb][i], dqb = aQ[jb][i];
+      // dKbar = -beta Z, Kbar = kn e^Gam, Khat = kn e^(GamC-Gam), Qbar = scale qn e^Gam
+      dgam_row += -br * z * kn * eg - dkh * kn * eh + dqb * scale * qn * eg;
+      dbeta_row -= kn * eg * z;
+      dgc_loc += dkh * kn * eh;
+      dkn[jb][i] = -br * z * eg + dkh * eh;
+      dqn[jb][i] = scale * dqb * eg;
+    }
+  }
+
+  // ---- phase 3: M, P, dP, dL (transposed tiles: lane owns X[r][s .. s+3]) ----
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
     const int s0 = 16 * sb + 4 * g;
@@ -396,12 +474,12 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
       f32x4 G1 = zero4(), G2 = zero4(), Mr = zero4(), Pr = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < D; k0 += 32) {
-        const bf16x8 aU = frag_kc(UsT, PC, 16 * sb, k0);
-        G1 = mma(aU, frag_rk(dOs, PD, 16 * w, k0), G1);
-        G2 = mma(aU, frag_rk(dYs, PD, 16 * w, k0), G2);
-        const bf16x8 aK = frag_rk(Kn, PD, 16 * sb, k0);
-        Mr = mma(aK, frag_rk(Kn, PD, 16 * w, k0), Mr);
-        Pr = mma(aK, frag_rk(Qn, PD, 16 * w, k0), Pr);
+        const bf16x8 aU = frag_kc_s<C, 0>(UT, 16 * sb, k0);
+        G1 = mma(aU, frag_rk_s<D>(dOt, 16 * w, k0), G1);
+        G2 = mma(aU, frag_rk_s<D>(dYt, 16 * w, k0), G2);
+        const bf16x8 aK = frag_rk_s<D>(Kn, 16 * sb, k0);
+        Mr = mma(aK, frag_rk_s<D>(Kn, 16 * w, k0), Mr);
+        Pr = mma(aK, frag_rk_s<D>(Qn, 16 * w, k0), Pr);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -427,46 +505,72 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
         if (jj == 0) colsum_s[w][s] = -col;
       }
     }
-    st_bf16x4(dMEs + r * PC + s0, dme[0], dme[1], dme[2], dme[3]);
-    st_bf16x4(dPEs + r * PC + s0, dpe[0], dpe[1], dpe[2], dpe[3]);
+    st4_s<C, 0>(dME, r, s0, dme[0], dme[1], dme[2], dme[3]);
+    st4_s<C, 0>(dPE, r, s0, dpe[0], dpe[1], dpe[2], dpe[3]);
   }
-  // ---- fold the state-side terms (lane owns (r, j .. j+3)) ----
-  const float eg = fast_exp(gr), eh = fast_exp(gam_s[C - 1] - gr);
-  float dgc_loc = 0.f;
-  f32x4 dkn[NJB], dqn[NJB];
+  // raw q, k of this lane's outputs, for the L2-norm backward at the end
+  typename IO<TIO>::Raw4 qo[kDma ? 1 : NJB], ko[kDma ? 1 : NJB];
+  if constexpr (!kDma) {
 #pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
-    const int j = 16 * jb + 4 * g;
-    const bf16x4 kb = *reinterpret_cast<const bf16x4*>(Kn + r * PD + j);
-    const bf16x4 qb = *reinterpret_cast<const bf16x4*>(Qn + r * PD + j);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float kn = float(kb[i]), qn = float(qb[i]);
-      const float z = aZ[jb][i], dkh = aK[jb][i], dqb = aQ[jb][i];
-      // dKbar = -beta Z, Kbar = kn e^Gam, Khat = kn e^(GamC-Gam), Qbar = scale qn e^Gam
-      dgam_row += -br * z * kn * eg - dkh * kn * eh + dqb * scale * qn * eg;
-      dbeta_row -= kn * eg * z;
-      dgc_loc += dkh * kn * eh;
-      dkn[jb][i] = -br * z * eg + dkh * eh;
-      dqn[jb][i] = scale * dqb * eg;
+    for (int jb = 0; jb < NJB; ++jb) {
+      qo[jb] = IO<TIO>::load_raw4(p.q, trow + 16 * jb + 4 * g);
+      ko[jb] = IO<TIO>::load_raw4(p.k, trow + 16 * jb + 4 * g);
     }
   }
-  __syncthreads();
+  chain_barrier();   // B_e: dME, dPE complete
+
   // ---- phase 4: pairwise terms, dkn += (dME + dME^T) Kn + scale dPE^T Qn, dqn += scale dPE Kn ----
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) {
 #pragma unroll
     for (int k0 = 0; k0 < C; k0 += 32) {
-      const bf16x8 aK = frag_kc(Kn, PD, 16 * jb, k0);
-      const bf16x8 aQ2 = frag_kc(Qn, PD, 16 * jb, k0);
-      dkn[jb] = mma(aK, frag_rk(dMEs, PC, 16 * w, k0), dkn[jb]);
-      dkn[jb] = mma(aK, frag_kc(dMEs, PC, 16 * w, k0), dkn[jb]);
-      dkn[jb] = mma(aQ2, frag_kc(dPEs, PC, 16 * w, k0), dkn[jb]);
-      dqn[jb] = mma(aK, frag_rk(dPEs, PC, 16 * w, k0), dqn[jb]);
+      const bf16x8 aK = frag_kc_s<D>(Kn, 16 * jb, k0);
+      const bf16x8 aQ2 = frag_kc_s<D>(Qn, 16 * jb, k0);
+      dkn[jb] = mma(aK, frag_rk_s<C, 0>(dME, 16 * w, k0), dkn[jb]);
+      dkn[jb] = mma(aK, frag_kc_s<C, 0>(dME, 16 * w, k0), dkn[jb]);
+      dkn[jb] = mma(aQ2, frag_kc_s<C, 0>(dPE, 16 * w, k0), dkn[jb]);
+      dqn[jb] = mma(aK, frag_rk_s<C, 0>(dPE, 16 * w, k0), dqn[jb]);
     }
-    const int j = 16 * jb + 4 * g;
-    *reinterpret_cast<float4*>(p.dqn + (ch * C + r) * D + j) = make_float4(dqn[jb][0], dqn[jb][1], dqn[jb][2], dqn[jb][3]);
-    *reinterpret_cast<float4*>(p.dkn + (ch * C + r) * D + j) = make_float4(dkn[jb][0], dkn[jb][1], dkn[jb][2], dkn[jb][3]);
+  }
+  // ---- L2-norm backward: dq = rq (dqn - qn <qn, dqn>), dk likewise (K1 page, 3.3) ----
+  {
+    const float m = r < len ? 1.f : 0.f;
+    const float rq = m * rq_s[r], rk = m * rk_s[r];
+    float pq = 0.f, pk = 0.f;
+    float qn[NJB][4], kn[NJB][4];
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+      if constexpr (kDma) {
+        const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(dUT + soff<D>(r, 16 * jb + 4 * g));
+        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Vt + soff<D>(r, 16 * jb + 4 * g));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { qn[jb][i] = float(q4[i]); kn[jb][i] = float(k4[i]); }
+      } else {
+        IO<TIO>::unpack4(qo[jb], qn[jb]);
+        IO<TIO>::unpack4(ko[jb], kn[jb]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qn[jb][i] *= rq;
+        kn[jb][i] *= rk;
+        pq += qn[jb][i] * dqn[jb][i];
+        pk += kn[jb][i] * dkn[jb][i];
+      }
+    }
+    pq += __shfl_xor(pq, 16, 64);
+    pq += __shfl_xor(pq, 32, 64);
+    pk += __shfl_xor(pk, 16, 64);
+    pk += __shfl_xor(pk, 32, 64);
+    if (r < len) {
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const int64_t o = trow + 16 * jb + 4 * g;
+        IO<TIO>::store4(p.dq, o, rq * (dqn[jb][0] - qn[jb][0] * pq), rq * (dqn[jb][1] - qn[jb][1] * pq),
+                        rq * (dqn[jb][2] - qn[jb][2] * pq), rq * (dqn[jb][3] - qn[jb][3] * pq));
+        IO<TIO>::store4(p.dk, o, rk * (dkn[jb][0] - kn[jb][0] * pk), rk * (dkn[jb][1] - kn[jb][1] * pk),
+                        rk * (dkn[jb][2] - kn[jb][2] * pk), rk * (dkn[jb][3] - kn[jb][3] * pk));
+      }
+    }
   }
   // ---- row and chunk reductions ----
   dgam_row += __shfl_xor(dgam_row, 16, 64);
@@ -475,7 +579,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   dbeta_row += __shfl_xor(dbeta_row, 32, 64);
   if (g == 0) {
     rowsum_s[r] = dgam_row;
-    p.dbeta[ch * C + r] = dbeta_row;
+    dbeta_s[r] = dbeta_row;
   }
   const float tot = group_sum<64>(dgc_loc);
   const float st = group_sum<64>(sdot);
@@ -483,81 +587,22 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     red_s[w][0] = tot;
     red_s[w][1] = st;
   }
-  __syncthreads();
-  if (tid < C)
-    p.dgam[ch * C + tid] = rowsum_s[tid] + ((colsum_s[0][tid] + colsum_s[1][tid]) + (colsum_s[2][tid] + colsum_s[3][tid]));
-  if (tid == 0) {
-    const float a = (red_s[0][0] + red_s[1][0]) + (red_s[2][0] + red_s[3][0]);
-    const float b = (red_s[0][1] + red_s[1][1]) + (red_s[2][1] + red_s[3][1]);
-    p.dgamc[ch] = a + b * fast_exp(gam_s[C - 1]);
-  }
-}
-
-// ===========================================================================
-// k_finish (scalar gate): L2-norm / sigmoid backward, gate reverse cumsum
-// ===========================================================================
-template <int D, typename TIO>
-__global__ __launch_bounds__(kThreads) void k_finish_gdn(const Params p) {
-  using Dm = Dims<D>;
-  constexpr int TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS;
-  const int c = blockIdx.x, h = blockIdx.y;
-  const ChunkEntry ce = p.ctab[c];
-  const int t0 = ce.t_start, len = ce.len;
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
-  const int64_t ch = int64_t(h) * p.NC + c;
-  const int H = p.H;
-#pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
-    const bool ok = r < len;
-    float q[8], k[8], dq[8], dk[8];
-    const int64_t o = tok(t0 + min(r, len - 1), H, h) * D + c0;
-    const float m = ok ? 1.f : 0.f;
-    const float rq = m * p.rho[ch * 2 * C + r], rk = m * p.rho[ch * 2 * C + C + r];
-    IO<TIO>::load8(p.q, o, q);
-    IO<TIO>::load8(p.k, o, k);
-    {
-      const float4* a = reinterpret_cast<const float4*>(p.dqn + (ch * C + r) * D + c0);
-      const float4* b = reinterpret_cast<const float4*>(p.dkn + (ch * C + r) * D + c0);
-      const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
-      dq[0] = a0.x; dq[1] = a0.y; dq[2] = a0.z; dq[3] = a0.w; dq[4] = a1.x; dq[5] = a1.y; dq[6] = a1.z; dq[7] = a1.w;
-      dk[0] = b0.x; dk[1] = b0.y; dk[2] = b0.z; dk[3] = b0.w; dk[4] = b1.x; dk[5] = b1.y; dk[6] = b1.z; dk[7] = b1.w;
-    }
-    float pq = 0.f, pk = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      q[e] *= rq;
-      k[e] *= rk;
-      pq += q[e] * dq[e];
-      pk += k[e] * dk[e];
-    }
-    pq = group_sum<TPR>(pq);
-    pk = group_sum<TPR>(pk);
-    if (ok) {
-      float oq[8], ok8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        oq[e] = rq * (dq[e] - q[e] * pq);
-        ok8[e] = rk * (dk[e] - k[e] * pk);
-      }
-      IO<TIO>::store8(p.dq, o, oq);
-      IO<TIO>::store8(p.dk, o, ok8);
-    }
-  }
+  chain_barrier();   // B_f
   if (w == 0) {
-    // dlam_s = sum_{r >= s} dGam_r + dGamC (suffix sum; FlashKDA backward page, §5)
-    float x = p.dgam[ch * C + l];
+    // dlam_s = sum_{r >= s} dGam_r + dGamC (suffix sum; FlashKDA backward page, section 5)
+    const float dgc = ((red_s[0][0] + red_s[1][0]) + (red_s[2][0] + red_s[3][0])) +
+                      ((red_s[0][1] + red_s[1][1]) + (red_s[2][1] + red_s[3][1])) * fast_exp(gam_s[C - 1]);
+    float x = rowsum_s[l] + ((colsum_s[0][l] + colsum_s[1][l]) + (colsum_s[2][l] + colsum_s[3][l]));
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
       const float y = __shfl_down(x, m, 64);
       if (l + m < 64) x += y;
     }
-    const int64_t o = tok(t0 + min(l, len - 1), H, h);
-    const float bt = sigmoidf(IO<TIO>::load1(p.b, o));
-    const float dgc = p.dgamc[ch], dbs = p.dbeta[ch * C + l];
     if (l < len) {
+      const int64_t o = tok(t0 + l, H, h);
+      const float bt = beta_s[l];   // sigma(b) on valid rows
       IO<TIO>::store1(p.dg, o, x + dgc);
-      IO<TIO>::store1(p.db, o, dbs * bt * (1.f - bt));
+      IO<TIO>::store1(p.db, o, dbeta_s[l] * bt * (1.f - bt));
     }
   }
 }
@@ -598,18 +643,10 @@ struct RunGrads {
     k_grads_gdn<D, TIO><<<dim3(p.NC, p.H), kThreads, 0, s>>>(p);
   }
 };
-template <int D, typename TIO>
-struct RunFinish {
-  static void run(const Params& p, hipStream_t s) {
-    k_finish_gdn<D, TIO><<<dim3(p.NC, p.H), kThreads, 0, s>>>(p);
-  }
-};
-
 }  // namespace
 
 int launch_prep(const Params& p, void* stream) { return dispatch<RunPrep>(p, stream); }
 int launch_grads(const Params& p, void* stream) { return dispatch<RunGrads>(p, stream); }
-int launch_finish(const Params& p, void* stream) { return dispatch<RunFinish>(p, stream); }
 int launch_zero_params(const Params& p, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();

@@ -1,0 +1,129 @@
+// LDS tile helpers shared by the chain and gradient kernels (gfx950): XOR-swizzled
+// unpadded bf16 tiles, MFMA fragments read from them, direct-to-LDS loads, and a
+// workgroup barrier that orders LDS traffic only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gdr_device.h"
+
+namespace gdr {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// ---------------------------------------------------------------------------
+// swizzled LDS tiles
+// ---------------------------------------------------------------------------
+// Piece p (16 bytes) of row r of a W-column bf16 tile sits at piece p ^ swz(r).
+// The functions were chosen by measuring LDS bank conflicts on gfx950:
+//   W = 128: (r ^ 2r) mod 16 is conflict-free for both row-fragment reads (16
+//            rows at one piece, ds_read_b128) and transposed reads (rows
+//            r..r+3 and r+8..r+11 at two adjacent pieces, ds_read_b64_tr_b16);
+//   W = 64, kind 0: conflict-free transposed reads (the P tile, 64-wide tiles);
+//   W = 64, kind 1: r mod 8, conflict-free row-fragment reads (16-row tiles);
+//   W = 16: no swizzle, but rows 8-11 and 12-15 of every 16 swap places, so
+//            that the two 16-lane halves of a transposed read hit different banks.
+template <int W, int KIND>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (W == 128) return (r ^ (r << 1)) & 15;
+  else if constexpr (W == 64 && KIND == 0) return 4 * ((r >> 1) & 1) + 2 * ((r & 1) ^ ((r >> 3) & 1)) + ((r >> 2) & 1);
+  else if constexpr (W == 64) return r & 7;
+  else return 0;
+}
+
+// physical row of logical row r (only 16-wide tiles permute rows)
+template <int W>
+__device__ __forceinline__ int prow(int r) {
+  if constexpr (W == 16) return r ^ (((r >> 3) & 1) << 2);
+  else return r;
+}
+
+// byte offset of element (r, c) of a swizzled W-column bf16 tile
+template <int W, int KIND = 0>
+__device__ __forceinline__ int soff(int r, int c) {
+  return prow<W>(r) * (2 * W) + (((c >> 3) ^ swz<W, KIND>(r)) << 4) + ((c & 7) << 1);
+}
+
+// T[r0 + j][k0 + 8g .. 8g+7] (see frag_rk)
+template <int W, int KIND = 0>
+__device__ __forceinline__ bf16x8 frag_rk_s(const char* T, int r0, int k0) {
+  const int l = lane_id();
+  return *reinterpret_cast<const bf16x8*>(T + soff<W, KIND>(r0 + (l & 15), k0 + 8 * (l >> 4)));
+}
+
+// T[k0 + 8g .. 8g+7][c0 + j] by transposed reads (see frag_kc)
+template <int W, int KIND = 0>
+__device__ __forceinline__ bf16x8 frag_kc_s(const char* T, int c0, int k0) {
+  const int l = lane_id();
+  const int g = l >> 4, q = l & 15;
+  const int r = k0 + 8 * g + (q >> 2), c = c0 + 4 * (q & 3);
+  const char* p0 = T + soff<W, KIND>(r, c);
+  const char* p1 = T + soff<W, KIND>(r + 4, c);
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(p0)));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(p1)));
+  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+  const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+  return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int W, int KIND = 0>
+__device__ __forceinline__ void st4_s(char* T, int r, int c, float a, float b, float d, float e) {
+  *reinterpret_cast<uint2*>(T + soff<W, KIND>(r, c)) = pack4_bf16(a, b, d, e);
+}
+
+// x - bf16(x): the low part of a two-part bf16 value
+__device__ __forceinline__ float lo_part(float x) { return x - float(to_bf16(x)); }
+
+// one 16-byte direct-to-LDS load per lane: lane l's bytes land at lds + 16 l
+__device__ __forceinline__ void dma16(const void* src, char* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)((lds_char_t*)lds), 16, 0, 0);
+}
+
+// a 4-byte direct-to-LDS load: used to pull a cache line into L2 ahead of time
+__device__ __forceinline__ void dma4(const void* src, char* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)((lds_char_t*)lds), 4, 0, 0);
+}
+
+// Workgroup barrier that orders LDS traffic only: each wave's LDS reads and
+// writes complete first (lgkmcnt), while its global stores and loads stay in
+// flight (a __syncthreads fence would drain them every chunk step; the movers
+// wait for exactly the loads a barrier publishes).  The signal fences keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void chain_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt vmcnt(N), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+
+// Direct-to-LDS copy of a ROWS x W bf16 tile (rows of 2W bytes) into a swizzled
+// LDS tile at `dst`; row_src(row) is the global address of the row's first byte.
+// The tile's 1 KB loads are dealt to NW waves: wave `iw` issues loads iw,
+// iw + NW, ...
+template <int W, int KIND, int ROWS, int NW, typename F>
+__device__ __forceinline__ void dma_tile(char* dst, F row_src, int iw) {
+  // the trip count is a compile-time constant, so the loop unrolls and the
+  // compiler can count the loads in flight (an unknown count makes it wait for all)
+  constexpr int kLoads = ROWS * 2 * W / 1024;
+  static_assert(kLoads % NW == 0, "loads split evenly over the issuing waves");
+  const int l = lane_id();
+#pragma unroll
+  for (int it = 0; it < kLoads / NW; ++it) {
+    const int i = iw + NW * it;
+    const int pos = i * 1024 + 16 * l;
+    const int row = pos / (2 * W), lp = ((pos % (2 * W)) >> 4) ^ swz<W, KIND>(row);
+    dma16(row_src(row) + 16 * lp, dst + i * 1024);
+  }
+}
+
+}  // namespace gdr
