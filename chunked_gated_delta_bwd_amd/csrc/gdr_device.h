@@ -187,6 +187,22 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// lane exchange inside the 16-lane DPP rows of a wave
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// sum over the 16 lanes 16k .. 16k+15 of a wave, returned to all of them (DPP
+// row rotations by 8 and 4, then two quad permutations; no LDS traffic)
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0x128>(x);   // row_ror:8
+  x += dpp_f<0x124>(x);   // row_ror:4
+  x += dpp_f<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_f<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  return x;
+}
+
 // ---- tile geometry shared by the kernels ----
 constexpr int C = 64;       // tokens per chunk
 constexpr int PC = C + 8;   // LDS pitch of 64-wide bf16 tiles (elements)

@@ -286,6 +286,8 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   // fixed-order partial sums (deterministic): column sums of the pairwise dGamma
   // term per wave, row sums and dbeta per row, two per-wave chunk scalars
   __shared__ float colsum_s[4][C], rowsum_s[C], dbeta_s[C], red_s[4][2];
+  // phase-3 row sums of dGamma and dbeta per column block sb (written for sb <= r / 16)
+  __shared__ float rowq_s[4][C], rowb_s[4][C];
   const float* const gam_s = sc_s[0];
   const float* const rq_s = sc_s[1];
   const float* const rk_s = sc_s[2];
@@ -440,12 +442,19 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     *reinterpret_cast<bf16x8*>(Qn + soff<D>(rr, c0)) = qb;
     *reinterpret_cast<bf16x8*>(Kn + soff<D>(rr, c0)) = kb;
   }
+  // dME, dPE start at zero: phase 3 writes only the tiles on and below the diagonal
+  for (int o = 16 * tid; o < 2 * Ly::TA; o += 16 * kThreads) *reinterpret_cast<u32x4*>(dME + o) = u32x4{0u, 0u, 0u, 0u};
   chain_barrier();   // B_d
 
   // ---- fold the state-side terms (lane owns (r, j .. j+3)) ----
+  // dKbar = -beta Z, Kbar = kn e^Gam, Khat = kn e^(GamC-Gam), Qbar = scale qn e^Gam:
+  //   dkn = -beta e^Gam Z + e^(GamC-Gam) dKhat,  dqn = scale e^Gam dQbar,
+  //   dGam_r  += <kn, dkn> - 2 e^(GamC-Gam) <kn, dKhat> + <qn, dqn>,
+  //   dbeta_r -= e^Gam <kn, Z>,   dGam_C += e^(GamC-Gam) <kn, dKhat>
   const float gr = gam_s[r];
   const float eg = fast_exp(gr), eh = fast_exp(gam_s[C - 1] - gr);
-  float dgc_loc = 0.f;
+  const float cz = -br * eg, cq = scale * eg;
+  float s_kdkn = 0.f, s_kdkh = 0.f, s_qdqn = 0.f, s_kz = 0.f;
   f32x4 dkn[NJB], dqn[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) {
@@ -455,58 +464,85 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float kn = float(kb[i]), qn = float(qb[i]);
-      const float z = aZ[jb][i], dkh = aK[jb][i], dqb = aQ[jb][i];
-      // dKbar = -beta Z, Kbar = kn e^Gam, Khat = kn e^(GamC-Gam), Qbar = scale qn e^Gam
-      dgam_row += -br * z * kn * eg - dkh * kn * eh + dqb * scale * qn * eg;
-      dbeta_row -= kn * eg * z;
-      dgc_loc += dkh * kn * eh;
-      dkn[jb][i] = -br * z * eg + dkh * eh;
-      dqn[jb][i] = scale * dqb * eg;
+      const float z = aZ[jb][i], dkh = aK[jb][i];
+      dkn[jb][i] = fmaf(cz, z, eh * dkh);
+      dqn[jb][i] = cq * aQ[jb][i];
+      s_kdkn = fmaf(kn, dkn[jb][i], s_kdkn);
+      s_kdkh = fmaf(kn, dkh, s_kdkh);
+      s_qdqn = fmaf(qn, dqn[jb][i], s_qdqn);
+      s_kz = fmaf(kn, z, s_kz);
     }
   }
+  dgam_row += s_kdkn - 2.f * eh * s_kdkh + s_qdqn;
+  dbeta_row -= eg * s_kz;
+  const float dgc_loc = eh * s_kdkh;
 
-  // ---- phase 3: M, P, dP, dL (transposed tiles: lane owns X[r][s .. s+3]) ----
+  // ---- phase 3: M, P, dP, dL on the 10 tiles (rb, sb), sb <= rb, of the strictly
+  // lower / diagonal 16x16 blocks, dealt 3-3-2-2 over the waves (the third slot of
+  // waves 2 and 3 repeats a tile and stores nothing).  Lane owns X[r][s .. s+3],
+  // r = 16 rb + jj, s = 16 sb + 4g + i. ----
+  // per wave, nibble `slot` of these words: rb and sb of its tiles
+  constexpr uint32_t kRb[4] = {0x333, 0x223, 0x112, 0x001};
+  constexpr uint32_t kSb[4] = {0x210, 0x103, 0x002, 0x001};
+  float dme[3][4], dpe[3][4];
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
-    const int s0 = 16 * sb + 4 * g;
-    float dme[4] = {0.f, 0.f, 0.f, 0.f}, dpe[4] = {0.f, 0.f, 0.f, 0.f};
-    if (sb <= w) {
-      f32x4 G1 = zero4(), G2 = zero4(), Mr = zero4(), Pr = zero4();
+  for (int slot = 0; slot < 3; ++slot) {
+    const uint32_t rbw = w == 0 ? kRb[0] : w == 1 ? kRb[1] : w == 2 ? kRb[2] : kRb[3];
+    const uint32_t sbw = w == 0 ? kSb[0] : w == 1 ? kSb[1] : w == 2 ? kSb[2] : kSb[3];
+    const int rb = (rbw >> (4 * slot)) & 15, sb = (sbw >> (4 * slot)) & 15;
+    const bool valid = slot < 2 || w < 2;
+    const int rr = 16 * rb + jj, s0 = 16 * sb + 4 * g;
+    f32x4 G1 = zero4(), G2 = zero4(), Mr = zero4(), Pr = zero4();
 #pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) {
-        const bf16x8 aU = frag_kc_s<C, 0>(UT, 16 * sb, k0);
-        G1 = mma(aU, frag_rk_s<D>(dOt, 16 * w, k0), G1);
-        G2 = mma(aU, frag_rk_s<D>(dYt, 16 * w, k0), G2);
-        const bf16x8 aK = frag_rk_s<D>(Kn, 16 * sb, k0);
-        Mr = mma(aK, frag_rk_s<D>(Kn, 16 * w, k0), Mr);
-        Pr = mma(aK, frag_rk_s<D>(Qn, 16 * w, k0), Pr);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = s0 + i;
-        float qv = 0.f;
-        if (r >= s) {
-          const float E = fast_exp(gr - gam_s[s]);
-          const float P = scale * Pr[i] * E;
-          const float dP = G1[i];
-          qv = dP * P;
-          dpe[i] = scale * dP * E;
-          if (r > s) {
-            const float M = Mr[i] * E;
-            const float dL = -G2[i];
-            const float dM = br * dL;
-            dbeta_row += dL * M;
-            qv += dM * M;
-            dme[i] = dM * E;
-          }
-        }
-        dgam_row += qv;
-        const float col = group_sum<16>(qv);   // sum over the 16 rows r of this tile
-        if (jj == 0) colsum_s[w][s] = -col;
-      }
+    for (int k0 = 0; k0 < D; k0 += 32) {
+      const bf16x8 aU = frag_kc_s<C, 0>(UT, 16 * sb, k0);
+      G1 = mma(aU, frag_rk_s<D>(dOt, 16 * rb, k0), G1);
+      G2 = mma(aU, frag_rk_s<D>(dYt, 16 * rb, k0), G2);
+      const bf16x8 aK = frag_rk_s<D>(Kn, 16 * sb, k0);
+      Mr = mma(aK, frag_rk_s<D>(Kn, 16 * rb, k0), Mr);
+      Pr = mma(aK, frag_rk_s<D>(Qn, 16 * rb, k0), Pr);
     }
-    st4_s<C, 0>(dME, r, s0, dme[0], dme[1], dme[2], dme[3]);
-    st4_s<C, 0>(dPE, r, s0, dpe[0], dpe[1], dpe[2], dpe[3]);
+    const float grr = gam_s[rr], brr = beta_s[rr];
+    float rq = 0.f, rbt = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = s0 + i;
+      // Gamma is non-increasing, so the exponent is <= 0 wherever it is used
+      const float E = fast_exp(fminf(grr - gam_s[s], 0.f));
+      const float le = rr >= s ? 1.f : 0.f, lt = rr > s ? 1.f : 0.f;
+      const float dP = G1[i];
+      const float M = lt * Mr[i] * E;
+      const float dL = -G2[i];
+      const float dM = brr * dL;
+      const float qv = le * dP * scale * Pr[i] * E + dM * M;
+      dpe[slot][i] = le * scale * dP * E;
+      dme[slot][i] = lt * dM * E;
+      rbt = fmaf(dL, M, rbt);
+      rq += qv;
+      // column sum over the 16 rows of the tile
+      const float col = row16_sum(qv);
+      if (valid && jj == 0) colsum_s[rb][s] = -col;
+    }
+    // row sums over the 16 columns of the tile
+    rq += __shfl_xor(rq, 16, 64);
+    rq += __shfl_xor(rq, 32, 64);
+    rbt += __shfl_xor(rbt, 16, 64);
+    rbt += __shfl_xor(rbt, 32, 64);
+    if (valid && g == 0) {
+      rowq_s[sb][rr] = rq;
+      rowb_s[sb][rr] = rbt;
+    }
+  }
+#pragma unroll
+  for (int slot = 0; slot < 3; ++slot) {
+    const uint32_t rbw = w == 0 ? kRb[0] : w == 1 ? kRb[1] : w == 2 ? kRb[2] : kRb[3];
+    const uint32_t sbw = w == 0 ? kSb[0] : w == 1 ? kSb[1] : w == 2 ? kSb[2] : kSb[3];
+    const int rb = (rbw >> (4 * slot)) & 15, sb = (sbw >> (4 * slot)) & 15;
+    if (slot < 2 || w < 2) {
+      const int rr = 16 * rb + jj, s0 = 16 * sb + 4 * g;
+      st4_s<C, 0>(dME, rr, s0, dme[slot][0], dme[slot][1], dme[slot][2], dme[slot][3]);
+      st4_s<C, 0>(dPE, rr, s0, dpe[slot][0], dpe[slot][1], dpe[slot][2], dpe[slot][3]);
+    }
   }
   // raw q, k of this lane's outputs, for the L2-norm backward at the end
   typename IO<TIO>::Raw4 qo[kDma ? 1 : NJB], ko[kDma ? 1 : NJB];
@@ -593,6 +629,11 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     const float dgc = ((red_s[0][0] + red_s[1][0]) + (red_s[2][0] + red_s[3][0])) +
                       ((red_s[0][1] + red_s[1][1]) + (red_s[2][1] + red_s[3][1])) * fast_exp(gam_s[C - 1]);
     float x = rowsum_s[l] + ((colsum_s[0][l] + colsum_s[1][l]) + (colsum_s[2][l] + colsum_s[3][l]));
+    float dbt = dbeta_s[l];
+    for (int sb = 0; sb <= (l >> 4); ++sb) {
+      x += rowq_s[sb][l];
+      dbt += rowb_s[sb][l];
+    }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
       const float y = __shfl_down(x, m, 64);
@@ -602,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
       const int64_t o = tok(t0 + l, H, h);
       const float bt = beta_s[l];   // sigma(b) on valid rows
       IO<TIO>::store1(p.dg, o, x + dgc);
-      IO<TIO>::store1(p.db, o, dbeta_s[l] * bt * (1.f - bt));
+      IO<TIO>::store1(p.db, o, dbt * bt * (1.f - bt));
     }
   }
 }
