@@ -203,6 +203,30 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// x + (x of lane l ^ 16): v_permlane16_swap exchanges the odd 16-lane rows of
+// one register with the even rows of another; on two copies of x the two
+// registers then hold both rows of each pair, and their sum is the same on both.
+// (Inline assembly: the compiler builtin returns its first result twice.  The
+// compiler does not pad inline assembly for hazards: a VALU write of an operand
+// needs two wait states before the swap, a v_cmpx write of EXEC four; the
+// trailing nop separates the swap from the VALU that reads its results.)
+#define GDR_SWAP_ASM(op) "s_nop 4\n\t" op " %0, %1\n\ts_nop 1"
+__device__ __forceinline__ float pair16_sum(float x) {
+  float a = x, b = x;
+  asm volatile(GDR_SWAP_ASM("v_permlane16_swap_b32") : "+v"(a), "+v"(b));
+  return a + b;
+}
+// x + (x of lane l ^ 32), by the same exchange of the two 32-lane halves
+__device__ __forceinline__ float pair32_sum(float x) {
+  float a = x, b = x;
+  asm volatile(GDR_SWAP_ASM("v_permlane32_swap_b32") : "+v"(a), "+v"(b));
+  return a + b;
+}
+// sum over lanes l, l^16, l^32, l^48 (the four 16-lane rows), on every lane
+__device__ __forceinline__ float xrow_sum(float x) { return pair32_sum(pair16_sum(x)); }
+// sum over the whole wave, on every lane (no LDS traffic)
+__device__ __forceinline__ float wave_sum(float x) { return xrow_sum(row16_sum(x)); }
+
 // ---- tile geometry shared by the kernels ----
 constexpr int C = 64;       // tokens per chunk
 constexpr int PC = C + 8;   // LDS pitch of 64-wide bf16 tiles (elements)

@@ -405,14 +405,17 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
       aK[jb] = mma(frag_kc_s<D>(dSx, 16 * jb, k0), frag_kc_s<C, 0>(UT, 16 * w, k0), aK[jb]);
     }
   }
-  // state term of dGamma_C: sum_{v,j} dS * S
+  // state term of dGamma_C: sum_{v,j} S dS, the trace of S dS^T taken over its
+  // diagonal 16x16 blocks on MFMA (lane holds block rows 4g+i, column jj)
   float sdot = 0.f;
-  for (int pc = tid; pc < D * D / 8; pc += kThreads) {
-    const int row = pc / (D / 8), col = (pc % (D / 8)) * 8;
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Sx + soff<D>(row, col));
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dSx + soff<D>(row, col));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sdot += float(a[e]) * float(b[e]);
+  for (int bb = 0; bb < NJB / 4; ++bb) {
+    const int vb = 16 * (w + 4 * bb);
+    f32x4 t = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 32) t = mma(frag_rk_s<D>(Sx, vb, k0), frag_rk_s<D>(dSx, vb, k0), t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sdot += 4 * g + i == jj ? t[i] : 0.f;
   }
   wait_vm<0>();
   chain_barrier();   // B_c: S and dS are no longer read; raw q, k in LDS
@@ -524,10 +527,8 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
       if (valid && jj == 0) colsum_s[rb][s] = -col;
     }
     // row sums over the 16 columns of the tile
-    rq += __shfl_xor(rq, 16, 64);
-    rq += __shfl_xor(rq, 32, 64);
-    rbt += __shfl_xor(rbt, 16, 64);
-    rbt += __shfl_xor(rbt, 32, 64);
+    rq = xrow_sum(rq);
+    rbt = xrow_sum(rbt);
     if (valid && g == 0) {
       rowq_s[sb][rr] = rq;
       rowb_s[sb][rr] = rbt;
@@ -593,11 +594,19 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
         pk += kn[jb][i] * dkn[jb][i];
       }
     }
-    pq += __shfl_xor(pq, 16, 64);
-    pq += __shfl_xor(pq, 32, 64);
-    pk += __shfl_xor(pk, 16, 64);
-    pk += __shfl_xor(pk, 32, 64);
-    if (r < len) {
+    pq = xrow_sum(pq);
+    pk = xrow_sum(pk);
+    if constexpr (kDma) {
+      // bf16 rows go out through LDS (the dO and dY tiles are free now), below
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const int j = 16 * jb + 4 * g;
+        st4_s<D>(dOt, r, j, rq * (dqn[jb][0] - qn[jb][0] * pq), rq * (dqn[jb][1] - qn[jb][1] * pq),
+                 rq * (dqn[jb][2] - qn[jb][2] * pq), rq * (dqn[jb][3] - qn[jb][3] * pq));
+        st4_s<D>(dYt, r, j, rk * (dkn[jb][0] - kn[jb][0] * pk), rk * (dkn[jb][1] - kn[jb][1] * pk),
+                 rk * (dkn[jb][2] - kn[jb][2] * pk), rk * (dkn[jb][3] - kn[jb][3] * pk));
+      }
+    } else if (r < len) {
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
         const int64_t o = trow + 16 * jb + 4 * g;
@@ -609,16 +618,14 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     }
   }
   // ---- row and chunk reductions ----
-  dgam_row += __shfl_xor(dgam_row, 16, 64);
-  dgam_row += __shfl_xor(dgam_row, 32, 64);
-  dbeta_row += __shfl_xor(dbeta_row, 16, 64);
-  dbeta_row += __shfl_xor(dbeta_row, 32, 64);
+  dgam_row = xrow_sum(dgam_row);
+  dbeta_row = xrow_sum(dbeta_row);
   if (g == 0) {
     rowsum_s[r] = dgam_row;
     dbeta_s[r] = dbeta_row;
   }
-  const float tot = group_sum<64>(dgc_loc);
-  const float st = group_sum<64>(sdot);
+  const float tot = wave_sum(dgc_loc);
+  const float st = wave_sum(sdot);
   if (l == 0) {
     red_s[w][0] = tot;
     red_s[w][1] = st;
@@ -644,6 +651,19 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
       const float bt = beta_s[l];   // sigma(b) on valid rows
       IO<TIO>::store1(p.dg, o, x + dgc);
       IO<TIO>::store1(p.db, o, dbt * bt * (1.f - bt));
+    }
+  }
+  if constexpr (kDma) {
+    // dq, dk rows: 1 KB (four rows) per wave instruction, 16 bytes per lane
+#pragma unroll
+    for (int it = 0; it < Ly::TR / 1024 / 4; ++it) {
+      const int pos = (w + 4 * it) * 1024 + 16 * l;
+      const int row = pos / (2 * D), c0 = (pos % (2 * D)) / 2;
+      if (row < len) {
+        const int64_t o = tok(t0 + row, H, h) * D + c0;
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.dq) + o) = *reinterpret_cast<const u32x4*>(dOt + soff<D>(row, c0));
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.dk) + o) = *reinterpret_cast<const u32x4*>(dYt + soff<D>(row, c0));
+      }
     }
   }
 }

@@ -109,21 +109,30 @@ __device__ __forceinline__ void wait_vm() {
 // Direct-to-LDS copy of a ROWS x W bf16 tile (rows of 2W bytes) into a swizzled
 // LDS tile at `dst`; row_src(row) is the global address of the row's first byte.
 // The tile's 1 KB loads are dealt to NW waves: wave `iw` issues loads iw,
-// iw + NW, ...
+// iw + NW, ...  dma_piece issues the wave's load number `it` alone, so that the
+// copies can be spread over compute (a wave that issues many loads back to back
+// stalls until the memory pipeline takes them).
+template <int W, int ROWS, int NW>
+struct DmaTile {
+  static constexpr int kLoads = ROWS * 2 * W / 1024;
+  static_assert(kLoads % NW == 0, "loads split evenly over the issuing waves");
+  static constexpr int kPerWave = kLoads / NW;
+};
+
+template <int W, int KIND, int ROWS, int NW, typename F>
+__device__ __forceinline__ void dma_piece(char* dst, F row_src, int iw, int it) {
+  const int i = iw + NW * it;
+  const int pos = i * 1024 + 16 * lane_id();
+  const int row = pos / (2 * W), lp = ((pos % (2 * W)) >> 4) ^ swz<W, KIND>(row);
+  dma16(row_src(row) + 16 * lp, dst + i * 1024);
+}
+
 template <int W, int KIND, int ROWS, int NW, typename F>
 __device__ __forceinline__ void dma_tile(char* dst, F row_src, int iw) {
   // the trip count is a compile-time constant, so the loop unrolls and the
   // compiler can count the loads in flight (an unknown count makes it wait for all)
-  constexpr int kLoads = ROWS * 2 * W / 1024;
-  static_assert(kLoads % NW == 0, "loads split evenly over the issuing waves");
-  const int l = lane_id();
 #pragma unroll
-  for (int it = 0; it < kLoads / NW; ++it) {
-    const int i = iw + NW * it;
-    const int pos = i * 1024 + 16 * l;
-    const int row = pos / (2 * W), lp = ((pos % (2 * W)) >> 4) ^ swz<W, KIND>(row);
-    dma16(row_src(row) + 16 * lp, dst + i * 1024);
-  }
+  for (int it = 0; it < DmaTile<W, ROWS, NW>::kPerWave; ++it) dma_piece<W, KIND, ROWS, NW>(dst, row_src, iw, it);
 }
 
 }  // namespace gdr
