@@ -203,6 +203,21 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// sum over aligned groups of W lanes (W = 16: the DPP row; W = 8: half rows,
+// by a mirror within each half and two quad permutations), on every lane
+template <int W>
+__device__ __forceinline__ float group_sum_dpp(float x) {
+  static_assert(W == 16 || W == 8, "DPP group width");
+  if constexpr (W == 16) {
+    return row16_sum(x);
+  } else {
+    x += dpp_f<0x141>(x);   // row_half_mirror
+    x += dpp_f<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_f<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    return x;
+  }
+}
+
 // x + (x of lane l ^ 16): v_permlane16_swap exchanges the odd 16-lane rows of
 // one register with the even rows of another; on two copies of x the two
 // registers then hold both rows of each pair, and their sum is the same on both.

@@ -31,17 +31,41 @@ static_assert(Dims<128>::RPP * Dims<128>::TPR == kThreads, "row sweep covers the
 // ===========================================================================
 // k_prep (scalar gate)
 // ===========================================================================
+// Tiles (rb, sb), sb <= rb, of the 10 lower / diagonal 16x16 blocks of a 64x64
+// chunk matrix, dealt 3-3-2-2 over four waves: nibble `slot` of these words is
+// the rb / sb of a wave's tile in that slot (the third slot of waves 2 and 3
+// repeats a tile and stores nothing).
+constexpr uint32_t kTileRb[4] = {0x333, 0x223, 0x112, 0x001};
+constexpr uint32_t kTileSb[4] = {0x210, 0x103, 0x002, 0x001};
+__device__ __forceinline__ int tile_rb(int w, int slot) {
+  const uint32_t x = w == 0 ? kTileRb[0] : w == 1 ? kTileRb[1] : w == 2 ? kTileRb[2] : kTileRb[3];
+  return (x >> (4 * slot)) & 15;
+}
+__device__ __forceinline__ int tile_sb(int w, int slot) {
+  const uint32_t x = w == 0 ? kTileSb[0] : w == 1 ? kTileSb[1] : w == 2 ? kTileSb[2] : kTileSb[3];
+  return (x >> (4 * slot)) & 15;
+}
+__device__ __forceinline__ bool tile_valid(int w, int slot) { return slot < 2 || w < 2; }
+
+// 16x16x4 fp32 MFMA: lane l gives A[l%16][l/16] and B[l/16][l%16]
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <int D, typename TIO>
 __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   using Dm = Dims<D>;
   constexpr int PD = Dm::PD, TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS;
-  constexpr int PL = C + 4;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[C * PD];
+  constexpr int PL = C + 4;   // pitch (floats) of the fp32 64x64 tiles L and X
+  constexpr int kQX = C * PD * 2 > C * PL * 4 ? C * PD * 2 : C * PL * 4;
+  __shared__ __attribute__((aligned(16))) char QX[kQX];          // Qn; from the inverse on: X = A, fp32
   __shared__ __attribute__((aligned(16))) bf16 Ks[C * PD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[C * PD];
-  __shared__ __attribute__((aligned(16))) bf16 As[C * PC];
+  __shared__ __attribute__((aligned(16))) bf16 As[C * PC];       // P on its way out; inverse scratch; A
   __shared__ __attribute__((aligned(16))) float Lf[C * PL];
   __shared__ float gam_s[C], beta_s[C], rq_s[C], rk_s[C];
+  bf16* const Qs = reinterpret_cast<bf16*>(QX);
+  float* const Xf = reinterpret_cast<float*>(QX);
   // fp32 inputs: the recursions take materialised Khat / Qbar tiles (Qbar split
   // into bf16 high and low parts); bf16 inputs use the raw rows and row factors
   constexpr bool kMat = std::is_same<TIO, float>::value;
@@ -50,36 +74,53 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  const int g = l >> 4, jj = l & 15;
   const int64_t ch = int64_t(h) * p.NC + c;
   const int H = p.H;
 
-  // --- rows: L2 norms; qn, kn to LDS; kn and v kept in registers ---
+  // --- rows: every load issued first (unconditional, from a clamped row, masked
+  // afterwards), so that their latencies overlap ---
+  typename IO<TIO>::Raw8 qraw[NPASS], kraw[NPASS], vraw[NPASS];
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
+    const int64_t off = tok(t0 + min(r, len - 1), H, h) * D + c0;
+    qraw[ps] = IO<TIO>::load_raw8(p.q, off);
+    kraw[ps] = IO<TIO>::load_raw8(p.k, off);
+    vraw[ps] = IO<TIO>::load_raw8(p.v, off);
+  }
+  float graw = 0.f, braw = 0.f;
+  if (w == 0) {
+    const int64_t o = tok(t0 + min(l, len - 1), H, h);
+    graw = IO<TIO>::load1(p.g, o);
+    braw = IO<TIO>::load1(p.b, o);
+  }
+  // the P tile goes out through As, which starts at zero (tiles above the diagonal)
+  for (int o = 16 * tid; o < C * PC * 2; o += 16 * kThreads)
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(As) + o) = u32x4{0u, 0u, 0u, 0u};
+
+  // --- L2 norms; qn, kn to LDS; kn and v kept in registers ---
   float kn_r[NPASS][8], v_r[NPASS][8];
   float qn_r[kMat ? NPASS : 1][8];
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     float qv[8], kv[8];
-    {
-      // unconditional loads from a clamped row, masked afterwards (no branch
-      // around the loads, so they are not serialised)
-      const int64_t off = tok(t0 + min(r, len - 1), H, h) * D + c0;
-      IO<TIO>::load8(p.q, off, qv);
-      IO<TIO>::load8(p.k, off, kv);
-      IO<TIO>::load8(p.v, off, v_r[ps]);
-      const float m = r < len ? 1.f : 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qv[e] *= m;
-        kv[e] *= m;
-        v_r[ps][e] *= m;
-      }
-    }
+    IO<TIO>::unpack8(qraw[ps], qv);
+    IO<TIO>::unpack8(kraw[ps], kv);
+    IO<TIO>::unpack8(vraw[ps], v_r[ps]);
+    const float m = r < len ? 1.f : 0.f;
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
-    sq = group_sum<TPR>(sq);
-    sk = group_sum<TPR>(sk);
+    for (int e = 0; e < 8; ++e) {
+      qv[e] *= m;
+      kv[e] *= m;
+      v_r[ps][e] *= m;
+      sq += qv[e] * qv[e];
+      sk += kv[e] * kv[e];
+    }
+    sq = group_sum_dpp<TPR>(sq);
+    sk = group_sum_dpp<TPR>(sk);
     const float rq = 1.0f / sqrtf(sq + 1e-6f), rk = 1.0f / sqrtf(sk + 1e-6f);
     bf16x8 qb, kb;
 #pragma unroll
@@ -100,10 +141,9 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   }
   // --- beta and the in-chunk cumsum of the log decay (wave 0) ---
   if (w == 0) {
-    const int64_t o = tok(t0 + min(l, len - 1), H, h);
     const float m = l < len ? 1.f : 0.f;
-    float lam = m * IO<TIO>::load1(p.g, o);
-    const float bt = m * sigmoidf(IO<TIO>::load1(p.b, o));
+    float lam = m * graw;
+    const float bt = m * sigmoidf(braw);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
       const float y = __shfl_up(lam, m, 64);
@@ -144,38 +184,42 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
     }
   }
 
-  // --- M and P, transposed tiles so that each lane owns 4 consecutive s ---
-  {
-    const int R = w;
-    const int r = 16 * R + (l & 15);
+  // --- M and P on the lower / diagonal tiles: lane owns X[r][s .. s+3],
+  // r = 16 rb + jj, s = 16 sb + 4g + i ---
+#pragma unroll
+  for (int slot = 0; slot < 3; ++slot) {
+    const int rb = tile_rb(w, slot), sb = tile_sb(w, slot);
+    const int r = 16 * rb + jj, s0 = 16 * sb + 4 * g;
+    f32x4 aM = zero4(), aP = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 32) {
+      const bf16x8 a = frag_rk(Ks, PD, 16 * sb, k0);
+      aM = mma(a, frag_rk(Ks, PD, 16 * rb, k0), aM);
+      aP = mma(a, frag_rk(Qs, PD, 16 * rb, k0), aP);
+    }
     const float gr = gam_s[r], br = beta_s[r];
+    float Lv[4], Pv[4];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      float Lv[4] = {0.f, 0.f, 0.f, 0.f}, Pv[4] = {0.f, 0.f, 0.f, 0.f};
-      const int s0 = 16 * sb + 4 * (l >> 4);
-      if (sb <= R) {
-        f32x4 aM = zero4(), aP = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < D; k0 += 32) {
-          const bf16x8 a = frag_rk(Ks, PD, 16 * sb, k0);
-          aM = mma(a, frag_rk(Ks, PD, 16 * R, k0), aM);
-          aP = mma(a, frag_rk(Qs, PD, 16 * R, k0), aP);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = s0 + i;
-          if (r >= s) {
-            const float E = fast_exp(gr - gam_s[s]);
-            Pv[i] = p.scale * aP[i] * E;
-            if (r > s) Lv[i] = br * aM[i] * E;
-          }
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int s = s0 + i;
+      // Gamma is non-increasing, so the exponent is <= 0 wherever it is used
+      const float E = fast_exp(fminf(gr - gam_s[s], 0.f));
+      Pv[i] = r >= s ? p.scale * aP[i] * E : 0.f;
+      Lv[i] = r > s ? br * aM[i] * E : 0.f;
+    }
+    if (tile_valid(w, slot)) {
       *reinterpret_cast<float4*>(Lf + r * PL + s0) = make_float4(Lv[0], Lv[1], Lv[2], Lv[3]);
-      st_bf16x4(p.P + (ch * C + r) * C + s0, Pv[0], Pv[1], Pv[2], Pv[3]);
+      st_bf16x4(As + r * PC + s0, Pv[0], Pv[1], Pv[2], Pv[3]);
     }
   }
   __syncthreads();
+
+  // --- P out: rows of 128 bytes, 16 bytes per lane ---
+#pragma unroll
+  for (int it = 0; it < C * C / 8 / kThreads; ++it) {
+    const int idx = tid + kThreads * it, row = idx / 8, c8 = (idx % 8) * 8;
+    *reinterpret_cast<u32x4*>(p.P + (ch * C + row) * C + c8) = *reinterpret_cast<const u32x4*>(As + row * PC + c8);
+  }
 
   // --- beta * Kbar and beta * V overwrite the operand tiles ---
 #pragma unroll
@@ -192,26 +236,58 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
     *reinterpret_cast<bf16x8*>(Vs + r * PD + c0) = vb;
   }
 
-  // --- A = (I + L)^-1 by forward substitution, one column per lane (wave 0) ---
-  if (w == 0) {
-    float a[C];
+  // --- A = (I + L)^-1 in 16x16 blocks X_ij (fp32): wave i inverts the diagonal
+  // block I + L_ii by forward substitution (lane = column) ... ---
+  {
+    const int i0 = 16 * w;
+    float a[16];
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      float acc = (r == l) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      float acc = r == jj ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < (r & ~3); s += 4) {
-        const float4 L4 = *reinterpret_cast<const float4*>(Lf + r * PL + s);
-        acc -= L4.x * a[s] + L4.y * a[s + 1] + L4.z * a[s + 2] + L4.w * a[s + 3];
-      }
-#pragma unroll
-      for (int s = (r & ~3); s < r; ++s) acc -= Lf[r * PL + s] * a[s];
+      for (int s = 0; s < r; ++s) acc -= Lf[(i0 + r) * PL + i0 + s] * a[s];
       a[r] = acc;
     }
+    if (l < 16) {
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      As[r * PC + l] = to_bf16(a[r]);
-      p.A[(ch * C + r) * C + l] = f32_to_bf16_bits(a[r]);
+      for (int r = 0; r < 16; ++r) Xf[(i0 + r) * PL + i0 + jj] = a[r];
     }
+  }
+  __syncthreads();
+  // ... then wave j walks down block column j on fp32 MFMA:
+  //   X_ij = -X_ii (sum_{m=j}^{i-1} L_im X_mj),  i = j+1 .. 3
+  {
+    const int j0 = 16 * w;
+    float* const scr = reinterpret_cast<float*>(As) + 256 * w;   // 16x16 per wave
+    for (int i = w + 1; i < 4; ++i) {
+      const int i0 = 16 * i;
+      f32x4 sacc = zero4();
+      for (int m = w; m < i; ++m) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          sacc = mma_f32(Lf[(i0 + jj) * PL + 16 * m + 4 * kk + g], Xf[(16 * m + 4 * kk + g) * PL + j0 + jj], sacc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) scr[(4 * g + e) * 16 + jj] = sacc[e];
+      f32x4 x = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) x = mma_f32(Xf[(i0 + jj) * PL + i0 + 4 * kk + g], scr[(4 * kk + g) * 16 + jj], x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Xf[(i0 + 4 * g + e) * PL + j0 + jj] = -x[e];
+    }
+  }
+  __syncthreads();
+  // --- A out (bf16): the operand tile for W, U' and the workspace copy; the
+  // blocks above the diagonal are zero ---
+#pragma unroll
+  for (int it = 0; it < C * C / 8 / kThreads; ++it) {
+    const int idx = tid + kThreads * it, row = idx / 8, c8 = (idx % 8) * 8;
+    const bool on = (c8 >> 4) <= (row >> 4);
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = to_bf16(on ? Xf[row * PL + c8 + e] : 0.f);
+    *reinterpret_cast<bf16x8*>(As + row * PC + c8) = v;
+    *reinterpret_cast<bf16x8*>(p.A + (ch * C + row) * C + c8) = v;
   }
   __syncthreads();
 
@@ -480,20 +556,14 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   dbeta_row -= eg * s_kz;
   const float dgc_loc = eh * s_kdkh;
 
-  // ---- phase 3: M, P, dP, dL on the 10 tiles (rb, sb), sb <= rb, of the strictly
-  // lower / diagonal 16x16 blocks, dealt 3-3-2-2 over the waves (the third slot of
-  // waves 2 and 3 repeats a tile and stores nothing).  Lane owns X[r][s .. s+3],
+  // ---- phase 3: M, P, dP, dL on the 10 lower / diagonal tiles (rb, sb), three
+  // slots per wave (tile_rb / tile_sb).  Lane owns X[r][s .. s+3],
   // r = 16 rb + jj, s = 16 sb + 4g + i. ----
-  // per wave, nibble `slot` of these words: rb and sb of its tiles
-  constexpr uint32_t kRb[4] = {0x333, 0x223, 0x112, 0x001};
-  constexpr uint32_t kSb[4] = {0x210, 0x103, 0x002, 0x001};
   float dme[3][4], dpe[3][4];
 #pragma unroll
   for (int slot = 0; slot < 3; ++slot) {
-    const uint32_t rbw = w == 0 ? kRb[0] : w == 1 ? kRb[1] : w == 2 ? kRb[2] : kRb[3];
-    const uint32_t sbw = w == 0 ? kSb[0] : w == 1 ? kSb[1] : w == 2 ? kSb[2] : kSb[3];
-    const int rb = (rbw >> (4 * slot)) & 15, sb = (sbw >> (4 * slot)) & 15;
-    const bool valid = slot < 2 || w < 2;
+    const int rb = tile_rb(w, slot), sb = tile_sb(w, slot);
+    const bool valid = tile_valid(w, slot);
     const int rr = 16 * rb + jj, s0 = 16 * sb + 4 * g;
     f32x4 G1 = zero4(), G2 = zero4(), Mr = zero4(), Pr = zero4();
 #pragma unroll
@@ -536,10 +606,8 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   }
 #pragma unroll
   for (int slot = 0; slot < 3; ++slot) {
-    const uint32_t rbw = w == 0 ? kRb[0] : w == 1 ? kRb[1] : w == 2 ? kRb[2] : kRb[3];
-    const uint32_t sbw = w == 0 ? kSb[0] : w == 1 ? kSb[1] : w == 2 ? kSb[2] : kSb[3];
-    const int rb = (rbw >> (4 * slot)) & 15, sb = (sbw >> (4 * slot)) & 15;
-    if (slot < 2 || w < 2) {
+    const int rb = tile_rb(w, slot), sb = tile_sb(w, slot);
+    if (tile_valid(w, slot)) {
       const int rr = 16 * rb + jj, s0 = 16 * sb + 4 * g;
       st4_s<C, 0>(dME, rr, s0, dme[slot][0], dme[slot][1], dme[slot][2], dme[slot][3]);
       st4_s<C, 0>(dPE, rr, s0, dpe[slot][0], dpe[slot][1], dpe[slot][2], dpe[slot][3]);
