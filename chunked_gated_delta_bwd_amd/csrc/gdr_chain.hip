@@ -14,12 +14,12 @@
 // Workgroups have nine waves with fixed jobs:
 //   waves 0-3  compute: the MFMA products of one chunk step, two barriers a step;
 //              their results for later kernels (S, U or dS, dU of the chunk) go
-//              to LDS only;
+//              to LDS only; for the scalar gate with bf16 inputs they also turn
+//              the next chunk's dO slice into fq dO in bf16 high + low parts;
 //   wave  4    converter: writes those slices from LDS to global memory with
-//              16-byte stores, and turns the chunk's dO slice into the bf16 form
-//              the MFMAs take (fq dO in high + low parts for the scalar gate with
-//              bf16 inputs; fp32 inputs: dO high + low, loaded into registers one
-//              step ahead);
+//              16-byte stores (dU one step late, from a second buffer, where LDS
+//              allows), and for fp32 inputs forms dO high + low from registers
+//              loaded one step ahead;
 //   waves 5-8  movers: copy the chunk tiles and the small per-chunk data (dO
 //              slice, row factors, decay) global -> LDS with direct-to-LDS loads
 //              (no registers, no ALU), up to two chunks ahead.
@@ -83,7 +83,11 @@ struct ChainCfg {
   static constexpr int bSlot = bX3 + (RAW ? 2 * XB : 0);
   static constexpr int bdS = bSlot + 3 * SLOT;                     // 16 x D state-gradient slice
   static constexpr int bdU = bdS + 16 * D * 2;                     // 16 x 64: dU^T
-  static constexpr int bPF = bdU + 16 * C * 2;                     // 256 B sink of the L2 prefetches
+  static constexpr int dUB = 16 * C * 2;
+  // dU^T in two buffers (step parity) where LDS allows: the converter then stores
+  // it during the next step instead of holding up the first barrier
+  static constexpr int NDU = bdU + 2 * dUB + 256 <= 160 * 1024 ? 2 : 1;
+  static constexpr int bPF = bdU + NDU * dUB;                      // 256 B sink of the L2 prefetches
   static constexpr int bEnd = bPF + 256;
   // forward role
   static constexpr int fW = 0, fK = TB, fUp = 2 * TB, fUpl = fUp + XB, bufF = fUpl + (SPLIT ? XB : 0);
@@ -101,9 +105,11 @@ struct ChainCfg {
   static constexpr int nSb = LO ? 0 : (RAW ? 3 : 2);   // dO, fac, decay
   static constexpr int nSf = LO ? 0 : (RAW ? 2 : 1);   // fac, decay
   static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 : 2) * NJ + nSb;
+  // L2 prefetch distance in chunk steps (one prefetch load per mover wave per step)
+  static constexpr int PFD = 5;
   static constexpr int fwdA = NJ + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
   static_assert(bytes <= 160 * 1024, "LDS budget");
-  static_assert(2 * bwdA + bwdB + 3 < 64 && 2 * fwdA + fwdB + 3 < 64, "vmcnt range");
+  static_assert(2 * bwdA + bwdB + PFD - 2 < 64 && 2 * fwdA + fwdB + PFD - 2 < 64, "vmcnt range");
 };
 
 struct ChunkGeo {
@@ -393,31 +399,27 @@ struct LoRegs {
   }
 };
 
-// raw mode: fq dO split into bf16 high and low parts, from the slot's dO slice
+// scalar gate, bf16 inputs: fq dO of the chunk's dO slice in bf16 high + low
+// parts (X2, X3), rows 16w .. 16w+15 by compute wave w (lane: row 16w + l/4,
+// columns 4(l%4) .. +3)
 template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void convert_raw(const char* slot, char* x2, char* x3) {
+__device__ __forceinline__ void convert_raw_rows(const char* slot, char* x2, char* x3, int w) {
   using Cf = ChainCfg<D, TIO, GATE>;
   const int l = lane_id();
-  const int o = prow<16>(l) * 32;
-  const u32x4 r0 = *reinterpret_cast<const u32x4*>(slot + Cf::sDO + o);
-  const u32x4 r1 = *reinterpret_cast<const u32x4*>(slot + Cf::sDO + o + 16);
-  const float fq = reinterpret_cast<const float*>(slot + Cf::sFac)[l];
-  float a[8], b[8];
-  IO<bf16>::unpack8(r0, a);
-  IO<bf16>::unpack8(r1, b);
-  bf16x8 h0, h1, l0, l1;
+  const int row = 16 * w + (l >> 2), o = prow<16>(row) * 32 + (l & 3) * 8;
+  const uint2 r = *reinterpret_cast<const uint2*>(slot + Cf::sDO + o);
+  const float fq = reinterpret_cast<const float*>(slot + Cf::sFac)[row];
+  const float a[4] = {bf16_bits_to_f32(r.x & 0xffffu), bf16_bits_to_f32(r.x >> 16), bf16_bits_to_f32(r.y & 0xffffu),
+                      bf16_bits_to_f32(r.y >> 16)};
+  float hv[4], lv[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float ya = fq * a[e], yb = fq * b[e];
-    h0[e] = to_bf16(ya);
-    h1[e] = to_bf16(yb);
-    l0[e] = to_bf16(ya - float(h0[e]));
-    l1[e] = to_bf16(yb - float(h1[e]));
+  for (int e = 0; e < 4; ++e) {
+    const float y = fq * a[e];
+    hv[e] = float(to_bf16(y));
+    lv[e] = y - hv[e];
   }
-  *reinterpret_cast<bf16x8*>(x2 + o) = h0;
-  *reinterpret_cast<bf16x8*>(x2 + o + 16) = h1;
-  *reinterpret_cast<bf16x8*>(x3 + o) = l0;
-  *reinterpret_cast<bf16x8*>(x3 + o + 16) = l1;
+  *reinterpret_cast<uint2*>(x2 + o) = pack4_bf16(hv[0], hv[1], hv[2], hv[3]);
+  *reinterpret_cast<uint2*>(x3 + o) = pack4_bf16(lv[0], lv[1], lv[2], lv[3]);
 }
 
 // the decay of this lane's four accumulator rows j = 16 jb + 4 g .. +3
@@ -555,10 +557,10 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
     move_small<D, TIO, GATE>(p, se, h, chunk(1), v0, slot(1), mw, false);
     move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), v0, smem + Cf::bufF, mw);
-    for (int c = 2; c < 5; ++c) prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(c), sl, mw, smem + Cf::fPF);
-    wait_vm<Cf::fwdA + Cf::fwdB + Cf::fwdA + 3>();
+    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(c), sl, mw, smem + Cf::fPF);
+    wait_vm<Cf::fwdA + Cf::fwdB + Cf::fwdA + Cf::PFD - 2>();
     chain_barrier();   // B0
-    wait_vm<Cf::fwdB + Cf::fwdA + 3>();
+    wait_vm<Cf::fwdB + Cf::fwdA + Cf::PFD - 2>();
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
@@ -566,7 +568,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       wait_vm<Cf::fwdA + 1 + Cf::fwdB>();
       chain_barrier();   // B2
       move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0, smem + (k & 1) * Cf::bufF, mw);
-      prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(k + 5), sl, mw, smem + Cf::fPF);
+      prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(k + Cf::PFD), sl, mw, smem + Cf::fPF);
       wait_vm<Cf::fwdB + Cf::fwdA + 2>();
     }
     wait_vm<0>();
@@ -585,7 +587,8 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
   const int v0 = 16 * sl;
   const int nck = se.nchunks;
   char* dSl = smem + Cf::bdS;
-  char* dUt = smem + Cf::bdU;
+  // dU^T of step k (buffer k & 1 when there are two)
+  auto dUbuf = [&](int k) { return smem + Cf::bdU + (Cf::NDU == 2 ? (k & 1) : 0) * Cf::dUB; };
   // step k walks chunk c0 + nck - 1 - k (last to first), clamped past the end
   auto chunk = [&](int k) { return se.c0 + nck - 1 - min(k, nck - 1); };
   auto slot = [&](int k) { return smem + Cf::bSlot + (k % 3) * Cf::SLOT; };
@@ -604,6 +607,10 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       }
     }
     if (nck > 0) chain_barrier();   // B0
+    // raw mode: the compute waves form fq dO (high, low) of each chunk's dO slice
+    // one step ahead, a quarter each (published by the next first barrier)
+    if constexpr (Cf::RAW)
+      if (nck > 0) convert_raw_rows<D, TIO, GATE>(slot(0), smem + Cf::bX2, smem + Cf::bX3, w);
     for (int k = 0; k < nck; ++k) {
       const int buf = k & 1;
       const char* Bb = smem + buf * Cf::bufB;
@@ -611,6 +618,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       const char* X1 = Cf::LO ? smem + Cf::bX1 + buf * Cf::XB : sl_k + Cf::sDO;
       const char* X2 = smem + Cf::bX2 + buf * Cf::XB;
       const char* X3 = smem + Cf::bX3 + buf * Cf::XB;
+      char* dUt = dUbuf(k);
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
@@ -638,13 +646,14 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         ad += ak;
       }
       st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
-      chain_barrier();   // B2
-      // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU
+      // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU: the first two terms do
+      // not depend on dU and are issued before the barrier
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
+      f32x4 an[NJW];
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int jb = w * NJW + x;
-        f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g), aw = zero4();
+        f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += 32) {
           const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, k0);
@@ -657,10 +666,21 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
             a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, k0), bh, a);
             if constexpr (Cf::LO) a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
           }
-          aw = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C, 1>(dUt, 0, k0), aw);
         }
-        acc[x] = a - aw;
+        an[x] = a;
       }
+      chain_barrier();   // B2
+#pragma unroll
+      for (int x = 0; x < NJW; ++x) {
+        const int jb = w * NJW + x;
+        f32x4 aw = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32)
+          aw = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C, 1>(dUt, 0, k0), aw);
+        acc[x] = an[x] - aw;
+      }
+      if constexpr (Cf::RAW)
+        convert_raw_rows<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
     }
     if (p.dh0) {
 #pragma unroll
@@ -680,22 +700,24 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       R.load(p, se, h, chunk(1), v0, true);
     }
     chain_barrier();   // B0
-    if constexpr (Cf::RAW) convert_raw<D, TIO, GATE>(slot(0), smem + Cf::bX2, smem + Cf::bX3);
     for (int k = 0; k < nck; ++k) {
       const int64_t ch = int64_t(h) * p.NC + chunk(k);
       const int nb = (k + 1) & 1;
       chain_barrier();   // B1
       store_slice<D>(dSl, p.dS + (ch * D + v0) * D);
+      // two dU buffers: dU of the previous step (its buffer is not written again
+      // before the next B2); one buffer: this step's, after B2
+      if (Cf::NDU == 2 && k > 0)
+        store_slice<C, 1>(dUbuf(k - 1), p.dU + ((int64_t(h) * p.NC + chunk(k - 1)) * D + v0) * C);
       chain_barrier();   // B2
-      store_slice<C, 1>(dUt, p.dU + (ch * D + v0) * C);
-      if constexpr (Cf::RAW) {
-        convert_raw<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + nb * Cf::XB, smem + Cf::bX3 + nb * Cf::XB);
-      } else if constexpr (Cf::LO) {
+      if (Cf::NDU == 1) store_slice<C, 1>(dUbuf(k), p.dU + (ch * D + v0) * C);
+      if constexpr (Cf::LO) {
         R.store_dO(smem + Cf::bX1 + nb * Cf::XB, smem + Cf::bX2 + nb * Cf::XB);
         R.store_dec(reinterpret_cast<float*>(slot(k + 1) + Cf::sDec));
         R.load(p, se, h, chunk(k + 2), v0, true);
       }
     }
+    if (Cf::NDU == 2) store_slice<C, 1>(dUbuf(nck - 1), p.dU + ((int64_t(h) * p.NC + chunk(nck - 1)) * D + v0) * C);
     wait_vm<0>();
   } else {
     if (nck == 0) return;
@@ -707,10 +729,10 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
     move_small<D, TIO, GATE>(p, se, h, chunk(1), v0, slot(1), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), smem + Cf::bufB, mw);
-    for (int c = 2; c < 5; ++c) prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(c), sl, mw, smem + Cf::bPF);
-    wait_vm<Cf::bwdA + Cf::bwdB + Cf::bwdA + 3>();
+    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(c), sl, mw, smem + Cf::bPF);
+    wait_vm<Cf::bwdA + Cf::bwdB + Cf::bwdA + Cf::PFD - 2>();
     chain_barrier();   // B0
-    wait_vm<Cf::bwdB + Cf::bwdA + 3>();
+    wait_vm<Cf::bwdB + Cf::bwdA + Cf::PFD - 2>();
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
@@ -718,7 +740,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       wait_vm<Cf::bwdA + 1 + Cf::bwdB>();
       chain_barrier();   // B2
       move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
-      prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(k + 5), sl, mw, smem + Cf::bPF);
+      prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(k + Cf::PFD), sl, mw, smem + Cf::bPF);
       wait_vm<Cf::bwdB + Cf::bwdA + 2>();
     }
     wait_vm<0>();
