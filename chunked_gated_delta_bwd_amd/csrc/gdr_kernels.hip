@@ -336,19 +336,30 @@ struct GradLds {
   // the S tile later holds Kn and Qn, the dS tile dME and dPE
   static constexpr int TSx = TS > 2 * TR ? TS : 2 * TR;
   static constexpr int TdSx = TS > 2 * TA ? TS : 2 * TA;
-  // loads per wave of the first group (tiles + one row of per-row scalars) and
-  // of the second (S, dS)
-  static constexpr int G1 = (2 * TU + TA + (kDma ? 2 * TR : 0)) / 1024 / 4 + 1;
-  static constexpr int G2 = 2 * TS / 1024 / 4;
   static_assert(TU == TR, "raw q rows reuse the dU^T tile");
 };
 
+// Eight waves: wave w works on row block rb = w % 4 (rows 16 rb ..) and column
+// half hf = w / 4 of every D-wide result; waves w and w + 4 share a SIMD.
+constexpr int kGradWaves = 8;
+constexpr int kGradThreads = 64 * kGradWaves;
+
+// phase-3 tiles (rb, sb), sb <= rb: slot 0 of every wave, slot 1 of waves 0 and 1
+// (so that each SIMD gets two or three of the ten tiles)
+__device__ __forceinline__ int g3_rb(int w, int slot) {
+  return slot == 0 ? (w < 4 ? 3 : w < 7 ? 2 : 1) : (w == 0 ? 1 : 0);
+}
+__device__ __forceinline__ int g3_sb(int w, int slot) {
+  return slot == 0 ? (w < 4 ? w : w < 7 ? w - 4 : 0) : (w == 0 ? 1 : 0);
+}
+
 template <int D, typename TIO>
-__global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
-  using Dm = Dims<D>;
+__global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
   using Ly = GradLds<D, TIO>;
   constexpr bool kDma = Ly::kDma;
-  constexpr int TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS, NJB = Dm::NJB;
+  constexpr int NJB = D / 16, NJH = NJB / 2;                 // 16-wide blocks along D; per half
+  constexpr int TPR = D / 8, RPP = kGradThreads / TPR, NPASS = C / RPP;   // row sweeps, 8 elements a thread
+  static_assert(NPASS >= 1 && C % RPP == 0, "row sweep");
   __shared__ __attribute__((aligned(1024))) char Sx[Ly::TSx];         // S; phases 3-4: Kn, Qn
   __shared__ __attribute__((aligned(1024))) char dSx[Ly::TdSx];       // dS; phases 3-4: dME, dPE
   __shared__ __attribute__((aligned(1024))) char dUT[Ly::TU];         // phase 1: dU^T; then raw q
@@ -360,10 +371,11 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   // per-row scalars: Gamma, 1/|q|, 1/|k|, beta (0 past the end)
   __shared__ __attribute__((aligned(256))) float sc_s[4][C];
   // fixed-order partial sums (deterministic): column sums of the pairwise dGamma
-  // term per wave, row sums and dbeta per row, two per-wave chunk scalars
-  __shared__ float colsum_s[4][C], rowsum_s[C], dbeta_s[C], red_s[4][2];
-  // phase-3 row sums of dGamma and dbeta per column block sb (written for sb <= r / 16)
-  __shared__ float rowq_s[4][C], rowb_s[4][C];
+  // term per row block, row sums and dbeta per column half, phase-3 row sums per
+  // column block (written for sb <= r / 16), the L2-norm dot products per half,
+  // two per-wave chunk scalars
+  __shared__ float colsum_s[4][C], rowsum_s[2][C], dbeta_s[2][C], rowq_s[4][C], rowb_s[4][C];
+  __shared__ float l2_s[2][2][C], red_s[kGradWaves][2];
   const float* const gam_s = sc_s[0];
   const float* const rq_s = sc_s[1];
   const float* const rk_s = sc_s[2];
@@ -374,6 +386,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   const int t0 = ce.t_start, len = ce.len;
   const int tid = threadIdx.x, l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = w & 3, hf = w >> 2;
   const int g = l >> 4, jj = l & 15;
   const int64_t ch = int64_t(h) * p.NC + c;
   const int H = p.H;
@@ -382,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   char* const Qn = Sx + Ly::TR;
   char* const dME = dSx;
   char* const dPE = dSx + Ly::TA;
-  const int r = 16 * w + jj;
+  const int r = 16 * rb + jj;
   const int64_t trow = tok(t0 + min(r, len - 1), H, h) * D;
   auto u16 = [](const uint16_t* x) { return reinterpret_cast<const char*>(x); };
   auto row_of = [&](const void* x, int rr) {
@@ -390,25 +403,27 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   };
 
   // ---- first group: per-row scalars, phase-1 tiles, dO (and v) ----
-  dma4(w == 0 ? static_cast<const void*>(p.gam + ch * C + l) : static_cast<const void*>(p.rho + (ch * 3 + w - 1) * C + l),
-       reinterpret_cast<char*>(sc_s[w]));
-  dma_tile<C, 1, D, 4>(dUT, [&](int v) { return u16(p.dU + (ch * D + v) * C); }, w);
-  dma_tile<C, 0, C, 4>(At, [&](int rr) { return u16(p.A + (ch * C + rr) * C); }, w);
-  dma_tile<C, 0, D, 4>(UT, [&](int v) { return u16(p.U + (ch * D + v) * C); }, w);
+  if (w < 4)
+    dma4(w == 0 ? static_cast<const void*>(p.gam + ch * C + l) : static_cast<const void*>(p.rho + (ch * 3 + w - 1) * C + l),
+         reinterpret_cast<char*>(sc_s[w]));
+  dma_tile<C, 1, D, kGradWaves>(dUT, [&](int v) { return u16(p.dU + (ch * D + v) * C); }, w);
+  dma_tile<C, 0, C, kGradWaves>(At, [&](int rr) { return u16(p.A + (ch * C + rr) * C); }, w);
+  dma_tile<C, 0, D, kGradWaves>(UT, [&](int v) { return u16(p.U + (ch * D + v) * C); }, w);
   if constexpr (kDma) {
-    dma_tile<D, 0, C, 4>(dOt, [&](int rr) { return row_of(p.dO, rr); }, w);
-    dma_tile<D, 0, C, 4>(Vt, [&](int rr) { return row_of(p.v, rr); }, w);
+    dma_tile<D, 0, C, kGradWaves>(dOt, [&](int rr) { return row_of(p.dO, rr); }, w);
+    dma_tile<D, 0, C, kGradWaves>(Vt, [&](int rr) { return row_of(p.v, rr); }, w);
   }
   // ---- second group: S, dS ----
-  dma_tile<D, 0, D, 4>(Sx, [&](int v) { return u16(p.S + (ch * D + v) * D); }, w);
-  dma_tile<D, 0, D, 4>(dSx, [&](int v) { return u16(p.dS + (ch * D + v) * D); }, w);
+  dma_tile<D, 0, D, kGradWaves>(Sx, [&](int v) { return u16(p.S + (ch * D + v) * D); }, w);
+  dma_tile<D, 0, D, kGradWaves>(dSx, [&](int v) { return u16(p.dS + (ch * D + v) * D); }, w);
+  constexpr int G2 = 2 * DmaTile<D, D, kGradWaves>::kPerWave;   // loads of the second group per wave
 
   // fp32 inputs: dO rounded into its tile, v and raw q, k rows kept in registers
-  typename IO<TIO>::Raw4 vraw[kDma ? 1 : NJB];
+  typename IO<TIO>::Raw4 vraw[kDma ? 1 : NJH];
   typename IO<TIO>::Raw8 qraw[kDma ? 1 : NPASS], kraw[kDma ? 1 : NPASS];
   if constexpr (!kDma) {
 #pragma unroll
-    for (int vb = 0; vb < NJB; ++vb) vraw[vb] = IO<TIO>::load_raw4(p.v, trow + 16 * vb + 4 * g);
+    for (int q = 0; q < NJH; ++q) vraw[q] = IO<TIO>::load_raw4(p.v, trow + 16 * (hf * NJH + q) + 4 * g);
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int rr = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
@@ -427,19 +442,21 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) colsum_s[x][tid] = 0.f;
   }
-  if constexpr (kDma) wait_vm<Ly::G2>();   // the first group has landed
+  if constexpr (kDma) wait_vm<G2>();   // the first group has landed
   else wait_vm<0>();
   chain_barrier();   // B_a
 
-  // ---- phase 1: dY = A^T dU (lane owns dY[r][v .. v+3], r = 16w + jj); dv; sum dY*v ----
+  // ---- phase 1: dY = A^T dU (lane owns dY[r][v .. v+3], r = 16 rb + jj, v in
+  // this wave's half); dv; sum dY*v ----
   const float br = beta_s[r];
   float dbeta_row = 0.f, dgam_row = 0.f;
-  f32x4 dvv[NJB];
+  f32x4 dvv[NJH];
 #pragma unroll
-  for (int vb = 0; vb < NJB; ++vb) {
+  for (int q = 0; q < NJH; ++q) {
+    const int vb = hf * NJH + q;
     f32x4 a = zero4();
 #pragma unroll
-    for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_rk_s<C, 1>(dUT, 16 * vb, k0), frag_kc_s<C, 0>(At, 16 * w, k0), a);
+    for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_rk_s<C, 1>(dUT, 16 * vb, k0), frag_kc_s<C, 0>(At, 16 * rb, k0), a);
     const int v = 16 * vb + 4 * g;
     st4_s<D>(dYt, r, v, a[0], a[1], a[2], a[3]);
     // rows past the end: dY is exactly zero there, so the clamped v row adds nothing
@@ -449,44 +466,47 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) vv[i] = float(vb4[i]);
     } else {
-      IO<TIO>::unpack4(vraw[vb], vv);
+      IO<TIO>::unpack4(vraw[q], vv);
     }
     dbeta_row += a[0] * vv[0] + a[1] * vv[1] + a[2] * vv[2] + a[3] * vv[3];
-    dvv[vb] = a;
+    dvv[q] = a;
   }
   wait_vm<0>();
   chain_barrier();   // B_b: S, dS and all of dY in LDS; dU^T, A and v are no longer read
 
   // ---- raw q, k rows (bf16 inputs) into the freed dU^T and v tiles; dv ----
   if constexpr (kDma) {
-    dma_tile<D, 0, C, 4>(dUT, [&](int rr) { return row_of(p.q, rr); }, w);
-    dma_tile<D, 0, C, 4>(Vt, [&](int rr) { return row_of(p.k, rr); }, w);
+    dma_tile<D, 0, C, kGradWaves>(dUT, [&](int rr) { return row_of(p.q, rr); }, w);
+    dma_tile<D, 0, C, kGradWaves>(Vt, [&](int rr) { return row_of(p.k, rr); }, w);
   }
   if (r < len) {
 #pragma unroll
-    for (int vb = 0; vb < NJB; ++vb)
-      IO<TIO>::store4(p.dv, trow + 16 * vb + 4 * g, br * dvv[vb][0], br * dvv[vb][1], br * dvv[vb][2], br * dvv[vb][3]);
+    for (int q = 0; q < NJH; ++q)
+      IO<TIO>::store4(p.dv, trow + 16 * (hf * NJH + q) + 4 * g, br * dvv[q][0], br * dvv[q][1], br * dvv[q][2],
+                      br * dvv[q][3]);
   }
 
-  // ---- phase 2: Z = dY S, dQbar = dO S, dKhat = U dS (transposed tiles) ----
-  f32x4 aZ[NJB], aQ[NJB], aK[NJB];
+  // ---- phase 2: Z = dY S, dQbar = dO S, dKhat = U dS (transposed tiles), this
+  // wave's column half ----
+  f32x4 aZ[NJH], aQ[NJH], aK[NJH];
 #pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
-    aZ[jb] = aQ[jb] = aK[jb] = zero4();
+  for (int q = 0; q < NJH; ++q) {
+    const int jb = hf * NJH + q;
+    aZ[q] = aQ[q] = aK[q] = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += 32) {
       const bf16x8 aS = frag_kc_s<D>(Sx, 16 * jb, k0);
-      aZ[jb] = mma(aS, frag_rk_s<D>(dYt, 16 * w, k0), aZ[jb]);
-      aQ[jb] = mma(aS, frag_rk_s<D>(dOt, 16 * w, k0), aQ[jb]);
-      aK[jb] = mma(frag_kc_s<D>(dSx, 16 * jb, k0), frag_kc_s<C, 0>(UT, 16 * w, k0), aK[jb]);
+      aZ[q] = mma(aS, frag_rk_s<D>(dYt, 16 * rb, k0), aZ[q]);
+      aQ[q] = mma(aS, frag_rk_s<D>(dOt, 16 * rb, k0), aQ[q]);
+      aK[q] = mma(frag_kc_s<D>(dSx, 16 * jb, k0), frag_kc_s<C, 0>(UT, 16 * rb, k0), aK[q]);
     }
   }
   // state term of dGamma_C: sum_{v,j} S dS, the trace of S dS^T taken over its
-  // diagonal 16x16 blocks on MFMA (lane holds block rows 4g+i, column jj)
+  // diagonal 16x16 blocks on MFMA (one block per wave; lane holds block rows
+  // 4g+i, column jj)
   float sdot = 0.f;
-#pragma unroll
-  for (int bb = 0; bb < NJB / 4; ++bb) {
-    const int vb = 16 * (w + 4 * bb);
+  if (w < NJB) {
+    const int vb = 16 * w;
     f32x4 t = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += 32) t = mma(frag_rk_s<D>(Sx, vb, k0), frag_rk_s<D>(dSx, vb, k0), t);
@@ -522,10 +542,10 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     *reinterpret_cast<bf16x8*>(Kn + soff<D>(rr, c0)) = kb;
   }
   // dME, dPE start at zero: phase 3 writes only the tiles on and below the diagonal
-  for (int o = 16 * tid; o < 2 * Ly::TA; o += 16 * kThreads) *reinterpret_cast<u32x4*>(dME + o) = u32x4{0u, 0u, 0u, 0u};
+  for (int o = 16 * tid; o < 2 * Ly::TA; o += 16 * kGradThreads) *reinterpret_cast<u32x4*>(dME + o) = u32x4{0u, 0u, 0u, 0u};
   chain_barrier();   // B_d
 
-  // ---- fold the state-side terms (lane owns (r, j .. j+3)) ----
+  // ---- fold the state-side terms (lane owns (r, j .. j+3), j in this wave's half) ----
   // dKbar = -beta Z, Kbar = kn e^Gam, Khat = kn e^(GamC-Gam), Qbar = scale qn e^Gam:
   //   dkn = -beta e^Gam Z + e^(GamC-Gam) dKhat,  dqn = scale e^Gam dQbar,
   //   dGam_r  += <kn, dkn> - 2 e^(GamC-Gam) <kn, dKhat> + <qn, dqn>,
@@ -534,21 +554,21 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   const float eg = fast_exp(gr), eh = fast_exp(gam_s[C - 1] - gr);
   const float cz = -br * eg, cq = scale * eg;
   float s_kdkn = 0.f, s_kdkh = 0.f, s_qdqn = 0.f, s_kz = 0.f;
-  f32x4 dkn[NJB], dqn[NJB];
+  f32x4 dkn[NJH], dqn[NJH];
 #pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
-    const int j = 16 * jb + 4 * g;
+  for (int q = 0; q < NJH; ++q) {
+    const int j = 16 * (hf * NJH + q) + 4 * g;
     const bf16x4 kb = *reinterpret_cast<const bf16x4*>(Kn + soff<D>(r, j));
     const bf16x4 qb = *reinterpret_cast<const bf16x4*>(Qn + soff<D>(r, j));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float kn = float(kb[i]), qn = float(qb[i]);
-      const float z = aZ[jb][i], dkh = aK[jb][i];
-      dkn[jb][i] = fmaf(cz, z, eh * dkh);
-      dqn[jb][i] = cq * aQ[jb][i];
-      s_kdkn = fmaf(kn, dkn[jb][i], s_kdkn);
+      const float z = aZ[q][i], dkh = aK[q][i];
+      dkn[q][i] = fmaf(cz, z, eh * dkh);
+      dqn[q][i] = cq * aQ[q][i];
+      s_kdkn = fmaf(kn, dkn[q][i], s_kdkn);
       s_kdkh = fmaf(kn, dkh, s_kdkh);
-      s_qdqn = fmaf(qn, dqn[jb][i], s_qdqn);
+      s_qdqn = fmaf(qn, dqn[q][i], s_qdqn);
       s_kz = fmaf(kn, z, s_kz);
     }
   }
@@ -556,24 +576,24 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
   dbeta_row -= eg * s_kz;
   const float dgc_loc = eh * s_kdkh;
 
-  // ---- phase 3: M, P, dP, dL on the 10 lower / diagonal tiles (rb, sb), three
-  // slots per wave (tile_rb / tile_sb).  Lane owns X[r][s .. s+3],
-  // r = 16 rb + jj, s = 16 sb + 4g + i. ----
-  float dme[3][4], dpe[3][4];
+  // ---- phase 3: M, P, dP, dL on the 10 lower / diagonal tiles (tb, sb), slot 0
+  // of every wave and slot 1 of waves 0, 1 (g3_rb / g3_sb).  Lane owns X[rr][s .. s+3],
+  // rr = 16 tb + jj, s = 16 sb + 4g + i. ----
+  float dme[2][4], dpe[2][4];
 #pragma unroll
-  for (int slot = 0; slot < 3; ++slot) {
-    const int rb = tile_rb(w, slot), sb = tile_sb(w, slot);
-    const bool valid = tile_valid(w, slot);
-    const int rr = 16 * rb + jj, s0 = 16 * sb + 4 * g;
+  for (int slot = 0; slot < 2; ++slot) {
+    if (slot == 1 && w >= 2) break;
+    const int tb = g3_rb(w, slot), sb = g3_sb(w, slot);
+    const int rr = 16 * tb + jj, s0 = 16 * sb + 4 * g;
     f32x4 G1 = zero4(), G2 = zero4(), Mr = zero4(), Pr = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += 32) {
       const bf16x8 aU = frag_kc_s<C, 0>(UT, 16 * sb, k0);
-      G1 = mma(aU, frag_rk_s<D>(dOt, 16 * rb, k0), G1);
-      G2 = mma(aU, frag_rk_s<D>(dYt, 16 * rb, k0), G2);
+      G1 = mma(aU, frag_rk_s<D>(dOt, 16 * tb, k0), G1);
+      G2 = mma(aU, frag_rk_s<D>(dYt, 16 * tb, k0), G2);
       const bf16x8 aK = frag_rk_s<D>(Kn, 16 * sb, k0);
-      Mr = mma(aK, frag_rk_s<D>(Kn, 16 * rb, k0), Mr);
-      Pr = mma(aK, frag_rk_s<D>(Qn, 16 * rb, k0), Pr);
+      Mr = mma(aK, frag_rk_s<D>(Kn, 16 * tb, k0), Mr);
+      Pr = mma(aK, frag_rk_s<D>(Qn, 16 * tb, k0), Pr);
     }
     const float grr = gam_s[rr], brr = beta_s[rr];
     float rq = 0.f, rbt = 0.f;
@@ -594,103 +614,89 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
       rq += qv;
       // column sum over the 16 rows of the tile
       const float col = row16_sum(qv);
-      if (valid && jj == 0) colsum_s[rb][s] = -col;
+      if (jj == 0) colsum_s[tb][s] = -col;
     }
     // row sums over the 16 columns of the tile
     rq = xrow_sum(rq);
     rbt = xrow_sum(rbt);
-    if (valid && g == 0) {
+    if (g == 0) {
       rowq_s[sb][rr] = rq;
       rowb_s[sb][rr] = rbt;
     }
   }
 #pragma unroll
-  for (int slot = 0; slot < 3; ++slot) {
-    const int rb = tile_rb(w, slot), sb = tile_sb(w, slot);
-    if (tile_valid(w, slot)) {
-      const int rr = 16 * rb + jj, s0 = 16 * sb + 4 * g;
+  for (int slot = 0; slot < 2; ++slot) {
+    if (slot == 0 || w < 2) {
+      const int rr = 16 * g3_rb(w, slot) + jj, s0 = 16 * g3_sb(w, slot) + 4 * g;
       st4_s<C, 0>(dME, rr, s0, dme[slot][0], dme[slot][1], dme[slot][2], dme[slot][3]);
       st4_s<C, 0>(dPE, rr, s0, dpe[slot][0], dpe[slot][1], dpe[slot][2], dpe[slot][3]);
     }
   }
   // raw q, k of this lane's outputs, for the L2-norm backward at the end
-  typename IO<TIO>::Raw4 qo[kDma ? 1 : NJB], ko[kDma ? 1 : NJB];
+  typename IO<TIO>::Raw4 qo[kDma ? 1 : NJH], ko[kDma ? 1 : NJH];
   if constexpr (!kDma) {
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
-      qo[jb] = IO<TIO>::load_raw4(p.q, trow + 16 * jb + 4 * g);
-      ko[jb] = IO<TIO>::load_raw4(p.k, trow + 16 * jb + 4 * g);
+    for (int q = 0; q < NJH; ++q) {
+      qo[q] = IO<TIO>::load_raw4(p.q, trow + 16 * (hf * NJH + q) + 4 * g);
+      ko[q] = IO<TIO>::load_raw4(p.k, trow + 16 * (hf * NJH + q) + 4 * g);
     }
   }
   chain_barrier();   // B_e: dME, dPE complete
 
   // ---- phase 4: pairwise terms, dkn += (dME + dME^T) Kn + scale dPE^T Qn, dqn += scale dPE Kn ----
 #pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
+  for (int q = 0; q < NJH; ++q) {
+    const int jb = hf * NJH + q;
 #pragma unroll
     for (int k0 = 0; k0 < C; k0 += 32) {
       const bf16x8 aK = frag_kc_s<D>(Kn, 16 * jb, k0);
       const bf16x8 aQ2 = frag_kc_s<D>(Qn, 16 * jb, k0);
-      dkn[jb] = mma(aK, frag_rk_s<C, 0>(dME, 16 * w, k0), dkn[jb]);
-      dkn[jb] = mma(aK, frag_kc_s<C, 0>(dME, 16 * w, k0), dkn[jb]);
-      dkn[jb] = mma(aQ2, frag_kc_s<C, 0>(dPE, 16 * w, k0), dkn[jb]);
-      dqn[jb] = mma(aK, frag_rk_s<C, 0>(dPE, 16 * w, k0), dqn[jb]);
+      dkn[q] = mma(aK, frag_rk_s<C, 0>(dME, 16 * rb, k0), dkn[q]);
+      dkn[q] = mma(aK, frag_kc_s<C, 0>(dME, 16 * rb, k0), dkn[q]);
+      dkn[q] = mma(aQ2, frag_kc_s<C, 0>(dPE, 16 * rb, k0), dkn[q]);
+      dqn[q] = mma(aK, frag_rk_s<C, 0>(dPE, 16 * rb, k0), dqn[q]);
     }
   }
-  // ---- L2-norm backward: dq = rq (dqn - qn <qn, dqn>), dk likewise (K1 page, 3.3) ----
+  // ---- L2-norm backward: dq = rq (dqn - qn <qn, dqn>), dk likewise (K1 page, 3.3);
+  // the dot products add the two column halves ----
+  const float m = r < len ? 1.f : 0.f;
+  const float rq = m * rq_s[r], rk = m * rk_s[r];
+  float qn[NJH][4], kn[NJH][4];
   {
-    const float m = r < len ? 1.f : 0.f;
-    const float rq = m * rq_s[r], rk = m * rk_s[r];
     float pq = 0.f, pk = 0.f;
-    float qn[NJB][4], kn[NJB][4];
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
+    for (int q = 0; q < NJH; ++q) {
+      const int j = 16 * (hf * NJH + q) + 4 * g;
       if constexpr (kDma) {
-        const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(dUT + soff<D>(r, 16 * jb + 4 * g));
-        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Vt + soff<D>(r, 16 * jb + 4 * g));
+        const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(dUT + soff<D>(r, j));
+        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Vt + soff<D>(r, j));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { qn[jb][i] = float(q4[i]); kn[jb][i] = float(k4[i]); }
+        for (int i = 0; i < 4; ++i) { qn[q][i] = float(q4[i]); kn[q][i] = float(k4[i]); }
       } else {
-        IO<TIO>::unpack4(qo[jb], qn[jb]);
-        IO<TIO>::unpack4(ko[jb], kn[jb]);
+        IO<TIO>::unpack4(qo[q], qn[q]);
+        IO<TIO>::unpack4(ko[q], kn[q]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        qn[jb][i] *= rq;
-        kn[jb][i] *= rk;
-        pq += qn[jb][i] * dqn[jb][i];
-        pk += kn[jb][i] * dkn[jb][i];
+        qn[q][i] *= rq;
+        kn[q][i] *= rk;
+        pq += qn[q][i] * dqn[q][i];
+        pk += kn[q][i] * dkn[q][i];
       }
     }
     pq = xrow_sum(pq);
     pk = xrow_sum(pk);
-    if constexpr (kDma) {
-      // bf16 rows go out through LDS (the dO and dY tiles are free now), below
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const int j = 16 * jb + 4 * g;
-        st4_s<D>(dOt, r, j, rq * (dqn[jb][0] - qn[jb][0] * pq), rq * (dqn[jb][1] - qn[jb][1] * pq),
-                 rq * (dqn[jb][2] - qn[jb][2] * pq), rq * (dqn[jb][3] - qn[jb][3] * pq));
-        st4_s<D>(dYt, r, j, rk * (dkn[jb][0] - kn[jb][0] * pk), rk * (dkn[jb][1] - kn[jb][1] * pk),
-                 rk * (dkn[jb][2] - kn[jb][2] * pk), rk * (dkn[jb][3] - kn[jb][3] * pk));
-      }
-    } else if (r < len) {
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const int64_t o = trow + 16 * jb + 4 * g;
-        IO<TIO>::store4(p.dq, o, rq * (dqn[jb][0] - qn[jb][0] * pq), rq * (dqn[jb][1] - qn[jb][1] * pq),
-                        rq * (dqn[jb][2] - qn[jb][2] * pq), rq * (dqn[jb][3] - qn[jb][3] * pq));
-        IO<TIO>::store4(p.dk, o, rk * (dkn[jb][0] - kn[jb][0] * pk), rk * (dkn[jb][1] - kn[jb][1] * pk),
-                        rk * (dkn[jb][2] - kn[jb][2] * pk), rk * (dkn[jb][3] - kn[jb][3] * pk));
-      }
+    if (g == 0) {
+      l2_s[hf][0][r] = pq;
+      l2_s[hf][1][r] = pk;
     }
   }
   // ---- row and chunk reductions ----
   dgam_row = xrow_sum(dgam_row);
   dbeta_row = xrow_sum(dbeta_row);
   if (g == 0) {
-    rowsum_s[r] = dgam_row;
-    dbeta_s[r] = dbeta_row;
+    rowsum_s[hf][r] = dgam_row;
+    dbeta_s[hf][r] = dbeta_row;
   }
   const float tot = wave_sum(dgc_loc);
   const float st = wave_sum(sdot);
@@ -699,12 +705,40 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     red_s[w][1] = st;
   }
   chain_barrier();   // B_f
+  {
+    const float pq = l2_s[0][0][r] + l2_s[1][0][r], pk = l2_s[0][1][r] + l2_s[1][1][r];
+    if constexpr (kDma) {
+      // bf16 rows go out through LDS (the dO and dY tiles are free now), below
+#pragma unroll
+      for (int q = 0; q < NJH; ++q) {
+        const int j = 16 * (hf * NJH + q) + 4 * g;
+        st4_s<D>(dOt, r, j, rq * (dqn[q][0] - qn[q][0] * pq), rq * (dqn[q][1] - qn[q][1] * pq),
+                 rq * (dqn[q][2] - qn[q][2] * pq), rq * (dqn[q][3] - qn[q][3] * pq));
+        st4_s<D>(dYt, r, j, rk * (dkn[q][0] - kn[q][0] * pk), rk * (dkn[q][1] - kn[q][1] * pk),
+                 rk * (dkn[q][2] - kn[q][2] * pk), rk * (dkn[q][3] - kn[q][3] * pk));
+      }
+    } else if (r < len) {
+#pragma unroll
+      for (int q = 0; q < NJH; ++q) {
+        const int64_t o = trow + 16 * (hf * NJH + q) + 4 * g;
+        IO<TIO>::store4(p.dq, o, rq * (dqn[q][0] - qn[q][0] * pq), rq * (dqn[q][1] - qn[q][1] * pq),
+                        rq * (dqn[q][2] - qn[q][2] * pq), rq * (dqn[q][3] - qn[q][3] * pq));
+        IO<TIO>::store4(p.dk, o, rk * (dkn[q][0] - kn[q][0] * pk), rk * (dkn[q][1] - kn[q][1] * pk),
+                        rk * (dkn[q][2] - kn[q][2] * pk), rk * (dkn[q][3] - kn[q][3] * pk));
+      }
+    }
+  }
   if (w == 0) {
     // dlam_s = sum_{r >= s} dGam_r + dGamC (suffix sum; FlashKDA backward page, section 5)
-    const float dgc = ((red_s[0][0] + red_s[1][0]) + (red_s[2][0] + red_s[3][0])) +
-                      ((red_s[0][1] + red_s[1][1]) + (red_s[2][1] + red_s[3][1])) * fast_exp(gam_s[C - 1]);
-    float x = rowsum_s[l] + ((colsum_s[0][l] + colsum_s[1][l]) + (colsum_s[2][l] + colsum_s[3][l]));
-    float dbt = dbeta_s[l];
+    float rs = 0.f, ss = 0.f;
+#pragma unroll
+    for (int x = 0; x < kGradWaves; ++x) {
+      rs += red_s[x][0];
+      ss += red_s[x][1];
+    }
+    const float dgc = rs + ss * fast_exp(gam_s[C - 1]);
+    float x = (rowsum_s[0][l] + rowsum_s[1][l]) + ((colsum_s[0][l] + colsum_s[1][l]) + (colsum_s[2][l] + colsum_s[3][l]));
+    float dbt = dbeta_s[0][l] + dbeta_s[1][l];
     for (int sb = 0; sb <= (l >> 4); ++sb) {
       x += rowq_s[sb][l];
       dbt += rowb_s[sb][l];
@@ -722,10 +756,11 @@ __global__ __launch_bounds__(kThreads) void k_grads_gdn(const Params p) {
     }
   }
   if constexpr (kDma) {
+    chain_barrier();   // B_g: dq, dk rows staged
     // dq, dk rows: 1 KB (four rows) per wave instruction, 16 bytes per lane
 #pragma unroll
-    for (int it = 0; it < Ly::TR / 1024 / 4; ++it) {
-      const int pos = (w + 4 * it) * 1024 + 16 * l;
+    for (int it = 0; it < Ly::TR / 1024 / kGradWaves; ++it) {
+      const int pos = (w + kGradWaves * it) * 1024 + 16 * l;
       const int row = pos / (2 * D), c0 = (pos % (2 * D)) / 2;
       if (row < len) {
         const int64_t o = tok(t0 + row, H, h) * D + c0;
@@ -769,7 +804,7 @@ struct RunPrep {
 template <int D, typename TIO>
 struct RunGrads {
   static void run(const Params& p, hipStream_t s) {
-    k_grads_gdn<D, TIO><<<dim3(p.NC, p.H), kThreads, 0, s>>>(p);
+    k_grads_gdn<D, TIO><<<dim3(p.NC, p.H), kGradThreads, 0, s>>>(p);
   }
 };
 }  // namespace
