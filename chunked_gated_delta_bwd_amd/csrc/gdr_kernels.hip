@@ -739,15 +739,22 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
     const float dgc = rs + ss * fast_exp(gam_s[C - 1]);
     float x = (rowsum_s[0][l] + rowsum_s[1][l]) + ((colsum_s[0][l] + colsum_s[1][l]) + (colsum_s[2][l] + colsum_s[3][l]));
     float dbt = dbeta_s[0][l] + dbeta_s[1][l];
-    for (int sb = 0; sb <= (l >> 4); ++sb) {
-      x += rowq_s[sb][l];
-      dbt += rowb_s[sb][l];
-    }
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const float y = __shfl_down(x, m, 64);
-      if (l + m < 64) x += y;
+    for (int sb = 0; sb < 4; ++sb) {   // entries exist for sb <= l / 16 only
+      x += sb <= (l >> 4) ? rowq_s[sb][l] : 0.f;
+      dbt += sb <= (l >> 4) ? rowb_s[sb][l] : 0.f;
     }
+    // suffix sums inside each 16-lane row (DPP shifts toward lower lanes, zero
+    // filled), then the totals of the rows above
+#pragma unroll
+    for (int sh = 1; sh < 16; sh <<= 1) {
+      const float y = sh == 1 ? dpp_f<0x101>(x) : sh == 2 ? dpp_f<0x102>(x) : sh == 4 ? dpp_f<0x104>(x) : dpp_f<0x108>(x);
+      x += (l & 15) + sh < 16 ? y : 0.f;
+    }
+    const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float t3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    x += g == 0 ? t1 + (t2 + t3) : g == 1 ? t2 + t3 : g == 2 ? t3 : 0.f;
     if (l < len) {
       const int64_t o = tok(t0 + l, H, h);
       const float bt = beta_s[l];   // sigma(b) on valid rows
