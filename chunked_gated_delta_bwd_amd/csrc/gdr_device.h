@@ -28,6 +28,11 @@ __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x4 fp32 MFMA: lane l gives A[l%16][l/16] and B[l/16][l%16]
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Fragment of a tile stored T[row][k] (k contiguous, pitch P elements):
@@ -267,7 +272,9 @@ __device__ __forceinline__ void st_bf16x4(uint16_t* dst, float a, float b, float
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
-// softplus(x) = max(x, 0) + log1p(exp(-|x|)), stable for every x
-__device__ __forceinline__ float softplusf(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
+// softplus(x) = max(x, 0) + log(1 + exp(-|x|)), stable for every x.  The
+// argument of the log lies in (1, 2], where the hardware log is accurate; rounding
+// 1 + e for tiny e costs at most 2^-24 absolute, far below the bf16 data.
+__device__ __forceinline__ float softplusf(float x) { return fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))); }
 
 }  // namespace gdr

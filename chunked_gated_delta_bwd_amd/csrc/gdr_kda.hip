@@ -71,7 +71,10 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   using Dm = Dims<D>;
   constexpr int PD = Dm::PD, TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS;
   constexpr int PL = C + 4, PG = D + 4;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[C * PD];
+  constexpr int kQX = C * PD * 2 > C * PL * 4 ? C * PD * 2 : C * PL * 4;
+  __shared__ __attribute__((aligned(16))) char QX[kQX];   // Qn; from the inverse on: X = A, fp32
+  bf16* const Qs = reinterpret_cast<bf16*>(QX);
+  float* const Xf = reinterpret_cast<float*>(QX);
   __shared__ __attribute__((aligned(16))) bf16 Ks[C * PD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[C * PD];
   __shared__ __attribute__((aligned(16))) bf16 As[C * PC];
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   // low bf16 parts of A and beta V: U' = A beta V is formed to ~fp32 accuracy
   __shared__ __attribute__((aligned(16))) bf16 Asl[C * PC];
   __shared__ __attribute__((aligned(16))) bf16 Vsl[C * PD];
-  __shared__ float beta_s[C];
+  __shared__ float beta_s[C], tot_s[4][D];
 
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkEntry ce = p.ctab[c];
@@ -91,16 +94,35 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   const int H = p.H;
   const float scale = p.scale;
 
-  // --- rows: L2 norms; qn, kn to LDS; kn, qn, v kept in registers ---
-  float kn_r[NPASS][8], qn_r[NPASS][8], v_r[NPASS][8];
+  // --- rows: every load issued first (unconditional, from a clamped row, masked
+  // afterwards), so that their latencies overlap: q, k, v, the raw gate, beta ---
+  typename IO<TIO>::Raw8 qraw[NPASS], kraw[NPASS], vraw[NPASS], graw[NPASS];
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
-    float qv[8], kv[8];
     const int64_t off = tok(t0 + min(r, len - 1), H, h) * D + c0;
-    IO<TIO>::load8(p.q, off, qv);
-    IO<TIO>::load8(p.k, off, kv);
-    IO<TIO>::load8(p.v, off, v_r[ps]);
+    qraw[ps] = IO<TIO>::load_raw8(p.q, off);
+    kraw[ps] = IO<TIO>::load_raw8(p.k, off);
+    vraw[ps] = IO<TIO>::load_raw8(p.v, off);
+    graw[ps] = IO<TIO>::load_raw8(p.g, off);
+  }
+  const int cg0 = (tid % TPR) * 8;   // this thread's 8 channels in the row sweeps
+  const float4 bias0 = ld4(p.dt_bias + h * D + cg0), bias1 = ld4(p.dt_bias + h * D + cg0 + 4);
+  const float ea = fast_exp(p.A_log[h]);
+  float braw = 0.f;
+  if (tid >= kThreads - C) braw = IO<TIO>::load1(p.b, tok(t0 + min(tid - (kThreads - C), len - 1), H, h));
+
+  // --- L2 norms; qn, kn to LDS; kn, qn, v kept in registers; the log decay
+  // lambda = -e^A_log softplus(g + dt_bias) (0 past the end) to Gs ---
+  float kn_r[NPASS][8], qn_r[NPASS][8], v_r[NPASS][8];
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int r = ps * RPP + tid / TPR, c0 = cg0;
+    float qv[8], kv[8], gv[8];
+    IO<TIO>::unpack8(qraw[ps], qv);
+    IO<TIO>::unpack8(kraw[ps], kv);
+    IO<TIO>::unpack8(vraw[ps], v_r[ps]);
+    IO<TIO>::unpack8(graw[ps], gv);
     const float m = r < len ? 1.f : 0.f;
     float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -110,9 +132,12 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
       v_r[ps][e] *= m;
       sq += qv[e] * qv[e];
       sk += kv[e] * kv[e];
+      gv[e] = m * (-ea * softplusf(gv[e] + (e < 4 ? el(bias0, e) : el(bias1, e - 4))));
     }
-    sq = group_sum<TPR>(sq);
-    sk = group_sum<TPR>(sk);
+    *reinterpret_cast<float4*>(Gs + r * PG + c0) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+    *reinterpret_cast<float4*>(Gs + r * PG + c0 + 4) = make_float4(gv[4], gv[5], gv[6], gv[7]);
+    sq = group_sum_dpp<TPR>(sq);
+    sk = group_sum_dpp<TPR>(sk);
     const float rq = 1.0f / sqrtf(sq + 1e-6f), rk = 1.0f / sqrtf(sk + 1e-6f);
     bf16x8 qb, kb;
 #pragma unroll
@@ -129,23 +154,34 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
       p.rho[ch * 3 * C + C + r] = rk;
     }
   }
-  // --- gate and its per-channel cumsum (thread = channel), beta (last wave) ---
-  if (tid < D) {
-    const float ea = fast_exp(p.A_log[h]);
-    const float bias = p.dt_bias[h * D + tid];
-    float acc = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < C; ++r) {
-      const float x = IO<TIO>::load1(p.g, tok(t0 + min(r, len - 1), H, h) * D + tid) + bias;
-      acc += r < len ? -ea * softplusf(x) : 0.f;
-      Gs[r * PG + tid] = acc;
-      p.gam[(ch * C + r) * D + tid] = acc;
-    }
-  } else if (tid >= kThreads - C) {
+  if (tid >= kThreads - C) {
     const int r = tid - (kThreads - C);
-    const float bt = (r < len ? 1.f : 0.f) * sigmoidf(IO<TIO>::load1(p.b, tok(t0 + min(r, len - 1), H, h)));
+    const float bt = (r < len ? 1.f : 0.f) * sigmoidf(braw);
     beta_s[r] = bt;
     p.rho[ch * 3 * C + 2 * C + r] = bt;
+  }
+  __syncthreads();
+  // --- in-chunk cumsum Gamma per channel: thread = (channel, one of NPART row
+  // ranges) scans its range in registers, then adds the totals of the ranges before ---
+  {
+    constexpr int NPART = kThreads / D, RP = C / NPART;
+    const int cc = tid % D, part = tid / D;
+    float x[RP];
+#pragma unroll
+    for (int i = 0; i < RP; ++i) x[i] = Gs[(part * RP + i) * PG + cc];
+#pragma unroll
+    for (int i = 1; i < RP; ++i) x[i] += x[i - 1];
+    tot_s[part][cc] = x[RP - 1];
+    __syncthreads();
+    float before = 0.f;
+#pragma unroll
+    for (int q = 0; q < NPART - 1; ++q) before += q < part ? tot_s[q][cc] : 0.f;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+      const float v = x[i] + before;
+      Gs[(part * RP + i) * PG + cc] = v;
+      p.gam[(ch * C + part * RP + i) * D + cc] = v;
+    }
   }
   __syncthreads();
 
@@ -276,28 +312,63 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   }
   if (tid < D) p.edec[ch * D + tid] = fast_exp(Gs[(C - 1) * PG + tid]);
 
-  // --- A = (I + L)^-1 by forward substitution, one column per lane (wave 0) ---
-  if (w == 0) {
-    float a[C];
+  // --- A = (I + L)^-1 in 16x16 blocks X_ij (fp32): wave i inverts the diagonal
+  // block I + L_ii by forward substitution (lane = column) ... ---
+  {
+    const int i0 = 16 * w;
+    float a[16];
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      float acc = (r == l) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      float acc = r == jj ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < (r & ~3); s += 4) {
-        const float4 L4 = *reinterpret_cast<const float4*>(Lf + r * PL + s);
-        acc -= L4.x * a[s] + L4.y * a[s + 1] + L4.z * a[s + 2] + L4.w * a[s + 3];
-      }
-#pragma unroll
-      for (int s = (r & ~3); s < r; ++s) acc -= Lf[r * PL + s] * a[s];
+      for (int s = 0; s < r; ++s) acc -= Lf[(i0 + r) * PL + i0 + s] * a[s];
       a[r] = acc;
     }
+    if (l < 16) {
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      const bf16 ah = to_bf16(a[r]);
-      As[r * PC + l] = ah;
-      Asl[r * PC + l] = to_bf16(a[r] - float(ah));
-      p.A[(ch * C + r) * C + l] = f32_to_bf16_bits(a[r]);
+      for (int r = 0; r < 16; ++r) Xf[(i0 + r) * PL + i0 + jj] = a[r];
     }
+  }
+  __syncthreads();
+  // ... then wave j walks down block column j on fp32 MFMA:
+  //   X_ij = -X_ii (sum_{m=j}^{i-1} L_im X_mj),  i = j+1 .. 3
+  {
+    const int j0 = 16 * w;
+    float* const scr = reinterpret_cast<float*>(As) + 256 * w;   // 16x16 per wave
+    for (int i = w + 1; i < 4; ++i) {
+      const int i0 = 16 * i;
+      f32x4 sacc = zero4();
+      for (int m = w; m < i; ++m) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          sacc = mma_f32(Lf[(i0 + jj) * PL + 16 * m + 4 * kk + g], Xf[(16 * m + 4 * kk + g) * PL + j0 + jj], sacc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) scr[(4 * g + e) * 16 + jj] = sacc[e];
+      f32x4 x = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) x = mma_f32(Xf[(i0 + jj) * PL + i0 + 4 * kk + g], scr[(4 * kk + g) * 16 + jj], x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Xf[(i0 + 4 * g + e) * PL + j0 + jj] = -x[e];
+    }
+  }
+  __syncthreads();
+  // --- A out: high and low bf16 parts for the W, U' products, the high part to the
+  // workspace; the blocks above the diagonal are zero ---
+#pragma unroll
+  for (int it = 0; it < C * C / 8 / kThreads; ++it) {
+    const int idx = tid + kThreads * it, row = idx / 8, c8 = (idx % 8) * 8;
+    const bool on = (c8 >> 4) <= (row >> 4);
+    bf16x8 vh, vl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = on ? Xf[row * PL + c8 + e] : 0.f;
+      vh[e] = to_bf16(x);
+      vl[e] = to_bf16(x - float(vh[e]));
+    }
+    *reinterpret_cast<bf16x8*>(As + row * PC + c8) = vh;
+    *reinterpret_cast<bf16x8*>(Asl + row * PC + c8) = vl;
+    *reinterpret_cast<bf16x8*>(p.A + (ch * C + row) * C + c8) = vh;
   }
   __syncthreads();
 
@@ -363,12 +434,11 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   using Sm = KdaGradSmem<D>;
   constexpr int PD = Dm::PD, TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS, NJB = Dm::NJB;
   constexpr int PG = Sm::PG;
-  constexpr int NPART = kThreads / D;   // row groups of the per-channel state sum
   __shared__ __attribute__((aligned(16))) char RX[Sm::xb];
   __shared__ __attribute__((aligned(16))) char RY[Sm::yb];
   __shared__ float beta_s[C], rq_s[C], rk_s[C];
   // fixed-order partial sums for the per-channel chunk-total gradient
-  __shared__ float csum_s[4][D], ssum_s[NPART][D];
+  __shared__ float csum_s[4][D], ssum_s[4][D];
 
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkEntry ce = p.ctab[c];
@@ -401,18 +471,40 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     rk_s[tid] = p.rho[ch * 3 * C + C + tid];
     beta_s[tid] = p.rho[ch * 3 * C + 2 * C + tid];
   }
-  for (int pc = tid; pc < D * C / 8; pc += kThreads) {
-    const int v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
+  // every tile load issued first (their latencies overlap), then the LDS writes
+  constexpr int NU = D * C / 8 / kThreads;   // 16-byte pieces per thread of a [D][64] tile
+  uint4 du_r[NU], u_r[NU], ul_r[NU], a_r[2];
+  typename IO<TIO>::Raw8 do_r[NPASS];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int pc = tid + i * kThreads, v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
     const int64_t o = (ch * D + v) * C + c0;
-    *reinterpret_cast<uint4*>(dUsT + v * PC + c0) = *reinterpret_cast<const uint4*>(p.dU + o);
-    *reinterpret_cast<uint4*>(UsT + v * PC + c0) = *reinterpret_cast<const uint4*>(p.U + o);
-    *reinterpret_cast<uint4*>(UsTl + v * PC + c0) = *reinterpret_cast<const uint4*>(p.Ulo + o);
+    du_r[i] = *reinterpret_cast<const uint4*>(p.dU + o);
+    u_r[i] = *reinterpret_cast<const uint4*>(p.U + o);
+    ul_r[i] = *reinterpret_cast<const uint4*>(p.Ulo + o);
+  }
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
+    do_r[ps] = IO<TIO>::load_raw8(p.dO, tok(t0 + min(r, len - 1), H, h) * D + c0);
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int pc = tid + x * kThreads;
+    a_r[x] = *reinterpret_cast<const uint4*>(p.A + (ch * C + pc / 8) * C + (pc % 8) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int pc = tid + i * kThreads, v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
+    *reinterpret_cast<uint4*>(dUsT + v * PC + c0) = du_r[i];
+    *reinterpret_cast<uint4*>(UsT + v * PC + c0) = u_r[i];
+    *reinterpret_cast<uint4*>(UsTl + v * PC + c0) = ul_r[i];
   }
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     float x[8];
-    IO<TIO>::load8(p.dO, tok(t0 + min(r, len - 1), H, h) * D + c0, x);
+    IO<TIO>::unpack8(do_r[ps], x);
     const float m = r < len ? 1.f : 0.f;
     bf16x8 xb, xl;
 #pragma unroll
@@ -426,8 +518,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int pc = tid + x * kThreads;
-    *reinterpret_cast<uint4*>(As + (pc / 8) * PC + (pc % 8) * 8) =
-        *reinterpret_cast<const uint4*>(p.A + (ch * C + pc / 8) * C + (pc % 8) * 8);
+    *reinterpret_cast<uint4*>(As + (pc / 8) * PC + (pc % 8) * 8) = a_r[x];
   }
   __syncthreads();
 
@@ -455,16 +546,23 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   f32x4 aZ[NJB], aQ[NJB], aK[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) aZ[jb] = aQ[jb] = aK[jb] = zero4();
-  float sdot = 0.f;   // per-channel state sum, this thread's (part, channel)
-  const int scc = tid % D, spart = tid / D;
+  constexpr int NSL = D * D / 8 / kThreads;   // 16-byte pieces per thread of a [D][D] tile
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const uint16_t* Sg = pass ? p.Slo : p.S;
     const uint16_t* dSg = pass ? p.dSlo : p.dS;
-    for (int pc = tid; pc < D * D / 8; pc += kThreads) {
-      const int row = pc / (D / 8), col = (pc % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(Sx + row * PD + col) = *reinterpret_cast<const uint4*>(Sg + (ch * D + row) * D + col);
-      *reinterpret_cast<uint4*>(dSx + row * PD + col) = *reinterpret_cast<const uint4*>(dSg + (ch * D + row) * D + col);
+    uint4 s_r[NSL], d_r[NSL];
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) {
+      const int pc = tid + i * kThreads, row = pc / (D / 8), col = (pc % (D / 8)) * 8;
+      s_r[i] = *reinterpret_cast<const uint4*>(Sg + (ch * D + row) * D + col);
+      d_r[i] = *reinterpret_cast<const uint4*>(dSg + (ch * D + row) * D + col);
+    }
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) {
+      const int pc = tid + i * kThreads, row = pc / (D / 8), col = (pc % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(Sx + row * PD + col) = s_r[i];
+      *reinterpret_cast<uint4*>(dSx + row * PD + col) = d_r[i];
     }
     __syncthreads();
 #pragma unroll
@@ -480,20 +578,38 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         if (pass == 0) aK[jb] = mma(aD, frag_kc(UsTl, PC, 16 * w, k0), aK[jb]);
       }
     }
-    // sum_v S dS per channel: pass 0 the high x high part, pass 1 the rest
-    // (the high parts re-read from global memory)
-    for (int v = spart; v < D; v += NPART) {
-      const float a = float(Sx[v * PD + scc]), b = float(dSx[v * PD + scc]);
-      if (pass == 0) {
-        sdot += a * b;
-      } else {
-        const int64_t o = (ch * D + v) * D + scc;
-        sdot += a * b + a * bf16_bits_to_f32(p.dS[o]) + bf16_bits_to_f32(p.S[o]) * b;
-      }
-    }
     __syncthreads();
   }
-  ssum_s[spart][scc] = sdot;
+  // ---- per-channel state sum sum_v S dS with S = high + low, dS likewise (fp32
+  // products): thread (row group, 8 channels), 16-byte loads (the tiles were just
+  // read, so these mostly hit L2); rows groups summed across lanes, then waves ----
+  {
+    constexpr int CG = D / 8, VG = kThreads / CG, NV = D / VG;
+    const int c8 = (tid % CG) * 8, vg = tid / CG;
+    float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int64_t o = (ch * D + vg + VG * i) * D + c8;
+      const u32x4 sh = *reinterpret_cast<const u32x4*>(p.S + o), sl = *reinterpret_cast<const u32x4*>(p.Slo + o);
+      const u32x4 dh = *reinterpret_cast<const u32x4*>(p.dS + o), dl = *reinterpret_cast<const u32x4*>(p.dSlo + o);
+      float a[8], b[8], c2[8], d2[8];
+      IO<bf16>::unpack8(sh, a);
+      IO<bf16>::unpack8(sl, b);
+      IO<bf16>::unpack8(dh, c2);
+      IO<bf16>::unpack8(dl, d2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc8[e] = fmaf(a[e] + b[e], c2[e] + d2[e], acc8[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (CG == 8) acc8[e] += dpp_f<0x128>(acc8[e]);   // lanes l and l + 8 of a row
+      acc8[e] = xrow_sum(acc8[e]);
+    }
+    if (l < CG) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ssum_s[w][c8 + e] = acc8[e];
+    }
+  }
 
   // ---- kn, qn in fp32 (region X) ----
 #pragma unroll
@@ -547,7 +663,15 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       }
     }
   }
-  __syncthreads();   // region Y is rewritten below
+  // Gamma rows for phase 4 (loads first; region Y is rewritten below)
+  constexpr int NGL = C * D / 4 / kThreads;
+  float4 g_r[NGL];
+#pragma unroll
+  for (int i = 0; i < NGL; ++i) {
+    const int pc = tid + i * kThreads, rr = pc / (D / 4), c4 = (pc % (D / 4)) * 4;
+    g_r[i] = ld4(p.gam + (ch * C + rr) * D + c4);
+  }
+  __syncthreads();
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
     const int s0 = 16 * sb + 4 * g;
@@ -564,9 +688,10 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     st_bf16x4(dPh + r * PC + s0, hp[0], hp[1], hp[2], hp[3]);
     st_bf16x4(dPl + r * PC + s0, lp[0], lp[1], lp[2], lp[3]);
   }
-  for (int pc = tid; pc < C * D / 4; pc += kThreads) {
-    const int rr = pc / (D / 4), c4 = (pc % (D / 4)) * 4;
-    *reinterpret_cast<float4*>(Gs + rr * PG + c4) = ld4(p.gam + (ch * C + rr) * D + c4);
+#pragma unroll
+  for (int i = 0; i < NGL; ++i) {
+    const int pc = tid + i * kThreads, rr = pc / (D / 4), c4 = (pc % (D / 4)) * 4;
+    *reinterpret_cast<float4*>(Gs + rr * PG + c4) = g_r[i];
   }
   __syncthreads();
 
@@ -593,7 +718,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float col = group_sum<16>(csum[i]);   // over the 16 rows of this wave
+      const float col = row16_sum(csum[i]);   // over the 16 rows of this wave
       if (jj == 0) csum_s[w][j + i] = col;
     }
   }
@@ -674,6 +799,12 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     }
   }
   // diagonal block w, exactly: E = exp(-|Gamma_r - Gamma_t|) for both orders
+  float4 kr_d[NJB], qr_d[NJB];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) {
+    kr_d[jb] = ld4(Knf + r * PG + 16 * jb + 4 * g);
+    qr_d[jb] = ld4(Qnf + r * PG + 16 * jb + 4 * g);
+  }
   for (int t = 16 * w; t < 16 * w + 16; ++t) {
     const float mrt = float(dMh[r * PC + t]) + float(dMl[r * PC + t]);
     const float prt = scale * (float(dPh[r * PC + t]) + float(dPl[r * PC + t]));
@@ -684,7 +815,6 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       const int j = 16 * jb + 4 * g;
       const float4 gt = ld4(Gs + t * PG + j);
       const float4 kt = ld4(Knf + t * PG + j), qt = ld4(Qnf + t * PG + j);
-      const float4 kr = ld4(Knf + r * PG + j), qr = ld4(Qnf + r * PG + j);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float E = fast_exp(-fabsf(Gr[jb][i] - el(gt, i)));
@@ -692,7 +822,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         const float x1 = mrt * ke, x3 = prt * ke, x24 = mtr * ke + ptr * qe;
         dkn[jb][i] += x1 + x24;
         dqn[jb][i] += x3;
-        dgm[jb][i] += el(kr, i) * (x1 - x24) + el(qr, i) * x3;
+        dgm[jb][i] += el(kr_d[jb], i) * (x1 - x24) + el(qr_d[jb], i) * x3;
       }
     }
   }
@@ -710,9 +840,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   if (g == 0) p.dbeta[ch * C + r] = dbeta_row;
   __syncthreads();
   if (tid < D) {
-    float st = 0.f;
-#pragma unroll
-    for (int x = 0; x < NPART; ++x) st += ssum_s[x][tid];
+    const float st = (ssum_s[0][tid] + ssum_s[1][tid]) + (ssum_s[2][tid] + ssum_s[3][tid]);
     const float a = (csum_s[0][tid] + csum_s[1][tid]) + (csum_s[2][tid] + csum_s[3][tid]);
     p.dgamc[ch * D + tid] = a + st * fast_exp(Gs[(C - 1) * PG + tid]);
   }
@@ -726,29 +854,60 @@ template <int D, typename TIO>
 __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
   using Dm = Dims<D>;
   constexpr int TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS;
-  __shared__ float pa_s[kThreads / 64];
+  constexpr int PG = D + 4;
+  constexpr int NPART = kThreads / D, RP = C / NPART;   // per-channel scans: row ranges per channel
+  __shared__ __attribute__((aligned(16))) float dG_s[C * PG];   // dGamma [r][c]
+  __shared__ __attribute__((aligned(16))) float X_s[C * PG];    // g_raw + dt_bias [r][c]
+  __shared__ float tot_s[NPART][D], pd_s[NPART][D], pa_s[kThreads / 64];
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
   const int64_t ch = int64_t(h) * p.NC + c;
   const int H = p.H;
+  const int c0 = (tid % TPR) * 8;
+
+  // ---- every load first (their latencies overlap): q, k, dqn, dkn, dGamma and
+  // the raw gate rows, beta logits ----
+  typename IO<TIO>::Raw8 qraw[NPASS], kraw[NPASS], graw[NPASS];
+  float4 dq4[NPASS][2], dk4[NPASS][2], dg4[NPASS][2];
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
-    const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
-    const bool ok = r < len;
-    float q[8], k[8], dq[8], dk[8];
+    const int r = ps * RPP + tid / TPR;
     const int64_t o = tok(t0 + min(r, len - 1), H, h) * D + c0;
+    const int64_t wo = (ch * C + r) * D + c0;
+    qraw[ps] = IO<TIO>::load_raw8(p.q, o);
+    kraw[ps] = IO<TIO>::load_raw8(p.k, o);
+    graw[ps] = IO<TIO>::load_raw8(p.g, o);
+    dq4[ps][0] = ld4(p.dqn + wo);
+    dq4[ps][1] = ld4(p.dqn + wo + 4);
+    dk4[ps][0] = ld4(p.dkn + wo);
+    dk4[ps][1] = ld4(p.dkn + wo + 4);
+    dg4[ps][0] = ld4(p.dgam + wo);
+    dg4[ps][1] = ld4(p.dgam + wo + 4);
+  }
+  const float4 bias0 = ld4(p.dt_bias + h * D + c0), bias1 = ld4(p.dt_bias + h * D + c0 + 4);
+  float braw = 0.f, dbs = 0.f;
+  if (w == kThreads / 64 - 1) {
+    braw = IO<TIO>::load1(p.b, tok(t0 + min(l, len - 1), H, h));
+    dbs = p.dbeta[ch * C + l];
+  }
+
+  // ---- L2-norm backward: dq = rq (dqn - qn <qn, dqn>), dk likewise (K1 page, 3.3) ----
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int r = ps * RPP + tid / TPR;
+    const bool ok = r < len;
     const float m = ok ? 1.f : 0.f;
     const float rq = m * p.rho[ch * 3 * C + r], rk = m * p.rho[ch * 3 * C + C + r];
-    IO<TIO>::load8(p.q, o, q);
-    IO<TIO>::load8(p.k, o, k);
-    {
-      const float4 a0 = ld4(p.dqn + (ch * C + r) * D + c0), a1 = ld4(p.dqn + (ch * C + r) * D + c0 + 4);
-      const float4 b0 = ld4(p.dkn + (ch * C + r) * D + c0), b1 = ld4(p.dkn + (ch * C + r) * D + c0 + 4);
-      dq[0] = a0.x; dq[1] = a0.y; dq[2] = a0.z; dq[3] = a0.w; dq[4] = a1.x; dq[5] = a1.y; dq[6] = a1.z; dq[7] = a1.w;
-      dk[0] = b0.x; dk[1] = b0.y; dk[2] = b0.z; dk[3] = b0.w; dk[4] = b1.x; dk[5] = b1.y; dk[6] = b1.z; dk[7] = b1.w;
-    }
+    float q[8], k[8], g8[8];
+    IO<TIO>::unpack8(qraw[ps], q);
+    IO<TIO>::unpack8(kraw[ps], k);
+    IO<TIO>::unpack8(graw[ps], g8);
+    const float dq[8] = {dq4[ps][0].x, dq4[ps][0].y, dq4[ps][0].z, dq4[ps][0].w,
+                         dq4[ps][1].x, dq4[ps][1].y, dq4[ps][1].z, dq4[ps][1].w};
+    const float dk[8] = {dk4[ps][0].x, dk4[ps][0].y, dk4[ps][0].z, dk4[ps][0].w,
+                         dk4[ps][1].x, dk4[ps][1].y, dk4[ps][1].z, dk4[ps][1].w};
     float pq = 0.f, pk = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -757,8 +916,8 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
       pq += q[e] * dq[e];
       pk += k[e] * dk[e];
     }
-    pq = group_sum<TPR>(pq);
-    pk = group_sum<TPR>(pk);
+    pq = group_sum_dpp<TPR>(pq);
+    pk = group_sum_dpp<TPR>(pk);
     if (ok) {
       float oq[8], ok8[8];
 #pragma unroll
@@ -766,60 +925,95 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
         oq[e] = rq * (dq[e] - q[e] * pq);
         ok8[e] = rk * (dk[e] - k[e] * pk);
       }
-      IO<TIO>::store8(p.dq, o, oq);
-      IO<TIO>::store8(p.dk, o, ok8);
+      IO<TIO>::store8(p.dq, tok(t0 + r, H, h) * D + c0, oq);
+      IO<TIO>::store8(p.dk, tok(t0 + r, H, h) * D + c0, ok8);
     }
+    *reinterpret_cast<float4*>(dG_s + r * PG + c0) = dg4[ps][0];
+    *reinterpret_cast<float4*>(dG_s + r * PG + c0 + 4) = dg4[ps][1];
+    *reinterpret_cast<float4*>(X_s + r * PG + c0) =
+        make_float4(g8[0] + bias0.x, g8[1] + bias0.y, g8[2] + bias0.z, g8[3] + bias0.w);
+    *reinterpret_cast<float4*>(X_s + r * PG + c0 + 4) =
+        make_float4(g8[4] + bias1.x, g8[5] + bias1.y, g8[6] + bias1.z, g8[7] + bias1.w);
   }
   if (w == kThreads / 64 - 1) {
-    const int64_t o = tok(t0 + min(l, len - 1), H, h);
-    const float bt = sigmoidf(IO<TIO>::load1(p.b, o));
-    const float dbs = p.dbeta[ch * C + l];
-    if (l < len) IO<TIO>::store1(p.db, o, dbs * bt * (1.f - bt));
+    const float bt = sigmoidf(braw);
+    if (l < len) IO<TIO>::store1(p.db, tok(t0 + l, H, h), dbs * bt * (1.f - bt));
   }
-  // per-channel: dlam_s = sum_{r >= s} dGamma_r + dGamma_C (FlashKDA backward
-  // page, section 5), then through lambda = -e^A softplus(x): dx = dlam (-e^A sigmoid(x))
-  float pa = 0.f;
-  if (tid < D) {
-    const float ea = fast_exp(p.A_log[h]);
-    const float bias = p.dt_bias[h * D + tid];
-    float acc = p.dgamc[ch * D + tid], pd = 0.f;
-#pragma unroll 4
-    for (int r = C - 1; r >= 0; --r) {
-      acc += p.dgam[(ch * C + r) * D + tid];
-      if (r < len) {
-        const int64_t o = tok(t0 + r, H, h) * D + tid;
-        const float x = IO<TIO>::load1(p.g, o) + bias;
-        const float dx = acc * (-ea * sigmoidf(x));
-        IO<TIO>::store1(p.dg, o, dx);
-        pd += dx;
-        pa += acc * (-ea * softplusf(x));
-      }
+  __syncthreads();
+
+  // ---- per channel: dlam_r = sum_{r' >= r} dGamma_r' + dGamma_C (FlashKDA
+  // backward page, section 5), then through lambda = -e^A softplus(x):
+  // dx = dlam (-e^A sigmoid(x)).  Thread = (channel, one of NPART row ranges):
+  // a suffix scan of its range in registers plus the totals of the ranges after it ----
+  const int cc = tid % D, part = tid / D;
+  float x[RP];
+#pragma unroll
+  for (int i = RP - 1; i >= 0; --i) x[i] = dG_s[(part * RP + i) * PG + cc] + (i < RP - 1 ? x[i + 1] : 0.f);
+  tot_s[part][cc] = x[0];
+  __syncthreads();
+  float after = p.dgamc[ch * D + cc];
+#pragma unroll
+  for (int q = NPART - 1; q > 0; --q) after += q > part ? tot_s[q][cc] : 0.f;
+  const float ea = fast_exp(p.A_log[h]);
+  float pd = 0.f, pa = 0.f;
+#pragma unroll
+  for (int i = 0; i < RP; ++i) {
+    const int r = part * RP + i;
+    if (r < len) {
+      const float acc = x[i] + after;
+      const float xg = X_s[r * PG + cc];
+      const float dx = acc * (-ea * sigmoidf(xg));
+      IO<TIO>::store1(p.dg, tok(t0 + r, H, h) * D + cc, dx);
+      pd += dx;
+      pa += acc * (-ea * softplusf(xg));
     }
-    p.pddt[ch * D + tid] = pd;
   }
-  pa = group_sum<64>(pa);
+  pd_s[part][cc] = pd;
+  pa = wave_sum(pa);
   if (l == 0) pa_s[w] = pa;
   __syncthreads();
-  if (tid == 0) {
-    float s = 0.f;
+  if (tid < D) {
+    float sdt = 0.f;
 #pragma unroll
-    for (int x = 0; x < kThreads / 64; ++x) s += pa_s[x];
-    p.pdA[ch] = s;
+    for (int q = 0; q < NPART; ++q) sdt += pd_s[q][tid];
+    p.pddt[ch * D + tid] = sdt;
+  }
+  if (tid == 0) {
+    float sa = 0.f;
+#pragma unroll
+    for (int q = 0; q < kThreads / 64; ++q) sa += pa_s[q];
+    p.pdA[ch] = sa;
   }
 }
 
-// dA_log[h] and ddt_bias[h][:] from the per-chunk partials, summed in chunk order.
+// dA_log[h] and ddt_bias[h][:] from the per-chunk partials, in a fixed order:
+// thread (channel, part) sums chunks part, part + NP, ... (loads independent of
+// each other), then the parts are added in order; dA_log likewise over one wave.
+constexpr int kParamThreads = 1024;
 template <int D>
-__global__ __launch_bounds__(D) void k_params_kda(const Params p) {
-  const int h = blockIdx.x, t = threadIdx.x;
+__global__ __launch_bounds__(kParamThreads) void k_params_kda(const Params p) {
+  constexpr int NP = kParamThreads / D;
+  __shared__ float part_s[NP][D];
+  const int h = blockIdx.x, t = threadIdx.x, cc = t % D, part = t / D;
+  const int64_t base = int64_t(h) * p.NC;
   float s = 0.f;
-  for (int c = 0; c < p.NC; ++c) s += p.pddt[(int64_t(h) * p.NC + c) * D + t];
-  p.ddt_bias[h * D + t] = s;
-  if (t == 0) {
-    float a = 0.f;
-    for (int c = 0; c < p.NC; ++c) a += p.pdA[int64_t(h) * p.NC + c];
-    p.dA_log[h] = a;
+#pragma unroll 8
+  for (int c = part; c < p.NC; c += NP) s += p.pddt[(base + c) * D + cc];
+  part_s[part][cc] = s;
+  float a = 0.f;
+  if (t < 64) {
+#pragma unroll 8
+    for (int c = t; c < p.NC; c += 64) a += p.pdA[base + c];
+    a = wave_sum(a);
   }
+  __syncthreads();
+  if (t < D) {
+    float x = 0.f;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) x += part_s[q][t];
+    p.ddt_bias[h * D + t] = x;
+  }
+  if (t == 0) p.dA_log[h] = a;
 }
 
 // ===========================================================================
@@ -832,7 +1026,7 @@ void run_kda(const Params& p, int stage, hipStream_t s) {
   if (stage == 0) k_prep_kda<D, TIO><<<grid, kThreads, 0, s>>>(p);
   else if (stage == 1) k_grads_kda<D, TIO><<<grid, kThreads, 0, s>>>(p);
   else if (stage == 2) k_finish_kda<D, TIO><<<grid, kThreads, 0, s>>>(p);
-  else k_params_kda<D><<<p.H, D, 0, s>>>(p);
+  else k_params_kda<D><<<p.H, kParamThreads, 0, s>>>(p);
 }
 }  // namespace
 

@@ -47,10 +47,6 @@ __device__ __forceinline__ int tile_sb(int w, int slot) {
 }
 __device__ __forceinline__ bool tile_valid(int w, int slot) { return slot < 2 || w < 2; }
 
-// 16x16x4 fp32 MFMA: lane l gives A[l%16][l/16] and B[l/16][l%16]
-__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 template <int D, typename TIO>
 __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
