@@ -35,6 +35,11 @@ namespace {
 
 typedef short s16x4v __attribute__((ext_vector_type(4)));
 
+// largest in-block decay span (Gamma of the first row minus the last, per channel)
+// for which a diagonal 16-row block is factored at its first row: both factors
+// and their products stay normal fp32 numbers far from overflow
+constexpr float kSpanMax = 60.f;
+
 // v_mfma_f32_16x16x16_bf16: A lane (m = l % 16, k = 4 (l / 16) .. +3),
 // B lane (k = 4 (l / 16) .. +3, n = l % 16), C as for the K = 32 form.
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
@@ -730,6 +735,18 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   //   X4_sc = scale sum_{r>=s} dP_rs qn_rc E  -> dkn_s, dGamma_s (- kn_s X4)
   // wave w owns the 16 rows of block w on both sides; products with split operands
   // take a_h b_h + a_h b_l + a_l b_h.
+  bool fact_ok[NJB];
+  // B operands of the diagonal block's fp32 products (lane: k = 4 kk + g, n = jj):
+  // dM[f+n][f+k] and dP[f+n][f+k] (row side), dM[f+k][f+n] and dP[f+k][f+n] (column side)
+  float dm_row[4], dp_row[4], dm_col[4], dp_col[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int f = 16 * w, kx = f + 4 * kk + g, nx = f + jj;
+    dm_row[kk] = float(dMh[nx * PC + kx]) + float(dMl[nx * PC + kx]);
+    dp_row[kk] = float(dPh[nx * PC + kx]) + float(dPl[nx * PC + kx]);
+    dm_col[kk] = float(dMh[kx * PC + nx]) + float(dMl[kx * PC + nx]);
+    dp_col[kk] = float(dPh[kx * PC + nx]) + float(dPl[kx * PC + nx]);
+  }
   auto split4 = [](const float (&x)[4], bf16x4& hi, bf16x4& lo) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -797,14 +814,57 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         dgm[jb][i] -= el(kr, i) * x;
       }
     }
+    // diagonal block w, factored at its first row f = 16w: E_rt = e^(Gam_r - Gam_f)
+    // e^(Gam_f - Gam_t), the first factor <= 1, the second >= 1.  The products run
+    // on fp32 MFMA (16x16x4, four k-steps) with fp32 operands, so they keep the
+    // exact path's accuracy.  Valid while the block's decay span Gam_f - Gam_(f+15)
+    // stays below kSpanMax for all 16 channels of this tile (no overflow, no
+    // underflow of the small factor); otherwise the tile takes the exact
+    // per-element path below.
+    {
+      const int f = 16 * w;
+      const float gf = Gs[f * PG + cm];
+      const bool wide = gf - Gs[(f + 15) * PG + cm] >= kSpanMax;
+      fact_ok[jb] = __builtin_amdgcn_ballot_w64(wide) == 0;
+      if (fact_ok[jb]) {
+        f32x4 t1 = zero4(), t2 = zero4(), t3 = zero4(), t4 = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int s = f + 4 * kk + g;   // A: m = channel cm, k = s - f
+          const float gs = Gs[s * PG + cm];
+          const float kb = Knf[s * PG + cm] * fast_exp(gf - gs);   // kn_s b_s
+          const float d = fast_exp(gs - gf);                        // a_s
+          t1 = mma_f32(kb, dm_row[kk], t1);
+          t3 = mma_f32(kb, dp_row[kk], t3);
+          t2 = mma_f32(Knf[s * PG + cm] * d, dm_col[kk], t2);
+          t4 = mma_f32(Qnf[s * PG + cm] * d, dp_col[kk], t4);
+        }
+        const float4 gfv = ld4(Gs + f * PG + j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float arow = fast_exp(Gr[jb][i] - el(gfv, i));   // a_r <= 1
+          const float bcol = fast_exp(el(gfv, i) - Gr[jb][i]);   // b_r >= 1
+          const float x1 = t1[i] * arow, x3 = scale * t3[i] * arow;
+          const float x24 = (t2[i] + scale * t4[i]) * bcol;
+          dkn[jb][i] += x1 + x24;
+          dqn[jb][i] += x3;
+          dgm[jb][i] += el(kr, i) * (x1 - x24) + el(qr, i) * x3;
+        }
+      }
+    }
   }
-  // diagonal block w, exactly: E = exp(-|Gamma_r - Gamma_t|) for both orders
+  // diagonal block w, tiles whose decay span is too wide for the factored form,
+  // exactly: E = exp(-|Gamma_r - Gamma_t|) for both orders
   float4 kr_d[NJB], qr_d[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) {
     kr_d[jb] = ld4(Knf + r * PG + 16 * jb + 4 * g);
     qr_d[jb] = ld4(Qnf + r * PG + 16 * jb + 4 * g);
   }
+  bool any_exact = false;
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) any_exact |= !fact_ok[jb];
+  if (any_exact)
   for (int t = 16 * w; t < 16 * w + 16; ++t) {
     const float mrt = float(dMh[r * PC + t]) + float(dMl[r * PC + t]);
     const float prt = scale * (float(dPh[r * PC + t]) + float(dPl[r * PC + t]));
@@ -812,6 +872,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     const float ptr = scale * (float(dPh[t * PC + r]) + float(dPl[t * PC + r]));
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
+      if (fact_ok[jb]) continue;
       const int j = 16 * jb + 4 * g;
       const float4 gt = ld4(Gs + t * PG + j);
       const float4 kt = ld4(Knf + t * PG + j), qt = ld4(Qnf + t * PG + j);
