@@ -736,6 +736,25 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   // wave w owns the 16 rows of block w on both sides; products with split operands
   // take a_h b_h + a_h b_l + a_l b_h.
   bool fact_ok[NJB];
+  // K = 16 B fragments of the off-diagonal block pairs (the same for every channel
+  // tile): row side blocks sb < w, column side blocks rb > w
+  bf16x4 fr_mh[3], fr_ml[3], fr_ph[3], fr_pl[3], fc_mh[3], fc_ml[3], fc_ph[3], fc_pl[3];
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    if (x < w) {
+      fr_mh[x] = frag16_rk(dMh, PC, 16 * w, 16 * x);
+      fr_ml[x] = frag16_rk(dMl, PC, 16 * w, 16 * x);
+      fr_ph[x] = frag16_rk(dPh, PC, 16 * w, 16 * x);
+      fr_pl[x] = frag16_rk(dPl, PC, 16 * w, 16 * x);
+    }
+    if (x + 1 > w) {
+      const int rs = 16 * (x + 1);
+      fc_mh[x] = frag16_kc(dMh, PC, 16 * w, rs);
+      fc_ml[x] = frag16_kc(dMl, PC, 16 * w, rs);
+      fc_ph[x] = frag16_kc(dPh, PC, 16 * w, rs);
+      fc_pl[x] = frag16_kc(dPl, PC, 16 * w, rs);
+    }
+  }
   // B operands of the diagonal block's fp32 products (lane: k = 4 kk + g, n = jj):
   // dM[f+n][f+k] and dP[f+n][f+k] (row side), dM[f+k][f+n] and dP[f+k][f+n] (column side)
   float dm_row[4], dp_row[4], dm_col[4], dp_col[4];
@@ -761,7 +780,9 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     const int j = c0 + 4 * g;        // channels of this lane in the outputs
     const float4 kr = ld4(Knf + r * PG + j), qr = ld4(Qnf + r * PG + j);
     // row side, earlier blocks sb < w: reference = last row of block sb
-    for (int sb = 0; sb < w; ++sb) {
+#pragma unroll
+    for (int sb = 0; sb < 3; ++sb) {
+      if (sb >= w) break;
       const int se = 16 * sb + 15;
       const float ge = Gs[se * PG + cm];
       float av[4];
@@ -772,8 +793,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       }
       bf16x4 ah, al;
       split4(av, ah, al);
-      const bf16x4 mh = frag16_rk(dMh, PC, 16 * w, 16 * sb), ml = frag16_rk(dMl, PC, 16 * w, 16 * sb);
-      const bf16x4 ph = frag16_rk(dPh, PC, 16 * w, 16 * sb), pl = frag16_rk(dPl, PC, 16 * w, 16 * sb);
+      const bf16x4 mh = fr_mh[sb], ml = fr_ml[sb], ph = fr_ph[sb], pl = fr_pl[sb];
       const f32x4 t1 = mma16(al, mh, mma16(ah, ml, mma16(ah, mh, zero4())));
       const f32x4 t3 = mma16(al, ph, mma16(ah, pl, mma16(ah, ph, zero4())));
       const float4 gend = ld4(Gs + se * PG + j);
@@ -787,7 +807,9 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       }
     }
     // column side, later blocks rb > w: reference = first row of block rb
-    for (int rb = w + 1; rb < 4; ++rb) {
+#pragma unroll
+    for (int rb = 1; rb < 4; ++rb) {
+      if (rb <= w) continue;
       const int rs = 16 * rb;
       const float gst = Gs[rs * PG + cm];
       float kv[4], qv[4];
@@ -801,8 +823,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       bf16x4 kh, kl, qh, ql;
       split4(kv, kh, kl);
       split4(qv, qh, ql);
-      const bf16x4 mh = frag16_kc(dMh, PC, 16 * w, rs), ml = frag16_kc(dMl, PC, 16 * w, rs);
-      const bf16x4 ph = frag16_kc(dPh, PC, 16 * w, rs), pl = frag16_kc(dPl, PC, 16 * w, rs);
+      const bf16x4 mh = fc_mh[rb - 1], ml = fc_ml[rb - 1], ph = fc_ph[rb - 1], pl = fc_pl[rb - 1];
       const f32x4 t2 = mma16(kl, mh, mma16(kh, ml, mma16(kh, mh, zero4())));
       const f32x4 t4 = mma16(ql, ph, mma16(qh, pl, mma16(qh, ph, zero4())));
       const float4 gsv = ld4(Gs + rs * PG + j);
