@@ -249,7 +249,54 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
       st_bf16x4(p.Mk + (ch * C + r) * C + s0, Mv[0], Mv[1], Mv[2], Mv[3]);
     }
   }
-  // --- diagonal blocks exactly: thread owns row r and four columns s ---
+  // --- diagonal blocks: wave R's block factored at its first row f,
+  // E_rs = e^(Gam_r - Gam_f) e^(Gam_f - Gam_s), on 16x16x4 fp32 MFMA with fp32
+  // operands (contraction over channels; lane group g takes channels g D/4 .. +D/4),
+  // while the block's decay span Gam_f - Gam_(f+15) stays below kSpanMax in every
+  // channel; otherwise exactly, thread owns row r and four columns s ---
+  bool diag_fact;
+  {
+    const int f = 16 * w, rr = f + jj;
+    bool wide = false;
+#pragma unroll
+    for (int kq = 0; kq < D / 16; ++kq) {   // this lane's 32 (D = 128) or 16 (D = 64) channels
+      const float4 a4 = ld4(Gs + f * PG + (D / 4) * g + 4 * kq), b4 = ld4(Gs + (f + 15) * PG + (D / 4) * g + 4 * kq);
+      wide |= a4.x - b4.x >= kSpanMax || a4.y - b4.y >= kSpanMax || a4.z - b4.z >= kSpanMax || a4.w - b4.w >= kSpanMax;
+    }
+    diag_fact = __builtin_amdgcn_ballot_w64(wide) == 0;
+    if (diag_fact) {
+      f32x4 aM = zero4(), aP = zero4();
+#pragma unroll
+      for (int kq = 0; kq < D / 16; ++kq) {
+        const int c4 = (D / 4) * g + 4 * kq;
+        const float4 gr4 = ld4(Gs + rr * PG + c4), gf4 = ld4(Gs + f * PG + c4);
+        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Ks + rr * PD + c4);
+        const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qs + rr * PD + c4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ea = fast_exp(el(gr4, e) - el(gf4, e));   // a <= 1 (row as r)
+          const float eb = fast_exp(el(gf4, e) - el(gr4, e));   // b >= 1 (row as s)
+          const float kn = float(k4[e]);
+          aM = mma_f32(kn * eb, kn * ea, aM);
+          aP = mma_f32(kn * eb, float(q4[e]) * ea, aP);
+        }
+      }
+      const int s0 = f + 4 * g;
+      const float br = beta_s[rr];
+      float Mv[4], Pv[4], Lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = s0 + i;
+        Mv[i] = s < rr ? aM[i] : 0.f;
+        Pv[i] = s <= rr ? scale * aP[i] : 0.f;
+        Lv[i] = br * Mv[i];
+      }
+      *reinterpret_cast<float4*>(Lf + rr * PL + s0) = make_float4(Lv[0], Lv[1], Lv[2], Lv[3]);
+      st_bf16x4(p.P + (ch * C + rr) * C + s0, Pv[0], Pv[1], Pv[2], Pv[3]);
+      st_bf16x4(p.Mk + (ch * C + rr) * C + s0, Mv[0], Mv[1], Mv[2], Mv[3]);
+    }
+  }
+  if (!diag_fact)
   {
     const int blk = tid >> 6, r = 16 * blk + ((tid >> 2) & 15), s0 = 16 * blk + 4 * (tid & 3);
     float Mv[4] = {0.f, 0.f, 0.f, 0.f}, Pv[4] = {0.f, 0.f, 0.f, 0.f};
