@@ -17,11 +17,11 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def _check(inp, got, label, heads=None):
+def _check(inp, got, label, heads=None, tol_fp32=TOL_FP32):
     sub = inp if heads is None else subset_heads(inp, heads)
     ref = oracle.run(sub)
     compare(got, ref, TOKEN_GRADS, TOL_BF16, label + " grads", heads)
-    compare(got, ref, FP32_GRADS, TOL_FP32, label + " fp32", heads)
+    compare(got, ref, FP32_GRADS, tol_fp32, label + " fp32", heads)
     compare(got, ref, ("ht",), TOL_FP32 * 5, label + " ht", heads)
 
 
@@ -114,6 +114,24 @@ def test_kda_small_against_oracle(name, spec, mode):
     inp = synth.generate(spec)
     got = gpu_run(inp, mode=mode)
     _check(inp, got, f"{name}/{mode}")
+
+
+# Outside the synthetic recipe's A_log ~ U(0, 1.5): weak decay (e^A_log = 0.05,
+# per-token log decays ~ -0.04) sends every 16-row diagonal block of the gradient
+# and prologue kernels down the factored fp32-MFMA path; strong decay (e^A_log = 20,
+# log decays ~ -15, in-block spans far above 60) sends every block down the exact
+# per-element path.  With almost no forgetting the fp32 parameter gradients lose
+# precision to the bf16 chunk states accumulated over the whole sequence
+# (measured 1.7e-3 on dA_log, the same before the factored paths existed), so the
+# weak regime is held to 3e-3 there; everything else keeps the standard bars.
+@pytest.mark.parametrize("a_log,tol_fp32", [(-3.0, 3e-3), (3.0, TOL_FP32)], ids=["weak_decay", "strong_decay"])
+def test_kda_decay_regimes(a_log, tol_fp32):
+    log(f"case kda decay regime A_log={a_log}")
+    inp = synth.generate(synth.Spec("kd", 1, "bf16", H=2, K=128, V=128, lengths=[200, 77], h0_std=0.1,
+                                    dht_std=0.1, seed=47))
+    inp["A_log"] = torch.full_like(inp["A_log"], a_log)
+    got = gpu_run(inp)
+    _check(inp, got, f"kda_decay_{a_log}", tol_fp32=tol_fp32)
 
 
 def test_kda_chunk_boundary_states():
