@@ -63,7 +63,7 @@ struct ChainCfg {
   static constexpr bool MAT = GATE == 1 || LO;                 // materialised Khat / Qbar tiles
   static constexpr bool RAW = !MAT;                            // raw q, k rows and row factors
   static constexpr bool SPLIT = GATE == 1;   // U', U, S, dS also carried as bf16 high + low parts
-  static constexpr int DG = GATE == 1 ? D : 16;    // decay floats per slot (scalar: a 4-float copy per mover)
+  static constexpr int DG = GATE == 1 ? D : 16;    // decay floats per slot (scalar: one value, 64-byte slot part)
   static constexpr int TB = C * D * 2;             // one 64 x D bf16 tile
   static constexpr int PB = C * C * 2;             // the 64 x 64 P tile
   static constexpr int XB = C * 16 * 2;            // a 64 x 16 bf16 slice
@@ -102,8 +102,10 @@ struct ChainCfg {
   static constexpr int bytes = bEnd > fEnd ? bEnd : fEnd;
   // mover loads per wave per chunk: first-window set A, second-window set B
   // (set B carries the small data of the chunk after its own)
-  static constexpr int nSb = LO ? 0 : (RAW ? 3 : 2);   // dO, fac, decay
-  static constexpr int nSf = LO ? 0 : (RAW ? 2 : 1);   // fac, decay
+  // small data loads per mover wave and chunk, counted as one (movers that issue
+  // none wait for one fewer: wait_mover)
+  static constexpr int nSb = 1;
+  static constexpr int nSf = 1;
   static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 : 2) * NJ + nSb;
   // L2 prefetch distance in chunk steps (one prefetch load per mover wave per step)
   static constexpr int PFD = 5;
@@ -183,8 +185,19 @@ __device__ __forceinline__ void move_p(const MoverLane<D>& ml, const void* src, 
   for (int j = 0; j < 2; ++j) dma16(s + ml.tP[j], dst + mw * 2048 + j * 1024);
 }
 
-// small data of chunk c into a slot: the dO slice (reverse role), fq / fk, decay.
-// Every mover wave issues the same number of loads (partial-wave loads).
+// small data of chunk c into a slot: the dO slice (reverse role), fq / fk, decay,
+// in as few whole-wave loads as possible (a load costs about the same however few
+// bytes it carries): reverse role, movers 0 and 1 one half of the dO slice each
+// (rows 32 mw .. 32 mw + 31, two pieces a row), mover 2 the row factors and the
+// decay together (contiguous in the slot); forward role, mover 0 the latter.
+// small_loads() is the number of loads a mover issues here (0 or 1).
+template <int D, typename TIO, int GATE>
+__device__ __forceinline__ bool small_loads(int mw, bool with_dO) {
+  using Cf = ChainCfg<D, TIO, GATE>;
+  if constexpr (Cf::LO) return false;
+  return with_dO ? mw < 3 : mw == 0;
+}
+
 template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void move_small(const Params& p, const SeqEntry& se, int h, int c, int v0, char* slot,
                                            int mw, bool with_dO) {
@@ -192,22 +205,31 @@ __device__ __forceinline__ void move_small(const Params& p, const SeqEntry& se, 
   if constexpr (!Cf::LO) {
     const ChunkGeo cg = geo(p, se, h, c);
     const int l = lane_id();
-    if (with_dO && l < 32) {
-      // rows 16 mw .. 16 mw + 15 of the 64 x 16 slice, two pieces a row
-      const int row = prow<16>(16 * mw + (l >> 1));   // logical row landing at physical row 16 mw + l/2
+    if (with_dO && mw < 2) {
+      const int row = prow<16>(32 * mw + (l >> 1));   // logical row landing at physical row 32 mw + l/2
       const char* src = reinterpret_cast<const char*>(p.dO) +
                         (tok(cg.t0 + min(row, cg.len - 1), p.H, h) * D + v0) * 2 + (l & 1) * 16;
-      dma16(src, slot + Cf::sDO + mw * 512);
-    }
-    if constexpr (Cf::RAW) {
-      if (l < 8) dma16(reinterpret_cast<const char*>(p.fac + cg.ch * 2 * C) + mw * 128 + l * 16, slot + Cf::sFac + mw * 128);
-    }
-    if constexpr (GATE == 1) {
-      if (l < D / 16) dma16(reinterpret_cast<const char*>(p.edec + cg.ch * D) + mw * D + l * 16, slot + Cf::sDec + mw * D);
-    } else {
-      if (l == 0) dma16(p.edec + cg.ch * 4, slot + Cf::sDec + mw * 16);
+      dma16(src, slot + Cf::sDO + mw * 1024);
+    } else if (mw == (with_dO ? 2 : 0)) {
+      if constexpr (Cf::RAW) {
+        // fq, fk (512 bytes, lanes 0-31), then the decay (lane 32) right behind them
+        static_assert(Cf::sDec == Cf::sFac + 2 * C * 4, "decay follows the row factors");
+        if (l < 32) dma16(reinterpret_cast<const char*>(p.fac + cg.ch * 2 * C) + l * 16, slot + Cf::sFac);
+        else if (l == 32) dma16(p.edec + cg.ch * 4, slot + Cf::sFac);
+      } else {
+        if (l < D / 4) dma16(reinterpret_cast<const char*>(p.edec + cg.ch * D) + l * 16, slot + Cf::sDec);
+      }
     }
   }
+}
+
+// s_waitcnt vmcnt for the movers: every wait below counts one small load; a mover
+// that issues none (small_loads() false) waits for one fewer
+template <int N>
+__device__ __forceinline__ void wait_mover(bool has_small) {
+  static_assert(N >= 1, "count includes the small load");
+  if (has_small) wait_vm<N>();
+  else wait_vm<N - 1>();
 }
 
 // reverse role: set A (Khat or k, P), set B (Qbar high [+ low] or q, W)
@@ -550,6 +572,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
   } else {
     if (nck == 0) return;
     const int mw = wv - kMoveWave0;
+    const bool hs = small_loads<D, TIO, GATE>(mw, false);
     MoverLane<D> ml;
     ml.init(mw, l);
     move_small<D, TIO, GATE>(p, se, h, chunk(0), v0, slot(0), mw, false);
@@ -558,18 +581,18 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     move_small<D, TIO, GATE>(p, se, h, chunk(1), v0, slot(1), mw, false);
     move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), v0, smem + Cf::bufF, mw);
     for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(c), sl, mw, smem + Cf::fPF);
-    wait_vm<Cf::fwdA + Cf::fwdB + Cf::fwdA + Cf::PFD - 2>();
+    wait_mover<Cf::fwdA + Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
     chain_barrier();   // B0
-    wait_vm<Cf::fwdB + Cf::fwdA + Cf::PFD - 2>();
+    wait_mover<Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
       move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0, slot(k + 2), mw, false);
-      wait_vm<Cf::fwdA + 1 + Cf::fwdB>();
+      wait_mover<Cf::fwdA + 1 + Cf::fwdB>(hs);
       chain_barrier();   // B2
       move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0, smem + (k & 1) * Cf::bufF, mw);
       prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(k + Cf::PFD), sl, mw, smem + Cf::fPF);
-      wait_vm<Cf::fwdB + Cf::fwdA + 2>();
+      wait_mover<Cf::fwdB + Cf::fwdA + 2>(hs);
     }
     wait_vm<0>();
   }
@@ -722,6 +745,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
   } else {
     if (nck == 0) return;
     const int mw = wv - kMoveWave0;
+    const bool hs = small_loads<D, TIO, GATE>(mw, true);
     MoverLane<D> ml;
     ml.init(mw, l);
     move_small<D, TIO, GATE>(p, se, h, chunk(0), v0, slot(0), mw, true);
@@ -730,18 +754,18 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     move_small<D, TIO, GATE>(p, se, h, chunk(1), v0, slot(1), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), smem + Cf::bufB, mw);
     for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(c), sl, mw, smem + Cf::bPF);
-    wait_vm<Cf::bwdA + Cf::bwdB + Cf::bwdA + Cf::PFD - 2>();
+    wait_mover<Cf::bwdA + Cf::bwdB + Cf::bwdA + Cf::PFD - 2>(hs);
     chain_barrier();   // B0
-    wait_vm<Cf::bwdB + Cf::bwdA + Cf::PFD - 2>();
+    wait_mover<Cf::bwdB + Cf::bwdA + Cf::PFD - 2>(hs);
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
       move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0, slot(k + 2), mw, true);
-      wait_vm<Cf::bwdA + 1 + Cf::bwdB>();
+      wait_mover<Cf::bwdA + 1 + Cf::bwdB>(hs);
       chain_barrier();   // B2
       move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
       prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(k + Cf::PFD), sl, mw, smem + Cf::bPF);
-      wait_vm<Cf::bwdB + Cf::bwdA + 2>();
+      wait_mover<Cf::bwdB + Cf::bwdA + 2>(hs);
     }
     wait_vm<0>();
   }
