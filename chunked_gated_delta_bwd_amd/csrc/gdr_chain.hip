@@ -24,10 +24,12 @@
 //              slice, row factors, decay) global -> LDS with direct-to-LDS loads
 //              (no registers, no ALU), up to two chunks ahead.
 // Every big tile has two LDS buffers (chunk k in buffer k % 2), the small data
-// three rotating slots.  A tile read in the first window of a step (between its
-// barriers B1 and B2) is refilled after B2, a tile read in the second window
-// after the next B1, so each load has one and a half steps to land; the movers
-// wait for their own loads with vmcnt before the barrier that publishes them.
+// three rotating slots.  Set A, read only in the first window of a step (between
+// its barriers B1 and B2), is refilled after B2 with the chunk two steps ahead
+// (one and a half steps to land); set B, read in the second window (and in the
+// reverse role in the first as well), is refilled after the next B1 with the
+// next chunk (one step to land).  The movers wait for their own loads with
+// vmcnt before the barrier that publishes them.
 //
 // Tiles are stored unpadded with an XOR swizzle of their 16-byte pieces (one
 // direct-to-LDS load writes 1 KB contiguously, so the swizzle is applied by
@@ -756,7 +758,8 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(c), sl, mw, smem + Cf::bPF);
     wait_mover<Cf::bwdA + Cf::bwdB + Cf::bwdA + Cf::PFD - 2>(hs);
     chain_barrier();   // B0
-    wait_mover<Cf::bwdB + Cf::bwdA + Cf::PFD - 2>(hs);
+    // both sets of chunk 0 land before B1 (set B is read in the first window too)
+    wait_mover<Cf::bwdA + Cf::PFD - 1>(hs);
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
@@ -765,7 +768,9 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       chain_barrier();   // B2
       move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
       prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(k + Cf::PFD), sl, mw, smem + Cf::bPF);
-      wait_mover<Cf::bwdB + Cf::bwdA + 2>(hs);
+      // set B of chunk k + 1 lands before the next B1: only the small data of
+      // chunk k + 2, set A of chunk k + 2 and the prefetch stay in flight
+      wait_mover<Cf::bwdA + 2>(hs);
     }
     wait_vm<0>();
   }
