@@ -74,7 +74,7 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.stab = take(N * sizeof(gdr::SeqEntry));
   L.gam = take(H * NC * C * gk * 4);
   L.rho = take(H * NC * 3 * C * 4);
-  L.fac = take(H * NC * 2 * C * 4);
+  L.fac = take(H * NC * 3 * C * 4);
   L.edec = take(H * NC * (gk == 1 ? 4 : gk) * 4);
   L.A = take(H * NC * C * C * 2);
   L.P = take(H * NC * C * C * 2);

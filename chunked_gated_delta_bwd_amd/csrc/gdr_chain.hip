@@ -71,14 +71,19 @@ struct ChainCfg {
   static constexpr int XB = C * 16 * 2;            // a 64 x 16 bf16 slice
   static constexpr int NJ = TB / 4096;             // 1 KB loads per mover wave per 64 x D tile
   // small per-chunk data, three rotating slots: the raw dO slice (bf16 inputs),
-  // the row factors fq, fk (raw mode) and the decay
+  // the row factors fq, fk, fw (raw mode) and the decay
+  static constexpr int NFAC = 3;
   static constexpr int sDO = 0;
   static constexpr int sFac = sDO + (LO ? 0 : XB);
-  static constexpr int sDec = sFac + (RAW ? 2 * C * 4 : 0);
+  static constexpr int sDec = sFac + (RAW ? NFAC * C * 4 : 0);
   static constexpr int SLOT = sDec + DG * 4;
-  // reverse role, byte offsets; the tile buffers first
-  static constexpr int bK = 0, bQh = TB, bQl = 2 * TB, bW = (MAT ? 3 : 2) * TB, bP = bW + TB;
-  static constexpr int bufB = bP + PB;
+  // reverse role, byte offsets; the tile buffers first.  Materialised tiles:
+  // Khat, Qbar high, low, W, P.  Raw mode: q, P (set A), k, A (set B), where
+  // W^T dU is formed as k^T (Diag(fw) A^T dU) from the raw k rows already there
+  static constexpr int bK = 0, bQh = TB, bQl = 2 * TB, bW = 3 * TB;
+  static constexpr int bP = MAT ? 4 * TB : 2 * TB;
+  static constexpr int bA = 2 * TB + PB;                           // raw mode
+  static constexpr int bufB = MAT ? 4 * TB + PB : 2 * TB + 2 * PB;
   static constexpr int bX1 = 2 * bufB;                             // LO: dO high part
   static constexpr int bX2 = bX1 + (LO ? 2 * XB : 0);              // RAW: fq dO high; LO: dO low
   static constexpr int bX3 = bX2 + ((RAW || LO) ? 2 * XB : 0);     // RAW: fq dO low
@@ -108,7 +113,7 @@ struct ChainCfg {
   // none wait for one fewer: wait_mover)
   static constexpr int nSb = 1;
   static constexpr int nSf = 1;
-  static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 : 2) * NJ + nSb;
+  static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 * NJ : NJ + 2) + nSb;
   // L2 prefetch distance in chunk steps (one prefetch load per mover wave per step)
   static constexpr int PFD = 5;
   static constexpr int fwdA = NJ + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
@@ -187,7 +192,7 @@ __device__ __forceinline__ void move_p(const MoverLane<D>& ml, const void* src, 
   for (int j = 0; j < 2; ++j) dma16(s + ml.tP[j], dst + mw * 2048 + j * 1024);
 }
 
-// small data of chunk c into a slot: the dO slice (reverse role), fq / fk, decay,
+// small data of chunk c into a slot: the dO slice (reverse role), fq / fk / fw, decay,
 // in as few whole-wave loads as possible (a load costs about the same however few
 // bytes it carries): reverse role, movers 0 and 1 one half of the dO slice each
 // (rows 32 mw .. 32 mw + 31, two pieces a row), mover 2 the row factors and the
@@ -214,10 +219,11 @@ __device__ __forceinline__ void move_small(const Params& p, const SeqEntry& se, 
       dma16(src, slot + Cf::sDO + mw * 1024);
     } else if (mw == (with_dO ? 2 : 0)) {
       if constexpr (Cf::RAW) {
-        // fq, fk (512 bytes, lanes 0-31), then the decay (lane 32) right behind them
-        static_assert(Cf::sDec == Cf::sFac + 2 * C * 4, "decay follows the row factors");
-        if (l < 32) dma16(reinterpret_cast<const char*>(p.fac + cg.ch * 2 * C) + l * 16, slot + Cf::sFac);
-        else if (l == 32) dma16(p.edec + cg.ch * 4, slot + Cf::sFac);
+        // fq, fk, fw (768 bytes, lanes 0-47), then the decay (lane 48) right behind them
+        constexpr int NL = Cf::NFAC * C * 4 / 16;
+        static_assert(Cf::sDec == Cf::sFac + NL * 16, "decay follows the row factors");
+        if (l < NL) dma16(reinterpret_cast<const char*>(p.fac + cg.ch * Cf::NFAC * C) + l * 16, slot + Cf::sFac);
+        else if (l == NL) dma16(p.edec + cg.ch * 4, slot + Cf::sFac);
       } else {
         if (l < D / 4) dma16(reinterpret_cast<const char*>(p.edec + cg.ch * D) + l * 16, slot + Cf::sDec);
       }
@@ -234,14 +240,15 @@ __device__ __forceinline__ void wait_mover(bool has_small) {
   else wait_vm<N - 1>();
 }
 
-// reverse role: set A (Khat or k, P), set B (Qbar high [+ low] or q, W)
+// reverse role: set A (Khat, P; raw mode q, P), set B (Qbar high + low, W; raw
+// mode k, A)
 template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void move_bwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            char* buf, int mw) {
   using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
   if constexpr (Cf::RAW)
-    move_rows<D>(ml, p.k, p, cg, h, buf + Cf::bK, mw);
+    move_rows<D>(ml, p.q, p, cg, h, buf + Cf::bQh, mw);
   else
     move_tile<D>(ml, p.Kh + cg.ch * C * D, buf + Cf::bK, mw);
   move_p<D>(ml, p.P + cg.ch * C * C, buf + Cf::bP, mw);
@@ -253,12 +260,13 @@ __device__ __forceinline__ void move_bwd_b(const MoverLane<D>& ml, const Params&
   using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
   if constexpr (Cf::RAW) {
-    move_rows<D>(ml, p.q, p, cg, h, buf + Cf::bQh, mw);
+    move_rows<D>(ml, p.k, p, cg, h, buf + Cf::bK, mw);
+    move_p<D>(ml, p.A + cg.ch * C * C, buf + Cf::bA, mw);
   } else {
     move_tile<D>(ml, p.Qh + cg.ch * C * D, buf + Cf::bQh, mw);
     move_tile<D>(ml, p.Ql + cg.ch * C * D, buf + Cf::bQl, mw);
+    move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::bW, mw);
   }
-  move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::bW, mw);
 }
 
 // forward role: set A (W, the U' slice), set B (Khat or k)
@@ -298,10 +306,12 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const SeqEntry& 
   constexpr int LB = 64;                                   // bytes per prefetch load
   constexpr int LPR = (2 * D) / LB;                        // loads per row of a 64 x D bf16 tile
   constexpr int DOL = int(D * sizeof(TIO)) / LB;           // loads per dO row of one head
-  constexpr int NP = 128 / LB;                             // loads per P row
-  constexpr int NT = BWD ? (Cf::MAT ? 4 : 3) : 2;          // tiles with D-wide rows
-  constexpr int N1 = NT * RW * LPR, N2 = N1 + (BWD ? RW * NP : 0), N3 = N2 + (BWD ? RW * DOL : RW * LPR);
-  static_assert(N3 + 512 / LB <= 64, "one prefetch load per wave");
+  constexpr int NP = 128 / LB;                             // loads per row of a 64 x 64 tile
+  constexpr int NT = BWD ? (Cf::MAT ? 4 : 2) : 2;          // tiles with D-wide rows
+  constexpr int NT64 = BWD ? (Cf::MAT ? 1 : 2) : 0;        // 64 x 64 tiles (P; raw mode P, A)
+  constexpr int NTAIL = (Cf::RAW ? Cf::NFAC * C * 4 : 512) / LB;   // row factors or the decay
+  constexpr int N1 = NT * RW * LPR, N2 = N1 + NT64 * RW * NP, N3 = N2 + (BWD ? RW * DOL : RW * LPR);
+  static_assert(N3 + NTAIL <= 64, "one prefetch load per wave");
   const ChunkGeo cg = geo(p, se, h, c);
   const int l = lane_id(), r0 = sl * R + mw * RW;
   const char* a = nullptr;
@@ -317,7 +327,7 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const SeqEntry& 
     const char* rb;
     if constexpr (BWD) {
       if constexpr (Cf::RAW)
-        rb = t == 0 ? tok_row(p.k, row, 2) : t == 1 ? tok_row(p.q, row, 2) : tile_row(p.W, row);
+        rb = t == 0 ? tok_row(p.k, row, 2) : tok_row(p.q, row, 2);
       else
         rb = t == 0 ? tile_row(p.Kh, row) : t == 1 ? tile_row(p.Qh, row) : t == 2 ? tile_row(p.Ql, row) : tile_row(p.W, row);
     } else {
@@ -328,7 +338,9 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const SeqEntry& 
     }
     a = rb + line * LB;
   } else if (l < N2) {
-    a = reinterpret_cast<const char*>(p.P + (cg.ch * C + r0 + (l - N1) / NP) * C) + ((l - N1) % NP) * LB;
+    const int i = l - N1, t = i / (RW * NP), rem = i % (RW * NP);
+    const uint16_t* base = t == 0 ? p.P : p.A;
+    a = reinterpret_cast<const char*>(base + (cg.ch * C + r0 + rem / NP) * C) + (rem % NP) * LB;
   } else if (l < N3) {
     if constexpr (BWD) {
       const int i = l - N2;
@@ -337,12 +349,12 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const SeqEntry& 
       const int i = l - N2;
       a = tile_row(p.Up, r0 + i / LPR) + (i % LPR) * LB;
     }
-  } else if (sl == 0 && mw == 0 && l < N3 + 512 / LB) {
+  } else if (sl == 0 && mw == 0 && l < N3 + NTAIL) {
     const int i = l - N3;
-    if constexpr (GATE == 1)
-      a = reinterpret_cast<const char*>(p.edec + cg.ch * D) + (i * LB) % (D * 4);
+    if constexpr (Cf::RAW)
+      a = reinterpret_cast<const char*>(p.fac + cg.ch * Cf::NFAC * C) + i * LB;
     else
-      a = reinterpret_cast<const char*>(p.fac + cg.ch * 2 * C) + i * LB;
+      a = reinterpret_cast<const char*>(p.edec + cg.ch * (GATE == 1 ? D : 4)) + (i * LB) % (GATE == 1 ? D * 4 : 16);
   }
   if (a) dma4(a, sink);
 }
@@ -694,15 +706,57 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         }
         an[x] = a;
       }
+      f32x4 fwv[4];   // raw mode: fw of this lane's Y rows 16 rb + 4g .. +3
+      if constexpr (Cf::RAW) {
+        const float* fw = reinterpret_cast<const float*>(sl_k + Cf::sFac) + 2 * C;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const float4 f = *reinterpret_cast<const float4*>(fw + 16 * rb + 4 * g);
+          fwv[rb] = f32x4{f.x, f.y, f.z, f.w};
+        }
+      }
       chain_barrier();   // B2
+      if constexpr (Cf::RAW) {
+        // W^T dU = k^T Y with Y = Diag(fw) A^T dU (W = A Diag(fw) k).  Every wave
+        // forms all 64 rows of Y (A is block lower triangular: row block rb takes
+        // dU rows from 16 rb on) and feeds its accumulators, rounded to bf16,
+        // straight back as the B operand of k^T Y, K-step kk pairing the row
+        // blocks 2kk and 2kk+1 (frag_kc_split_s reads k^T in that row order)
+        const bf16x8 du0 = frag_rk_s<C, 1>(dUt, 0, 0), du1 = frag_rk_s<C, 1>(dUt, 0, 32);
+        f32x4 y[4];
 #pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        const int jb = w * NJW + x;
-        f32x4 aw = zero4();
+        for (int rb = 0; rb < 4; ++rb) {
+          y[rb] = zero4();
+          if (rb < 2) y[rb] = mma(frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 0), du0, y[rb]);
+          y[rb] = mma(frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 32), du1, y[rb]);
+          y[rb] *= fwv[rb];
+        }
+        bf16x8 yb[2];
 #pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32)
-          aw = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C, 1>(dUt, 0, k0), aw);
-        acc[x] = an[x] - aw;
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            yb[kk][i] = to_bf16(y[2 * kk][i]);
+            yb[kk][4 + i] = to_bf16(y[2 * kk + 1][i]);
+          }
+#pragma unroll
+        for (int x = 0; x < NJW; ++x) {
+          const int jb = w * NJW + x;
+          f32x4 aw = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) aw = mma(frag_kc_split_s<D>(Bb + Cf::bK, 16 * jb, 32 * kk), yb[kk], aw);
+          acc[x] = an[x] - aw;
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < NJW; ++x) {
+          const int jb = w * NJW + x;
+          f32x4 aw = zero4();
+#pragma unroll
+          for (int k0 = 0; k0 < C; k0 += 32)
+            aw = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C, 1>(dUt, 0, k0), aw);
+          acc[x] = an[x] - aw;
+        }
       }
       if constexpr (Cf::RAW)
         convert_raw_rows<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);

@@ -156,8 +156,9 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   // inputs the Khat and Qbar (high + low) tiles ---
   if (tid < C) {
     const float m = tid < len ? 1.f : 0.f, gC = gam_s[C - 1], gr = gam_s[tid];
-    p.fac[ch * 2 * C + tid] = m * p.scale * rq_s[tid] * fast_exp(gr);
-    p.fac[ch * 2 * C + C + tid] = m * rk_s[tid] * fast_exp(gC - gr);
+    p.fac[ch * 3 * C + tid] = m * p.scale * rq_s[tid] * fast_exp(gr);
+    p.fac[ch * 3 * C + C + tid] = m * rk_s[tid] * fast_exp(gC - gr);
+    p.fac[ch * 3 * C + 2 * C + tid] = beta_s[tid] * rk_s[tid] * fast_exp(gr);   // W = A Diag(this) k
     if (tid == 0) p.edec[ch * 4] = fast_exp(gC);
   }
   if constexpr (kMat) {
