@@ -645,7 +645,8 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     }
     if (nck > 0) chain_barrier();   // B0
     // raw mode: the compute waves form fq dO (high, low) of each chunk's dO slice
-    // one step ahead, a quarter each (published by the next first barrier)
+    // one step ahead, a quarter each (chunk 0 here, chunk k + 1 in the first
+    // window of step k; published by the next barrier)
     if constexpr (Cf::RAW)
       if (nck > 0) convert_raw_rows<D, TIO, GATE>(slot(0), smem + Cf::bX2, smem + Cf::bX3, w);
     for (int k = 0; k < nck; ++k) {
@@ -683,6 +684,8 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         ad += ak;
       }
       st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
+      if constexpr (Cf::RAW)
+        convert_raw_rows<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
       // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU: the first two terms do
       // not depend on dU and are issued before the barrier
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
@@ -706,7 +709,10 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         }
         an[x] = a;
       }
-      f32x4 fwv[4];   // raw mode: fw of this lane's Y rows 16 rb + 4g .. +3
+      // raw mode: fw of this lane's Y rows 16 rb + 4g .. +3 and the k^T fragments
+      // of the second window, read before B2
+      f32x4 fwv[4];
+      bf16x8 kfr[NJW][2];
       if constexpr (Cf::RAW) {
         const float* fw = reinterpret_cast<const float*>(sl_k + Cf::sFac) + 2 * C;
 #pragma unroll
@@ -714,6 +720,10 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
           const float4 f = *reinterpret_cast<const float4*>(fw + 16 * rb + 4 * g);
           fwv[rb] = f32x4{f.x, f.y, f.z, f.w};
         }
+#pragma unroll
+        for (int x = 0; x < NJW; ++x)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) kfr[x][kk] = frag_kc_split_s<D>(Bb + Cf::bK, 16 * (w * NJW + x), 32 * kk);
       }
       chain_barrier();   // B2
       if constexpr (Cf::RAW) {
@@ -744,7 +754,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
           const int jb = w * NJW + x;
           f32x4 aw = zero4();
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) aw = mma(frag_kc_split_s<D>(Bb + Cf::bK, 16 * jb, 32 * kk), yb[kk], aw);
+          for (int kk = 0; kk < 2; ++kk) aw = mma(kfr[x][kk], yb[kk], aw);
           acc[x] = an[x] - aw;
         }
       } else {
@@ -758,8 +768,6 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
           acc[x] = an[x] - aw;
         }
       }
-      if constexpr (Cf::RAW)
-        convert_raw_rows<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
     }
     if (p.dh0) {
 #pragma unroll
@@ -812,8 +820,9 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(c), sl, mw, smem + Cf::bPF);
     wait_mover<Cf::bwdA + Cf::bwdB + Cf::bwdA + Cf::PFD - 2>(hs);
     chain_barrier();   // B0
-    // both sets of chunk 0 land before B1 (set B is read in the first window too)
-    wait_mover<Cf::bwdA + Cf::PFD - 1>(hs);
+    // both sets of chunk 0 and the small data of chunk 1 land before B1 (set B is
+    // read in the first window too, and so is the next chunk's small data)
+    wait_vm<Cf::bwdA + Cf::PFD - 2>();
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
@@ -822,9 +831,9 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       chain_barrier();   // B2
       move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
       prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(k + Cf::PFD), sl, mw, smem + Cf::bPF);
-      // set B of chunk k + 1 lands before the next B1: only the small data of
-      // chunk k + 2, set A of chunk k + 2 and the prefetch stay in flight
-      wait_mover<Cf::bwdA + 2>(hs);
+      // set B of chunk k + 1 and the small data of chunk k + 2 land before the
+      // next B1: only set A of chunk k + 2 and the prefetch stay in flight
+      wait_vm<Cf::bwdA + 1>();
     }
     wait_vm<0>();
   }
