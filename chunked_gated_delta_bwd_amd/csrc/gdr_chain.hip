@@ -97,7 +97,10 @@ struct ChainCfg {
   static constexpr int bPF = bdU + NDU * dUB;                      // 256 B sink of the L2 prefetches
   static constexpr int bEnd = bPF + 256;
   // forward role
-  static constexpr int fW = 0, fK = TB, fUp = 2 * TB, fUpl = fUp + XB, bufF = fUpl + (SPLIT ? XB : 0);
+  // forward role: materialised tiles W, Khat; raw mode A (in W's place) and k,
+  // with W S^T formed as A (Diag(fw) k S^T)
+  static constexpr int fW = 0, fA = 0, fK = MAT ? TB : PB, fUp = fK + TB, fUpl = fUp + XB;
+  static constexpr int bufF = fUpl + (SPLIT ? XB : 0);
   static constexpr int fSlot = 2 * bufF;
   static constexpr int fS = fSlot + 3 * SLOT;                      // 16 x D state slice
   static constexpr int fU = fS + 16 * D * 2;                       // 16 x 64: U^T as the MFMA takes it
@@ -116,7 +119,7 @@ struct ChainCfg {
   static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 * NJ : NJ + 2) + nSb;
   // L2 prefetch distance in chunk steps (one prefetch load per mover wave per step)
   static constexpr int PFD = 5;
-  static constexpr int fwdA = NJ + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
+  static constexpr int fwdA = (MAT ? NJ : 2) + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(2 * bwdA + bwdB + PFD - 2 < 64 && 2 * fwdA + fwdB + PFD - 2 < 64, "vmcnt range");
 };
@@ -269,13 +272,16 @@ __device__ __forceinline__ void move_bwd_b(const MoverLane<D>& ml, const Params&
   }
 }
 
-// forward role: set A (W, the U' slice), set B (Khat or k)
+// forward role: set A (W or, raw mode, A; the U' slice), set B (Khat or k)
 template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void move_fwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            int v0, char* buf, int mw) {
   using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
-  move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::fW, mw);
+  if constexpr (Cf::MAT)
+    move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::fW, mw);
+  else
+    move_p<D>(ml, p.A + cg.ch * C * C, buf + Cf::fA, mw);
   if (lane_id() < 32) dma16(reinterpret_cast<const char*>(p.Up + cg.ch * C * D + v0) + ml.up, buf + Cf::fUp + mw * 512);
   if constexpr (Cf::SPLIT) {
     if (lane_id() < 32)
@@ -307,8 +313,8 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const SeqEntry& 
   constexpr int LPR = (2 * D) / LB;                        // loads per row of a 64 x D bf16 tile
   constexpr int DOL = int(D * sizeof(TIO)) / LB;           // loads per dO row of one head
   constexpr int NP = 128 / LB;                             // loads per row of a 64 x 64 tile
-  constexpr int NT = BWD ? (Cf::MAT ? 4 : 2) : 2;          // tiles with D-wide rows
-  constexpr int NT64 = BWD ? (Cf::MAT ? 1 : 2) : 0;        // 64 x 64 tiles (P; raw mode P, A)
+  constexpr int NT = BWD ? (Cf::MAT ? 4 : 2) : (Cf::MAT ? 2 : 1);   // tiles with D-wide rows
+  constexpr int NT64 = BWD ? (Cf::MAT ? 1 : 2) : (Cf::MAT ? 0 : 1);  // 64 x 64 tiles (P, A)
   constexpr int NTAIL = (Cf::RAW ? Cf::NFAC * C * 4 : 512) / LB;   // row factors or the decay
   constexpr int N1 = NT * RW * LPR, N2 = N1 + NT64 * RW * NP, N3 = N2 + (BWD ? RW * DOL : RW * LPR);
   static_assert(N3 + NTAIL <= 64, "one prefetch load per wave");
@@ -332,14 +338,14 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const SeqEntry& 
         rb = t == 0 ? tile_row(p.Kh, row) : t == 1 ? tile_row(p.Qh, row) : t == 2 ? tile_row(p.Ql, row) : tile_row(p.W, row);
     } else {
       if constexpr (Cf::RAW)
-        rb = t == 0 ? tile_row(p.W, row) : tok_row(p.k, row, 2);
+        rb = tok_row(p.k, row, 2);
       else
         rb = t == 0 ? tile_row(p.W, row) : tile_row(p.Kh, row);
     }
     a = rb + line * LB;
   } else if (l < N2) {
     const int i = l - N1, t = i / (RW * NP), rem = i % (RW * NP);
-    const uint16_t* base = t == 0 ? p.P : p.A;
+    const uint16_t* base = BWD && t == 0 ? p.P : p.A;
     a = reinterpret_cast<const char*>(base + (cg.ch * C + r0 + rem / NP) * C) + (rem % NP) * LB;
   } else if (l < N3) {
     if constexpr (BWD) {
@@ -518,8 +524,37 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       chain_barrier();   // B1
       // U = U' - W S^T, rows 16w.., columns of this slice
       f32x4 au = zero4();
+      if constexpr (Cf::RAW) {
+        // W S^T = A Y with Y = Diag(fw) k S^T (W = A Diag(fw) k): every wave forms all
+        // 64 rows of Y (straight-line code schedules better than skipping the blocks
+        // that A's zero upper blocks do not need) and feeds its accumulators, rounded
+        // to bf16, straight back as the B operand, K-step kk pairing the row blocks
+        // 2kk and 2kk+1 (frag_rk_split_s reads the rows of A in that column order)
+        const float* fw = reinterpret_cast<const float*>(sl_k + Cf::sFac) + 2 * C;
+        f32x4 y[4];
 #pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) au = mma(frag_rk_s<D>(Fb + Cf::fW, 16 * w, k0), frag_rk_s<D>(Ss, 0, k0), au);
+        for (int rb = 0; rb < 4; ++rb) {
+          y[rb] = zero4();
+#pragma unroll
+          for (int k0 = 0; k0 < D; k0 += 32)
+            y[rb] = mma(frag_rk_s<D>(Fb + Cf::fK, 16 * rb, k0), frag_rk_s<D>(Ss, 0, k0), y[rb]);
+          const float4 f = *reinterpret_cast<const float4*>(fw + 16 * rb + 4 * g);
+          y[rb] *= f32x4{f.x, f.y, f.z, f.w};
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bf16x8 yb;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            yb[i] = to_bf16(y[2 * kk][i]);
+            yb[4 + i] = to_bf16(y[2 * kk + 1][i]);
+          }
+          au = mma(frag_rk_split_s<C>(Fb + Cf::fA, 16 * w, 32 * kk), yb, au);
+        }
+      } else {
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 32) au = mma(frag_rk_s<D>(Fb + Cf::fW, 16 * w, k0), frag_rk_s<D>(Ss, 0, k0), au);
+      }
       const uint16_t* Up = reinterpret_cast<const uint16_t*>(Fb + Cf::fUp);
       float u[4];
 #pragma unroll
@@ -597,7 +632,10 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(c), sl, mw, smem + Cf::fPF);
     wait_mover<Cf::fwdA + Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
     chain_barrier();   // B0
-    wait_mover<Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
+    // raw mode reads set B (k) in the first window too: both sets of chunk 0 land
+    // before B1; otherwise set B may land by B2
+    if constexpr (Cf::RAW) wait_mover<Cf::fwdA + Cf::PFD - 1>(hs);
+    else wait_mover<Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
@@ -606,7 +644,8 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       chain_barrier();   // B2
       move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0, smem + (k & 1) * Cf::bufF, mw);
       prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(k + Cf::PFD), sl, mw, smem + Cf::fPF);
-      wait_mover<Cf::fwdB + Cf::fwdA + 2>(hs);
+      if constexpr (Cf::RAW) wait_mover<Cf::fwdA + 2>(hs);   // set B of chunk k + 1 before the next B1
+      else wait_mover<Cf::fwdB + Cf::fwdA + 2>(hs);
     }
     wait_vm<0>();
   }

@@ -44,7 +44,7 @@ struct WsLayout {
   size_t edec = 0;   // fp32 [H][NC][4] (value, 3 pad) or [H][NC][K]: chunk decay e^GamC
   size_t A = 0;      // bf16 [H][NC][64][64]: UT/WY inverse
   size_t P = 0;      // bf16 [H][NC][64][64]: scale * (Qn Kn^T o E), lower incl. diagonal
-  size_t W = 0;      // bf16 [H][NC][64][K]:  A diag(beta) Kbar
+  size_t W = 0;      // bf16 [H][NC][64][K]:  A diag(beta) Kbar (materialised tiles only)
   size_t Up = 0;     // bf16 [H][NC][64][V]:  U' = A diag(beta) V
   size_t U = 0;      // bf16 [H][NC][V][64]:  v_new = U' - W S^T (forward state pass), transposed
   size_t S = 0;      // bf16 [H][NC][V][K]:   state at chunk start

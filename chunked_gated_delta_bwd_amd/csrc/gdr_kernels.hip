@@ -218,7 +218,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
     *reinterpret_cast<u32x4*>(p.P + (ch * C + row) * C + c8) = *reinterpret_cast<const u32x4*>(As + row * PC + c8);
   }
 
-  // --- beta * Kbar and beta * V overwrite the operand tiles ---
+  // --- beta * Kbar (for W; fp32 inputs only, bf16 inputs leave W to the
+  // recursions as A Diag(fw) k) and beta * V overwrite the operand tiles ---
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
       kb[e] = to_bf16(kn_r[ps][e] * fk);
       vb[e] = to_bf16(v_r[ps][e] * fv);
     }
-    *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
+    if constexpr (kMat) *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
     *reinterpret_cast<bf16x8*>(Vs + r * PD + c0) = vb;
   }
 
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   }
   __syncthreads();
 
-  // --- W^T and U'^T tiles: lane owns W[r][j .. j+3] ---
+  // --- W (fp32 inputs) and U' tiles: lane owns W[r][j .. j+3] ---
   {
     const int r = 16 * w + (l & 15);
 #pragma unroll
@@ -297,11 +298,11 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
 #pragma unroll
       for (int k0 = 0; k0 < C; k0 += 32) {
         const bf16x8 b = frag_rk(As, PC, 16 * w, k0);  // B[s][r] = A[r][s]
-        aW = mma(frag_kc(Ks, PD, 16 * jb, k0), b, aW);
+        if constexpr (kMat) aW = mma(frag_kc(Ks, PD, 16 * jb, k0), b, aW);
         aU = mma(frag_kc(Vs, PD, 16 * jb, k0), b, aU);
       }
       const int j0 = 16 * jb + 4 * (l >> 4);
-      st_bf16x4(p.W + (ch * C + r) * D + j0, aW[0], aW[1], aW[2], aW[3]);
+      if constexpr (kMat) st_bf16x4(p.W + (ch * C + r) * D + j0, aW[0], aW[1], aW[2], aW[3]);
       st_bf16x4(p.Up + (ch * C + r) * D + j0, aU[0], aU[1], aU[2], aU[3]);
     }
   }

@@ -84,6 +84,17 @@ __device__ __forceinline__ bf16x8 frag_kc_split_s(const char* T, int c0, int k0)
   return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// T[r0 + j][m_e], m_e as in frag_kc_split_s: the row-fragment form of the same
+// K order (two 8-byte reads)
+template <int W, int KIND = 0>
+__device__ __forceinline__ bf16x8 frag_rk_split_s(const char* T, int r0, int k0) {
+  const int l = lane_id();
+  const int r = r0 + (l & 15), c = k0 + 4 * (l >> 4);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(T + soff<W, KIND>(r, c));
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(T + soff<W, KIND>(r, c + 16));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 template <int W, int KIND = 0>
 __device__ __forceinline__ void st4_s(char* T, int r, int c, float a, float b, float d, float e) {
   *reinterpret_cast<uint2*>(T + soff<W, KIND>(r, c)) = pack4_bf16(a, b, d, e);
