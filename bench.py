@@ -73,13 +73,21 @@ def algorithmic_work(inp, stage: str):
     f_fwd = 4 * C * D * D
     f_bwd = 6 * C * D * D + C * C * D
     f_grads = 6 * C * D * D + 9 * C * C * D
+    # scalar gate with bf16 inputs: the recursions take the raw q, k rows and row
+    # factors, and W = A Diag(fw) k is never formed (A, 64 x 64, replaces W, 64 x D)
+    raw = inp["gate"] == 0 and inp["dtype"] == "bf16"
+    wt = C * C * 2 if raw else C * D * 2
     if stage == "prep":
-        b = tokens * H * (3 * D * io + (1 + gk) * io) + ch * (C * gk * 4 + 2 * C * 4 + 2 * C * C * 2 + 2 * C * D * 2)
+        # q, k, v, g, b in; Gamma, row scalars, A, P, U' (and W unless raw) out
+        b = tokens * H * (3 * D * io + (1 + gk) * io) + ch * (C * gk * 4 + 2 * C * 4 + 2 * C * C * 2
+                                                              + (1 if raw else 2) * C * D * 2)
         return ch * f_prep, b
     if stage == "chain_fwd":
-        return ch * f_fwd, ch * (C * D * 2 * 2 + D * D * 2 + C * D * 2) + tokens * H * D * io
+        # W (or A), U', k in; S, U out
+        return ch * f_fwd, ch * (wt + C * D * 2 + D * D * 2 + C * D * 2) + tokens * H * D * io
     if stage == "chain_bwd":
-        return ch * f_bwd, ch * (C * D * 2 + C * C * 2 + D * D * 2 + C * D * 2) + tokens * H * 3 * D * io
+        # W (or A), P, q, k, dO in; dS, dU out
+        return ch * f_bwd, ch * (wt + C * C * 2 + D * D * 2 + C * D * 2) + tokens * H * 3 * D * io
     if stage == "chain_both":
         a, b = algorithmic_work(inp, "chain_fwd"), algorithmic_work(inp, "chain_bwd")
         return a[0] + b[0], a[1] + b[1]
