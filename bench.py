@@ -35,9 +35,9 @@ CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 # 1 GiB copy; profiles/gdn_t32768_h16_d128.md), valid only for the kernel
 # sources they were taken on: (workload, stage, sha256 prefix) -> bytes.
 MEASURED_TRAFFIC = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "2fbbfd42bff3"): 0.851e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "2fbbfd42bff3"): 1.824e9,
-    ("gdn_bf16_t32768_h16_d128", "grads", "2fbbfd42bff3"): 1.855e9,
+    ("gdn_bf16_t32768_h16_d128", "prep", "f7d3ee63dca0"): 0.716e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "f7d3ee63dca0"): 1.690e9,
+    ("gdn_bf16_t32768_h16_d128", "grads", "f7d3ee63dca0"): 1.855e9,
 }
 
 
