@@ -705,6 +705,10 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
                     lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
       }
       chain_barrier();   // B1
+      // raw mode: fq dO (high, low) of the next chunk first, so that its LDS round
+      // trip overlaps the fragment reads below
+      if constexpr (Cf::RAW)
+        convert_raw_rows<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
       // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice
       f32x4 ad = zero4(), ak = zero4();
 #pragma unroll
@@ -723,8 +727,6 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         ad += ak;
       }
       st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
-      if constexpr (Cf::RAW)
-        convert_raw_rows<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
       // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU: the first two terms do
       // not depend on dU and are issued before the barrier
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
@@ -748,22 +750,6 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         }
         an[x] = a;
       }
-      // raw mode: fw of this lane's Y rows 16 rb + 4g .. +3 and the k^T fragments
-      // of the second window, read before B2
-      f32x4 fwv[4];
-      bf16x8 kfr[NJW][2];
-      if constexpr (Cf::RAW) {
-        const float* fw = reinterpret_cast<const float*>(sl_k + Cf::sFac) + 2 * C;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const float4 f = *reinterpret_cast<const float4*>(fw + 16 * rb + 4 * g);
-          fwv[rb] = f32x4{f.x, f.y, f.z, f.w};
-        }
-#pragma unroll
-        for (int x = 0; x < NJW; ++x)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) kfr[x][kk] = frag_kc_split_s<D>(Bb + Cf::bK, 16 * (w * NJW + x), 32 * kk);
-      }
       chain_barrier();   // B2
       if constexpr (Cf::RAW) {
         // W^T dU = k^T Y with Y = Diag(fw) A^T dU (W = A Diag(fw) k).  Every wave
@@ -772,6 +758,20 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         // straight back as the B operand of k^T Y, K-step kk pairing the row
         // blocks 2kk and 2kk+1 (frag_kc_split_s reads k^T in that row order)
         const bf16x8 du0 = frag_rk_s<C, 1>(dUt, 0, 0), du1 = frag_rk_s<C, 1>(dUt, 0, 32);
+        // fw of this lane's Y rows 16 rb + 4g .. +3 and the k^T fragments, read in
+        // the same round trip as dU
+        const float* fw = reinterpret_cast<const float*>(sl_k + Cf::sFac) + 2 * C;
+        f32x4 fwv[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const float4 f = *reinterpret_cast<const float4*>(fw + 16 * rb + 4 * g);
+          fwv[rb] = f32x4{f.x, f.y, f.z, f.w};
+        }
+        bf16x8 kfr[NJW][2];
+#pragma unroll
+        for (int x = 0; x < NJW; ++x)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) kfr[x][kk] = frag_kc_split_s<D>(Bb + Cf::bK, 16 * (w * NJW + x), 32 * kk);
         f32x4 y[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
