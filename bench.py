@@ -91,6 +91,10 @@ def algorithmic_work(inp, stage: str):
     if stage == "chain_both":
         a, b = algorithmic_work(inp, "chain_fwd"), algorithmic_work(inp, "chain_bwd")
         return a[0] + b[0], a[1] + b[1]
+    if stage == "output":
+        # S_n, U, P and Qbar (or the raw q rows and row factors) in; o out
+        b = ch * (D * D * 2 + C * D * 2 + C * C * 2 + (0 if raw else C * D * 2)) + tokens * H * D * io * (2 if raw else 1)
+        return ch * (2 * C * D * D + C * C * D), b
     if stage == "grads":
         if inp["gate"] == 0:
             # fused with the prepare-backward: S, dS, U, dU, A, Gamma, (1/|q|, 1/|k|, beta)
@@ -122,7 +126,7 @@ def time_it(fn, iters: int) -> float:
     return start.elapsed_time(end) / iters
 
 
-def cpu_baseline(inp, tokens: int):
+def cpu_baseline(inp, tokens: int, backward: bool = True):
     """The float64 oracle on the first `tokens` tokens of the workload (all heads)."""
     import oracle  # test infrastructure: only this leg of the benchmark uses it
 
@@ -138,14 +142,46 @@ def cpu_baseline(inp, tokens: int):
         sub["cu_seqlens"] = cu
         sub["lengths"] = [int(x) for x in (cu[1:] - cu[:-1])]
     threads = oracle.default_threads()
-    oracle.run(sub, nthreads=threads)  # build/load outside the timed call
+    oracle.run(sub, nthreads=threads, backward=backward)  # build/load outside the timed call
     t0 = time.perf_counter()
-    oracle.run(sub, nthreads=threads)
+    oracle.run(sub, nthreads=threads, backward=backward)
     dt = time.perf_counter() - t0
+    what = "token recurrence + adjoint" if backward else "token recurrence (forward only)"
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"first {tokens} of {inp['T']} tokens, all {inp['H']} heads of the same workload; "
-                      f"float64 token recurrence + adjoint, {threads} threads over (sequence, head)"}
+                      f"float64 {what}, {threads} threads over (sequence, head)"}
+
+
+def roofline(inp, workload: str, name: str, ms: float) -> Dict:
+    """The roofline record of one kernel: below the ridge point (peak FLOP/s over
+    peak bytes/s) its attainable rate is set by HBM, above it by the matrix cores."""
+    flops, nbytes = algorithmic_work(inp, name)
+    secs = ms * 1e-3
+    if flops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = nbytes / secs / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = flops / secs / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roof["traffic"] = MEASURED_TRAFFIC.get((workload, name, kernel_source_hash()))
+    roof["source_hash"] = kernel_source_hash()
+    roof["kernel"] = name
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = flops
+    roof["mfma_frac"] = round(flops / secs / 1e12 / PEAK_BF16_TFLOPS, 4)
+    return roof
+
+
+def kernel_record(inp, name: str, t: float) -> Dict:
+    flops, nbytes = algorithmic_work(inp, name)
+    return {"ms": round(t, 4),
+            "tflops": round(flops / t / 1e9, 2) if flops else 0.0,
+            "mfma_frac": round(flops / t / 1e9 / PEAK_BF16_TFLOPS, 4) if flops else 0.0,
+            "gbs": round(nbytes / t / 1e6, 1),
+            "hbm_frac": round(nbytes / t / 1e6 / PEAK_HBM_GBS, 4)}
 
 
 def main() -> int:
@@ -161,6 +197,8 @@ def main() -> int:
                     help="also time the forward and reverse recursions alone (two more chain launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy, the reference for HBM byte counters")
+    ap.add_argument("--path", choices=("bwd", "fwd"), default="bwd",
+                    help="bwd: the backward (gdr_fwd_bwd, the headline); fwd: the forward with its output (gdr_fwd)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU path is not built",
@@ -188,6 +226,8 @@ def main() -> int:
     out = B.alloc_outputs(inp, dev)
     N, H, K, V = inp["N"], inp["H"], inp["K"], inp["V"]
     ht = torch.empty((N, H, V, K), dtype=torch.float32, device="cuda")
+    if args.path == "fwd":
+        return bench_forward(args, inp, dev, prob, ws, out, ht)
 
     def step():
         B.gdr_fwd_bwd(prob, dev, dev["dO"], dev["dht"], ws, out, ht=ht)
@@ -211,32 +251,9 @@ def main() -> int:
         name = B.STAGE_NAMES[stage]
         fn = lambda s=stage: B.gdr_run_stage(prob, dev, dev["dO"], dev["dht"], ws, out, s, ht=ht)  # noqa: E731
         fn()
-        t = time_it(fn, args.stage_iters)
-        flops, nbytes = algorithmic_work(inp, name)
-        kernels[name] = {"ms": round(t, 4),
-                         "tflops": round(flops / t / 1e9, 2) if flops else 0.0,
-                         "mfma_frac": round(flops / t / 1e9 / PEAK_BF16_TFLOPS, 4) if flops else 0.0,
-                         "gbs": round(nbytes / t / 1e6, 1),
-                         "hbm_frac": round(nbytes / t / 1e6 / PEAK_HBM_GBS, 4)}
+        kernels[name] = kernel_record(inp, name, time_it(fn, args.stage_iters))
     dom = max(path, key=lambda n: kernels[n]["ms"])
-    flops, nbytes = algorithmic_work(inp, dom)
-    # roofline: below the ridge point (peak FLOP/s over peak bytes/s) a kernel's
-    # attainable rate is set by HBM, above it by the matrix cores
-    secs = kernels[dom]["ms"] * 1e-3
-    if flops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        achieved = nbytes / secs / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        achieved = flops / secs / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = MEASURED_TRAFFIC.get((args.workload, dom, kernel_source_hash()))
-    roof["source_hash"] = kernel_source_hash()
-    roof["kernel"] = dom
-    roof["algorithmic_bytes"] = nbytes
-    roof["algorithmic_flops"] = flops
-    roof["mfma_frac"] = round(flops / secs / 1e12 / PEAK_BF16_TFLOPS, 4)
+    roof = roofline(inp, args.workload, dom, kernels[dom]["ms"])
 
     line = {
         "metric": METRIC,
@@ -258,6 +275,56 @@ def main() -> int:
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_tokens, inp["T"]))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_forward(args, inp, dev, prob, ws, out, ht) -> int:
+    """The forward with its output (gdr_fwd): prologue, forward state pass, output
+    kernel.  The output kernel has no stage of its own: its time is the whole call's
+    minus the two stages before it."""
+    dt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    o = torch.empty((inp["B"], inp["T"], inp["H"], inp["V"]), dtype=dt, device="cuda")
+
+    def step():
+        B.gdr_fwd(prob, dev, ws, o, ht=ht)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_it(step, args.steps)
+    tokens = inp["B"] * inp["T"]
+    kernels = {}
+    for stage in (B.GDR_STAGE_PREP, B.GDR_STAGE_CHAIN_FWD):
+        name = B.STAGE_NAMES[stage]
+        fn = lambda s=stage: B.gdr_run_stage(prob, dev, dev["dO"], dev["dht"], ws, out, s, ht=ht)  # noqa: E731
+        fn()
+        kernels[name] = kernel_record(inp, name, time_it(fn, args.stage_iters))
+    step()
+    t_out = max(time_it(step, args.stage_iters) - kernels["prep"]["ms"] - kernels["chain_fwd"]["ms"], 1e-4)
+    kernels["output"] = kernel_record(inp, "output", t_out)
+    kernels["output"]["derived"] = True
+    dom = max(("prep", "chain_fwd"), key=lambda n: kernels[n]["ms"])
+    line = {
+        "metric": "gated-delta-rule fwd (o, ht) tokens/s + ms/fwd",
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if inp["dtype"] == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "path": "fwd", "B": inp["B"], "T": inp["T"], "H": inp["H"],
+                   "D": inp["K"], "gate": "scalar" if inp["gate"] == 0 else "channel", "chunk": C},
+        "roofline": roofline(inp, args.workload, dom, kernels[dom]["ms"]),
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_tokens, inp["T"]), backward=False)
     print(json.dumps(line), flush=True)
     return 0
 

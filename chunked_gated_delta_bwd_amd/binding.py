@@ -27,7 +27,7 @@ GDR_STAGE_GRADS, GDR_STAGE_FINISH = 4, 5
 STAGE_NAMES = {GDR_STAGE_PREP: "prep", GDR_STAGE_CHAIN_FWD: "chain_fwd", GDR_STAGE_CHAIN_BWD: "chain_bwd",
                GDR_STAGE_CHAIN_BOTH: "chain_both", GDR_STAGE_GRADS: "grads", GDR_STAGE_FINISH: "finish"}
 
-SYMBOLS = ("gdr_workspace_bytes", "gdr_fwd_recompute", "gdr_bwd", "gdr_fwd_bwd",
+SYMBOLS = ("gdr_workspace_bytes", "gdr_fwd_recompute", "gdr_fwd", "gdr_bwd", "gdr_fwd_bwd",
            "gdr_workspace_region", "gdr_run_stage", "gdr_last_error")
 
 
@@ -72,6 +72,8 @@ def load_library():
     lib.gdr_workspace_bytes.argtypes = [P(Shape), P(ctypes.c_size_t)]
     lib.gdr_fwd_recompute.argtypes = [P(Shape), P(Inputs), ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.gdr_fwd.argtypes = [P(Shape), P(Inputs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                            ctypes.c_void_p]
     lib.gdr_bwd.argtypes = [P(Shape), P(Inputs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                             ctypes.c_size_t, P(Grads), ctypes.c_void_p]
     lib.gdr_fwd_bwd.argtypes = [P(Shape), P(Inputs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -159,6 +161,13 @@ def gdr_fwd_recompute(prob: Problem, t: Dict, ws: torch.Tensor, ht: Optional[tor
     inp = _inputs(t)
     _check(load_library().gdr_fwd_recompute(ctypes.byref(prob.shape), ctypes.byref(inp), _ptr(ws),
                                             ws.numel() * ws.element_size(), _ptr(ht), _stream(stream)))
+
+
+def gdr_fwd(prob: Problem, t: Dict, ws: torch.Tensor, o: torch.Tensor, ht: Optional[torch.Tensor] = None,
+            stream=None) -> None:
+    inp = _inputs(t)
+    _check(load_library().gdr_fwd(ctypes.byref(prob.shape), ctypes.byref(inp), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _ptr(o), _ptr(ht), _stream(stream)))
 
 
 def gdr_bwd(prob: Problem, t: Dict, dO: torch.Tensor, dht: Optional[torch.Tensor], ws: torch.Tensor,

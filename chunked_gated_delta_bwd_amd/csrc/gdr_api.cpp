@@ -240,13 +240,15 @@ enum Stage { kFwd = 1, kBwd = 2, kFused = 3 };
 
 // `only` >= 0 restricts the launch sequence to one GDR_STAGE_* kernel.
 gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* dO, const float* dht,
-               void* ws, size_t ws_bytes, const gdr_grads* gr, float* ht, void* stream, int only = -1) {
+               void* ws, size_t ws_bytes, const gdr_grads* gr, float* ht, void* stream, int only = -1,
+               void* o = nullptr) {
   int64_t NC = 0;
   gdr_status st = check_shape(s, &NC);
   if (st != GDR_OK) return st;
   if ((st = check_inputs(s, in)) != GDR_OK) return st;
   if (stage != kFwd && (st = check_grads(s, dO, dht, gr)) != GDR_OK) return st;
   if (ht && !aligned16(ht)) return fail(GDR_EINVAL, "ht is not 16-byte aligned");
+  if (o && !aligned16(o)) return fail(GDR_EINVAL, "o is not 16-byte aligned");
   const gdr::WsLayout L = layout(s, NC);
   if ((st = check_ws(L, ws, ws_bytes)) != GDR_OK) return st;
 
@@ -254,6 +256,7 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
   if ((st = upload_tables(s, L, ws, hs)) != GDR_OK) return st;
   gdr::Params p = make_params(s, L, in, ws);
   p.ht = ht;
+  p.o = o;
   if (stage != kFwd) set_grads(p, dO, dht, gr);
 
   const bool kda = s->gate == GDR_GATE_CHANNEL;
@@ -283,6 +286,9 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
   }
   const int mode = stage == kFwd ? gdr::kChainFwd : stage == kBwd ? gdr::kChainBwd : gdr::kChainBoth;
   if ((st = hip_status(gdr::launch_chain(p, mode, stream), "chain kernel")) != GDR_OK) return st;
+  if (o && NC > 0) {
+    if ((st = hip_status(gdr::launch_output(p, stream), "output kernel")) != GDR_OK) return st;
+  }
   if (stage != kFwd) {
     if (NC > 0) {
       if ((st = hip_status(grads(), "gradient kernel")) != GDR_OK) return st;
@@ -311,6 +317,12 @@ gdr_status gdr_workspace_bytes(const gdr_shape* shape, size_t* bytes) {
 gdr_status gdr_fwd_recompute(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes, float* ht,
                              void* stream) {
   return run(kFwd, shape, in, nullptr, nullptr, ws, ws_bytes, nullptr, ht, stream);
+}
+
+gdr_status gdr_fwd(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes, void* o, float* ht,
+                   void* stream) {
+  if (!o) return fail(GDR_EINVAL, "o is NULL");
+  return run(kFwd, shape, in, nullptr, nullptr, ws, ws_bytes, nullptr, ht, stream, -1, o);
 }
 
 gdr_status gdr_bwd(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht, void* ws,

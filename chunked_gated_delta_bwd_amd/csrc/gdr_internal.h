@@ -83,6 +83,7 @@ struct Params {
   // outputs
   void *dq, *dk, *dv, *dg, *db;
   float *dh0, *dA_log, *ddt_bias, *ht;
+  void* o;   // forward output (gdr_fwd only)
   // workspace
   const ChunkEntry* ctab;
   const SeqEntry* stab;
@@ -105,6 +106,8 @@ int launch_prep(const Params& p, void* stream);
 int launch_chain(const Params& p, int mode, void* stream);
 int launch_grads(const Params& p, void* stream);
 int launch_zero_params(const Params& p, void* stream);
+// Forward output from the forward recompute's workspace (gdr_out.hip).
+int launch_output(const Params& p, void* stream);
 // Per-channel gate kernels (gdr_kda.hip): stage 0 prologue, 1 gradients,
 // 2 prepare-backward, 3 dA_log / ddt_bias reduction.
 int launch_kda(const Params& p, int stage, void* stream);

@@ -85,7 +85,7 @@ typedef struct {                    /* device pointers, all overwritten */
   float *dA_log, *ddt_bias;         /* CHANNEL: [H], [H,Dk] required; SCALAR: must be NULL */
 } gdr_grads;
 
-/* Bytes of workspace the three compute calls need for this shape. */
+/* Bytes of workspace the compute calls need for this shape. */
 gdr_status gdr_workspace_bytes(const gdr_shape* shape, size_t* bytes);
 
 /* Forward recompute: per-chunk prologue (normalisation, beta, in-chunk gate
@@ -97,6 +97,15 @@ gdr_status gdr_workspace_bytes(const gdr_shape* shape, size_t* bytes);
  * what earlier stages wrote, so any call may be repeated. */
 gdr_status gdr_fwd_recompute(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes,
                              float* ht, void* stream);
+
+/* Forward pass with its output, for training use: gdr_fwd_recompute followed by
+ * the chunk-parallel output O = Qbar S_n^T + P U per chunk (Qbar = scale qn e^Gamma,
+ * P = scale (Qn Kn^T o decay) on and below the diagonal, U = v_new), the chunked
+ * form of o_t = scale S_t qn_t (FlashQLA GDN overview, section 3).  o: [B,T,H,Dv]
+ * in the input dtype, 16-byte aligned, required (GDR_EINVAL if NULL); ht as for
+ * gdr_fwd_recompute.  Leaves the same workspace, so gdr_bwd may follow. */
+gdr_status gdr_fwd(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes, void* o, float* ht,
+                   void* stream);
 
 /* Backward, after gdr_fwd_recompute on the same shape, inputs and workspace:
  * reverse-chunk state-gradient recursion (dh0), chunk-parallel gradients, and

@@ -165,6 +165,28 @@ def test_bwd_rejects(case):
         assert e.value.status == B.GDR_EINVAL
 
 
+@pytest.mark.parametrize("case", ["null_o", "misaligned_o", "misaligned_ht", "null_q", "small_workspace"])
+def test_fwd_rejects(case):
+    p = _prob(gate=0)
+    need = B.gdr_workspace_bytes(p)
+    ws = _Fake(0x40000000, need)
+    t = _tensors(0)
+    o, ht = _Fake(0x30000000), None
+    if case == "null_o":
+        o = None
+    elif case == "misaligned_o":
+        o = _Fake(0x30000008)
+    elif case == "misaligned_ht":
+        ht = _Fake(0x50000004)
+    elif case == "null_q":
+        t["q"] = None
+    elif case == "small_workspace":
+        ws = _Fake(0x40000000, need - 1)
+    with pytest.raises(B.GdrError) as e:
+        B.gdr_fwd(p, t, ws, o, ht=ht, stream=0)
+    assert e.value.status == (B.GDR_EWORKSPACE if case == "small_workspace" else B.GDR_EINVAL)
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "_LIB_PATH", str(tmp_path / "missing.so"))
