@@ -14,8 +14,9 @@ the fixed order q, k, v, dO, b, g / g_raw, A_log, dt_bias, h0, dht, lengths):
 * scalar gate (GDN): the per-token log decay g = -0.1 * softplus(N(0, 1)),
   shape [B, T, H] -- this is the input distribution itself, the op takes g as
   given;
-* per-channel gate (KDA): g_raw ~ N(0, 1) [B, T, H, Dk],
-  dt_bias ~ N(0, 0.5) [H, Dk], A_log ~ U(0, 1.5) [H];
+* per-channel gate (KDA, either gate function): g_raw ~ N(0, 1) [B, T, H, Dk],
+  dt_bias ~ N(0, 0.5) [H, Dk], A_log ~ U(0, 1.5) [H]; the bounded sigmoid form
+  also takes the fixed ``gate_scale`` of the spec (default -2);
 * h0, dht ~ N(0, sigma) fp32, shape [N, H, Dv, Dk] when requested;
 * varlen lengths: ``n_seqs`` draws from U[1, max_len], rescaled so that they
   sum to exactly ``total`` (floor, at least 1, remainder to the longest).
@@ -35,6 +36,7 @@ import torch
 
 GATE_SCALAR = 0   # GDN: one log decay per token and head
 GATE_CHANNEL = 1  # KDA: one log decay per token, head and key channel
+GATE_CHANNEL_SIGMOID = 2  # KDA with the bounded sigmoid gate function
 
 _ORDER = ("q", "k", "v", "dO", "b", "g", "A_log", "dt_bias", "h0", "dht", "lengths")
 
@@ -59,6 +61,7 @@ class Spec:
     dht_std: Optional[float] = None
     seed: int = 0
     scale: Optional[float] = None
+    gate_scale: float = -2.0   # bounded sigmoid gate only: the lower bound of the log decay
 
     @property
     def eff_scale(self) -> float:
@@ -134,6 +137,7 @@ def generate(spec: Spec) -> Dict[str, object]:
     out["h0"] = None if spec.h0_std is None else _round(normal("h0", (N, H, V, K), spec.h0_std), "f32")
     out["dht"] = None if spec.dht_std is None else _round(normal("dht", (N, H, V, K), spec.dht_std), "f32")
     out["cu_seqlens"] = torch.from_numpy(cu)
+    out["gate_scale"] = spec.gate_scale if spec.gate == GATE_CHANNEL_SIGMOID else 0.0
     out.update(B=B, T=T, H=H, K=K, V=V, N=N, gate=spec.gate, scale=spec.eff_scale,
                dtype=spec.dtype, lengths=lengths, name=spec.name)
     return out
@@ -151,10 +155,12 @@ def workload(name: str) -> Spec:
         return Spec(name, GATE_SCALAR, "bf16", H=16, K=128, V=128, B=2, T=4096, h0_std=0.1, seed=1001)
     if name == "kda_bf16_t8192_h16_d128":
         return Spec(name, GATE_CHANNEL, "bf16", H=16, K=128, V=128, B=1, T=8192, seed=1002)
+    if name == "kdas_bf16_t8192_h16_d128":   # the bounded sigmoid gate on the same inputs
+        return Spec(name, GATE_CHANNEL_SIGMOID, "bf16", H=16, K=128, V=128, B=1, T=8192, seed=1002)
     if name == "gdn_varlen12_bf16_t32768_h32_d128":
         return Spec(name, GATE_SCALAR, "bf16", H=32, K=128, V=128, varlen_n=12, varlen_max=8192,
                     varlen_total=32768, h0_std=0.1, dht_std=0.1, seed=1003)
-    for gate_name, gate in (("gdn", GATE_SCALAR), ("kda", GATE_CHANNEL)):
+    for gate_name, gate in (("gdn", GATE_SCALAR), ("kda", GATE_CHANNEL), ("kdas", GATE_CHANNEL_SIGMOID)):
         for H in (16, 32):
             if name == f"{gate_name}_bf16_t32768_h{H}_d128":
                 return Spec(name, gate, "bf16", H=H, K=128, V=128, B=1, T=32768,
@@ -171,6 +177,8 @@ WORKLOADS = (
     "gdn_bf16_t32768_h32_d128",
     "kda_bf16_t32768_h16_d128",
     "kda_bf16_t32768_h32_d128",
+    "kdas_bf16_t8192_h16_d128",
+    "kdas_bf16_t32768_h16_d128",
 )
 
 HEADLINE = "gdn_bf16_t32768_h16_d128"

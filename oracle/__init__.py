@@ -41,6 +41,7 @@ class _Args(ctypes.Structure):
         ("dh0", _D), ("dA_log", _D), ("ddt_bias", _D),
         ("S_chunk", _D), ("dS_chunk", _D), ("u_out", _D), ("dqn", _D), ("dkn", _D),
         ("dbeta", _D), ("dlam", _D),
+        ("gate_scale", ctypes.c_double),
     ]
 
 
@@ -103,7 +104,7 @@ def run(inp: Dict, backward: bool = True, exports: bool = False, chunk: int = 64
     h0 = _f64(inp.get("h0"))
     dhta = _f64(inp.get("dht")) if isinstance(dht, str) and dht == "input" else _f64(dht)
     NC = int(sum((int(cu[n + 1] - cu[n]) + chunk - 1) // chunk for n in range(N)))
-    gK = (K,) if gate == 1 else ()
+    gK = (K,) if gate >= 1 else ()
 
     out: Dict[str, np.ndarray] = {}
 
@@ -115,6 +116,7 @@ def run(inp: Dict, backward: bool = True, exports: bool = False, chunk: int = 64
     a = _Args()
     a.N, a.H, a.K, a.V, a.gate, a.chunk = N, H, K, V, gate, chunk
     a.nthreads = nthreads if nthreads is not None else default_threads()
+    a.gate_scale = float(inp.get("gate_scale", 0.0))
     a.do_backward = 1 if backward else 0
     a.scale = float(inp["scale"])
     a.cu = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
@@ -131,7 +133,7 @@ def run(inp: Dict, backward: bool = True, exports: bool = False, chunk: int = 64
         a.dg = _ptr(alloc("dg", (B, T, H) + gK))
         a.db = _ptr(alloc("db", (B, T, H)))
         a.dh0 = _ptr(alloc("dh0", (N, H, V, K)))
-        if gate == 1:
+        if gate >= 1:
             a.dA_log = _ptr(alloc("dA_log", (H,)))
             a.ddt_bias = _ptr(alloc("ddt_bias", (H, K)))
     if exports:

@@ -78,7 +78,10 @@ def _prep(inp, n, h):
         A_log, dtb = _f64(inp["A_log"]), _f64(inp["dt_bias"])
         ea = np.exp(A_log[h])
         x = g + dtb[h][None, :]
-        lam = -ea * _softplus(x)
+        if int(inp["gate"]) == 1:
+            lam = -ea * _softplus(x)
+        else:   # bounded sigmoid form (FlashKDA K1 page, section 5.2), natural log
+            lam = float(inp["gate_scale"]) * _sigmoid(ea * x)
     return dict(t0=t0, t1=t1, q=q, k=k, v=v, dO=dO, qn=qn, kn=kn, rq=rq, rk=rk, beta=beta,
                 lam=lam, x=x, ea=ea)
 
@@ -143,7 +146,7 @@ def run(inp: Dict, chunk: int = 64, dht="input") -> Dict[str, np.ndarray]:
     TT = B * T
     h0 = _f64(inp.get("h0"))
     dhtv = _f64(inp.get("dht") if isinstance(dht, str) else dht)
-    gK = (K,) if gate == 1 else ()
+    gK = (K,) if gate >= 1 else ()
     o = np.zeros((TT, H, V)); dq = np.zeros((TT, H, K)); dk = np.zeros((TT, H, K))
     dv = np.zeros((TT, H, V)); dg = np.zeros((TT, H) + gK); db = np.zeros((TT, H))
     ht = np.zeros((N, H, V, K)); dh0 = np.zeros((N, H, V, K))
@@ -186,11 +189,17 @@ def run(inp: Dict, chunk: int = 64, dht="input") -> Dict[str, np.ndarray]:
             db[t0:t1, h] = dbeta * beta * (1 - beta)
             if gate == 0:
                 dg[t0:t1, h] = dlam.sum(1)
-            else:
+            elif gate == 1:
                 dgr = dlam * (-p["ea"] * _sigmoid(p["x"]))
                 dg[t0:t1, h] = dgr
                 ddt[h] += dgr.sum(0)
                 dA[h] += (dlam * p["lam"]).sum()
+            else:
+                sz = _sigmoid(p["ea"] * p["x"])
+                dz = dlam * float(inp["gate_scale"]) * sz * (1 - sz)
+                dg[t0:t1, h] = dz * p["ea"]
+                ddt[h] += (dz * p["ea"]).sum(0)
+                dA[h] += (dz * p["ea"] * p["x"]).sum()
             S_h += Ss; dS_h += dSs; A_h += [z["A"] for z in zs]
         S_chunk.append(S_h); dS_chunk.append(dS_h); A_chunk.append(A_h)
     sh = lambda x: x.reshape((B, T) + x.shape[1:])  # noqa: E731
@@ -198,6 +207,6 @@ def run(inp: Dict, chunk: int = 64, dht="input") -> Dict[str, np.ndarray]:
                S_chunk=np.array([np.stack(s) for s in S_chunk]) if S_chunk and S_chunk[0] else None,
                dS_chunk=np.array([np.stack(s) for s in dS_chunk]) if dS_chunk and dS_chunk[0] else None,
                A_chunk=A_chunk)
-    if gate == 1:
+    if gate >= 1:
         out["dA_log"], out["ddt_bias"] = dA, ddt
     return out

@@ -15,6 +15,9 @@
  *   beta = sigmoid(b)                                    (same page, §6)
  *   lambda = g                         (scalar gate, the given log decay)
  *   lambda = -exp(A_log) * softplus(g_raw + dt_bias)     (per-channel gate)
+ *   lambda = gate_scale * sigmoid(exp(A_log) * (g_raw + dt_bias))
+ *                                     (per-channel gate, bounded sigmoid form,
+ *                                      FlashKDA K1 page, section 5.2; natural log)
  *   For t = 1..T, with S a Dv x Dk matrix (S = h0 or 0 at t = 0):
  *     St  = S * Diag(exp(lambda_t))
  *     e   = St kn_t,   u = beta_t (v_t - e),   S = St + u kn_t^T
@@ -39,7 +42,8 @@
 typedef struct {
   /* shape */
   int32_t N, H, K, V;
-  int32_t gate;       /* 0: scalar log decay [T][H]; 1: per-channel gate from g_raw [T][H][K] */
+  int32_t gate;       /* 0: scalar log decay [T][H]; 1, 2: per-channel gate from g_raw [T][H][K]
+                         (1 softplus form, 2 bounded sigmoid form) */
   int32_t chunk;      /* checkpoint spacing, also the chunking of the exports */
   int32_t nthreads;   /* worker threads (<= 0: 1) */
   int32_t do_backward;
@@ -71,6 +75,7 @@ typedef struct {
   double *dqn, *dkn;       /* [T][H][K] gradients w.r.t. the normalised q, k */
   double *dbeta;           /* [T][H] gradient w.r.t. beta (after the sigmoid) */
   double *dlam;            /* [T][H] (gate 0) or [T][H][K] (gate 1) gradient w.r.t. lambda_t */
+  double gate_scale;       /* gate 2: the bound of the per-token log decay */
 } oracle_args;
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
@@ -139,10 +144,14 @@ static int run_item(pool_t* P, int n, int h) {
     beta[t] = sigmoid(a->b[row]);
     if (a->gate == 0) {
       for (int j = 0; j < K; ++j) lam[(size_t)t * K + j] = a->g[row];
-    } else {
+    } else if (a->gate == 1) {
       const double ea = exp(a->A_log[h]);
       for (int j = 0; j < K; ++j)
         lam[(size_t)t * K + j] = -ea * softplus(a->g[row * K + j] + a->dt_bias[(size_t)h * K + j]);
+    } else {
+      const double ea = exp(a->A_log[h]);
+      for (int j = 0; j < K; ++j)
+        lam[(size_t)t * K + j] = a->gate_scale * sigmoid(ea * (a->g[row * K + j] + a->dt_bias[(size_t)h * K + j]));
     }
   }
 
@@ -251,7 +260,7 @@ static int run_item(pool_t* P, int n, int h) {
 
   /* ---- epilogue ---- */
   {
-    const double ea = (a->gate == 1) ? exp(a->A_log[h]) : 0.0;
+    const double ea = (a->gate >= 1) ? exp(a->A_log[h]) : 0.0;
     double* pdA = P->part_dA + (size_t)n * H + h;
     double* pdt = P->part_ddt + ((size_t)n * H + h) * K;
     for (int t = 0; t < len; ++t) {
@@ -276,7 +285,8 @@ static int run_item(pool_t* P, int n, int h) {
         for (int j = 0; j < K; ++j) s += dlt[j];
         if (a->dg) a->dg[row] = s;
         if (a->dlam) a->dlam[row] = s;
-      } else {
+      } else if (a->gate == 1) {
+        /* d lambda / d x = -e^A_log sigmoid(x), d lambda / d A_log = lambda */
         for (int j = 0; j < K; ++j) {
           const double x = a->g[row * K + j] + a->dt_bias[(size_t)h * K + j];
           const double dgr = dlt[j] * (-ea * sigmoid(x));
@@ -284,6 +294,18 @@ static int run_item(pool_t* P, int n, int h) {
           if (a->dlam) a->dlam[row * K + j] = dlt[j];
           pdt[j] += dgr;
           *pdA += dlt[j] * lam[(size_t)t * K + j];
+        }
+      } else {
+        /* z = e^A_log x: d lambda / dz = gate_scale sigmoid(z) (1 - sigmoid(z)),
+         * dz / dx = e^A_log, dz / d A_log = e^A_log x */
+        for (int j = 0; j < K; ++j) {
+          const double x = a->g[row * K + j] + a->dt_bias[(size_t)h * K + j];
+          const double sz = sigmoid(ea * x);
+          const double dz = dlt[j] * a->gate_scale * sz * (1.0 - sz);
+          if (a->dg) a->dg[row * K + j] = dz * ea;
+          if (a->dlam) a->dlam[row * K + j] = dlt[j];
+          pdt[j] += dz * ea;
+          *pdA += dz * ea * x;
         }
       }
     }
@@ -318,7 +340,8 @@ int oracle_run(const oracle_args* a) {
   if (!a || a->N < 0 || a->H <= 0 || a->K <= 0 || a->V <= 0 || a->chunk <= 0 || !a->cu) return -1;
   if (!a->q || !a->k || !a->v || !a->b || !a->g) return -1;
   if (a->do_backward && !a->dO) return -1;
-  if (a->gate == 1 && (!a->A_log || !a->dt_bias)) return -1;
+  if (a->gate < 0 || a->gate > 2) return -1;
+  if (a->gate >= 1 && (!a->A_log || !a->dt_bias)) return -1;
   for (int n = 0; n < a->N; ++n)
     if (a->cu[n + 1] < a->cu[n]) return -1;
 
@@ -348,7 +371,7 @@ int oracle_run(const oracle_args* a) {
   free(th);
   pthread_mutex_destroy(&P.mu);
 
-  if (a->do_backward && a->gate == 1) {
+  if (a->do_backward && a->gate >= 1) {
     /* per-head parameter gradients: sum over sequences in a fixed order */
     for (int h = 0; h < a->H; ++h) {
       double s = 0.0;

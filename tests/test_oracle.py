@@ -43,11 +43,23 @@ def _loss(inp):
     return L
 
 
+def _gate_lam(inp, gate, g, h):
+    """The per-token log decay from the definitions: g itself (scalar gate);
+    -e^A_log softplus(g + dt_bias) or gate_scale sigmoid(e^A_log (g + dt_bias))
+    (per-channel gate, FlashKDA K1 page section 5.2, natural log)."""
+    if gate == 0:
+        return g
+    x = g + inp["dt_bias"][h]
+    if gate == 1:
+        return -np.exp(inp["A_log"][h]) * np.log1p(np.exp(x))
+    return inp["gate_scale"] / (1 + np.exp(-np.exp(inp["A_log"][h]) * x))
+
+
 GRAD_OF = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "b": "db", "h0": "dh0",
            "A_log": "dA_log", "dt_bias": "ddt_bias"}
 
 
-@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("gate", [0, 1, 2])
 @pytest.mark.parametrize("lengths,chunk", [([1], 4), ([5, 11], 4), ([70], 64), ([3, 0, 9], 4)])
 def test_finite_differences_all_inputs(gate, lengths, chunk):
     inp = _np_inputs(gate, lengths, K=4, V=4, seed=11 + len(lengths))
@@ -72,7 +84,7 @@ def test_finite_differences_all_inputs(gate, lengths, chunk):
         assert err < 1e-7, (name, err)
 
 
-@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("gate", [0, 1, 2])
 def test_forward_matches_literal_matrix_form(gate):
     """S_t = S_{t-1} Diag(e^lam)(I - beta kn kn^T) + beta v kn^T, o_t = scale S_t qn_t."""
     inp = _np_inputs(gate, [9, 4], H=2, K=5, V=3, seed=3)
@@ -87,17 +99,13 @@ def test_forward_matches_literal_matrix_form(gate):
                 qn = q / np.sqrt(q @ q + 1e-6)
                 kn = k / np.sqrt(k @ k + 1e-6)
                 beta = 1 / (1 + np.exp(-inp["b"][0, t, h]))
-                if gate == 0:
-                    lam = np.full(K, inp["g"][0, t, h])
-                else:
-                    x = inp["g"][0, t, h] + inp["dt_bias"][h]
-                    lam = -np.exp(inp["A_log"][h]) * np.log1p(np.exp(x))
+                lam = np.full(K, inp["g"][0, t, h]) if gate == 0 else _gate_lam(inp, gate, inp["g"][0, t, h], h)
                 S = S @ np.diag(np.exp(lam)) @ (np.eye(K) - beta * np.outer(kn, kn)) + beta * np.outer(v, kn)
                 np.testing.assert_allclose(r["o"][0, t, h], inp["scale"] * S @ qn, rtol=1e-12, atol=1e-13)
             np.testing.assert_allclose(r["ht"][n, h], S, rtol=1e-12, atol=1e-13)
 
 
-@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("gate", [0, 1, 2])
 def test_single_token_closed_form(gate):
     inp = _np_inputs(gate, [1], H=1, K=5, V=4, seed=5)
     r = oracle.run(inp)
@@ -106,11 +114,7 @@ def test_single_token_closed_form(gate):
     rq, rk = 1 / np.sqrt(q @ q + 1e-6), 1 / np.sqrt(k @ k + 1e-6)
     qn, kn = q * rq, k * rk
     beta = 1 / (1 + np.exp(-inp["b"][0, 0, 0]))
-    if gate == 0:
-        lam = np.full(5, inp["g"][0, 0, 0])
-    else:
-        x = inp["g"][0, 0, 0] + inp["dt_bias"][0]
-        lam = -np.exp(inp["A_log"][0]) * np.log1p(np.exp(x))
+    lam = np.full(5, inp["g"][0, 0, 0]) if gate == 0 else _gate_lam(inp, gate, inp["g"][0, 0, 0], 0)
     D = np.diag(np.exp(lam))
     S1 = h0 @ D @ (np.eye(5) - beta * np.outer(kn, kn)) + beta * np.outer(v, kn)
     G = sc * np.outer(dO, qn) + dht                      # dL/dS_1
@@ -129,14 +133,23 @@ def test_single_token_closed_form(gate):
     np.testing.assert_allclose(r["db"][0, 0, 0], dbeta * beta * (1 - beta), rtol=1e-10, atol=1e-14)
     if gate == 0:
         np.testing.assert_allclose(r["dg"][0, 0, 0], dlam.sum(), rtol=1e-10, atol=1e-14)
-    else:
+    elif gate == 1:
         x = inp["g"][0, 0, 0] + inp["dt_bias"][0]
         sig = 1 / (1 + np.exp(-x))
         np.testing.assert_allclose(r["dg"][0, 0, 0], dlam * (-np.exp(inp["A_log"][0]) * sig), rtol=1e-10, atol=1e-14)
         np.testing.assert_allclose(r["dA_log"][0], (dlam * lam).sum(), rtol=1e-10, atol=1e-14)
+    else:
+        # lam = c sigma(z), z = a x, a = e^A_log: dlam/dx = c sigma(z)(1 - sigma(z)) a,
+        # dlam/dA_log = c sigma(z)(1 - sigma(z)) a x
+        a, x, c = np.exp(inp["A_log"][0]), inp["g"][0, 0, 0] + inp["dt_bias"][0], inp["gate_scale"]
+        sz = 1 / (1 + np.exp(-a * x))
+        dz = dlam * c * sz * (1 - sz)
+        np.testing.assert_allclose(r["dg"][0, 0, 0], dz * a, rtol=1e-10, atol=1e-14)
+        np.testing.assert_allclose(r["ddt_bias"][0], dz * a, rtol=1e-10, atol=1e-14)
+        np.testing.assert_allclose(r["dA_log"][0], (dz * a * x).sum(), rtol=1e-10, atol=1e-14)
 
 
-@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("gate", [0, 1, 2])
 def test_beta_zero_reduces_to_gated_linear_attention(gate):
     """beta = 0 (logit -inf): no writes; readout, dq, dlam, dh0 and dbeta in closed form."""
     inp = _np_inputs(gate, [13], H=1, K=4, V=3, seed=9)
@@ -151,7 +164,7 @@ def test_beta_zero_reduces_to_gated_linear_attention(gate):
     if gate == 0:
         lam = np.repeat(inp["g"][0, :, 0][:, None], 4, axis=1)
     else:
-        lam = -np.exp(inp["A_log"][0]) * np.log1p(np.exp(inp["g"][0, :, 0] + inp["dt_bias"][0]))
+        lam = _gate_lam(inp, gate, inp["g"][0, :, 0], 0)
     Lam = np.cumsum(lam, axis=0)                          # global cumsum
     o = sc * np.einsum("ij,tj,tj->ti", h0, np.exp(Lam), qn)
     np.testing.assert_allclose(r["o"][0, :, 0], o, rtol=1e-12, atol=1e-14)
@@ -180,7 +193,7 @@ def test_beta_zero_reduces_to_gated_linear_attention(gate):
     np.testing.assert_allclose(r["dbeta"][0, :, 0], dbeta, rtol=1e-10, atol=1e-13)
 
 
-@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("gate", [0, 1, 2])
 @pytest.mark.parametrize("chunk", [4, 16, 64])
 def test_chunked_algorithm_matches_recurrence(gate, chunk):
     inp = _np_inputs(gate, [70, 1, 33, 0, 64], H=2, K=8, V=6, seed=21)
@@ -204,7 +217,7 @@ def test_reverse_cumsum_worked_example():
     np.testing.assert_array_equal(got2, np.array(ex["expected_suffix_sums"]) + 1.5)
 
 
-@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("gate", [0, 1, 2])
 def test_l2_gradient_orthogonal_and_scale_invariant(gate):
     inp = _np_inputs(gate, [20], H=2, K=8, V=8, seed=4)
     r = oracle.run(inp)
@@ -220,7 +233,7 @@ def test_l2_gradient_orthogonal_and_scale_invariant(gate):
     assert np.abs(r2["dq"] * 3.0 - r["dq"]).max() <= 1e-6 * np.abs(r["dq"]).max()
 
 
-@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("gate", [0, 1, 2])
 def test_gradients_linear_in_upstream(gate):
     inp = _np_inputs(gate, [17, 6], H=2, K=4, V=5, seed=8)
     rng = np.random.default_rng(0)
@@ -233,12 +246,13 @@ def test_gradients_linear_in_upstream(gate):
         np.testing.assert_allclose(c[key], 2.0 * a[key] - b[key], rtol=1e-9, atol=1e-11)
 
 
-def test_channel_constant_gate_equals_scalar_gate():
-    kda = _np_inputs(1, [19, 7], H=2, K=6, V=5, seed=12)
+@pytest.mark.parametrize("gate", [1, 2])
+def test_channel_constant_gate_equals_scalar_gate(gate):
+    kda = _np_inputs(gate, [19, 7], H=2, K=6, V=5, seed=12)
     # constant across channels: g_raw[t,h,:] = c_th, dt_bias[h,:] = d_h
     kda["g"] = np.repeat(kda["g"][..., :1], 6, axis=-1)
     kda["dt_bias"] = np.repeat(kda["dt_bias"][:, :1], 6, axis=-1)
-    lam = -np.exp(kda["A_log"])[None, None, :] * np.log1p(np.exp(kda["g"][..., 0] + kda["dt_bias"][None, None, :, 0]))
+    lam = np.stack([_gate_lam(kda, gate, kda["g"][:, :, h, :], h)[..., 0] for h in range(2)], axis=-1)
     gdn = dict(kda)
     gdn["gate"] = 0
     gdn["g"] = lam
@@ -250,7 +264,7 @@ def test_channel_constant_gate_equals_scalar_gate():
     np.testing.assert_allclose(a["dlam"].sum(-1), b["dg"], rtol=1e-10, atol=1e-12)
 
 
-@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("gate", [0, 1, 2])
 def test_varlen_pack_equals_separate_runs(gate):
     lengths = [9, 0, 21, 1]
     inp = _np_inputs(gate, lengths, H=2, K=4, V=4, seed=13)
@@ -279,6 +293,22 @@ def test_varlen_pack_equals_separate_runs(gate):
     if gate:
         np.testing.assert_allclose(packed["dA_log"], dA, rtol=1e-12)
         np.testing.assert_allclose(packed["ddt_bias"], ddt, rtol=1e-12)
+
+
+def test_sigmoid_gate_with_zero_scale_has_no_decay():
+    """gate_scale = 0: lambda = 0 for every token, the scalar gate with g = 0; the
+    parameter gradients vanish."""
+    kda = _np_inputs(2, [15, 6], H=2, K=4, V=4, seed=17)
+    kda["gate_scale"] = 0.0
+    gdn = dict(kda)
+    gdn["gate"] = 0
+    gdn["g"] = np.zeros(kda["g"].shape[:3])
+    gdn["A_log"] = gdn["dt_bias"] = None
+    a = oracle.run(kda)
+    b = oracle.run(gdn)
+    for key in ("o", "ht", "dq", "dk", "dv", "db", "dh0"):
+        np.testing.assert_allclose(a[key], b[key], rtol=1e-13, atol=1e-15)
+    assert np.all(a["dg"] == 0) and np.all(a["dA_log"] == 0) and np.all(a["ddt_bias"] == 0)
 
 
 def test_oracle_rejects_bad_arguments():
