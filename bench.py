@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 from chunked_gated_delta_bwd_amd import binding as B  # noqa: E402
 from chunked_gated_delta_bwd_amd import synth  # noqa: E402
 
+GATE_NAMES = {0: "scalar", 1: "channel", 2: "channel_sigmoid"}
 METRIC = "gated-delta-rule bwd tokens/s + ms/bwd at T=32k,H=16,D=128 bf16; MFMA %"
 CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 # HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by a
@@ -69,7 +70,7 @@ def algorithmic_work(inp, stage: str):
     NC = sum((L + C - 1) // C for L in inp["lengths"])
     tokens = inp["B"] * inp["T"]
     ch = NC * H
-    gk = D if inp["gate"] == 1 else 1
+    gk = D if inp["gate"] != 0 else 1
     io = 2 if inp["dtype"] == "bf16" else 4
     f_prep = 4 * C * C * D + C ** 3 // 3
     f_fwd = 4 * C * D * D
@@ -109,7 +110,7 @@ def algorithmic_work(inp, stage: str):
     if stage == "finish":
         # read q, k, dqn, dkn, rho, dGamma, dbeta, b (and g_raw for KDA); write dq, dk, dg, db
         b = tokens * H * (2 * D * io + 2 * D * 4 + 8 + gk * 4 + 4 + io + 2 * D * io + gk * io + io)
-        if inp["gate"] == 1:
+        if inp["gate"] != 0:
             b += tokens * H * D * io
         return 0, b
     raise KeyError(stage)
@@ -243,9 +244,9 @@ def main() -> int:
     # every kernel alone (the workspace already holds what earlier stages leave)
     kernels = {}
     # the scalar gate's prepare-backward runs inside its gradient kernel
-    path = ("prep", "chain_both", "grads") + (("finish",) if inp["gate"] == 1 else ())
+    path = ("prep", "chain_both", "grads") + (("finish",) if inp["gate"] != 0 else ())
     stages = [B.GDR_STAGE_PREP, B.GDR_STAGE_CHAIN_BOTH, B.GDR_STAGE_GRADS]
-    if inp["gate"] == 1:
+    if inp["gate"] != 0:
         stages.append(B.GDR_STAGE_FINISH)
     if args.all_stages:
         stages += [B.GDR_STAGE_CHAIN_FWD, B.GDR_STAGE_CHAIN_BWD]
@@ -271,7 +272,7 @@ def main() -> int:
         "dtype": "bf16" if inp["dtype"] == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": inp["B"], "T": inp["T"], "H": H, "D": K,
-                   "gate": "scalar" if inp["gate"] == 0 else "channel", "chunk": C},
+                   "gate": GATE_NAMES[inp["gate"]], "chunk": C},
         "roofline": roof,
         "kernels": kernels,
     }
@@ -321,7 +322,7 @@ def bench_forward(args, inp, dev, prob, ws, out, ht) -> int:
         "dtype": "bf16" if inp["dtype"] == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "path": "fwd", "B": inp["B"], "T": inp["T"], "H": inp["H"],
-                   "D": inp["K"], "gate": "scalar" if inp["gate"] == 0 else "channel", "chunk": C},
+                   "D": inp["K"], "gate": GATE_NAMES[inp["gate"]], "chunk": C},
         "roofline": roofline(inp, args.workload, dom, kernels[dom]["ms"]),
         "kernels": kernels,
     }

@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so"
 _lib = None
 
 GDR_OK, GDR_EINVAL, GDR_EUNSUPPORTED, GDR_EWORKSPACE, GDR_EHIP = 0, 1, 2, 3, 4
-GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
+GDR_GATE_SCALAR, GDR_GATE_CHANNEL, GDR_GATE_CHANNEL_SIGMOID = 0, 1, 2
 GDR_BF16, GDR_F32 = 0, 1
 GDR_WS_STATE, GDR_WS_DSTATE, GDR_WS_U, GDR_WS_A, GDR_WS_GAMMA = 0, 1, 2, 3, 4
 
@@ -41,7 +41,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int64)),
-                ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("gate_scale", ctypes.c_float)]
 
 
 class Inputs(ctypes.Structure):
@@ -113,14 +114,14 @@ class Problem:
     """
 
     def __init__(self, B: int, T: int, H: int, D: int, N: int, gate: int, dtype: int, scale: float,
-                 cu_seqlens=None):
+                 cu_seqlens=None, gate_scale: float = 0.0):
         self.cu = None
         if cu_seqlens is not None:
             cu = torch.as_tensor(cu_seqlens, dtype=torch.int64).contiguous().cpu()
             self.cu = cu
         self.shape = Shape(B, T, H, D, D, N,
                            None if self.cu is None else ctypes.cast(self.cu.data_ptr(), ctypes.POINTER(ctypes.c_int64)),
-                           gate, dtype, scale)
+                           gate, dtype, scale, gate_scale)
 
     @staticmethod
     def from_inputs(inp: Dict, varlen: Optional[bool] = None) -> "Problem":
@@ -128,10 +129,12 @@ class Problem:
         if varlen is None:
             varlen = inp["B"] == 1 and (len(lengths) > 1 or lengths[0] != inp["T"])
         dtype = GDR_BF16 if inp["dtype"] == "bf16" else GDR_F32
+        gs = float(inp.get("gate_scale", 0.0))
         if varlen:
             return Problem(1, inp["T"], inp["H"], inp["K"], inp["N"], inp["gate"], dtype, inp["scale"],
-                           cu_seqlens=inp["cu_seqlens"])
-        return Problem(inp["B"], inp["T"], inp["H"], inp["K"], inp["N"], inp["gate"], dtype, inp["scale"])
+                           cu_seqlens=inp["cu_seqlens"], gate_scale=gs)
+        return Problem(inp["B"], inp["T"], inp["H"], inp["K"], inp["N"], inp["gate"], dtype, inp["scale"],
+                       gate_scale=gs)
 
 
 def gdr_workspace_bytes(prob: Problem) -> int:
@@ -213,7 +216,7 @@ def alloc_outputs(inp: Dict, dev: Dict, want_dh0: bool = True) -> Dict:
            "dg": torch.empty_like(g), "db": torch.empty_like(dev["b"])}
     N, H, K, V = inp["N"], inp["H"], inp["K"], inp["V"]
     out["dh0"] = torch.empty((N, H, V, K), dtype=torch.float32, device=q.device) if want_dh0 else None
-    if inp["gate"] == GDR_GATE_CHANNEL:
+    if inp["gate"] != GDR_GATE_SCALAR:
         out["dA_log"] = torch.empty((H,), dtype=torch.float32, device=q.device)
         out["ddt_bias"] = torch.empty((H, K), dtype=torch.float32, device=q.device)
     return out

@@ -34,8 +34,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Validates the shape and computes the chunk count.
 gdr_status check_shape(const gdr_shape* s, int64_t* NC_out) {
   if (!s) return fail(GDR_EINVAL, "shape is NULL");
-  if (s->gate != GDR_GATE_SCALAR && s->gate != GDR_GATE_CHANNEL)
+  if (s->gate != GDR_GATE_SCALAR && s->gate != GDR_GATE_CHANNEL && s->gate != GDR_GATE_CHANNEL_SIGMOID)
     return fail(GDR_EINVAL, "unknown gate %d", s->gate);
+  if (s->gate == GDR_GATE_CHANNEL_SIGMOID && !(s->gate_scale <= 0.f && s->gate_scale > -1e30f))
+    return fail(GDR_EINVAL, "gate_scale %g must be finite and <= 0 (a log decay)", double(s->gate_scale));
   if (s->dtype != GDR_BF16 && s->dtype != GDR_F32) return fail(GDR_EINVAL, "unknown dtype %d", s->dtype);
   if (s->Dk != s->Dv) return fail(GDR_EUNSUPPORTED, "Dk (%d) != Dv (%d)", s->Dk, s->Dv);
   if (s->Dk != 64 && s->Dk != 128) return fail(GDR_EUNSUPPORTED, "head dim %d not in {64, 128}", s->Dk);
@@ -67,7 +69,7 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   gdr::WsLayout L;
   L.NC = NC;
   const size_t H = s->H, K = s->Dk, V = s->Dv, C = gdr::kChunk, N = s->N;
-  const size_t gk = s->gate == GDR_GATE_CHANNEL ? K : 1;
+  const size_t gk = s->gate != GDR_GATE_SCALAR ? K : 1;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   L.ctab = take(NC * sizeof(gdr::ChunkEntry));
@@ -78,7 +80,7 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.edec = take(H * NC * (gk == 1 ? 4 : gk) * 4);
   // materialised Khat / Qbar / W tiles: the per-channel gate and fp32 inputs (the
   // scalar gate with bf16 inputs works from the raw rows, row factors and A)
-  const size_t mat = (s->gate == GDR_GATE_CHANNEL || s->dtype == GDR_F32) ? 1 : 0;
+  const size_t mat = (s->gate != GDR_GATE_SCALAR || s->dtype == GDR_F32) ? 1 : 0;
   L.A = take(H * NC * C * C * 2);
   L.P = take(H * NC * C * C * 2);
   L.W = take(mat * H * NC * C * K * 2);
@@ -88,7 +90,7 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.dS = take(H * NC * V * K * 2);
   L.dU = take(H * NC * C * V * 2);
   // handed from the gradient kernel to the prepare-backward (per-channel gate only)
-  const size_t sep = s->gate == GDR_GATE_CHANNEL ? 1 : 0;
+  const size_t sep = s->gate != GDR_GATE_SCALAR ? 1 : 0;
   L.dqn = take(sep * H * NC * C * K * 4);
   L.dkn = take(sep * H * NC * C * K * 4);
   L.dgam = take(sep * H * NC * C * gk * 4);
@@ -97,7 +99,7 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.Kh = take(mat * H * NC * C * K * 2);
   L.Qh = take(mat * H * NC * C * K * 2);
   L.Ql = take(mat * H * NC * C * K * 2);
-  const size_t kda = s->gate == GDR_GATE_CHANNEL ? 1 : 0;
+  const size_t kda = s->gate != GDR_GATE_SCALAR ? 1 : 0;
   L.Mk = take(kda * H * NC * C * C * 2);
   L.pdA = take(kda * H * NC * 4);
   L.pddt = take(kda * H * NC * K * 4);
@@ -118,7 +120,7 @@ gdr_status check_inputs(const gdr_shape* s, const gdr_inputs* in) {
     if (!aligned16(req[i])) return fail(GDR_EINVAL, "input %s is not 16-byte aligned", names[i]);
   }
   if (in->h0 && !aligned16(in->h0)) return fail(GDR_EINVAL, "h0 is not 16-byte aligned");
-  if (s->gate == GDR_GATE_CHANNEL) {
+  if (s->gate != GDR_GATE_SCALAR) {
     if (!in->A_log || !in->dt_bias) return fail(GDR_EINVAL, "per-channel gate needs A_log and dt_bias");
     if (!aligned16(in->A_log) || !aligned16(in->dt_bias))
       return fail(GDR_EINVAL, "A_log/dt_bias not 16-byte aligned");
@@ -140,7 +142,7 @@ gdr_status check_grads(const gdr_shape* s, const void* dO, const float* dht, con
     if (!aligned16(req[i])) return fail(GDR_EINVAL, "output %s is not 16-byte aligned", names[i]);
   }
   if (gr->dh0 && !aligned16(gr->dh0)) return fail(GDR_EINVAL, "dh0 is not 16-byte aligned");
-  if (s->gate == GDR_GATE_CHANNEL) {
+  if (s->gate != GDR_GATE_SCALAR) {
     if (!gr->dA_log || !gr->ddt_bias) return fail(GDR_EINVAL, "per-channel gate needs dA_log and ddt_bias outputs");
     if (!aligned16(gr->dA_log) || !aligned16(gr->ddt_bias))
       return fail(GDR_EINVAL, "dA_log/ddt_bias not 16-byte aligned");
@@ -189,7 +191,12 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   gdr::Params p;
   std::memset(&p, 0, sizeof(p));
   p.H = s->H; p.K = s->Dk; p.V = s->Dv; p.N = s->N; p.NC = int32_t(L.NC); p.T = s->B * s->T;
-  p.gate = s->gate; p.dtype = s->dtype; p.scale = s->scale;
+  // the kernels tell the scalar gate from the per-channel one; the per-channel
+  // gate function (softplus or bounded sigmoid) matters only where it is applied
+  p.gate = s->gate == GDR_GATE_SCALAR ? 0 : 1;
+  p.gate_fn = s->gate == GDR_GATE_CHANNEL_SIGMOID ? 1 : 0;
+  p.gate_scale = s->gate_scale;
+  p.dtype = s->dtype; p.scale = s->scale;
   p.q = in->q; p.k = in->k; p.v = in->v; p.g = in->g; p.b = in->beta_logit;
   p.A_log = in->A_log; p.dt_bias = in->dt_bias; p.h0 = in->h0;
   char* w = static_cast<char*>(ws);
@@ -259,7 +266,7 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
   p.o = o;
   if (stage != kFwd) set_grads(p, dO, dht, gr);
 
-  const bool kda = s->gate == GDR_GATE_CHANNEL;
+  const bool kda = s->gate != GDR_GATE_SCALAR;
   auto prep = [&]() { return kda ? gdr::launch_kda(p, 0, stream) : gdr::launch_prep(p, stream); };
   auto grads = [&]() { return kda ? gdr::launch_kda(p, 1, stream) : gdr::launch_grads(p, stream); };
   // the scalar gate's prepare-backward is fused into its gradient kernel
@@ -348,7 +355,7 @@ gdr_status gdr_workspace_region(const gdr_shape* shape, int32_t which, size_t* o
   if (!offset || !bytes) return fail(GDR_EINVAL, "offset/bytes is NULL");
   const gdr::WsLayout L = layout(shape, NC);
   const size_t H = shape->H, K = shape->Dk, V = shape->Dv, C = gdr::kChunk;
-  const size_t gk = shape->gate == GDR_GATE_CHANNEL ? K : 1;
+  const size_t gk = shape->gate != GDR_GATE_SCALAR ? K : 1;
   switch (which) {
     case GDR_WS_STATE: *offset = L.S; *bytes = H * NC * V * K * 2; break;
     case GDR_WS_DSTATE: *offset = L.dS; *bytes = H * NC * V * K * 2; break;

@@ -75,8 +75,10 @@ struct WsLayout {
 
 struct Params {
   int32_t H, K, V, N, NC, T;     // T = total tokens
-  int32_t gate, dtype;
+  int32_t gate, dtype;            // gate: 0 scalar, 1 per-channel (either gate function)
   float scale;
+  int32_t gate_fn;                // per-channel: 0 -e^A_log softplus(x), 1 gate_scale sigmoid(e^A_log x)
+  float gate_scale;
   // inputs
   const void *q, *k, *v, *g, *b, *dO;
   const float *A_log, *dt_bias, *h0, *dht;

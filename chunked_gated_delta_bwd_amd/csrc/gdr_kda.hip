@@ -1,7 +1,8 @@
 // HIP kernels for gfx950: the chunk-parallel parts of the per-channel (KDA) gate.
 //
-// The gate is lambda = -exp(A_log) softplus(g_raw + dt_bias), one value per token,
-// head and key channel (FlashKDA backward (K1) page, section 5).  Its in-chunk
+// The gate is lambda = -exp(A_log) softplus(g_raw + dt_bias), or in the bounded
+// form lambda = gate_scale sigmoid(exp(A_log) (g_raw + dt_bias)), one value per
+// token, head and key channel (FlashKDA backward (K1) page, section 5).  Its in-chunk
 // cumsum Gamma is per channel, so the decay between rows r and s of a chunk is
 // the per-channel factor E_rsc = exp(Gamma_rc - Gamma_sc) inside every
 // contraction over channels:
@@ -30,6 +31,13 @@
 #include "gdr_internal.h"
 
 namespace gdr {
+
+// The per-channel gate function of x = g_raw + dt_bias, with ea = e^A_log:
+//   softplus form         lambda = -ea softplus(x)
+//   bounded sigmoid form  lambda = gate_scale sigmoid(ea x)
+__device__ __forceinline__ float gate_lambda(const Params& p, float ea, float x) {
+  return p.gate_fn ? p.gate_scale * sigmoidf(ea * x) : -ea * softplusf(x);
+}
 
 namespace {
 
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   if (tid >= kThreads - C) braw = IO<TIO>::load1(p.b, tok(t0 + min(tid - (kThreads - C), len - 1), H, h));
 
   // --- L2 norms; qn, kn to LDS; kn, qn, v kept in registers; the log decay
-  // lambda = -e^A_log softplus(g + dt_bias) (0 past the end) to Gs ---
+  // lambda = gate_lambda(g + dt_bias) (0 past the end) to Gs ---
   float kn_r[NPASS][8], qn_r[NPASS][8], v_r[NPASS][8];
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
@@ -137,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
       v_r[ps][e] *= m;
       sq += qv[e] * qv[e];
       sk += kv[e] * kv[e];
-      gv[e] = m * (-ea * softplusf(gv[e] + (e < 4 ? el(bias0, e) : el(bias1, e - 4))));
+      gv[e] = m * gate_lambda(p, ea, gv[e] + (e < 4 ? el(bias0, e) : el(bias1, e - 4)));
     }
     *reinterpret_cast<float4*>(Gs + r * PG + c0) = make_float4(gv[0], gv[1], gv[2], gv[3]);
     *reinterpret_cast<float4*>(Gs + r * PG + c0 + 4) = make_float4(gv[4], gv[5], gv[6], gv[7]);
@@ -1071,8 +1079,9 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
   __syncthreads();
 
   // ---- per channel: dlam_r = sum_{r' >= r} dGamma_r' + dGamma_C (FlashKDA
-  // backward page, section 5), then through lambda = -e^A softplus(x):
-  // dx = dlam (-e^A sigmoid(x)).  Thread = (channel, one of NPART row ranges):
+  // backward page, section 5), then through the gate function: softplus form
+  // dx = dlam (-e^A sigmoid(x)), d/dA_log: dlam lambda; bounded sigmoid form
+  // (z = e^A x) dx = dlam gate_scale sigma(z) (1 - sigma(z)) e^A, d/dA_log: dx x.  Thread = (channel, one of NPART row ranges):
   // a suffix scan of its range in registers plus the totals of the ranges after it ----
   const int cc = tid % D, part = tid / D;
   float x[RP];
@@ -1091,10 +1100,17 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
     if (r < len) {
       const float acc = x[i] + after;
       const float xg = X_s[r * PG + cc];
-      const float dx = acc * (-ea * sigmoidf(xg));
+      float dx;
+      if (p.gate_fn) {
+        const float sz = sigmoidf(ea * xg);
+        dx = acc * p.gate_scale * sz * (1.f - sz) * ea;
+        pa += dx * xg;
+      } else {
+        dx = acc * (-ea * sigmoidf(xg));
+        pa += acc * (-ea * softplusf(xg));
+      }
       IO<TIO>::store1(p.dg, tok(t0 + r, H, h) * D + cc, dx);
       pd += dx;
-      pa += acc * (-ea * softplusf(xg));
     }
   }
   pd_s[part][cc] = pd;

@@ -5,6 +5,9 @@
  *   qn = q / sqrt(|q|^2 + 1e-6), kn likewise, beta = sigmoid(b),
  *   lambda_t = g_t                                   (GDR_GATE_SCALAR, GDN)
  *   lambda_t = -exp(A_log[h]) * softplus(g_t + dt_bias[h])  (GDR_GATE_CHANNEL, KDA)
+ *   lambda_t = gate_scale * sigmoid(exp(A_log[h]) * (g_t + dt_bias[h]))
+ *                                        (GDR_GATE_CHANNEL_SIGMOID, the bounded KDA
+ *                                         gate of the FlashKDA K1 page, section 5.2)
  *   S_t = S_{t-1} Diag(exp(lambda_t)) (I - beta_t kn_t kn_t^T) + beta_t v_t kn_t^T,
  *   o_t = scale * S_t qn_t,  S_0 = h0 (or 0).
  * The backward returns the gradients of L = sum_t <dO_t, o_t> + <dht, S_T> with
@@ -53,7 +56,7 @@ typedef enum {
   GDR_EHIP = 4           /* a HIP runtime call failed while enqueueing */
 } gdr_status;
 
-typedef enum { GDR_GATE_SCALAR = 0, GDR_GATE_CHANNEL = 1 } gdr_gate;
+typedef enum { GDR_GATE_SCALAR = 0, GDR_GATE_CHANNEL = 1, GDR_GATE_CHANNEL_SIGMOID = 2 } gdr_gate;
 typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
 
 typedef struct {
@@ -64,8 +67,14 @@ typedef struct {
   int32_t gate;                     /* gdr_gate */
   int32_t dtype;                    /* gdr_dtype of q, k, v, g, b, dO and of dq, dk, dv, dg, dbeta */
   float scale;                      /* readout scale (usually 1/sqrt(Dk)) */
+  float gate_scale;                 /* GDR_GATE_CHANNEL_SIGMOID: the bound of the per-token log decay,
+                                       finite and <= 0 (natural log: the pages' log2-unit bound times
+                                       ln 2); ignored otherwise */
 } gdr_shape;
 
+/* Below, CHANNEL stands for either per-channel gate (GDR_GATE_CHANNEL or
+ * GDR_GATE_CHANNEL_SIGMOID): both take the raw gate g, A_log and dt_bias and return
+ * dg, dA_log and ddt_bias in the same shapes. */
 typedef struct {                    /* device pointers */
   const void *q, *k;                /* [B,T,H,Dk] dtype */
   const void *v;                    /* [B,T,H,Dv] dtype */

@@ -49,6 +49,11 @@ def test_workspace_bytes_scales_with_chunks():
     assert v4 > v3
 
 
+def test_sigmoid_gate_uses_the_per_channel_workspace():
+    sig = B.gdr_workspace_bytes(_prob(gate=2, gate_scale=-1.0, D=128))
+    assert sig == B.gdr_workspace_bytes(_prob(gate=1, D=128))
+
+
 def test_workspace_regions_are_disjoint_and_inside():
     p = _prob(T=200, D=128, gate=1)
     total = B.gdr_workspace_bytes(p)
@@ -70,6 +75,9 @@ def test_workspace_regions_are_disjoint_and_inside():
     (dict(N=2, cu_seqlens=[0, 100, 90]), B.GDR_EINVAL),        # decreasing
     (dict(N=2, cu_seqlens=[0, 50, 100]), B.GDR_EINVAL),        # last != T (128)
     (dict(N=1, cu_seqlens=[5, 128]), B.GDR_EINVAL),            # first != 0
+    (dict(gate=2, gate_scale=0.5), B.GDR_EINVAL),               # the bound of a log decay is <= 0
+    (dict(gate=2, gate_scale=float("nan")), B.GDR_EINVAL),
+    (dict(gate=2, gate_scale=float("-inf")), B.GDR_EINVAL),
 ])
 def test_shape_validation(kw, status):
     with pytest.raises(B.GdrError) as e:

@@ -49,6 +49,8 @@ SMALL = [
      synth.Spec("fk", 1, "bf16", H=3, K=128, V=128, lengths=[1, 63, 64, 65, 0, 200], h0_std=0.1, seed=54)),
     ("kda_f32_b2_t100_d128", synth.Spec("fl", 1, "f32", H=2, K=128, V=128, B=2, T=100, h0_std=0.2, seed=55)),
     ("kda_bf16_b1_t300_d64", synth.Spec("fm", 1, "bf16", H=4, K=64, V=64, B=1, T=300, seed=56)),
+    ("kdas_bf16_varlen_edges_d128",
+     synth.Spec("fs", 2, "bf16", H=3, K=128, V=128, lengths=[1, 63, 64, 65, 0, 200], h0_std=0.1, seed=58)),
 ]
 
 

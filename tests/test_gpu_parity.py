@@ -5,6 +5,7 @@ ddt_bias (fp32).  Small problems are compared in full; full-size workloads are
 compared on sampled heads (heads are independent, so the oracle runs the exact
 same computation for them)."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -162,3 +163,52 @@ def test_kda_workload_t32768_sampled_heads(H):
     inp = synth.generate(synth.workload(f"kda_bf16_t32768_h{H}_d128"))
     got = gpu_run(inp)
     _check(inp, got, f"kda_t32768_h{H}", heads=[0, H - 1])
+
+
+# ---------------------------------------------------------------------------
+# per-channel gate, bounded sigmoid form: lambda = gate_scale sigma(e^A_log (g + dt_bias))
+# ---------------------------------------------------------------------------
+# dA_log = sum over tokens and channels of dg * (g + dt_bias): for this gate form
+# the terms cancel 60-850x on the synthetic recipe (softplus form: 30-50x), so the
+# per-term error of the bf16 pipeline (dg within 1e-3) is amplified by that much;
+# dA_log is held to 2e-2 here and, separately, checked to be exactly the reduction
+# of the kernel's own fp32 dg (which pins the reduction, not the precision).
+TOL_KDAS_DA_LOG = 2e-2
+
+
+def _check_kdas(inp, got, label):
+    ref = oracle.run(inp)
+    compare(got, ref, TOKEN_GRADS, TOL_BF16, label + " grads")
+    compare(got, ref, ("dh0", "ddt_bias"), TOL_FP32, label + " fp32")
+    compare(got, ref, ("dA_log",), TOL_KDAS_DA_LOG, label + " dA_log")
+    compare(got, ref, ("ht",), TOL_FP32 * 5, label + " ht")
+    if inp["dtype"] == "f32":
+        x = inp["g"].double().numpy() + inp["dt_bias"].double().numpy()[None, None]
+        own = np.einsum("bthk,bthk->h", got["dg"], x)
+        scale = np.einsum("bthk,bthk->h", np.abs(got["dg"]), np.abs(x))
+        assert np.all(np.abs(own - got["dA_log"]) <= 1e-5 * scale), (label, own, got["dA_log"])
+
+
+SMALL_KDAS = [
+    ("kdas_f32_t128_h2_d64", synth.Spec("sf", 2, "f32", H=2, K=64, V=64, B=1, T=128, seed=61)),
+    ("kdas_bf16_varlen_edges_d128",
+     synth.Spec("se", 2, "bf16", H=3, K=128, V=128, lengths=[1, 63, 64, 65, 0, 200], h0_std=0.1,
+                dht_std=0.1, seed=62)),
+    ("kdas_f32_b1_t300_d64_gs05", synth.Spec("sh", 2, "f32", H=4, K=64, V=64, B=1, T=300, h0_std=0.5,
+                                             dht_std=0.5, seed=63, gate_scale=-0.5)),
+]
+
+
+@pytest.mark.parametrize("name,spec", SMALL_KDAS, ids=[s[0] for s in SMALL_KDAS])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_kdas_small_against_oracle(name, spec, mode):
+    log(f"case {name} mode {mode}")
+    inp = synth.generate(spec)
+    got = gpu_run(inp, mode=mode)
+    _check_kdas(inp, got, f"{name}/{mode}")
+
+
+def test_kdas_workload_t8192_h16():
+    inp = synth.generate(synth.workload("kdas_bf16_t8192_h16_d128"))
+    got = gpu_run(inp)
+    _check_kdas(inp, got, "kdas_bf16_t8192_h16_d128")
