@@ -9,7 +9,8 @@ path and the oracle consume the exact tensors returned by :func:`generate`.
 Recipe (one ``numpy.random.PCG64`` stream per tensor, spawned from one seed in
 the fixed order q, k, v, dO, b, g / g_raw, A_log, dt_bias, h0, dht, lengths):
 
-* q, k, v, dO ~ N(0, 1), shape [B, T, H, D] (raw, not normalised);
+* q, k, v, dO ~ N(0, 1), shape [B, T, H, D] (raw, not normalised); with grouped
+  heads q and k have ``Hk`` heads, each shared by H / Hk value heads;
 * b (beta logit) ~ N(0, 1), shape [B, T, H];
 * scalar gate (GDN): the per-token log decay g = -0.1 * softplus(N(0, 1)),
   shape [B, T, H] -- this is the input distribution itself, the op takes g as
@@ -62,6 +63,7 @@ class Spec:
     seed: int = 0
     scale: Optional[float] = None
     gate_scale: float = -2.0   # bounded sigmoid gate only: the lower bound of the log decay
+    Hk: Optional[int] = None   # key heads of q, k (grouped heads); None = H
 
     @property
     def eff_scale(self) -> float:
@@ -121,8 +123,10 @@ def generate(spec: Spec) -> Dict[str, object]:
         return rng[name].standard_normal(size=shape) * std
 
     out: Dict[str, object] = {}
-    out["q"] = _round(normal("q", (B, T, H, K)), spec.dtype)
-    out["k"] = _round(normal("k", (B, T, H, K)), spec.dtype)
+    Hk = H if spec.Hk is None else spec.Hk
+    assert H % Hk == 0, "value heads come in whole groups per key head"
+    out["q"] = _round(normal("q", (B, T, Hk, K)), spec.dtype)
+    out["k"] = _round(normal("k", (B, T, Hk, K)), spec.dtype)
     out["v"] = _round(normal("v", (B, T, H, V)), spec.dtype)
     out["dO"] = _round(normal("dO", (B, T, H, V)), spec.dtype)
     out["b"] = _round(normal("b", (B, T, H)), spec.dtype)
@@ -138,7 +142,7 @@ def generate(spec: Spec) -> Dict[str, object]:
     out["dht"] = None if spec.dht_std is None else _round(normal("dht", (N, H, V, K), spec.dht_std), "f32")
     out["cu_seqlens"] = torch.from_numpy(cu)
     out["gate_scale"] = spec.gate_scale if spec.gate == GATE_CHANNEL_SIGMOID else 0.0
-    out.update(B=B, T=T, H=H, K=K, V=V, N=N, gate=spec.gate, scale=spec.eff_scale,
+    out.update(B=B, T=T, H=H, Hk=Hk, K=K, V=V, N=N, gate=spec.gate, scale=spec.eff_scale,
                dtype=spec.dtype, lengths=lengths, name=spec.name)
     return out
 
@@ -155,6 +159,9 @@ def workload(name: str) -> Spec:
         return Spec(name, GATE_SCALAR, "bf16", H=16, K=128, V=128, B=2, T=4096, h0_std=0.1, seed=1001)
     if name == "kda_bf16_t8192_h16_d128":
         return Spec(name, GATE_CHANNEL, "bf16", H=16, K=128, V=128, B=1, T=8192, seed=1002)
+    if name == "gdn_gqa4_bf16_t32768_h32_d128":   # grouped heads: 8 key heads, 4 value heads each
+        return Spec(name, GATE_SCALAR, "bf16", H=32, Hk=8, K=128, V=128, B=1, T=32768, h0_std=0.1,
+                    dht_std=0.1, seed=1005)
     if name == "kdas_bf16_t8192_h16_d128":   # the bounded sigmoid gate on the same inputs
         return Spec(name, GATE_CHANNEL_SIGMOID, "bf16", H=16, K=128, V=128, B=1, T=8192, seed=1002)
     if name == "gdn_varlen12_bf16_t32768_h32_d128":
@@ -179,6 +186,7 @@ WORKLOADS = (
     "kda_bf16_t32768_h32_d128",
     "kdas_bf16_t8192_h16_d128",
     "kdas_bf16_t32768_h16_d128",
+    "gdn_gqa4_bf16_t32768_h32_d128",
 )
 
 HEADLINE = "gdn_bf16_t32768_h16_d128"

@@ -42,6 +42,7 @@ class _Args(ctypes.Structure):
         ("S_chunk", _D), ("dS_chunk", _D), ("u_out", _D), ("dqn", _D), ("dkn", _D),
         ("dbeta", _D), ("dlam", _D),
         ("gate_scale", ctypes.c_double),
+        ("Hk", ctypes.c_int32),
     ]
 
 
@@ -117,6 +118,8 @@ def run(inp: Dict, backward: bool = True, exports: bool = False, chunk: int = 64
     a.N, a.H, a.K, a.V, a.gate, a.chunk = N, H, K, V, gate, chunk
     a.nthreads = nthreads if nthreads is not None else default_threads()
     a.gate_scale = float(inp.get("gate_scale", 0.0))
+    Hk = int(inp.get("Hk", H))
+    a.Hk = Hk
     a.do_backward = 1 if backward else 0
     a.scale = float(inp["scale"])
     a.cu = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
@@ -127,8 +130,8 @@ def run(inp: Dict, backward: bool = True, exports: bool = False, chunk: int = 64
     a.o = _ptr(alloc("o", (B, T, H, V)))
     a.ht = _ptr(alloc("ht", (N, H, V, K)))
     if backward:
-        a.dq = _ptr(alloc("dq", (B, T, H, K)))
-        a.dk = _ptr(alloc("dk", (B, T, H, K)))
+        a.dq = _ptr(alloc("dq", (B, T, Hk, K)))
+        a.dk = _ptr(alloc("dk", (B, T, Hk, K)))
         a.dv = _ptr(alloc("dv", (B, T, H, V)))
         a.dg = _ptr(alloc("dg", (B, T, H) + gK))
         a.db = _ptr(alloc("db", (B, T, H)))

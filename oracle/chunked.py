@@ -60,12 +60,14 @@ def _prep(inp, n, h):
     cu = np.asarray(inp["cu_seqlens"], dtype=np.int64)
     t0, t1 = int(cu[n]), int(cu[n + 1])
     H, K = int(inp["H"]), int(inp["K"])
+    Hk = int(inp.get("Hk", H))   # grouped heads: value head h reads key head h // (H / Hk)
 
-    def tok(name):
+    def tok(name, heads=H, head=h):
         x = _f64(inp[name])
-        return x.reshape((-1, H) + x.shape[3:])[t0:t1, h]
+        return x.reshape((-1, heads) + x.shape[3:])[t0:t1, head]
 
-    q, k, v, dO, b, g = (tok(s) for s in ("q", "k", "v", "dO", "b", "g"))
+    q, k = tok("q", Hk, h // (H // Hk)), tok("k", Hk, h // (H // Hk))
+    v, dO, b, g = (tok(s) for s in ("v", "dO", "b", "g"))
     rq = 1.0 / np.sqrt((q * q).sum(-1) + 1e-6)
     rk = 1.0 / np.sqrt((k * k).sum(-1) + 1e-6)
     qn, kn = q * rq[:, None], k * rk[:, None]
@@ -147,7 +149,9 @@ def run(inp: Dict, chunk: int = 64, dht="input") -> Dict[str, np.ndarray]:
     h0 = _f64(inp.get("h0"))
     dhtv = _f64(inp.get("dht") if isinstance(dht, str) else dht)
     gK = (K,) if gate >= 1 else ()
-    o = np.zeros((TT, H, V)); dq = np.zeros((TT, H, K)); dk = np.zeros((TT, H, K))
+    Hk = int(inp.get("Hk", H))
+    G = H // Hk
+    o = np.zeros((TT, H, V)); dq = np.zeros((TT, Hk, K)); dk = np.zeros((TT, Hk, K))
     dv = np.zeros((TT, H, V)); dg = np.zeros((TT, H) + gK); db = np.zeros((TT, H))
     ht = np.zeros((N, H, V, K)); dh0 = np.zeros((N, H, V, K))
     dA = np.zeros(H); ddt = np.zeros((H, K))
@@ -184,8 +188,9 @@ def run(inp: Dict, chunk: int = 64, dht="input") -> Dict[str, np.ndarray]:
                 dlam[cs:ce] = reverse_cumsum_with_total(r["dgam"], r["dgamC"][None, :])
             dh0[n, h] = dS
             qn, kn, rq, rk, beta = p["qn"], p["kn"], p["rq"], p["rk"], p["beta"]
-            dq[t0:t1, h] = rq[:, None] * (dqn - qn * (qn * dqn).sum(1, keepdims=True))
-            dk[t0:t1, h] = rk[:, None] * (dkn - kn * (kn * dkn).sum(1, keepdims=True))
+            # grouped heads: a key head's gradient sums its value heads' contributions
+            dq[t0:t1, h // G] += rq[:, None] * (dqn - qn * (qn * dqn).sum(1, keepdims=True))
+            dk[t0:t1, h // G] += rk[:, None] * (dkn - kn * (kn * dkn).sum(1, keepdims=True))
             db[t0:t1, h] = dbeta * beta * (1 - beta)
             if gate == 0:
                 dg[t0:t1, h] = dlam.sum(1)

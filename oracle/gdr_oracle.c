@@ -76,6 +76,8 @@ typedef struct {
   double *dbeta;           /* [T][H] gradient w.r.t. beta (after the sigmoid) */
   double *dlam;            /* [T][H] (gate 0) or [T][H][K] (gate 1) gradient w.r.t. lambda_t */
   double gate_scale;       /* gate 2: the bound of the per-token log decay */
+  int32_t Hk;              /* key heads of q, k, dq, dk ([T][Hk][K]); 0 = H.  Value head h reads
+                              key head h / (H / Hk) (grouped query attention) */
 } oracle_args;
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
@@ -87,6 +89,7 @@ typedef struct {
   int64_t NC;
   double* part_dA;       /* [N][H] */
   double* part_ddt;      /* [N][H][K] */
+  double *dq_v, *dk_v;   /* grouped heads: dq, dk per value head [T][H][K], summed per group at the end */
   int next;              /* work counter */
   pthread_mutex_t mu;
   int failed;
@@ -96,6 +99,9 @@ typedef struct {
 static int run_item(pool_t* P, int n, int h) {
   const oracle_args* a = P->a;
   const int H = a->H, K = a->K, V = a->V, C = a->chunk;
+  const int Hk = a->Hk > 0 ? a->Hk : H, hk = h / (H / Hk);
+  double* const dq_out = P->dq_v ? P->dq_v : a->dq;   /* indexed per value head below */
+  double* const dk_out = P->dk_v ? P->dk_v : a->dk;
   const int64_t t0 = a->cu[n];
   const int len = (int)(a->cu[n + 1] - a->cu[n]);
   const int nck = (len + C - 1) / C;
@@ -131,8 +137,8 @@ static int run_item(pool_t* P, int n, int h) {
   /* ---- per-token prologue: normalisation, beta, log decay ---- */
   for (int t = 0; t < len; ++t) {
     const int64_t row = (t0 + t) * H + h;
-    const double* qt = a->q + row * K;
-    const double* kt = a->k + row * K;
+    const double* qt = a->q + ((t0 + t) * Hk + hk) * K;
+    const double* kt = a->k + ((t0 + t) * Hk + hk) * K;
     double sq = 0.0, sk = 0.0;
     for (int j = 0; j < K; ++j) { sq += qt[j] * qt[j]; sk += kt[j] * kt[j]; }
     rq[t] = 1.0 / sqrt(sq + 1e-6);
@@ -273,8 +279,8 @@ static int run_item(pool_t* P, int n, int h) {
       double pq = 0.0, pk = 0.0;
       for (int j = 0; j < K; ++j) { pq += qnt[j] * dqt[j]; pk += knt[j] * dkt[j]; }
       for (int j = 0; j < K; ++j) {
-        if (a->dq) a->dq[row * K + j] = rq[t] * (dqt[j] - qnt[j] * pq);
-        if (a->dk) a->dk[row * K + j] = rk[t] * (dkt[j] - knt[j] * pk);
+        if (dq_out) dq_out[row * K + j] = rq[t] * (dqt[j] - qnt[j] * pq);
+        if (dk_out) dk_out[row * K + j] = rk[t] * (dkt[j] - knt[j] * pk);
         if (a->dqn) a->dqn[row * K + j] = dqt[j];
         if (a->dkn) a->dkn[row * K + j] = dkt[j];
       }
@@ -342,6 +348,7 @@ int oracle_run(const oracle_args* a) {
   if (a->do_backward && !a->dO) return -1;
   if (a->gate < 0 || a->gate > 2) return -1;
   if (a->gate >= 1 && (!a->A_log || !a->dt_bias)) return -1;
+  if (a->Hk < 0 || (a->Hk > 0 && a->H % a->Hk != 0)) return -1;
   for (int n = 0; n < a->N; ++n)
     if (a->cu[n + 1] < a->cu[n]) return -1;
 
@@ -351,8 +358,14 @@ int oracle_run(const oracle_args* a) {
   P.chunk_base = calloc(a->N > 0 ? a->N : 1, sizeof(int64_t));
   P.part_dA = calloc((size_t)(a->N > 0 ? a->N : 1) * a->H, sizeof(double));
   P.part_ddt = calloc((size_t)(a->N > 0 ? a->N : 1) * a->H * a->K, sizeof(double));
-  if (!P.chunk_base || !P.part_dA || !P.part_ddt) {
-    free(P.chunk_base); free(P.part_dA); free(P.part_ddt);
+  const int Hk = a->Hk > 0 ? a->Hk : a->H, G = a->H / Hk;
+  const int64_t TT = a->N > 0 ? a->cu[a->N] : 0;
+  if (G > 1 && a->do_backward) {
+    P.dq_v = calloc((size_t)(TT > 0 ? TT : 1) * a->H * a->K, sizeof(double));
+    P.dk_v = calloc((size_t)(TT > 0 ? TT : 1) * a->H * a->K, sizeof(double));
+  }
+  if (!P.chunk_base || !P.part_dA || !P.part_ddt || (G > 1 && a->do_backward && (!P.dq_v || !P.dk_v))) {
+    free(P.chunk_base); free(P.part_dA); free(P.part_ddt); free(P.dq_v); free(P.dk_v);
     return -2;
   }
   for (int n = 0; n < a->N; ++n) {
@@ -384,7 +397,22 @@ int oracle_run(const oracle_args* a) {
       }
     }
   }
+  if (P.dq_v) {
+    /* grouped heads: the key head's gradient is the sum over its G value heads, in order */
+    for (int64_t t = 0; t < TT; ++t)
+      for (int hk = 0; hk < Hk; ++hk)
+        for (int j = 0; j < a->K; ++j) {
+          double sq = 0.0, sk = 0.0;
+          for (int g = 0; g < G; ++g) {
+            const size_t i = ((size_t)t * a->H + (size_t)hk * G + g) * a->K + j;
+            sq += P.dq_v[i];
+            sk += P.dk_v[i];
+          }
+          if (a->dq) a->dq[((size_t)t * Hk + hk) * a->K + j] = sq;
+          if (a->dk) a->dk[((size_t)t * Hk + hk) * a->K + j] = sk;
+        }
+  }
   const int failed = P.failed;
-  free(P.chunk_base); free(P.part_dA); free(P.part_ddt);
+  free(P.chunk_base); free(P.part_dA); free(P.part_ddt); free(P.dq_v); free(P.dk_v);
   return failed ? -2 : 0;
 }

@@ -311,6 +311,59 @@ def test_sigmoid_gate_with_zero_scale_has_no_decay():
     assert np.all(a["dg"] == 0) and np.all(a["dA_log"] == 0) and np.all(a["ddt_bias"] == 0)
 
 
+@pytest.mark.parametrize("gate", [0, 1, 2])
+def test_grouped_heads_equal_repeated_heads(gate):
+    """Grouped heads by definition: value head h reads key head h // G; the problem
+    with q, k repeated per value head gives the same outputs, and a key head's dq,
+    dk are the sums over its G value heads."""
+    G = 3
+    sp = synth.Spec("gq", gate, "f32", H=6, Hk=2, K=5, V=4, lengths=[11, 0, 17], h0_std=0.3, dht_std=0.3,
+                    seed=23)
+    inp = synth.generate(sp)
+    for key in ("q", "k", "v", "dO", "b", "g", "A_log", "dt_bias", "h0", "dht"):
+        if inp.get(key) is not None:
+            inp[key] = inp[key].double().numpy()
+    inp["cu_seqlens"] = inp["cu_seqlens"].numpy()
+    rep = dict(inp)
+    rep["q"], rep["k"] = np.repeat(inp["q"], G, axis=2), np.repeat(inp["k"], G, axis=2)
+    rep["Hk"] = inp["H"]
+    a = oracle.run(inp, chunk=4)
+    b = oracle.run(rep, chunk=4)
+    for key in ("o", "ht", "dv", "dg", "db", "dh0") + (("dA_log", "ddt_bias") if gate else ()):
+        np.testing.assert_allclose(a[key], b[key], rtol=1e-13, atol=1e-15)
+    for key in ("dq", "dk"):
+        summed = b[key].reshape(b[key].shape[:2] + (2, G) + b[key].shape[3:]).sum(3)
+        np.testing.assert_allclose(a[key], summed, rtol=1e-12, atol=1e-14)
+    c = chunked.run(inp, chunk=4)
+    for key in ("o", "dq", "dk", "dv", "dg", "dh0"):
+        assert np.abs(a[key] - c[key]).max() / max(1.0, np.abs(a[key]).max()) < 1e-12, key
+
+
+def test_finite_differences_grouped_heads():
+    inp = _np_inputs(0, [7, 5], H=4, K=4, V=3, seed=29)
+    sp = synth.Spec("t", 0, "f32", H=4, Hk=2, K=4, V=3, lengths=[7, 5], h0_std=0.4, dht_std=0.3, seed=29)
+    g0 = synth.generate(sp)
+    for key in ("q", "k"):
+        inp[key] = g0[key].double().numpy().copy()
+    inp["Hk"] = 2
+    g = oracle.run(inp, backward=True, chunk=4, nthreads=1)
+    eps = 1e-6
+    for name in ("q", "k"):
+        x = inp[name]
+        num = np.zeros_like(x)
+        flat = x.reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + eps
+            lp = _loss(inp)
+            flat[i] = old - eps
+            lm = _loss(inp)
+            flat[i] = old
+            num.reshape(-1)[i] = (lp - lm) / (2 * eps)
+        err = np.abs(num - g["d" + name]).max() / max(1e-3, np.abs(num).max())
+        assert err < 1e-7, (name, err)
+
+
 def test_oracle_rejects_bad_arguments():
     inp = _np_inputs(1, [4], H=1, K=4, V=4, seed=1)
     inp["A_log"] = None
