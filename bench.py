@@ -65,8 +65,12 @@ def algorithmic_work(inp, stage: str):
     FLOPs are the chunked method's own contractions per (chunk, head), counting
     triangular products at half size; bytes are the HBM traffic the stage
     cannot avoid (inputs read, outputs written, its workspace in and out).
+    With grouped heads q and k have Hk < H heads and are read once per key head
+    (the value heads of a group share them through L2); dq and dk leave the
+    gradient stages per value head and the group sums (in "finish") reduce them.
     """
     H, D = inp["H"], inp["K"]
+    Hk = inp.get("Hk") or H
     NC = sum((L + C - 1) // C for L in inp["lengths"])
     tokens = inp["B"] * inp["T"]
     ch = NC * H
@@ -82,36 +86,41 @@ def algorithmic_work(inp, stage: str):
     wt = C * C * 2 if raw else C * D * 2
     if stage == "prep":
         # q, k, v, g, b in; Gamma, row scalars, A, P, U' (and W unless raw) out
-        b = tokens * H * (3 * D * io + (1 + gk) * io) + ch * (C * gk * 4 + 2 * C * 4 + 2 * C * C * 2
+        b = tokens * (2 * Hk * D * io + H * (D * io + (1 + gk) * io)) + ch * (C * gk * 4 + 2 * C * 4 + 2 * C * C * 2
                                                               + (1 if raw else 2) * C * D * 2)
         return ch * f_prep, b
     if stage == "chain_fwd":
         # W (or A), U', k in; S, U out
-        return ch * f_fwd, ch * (wt + C * D * 2 + D * D * 2 + C * D * 2) + tokens * H * D * io
+        return ch * f_fwd, ch * (wt + C * D * 2 + D * D * 2 + C * D * 2) + tokens * Hk * D * io
     if stage == "chain_bwd":
         # W (or A), P, q, k, dO in; dS, dU out
-        return ch * f_bwd, ch * (wt + C * C * 2 + D * D * 2 + C * D * 2) + tokens * H * 3 * D * io
+        return ch * f_bwd, ch * (wt + C * C * 2 + D * D * 2 + C * D * 2) + tokens * (2 * Hk + H) * D * io
     if stage == "chain_both":
         a, b = algorithmic_work(inp, "chain_fwd"), algorithmic_work(inp, "chain_bwd")
         return a[0] + b[0], a[1] + b[1]
     if stage == "output":
         # S_n, U, P and Qbar (or the raw q rows and row factors) in; o out
-        b = ch * (D * D * 2 + C * D * 2 + C * C * 2 + (0 if raw else C * D * 2)) + tokens * H * D * io * (2 if raw else 1)
+        b = ch * (D * D * 2 + C * D * 2 + C * C * 2 + (0 if raw else C * D * 2)) + tokens * (H + (Hk if raw else 0)) * D * io
         return ch * (2 * C * D * D + C * C * D), b
     if stage == "grads":
         if inp["gate"] == 0:
             # fused with the prepare-backward: S, dS, U, dU, A, Gamma, (1/|q|, 1/|k|, beta)
             # per chunk; q, k, v, dO read and dq, dk, dv, dg, db written per token
-            b = ch * (2 * D * D * 2 + 2 * C * D * 2 + C * C * 2 + C * 4 + 3 * C * 4) + tokens * H * (7 * D * io + 2 * io)
+            b = (ch * (2 * D * D * 2 + 2 * C * D * 2 + C * C * 2 + C * 4 + 3 * C * 4)
+                 + tokens * (2 * Hk * D * io + H * (5 * D * io + 2 * io)))
         else:
             b = (ch * (2 * D * D * 2 + 2 * C * D * 2 + C * C * 2 + 2 * C * D * 4 + C * gk * 4 + C * 4)
-                 + tokens * H * 5 * D * io)
+                 + tokens * (2 * Hk + 3 * H) * D * io)
         return ch * f_grads, b
     if stage == "finish":
-        # read q, k, dqn, dkn, rho, dGamma, dbeta, b (and g_raw for KDA); write dq, dk, dg, db
-        b = tokens * H * (2 * D * io + 2 * D * 4 + 8 + gk * 4 + 4 + io + 2 * D * io + gk * io + io)
+        b = 0
         if inp["gate"] != 0:
-            b += tokens * H * D * io
+            # read q, k, dqn, dkn, rho, dGamma, dbeta, b, g_raw; write dq, dk, dg, db
+            b = (tokens * 2 * Hk * D * io
+                 + tokens * H * (2 * D * 4 + 8 + gk * 4 + 4 + io + 2 * D * io + gk * io + io + D * io))
+        if Hk < H:
+            # group sums: dq, dk per value head in, per key head out
+            b += tokens * 2 * (H + Hk) * D * io
         return 0, b
     raise KeyError(stage)
 
@@ -244,9 +253,11 @@ def main() -> int:
     # every kernel alone (the workspace already holds what earlier stages leave)
     kernels = {}
     # the scalar gate's prepare-backward runs inside its gradient kernel
-    path = ("prep", "chain_both", "grads") + (("finish",) if inp["gate"] != 0 else ())
+    # and, with grouped heads, the dq, dk group sums make up the finish stage
+    has_finish = inp["gate"] != 0 or (inp.get("Hk") or H) < H
+    path = ("prep", "chain_both", "grads") + (("finish",) if has_finish else ())
     stages = [B.GDR_STAGE_PREP, B.GDR_STAGE_CHAIN_BOTH, B.GDR_STAGE_GRADS]
-    if inp["gate"] != 0:
+    if has_finish:
         stages.append(B.GDR_STAGE_FINISH)
     if args.all_stages:
         stages += [B.GDR_STAGE_CHAIN_FWD, B.GDR_STAGE_CHAIN_BWD]
@@ -271,7 +282,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if inp["dtype"] == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": inp["B"], "T": inp["T"], "H": H, "D": K,
+        "config": {"workload": args.workload, "B": inp["B"], "T": inp["T"], "H": H, "Hk": inp.get("Hk") or H, "D": K,
                    "gate": GATE_NAMES[inp["gate"]], "chunk": C},
         "roofline": roof,
         "kernels": kernels,

@@ -42,7 +42,7 @@ class Shape(ctypes.Structure):
                 ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int64)),
                 ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("gate_scale", ctypes.c_float)]
+                ("gate_scale", ctypes.c_float), ("Hk", ctypes.c_int32)]
 
 
 class Inputs(ctypes.Structure):
@@ -114,14 +114,14 @@ class Problem:
     """
 
     def __init__(self, B: int, T: int, H: int, D: int, N: int, gate: int, dtype: int, scale: float,
-                 cu_seqlens=None, gate_scale: float = 0.0):
+                 cu_seqlens=None, gate_scale: float = 0.0, Hk: int = 0):
         self.cu = None
         if cu_seqlens is not None:
             cu = torch.as_tensor(cu_seqlens, dtype=torch.int64).contiguous().cpu()
             self.cu = cu
         self.shape = Shape(B, T, H, D, D, N,
                            None if self.cu is None else ctypes.cast(self.cu.data_ptr(), ctypes.POINTER(ctypes.c_int64)),
-                           gate, dtype, scale, gate_scale)
+                           gate, dtype, scale, gate_scale, Hk)
 
     @staticmethod
     def from_inputs(inp: Dict, varlen: Optional[bool] = None) -> "Problem":
@@ -130,11 +130,12 @@ class Problem:
             varlen = inp["B"] == 1 and (len(lengths) > 1 or lengths[0] != inp["T"])
         dtype = GDR_BF16 if inp["dtype"] == "bf16" else GDR_F32
         gs = float(inp.get("gate_scale", 0.0))
+        hk = int(inp.get("Hk") or 0)
         if varlen:
             return Problem(1, inp["T"], inp["H"], inp["K"], inp["N"], inp["gate"], dtype, inp["scale"],
-                           cu_seqlens=inp["cu_seqlens"], gate_scale=gs)
+                           cu_seqlens=inp["cu_seqlens"], gate_scale=gs, Hk=hk)
         return Problem(inp["B"], inp["T"], inp["H"], inp["K"], inp["N"], inp["gate"], dtype, inp["scale"],
-                       gate_scale=gs)
+                       gate_scale=gs, Hk=hk)
 
 
 def gdr_workspace_bytes(prob: Problem) -> int:

@@ -42,6 +42,8 @@ gdr_status check_shape(const gdr_shape* s, int64_t* NC_out) {
   if (s->Dk != s->Dv) return fail(GDR_EUNSUPPORTED, "Dk (%d) != Dv (%d)", s->Dk, s->Dv);
   if (s->Dk != 64 && s->Dk != 128) return fail(GDR_EUNSUPPORTED, "head dim %d not in {64, 128}", s->Dk);
   if (s->H < 1 || s->B < 1 || s->T < 0 || s->N < 0) return fail(GDR_EINVAL, "bad B/T/H/N");
+  if (s->Hk < 0 || s->Hk > s->H || (s->Hk > 0 && s->H % s->Hk != 0))
+    return fail(GDR_EINVAL, "Hk (%d) must be 0 or divide H (%d)", s->Hk, s->H);
   int64_t NC = 0;
   if (s->cu_seqlens_host == nullptr) {
     if (s->N != s->B) return fail(GDR_EINVAL, "dense shape needs N == B (N=%d, B=%d)", s->N, s->B);
@@ -107,6 +109,10 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.Ulo = take(kda * H * NC * C * V * 2);
   L.Slo = take(kda * H * NC * V * K * 2);
   L.dSlo = take(kda * H * NC * V * K * 2);
+  const size_t grouped = s->Hk > 0 && s->Hk < s->H ? 1 : 0;
+  const size_t esz = s->dtype == GDR_BF16 ? 2 : 4;
+  L.dqv = take(grouped * size_t(s->B) * size_t(s->T) * H * K * esz);
+  L.dkv = take(grouped * size_t(s->B) * size_t(s->T) * H * K * esz);
   L.total = off;
   return L;
 }
@@ -191,6 +197,8 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   gdr::Params p;
   std::memset(&p, 0, sizeof(p));
   p.H = s->H; p.K = s->Dk; p.V = s->Dv; p.N = s->N; p.NC = int32_t(L.NC); p.T = s->B * s->T;
+  p.Hk = s->Hk > 0 ? s->Hk : s->H;
+  p.G = s->H / p.Hk;
   // the kernels tell the scalar gate from the per-channel one; the per-channel
   // gate function (softplus or bounded sigmoid) matters only where it is applied
   p.gate = s->gate == GDR_GATE_SCALAR ? 0 : 1;
@@ -237,9 +245,16 @@ gdr_status hip_status(int err, const char* what) {
   return fail(GDR_EHIP, "%s: %s", what, gdr::hip_error_string(err));
 }
 
-void set_grads(gdr::Params& p, const void* dO, const float* dht, const gdr_grads* gr) {
+// With grouped heads the kernels write dq, dk per value head into the workspace;
+// group_sum then reduces them into the caller's [tokens][Hk][K] outputs.
+void set_grads(gdr::Params& p, const gdr::WsLayout& L, void* ws, const void* dO, const float* dht,
+               const gdr_grads* gr) {
   p.dO = dO; p.dht = dht;
   p.dq = gr->dq; p.dk = gr->dk; p.dv = gr->dv; p.dg = gr->dg; p.db = gr->dbeta;
+  if (p.G > 1) {
+    p.dq = static_cast<char*>(ws) + L.dqv;
+    p.dk = static_cast<char*>(ws) + L.dkv;
+  }
   p.dh0 = gr->dh0; p.dA_log = gr->dA_log; p.ddt_bias = gr->ddt_bias;
 }
 
@@ -264,16 +279,20 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
   gdr::Params p = make_params(s, L, in, ws);
   p.ht = ht;
   p.o = o;
-  if (stage != kFwd) set_grads(p, dO, dht, gr);
+  if (stage != kFwd) set_grads(p, L, ws, dO, dht, gr);
 
   const bool kda = s->gate != GDR_GATE_SCALAR;
   auto prep = [&]() { return kda ? gdr::launch_kda(p, 0, stream) : gdr::launch_prep(p, stream); };
   auto grads = [&]() { return kda ? gdr::launch_kda(p, 1, stream) : gdr::launch_grads(p, stream); };
-  // the scalar gate's prepare-backward is fused into its gradient kernel
+  // the scalar gate's prepare-backward is fused into its gradient kernel; with
+  // grouped heads the dq, dk group sums end this stage
   auto finish = [&]() {
-    if (!kda) return 0;
-    const int e = gdr::launch_kda(p, 2, stream);
-    return e ? e : gdr::launch_kda(p, 3, stream);
+    int e = 0;
+    if (kda && !e) e = gdr::launch_kda(p, 2, stream);
+    if (kda && !e) e = gdr::launch_kda(p, 3, stream);
+    if (p.G > 1 && !e) e = gdr::launch_group_sum(p, p.dq, gr->dq, stream);
+    if (p.G > 1 && !e) e = gdr::launch_group_sum(p, p.dk, gr->dk, stream);
+    return e;
   };
   if (only >= 0) {
     switch (only) {

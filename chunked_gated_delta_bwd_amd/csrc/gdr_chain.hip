@@ -175,16 +175,17 @@ __device__ __forceinline__ void move_tile(const MoverLane<D>& ml, const void* sr
   for (int j = 0; j < NJ; ++j) dma16(s + ml.tD[j], dst + mw * (TB / 4) + j * 1024);
 }
 
-// a 64 x D tile of raw token rows (q or k of head h), rows past the end clamped
+// a 64 x D tile of raw token rows (q or k of the key head that value head h reads),
+// rows past the end clamped
 template <int D>
 __device__ __forceinline__ void move_rows(const MoverLane<D>& ml, const void* base, const Params& p, const ChunkGeo& cg,
                                           int h, char* dst, int mw) {
   constexpr int TB = C * D * 2, NJ = TB / 4096;
-  const char* s = static_cast<const char*>(base) + int64_t(h) * D * 2;
+  const char* s = static_cast<const char*>(base) + int64_t(h / p.G) * D * 2;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int64_t t = cg.t0 + min(ml.rD[j], cg.len - 1);
-    dma16(s + t * (int64_t(p.H) * D * 2) + ml.pD[j], dst + mw * (TB / 4) + j * 1024);
+    dma16(s + t * (int64_t(p.Hk) * D * 2) + ml.pD[j], dst + mw * (TB / 4) + j * 1024);
   }
 }
 
@@ -325,6 +326,9 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const SeqEntry& 
     return static_cast<const char*>(base) +
            (tok(cg.t0 + min(row, cg.len - 1), p.H, h) * D) * bytes_per_elem;
   };
+  auto qk_row = [&](const void* base, int row) {   // q, k: the key head of value head h
+    return static_cast<const char*>(base) + qk_tok(p, cg.t0 + min(row, cg.len - 1), h) * D * 2;
+  };
   auto tile_row = [&](const uint16_t* base, int row) {
     return reinterpret_cast<const char*>(base + (cg.ch * C + row) * D);
   };
@@ -333,12 +337,12 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const SeqEntry& 
     const char* rb;
     if constexpr (BWD) {
       if constexpr (Cf::RAW)
-        rb = t == 0 ? tok_row(p.k, row, 2) : tok_row(p.q, row, 2);
+        rb = t == 0 ? qk_row(p.k, row) : qk_row(p.q, row);
       else
         rb = t == 0 ? tile_row(p.Kh, row) : t == 1 ? tile_row(p.Qh, row) : t == 2 ? tile_row(p.Ql, row) : tile_row(p.W, row);
     } else {
       if constexpr (Cf::RAW)
-        rb = tok_row(p.k, row, 2);
+        rb = qk_row(p.k, row);
       else
         rb = t == 0 ? tile_row(p.W, row) : tile_row(p.Kh, row);
     }

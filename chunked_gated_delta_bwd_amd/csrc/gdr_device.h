@@ -262,6 +262,10 @@ struct Dims {
 };
 
 __device__ __forceinline__ int64_t tok(int t, int H, int h) { return int64_t(t) * H + h; }
+// token row of the q, k tensors for value head h: with grouped heads q and k have
+// Hk heads, value head h reading key head h / (H / Hk) (P is the kernels' Params)
+template <typename P>
+__device__ __forceinline__ int64_t qk_tok(const P& p, int t, int h) { return int64_t(t) * p.Hk + h / p.G; }
 
 __device__ __forceinline__ void st_bf16x4(bf16* dst, float a, float b, float c, float d) {
   *reinterpret_cast<uint2*>(dst) = pack4_bf16(a, b, c, d);

@@ -70,11 +70,15 @@ struct WsLayout {
   size_t Ulo = 0;    // bf16 [H][NC][V][64]
   size_t Slo = 0;    // bf16 [H][NC][V][K]
   size_t dSlo = 0;   // bf16 [H][NC][V][K]
+  // grouped heads only (Hk < H): dq, dk per value head before the group sum
+  size_t dqv = 0;    // dtype [tokens][H][K]
+  size_t dkv = 0;    // dtype [tokens][H][K]
   size_t total = 0;
 };
 
 struct Params {
   int32_t H, K, V, N, NC, T;     // T = total tokens
+  int32_t Hk, G;                  // q, k heads and value heads per key head (H = Hk G)
   int32_t gate, dtype;            // gate: 0 scalar, 1 per-channel (either gate function)
   float scale;
   int32_t gate_fn;                // per-channel: 0 -e^A_log softplus(x), 1 gate_scale sigmoid(e^A_log x)
@@ -110,6 +114,9 @@ int launch_grads(const Params& p, void* stream);
 int launch_zero_params(const Params& p, void* stream);
 // Forward output from the forward recompute's workspace (gdr_out.hip).
 int launch_output(const Params& p, void* stream);
+// Grouped heads (gdr_group.hip): dst[t][j][:] = sum over i < G of src[t][j G + i][:],
+// for the T tokens, Hk key heads and K channels of p, in p.dtype.
+int launch_group_sum(const Params& p, const void* src, void* dst, void* stream);
 // Per-channel gate kernels (gdr_kda.hip): stage 0 prologue, 1 gradients,
 // 2 prepare-backward, 3 dA_log / ddt_bias reduction.
 int launch_kda(const Params& p, int stage, void* stream);

@@ -114,8 +114,9 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     const int64_t off = tok(t0 + min(r, len - 1), H, h) * D + c0;
-    qraw[ps] = IO<TIO>::load_raw8(p.q, off);
-    kraw[ps] = IO<TIO>::load_raw8(p.k, off);
+    const int64_t qoff = qk_tok(p, t0 + min(r, len - 1), h) * D + c0;
+    qraw[ps] = IO<TIO>::load_raw8(p.q, qoff);
+    kraw[ps] = IO<TIO>::load_raw8(p.k, qoff);
     vraw[ps] = IO<TIO>::load_raw8(p.v, off);
     graw[ps] = IO<TIO>::load_raw8(p.g, off);
   }
@@ -676,7 +677,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   for (int ps = 0; ps < NPASS; ++ps) {
     const int rr = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     float qv[8], kv[8];
-    const int64_t o = tok(t0 + min(rr, len - 1), H, h) * D + c0;
+    const int64_t o = qk_tok(p, t0 + min(rr, len - 1), h) * D + c0;
     IO<TIO>::load8(p.q, o, qv);
     IO<TIO>::load8(p.k, o, kv);
     const float m = rr < len ? 1.f : 0.f;
@@ -1012,9 +1013,10 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR;
     const int64_t o = tok(t0 + min(r, len - 1), H, h) * D + c0;
+    const int64_t qo = qk_tok(p, t0 + min(r, len - 1), h) * D + c0;
     const int64_t wo = (ch * C + r) * D + c0;
-    qraw[ps] = IO<TIO>::load_raw8(p.q, o);
-    kraw[ps] = IO<TIO>::load_raw8(p.k, o);
+    qraw[ps] = IO<TIO>::load_raw8(p.q, qo);
+    kraw[ps] = IO<TIO>::load_raw8(p.k, qo);
     graw[ps] = IO<TIO>::load_raw8(p.g, o);
     dq4[ps][0] = ld4(p.dqn + wo);
     dq4[ps][1] = ld4(p.dqn + wo + 4);

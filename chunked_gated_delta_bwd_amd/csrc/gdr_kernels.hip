@@ -81,8 +81,9 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     const int64_t off = tok(t0 + min(r, len - 1), H, h) * D + c0;
-    qraw[ps] = IO<TIO>::load_raw8(p.q, off);
-    kraw[ps] = IO<TIO>::load_raw8(p.k, off);
+    const int64_t qoff = qk_tok(p, t0 + min(r, len - 1), h) * D + c0;
+    qraw[ps] = IO<TIO>::load_raw8(p.q, qoff);
+    kraw[ps] = IO<TIO>::load_raw8(p.k, qoff);
     vraw[ps] = IO<TIO>::load_raw8(p.v, off);
   }
   float graw = 0.f, braw = 0.f;
@@ -399,6 +400,10 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
   auto row_of = [&](const void* x, int rr) {
     return reinterpret_cast<const char*>(x) + tok(t0 + min(rr, len - 1), H, h) * D * 2;
   };
+  auto qk_row_of = [&](const void* x, int rr) {   // q, k rows (key head of this value head)
+    return reinterpret_cast<const char*>(x) + qk_tok(p, t0 + min(rr, len - 1), h) * D * 2;
+  };
+  const int64_t qtrow = qk_tok(p, t0 + min(r, len - 1), h) * D;
 
   // ---- first group: per-row scalars, phase-1 tiles, dO (and v) ----
   if (w < 4)
@@ -426,8 +431,9 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
     for (int ps = 0; ps < NPASS; ++ps) {
       const int rr = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
       const int64_t o = tok(t0 + min(rr, len - 1), H, h) * D + c0;
-      qraw[ps] = IO<TIO>::load_raw8(p.q, o);
-      kraw[ps] = IO<TIO>::load_raw8(p.k, o);
+      const int64_t qo = qk_tok(p, t0 + min(rr, len - 1), h) * D + c0;
+      qraw[ps] = IO<TIO>::load_raw8(p.q, qo);
+      kraw[ps] = IO<TIO>::load_raw8(p.k, qo);
       float x[8];
       IO<TIO>::load8(p.dO, o, x);
       bf16x8 xb;
@@ -474,8 +480,8 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
 
   // ---- raw q, k rows (bf16 inputs) into the freed dU^T and v tiles; dv ----
   if constexpr (kDma) {
-    dma_tile<D, 0, C, kGradWaves>(dUT, [&](int rr) { return row_of(p.q, rr); }, w);
-    dma_tile<D, 0, C, kGradWaves>(Vt, [&](int rr) { return row_of(p.k, rr); }, w);
+    dma_tile<D, 0, C, kGradWaves>(dUT, [&](int rr) { return qk_row_of(p.q, rr); }, w);
+    dma_tile<D, 0, C, kGradWaves>(Vt, [&](int rr) { return qk_row_of(p.k, rr); }, w);
   }
   if (r < len) {
 #pragma unroll
@@ -635,8 +641,8 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
   if constexpr (!kDma) {
 #pragma unroll
     for (int q = 0; q < NJH; ++q) {
-      qo[q] = IO<TIO>::load_raw4(p.q, trow + 16 * (hf * NJH + q) + 4 * g);
-      ko[q] = IO<TIO>::load_raw4(p.k, trow + 16 * (hf * NJH + q) + 4 * g);
+      qo[q] = IO<TIO>::load_raw4(p.q, qtrow + 16 * (hf * NJH + q) + 4 * g);
+      ko[q] = IO<TIO>::load_raw4(p.k, qtrow + 16 * (hf * NJH + q) + 4 * g);
     }
   }
   chain_barrier();   // B_e: dME, dPE complete

@@ -70,13 +70,18 @@ typedef struct {
   float gate_scale;                 /* GDR_GATE_CHANNEL_SIGMOID: the bound of the per-token log decay,
                                        finite and <= 0 (natural log: the pages' log2-unit bound times
                                        ln 2); ignored otherwise */
+  int32_t Hk;                       /* heads of q and k (grouped heads): 0 means H; else H % Hk == 0 and
+                                       value head h reads key head h / (H / Hk), and dq, dk sum over the
+                                       H / Hk value heads of each key head (FlashQLA GDN overview,
+                                       grouped-head note).  Hk < H needs workspace for the per-value-head
+                                       dq, dk before that sum. */
 } gdr_shape;
 
 /* Below, CHANNEL stands for either per-channel gate (GDR_GATE_CHANNEL or
  * GDR_GATE_CHANNEL_SIGMOID): both take the raw gate g, A_log and dt_bias and return
  * dg, dA_log and ddt_bias in the same shapes. */
 typedef struct {                    /* device pointers */
-  const void *q, *k;                /* [B,T,H,Dk] dtype */
+  const void *q, *k;                /* [B,T,Hk,Dk] dtype (Hk = H unless grouped) */
   const void *v;                    /* [B,T,H,Dv] dtype */
   const void *g;                    /* SCALAR: [B,T,H] log decay; CHANNEL: [B,T,H,Dk] raw gate; dtype */
   const void *beta_logit;           /* [B,T,H] dtype (pre-sigmoid) */
@@ -86,7 +91,7 @@ typedef struct {                    /* device pointers */
 } gdr_inputs;
 
 typedef struct {                    /* device pointers, all overwritten */
-  void *dq, *dk;                    /* [B,T,H,Dk] dtype */
+  void *dq, *dk;                    /* [B,T,Hk,Dk] dtype (Hk = H unless grouped) */
   void *dv;                         /* [B,T,H,Dv] dtype */
   void *dg;                         /* SCALAR: [B,T,H]; CHANNEL: [B,T,H,Dk] (w.r.t. the raw gate); dtype */
   void *dbeta;                      /* [B,T,H] dtype, w.r.t. the logit */

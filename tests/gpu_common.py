@@ -59,12 +59,26 @@ def gpu_run(inp: Dict, mode: str = "fused", exports: bool = False) -> Dict[str, 
     return res
 
 
+def key_heads(inp: Dict, heads: Iterable[int]) -> list:
+    """The q, k heads that value heads `heads` read (grouped heads: h // (H / Hk))."""
+    G = inp["H"] // (inp.get("Hk") or inp["H"])
+    return sorted({h // G for h in heads})
+
+
 def subset_heads(inp: Dict, heads: Iterable[int]) -> Dict:
-    """The same problem restricted to some heads (heads never interact)."""
+    """The same problem restricted to some heads (heads never interact; with
+    grouped heads the value heads must form whole groups, since dq and dk sum
+    over a group)."""
     heads = list(heads)
+    G = inp["H"] // (inp.get("Hk") or inp["H"])
+    kh = key_heads(inp, heads)
+    assert sorted(heads) == heads and heads == [j * G + i for j in kh for i in range(G)], "whole groups"
     idx = torch.tensor(heads, dtype=torch.long)
+    kidx = torch.tensor(kh, dtype=torch.long)
     out = dict(inp)
-    for key in ("q", "k", "v", "dO", "g", "b"):
+    for key in ("q", "k"):
+        out[key] = inp[key].index_select(2, kidx).contiguous()
+    for key in ("v", "dO", "g", "b"):
         out[key] = inp[key].index_select(2, idx).contiguous()
     for key in ("h0", "dht"):
         if inp.get(key) is not None:
@@ -73,10 +87,14 @@ def subset_heads(inp: Dict, heads: Iterable[int]) -> Dict:
         if inp.get(key) is not None:
             out[key] = inp[key].index_select(0, idx).contiguous()
     out["H"] = len(heads)
+    out["Hk"] = len(kh)
     return out
 
 
-def compare(got: Dict, ref: Dict, keys, tol: float, label: str, head_index: Optional[list] = None) -> Dict:
+def compare(got: Dict, ref: Dict, keys, tol: float, label: str, head_index: Optional[list] = None,
+            key_index: Optional[list] = None) -> Dict:
+    """Normalised error per output; `head_index` picks the value heads the oracle
+    ran, `key_index` the q, k heads (dq, dk) where they differ."""
     errs = {}
     for key in keys:
         if key not in ref:
@@ -84,7 +102,8 @@ def compare(got: Dict, ref: Dict, keys, tol: float, label: str, head_index: Opti
         x = got[key]
         if head_index is not None:
             axis = 0 if key in ("dA_log", "ddt_bias") else (1 if key in ("dh0", "ht") else 2)
-            x = np.take(x, head_index, axis=axis)
+            idx = key_index if key in ("dq", "dk") and key_index is not None else head_index
+            x = np.take(x, idx, axis=axis)
         errs[key] = nerr(x, ref[key])
     log(f"[{label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}

@@ -54,6 +54,15 @@ def test_sigmoid_gate_uses_the_per_channel_workspace():
     assert sig == B.gdr_workspace_bytes(_prob(gate=1, D=128))
 
 
+def test_grouped_heads_workspace_holds_per_value_head_dq_dk():
+    full = B.gdr_workspace_bytes(_prob(H=4, D=64, T=128))
+    assert B.gdr_workspace_bytes(_prob(H=4, Hk=4, D=64, T=128)) == full   # Hk == H: not grouped
+    grouped = B.gdr_workspace_bytes(_prob(H=4, Hk=2, D=64, T=128))
+    assert grouped >= full + 2 * 128 * 4 * 64 * 2                          # bf16 dq, dk per value head
+    f32 = B.gdr_workspace_bytes(_prob(H=4, Hk=2, D=64, T=128, dtype=1))
+    assert f32 - B.gdr_workspace_bytes(_prob(H=4, D=64, T=128, dtype=1)) >= 2 * 128 * 4 * 64 * 4
+
+
 def test_workspace_regions_are_disjoint_and_inside():
     p = _prob(T=200, D=128, gate=1)
     total = B.gdr_workspace_bytes(p)
@@ -78,6 +87,9 @@ def test_workspace_regions_are_disjoint_and_inside():
     (dict(gate=2, gate_scale=0.5), B.GDR_EINVAL),               # the bound of a log decay is <= 0
     (dict(gate=2, gate_scale=float("nan")), B.GDR_EINVAL),
     (dict(gate=2, gate_scale=float("-inf")), B.GDR_EINVAL),
+    (dict(H=4, Hk=3), B.GDR_EINVAL),                            # key heads must divide value heads
+    (dict(H=2, Hk=4), B.GDR_EINVAL),
+    (dict(Hk=-1), B.GDR_EINVAL),
 ])
 def test_shape_validation(kw, status):
     with pytest.raises(B.GdrError) as e:

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from chunked_gated_delta_bwd_amd import synth
-from gpu_common import (FP32_GRADS, TOKEN_GRADS, TOL_BF16, TOL_FP32, compare, gpu_run, log,
+from gpu_common import (FP32_GRADS, TOKEN_GRADS, TOL_BF16, TOL_FP32, compare, gpu_run, key_heads, log,
                         subset_heads)
 
 pytestmark = [pytest.mark.gpu,
@@ -20,10 +20,11 @@ pytestmark = [pytest.mark.gpu,
 
 def _check(inp, got, label, heads=None, tol_fp32=TOL_FP32):
     sub = inp if heads is None else subset_heads(inp, heads)
+    kh = None if heads is None else key_heads(inp, heads)
     ref = oracle.run(sub)
-    compare(got, ref, TOKEN_GRADS, TOL_BF16, label + " grads", heads)
-    compare(got, ref, FP32_GRADS, tol_fp32, label + " fp32", heads)
-    compare(got, ref, ("ht",), TOL_FP32 * 5, label + " ht", heads)
+    compare(got, ref, TOKEN_GRADS, TOL_BF16, label + " grads", heads, kh)
+    compare(got, ref, FP32_GRADS, tol_fp32, label + " fp32", heads, kh)
+    compare(got, ref, ("ht",), TOL_FP32 * 5, label + " ht", heads, kh)
 
 
 SMALL = [
@@ -212,3 +213,43 @@ def test_kdas_workload_t8192_h16():
     inp = synth.generate(synth.workload("kdas_bf16_t8192_h16_d128"))
     got = gpu_run(inp)
     _check_kdas(inp, got, "kdas_bf16_t8192_h16_d128")
+
+
+# ---------------------------------------------------------------------------
+# grouped heads: q, k with Hk heads, each read by H / Hk value heads; dq, dk are
+# the group sums (every gate, both dtypes, dense and ragged varlen)
+# ---------------------------------------------------------------------------
+SMALL_GQA = [
+    ("gqa2_gdn_bf16_b1_t300_d64", synth.Spec("qa", 0, "bf16", H=4, Hk=2, K=64, V=64, B=1, T=300,
+                                             h0_std=0.3, dht_std=0.3, seed=71)),
+    ("gqa3_gdn_f32_varlen_edges_d128",
+     synth.Spec("qb", 0, "f32", H=6, Hk=2, K=128, V=128, lengths=[1, 63, 64, 65, 0, 200], h0_std=0.1,
+                dht_std=0.1, seed=72)),
+    ("gqa4_kda_bf16_varlen_d128", synth.Spec("qc", 1, "bf16", H=4, Hk=1, K=128, V=128,
+                                             lengths=[130, 7, 64], h0_std=0.1, dht_std=0.1, seed=73)),
+    ("gqa2_kda_f32_b2_t100_d64", synth.Spec("qd", 1, "f32", H=4, Hk=2, K=64, V=64, B=2, T=100, seed=74)),
+]
+
+
+@pytest.mark.parametrize("name,spec", SMALL_GQA, ids=[s[0] for s in SMALL_GQA])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_grouped_heads_small_against_oracle(name, spec, mode):
+    log(f"case {name} mode {mode}")
+    inp = synth.generate(spec)
+    got = gpu_run(inp, mode=mode)
+    assert got["dq"].shape[2] == spec.Hk
+    _check(inp, got, f"{name}/{mode}")
+
+
+def test_grouped_heads_sigmoid_gate():
+    inp = synth.generate(synth.Spec("qe", 2, "f32", H=4, Hk=2, K=64, V=64, B=1, T=200, h0_std=0.2,
+                                    dht_std=0.2, seed=75))
+    _check_kdas(inp, gpu_run(inp), "gqa2_kdas_f32_t200_d64")
+
+
+def test_grouped_heads_workload_sampled_group():
+    """H = 32 value heads over Hk = 8 key heads at T = 32768; one whole group
+    (key head 5, value heads 20..23) against the oracle."""
+    inp = synth.generate(synth.workload("gdn_gqa4_bf16_t32768_h32_d128"))
+    got = gpu_run(inp)
+    _check(inp, got, "gdn_gqa4_t32768_h32", heads=[20, 21, 22, 23])
