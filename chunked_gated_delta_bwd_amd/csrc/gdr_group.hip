@@ -1,6 +1,7 @@
 // Grouped heads: q and k carry Hk heads, each read by G = H / Hk consecutive value
 // heads, so the gradient of a key head's q (or k) row is the sum of what its G value
-// heads contribute (FlashQLA GDN overview, grouped-head note).  The gradient kernels
+// heads contribute (FlashQLA GDN overview, section 4: its benchmarks name key and value
+// head counts apart, hk and hv, and its tests cover GQA).  The gradient kernels
 // write those contributions per value head, [tokens][H][K]; this kernel sums each
 // group into the [tokens][Hk][K] output.
 //

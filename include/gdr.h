@@ -73,7 +73,7 @@ typedef struct {
   int32_t Hk;                       /* heads of q and k (grouped heads): 0 means H; else H % Hk == 0 and
                                        value head h reads key head h / (H / Hk), and dq, dk sum over the
                                        H / Hk value heads of each key head (FlashQLA GDN overview,
-                                       grouped-head note).  Hk < H needs workspace for the per-value-head
+                                       section 4: hk and hv head counts, GQA tests).  Hk < H needs workspace for the per-value-head
                                        dq, dk before that sum. */
 } gdr_shape;
 
