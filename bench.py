@@ -36,11 +36,11 @@ CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 # 1 GiB copy; profiles/gdn_t32768_h16_d128.md), valid only for the kernel
 # sources they were taken on: (workload, stage, sha256 prefix) -> bytes.
 MEASURED_TRAFFIC = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "9dfad375b650"): 0.716e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "9dfad375b650"): 1.690e9,
-    ("gdn_bf16_t32768_h16_d128", "grads", "9dfad375b650"): 1.855e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "9dfad375b650"): 0.747e9,
-    ("gdn_bf16_t32768_h16_d128", "output", "9dfad375b650"): 0.745e9,
+    ("gdn_bf16_t32768_h16_d128", "prep", "968d4d3c69b4"): 0.716e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "968d4d3c69b4"): 1.690e9,
+    ("gdn_bf16_t32768_h16_d128", "grads", "968d4d3c69b4"): 1.855e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "968d4d3c69b4"): 0.747e9,
+    ("gdn_bf16_t32768_h16_d128", "output", "968d4d3c69b4"): 0.745e9,
 }
 
 
