@@ -554,6 +554,13 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     const int pc = tid + x * kThreads;
     a_r[x] = *reinterpret_cast<const uint4*>(p.A + (ch * C + pc / 8) * C + (pc % 8) * 8);
   }
+  // phase 1's v values (row 16w + jj, columns 16 vb + 4g ..): loaded here, since a
+  // load placed after the dv stores could not be moved above them
+  const int r = 16 * w + jj;
+  const int64_t trow = tok(t0 + min(r, len - 1), H, h) * D;
+  typename IO<TIO>::Raw4 v_raw[NJB];
+#pragma unroll
+  for (int vb = 0; vb < NJB; ++vb) v_raw[vb] = IO<TIO>::load_raw4(p.v, trow + 16 * vb + 4 * g);
 #pragma unroll
   for (int i = 0; i < NU; ++i) {
     const int pc = tid + i * kThreads, v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
@@ -583,8 +590,21 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   }
   __syncthreads();
 
+  // the high parts of S and dS for phase 2, in flight during phase 1; thread =
+  // (8 channels c8, rows vg + VG i), the same entries in both passes of phase 2
+  constexpr int NSL = D * D / 8 / kThreads;   // 16-byte pieces per thread of a [D][D] tile
+  constexpr int CG = D / 8, VG = kThreads / CG;
+  static_assert(NSL * VG == D, "one row set per thread");
+  const int c8 = (tid % CG) * 8, vg = tid / CG;
+  uint4 s_r[NSL], d_r[NSL];
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) {
+    const int64_t o = (ch * D + vg + VG * i) * D + c8;
+    s_r[i] = *reinterpret_cast<const uint4*>(p.S + o);
+    d_r[i] = *reinterpret_cast<const uint4*>(p.dS + o);
+  }
+
   // ---- phase 1: dY = A^T dU (lane owns dY[r][v .. v+3], r = 16w + jj); dv; sum dY*v ----
-  const int r = 16 * w + jj;
   const float br = beta_s[r];
   float dbeta_row = 0.f;
 #pragma unroll
@@ -594,11 +614,10 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_rk(dUsT, PC, 16 * vb, k0), frag_kc(As, PC, 16 * w, k0), a);
     const int v = 16 * vb + 4 * g;
     st_bf16x4(dYs + r * PD + v, a[0], a[1], a[2], a[3]);
-    const int64_t o = tok(t0 + min(r, len - 1), H, h) * D + v;
     float vv[4];
-    IO<TIO>::load4(p.v, o, vv);
+    IO<TIO>::unpack4(v_raw[vb], vv);
     dbeta_row += a[0] * vv[0] + a[1] * vv[1] + a[2] * vv[2] + a[3] * vv[3];
-    if (r < len) IO<TIO>::store4(p.dv, o, br * a[0], br * a[1], br * a[2], br * a[3]);
+    if (r < len) IO<TIO>::store4(p.dv, trow + v, br * a[0], br * a[1], br * a[2], br * a[3]);
   }
   __syncthreads();
 
@@ -607,23 +626,40 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   f32x4 aZ[NJB], aQ[NJB], aK[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) aZ[jb] = aQ[jb] = aK[jb] = zero4();
-  constexpr int NSL = D * D / 8 / kThreads;   // 16-byte pieces per thread of a [D][D] tile
+  // per-channel state sum sum_v S dS with S = high + low, dS likewise (fp32
+  // products), over this thread's entries: the high parts read back from LDS, the
+  // low parts from the registers that carry them there
+  float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // raw q, k rows (for kn, qn in fp32 below) and the M entries phase 3 needs,
+  // loaded during the second pass
+  typename IO<TIO>::Raw8 q_raw[NPASS], k_raw[NPASS];
+  uint2 mk_r[4];
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    const uint16_t* Sg = pass ? p.Slo : p.S;
-    const uint16_t* dSg = pass ? p.dSlo : p.dS;
-    uint4 s_r[NSL], d_r[NSL];
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
-      const int pc = tid + i * kThreads, row = pc / (D / 8), col = (pc % (D / 8)) * 8;
-      s_r[i] = *reinterpret_cast<const uint4*>(Sg + (ch * D + row) * D + col);
-      d_r[i] = *reinterpret_cast<const uint4*>(dSg + (ch * D + row) * D + col);
+      const int row = vg + VG * i;
+      *reinterpret_cast<uint4*>(Sx + row * PD + c8) = s_r[i];
+      *reinterpret_cast<uint4*>(dSx + row * PD + c8) = d_r[i];
     }
+    if (pass == 0) {
 #pragma unroll
-    for (int i = 0; i < NSL; ++i) {
-      const int pc = tid + i * kThreads, row = pc / (D / 8), col = (pc % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(Sx + row * PD + col) = s_r[i];
-      *reinterpret_cast<uint4*>(dSx + row * PD + col) = d_r[i];
+      for (int i = 0; i < NSL; ++i) {
+        const int64_t o = (ch * D + vg + VG * i) * D + c8;
+        s_r[i] = *reinterpret_cast<const uint4*>(p.Slo + o);
+        d_r[i] = *reinterpret_cast<const uint4*>(p.dSlo + o);
+      }
+    } else {
+#pragma unroll
+      for (int ps = 0; ps < NPASS; ++ps) {
+        const int rr = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
+        const int64_t o = qk_tok(p, t0 + min(rr, len - 1), h) * D + c0;
+        q_raw[ps] = IO<TIO>::load_raw8(p.q, o);
+        k_raw[ps] = IO<TIO>::load_raw8(p.k, o);
+      }
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+        mk_r[sb] = *reinterpret_cast<const uint2*>(p.Mk + (ch * C + r) * C + 16 * sb + 4 * g);
     }
     __syncthreads();
 #pragma unroll
@@ -639,28 +675,23 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         if (pass == 0) aK[jb] = mma(aD, frag_kc(UsTl, PC, 16 * w, k0), aK[jb]);
       }
     }
+    if (pass == 0) {   // the state sum over this thread's entries (high parts: its own LDS writes)
+#pragma unroll
+      for (int i = 0; i < NSL; ++i) {
+        const int row = vg + VG * i;
+        float a[8], b[8], c2[8], d2[8];
+        IO<bf16>::unpack8(*reinterpret_cast<const u32x4*>(Sx + row * PD + c8), a);
+        IO<bf16>::unpack8(*reinterpret_cast<const u32x4*>(&s_r[i]), b);
+        IO<bf16>::unpack8(*reinterpret_cast<const u32x4*>(dSx + row * PD + c8), c2);
+        IO<bf16>::unpack8(*reinterpret_cast<const u32x4*>(&d_r[i]), d2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc8[e] = fmaf(a[e] + b[e], c2[e] + d2[e], acc8[e]);
+      }
+    }
     __syncthreads();
   }
-  // ---- per-channel state sum sum_v S dS with S = high + low, dS likewise (fp32
-  // products): thread (row group, 8 channels), 16-byte loads (the tiles were just
-  // read, so these mostly hit L2); rows groups summed across lanes, then waves ----
+  // ---- the state sum: row groups summed across lanes, then waves ----
   {
-    constexpr int CG = D / 8, VG = kThreads / CG, NV = D / VG;
-    const int c8 = (tid % CG) * 8, vg = tid / CG;
-    float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int64_t o = (ch * D + vg + VG * i) * D + c8;
-      const u32x4 sh = *reinterpret_cast<const u32x4*>(p.S + o), sl = *reinterpret_cast<const u32x4*>(p.Slo + o);
-      const u32x4 dh = *reinterpret_cast<const u32x4*>(p.dS + o), dl = *reinterpret_cast<const u32x4*>(p.dSlo + o);
-      float a[8], b[8], c2[8], d2[8];
-      IO<bf16>::unpack8(sh, a);
-      IO<bf16>::unpack8(sl, b);
-      IO<bf16>::unpack8(dh, c2);
-      IO<bf16>::unpack8(dl, d2);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc8[e] = fmaf(a[e] + b[e], c2[e] + d2[e], acc8[e]);
-    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if constexpr (CG == 8) acc8[e] += dpp_f<0x128>(acc8[e]);   // lanes l and l + 8 of a row
@@ -677,9 +708,8 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   for (int ps = 0; ps < NPASS; ++ps) {
     const int rr = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     float qv[8], kv[8];
-    const int64_t o = qk_tok(p, t0 + min(rr, len - 1), h) * D + c0;
-    IO<TIO>::load8(p.q, o, qv);
-    IO<TIO>::load8(p.k, o, kv);
+    IO<TIO>::unpack8(q_raw[ps], qv);
+    IO<TIO>::unpack8(k_raw[ps], kv);
     const float m = rr < len ? 1.f : 0.f;
     const float fq = m * rq_s[rr], fk = m * rk_s[rr];
 #pragma unroll
@@ -689,6 +719,14 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       *reinterpret_cast<float4*>(Knf + rr * PG + c0 + e) =
           make_float4(kv[e] * fk, kv[e + 1] * fk, kv[e + 2] * fk, kv[e + 3] * fk);
     }
+  }
+  // Gamma rows for phase 4 (in flight during phase 3; region Y is rewritten below)
+  constexpr int NGL = C * D / 4 / kThreads;
+  float4 g_r[NGL];
+#pragma unroll
+  for (int i = 0; i < NGL; ++i) {
+    const int pc = tid + i * kThreads, rr = pc / (D / 4), c4 = (pc % (D / 4)) * 4;
+    g_r[i] = ld4(p.gam + (ch * C + rr) * D + c4);
   }
   // ---- phase 3: dP = dO U^T, dL = -dY U^T (U high + low); dM = beta dL ----
   float dmv[4][4], dpv[4][4];
@@ -709,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         G2 = mma(uh, by, G2);
         G2 = mma(ul, by, G2);
       }
-      const uint2 mk = *reinterpret_cast<const uint2*>(p.Mk + (ch * C + r) * C + s0);
+      const uint2 mk = mk_r[sb];
       const float Mv[4] = {__uint_as_float(mk.x << 16), __uint_as_float(mk.x & 0xffff0000u),
                            __uint_as_float(mk.y << 16), __uint_as_float(mk.y & 0xffff0000u)};
 #pragma unroll
@@ -723,14 +761,6 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         }
       }
     }
-  }
-  // Gamma rows for phase 4 (loads first; region Y is rewritten below)
-  constexpr int NGL = C * D / 4 / kThreads;
-  float4 g_r[NGL];
-#pragma unroll
-  for (int i = 0; i < NGL; ++i) {
-    const int pc = tid + i * kThreads, rr = pc / (D / 4), c4 = (pc % (D / 4)) * 4;
-    g_r[i] = ld4(p.gam + (ch * C + rr) * D + c4);
   }
   __syncthreads();
 #pragma unroll
