@@ -10,15 +10,17 @@
 // Between different 16-row blocks the factor splits at a reference row that lies
 // between them, E = exp(Gamma_r - Gamma_ref) exp(Gamma_ref - Gamma_s) with both
 // exponents <= 0 (Gamma never increases), so those blocks go to MFMA on operands
-// scaled in registers; inside a diagonal 16-row block E is evaluated exactly per
-// element.  The chunk recursions then take materialised Khat = kn e^(GamC - Gam),
+// scaled in registers; inside a diagonal 16-row block it splits at the block's
+// middle row (factors bounded by the half-spans of the block, fp32 MFMA), and a
+// channel whose half-span is too wide for that is evaluated exactly per element.  The chunk recursions then take materialised Khat = kn e^(GamC - Gam),
 // Qbar = scale qn e^Gam (high + low bf16 parts) and the per-channel chunk decay.
 //
 //   k_prep_kda    per (chunk, head): norms, gate and its cumsum, M and P, the
 //                 UT/WY inverse, W and U', Khat / Qbar tiles, chunk decay.
 //   k_grads_kda   per (chunk, head): the chunk-local gradients; the pairwise
 //                 terms are four E-weighted products (row and column sides of
-//                 dM o E and dP o E) on K = 16 MFMAs plus exact diagonal blocks.
+//                 dM o E and dP o E) on K = 16 MFMAs plus the diagonal blocks
+//                 on fp32 MFMA (exactly where their decay is too steep).
 //   k_finish_kda  per (chunk, head): L2-norm and sigmoid backward, the per-channel
 //                 reverse cumsum of dGamma plus the chunk-total term, the gate
 //                 backward, and per-chunk partial sums of dA_log and ddt_bias.
@@ -43,9 +45,10 @@ namespace {
 
 typedef short s16x4v __attribute__((ext_vector_type(4)));
 
-// largest in-block decay span (Gamma of the first row minus the last, per channel)
-// for which a diagonal 16-row block is factored at its first row: both factors
-// and their products stay normal fp32 numbers far from overflow
+// largest exponent of a factor of the in-block decay (per channel) for which a
+// diagonal 16-row block is factored at its middle row: the factors e^(Gam_r - Gam_m)
+// and e^(Gam_m - Gam_s) and their products stay normal fp32 numbers far from
+// overflow and underflow
 constexpr float kSpanMax = 60.f;
 
 // v_mfma_f32_16x16x16_bf16: A lane (m = l % 16, k = 4 (l / 16) .. +3),
@@ -258,88 +261,74 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
       st_bf16x4(p.Mk + (ch * C + r) * C + s0, Mv[0], Mv[1], Mv[2], Mv[3]);
     }
   }
-  // --- diagonal blocks: wave R's block factored at its first row f,
-  // E_rs = e^(Gam_r - Gam_f) e^(Gam_f - Gam_s), on 16x16x4 fp32 MFMA with fp32
-  // operands (contraction over channels; lane group g takes channels g D/4 .. +D/4),
-  // while the block's decay span Gam_f - Gam_(f+15) stays below kSpanMax in every
-  // channel; otherwise exactly, thread owns row r and four columns s ---
-  bool diag_fact;
+  // --- diagonal blocks: wave R's block factored at its middle row m = f + 8,
+  // E_rs = e^(Gam_r - Gam_m) e^(Gam_m - Gam_s), on 16x16x4 fp32 MFMA with fp32
+  // operands (contraction over channels; lane group g takes channels g D/4 .. +D/4).
+  // Every factor's exponent is bounded by the larger half-span of the block in its
+  // channel, max(Gam_f - Gam_m, Gam_m - Gam_(f+15)); a channel where that reaches
+  // kSpanMax is left out of the products (its operands are zero) and added exactly,
+  // one channel at a time, thread owns row r and four columns s ---
   {
-    const int f = 16 * w, rr = f + jj;
-    bool wide = false;
+    const int f = 16 * w, m = f + 8, rr = f + jj;
+    auto wide_ch = [&](int cc) {
+      const float gm = Gs[m * PG + cc];
+      return fmaxf(Gs[f * PG + cc] - gm, gm - Gs[(f + 15) * PG + cc]) >= kSpanMax;
+    };
+    // wave-uniform masks of the wide channels: lane l tests channels l and 64 + l
+    const uint64_t wide0 = __builtin_amdgcn_ballot_w64(wide_ch(l));
+    uint64_t wide1 = 0;
+    if constexpr (D > 64) wide1 = __builtin_amdgcn_ballot_w64(wide_ch(64 + l));
+    f32x4 aM = zero4(), aP = zero4();
 #pragma unroll
-    for (int kq = 0; kq < D / 16; ++kq) {   // this lane's 32 (D = 128) or 16 (D = 64) channels
-      const float4 a4 = ld4(Gs + f * PG + (D / 4) * g + 4 * kq), b4 = ld4(Gs + (f + 15) * PG + (D / 4) * g + 4 * kq);
-      wide |= a4.x - b4.x >= kSpanMax || a4.y - b4.y >= kSpanMax || a4.z - b4.z >= kSpanMax || a4.w - b4.w >= kSpanMax;
-    }
-    diag_fact = __builtin_amdgcn_ballot_w64(wide) == 0;
-    if (diag_fact) {
-      f32x4 aM = zero4(), aP = zero4();
+    for (int kq = 0; kq < D / 16; ++kq) {
+      const int c4 = (D / 4) * g + 4 * kq;
+      const float4 gr4 = ld4(Gs + rr * PG + c4), gm4 = ld4(Gs + m * PG + c4);
+      const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Ks + rr * PD + c4);
+      const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qs + rr * PD + c4);
 #pragma unroll
-      for (int kq = 0; kq < D / 16; ++kq) {
-        const int c4 = (D / 4) * g + 4 * kq;
-        const float4 gr4 = ld4(Gs + rr * PG + c4), gf4 = ld4(Gs + f * PG + c4);
-        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Ks + rr * PD + c4);
-        const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qs + rr * PD + c4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ea = fast_exp(el(gr4, e) - el(gf4, e));   // a <= 1 (row as r)
-          const float eb = fast_exp(el(gf4, e) - el(gr4, e));   // b >= 1 (row as s)
-          const float kn = float(k4[e]);
-          aM = mma_f32(kn * eb, kn * ea, aM);
-          aP = mma_f32(kn * eb, float(q4[e]) * ea, aP);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int cc = c4 + e;
+        const bool wd = ((cc < 64 ? wide0 >> cc : wide1 >> (cc & 63)) & 1) != 0;
+        const float ea = wd ? 0.f : fast_exp(el(gr4, e) - el(gm4, e));   // row as r
+        const float eb = wd ? 0.f : fast_exp(el(gm4, e) - el(gr4, e));   // row as s
+        const float kn = float(k4[e]);
+        aM = mma_f32(kn * eb, kn * ea, aM);
+        aP = mma_f32(kn * eb, float(q4[e]) * ea, aP);
       }
-      const int s0 = f + 4 * g;
-      const float br = beta_s[rr];
-      float Mv[4], Pv[4], Lv[4];
+    }
+    const int s0 = f + 4 * g;
+    // the wide channels, exactly: E = exp(-|Gamma_r - Gamma_s|) (Gamma does not increase)
+    uint64_t rest0 = wide0, rest1 = wide1;
+    while (rest0 | rest1) {
+      int cc;
+      if (rest0) {
+        cc = __builtin_ctzll(rest0);
+        rest0 &= rest0 - 1;
+      } else {
+        cc = 64 + __builtin_ctzll(rest1);
+        rest1 &= rest1 - 1;
+      }
+      const float gr = Gs[rr * PG + cc], kr = float(Ks[rr * PD + cc]), qr = float(Qs[rr * PD + cc]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int s = s0 + i;
-        Mv[i] = s < rr ? aM[i] : 0.f;
-        Pv[i] = s <= rr ? scale * aP[i] : 0.f;
-        Lv[i] = br * Mv[i];
-      }
-      *reinterpret_cast<float4*>(Lf + rr * PL + s0) = make_float4(Lv[0], Lv[1], Lv[2], Lv[3]);
-      st_bf16x4(p.P + (ch * C + rr) * C + s0, Pv[0], Pv[1], Pv[2], Pv[3]);
-      st_bf16x4(p.Mk + (ch * C + rr) * C + s0, Mv[0], Mv[1], Mv[2], Mv[3]);
-    }
-  }
-  if (!diag_fact)
-  {
-    const int blk = tid >> 6, r = 16 * blk + ((tid >> 2) & 15), s0 = 16 * blk + 4 * (tid & 3);
-    float Mv[4] = {0.f, 0.f, 0.f, 0.f}, Pv[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int c4 = 0; c4 < D; c4 += 4) {
-      const float4 gr = ld4(Gs + r * PG + c4);
-      const bf16x4 kr = *reinterpret_cast<const bf16x4*>(Ks + r * PD + c4);
-      const bf16x4 qr = *reinterpret_cast<const bf16x4*>(Qs + r * PD + c4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = s0 + i;
-        const float4 gs = ld4(Gs + s * PG + c4);
-        const bf16x4 ks = *reinterpret_cast<const bf16x4*>(Ks + s * PD + c4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // Gamma does not increase, so exp(-|Gamma_r - Gamma_s|) is E for either order
-          const float E = fast_exp(-fabsf(el(gr, e) - el(gs, e)));
-          const float kk = float(ks[e]) * E;
-          Mv[i] += float(kr[e]) * kk;
-          Pv[i] += float(qr[e]) * kk;
-        }
+        const int sc = s0 + i;
+        const float kk = float(Ks[sc * PD + cc]) * fast_exp(-fabsf(gr - Gs[sc * PG + cc]));
+        aM[i] += kr * kk;
+        aP[i] += qr * kk;
       }
     }
-    const float br = beta_s[r];
-    float Lv[4];
+    const float br = beta_s[rr];
+    float Mv[4], Pv[4], Lv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int s = s0 + i;
-      Mv[i] = s < r ? Mv[i] : 0.f;
-      Pv[i] = s <= r ? scale * Pv[i] : 0.f;
+      const int sc = s0 + i;
+      Mv[i] = sc < rr ? aM[i] : 0.f;
+      Pv[i] = sc <= rr ? scale * aP[i] : 0.f;
       Lv[i] = br * Mv[i];
     }
-    *reinterpret_cast<float4*>(Lf + r * PL + s0) = make_float4(Lv[0], Lv[1], Lv[2], Lv[3]);
-    st_bf16x4(p.P + (ch * C + r) * C + s0, Pv[0], Pv[1], Pv[2], Pv[3]);
-    st_bf16x4(p.Mk + (ch * C + r) * C + s0, Mv[0], Mv[1], Mv[2], Mv[3]);
+    *reinterpret_cast<float4*>(Lf + rr * PL + s0) = make_float4(Lv[0], Lv[1], Lv[2], Lv[3]);
+    st_bf16x4(p.P + (ch * C + rr) * C + s0, Pv[0], Pv[1], Pv[2], Pv[3]);
+    st_bf16x4(p.Mk + (ch * C + rr) * C + s0, Mv[0], Mv[1], Mv[2], Mv[3]);
   }
   __syncthreads();
 
@@ -921,17 +910,17 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         dgm[jb][i] -= el(kr, i) * x;
       }
     }
-    // diagonal block w, factored at its first row f = 16w: E_rt = e^(Gam_r - Gam_f)
-    // e^(Gam_f - Gam_t), the first factor <= 1, the second >= 1.  The products run
-    // on fp32 MFMA (16x16x4, four k-steps) with fp32 operands, so they keep the
-    // exact path's accuracy.  Valid while the block's decay span Gam_f - Gam_(f+15)
-    // stays below kSpanMax for all 16 channels of this tile (no overflow, no
-    // underflow of the small factor); otherwise the tile takes the exact
-    // per-element path below.
+    // diagonal block w, factored at its middle row m = 16w + 8: E_rt =
+    // e^(Gam_r - Gam_m) e^(Gam_m - Gam_t).  The products run on fp32 MFMA (16x16x4,
+    // four k-steps) with fp32 operands, so they keep the exact path's accuracy.
+    // Valid while the block's larger half-span max(Gam_f - Gam_m, Gam_m - Gam_(f+15))
+    // (f = 16w, the bound of every factor's exponent) stays below kSpanMax for all
+    // 16 channels of this tile (no overflow, no underflow of the small factors);
+    // otherwise the tile takes the exact per-element path below.
     {
-      const int f = 16 * w;
-      const float gf = Gs[f * PG + cm];
-      const bool wide = gf - Gs[(f + 15) * PG + cm] >= kSpanMax;
+      const int f = 16 * w, m = f + 8;
+      const float gm = Gs[m * PG + cm];
+      const bool wide = fmaxf(Gs[f * PG + cm] - gm, gm - Gs[(f + 15) * PG + cm]) >= kSpanMax;
       fact_ok[jb] = __builtin_amdgcn_ballot_w64(wide) == 0;
       if (fact_ok[jb]) {
         f32x4 t1 = zero4(), t2 = zero4(), t3 = zero4(), t4 = zero4();
@@ -939,18 +928,18 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         for (int kk = 0; kk < 4; ++kk) {
           const int s = f + 4 * kk + g;   // A: m = channel cm, k = s - f
           const float gs = Gs[s * PG + cm];
-          const float kb = Knf[s * PG + cm] * fast_exp(gf - gs);   // kn_s b_s
-          const float d = fast_exp(gs - gf);                        // a_s
+          const float kb = Knf[s * PG + cm] * fast_exp(gm - gs);   // kn_s b_s
+          const float d = fast_exp(gs - gm);                        // a_s
           t1 = mma_f32(kb, dm_row[kk], t1);
           t3 = mma_f32(kb, dp_row[kk], t3);
           t2 = mma_f32(Knf[s * PG + cm] * d, dm_col[kk], t2);
           t4 = mma_f32(Qnf[s * PG + cm] * d, dp_col[kk], t4);
         }
-        const float4 gfv = ld4(Gs + f * PG + j);
+        const float4 gmv = ld4(Gs + m * PG + j);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float arow = fast_exp(Gr[jb][i] - el(gfv, i));   // a_r <= 1
-          const float bcol = fast_exp(el(gfv, i) - Gr[jb][i]);   // b_r >= 1
+          const float arow = fast_exp(Gr[jb][i] - el(gmv, i));   // a_r
+          const float bcol = fast_exp(el(gmv, i) - Gr[jb][i]);   // b_r
           const float x1 = t1[i] * arow, x3 = scale * t3[i] * arow;
           const float x24 = (t2[i] + scale * t4[i]) * bcol;
           dkn[jb][i] += x1 + x24;
@@ -1061,6 +1050,17 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
     braw = IO<TIO>::load1(p.b, tok(t0 + min(l, len - 1), H, h));
     dbs = p.dbeta[ch * C + l];
   }
+  // row and channel scalars, here too: a load placed after the dq, dk stores
+  // below could not be moved above them
+  float rq_r[NPASS], rk_r[NPASS];
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int r = ps * RPP + tid / TPR;
+    rq_r[ps] = p.rho[ch * 3 * C + r];
+    rk_r[ps] = p.rho[ch * 3 * C + C + r];
+  }
+  const float dgamc = p.dgamc[ch * D + tid % D];
+  const float a_log = p.A_log[h];
 
   // ---- L2-norm backward: dq = rq (dqn - qn <qn, dqn>), dk likewise (K1 page, 3.3) ----
 #pragma unroll
@@ -1068,7 +1068,7 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
     const int r = ps * RPP + tid / TPR;
     const bool ok = r < len;
     const float m = ok ? 1.f : 0.f;
-    const float rq = m * p.rho[ch * 3 * C + r], rk = m * p.rho[ch * 3 * C + C + r];
+    const float rq = m * rq_r[ps], rk = m * rk_r[ps];
     float q[8], k[8], g8[8];
     IO<TIO>::unpack8(qraw[ps], q);
     IO<TIO>::unpack8(kraw[ps], k);
@@ -1121,10 +1121,10 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
   for (int i = RP - 1; i >= 0; --i) x[i] = dG_s[(part * RP + i) * PG + cc] + (i < RP - 1 ? x[i + 1] : 0.f);
   tot_s[part][cc] = x[0];
   __syncthreads();
-  float after = p.dgamc[ch * D + cc];
+  float after = dgamc;
 #pragma unroll
   for (int q = NPART - 1; q > 0; --q) after += q > part ? tot_s[q][cc] : 0.f;
-  const float ea = fast_exp(p.A_log[h]);
+  const float ea = fast_exp(a_log);
   float pd = 0.f, pa = 0.f;
 #pragma unroll
   for (int i = 0; i < RP; ++i) {
