@@ -775,42 +775,15 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   }
   __syncthreads();
 
-  // ---- fold the state-side terms (lane owns (r, c = 16 jb + 4g + i)) ----
-  // Kbar = kn e^Gam (dKbar = -beta Z), Khat = kn e^(GamC - Gam), Qbar = scale qn e^Gam
-  f32x4 dkn[NJB], dqn[NJB], dgm[NJB], Gr[NJB];
-#pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
-    const int j = 16 * jb + 4 * g;
-    const float4 kb = ld4(Knf + r * PG + j), qb = ld4(Qnf + r * PG + j);
-    const float4 gr = ld4(Gs + r * PG + j), gC = ld4(Gs + (C - 1) * PG + j);
-    float csum[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float kn = el(kb, i), qn = el(qb, i);
-      const float eg = fast_exp(el(gr, i)), eh = fast_exp(el(gC, i) - el(gr, i));
-      const float z = aZ[jb][i], dkh = aK[jb][i], dqb = aQ[jb][i];
-      dgm[jb][i] = -br * z * kn * eg - dkh * kn * eh + dqb * scale * qn * eg;
-      dbeta_row -= kn * eg * z;
-      csum[i] = dkh * kn * eh;
-      dkn[jb][i] = -br * z * eg + dkh * eh;
-      dqn[jb][i] = scale * dqb * eg;
-      Gr[jb][i] = el(gr, i);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float col = row16_sum(csum[i]);   // over the 16 rows of this wave
-      if (jj == 0) csum_s[w][j + i] = col;
-    }
-  }
-
   // ---- phase 4: pairwise terms ----
   //   X1_rc = sum_{s<r} dM_rs kn_sc E_rsc     -> dkn_r, dGamma_r (+ kn_r X1)
   //   X3_rc = scale sum_{s<=r} dP_rs kn_sc E  -> dqn_r, dGamma_r (+ qn_r X3)
   //   X2_sc = sum_{r>s} dM_rs kn_rc E_rsc     -> dkn_s, dGamma_s (- kn_s X2)
   //   X4_sc = scale sum_{r>=s} dP_rs qn_rc E  -> dkn_s, dGamma_s (- kn_s X4)
   // wave w owns the 16 rows of block w on both sides; products with split operands
-  // take a_h b_h + a_h b_l + a_l b_h.
-  bool fact_ok[NJB];
+  // take a_h b_h + a_h b_l + a_l b_h.  One 16-channel tile at a time: its state-side
+  // terms are folded in first, and its results are stored at the end of its step,
+  // so that only one tile's gradients are held in registers.
   // K = 16 B fragments of the off-diagonal block pairs (the same for every channel
   // tile): row side blocks sb < w, column side blocks rb > w
   bf16x4 fr_mh[3], fr_ml[3], fr_ph[3], fr_pl[3], fc_mh[3], fc_ml[3], fc_ph[3], fc_pl[3];
@@ -854,6 +827,30 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     const int cm = c0 + jj;          // channel of this lane in an A fragment (m = lane % 16)
     const int j = c0 + 4 * g;        // channels of this lane in the outputs
     const float4 kr = ld4(Knf + r * PG + j), qr = ld4(Qnf + r * PG + j);
+    // fold the state-side terms (lane owns (r, c = j + i)): Kbar = kn e^Gam
+    // (dKbar = -beta Z), Khat = kn e^(GamC - Gam), Qbar = scale qn e^Gam
+    f32x4 dkn, dqn, dgm, Gr;
+    {
+      const float4 gr = ld4(Gs + r * PG + j), gC = ld4(Gs + (C - 1) * PG + j);
+      float csum[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float kn = el(kr, i), qn = el(qr, i);
+        const float eg = fast_exp(el(gr, i)), eh = fast_exp(el(gC, i) - el(gr, i));
+        const float z = aZ[jb][i], dkh = aK[jb][i], dqb = aQ[jb][i];
+        dgm[i] = -br * z * kn * eg - dkh * kn * eh + dqb * scale * qn * eg;
+        dbeta_row -= kn * eg * z;
+        csum[i] = dkh * kn * eh;
+        dkn[i] = -br * z * eg + dkh * eh;
+        dqn[i] = scale * dqb * eg;
+        Gr[i] = el(gr, i);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float col = row16_sum(csum[i]);   // over the 16 rows of this wave
+        if (jj == 0) csum_s[w][j + i] = col;
+      }
+    }
     // row side, earlier blocks sb < w: reference = last row of block sb
 #pragma unroll
     for (int sb = 0; sb < 3; ++sb) {
@@ -874,11 +871,11 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       const float4 gend = ld4(Gs + se * PG + j);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float mlt = fast_exp(Gr[jb][i] - el(gend, i));
+        const float mlt = fast_exp(Gr[i] - el(gend, i));
         const float x1 = t1[i] * mlt, x3 = scale * t3[i] * mlt;
-        dkn[jb][i] += x1;
-        dqn[jb][i] += x3;
-        dgm[jb][i] += el(kr, i) * x1 + el(qr, i) * x3;
+        dkn[i] += x1;
+        dqn[i] += x3;
+        dgm[i] += el(kr, i) * x1 + el(qr, i) * x3;
       }
     }
     // column side, later blocks rb > w: reference = first row of block rb
@@ -904,12 +901,13 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       const float4 gsv = ld4(Gs + rs * PG + j);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float mlt = fast_exp(el(gsv, i) - Gr[jb][i]);
+        const float mlt = fast_exp(el(gsv, i) - Gr[i]);
         const float x = (t2[i] + scale * t4[i]) * mlt;
-        dkn[jb][i] += x;
-        dgm[jb][i] -= el(kr, i) * x;
+        dkn[i] += x;
+        dgm[i] -= el(kr, i) * x;
       }
     }
+    bool fact_ok;
     // diagonal block w, factored at its middle row m = 16w + 8: E_rt =
     // e^(Gam_r - Gam_m) e^(Gam_m - Gam_t).  The products run on fp32 MFMA (16x16x4,
     // four k-steps) with fp32 operands, so they keep the exact path's accuracy.
@@ -921,8 +919,8 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       const int f = 16 * w, m = f + 8;
       const float gm = Gs[m * PG + cm];
       const bool wide = fmaxf(Gs[f * PG + cm] - gm, gm - Gs[(f + 15) * PG + cm]) >= kSpanMax;
-      fact_ok[jb] = __builtin_amdgcn_ballot_w64(wide) == 0;
-      if (fact_ok[jb]) {
+      fact_ok = __builtin_amdgcn_ballot_w64(wide) == 0;
+      if (fact_ok) {
         f32x4 t1 = zero4(), t2 = zero4(), t3 = zero4(), t4 = zero4();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -938,59 +936,42 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         const float4 gmv = ld4(Gs + m * PG + j);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float arow = fast_exp(Gr[jb][i] - el(gmv, i));   // a_r
-          const float bcol = fast_exp(el(gmv, i) - Gr[jb][i]);   // b_r
+          const float arow = fast_exp(Gr[i] - el(gmv, i));   // a_r
+          const float bcol = fast_exp(el(gmv, i) - Gr[i]);   // b_r
           const float x1 = t1[i] * arow, x3 = scale * t3[i] * arow;
           const float x24 = (t2[i] + scale * t4[i]) * bcol;
-          dkn[jb][i] += x1 + x24;
-          dqn[jb][i] += x3;
-          dgm[jb][i] += el(kr, i) * (x1 - x24) + el(qr, i) * x3;
+          dkn[i] += x1 + x24;
+          dqn[i] += x3;
+          dgm[i] += el(kr, i) * (x1 - x24) + el(qr, i) * x3;
         }
       }
     }
-  }
-  // diagonal block w, tiles whose decay span is too wide for the factored form,
-  // exactly: E = exp(-|Gamma_r - Gamma_t|) for both orders
-  float4 kr_d[NJB], qr_d[NJB];
+    // a tile whose decay is too steep for the factored form, exactly:
+    // E = exp(-|Gamma_r - Gamma_t|) for both orders
+    if (!fact_ok) {
+      for (int t = 16 * w; t < 16 * w + 16; ++t) {
+        const float mrt = float(dMh[r * PC + t]) + float(dMl[r * PC + t]);
+        const float prt = scale * (float(dPh[r * PC + t]) + float(dPl[r * PC + t]));
+        const float mtr = float(dMh[t * PC + r]) + float(dMl[t * PC + r]);
+        const float ptr = scale * (float(dPh[t * PC + r]) + float(dPl[t * PC + r]));
+        const float4 gt = ld4(Gs + t * PG + j);
+        const float4 kt = ld4(Knf + t * PG + j), qt = ld4(Qnf + t * PG + j);
 #pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
-    kr_d[jb] = ld4(Knf + r * PG + 16 * jb + 4 * g);
-    qr_d[jb] = ld4(Qnf + r * PG + 16 * jb + 4 * g);
-  }
-  bool any_exact = false;
-#pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) any_exact |= !fact_ok[jb];
-  if (any_exact)
-  for (int t = 16 * w; t < 16 * w + 16; ++t) {
-    const float mrt = float(dMh[r * PC + t]) + float(dMl[r * PC + t]);
-    const float prt = scale * (float(dPh[r * PC + t]) + float(dPl[r * PC + t]));
-    const float mtr = float(dMh[t * PC + r]) + float(dMl[t * PC + r]);
-    const float ptr = scale * (float(dPh[t * PC + r]) + float(dPl[t * PC + r]));
-#pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
-      if (fact_ok[jb]) continue;
-      const int j = 16 * jb + 4 * g;
-      const float4 gt = ld4(Gs + t * PG + j);
-      const float4 kt = ld4(Knf + t * PG + j), qt = ld4(Qnf + t * PG + j);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float E = fast_exp(-fabsf(Gr[jb][i] - el(gt, i)));
-        const float ke = el(kt, i) * E, qe = el(qt, i) * E;
-        const float x1 = mrt * ke, x3 = prt * ke, x24 = mtr * ke + ptr * qe;
-        dkn[jb][i] += x1 + x24;
-        dqn[jb][i] += x3;
-        dgm[jb][i] += el(kr_d[jb], i) * (x1 - x24) + el(qr_d[jb], i) * x3;
+        for (int i = 0; i < 4; ++i) {
+          const float E = fast_exp(-fabsf(Gr[i] - el(gt, i)));
+          const float ke = el(kt, i) * E, qe = el(qt, i) * E;
+          const float x1 = mrt * ke, x3 = prt * ke, x24 = mtr * ke + ptr * qe;
+          dkn[i] += x1 + x24;
+          dqn[i] += x3;
+          dgm[i] += el(kr, i) * (x1 - x24) + el(qr, i) * x3;
+        }
       }
     }
-  }
-  // ---- stores ----
-#pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
-    const int j = 16 * jb + 4 * g;
+    // this tile's results
     const int64_t o = (ch * C + r) * D + j;
-    *reinterpret_cast<float4*>(p.dqn + o) = make_float4(dqn[jb][0], dqn[jb][1], dqn[jb][2], dqn[jb][3]);
-    *reinterpret_cast<float4*>(p.dkn + o) = make_float4(dkn[jb][0], dkn[jb][1], dkn[jb][2], dkn[jb][3]);
-    *reinterpret_cast<float4*>(p.dgam + o) = make_float4(dgm[jb][0], dgm[jb][1], dgm[jb][2], dgm[jb][3]);
+    *reinterpret_cast<float4*>(p.dqn + o) = make_float4(dqn[0], dqn[1], dqn[2], dqn[3]);
+    *reinterpret_cast<float4*>(p.dkn + o) = make_float4(dkn[0], dkn[1], dkn[2], dkn[3]);
+    *reinterpret_cast<float4*>(p.dgam + o) = make_float4(dgm[0], dgm[1], dgm[2], dgm[3]);
   }
   dbeta_row += __shfl_xor(dbeta_row, 16, 64);
   dbeta_row += __shfl_xor(dbeta_row, 32, 64);
