@@ -992,10 +992,7 @@ template <int D, typename TIO>
 __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
   using Dm = Dims<D>;
   constexpr int TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS;
-  constexpr int PG = D + 4;
   constexpr int NPART = kThreads / D, RP = C / NPART;   // per-channel scans: row ranges per channel
-  __shared__ __attribute__((aligned(16))) float dG_s[C * PG];   // dGamma [r][c]
-  __shared__ __attribute__((aligned(16))) float X_s[C * PG];    // g_raw + dt_bias [r][c]
   __shared__ float tot_s[NPART][D], pd_s[NPART][D], pa_s[kThreads / 64];
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkEntry ce = p.ctab[c];
@@ -1004,44 +1001,37 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
   const int64_t ch = int64_t(h) * p.NC + c;
   const int H = p.H;
   const int c0 = (tid % TPR) * 8;
+  const int cc = tid % D, part = tid / D;
 
-  // ---- every load first (their latencies overlap): q, k, dqn, dkn, dGamma and
-  // the raw gate rows, beta logits ----
-  typename IO<TIO>::Raw8 qraw[NPASS], kraw[NPASS], graw[NPASS];
-  float4 dq4[NPASS][2], dk4[NPASS][2], dg4[NPASS][2];
+  // ---- the L2-norm backward's loads first (their latencies overlap), row sweeps
+  // of 8 channels a thread: q, k, dqn, dkn, the row norms; the gate's per-channel
+  // loads follow once these registers are free (the workgroups sharing the CU
+  // keep the memory busy meanwhile) ----
+  typename IO<TIO>::Raw8 qraw[NPASS], kraw[NPASS];
+  float4 dq4[NPASS][2], dk4[NPASS][2];
+  float rq_r[NPASS], rk_r[NPASS];
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR;
-    const int64_t o = tok(t0 + min(r, len - 1), H, h) * D + c0;
     const int64_t qo = qk_tok(p, t0 + min(r, len - 1), h) * D + c0;
     const int64_t wo = (ch * C + r) * D + c0;
     qraw[ps] = IO<TIO>::load_raw8(p.q, qo);
     kraw[ps] = IO<TIO>::load_raw8(p.k, qo);
-    graw[ps] = IO<TIO>::load_raw8(p.g, o);
     dq4[ps][0] = ld4(p.dqn + wo);
     dq4[ps][1] = ld4(p.dqn + wo + 4);
     dk4[ps][0] = ld4(p.dkn + wo);
     dk4[ps][1] = ld4(p.dkn + wo + 4);
-    dg4[ps][0] = ld4(p.dgam + wo);
-    dg4[ps][1] = ld4(p.dgam + wo + 4);
+    rq_r[ps] = p.rho[ch * 3 * C + r];
+    rk_r[ps] = p.rho[ch * 3 * C + C + r];
   }
-  const float4 bias0 = ld4(p.dt_bias + h * D + c0), bias1 = ld4(p.dt_bias + h * D + c0 + 4);
+  const float bias = p.dt_bias[h * D + cc];
+  const float dgamc = p.dgamc[ch * D + cc];
+  const float a_log = p.A_log[h];
   float braw = 0.f, dbs = 0.f;
   if (w == kThreads / 64 - 1) {
     braw = IO<TIO>::load1(p.b, tok(t0 + min(l, len - 1), H, h));
     dbs = p.dbeta[ch * C + l];
   }
-  // row and channel scalars, here too: a load placed after the dq, dk stores
-  // below could not be moved above them
-  float rq_r[NPASS], rk_r[NPASS];
-#pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int r = ps * RPP + tid / TPR;
-    rq_r[ps] = p.rho[ch * 3 * C + r];
-    rk_r[ps] = p.rho[ch * 3 * C + C + r];
-  }
-  const float dgamc = p.dgamc[ch * D + tid % D];
-  const float a_log = p.A_log[h];
 
   // ---- L2-norm backward: dq = rq (dqn - qn <qn, dqn>), dk likewise (K1 page, 3.3) ----
 #pragma unroll
@@ -1050,10 +1040,9 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
     const bool ok = r < len;
     const float m = ok ? 1.f : 0.f;
     const float rq = m * rq_r[ps], rk = m * rk_r[ps];
-    float q[8], k[8], g8[8];
+    float q[8], k[8];
     IO<TIO>::unpack8(qraw[ps], q);
     IO<TIO>::unpack8(kraw[ps], k);
-    IO<TIO>::unpack8(graw[ps], g8);
     const float dq[8] = {dq4[ps][0].x, dq4[ps][0].y, dq4[ps][0].z, dq4[ps][0].w,
                          dq4[ps][1].x, dq4[ps][1].y, dq4[ps][1].z, dq4[ps][1].w};
     const float dk[8] = {dk4[ps][0].x, dk4[ps][0].y, dk4[ps][0].z, dk4[ps][0].w,
@@ -1078,29 +1067,29 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
       IO<TIO>::store8(p.dq, tok(t0 + r, H, h) * D + c0, oq);
       IO<TIO>::store8(p.dk, tok(t0 + r, H, h) * D + c0, ok8);
     }
-    *reinterpret_cast<float4*>(dG_s + r * PG + c0) = dg4[ps][0];
-    *reinterpret_cast<float4*>(dG_s + r * PG + c0 + 4) = dg4[ps][1];
-    *reinterpret_cast<float4*>(X_s + r * PG + c0) =
-        make_float4(g8[0] + bias0.x, g8[1] + bias0.y, g8[2] + bias0.z, g8[3] + bias0.w);
-    *reinterpret_cast<float4*>(X_s + r * PG + c0 + 4) =
-        make_float4(g8[4] + bias1.x, g8[5] + bias1.y, g8[6] + bias1.z, g8[7] + bias1.w);
+  }
+  // per channel (thread = channel cc, row range part): dGamma and the raw gate
+  float dg_r[RP], x_r[RP];
+#pragma unroll
+  for (int i = 0; i < RP; ++i) {
+    const int r = part * RP + i;
+    dg_r[i] = p.dgam[(ch * C + r) * D + cc];
+    x_r[i] = IO<TIO>::load1(p.g, tok(t0 + min(r, len - 1), H, h) * D + cc);
   }
   if (w == kThreads / 64 - 1) {
     const float bt = sigmoidf(braw);
     if (l < len) IO<TIO>::store1(p.db, tok(t0 + l, H, h), dbs * bt * (1.f - bt));
   }
-  __syncthreads();
 
   // ---- per channel: dlam_r = sum_{r' >= r} dGamma_r' + dGamma_C (FlashKDA
   // backward page, section 5), then through the gate function: softplus form
   // dx = dlam (-e^A sigmoid(x)), d/dA_log: dlam lambda; bounded sigmoid form
-  // (z = e^A x) dx = dlam gate_scale sigma(z) (1 - sigma(z)) e^A, d/dA_log: dx x.  Thread = (channel, one of NPART row ranges):
-  // a suffix scan of its range in registers plus the totals of the ranges after it ----
-  const int cc = tid % D, part = tid / D;
-  float x[RP];
+  // (z = e^A x) dx = dlam gate_scale sigma(z) (1 - sigma(z)) e^A, d/dA_log: dx x.
+  // Thread = (channel, one of NPART row ranges): a suffix scan of its range in
+  // registers plus the totals of the ranges after it ----
 #pragma unroll
-  for (int i = RP - 1; i >= 0; --i) x[i] = dG_s[(part * RP + i) * PG + cc] + (i < RP - 1 ? x[i + 1] : 0.f);
-  tot_s[part][cc] = x[0];
+  for (int i = RP - 2; i >= 0; --i) dg_r[i] += dg_r[i + 1];
+  tot_s[part][cc] = dg_r[0];
   __syncthreads();
   float after = dgamc;
 #pragma unroll
@@ -1111,8 +1100,8 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
   for (int i = 0; i < RP; ++i) {
     const int r = part * RP + i;
     if (r < len) {
-      const float acc = x[i] + after;
-      const float xg = X_s[r * PG + cc];
+      const float acc = dg_r[i] + after;
+      const float xg = x_r[i] + bias;
       float dx;
       if (p.gate_fn) {
         const float sz = sigmoidf(ea * xg);
