@@ -33,14 +33,19 @@ GATE_NAMES = {0: "scalar", 1: "channel", 2: "channel_sigmoid"}
 METRIC = "gated-delta-rule bwd tokens/s + ms/bwd at T=32k,H=16,D=128 bf16; MFMA %"
 CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 # HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by a
-# 1 GiB copy; profiles/gdn_t32768_h16_d128.md), valid only for the kernel
-# sources they were taken on: (workload, stage, sha256 prefix) -> bytes.
+# 1 GiB copy; profiles/gdn_t32768_h16_d128.md, profiles/kda_t32768_h16_d128.md),
+# valid only for the kernel sources they were taken on:
+# (workload, stage, sha256 prefix) -> bytes.
 MEASURED_TRAFFIC = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "968d4d3c69b4"): 0.716e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "968d4d3c69b4"): 1.690e9,
-    ("gdn_bf16_t32768_h16_d128", "grads", "968d4d3c69b4"): 1.855e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "968d4d3c69b4"): 0.747e9,
-    ("gdn_bf16_t32768_h16_d128", "output", "968d4d3c69b4"): 0.745e9,
+    ("gdn_bf16_t32768_h16_d128", "prep", "6bdec0c3fa29"): 0.716e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "6bdec0c3fa29"): 1.690e9,
+    ("gdn_bf16_t32768_h16_d128", "grads", "6bdec0c3fa29"): 1.855e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "6bdec0c3fa29"): 0.747e9,
+    ("gdn_bf16_t32768_h16_d128", "output", "6bdec0c3fa29"): 0.745e9,
+    ("kda_bf16_t32768_h16_d128", "prep", "6bdec0c3fa29"): 1.847e9,
+    ("kda_bf16_t32768_h16_d128", "chain_both", "6bdec0c3fa29"): 2.955e9,
+    ("kda_bf16_t32768_h16_d128", "grads", "6bdec0c3fa29"): 3.421e9,
+    ("kda_bf16_t32768_h16_d128", "finish", "6bdec0c3fa29"): 1.660e9,
 }
 
 
