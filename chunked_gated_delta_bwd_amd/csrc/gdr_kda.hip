@@ -461,6 +461,9 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
 // about fp32 accuracy: U, S and dS enter as bf16 high + low parts (two or three
 // MFMAs per product), kn and qn are fp32, dM and dP are split into two parts,
 // and the operands of the pairwise products are split likewise.
+// the gradient kernel runs eight waves (two per SIMD: phases alternate between them)
+constexpr int kKdaGradThreads = 2 * kThreads;
+
 template <int D>
 struct KdaGradSmem {
   static constexpr int PD = Dims<D>::PD;
@@ -478,23 +481,30 @@ struct KdaGradSmem {
 };
 
 template <int D, typename TIO>
-__global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
+__global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
   constexpr bool kLo = std::is_same<TIO, float>::value;   // fp32 dO is not exact in bf16
   using Dm = Dims<D>;
   using Sm = KdaGradSmem<D>;
-  constexpr int PD = Dm::PD, TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS, NJB = Dm::NJB;
+  constexpr int PD = Dm::PD, TPR = Dm::TPR, NJB = Dm::NJB;
+  constexpr int kT = kKdaGradThreads;
+  constexpr int RPP = kT / TPR, NPASS = C / RPP;   // row sweeps of 8 channels a thread
+  constexpr int NJH = NJB / 2;                     // 16-wide channel blocks per column half
   constexpr int PG = Sm::PG;
   __shared__ __attribute__((aligned(16))) char RX[Sm::xb];
   __shared__ __attribute__((aligned(16))) char RY[Sm::yb];
   __shared__ float beta_s[C], rq_s[C], rk_s[C];
   // fixed-order partial sums for the per-channel chunk-total gradient
   __shared__ float csum_s[4][D], ssum_s[4][D];
+  float* const dbt_s = rq_s;   // after kn, qn are formed: the second column half's dbeta partials
 
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
   const int g = l >> 4, jj = l & 15;
+  // eight waves: wave w owns row block rb = w % 4 (rows 16 rb ..) and column half
+  // hf = w / 4 of every channel-wide result; waves w and w + 4 share a SIMD
+  const int rb = __builtin_amdgcn_readfirstlane(w & 3), hf = __builtin_amdgcn_readfirstlane(w >> 2);
   const int64_t ch = int64_t(h) * p.NC + c;
   const int H = p.H;
   const float scale = p.scale;
@@ -522,12 +532,13 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     beta_s[tid] = p.rho[ch * 3 * C + 2 * C + tid];
   }
   // every tile load issued first (their latencies overlap), then the LDS writes
-  constexpr int NU = D * C / 8 / kThreads;   // 16-byte pieces per thread of a [D][64] tile
-  uint4 du_r[NU], u_r[NU], ul_r[NU], a_r[2];
+  constexpr int NU = D * C / 8 / kT;   // 16-byte pieces per thread of a [D][64] tile
+  static_assert(C * C / 8 == kT, "one 16-byte piece of A per thread");
+  uint4 du_r[NU], u_r[NU], ul_r[NU], a_r;
   typename IO<TIO>::Raw8 do_r[NPASS];
 #pragma unroll
   for (int i = 0; i < NU; ++i) {
-    const int pc = tid + i * kThreads, v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
+    const int pc = tid + i * kT, v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
     const int64_t o = (ch * D + v) * C + c0;
     du_r[i] = *reinterpret_cast<const uint4*>(p.dU + o);
     u_r[i] = *reinterpret_cast<const uint4*>(p.U + o);
@@ -538,21 +549,18 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     do_r[ps] = IO<TIO>::load_raw8(p.dO, tok(t0 + min(r, len - 1), H, h) * D + c0);
   }
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int pc = tid + x * kThreads;
-    a_r[x] = *reinterpret_cast<const uint4*>(p.A + (ch * C + pc / 8) * C + (pc % 8) * 8);
-  }
-  // phase 1's v values (row 16w + jj, columns 16 vb + 4g ..): loaded here, since a
-  // load placed after the dv stores could not be moved above them
-  const int r = 16 * w + jj;
+  a_r = *reinterpret_cast<const uint4*>(p.A + (ch * C + tid / 8) * C + (tid % 8) * 8);
+  // phase 1's v values (row 16 rb + jj, columns 16 vb + 4g .., vb in this wave's
+  // half): loaded here, since a load placed after the dv stores could not be
+  // moved above them
+  const int r = 16 * rb + jj;
   const int64_t trow = tok(t0 + min(r, len - 1), H, h) * D;
-  typename IO<TIO>::Raw4 v_raw[NJB];
+  typename IO<TIO>::Raw4 v_raw[NJH];
 #pragma unroll
-  for (int vb = 0; vb < NJB; ++vb) v_raw[vb] = IO<TIO>::load_raw4(p.v, trow + 16 * vb + 4 * g);
+  for (int q = 0; q < NJH; ++q) v_raw[q] = IO<TIO>::load_raw4(p.v, trow + 16 * (hf * NJH + q) + 4 * g);
 #pragma unroll
   for (int i = 0; i < NU; ++i) {
-    const int pc = tid + i * kThreads, v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
+    const int pc = tid + i * kT, v = pc / (C / 8), c0 = (pc % (C / 8)) * 8;
     *reinterpret_cast<uint4*>(dUsT + v * PC + c0) = du_r[i];
     *reinterpret_cast<uint4*>(UsT + v * PC + c0) = u_r[i];
     *reinterpret_cast<uint4*>(UsTl + v * PC + c0) = ul_r[i];
@@ -572,17 +580,13 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     *reinterpret_cast<bf16x8*>(dOs + r * PD + c0) = xb;
     if constexpr (kLo) *reinterpret_cast<bf16x8*>(dOl + r * PD + c0) = xl;
   }
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int pc = tid + x * kThreads;
-    *reinterpret_cast<uint4*>(As + (pc / 8) * PC + (pc % 8) * 8) = a_r[x];
-  }
+  *reinterpret_cast<uint4*>(As + (tid / 8) * PC + (tid % 8) * 8) = a_r;
   __syncthreads();
 
   // the high parts of S and dS for phase 2, in flight during phase 1; thread =
   // (8 channels c8, rows vg + VG i), the same entries in both passes of phase 2
-  constexpr int NSL = D * D / 8 / kThreads;   // 16-byte pieces per thread of a [D][D] tile
-  constexpr int CG = D / 8, VG = kThreads / CG;
+  constexpr int NSL = D * D / 8 / kT;   // 16-byte pieces per thread of a [D][D] tile
+  constexpr int CG = D / 8, VG = kT / CG;
   static_assert(NSL * VG == D, "one row set per thread");
   const int c8 = (tid % CG) * 8, vg = tid / CG;
   uint4 s_r[NSL], d_r[NSL];
@@ -593,28 +597,30 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     d_r[i] = *reinterpret_cast<const uint4*>(p.dS + o);
   }
 
-  // ---- phase 1: dY = A^T dU (lane owns dY[r][v .. v+3], r = 16w + jj); dv; sum dY*v ----
+  // ---- phase 1: dY = A^T dU (lane owns dY[r][v .. v+3], r = 16 rb + jj, v in this
+  // wave's half); dv; sum dY*v ----
   const float br = beta_s[r];
   float dbeta_row = 0.f;
 #pragma unroll
-  for (int vb = 0; vb < NJB; ++vb) {
+  for (int q = 0; q < NJH; ++q) {
+    const int vb = hf * NJH + q;
     f32x4 a = zero4();
 #pragma unroll
-    for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_rk(dUsT, PC, 16 * vb, k0), frag_kc(As, PC, 16 * w, k0), a);
+    for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_rk(dUsT, PC, 16 * vb, k0), frag_kc(As, PC, 16 * rb, k0), a);
     const int v = 16 * vb + 4 * g;
     st_bf16x4(dYs + r * PD + v, a[0], a[1], a[2], a[3]);
     float vv[4];
-    IO<TIO>::unpack4(v_raw[vb], vv);
+    IO<TIO>::unpack4(v_raw[q], vv);
     dbeta_row += a[0] * vv[0] + a[1] * vv[1] + a[2] * vv[2] + a[3] * vv[3];
     if (r < len) IO<TIO>::store4(p.dv, trow + v, br * a[0], br * a[1], br * a[2], br * a[3]);
   }
   __syncthreads();
 
   // ---- phase 2: Z = dY S, dQbar = dO S, dKhat = U dS in two passes (high, low
-  // parts of S and dS); lane owns (r, j .. j+3) ----
-  f32x4 aZ[NJB], aQ[NJB], aK[NJB];
+  // parts of S and dS); lane owns (r, j .. j+3), j in this wave's half ----
+  f32x4 aZ[NJH], aQ[NJH], aK[NJH];
 #pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) aZ[jb] = aQ[jb] = aK[jb] = zero4();
+  for (int q = 0; q < NJH; ++q) aZ[q] = aQ[q] = aK[q] = zero4();
   // per-channel state sum sum_v S dS with S = high + low, dS likewise (fp32
   // products), over this thread's entries: the high parts read back from LDS, the
   // low parts from the registers that carry them there
@@ -622,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   // raw q, k rows (for kn, qn in fp32 below) and the M entries phase 3 needs,
   // loaded during the second pass
   typename IO<TIO>::Raw8 q_raw[NPASS], k_raw[NPASS];
-  uint2 mk_r[4];
+  uint2 mk_r[2];   // phase 3's blocks of this wave: sb = hf, hf + 2
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -647,21 +653,22 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         k_raw[ps] = IO<TIO>::load_raw8(p.k, o);
       }
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
-        mk_r[sb] = *reinterpret_cast<const uint2*>(p.Mk + (ch * C + r) * C + 16 * sb + 4 * g);
+      for (int x = 0; x < 2; ++x)
+        mk_r[x] = *reinterpret_cast<const uint2*>(p.Mk + (ch * C + r) * C + 16 * (hf + 2 * x) + 4 * g);
     }
     __syncthreads();
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
+    for (int q = 0; q < NJH; ++q) {
+      const int jb = hf * NJH + q;
 #pragma unroll
       for (int k0 = 0; k0 < D; k0 += 32) {
         const bf16x8 aS = frag_kc(Sx, PD, 16 * jb, k0);
         const bf16x8 aD = frag_kc(dSx, PD, 16 * jb, k0);
-        aZ[jb] = mma(aS, frag_rk(dYs, PD, 16 * w, k0), aZ[jb]);
-        aQ[jb] = mma(aS, frag_rk(dOs, PD, 16 * w, k0), aQ[jb]);
-        if (kLo && pass == 0) aQ[jb] = mma(aS, frag_rk(dOl, PD, 16 * w, k0), aQ[jb]);
-        aK[jb] = mma(aD, frag_kc(UsT, PC, 16 * w, k0), aK[jb]);
-        if (pass == 0) aK[jb] = mma(aD, frag_kc(UsTl, PC, 16 * w, k0), aK[jb]);
+        aZ[q] = mma(aS, frag_rk(dYs, PD, 16 * rb, k0), aZ[q]);
+        aQ[q] = mma(aS, frag_rk(dOs, PD, 16 * rb, k0), aQ[q]);
+        if (kLo && pass == 0) aQ[q] = mma(aS, frag_rk(dOl, PD, 16 * rb, k0), aQ[q]);
+        aK[q] = mma(aD, frag_kc(UsT, PC, 16 * rb, k0), aK[q]);
+        if (pass == 0) aK[q] = mma(aD, frag_kc(UsTl, PC, 16 * rb, k0), aK[q]);
       }
     }
     if (pass == 0) {   // the state sum over this thread's entries (high parts: its own LDS writes)
@@ -686,9 +693,11 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       if constexpr (CG == 8) acc8[e] += dpp_f<0x128>(acc8[e]);   // lanes l and l + 8 of a row
       acc8[e] = xrow_sum(acc8[e]);
     }
-    if (l < CG) {
+    // waves 4 .. 7 leave their partials here; waves 0 .. 3 add theirs after the
+    // next barrier (a fixed order)
+    if (hf == 1 && l < CG) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ssum_s[w][c8 + e] = acc8[e];
+      for (int e = 0; e < 8; ++e) ssum_s[rb][c8 + e] = acc8[e];
     }
   }
 
@@ -710,58 +719,65 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     }
   }
   // Gamma rows for phase 4 (in flight during phase 3; region Y is rewritten below)
-  constexpr int NGL = C * D / 4 / kThreads;
+  constexpr int NGL = C * D / 4 / kT;
   float4 g_r[NGL];
 #pragma unroll
   for (int i = 0; i < NGL; ++i) {
-    const int pc = tid + i * kThreads, rr = pc / (D / 4), c4 = (pc % (D / 4)) * 4;
+    const int pc = tid + i * kT, rr = pc / (D / 4), c4 = (pc % (D / 4)) * 4;
     g_r[i] = ld4(p.gam + (ch * C + rr) * D + c4);
   }
-  // ---- phase 3: dP = dO U^T, dL = -dY U^T (U high + low); dM = beta dL ----
-  float dmv[4][4], dpv[4][4];
+  // ---- phase 3: dP = dO U^T, dL = -dY U^T (U high + low); dM = beta dL; this
+  // wave takes the column blocks sb = hf, hf + 2 of its row block (zero above it) ----
+  float dmv[2][4], dpv[2][4];
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
+  for (int x = 0; x < 2; ++x) {
+    const int sb = hf + 2 * x;
     const int s0 = 16 * sb + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dmv[sb][i] = dpv[sb][i] = 0.f;
-    if (sb <= w) {
+    for (int i = 0; i < 4; ++i) dmv[x][i] = dpv[x][i] = 0.f;
+    if (sb <= rb) {
       f32x4 G1 = zero4(), G2 = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < D; k0 += 32) {
         const bf16x8 uh = frag_kc(UsT, PC, 16 * sb, k0), ul = frag_kc(UsTl, PC, 16 * sb, k0);
-        const bf16x8 bo = frag_rk(dOs, PD, 16 * w, k0), by = frag_rk(dYs, PD, 16 * w, k0);
+        const bf16x8 bo = frag_rk(dOs, PD, 16 * rb, k0), by = frag_rk(dYs, PD, 16 * rb, k0);
         G1 = mma(uh, bo, G1);
         G1 = mma(ul, bo, G1);
-        if constexpr (kLo) G1 = mma(uh, frag_rk(dOl, PD, 16 * w, k0), G1);
+        if constexpr (kLo) G1 = mma(uh, frag_rk(dOl, PD, 16 * rb, k0), G1);
         G2 = mma(uh, by, G2);
         G2 = mma(ul, by, G2);
       }
-      const uint2 mk = mk_r[sb];
+      const uint2 mk = mk_r[x];
       const float Mv[4] = {__uint_as_float(mk.x << 16), __uint_as_float(mk.x & 0xffff0000u),
                            __uint_as_float(mk.y << 16), __uint_as_float(mk.y & 0xffff0000u)};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = s0 + i;
-        if (r >= s) dpv[sb][i] = G1[i];
+        if (r >= s) dpv[x][i] = G1[i];
         if (r > s) {
           const float dL = -G2[i];
           dbeta_row += dL * Mv[i];
-          dmv[sb][i] = br * dL;
+          dmv[x][i] = br * dL;
         }
       }
     }
   }
   __syncthreads();
+  if (hf == 0 && l < CG) {   // the state sum, waves 0 .. 3 after waves 4 .. 7
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
+    for (int e = 0; e < 8; ++e) ssum_s[rb][c8 + e] += acc8[e];
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int sb = hf + 2 * x;
     const int s0 = 16 * sb + 4 * g;
     float hm[4], lm[4], hp[4], lp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      hm[i] = float(to_bf16(dmv[sb][i]));
-      lm[i] = dmv[sb][i] - hm[i];
-      hp[i] = float(to_bf16(dpv[sb][i]));
-      lp[i] = dpv[sb][i] - hp[i];
+      hm[i] = float(to_bf16(dmv[x][i]));
+      lm[i] = dmv[x][i] - hm[i];
+      hp[i] = float(to_bf16(dpv[x][i]));
+      lp[i] = dpv[x][i] - hp[i];
     }
     st_bf16x4(dMh + r * PC + s0, hm[0], hm[1], hm[2], hm[3]);
     st_bf16x4(dMl + r * PC + s0, lm[0], lm[1], lm[2], lm[3]);
@@ -770,7 +786,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   }
 #pragma unroll
   for (int i = 0; i < NGL; ++i) {
-    const int pc = tid + i * kThreads, rr = pc / (D / 4), c4 = (pc % (D / 4)) * 4;
+    const int pc = tid + i * kT, rr = pc / (D / 4), c4 = (pc % (D / 4)) * 4;
     *reinterpret_cast<float4*>(Gs + rr * PG + c4) = g_r[i];
   }
   __syncthreads();
@@ -780,27 +796,27 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   //   X3_rc = scale sum_{s<=r} dP_rs kn_sc E  -> dqn_r, dGamma_r (+ qn_r X3)
   //   X2_sc = sum_{r>s} dM_rs kn_rc E_rsc     -> dkn_s, dGamma_s (- kn_s X2)
   //   X4_sc = scale sum_{r>=s} dP_rs qn_rc E  -> dkn_s, dGamma_s (- kn_s X4)
-  // wave w owns the 16 rows of block w on both sides; products with split operands
-  // take a_h b_h + a_h b_l + a_l b_h.  One 16-channel tile at a time: its state-side
+  // the waves of row block rb own its 16 rows on both sides, each for the channel
+  // tiles of its half; products with split operands take a_h b_h + a_h b_l + a_l b_h.  One 16-channel tile at a time: its state-side
   // terms are folded in first, and its results are stored at the end of its step,
   // so that only one tile's gradients are held in registers.
   // K = 16 B fragments of the off-diagonal block pairs (the same for every channel
-  // tile): row side blocks sb < w, column side blocks rb > w
+  // tile): row side blocks sb < rb, column side blocks cb > rb
   bf16x4 fr_mh[3], fr_ml[3], fr_ph[3], fr_pl[3], fc_mh[3], fc_ml[3], fc_ph[3], fc_pl[3];
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
-    if (x < w) {
-      fr_mh[x] = frag16_rk(dMh, PC, 16 * w, 16 * x);
-      fr_ml[x] = frag16_rk(dMl, PC, 16 * w, 16 * x);
-      fr_ph[x] = frag16_rk(dPh, PC, 16 * w, 16 * x);
-      fr_pl[x] = frag16_rk(dPl, PC, 16 * w, 16 * x);
+    if (x < rb) {
+      fr_mh[x] = frag16_rk(dMh, PC, 16 * rb, 16 * x);
+      fr_ml[x] = frag16_rk(dMl, PC, 16 * rb, 16 * x);
+      fr_ph[x] = frag16_rk(dPh, PC, 16 * rb, 16 * x);
+      fr_pl[x] = frag16_rk(dPl, PC, 16 * rb, 16 * x);
     }
-    if (x + 1 > w) {
+    if (x + 1 > rb) {
       const int rs = 16 * (x + 1);
-      fc_mh[x] = frag16_kc(dMh, PC, 16 * w, rs);
-      fc_ml[x] = frag16_kc(dMl, PC, 16 * w, rs);
-      fc_ph[x] = frag16_kc(dPh, PC, 16 * w, rs);
-      fc_pl[x] = frag16_kc(dPl, PC, 16 * w, rs);
+      fc_mh[x] = frag16_kc(dMh, PC, 16 * rb, rs);
+      fc_ml[x] = frag16_kc(dMl, PC, 16 * rb, rs);
+      fc_ph[x] = frag16_kc(dPh, PC, 16 * rb, rs);
+      fc_pl[x] = frag16_kc(dPl, PC, 16 * rb, rs);
     }
   }
   // B operands of the diagonal block's fp32 products (lane: k = 4 kk + g, n = jj):
@@ -808,7 +824,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   float dm_row[4], dp_row[4], dm_col[4], dp_col[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const int f = 16 * w, kx = f + 4 * kk + g, nx = f + jj;
+    const int f = 16 * rb, kx = f + 4 * kk + g, nx = f + jj;
     dm_row[kk] = float(dMh[nx * PC + kx]) + float(dMl[nx * PC + kx]);
     dp_row[kk] = float(dPh[nx * PC + kx]) + float(dPl[nx * PC + kx]);
     dm_col[kk] = float(dMh[kx * PC + nx]) + float(dMl[kx * PC + nx]);
@@ -822,7 +838,8 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     }
   };
 #pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
+  for (int q = 0; q < NJH; ++q) {
+    const int jb = hf * NJH + q;
     const int c0 = 16 * jb;
     const int cm = c0 + jj;          // channel of this lane in an A fragment (m = lane % 16)
     const int j = c0 + 4 * g;        // channels of this lane in the outputs
@@ -837,7 +854,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       for (int i = 0; i < 4; ++i) {
         const float kn = el(kr, i), qn = el(qr, i);
         const float eg = fast_exp(el(gr, i)), eh = fast_exp(el(gC, i) - el(gr, i));
-        const float z = aZ[jb][i], dkh = aK[jb][i], dqb = aQ[jb][i];
+        const float z = aZ[q][i], dkh = aK[q][i], dqb = aQ[q][i];
         dgm[i] = -br * z * kn * eg - dkh * kn * eh + dqb * scale * qn * eg;
         dbeta_row -= kn * eg * z;
         csum[i] = dkh * kn * eh;
@@ -848,13 +865,13 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float col = row16_sum(csum[i]);   // over the 16 rows of this wave
-        if (jj == 0) csum_s[w][j + i] = col;
+        if (jj == 0) csum_s[rb][j + i] = col;
       }
     }
-    // row side, earlier blocks sb < w: reference = last row of block sb
+    // row side, earlier blocks sb < rb: reference = last row of block sb
 #pragma unroll
     for (int sb = 0; sb < 3; ++sb) {
-      if (sb >= w) break;
+      if (sb >= rb) break;
       const int se = 16 * sb + 15;
       const float ge = Gs[se * PG + cm];
       float av[4];
@@ -878,11 +895,11 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
         dgm[i] += el(kr, i) * x1 + el(qr, i) * x3;
       }
     }
-    // column side, later blocks rb > w: reference = first row of block rb
+    // column side, later blocks cb > rb: reference = first row of block cb
 #pragma unroll
-    for (int rb = 1; rb < 4; ++rb) {
-      if (rb <= w) continue;
-      const int rs = 16 * rb;
+    for (int cb = 1; cb < 4; ++cb) {
+      if (cb <= rb) continue;
+      const int rs = 16 * cb;
       const float gst = Gs[rs * PG + cm];
       float kv[4], qv[4];
 #pragma unroll
@@ -895,7 +912,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       bf16x4 kh, kl, qh, ql;
       split4(kv, kh, kl);
       split4(qv, qh, ql);
-      const bf16x4 mh = fc_mh[rb - 1], ml = fc_ml[rb - 1], ph = fc_ph[rb - 1], pl = fc_pl[rb - 1];
+      const bf16x4 mh = fc_mh[cb - 1], ml = fc_ml[cb - 1], ph = fc_ph[cb - 1], pl = fc_pl[cb - 1];
       const f32x4 t2 = mma16(kl, mh, mma16(kh, ml, mma16(kh, mh, zero4())));
       const f32x4 t4 = mma16(ql, ph, mma16(qh, pl, mma16(qh, ph, zero4())));
       const float4 gsv = ld4(Gs + rs * PG + j);
@@ -908,15 +925,15 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
       }
     }
     bool fact_ok;
-    // diagonal block w, factored at its middle row m = 16w + 8: E_rt =
+    // diagonal block rb, factored at its middle row m = 16 rb + 8: E_rt =
     // e^(Gam_r - Gam_m) e^(Gam_m - Gam_t).  The products run on fp32 MFMA (16x16x4,
     // four k-steps) with fp32 operands, so they keep the exact path's accuracy.
     // Valid while the block's larger half-span max(Gam_f - Gam_m, Gam_m - Gam_(f+15))
-    // (f = 16w, the bound of every factor's exponent) stays below kSpanMax for all
+    // (f = 16 rb, the bound of every factor's exponent) stays below kSpanMax for all
     // 16 channels of this tile (no overflow, no underflow of the small factors);
     // otherwise the tile takes the exact per-element path below.
     {
-      const int f = 16 * w, m = f + 8;
+      const int f = 16 * rb, m = f + 8;
       const float gm = Gs[m * PG + cm];
       const bool wide = fmaxf(Gs[f * PG + cm] - gm, gm - Gs[(f + 15) * PG + cm]) >= kSpanMax;
       fact_ok = __builtin_amdgcn_ballot_w64(wide) == 0;
@@ -949,7 +966,7 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
     // a tile whose decay is too steep for the factored form, exactly:
     // E = exp(-|Gamma_r - Gamma_t|) for both orders
     if (!fact_ok) {
-      for (int t = 16 * w; t < 16 * w + 16; ++t) {
+      for (int t = 16 * rb; t < 16 * rb + 16; ++t) {
         const float mrt = float(dMh[r * PC + t]) + float(dMl[r * PC + t]);
         const float prt = scale * (float(dPh[r * PC + t]) + float(dPl[r * PC + t]));
         const float mtr = float(dMh[t * PC + r]) + float(dMl[t * PC + r]);
@@ -975,8 +992,9 @@ __global__ __launch_bounds__(kThreads) void k_grads_kda(const Params p) {
   }
   dbeta_row += __shfl_xor(dbeta_row, 16, 64);
   dbeta_row += __shfl_xor(dbeta_row, 32, 64);
-  if (g == 0) p.dbeta[ch * C + r] = dbeta_row;
+  if (hf == 1 && g == 0) dbt_s[r] = dbeta_row;
   __syncthreads();
+  if (hf == 0 && g == 0) p.dbeta[ch * C + r] = dbeta_row + dbt_s[r];
   if (tid < D) {
     const float st = (ssum_s[0][tid] + ssum_s[1][tid]) + (ssum_s[2][tid] + ssum_s[3][tid]);
     const float a = (csum_s[0][tid] + csum_s[1][tid]) + (csum_s[2][tid] + csum_s[3][tid]);
@@ -1171,7 +1189,7 @@ template <int D, typename TIO>
 void run_kda(const Params& p, int stage, hipStream_t s) {
   const dim3 grid(p.NC, p.H);
   if (stage == 0) k_prep_kda<D, TIO><<<grid, kThreads, 0, s>>>(p);
-  else if (stage == 1) k_grads_kda<D, TIO><<<grid, kThreads, 0, s>>>(p);
+  else if (stage == 1) k_grads_kda<D, TIO><<<grid, kKdaGradThreads, 0, s>>>(p);
   else if (stage == 2) k_finish_kda<D, TIO><<<grid, kThreads, 0, s>>>(p);
   else k_params_kda<D><<<p.H, kParamThreads, 0, s>>>(p);
 }
