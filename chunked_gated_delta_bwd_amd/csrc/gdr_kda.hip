@@ -82,10 +82,16 @@ __device__ __forceinline__ float el(const float4& v, int i) { return i == 0 ? v.
 // ===========================================================================
 // k_prep_kda
 // ===========================================================================
+// the prologue runs eight waves (two per SIMD)
+constexpr int kKdaPrepThreads = 2 * kThreads;
+
 template <int D, typename TIO>
-__global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
+__global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
   using Dm = Dims<D>;
-  constexpr int PD = Dm::PD, TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS;
+  constexpr int PD = Dm::PD, TPR = Dm::TPR;
+  constexpr int kT = kKdaPrepThreads;
+  constexpr int RPP = kT / TPR, NPASS = C / RPP;   // row sweeps of 8 channels a thread
+  constexpr int NPART = kT / D, RP = C / NPART;    // per-channel scans: row ranges per channel
   constexpr int PL = C + 4, PG = D + 4;
   constexpr int kQX = C * PD * 2 > C * PL * 4 ? C * PD * 2 : C * PL * 4;
   __shared__ __attribute__((aligned(16))) char QX[kQX];   // Qn; from the inverse on: X = A, fp32
@@ -99,12 +105,15 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   // low bf16 parts of A and beta V: U' = A beta V is formed to ~fp32 accuracy
   __shared__ __attribute__((aligned(16))) bf16 Asl[C * PC];
   __shared__ __attribute__((aligned(16))) bf16 Vsl[C * PD];
-  __shared__ float beta_s[C], tot_s[4][D];
+  __shared__ float beta_s[C], tot_s[NPART][D];
 
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  // eight waves: wave w works on row block rb = w % 4; the two waves of a row block
+  // (w, w + 4: one SIMD) split its work where it splits, else the first one works
+  const int rb = __builtin_amdgcn_readfirstlane(w & 3), hf = __builtin_amdgcn_readfirstlane(w >> 2);
   const int g = l >> 4, jj = l & 15;
   const int64_t ch = int64_t(h) * p.NC + c;
   const int H = p.H;
@@ -127,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   const float4 bias0 = ld4(p.dt_bias + h * D + cg0), bias1 = ld4(p.dt_bias + h * D + cg0 + 4);
   const float ea = fast_exp(p.A_log[h]);
   float braw = 0.f;
-  if (tid >= kThreads - C) braw = IO<TIO>::load1(p.b, tok(t0 + min(tid - (kThreads - C), len - 1), H, h));
+  if (tid >= kT - C) braw = IO<TIO>::load1(p.b, tok(t0 + min(tid - (kT - C), len - 1), H, h));
 
   // --- L2 norms; qn, kn to LDS; kn, qn, v kept in registers; the log decay
   // lambda = gate_lambda(g + dt_bias) (0 past the end) to Gs ---
@@ -171,8 +180,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
       p.rho[ch * 3 * C + C + r] = rk;
     }
   }
-  if (tid >= kThreads - C) {
-    const int r = tid - (kThreads - C);
+  if (tid >= kT - C) {
+    const int r = tid - (kT - C);
     const float bt = (r < len ? 1.f : 0.f) * sigmoidf(braw);
     beta_s[r] = bt;
     p.rho[ch * 3 * C + 2 * C + r] = bt;
@@ -181,7 +190,6 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   // --- in-chunk cumsum Gamma per channel: thread = (channel, one of NPART row
   // ranges) scans its range in registers, then adds the totals of the ranges before ---
   {
-    constexpr int NPART = kThreads / D, RP = C / NPART;
     const int cc = tid % D, part = tid / D;
     float x[RP];
 #pragma unroll
@@ -202,10 +210,11 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   }
   __syncthreads();
 
-  // --- M and P between blocks: wave R owns rows 16R.., blocks sb < R, reference
-  // row 16R (so both factors are <= 1); lane owns M[r][s .. s+3] ---
-  {
-    const int R = w, r = 16 * R + jj;
+  // --- M and P between blocks (the second wave of each row block): rows 16R..,
+  // blocks sb < R, reference row 16R (so both factors are <= 1); lane owns
+  // M[r][s .. s+3] ---
+  if (hf == 1) {
+    const int R = rb, r = 16 * R + jj;
     f32x4 aM[3], aP[3];
 #pragma unroll
     for (int x = 0; x < 3; ++x) aM[x] = aP[x] = zero4();
@@ -267,9 +276,10 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   // Every factor's exponent is bounded by the larger half-span of the block in its
   // channel, max(Gam_f - Gam_m, Gam_m - Gam_(f+15)); a channel where that reaches
   // kSpanMax is left out of the products (its operands are zero) and added exactly,
-  // one channel at a time, thread owns row r and four columns s ---
-  {
-    const int f = 16 * w, m = f + 8, rr = f + jj;
+  // one channel at a time, thread owns row r and four columns s (the first wave
+  // of each row block) ---
+  if (hf == 0) {
+    const int f = 16 * rb, m = f + 8, rr = f + jj;
     auto wide_ch = [&](int cc) {
       const float gm = Gs[m * PG + cc];
       return fmaxf(Gs[f * PG + cc] - gm, gm - Gs[(f + 15) * PG + cc]) >= kSpanMax;
@@ -364,8 +374,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
 
   // --- A = (I + L)^-1 in 16x16 blocks X_ij (fp32): wave i inverts the diagonal
   // block I + L_ii by forward substitution (lane = column) ... ---
-  {
-    const int i0 = 16 * w;
+  if (hf == 0) {
+    const int i0 = 16 * rb;
     float a[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -382,13 +392,13 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   __syncthreads();
   // ... then wave j walks down block column j on fp32 MFMA:
   //   X_ij = -X_ii (sum_{m=j}^{i-1} L_im X_mj),  i = j+1 .. 3
-  {
-    const int j0 = 16 * w;
-    float* const scr = reinterpret_cast<float*>(As) + 256 * w;   // 16x16 per wave
-    for (int i = w + 1; i < 4; ++i) {
+  if (hf == 0) {
+    const int j0 = 16 * rb;
+    float* const scr = reinterpret_cast<float*>(As) + 256 * rb;   // 16x16 per wave
+    for (int i = rb + 1; i < 4; ++i) {
       const int i0 = 16 * i;
       f32x4 sacc = zero4();
-      for (int m = w; m < i; ++m) {
+      for (int m = rb; m < i; ++m) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           sacc = mma_f32(Lf[(i0 + jj) * PL + 16 * m + 4 * kk + g], Xf[(16 * m + 4 * kk + g) * PL + j0 + jj], sacc);
@@ -406,8 +416,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   // --- A out: high and low bf16 parts for the W, U' products, the high part to the
   // workspace; the blocks above the diagonal are zero ---
 #pragma unroll
-  for (int it = 0; it < C * C / 8 / kThreads; ++it) {
-    const int idx = tid + kThreads * it, row = idx / 8, c8 = (idx % 8) * 8;
+  for (int it = 0; it < C * C / 8 / kT; ++it) {
+    const int idx = tid + kT * it, row = idx / 8, c8 = (idx % 8) * 8;
     const bool on = (c8 >> 4) <= (row >> 4);
     bf16x8 vh, vl;
 #pragma unroll
@@ -425,14 +435,15 @@ __global__ __launch_bounds__(kThreads) void k_prep_kda(const Params p) {
   // --- W^T and U'^T tiles: lane owns W[r][j .. j+3]; U' = A_h V_h + A_h V_l + A_l V_h,
   // stored as bf16 high + low parts ---
   {
-    const int r = 16 * w + jj;
+    const int r = 16 * rb + jj;
 #pragma unroll
-    for (int jb = 0; jb < D / 16; ++jb) {
+    for (int q = 0; q < D / 32; ++q) {   // this wave's half of the 16-wide column blocks
+      const int jb = hf * (D / 32) + q;
       f32x4 aW = zero4(), aU = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < C; k0 += 32) {
-        const bf16x8 b = frag_rk(As, PC, 16 * w, k0);
-        const bf16x8 bl = frag_rk(Asl, PC, 16 * w, k0);
+        const bf16x8 b = frag_rk(As, PC, 16 * rb, k0);
+        const bf16x8 bl = frag_rk(Asl, PC, 16 * rb, k0);
         const bf16x8 vh = frag_kc(Vs, PD, 16 * jb, k0);
         aW = mma(frag_kc(Ks, PD, 16 * jb, k0), b, aW);
         aU = mma(vh, b, aU);
@@ -1188,7 +1199,7 @@ namespace {
 template <int D, typename TIO>
 void run_kda(const Params& p, int stage, hipStream_t s) {
   const dim3 grid(p.NC, p.H);
-  if (stage == 0) k_prep_kda<D, TIO><<<grid, kThreads, 0, s>>>(p);
+  if (stage == 0) k_prep_kda<D, TIO><<<grid, kKdaPrepThreads, 0, s>>>(p);
   else if (stage == 1) k_grads_kda<D, TIO><<<grid, kKdaGradThreads, 0, s>>>(p);
   else if (stage == 2) k_finish_kda<D, TIO><<<grid, kThreads, 0, s>>>(p);
   else k_params_kda<D><<<p.H, kParamThreads, 0, s>>>(p);
