@@ -108,21 +108,20 @@ def algorithmic_work(inp, stage: str):
         b = ch * (D * D * 2 + C * D * 2 + C * C * 2 + (0 if raw else C * D * 2)) + tokens * (H + (Hk if raw else 0)) * D * io
         return ch * (2 * C * D * D + C * C * D), b
     if stage == "grads":
-        if inp["gate"] == 0:
-            # fused with the prepare-backward: S, dS, U, dU, A, Gamma, (1/|q|, 1/|k|, beta)
-            # per chunk; q, k, v, dO read and dq, dk, dv, dg, db written per token
-            b = (ch * (2 * D * D * 2 + 2 * C * D * 2 + C * C * 2 + C * 4 + 3 * C * 4)
-                 + tokens * (2 * Hk * D * io + H * (5 * D * io + 2 * io)))
-        else:
-            b = (ch * (2 * D * D * 2 + 2 * C * D * 2 + C * C * 2 + 2 * C * D * 4 + C * gk * 4 + C * 4)
-                 + tokens * (2 * Hk + 3 * H) * D * io)
+        # fused with the prepare-backward: S, dS, U, dU, A, Gamma, (1/|q|, 1/|k|, beta)
+        # per chunk (and M, the parameter partial sums for the per-channel gate);
+        # q, k, v, dO, the gate and the beta logit read, dq, dk, dv, dg, db written
+        # per token
+        b = (ch * (2 * D * D * 2 + 2 * C * D * 2 + C * C * 2 + C * gk * 4 + 3 * C * 4)
+             + tokens * (2 * Hk * D * io + H * (5 * D * io + 2 * gk * io + 2 * io)))
+        if inp["gate"] != 0:
+            b += ch * (C * C * 2 + (1 + gk) * 4)
         return ch * f_grads, b
     if stage == "finish":
         b = 0
         if inp["gate"] != 0:
-            # read q, k, dqn, dkn, rho, dGamma, dbeta, b, g_raw; write dq, dk, dg, db
-            b = (tokens * 2 * Hk * D * io
-                 + tokens * H * (2 * D * 4 + 8 + gk * 4 + 4 + io + 2 * D * io + gk * io + io + D * io))
+            # the per-head reduction of the dA_log, ddt_bias partial sums
+            b = ch * (1 + gk) * 4 + H * (1 + gk) * 4
         if Hk < H:
             # group sums: dq, dk per value head in, per key head out
             b += tokens * 2 * (H + Hk) * D * io

@@ -91,13 +91,6 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.S = take(H * NC * V * K * 2);
   L.dS = take(H * NC * V * K * 2);
   L.dU = take(H * NC * C * V * 2);
-  // handed from the gradient kernel to the prepare-backward (per-channel gate only)
-  const size_t sep = s->gate != GDR_GATE_SCALAR ? 1 : 0;
-  L.dqn = take(sep * H * NC * C * K * 4);
-  L.dkn = take(sep * H * NC * C * K * 4);
-  L.dgam = take(sep * H * NC * C * gk * 4);
-  L.dgamc = take(sep * H * NC * gk * 4);
-  L.dbeta = take(sep * H * NC * C * 4);
   L.Kh = take(mat * H * NC * C * K * 2);
   L.Qh = take(mat * H * NC * C * K * 2);
   L.Ql = take(mat * H * NC * C * K * 2);
@@ -222,11 +215,6 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   p.S = reinterpret_cast<uint16_t*>(w + L.S);
   p.dS = reinterpret_cast<uint16_t*>(w + L.dS);
   p.dU = reinterpret_cast<uint16_t*>(w + L.dU);
-  p.dqn = reinterpret_cast<float*>(w + L.dqn);
-  p.dkn = reinterpret_cast<float*>(w + L.dkn);
-  p.dgam = reinterpret_cast<float*>(w + L.dgam);
-  p.dgamc = reinterpret_cast<float*>(w + L.dgamc);
-  p.dbeta = reinterpret_cast<float*>(w + L.dbeta);
   p.Kh = reinterpret_cast<uint16_t*>(w + L.Kh);
   p.Qh = reinterpret_cast<uint16_t*>(w + L.Qh);
   p.Ql = reinterpret_cast<uint16_t*>(w + L.Ql);
@@ -284,12 +272,12 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
   const bool kda = s->gate != GDR_GATE_SCALAR;
   auto prep = [&]() { return kda ? gdr::launch_kda(p, 0, stream) : gdr::launch_prep(p, stream); };
   auto grads = [&]() { return kda ? gdr::launch_kda(p, 1, stream) : gdr::launch_grads(p, stream); };
-  // the scalar gate's prepare-backward is fused into its gradient kernel; with
-  // grouped heads the dq, dk group sums end this stage
+  // both gates' prepare-backward is fused into their gradient kernels; what is
+  // left: the per-head reduction of the per-channel gate's parameter partial
+  // sums and, with grouped heads, the dq, dk group sums
   auto finish = [&]() {
     int e = 0;
     if (kda && !e) e = gdr::launch_kda(p, 2, stream);
-    if (kda && !e) e = gdr::launch_kda(p, 3, stream);
     if (p.G > 1 && !e) e = gdr::launch_group_sum(p, p.dq, gr->dq, stream);
     if (p.G > 1 && !e) e = gdr::launch_group_sum(p, p.dk, gr->dk, stream);
     return e;
@@ -302,7 +290,7 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
       case GDR_STAGE_CHAIN_BOTH: return hip_status(gdr::launch_chain(p, gdr::kChainBoth, stream), "chain kernel");
       case GDR_STAGE_GRADS: return NC > 0 ? hip_status(grads(), "gradient kernel") : GDR_OK;
       case GDR_STAGE_FINISH:
-        if (NC > 0) return hip_status(finish(), "prepare-backward kernel");
+        if (NC > 0) return hip_status(finish(), "parameter reduction kernel");
         return kda ? hip_status(gdr::launch_zero_params(p, stream), "zero kernel") : GDR_OK;
       default: return fail(GDR_EINVAL, "unknown stage %d", only);
     }
@@ -318,7 +306,7 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
   if (stage != kFwd) {
     if (NC > 0) {
       if ((st = hip_status(grads(), "gradient kernel")) != GDR_OK) return st;
-      if ((st = hip_status(finish(), "prepare-backward kernel")) != GDR_OK) return st;
+      if ((st = hip_status(finish(), "parameter reduction kernel")) != GDR_OK) return st;
     } else if (kda) {
       // no tokens: the per-head parameter gradients are zero
       if ((st = hip_status(gdr::launch_zero_params(p, stream), "zero kernel")) != GDR_OK) return st;

@@ -50,11 +50,6 @@ struct WsLayout {
   size_t S = 0;      // bf16 [H][NC][V][K]:   state at chunk start
   size_t dS = 0;     // bf16 [H][NC][V][K]:   gradient w.r.t. the state at chunk end
   size_t dU = 0;     // bf16 [H][NC][V][64]:  gradient w.r.t. v_new, transposed
-  size_t dqn = 0;    // fp32 [H][NC][64][K]
-  size_t dkn = 0;    // fp32 [H][NC][64][K]
-  size_t dgam = 0;   // fp32 [H][NC][64] or [H][NC][64][K]
-  size_t dgamc = 0;  // fp32 [H][NC] or [H][NC][K]
-  size_t dbeta = 0;  // fp32 [H][NC][64]: gradient w.r.t. beta (sigmoid space)
   // per-channel gate or fp32 inputs: the recursions' operand tiles formed by the
   // prologue (the scalar gate with bf16 inputs applies row factors instead)
   size_t Kh = 0;     // bf16 [H][NC][64][K]: Khat = kn e^(GamC - Gam)
@@ -101,7 +96,6 @@ struct Params {
   uint16_t* Mk;                                  // per-channel gate only
   float *pdA, *pddt;
   uint16_t *Uplo, *Ulo, *Slo, *dSlo;             // per-channel gate only: low parts
-  float *dqn, *dkn, *dgam, *dgamc, *dbeta;
 };
 
 // Chain-kernel roles.
@@ -117,8 +111,8 @@ int launch_output(const Params& p, void* stream);
 // Grouped heads (gdr_group.hip): dst[t][j][:] = sum over i < G of src[t][j G + i][:],
 // for the T tokens, Hk key heads and K channels of p, in p.dtype.
 int launch_group_sum(const Params& p, const void* src, void* dst, void* stream);
-// Per-channel gate kernels (gdr_kda.hip): stage 0 prologue, 1 gradients,
-// 2 prepare-backward, 3 dA_log / ddt_bias reduction.
+// Per-channel gate kernels (gdr_kda.hip): stage 0 prologue, 1 gradients with the
+// prepare-backward, 2 dA_log / ddt_bias reduction.
 int launch_kda(const Params& p, int stage, void* stream);
 const char* hip_error_string(int err);
 

@@ -12,18 +12,19 @@
 // exponents <= 0 (Gamma never increases), so those blocks go to MFMA on operands
 // scaled in registers; inside a diagonal 16-row block it splits at the block's
 // middle row (factors bounded by the half-spans of the block, fp32 MFMA), and a
-// channel whose half-span is too wide for that is evaluated exactly per element.  The chunk recursions then take materialised Khat = kn e^(GamC - Gam),
-// Qbar = scale qn e^Gam (high + low bf16 parts) and the per-channel chunk decay.
+// channel whose half-span is too wide for that is evaluated exactly per element.
+// The chunk recursions then take materialised Khat = kn e^(GamC - Gam), Qbar =
+// scale qn e^Gam (high + low bf16 parts) and the per-channel chunk decay.
 //
 //   k_prep_kda    per (chunk, head): norms, gate and its cumsum, M and P, the
 //                 UT/WY inverse, W and U', Khat / Qbar tiles, chunk decay.
 //   k_grads_kda   per (chunk, head): the chunk-local gradients; the pairwise
 //                 terms are four E-weighted products (row and column sides of
 //                 dM o E and dP o E) on K = 16 MFMAs plus the diagonal blocks
-//                 on fp32 MFMA (exactly where their decay is too steep).
-//   k_finish_kda  per (chunk, head): L2-norm and sigmoid backward, the per-channel
-//                 reverse cumsum of dGamma plus the chunk-total term, the gate
-//                 backward, and per-chunk partial sums of dA_log and ddt_bias.
+//                 on fp32 MFMA (exactly where their decay is too steep); then,
+//                 fused, the prepare-backward: L2-norm and sigmoid backward, the
+//                 per-channel reverse cumsum of dGamma plus the chunk-total term,
+//                 the gate backward, per-chunk partial sums of dA_log, ddt_bias.
 //   k_params_kda  per head: the partial sums reduced in a fixed order.
 #include <hip/hip_runtime.h>
 
@@ -489,6 +490,8 @@ struct KdaGradSmem {
   static constexpr int y_p1 = (3 * C * PD + 2 * D * PC) * 2;
   static constexpr int y_p4 = 4 * C * PC * 2 + C * PG * 4;
   static constexpr int yb = y_p1 > y_p4 ? y_p1 : y_p4;
+  // from phase 4 on, region Y's bytes past the phase-4 tiles are free
+  static constexpr int y_tail = yb - y_p4;
 };
 
 template <int D, typename TIO>
@@ -506,7 +509,11 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
   __shared__ float beta_s[C], rq_s[C], rk_s[C];
   // fixed-order partial sums for the per-channel chunk-total gradient
   __shared__ float csum_s[4][D], ssum_s[4][D];
-  float* const dbt_s = rq_s;   // after kn, qn are formed: the second column half's dbeta partials
+  // the fused prepare-backward's small arrays: in region Y's tail where it has room
+  constexpr int NPART = kT / D, RP = C / NPART;   // per-channel scans: row ranges per channel
+  constexpr int kTailFloats = 2 * NPART * D + kT / 64 + 4 * C + C + D;
+  constexpr bool kTailInY = Sm::y_tail >= kTailFloats * 4;
+  __shared__ __attribute__((aligned(16))) float TX[kTailInY ? 4 : kTailFloats];
 
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkEntry ce = p.ctab[c];
@@ -536,6 +543,14 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
   bf16* dPh = dMl + C * PC;
   bf16* dPl = dPh + C * PC;
   float* Gs = reinterpret_cast<float*>(dPl + C * PC); // phase 4: Gamma [r][c]
+  float* Dg_s = reinterpret_cast<float*>(RY);         // after phase 4: dGamma [r][c]
+  float* const tail = kTailInY ? reinterpret_cast<float*>(RY + Sm::y_p4) : TX;
+  float* const tot_s = tail;                  // [NPART][D] range totals of the reverse cumsum
+  float* const pd_s = tot_s + NPART * D;      // [NPART][D] ddt_bias partials
+  float* const pa_s = pd_s + NPART * D;       // [waves]    dA_log partials
+  float* const l2_s = pa_s + kT / 64;         // [half][q, k][C] row dot products
+  float* const dbt_s = l2_s + 4 * C;          // [C] the second column half's dbeta partials
+  float* const dgc_s = dbt_s + C;             // [D] dGamma_C
 
   if (tid < C) {
     rq_s[tid] = p.rho[ch * 3 * C + tid];
@@ -848,8 +863,21 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
       lo[i] = to_bf16(x[i] - float(hi[i]));
     }
   };
+  // every tile's dqn, dkn, dGamma stay in registers for the prepare-backward below
+  f32x4 oq[NJH], ok[NJH], og[NJH];
+  // the prepare-backward's per-channel operands (thread = channel gc, row range gpart)
+  const int gc = tid % D, gpart = tid / D;
+  float x_r[RP], bias = 0.f, a_log = 0.f, braw = 0.f;
 #pragma unroll
   for (int q = 0; q < NJH; ++q) {
+    if (q == NJH - 1) {   // in flight during the last tile
+#pragma unroll
+      for (int i = 0; i < RP; ++i)
+        x_r[i] = IO<TIO>::load1(p.g, tok(t0 + min(gpart * RP + i, len - 1), H, h) * D + gc);
+      bias = p.dt_bias[h * D + gc];
+      a_log = p.A_log[h];
+      braw = IO<TIO>::load1(p.b, tok(t0 + min(r, len - 1), H, h));
+    }
     const int jb = hf * NJH + q;
     const int c0 = 16 * jb;
     const int cm = c0 + jj;          // channel of this lane in an A fragment (m = lane % 16)
@@ -995,141 +1023,95 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
         }
       }
     }
-    // this tile's results
-    const int64_t o = (ch * C + r) * D + j;
-    *reinterpret_cast<float4*>(p.dqn + o) = make_float4(dqn[0], dqn[1], dqn[2], dqn[3]);
-    *reinterpret_cast<float4*>(p.dkn + o) = make_float4(dkn[0], dkn[1], dkn[2], dkn[3]);
-    *reinterpret_cast<float4*>(p.dgam + o) = make_float4(dgm[0], dgm[1], dgm[2], dgm[3]);
+    oq[q] = dqn;
+    ok[q] = dkn;
+    og[q] = dgm;
   }
+
+  // ---- prepare-backward, fused (FlashKDA backward (K1) page, sections 3.3 and 5):
+  // the L2-norm backward of dqn, dkn (row dot products over both column halves),
+  // the sigmoid backward of dbeta, the per-channel reverse cumsum of dGamma plus the
+  // chunk-total term, the gate backward, per-chunk partials of dA_log and ddt_bias ----
+  float pq = 0.f, pk = 0.f;
+#pragma unroll
+  for (int q = 0; q < NJH; ++q) {
+    const int j = 16 * (hf * NJH + q) + 4 * g;
+    const float4 qn4 = ld4(Qnf + r * PG + j), kn4 = ld4(Knf + r * PG + j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pq = fmaf(el(qn4, i), oq[q][i], pq);
+      pk = fmaf(el(kn4, i), ok[q][i], pk);
+    }
+  }
+  pq = xrow_sum(pq);
+  pk = xrow_sum(pk);
   dbeta_row += __shfl_xor(dbeta_row, 16, 64);
   dbeta_row += __shfl_xor(dbeta_row, 32, 64);
-  if (hf == 1 && g == 0) dbt_s[r] = dbeta_row;
-  __syncthreads();
-  if (hf == 0 && g == 0) p.dbeta[ch * C + r] = dbeta_row + dbt_s[r];
+  __syncthreads();   // phase 4 is done everywhere: dM, dP are free (Gamma's last row is read below)
+#pragma unroll
+  for (int q = 0; q < NJH; ++q) {
+    const int j = 16 * (hf * NJH + q) + 4 * g;
+    *reinterpret_cast<float4*>(Dg_s + r * PG + j) = make_float4(og[q][0], og[q][1], og[q][2], og[q][3]);
+  }
+  if (g == 0) {
+    l2_s[(2 * hf) * C + r] = pq;
+    l2_s[(2 * hf + 1) * C + r] = pk;
+    if (hf == 1) dbt_s[r] = dbeta_row;
+  }
   if (tid < D) {
     const float st = (ssum_s[0][tid] + ssum_s[1][tid]) + (ssum_s[2][tid] + ssum_s[3][tid]);
     const float a = (csum_s[0][tid] + csum_s[1][tid]) + (csum_s[2][tid] + csum_s[3][tid]);
-    p.dgamc[ch * D + tid] = a + st * fast_exp(Gs[(C - 1) * PG + tid]);
+    dgc_s[tid] = a + st * fast_exp(Gs[(C - 1) * PG + tid]);
   }
-}
-
-// ===========================================================================
-// k_finish_kda: L2-norm / sigmoid backward, per-channel reverse cumsum, gate
-// backward, per-chunk partial sums of dA_log and ddt_bias
-// ===========================================================================
-template <int D, typename TIO>
-__global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
-  using Dm = Dims<D>;
-  constexpr int TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS;
-  constexpr int NPART = kThreads / D, RP = C / NPART;   // per-channel scans: row ranges per channel
-  __shared__ float tot_s[NPART][D], pd_s[NPART][D], pa_s[kThreads / 64];
-  const int c = blockIdx.x, h = blockIdx.y;
-  const ChunkEntry ce = p.ctab[c];
-  const int t0 = ce.t_start, len = ce.len;
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
-  const int64_t ch = int64_t(h) * p.NC + c;
-  const int H = p.H;
-  const int c0 = (tid % TPR) * 8;
-  const int cc = tid % D, part = tid / D;
-
-  // ---- the L2-norm backward's loads first (their latencies overlap), row sweeps
-  // of 8 channels a thread: q, k, dqn, dkn, the row norms; the gate's per-channel
-  // loads follow once these registers are free (the workgroups sharing the CU
-  // keep the memory busy meanwhile) ----
-  typename IO<TIO>::Raw8 qraw[NPASS], kraw[NPASS];
-  float4 dq4[NPASS][2], dk4[NPASS][2];
-  float rq_r[NPASS], rk_r[NPASS];
-#pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int r = ps * RPP + tid / TPR;
-    const int64_t qo = qk_tok(p, t0 + min(r, len - 1), h) * D + c0;
-    const int64_t wo = (ch * C + r) * D + c0;
-    qraw[ps] = IO<TIO>::load_raw8(p.q, qo);
-    kraw[ps] = IO<TIO>::load_raw8(p.k, qo);
-    dq4[ps][0] = ld4(p.dqn + wo);
-    dq4[ps][1] = ld4(p.dqn + wo + 4);
-    dk4[ps][0] = ld4(p.dkn + wo);
-    dk4[ps][1] = ld4(p.dkn + wo + 4);
-    rq_r[ps] = p.rho[ch * 3 * C + r];
-    rk_r[ps] = p.rho[ch * 3 * C + C + r];
-  }
-  const float bias = p.dt_bias[h * D + cc];
-  const float dgamc = p.dgamc[ch * D + cc];
-  const float a_log = p.A_log[h];
-  float braw = 0.f, dbs = 0.f;
-  if (w == kThreads / 64 - 1) {
-    braw = IO<TIO>::load1(p.b, tok(t0 + min(l, len - 1), H, h));
-    dbs = p.dbeta[ch * C + l];
-  }
-
-  // ---- L2-norm backward: dq = rq (dqn - qn <qn, dqn>), dk likewise (K1 page, 3.3) ----
-#pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int r = ps * RPP + tid / TPR;
-    const bool ok = r < len;
-    const float m = ok ? 1.f : 0.f;
-    const float rq = m * rq_r[ps], rk = m * rk_r[ps];
-    float q[8], k[8];
-    IO<TIO>::unpack8(qraw[ps], q);
-    IO<TIO>::unpack8(kraw[ps], k);
-    const float dq[8] = {dq4[ps][0].x, dq4[ps][0].y, dq4[ps][0].z, dq4[ps][0].w,
-                         dq4[ps][1].x, dq4[ps][1].y, dq4[ps][1].z, dq4[ps][1].w};
-    const float dk[8] = {dk4[ps][0].x, dk4[ps][0].y, dk4[ps][0].z, dk4[ps][0].w,
-                         dk4[ps][1].x, dk4[ps][1].y, dk4[ps][1].z, dk4[ps][1].w};
-    float pq = 0.f, pk = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      q[e] *= rq;
-      k[e] *= rk;
-      pq += q[e] * dq[e];
-      pk += k[e] * dk[e];
-    }
-    pq = group_sum_dpp<TPR>(pq);
-    pk = group_sum_dpp<TPR>(pk);
-    if (ok) {
-      float oq[8], ok8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        oq[e] = rq * (dq[e] - q[e] * pq);
-        ok8[e] = rk * (dk[e] - k[e] * pk);
-      }
-      IO<TIO>::store8(p.dq, tok(t0 + r, H, h) * D + c0, oq);
-      IO<TIO>::store8(p.dk, tok(t0 + r, H, h) * D + c0, ok8);
-    }
-  }
-  // per channel (thread = channel cc, row range part): dGamma and the raw gate
-  float dg_r[RP], x_r[RP];
-#pragma unroll
-  for (int i = 0; i < RP; ++i) {
-    const int r = part * RP + i;
-    dg_r[i] = p.dgam[(ch * C + r) * D + cc];
-    x_r[i] = IO<TIO>::load1(p.g, tok(t0 + min(r, len - 1), H, h) * D + cc);
-  }
-  if (w == kThreads / 64 - 1) {
-    const float bt = sigmoidf(braw);
-    if (l < len) IO<TIO>::store1(p.db, tok(t0 + l, H, h), dbs * bt * (1.f - bt));
-  }
-
-  // ---- per channel: dlam_r = sum_{r' >= r} dGamma_r' + dGamma_C (FlashKDA
-  // backward page, section 5), then through the gate function: softplus form
-  // dx = dlam (-e^A sigmoid(x)), d/dA_log: dlam lambda; bounded sigmoid form
-  // (z = e^A x) dx = dlam gate_scale sigma(z) (1 - sigma(z)) e^A, d/dA_log: dx x.
-  // Thread = (channel, one of NPART row ranges): a suffix scan of its range in
-  // registers plus the totals of the ranges after it ----
-#pragma unroll
-  for (int i = RP - 2; i >= 0; --i) dg_r[i] += dg_r[i + 1];
-  tot_s[part][cc] = dg_r[0];
   __syncthreads();
-  float after = dgamc;
+  // L2-norm backward (K1 page, 3.3): dq = rq (dqn - qn <qn, dqn>), dk likewise
+  {
+    const bool valid = r < len;
+    const float m = valid ? 1.f : 0.f;
+    const float rq = m * rq_s[r], rk = m * rk_s[r];
+    const float pqf = l2_s[r] + l2_s[2 * C + r], pkf = l2_s[C + r] + l2_s[3 * C + r];
 #pragma unroll
-  for (int q = NPART - 1; q > 0; --q) after += q > part ? tot_s[q][cc] : 0.f;
+    for (int q = 0; q < NJH; ++q) {
+      const int j = 16 * (hf * NJH + q) + 4 * g;
+      const float4 qn4 = ld4(Qnf + r * PG + j), kn4 = ld4(Knf + r * PG + j);
+      float dq[4], dk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dq[i] = rq * (oq[q][i] - el(qn4, i) * pqf);
+        dk[i] = rk * (ok[q][i] - el(kn4, i) * pkf);
+      }
+      if (valid) {
+        IO<TIO>::store4(p.dq, tok(t0 + r, H, h) * D + j, dq[0], dq[1], dq[2], dq[3]);
+        IO<TIO>::store4(p.dk, tok(t0 + r, H, h) * D + j, dk[0], dk[1], dk[2], dk[3]);
+      }
+    }
+  }
+  // sigmoid backward of beta (w.r.t. its logit)
+  if (hf == 0 && g == 0 && r < len) {
+    const float bt = sigmoidf(braw);
+    IO<TIO>::store1(p.db, tok(t0 + r, H, h), (dbeta_row + dbt_s[r]) * bt * (1.f - bt));
+  }
+  // per channel: dlam_r = sum_{r' >= r} dGamma_r' + dGamma_C (K1 page, section 5),
+  // then through the gate function: softplus form dx = dlam (-e^A sigmoid(x)),
+  // d/dA_log: dlam lambda; bounded sigmoid form (z = e^A x) dx = dlam gate_scale
+  // sigma(z) (1 - sigma(z)) e^A, d/dA_log: dx x.  Thread = (channel, one of NPART
+  // row ranges): a suffix scan of its range in registers plus the totals of the
+  // ranges after it
+  float xs[RP];
+#pragma unroll
+  for (int i = RP - 1; i >= 0; --i) xs[i] = Dg_s[(gpart * RP + i) * PG + gc] + (i < RP - 1 ? xs[i + 1] : 0.f);
+  tot_s[gpart * D + gc] = xs[0];
+  __syncthreads();
+  float after = dgc_s[gc];
+#pragma unroll
+  for (int qq = NPART - 1; qq > 0; --qq) after += qq > gpart ? tot_s[qq * D + gc] : 0.f;
   const float ea = fast_exp(a_log);
   float pd = 0.f, pa = 0.f;
 #pragma unroll
   for (int i = 0; i < RP; ++i) {
-    const int r = part * RP + i;
-    if (r < len) {
-      const float acc = dg_r[i] + after;
+    const int rr = gpart * RP + i;
+    if (rr < len) {
+      const float acc = xs[i] + after;
       const float xg = x_r[i] + bias;
       float dx;
       if (p.gate_fn) {
@@ -1140,24 +1122,24 @@ __global__ __launch_bounds__(kThreads) void k_finish_kda(const Params p) {
         dx = acc * (-ea * sigmoidf(xg));
         pa += acc * (-ea * softplusf(xg));
       }
-      IO<TIO>::store1(p.dg, tok(t0 + r, H, h) * D + cc, dx);
+      IO<TIO>::store1(p.dg, tok(t0 + rr, H, h) * D + gc, dx);
       pd += dx;
     }
   }
-  pd_s[part][cc] = pd;
+  pd_s[gpart * D + gc] = pd;
   pa = wave_sum(pa);
   if (l == 0) pa_s[w] = pa;
   __syncthreads();
   if (tid < D) {
     float sdt = 0.f;
 #pragma unroll
-    for (int q = 0; q < NPART; ++q) sdt += pd_s[q][tid];
+    for (int qq = 0; qq < NPART; ++qq) sdt += pd_s[qq * D + tid];
     p.pddt[ch * D + tid] = sdt;
   }
   if (tid == 0) {
     float sa = 0.f;
 #pragma unroll
-    for (int q = 0; q < kThreads / 64; ++q) sa += pa_s[q];
+    for (int x = 0; x < kT / 64; ++x) sa += pa_s[x];
     p.pdA[ch] = sa;
   }
 }
@@ -1201,8 +1183,7 @@ void run_kda(const Params& p, int stage, hipStream_t s) {
   const dim3 grid(p.NC, p.H);
   if (stage == 0) k_prep_kda<D, TIO><<<grid, kKdaPrepThreads, 0, s>>>(p);
   else if (stage == 1) k_grads_kda<D, TIO><<<grid, kKdaGradThreads, 0, s>>>(p);
-  else if (stage == 2) k_finish_kda<D, TIO><<<grid, kThreads, 0, s>>>(p);
-  else k_params_kda<D><<<p.H, kParamThreads, 0, s>>>(p);
+  else if (stage == 2) k_params_kda<D><<<p.H, kParamThreads, 0, s>>>(p);
 }
 }  // namespace
 

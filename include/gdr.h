@@ -154,10 +154,11 @@ gdr_status gdr_workspace_region(const gdr_shape* shape, int32_t which, size_t* o
  *   GDR_STAGE_CHAIN_FWD   forward state pass alone
  *   GDR_STAGE_CHAIN_BWD   reverse state-gradient recursion alone
  *   GDR_STAGE_CHAIN_BOTH  both recursions in one launch, as gdr_fwd_bwd runs them
- *   GDR_STAGE_GRADS       chunk-parallel gradients; for GDR_GATE_SCALAR this launch also
- *                         runs the prepare-backward and writes every gradient
- *   GDR_STAGE_FINISH      prepare-backward of GDR_GATE_CHANNEL (norm, sigmoid, gate,
- *                         parameter sums); enqueues nothing for GDR_GATE_SCALAR */
+ *   GDR_STAGE_GRADS       chunk-parallel gradients and the prepare-backward (norm,
+ *                         sigmoid, gate backward); writes every per-token gradient
+ *   GDR_STAGE_FINISH      the per-head reduction of dA_log, ddt_bias (CHANNEL) and the
+ *                         dq, dk group sums (grouped heads); enqueues nothing for
+ *                         GDR_GATE_SCALAR with Hk = H */
 enum { GDR_STAGE_PREP = 0, GDR_STAGE_CHAIN_FWD = 1, GDR_STAGE_CHAIN_BWD = 2, GDR_STAGE_CHAIN_BOTH = 3,
        GDR_STAGE_GRADS = 4, GDR_STAGE_FINISH = 5 };
 gdr_status gdr_run_stage(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht,
