@@ -31,27 +31,25 @@ static_assert(Dims<128>::RPP * Dims<128>::TPR == kThreads, "row sweep covers the
 // ===========================================================================
 // k_prep (scalar gate)
 // ===========================================================================
-// Tiles (rb, sb), sb <= rb, of the 10 lower / diagonal 16x16 blocks of a 64x64
-// chunk matrix, dealt 3-3-2-2 over four waves: nibble `slot` of these words is
-// the rb / sb of a wave's tile in that slot (the third slot of waves 2 and 3
-// repeats a tile and stores nothing).
-constexpr uint32_t kTileRb[4] = {0x333, 0x223, 0x112, 0x001};
-constexpr uint32_t kTileSb[4] = {0x210, 0x103, 0x002, 0x001};
-__device__ __forceinline__ int tile_rb(int w, int slot) {
-  const uint32_t x = w == 0 ? kTileRb[0] : w == 1 ? kTileRb[1] : w == 2 ? kTileRb[2] : kTileRb[3];
-  return (x >> (4 * slot)) & 15;
-}
-__device__ __forceinline__ int tile_sb(int w, int slot) {
-  const uint32_t x = w == 0 ? kTileSb[0] : w == 1 ? kTileSb[1] : w == 2 ? kTileSb[2] : kTileSb[3];
-  return (x >> (4 * slot)) & 15;
-}
-__device__ __forceinline__ bool tile_valid(int w, int slot) { return slot < 2 || w < 2; }
+// The prologue runs eight waves (two per SIMD).  Tiles (rb, sb), sb <= rb, of the
+// 10 lower / diagonal 16x16 blocks of a 64x64 chunk matrix, dealt over them: slot
+// 0 of wave w is tile w, slot 1 of waves 0 and 1 tiles 8 and 9 (nibble w of these
+// words, then nibbles 8 and 9, give rb / sb); the other waves have no slot 1.
+constexpr int kPrepThreads = 2 * kThreads;
+constexpr uint64_t kTileRb = 0x3333222110ull;   // tile t: rb = nibble t
+constexpr uint64_t kTileSb = 0x3210210100ull;   // tile t: sb = nibble t
+__device__ __forceinline__ int tile_of(int w, int slot) { return slot == 0 || w >= 2 ? w : 8 + w; }
+__device__ __forceinline__ int tile_rb(int w, int slot) { return int(kTileRb >> (4 * tile_of(w, slot))) & 15; }
+__device__ __forceinline__ int tile_sb(int w, int slot) { return int(kTileSb >> (4 * tile_of(w, slot))) & 15; }
+__device__ __forceinline__ bool tile_valid(int w, int slot) { return slot == 0 || w < 2; }
 
 
 template <int D, typename TIO>
-__global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
+__global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   using Dm = Dims<D>;
-  constexpr int PD = Dm::PD, TPR = Dm::TPR, RPP = Dm::RPP, NPASS = Dm::NPASS;
+  constexpr int PD = Dm::PD, TPR = Dm::TPR;
+  constexpr int kT = kPrepThreads;
+  constexpr int RPP = kT / TPR, NPASS = C / RPP;   // row sweeps of 8 channels a thread
   constexpr int PL = C + 4;   // pitch (floats) of the fp32 64x64 tiles L and X
   constexpr int kQX = C * PD * 2 > C * PL * 4 ? C * PD * 2 : C * PL * 4;
   __shared__ __attribute__((aligned(16))) char QX[kQX];          // Qn; from the inverse on: X = A, fp32
@@ -69,8 +67,11 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   const int c = blockIdx.x, h = blockIdx.y;
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  const int tid = threadIdx.x, l = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
   const int g = l >> 4, jj = l & 15;
+  // wave w: row block rb = w % 4; the two waves of a row block (one SIMD) split
+  // its work where it splits, else the first one works
+  const int rb = w & 3, hf = w >> 2;
   const int64_t ch = int64_t(h) * p.NC + c;
   const int H = p.H;
 
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
     braw = IO<TIO>::load1(p.b, o);
   }
   // the P tile goes out through As, which starts at zero (tiles above the diagonal)
-  for (int o = 16 * tid; o < C * PC * 2; o += 16 * kThreads)
+  for (int o = 16 * tid; o < C * PC * 2; o += 16 * kT)
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(As) + o) = u32x4{0u, 0u, 0u, 0u};
 
   // --- L2 norms; qn, kn to LDS; kn and v kept in registers ---
@@ -185,15 +186,16 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   // --- M and P on the lower / diagonal tiles: lane owns X[r][s .. s+3],
   // r = 16 rb + jj, s = 16 sb + 4g + i ---
 #pragma unroll
-  for (int slot = 0; slot < 3; ++slot) {
-    const int rb = tile_rb(w, slot), sb = tile_sb(w, slot);
-    const int r = 16 * rb + jj, s0 = 16 * sb + 4 * g;
+  for (int slot = 0; slot < 2; ++slot) {
+    if (!tile_valid(w, slot)) break;
+    const int tb = tile_rb(w, slot), sb = tile_sb(w, slot);
+    const int r = 16 * tb + jj, s0 = 16 * sb + 4 * g;
     f32x4 aM = zero4(), aP = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += 32) {
       const bf16x8 a = frag_rk(Ks, PD, 16 * sb, k0);
-      aM = mma(a, frag_rk(Ks, PD, 16 * rb, k0), aM);
-      aP = mma(a, frag_rk(Qs, PD, 16 * rb, k0), aP);
+      aM = mma(a, frag_rk(Ks, PD, 16 * tb, k0), aM);
+      aP = mma(a, frag_rk(Qs, PD, 16 * tb, k0), aP);
     }
     const float gr = gam_s[r], br = beta_s[r];
     float Lv[4], Pv[4];
@@ -214,8 +216,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
 
   // --- P out: rows of 128 bytes, 16 bytes per lane ---
 #pragma unroll
-  for (int it = 0; it < C * C / 8 / kThreads; ++it) {
-    const int idx = tid + kThreads * it, row = idx / 8, c8 = (idx % 8) * 8;
+  for (int it = 0; it < C * C / 8 / kT; ++it) {
+    const int idx = tid + kT * it, row = idx / 8, c8 = (idx % 8) * 8;
     *reinterpret_cast<u32x4*>(p.P + (ch * C + row) * C + c8) = *reinterpret_cast<const u32x4*>(As + row * PC + c8);
   }
 
@@ -237,8 +239,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
 
   // --- A = (I + L)^-1 in 16x16 blocks X_ij (fp32): wave i inverts the diagonal
   // block I + L_ii by forward substitution (lane = column) ... ---
-  {
-    const int i0 = 16 * w;
+  if (hf == 0) {
+    const int i0 = 16 * rb;
     float a[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -255,13 +257,13 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   __syncthreads();
   // ... then wave j walks down block column j on fp32 MFMA:
   //   X_ij = -X_ii (sum_{m=j}^{i-1} L_im X_mj),  i = j+1 .. 3
-  {
-    const int j0 = 16 * w;
-    float* const scr = reinterpret_cast<float*>(As) + 256 * w;   // 16x16 per wave
-    for (int i = w + 1; i < 4; ++i) {
+  if (hf == 0) {
+    const int j0 = 16 * rb;
+    float* const scr = reinterpret_cast<float*>(As) + 256 * rb;   // 16x16 per wave
+    for (int i = rb + 1; i < 4; ++i) {
       const int i0 = 16 * i;
       f32x4 sacc = zero4();
-      for (int m = w; m < i; ++m) {
+      for (int m = rb; m < i; ++m) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           sacc = mma_f32(Lf[(i0 + jj) * PL + 16 * m + 4 * kk + g], Xf[(16 * m + 4 * kk + g) * PL + j0 + jj], sacc);
@@ -279,8 +281,8 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
   // --- A out (bf16): the operand tile for W, U' and the workspace copy; the
   // blocks above the diagonal are zero ---
 #pragma unroll
-  for (int it = 0; it < C * C / 8 / kThreads; ++it) {
-    const int idx = tid + kThreads * it, row = idx / 8, c8 = (idx % 8) * 8;
+  for (int it = 0; it < C * C / 8 / kT; ++it) {
+    const int idx = tid + kT * it, row = idx / 8, c8 = (idx % 8) * 8;
     const bool on = (c8 >> 4) <= (row >> 4);
     bf16x8 v;
 #pragma unroll
@@ -292,13 +294,14 @@ __global__ __launch_bounds__(kThreads) void k_prep_gdn(const Params p) {
 
   // --- W (fp32 inputs) and U' tiles: lane owns W[r][j .. j+3] ---
   {
-    const int r = 16 * w + (l & 15);
+    const int r = 16 * rb + (l & 15);
 #pragma unroll
-    for (int jb = 0; jb < D / 16; ++jb) {
+    for (int q = 0; q < D / 32; ++q) {   // this wave's half of the 16-wide column blocks
+      const int jb = hf * (D / 32) + q;
       f32x4 aW = zero4(), aU = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < C; k0 += 32) {
-        const bf16x8 b = frag_rk(As, PC, 16 * w, k0);  // B[s][r] = A[r][s]
+        const bf16x8 b = frag_rk(As, PC, 16 * rb, k0);  // B[s][r] = A[r][s]
         if constexpr (kMat) aW = mma(frag_kc(Ks, PD, 16 * jb, k0), b, aW);
         aU = mma(frag_kc(Vs, PD, 16 * jb, k0), b, aU);
       }
@@ -809,7 +812,7 @@ int dispatch(const Params& p, void* stream) {
 template <int D, typename TIO>
 struct RunPrep {
   static void run(const Params& p, hipStream_t s) {
-    k_prep_gdn<D, TIO><<<dim3(p.NC, p.H), kThreads, 0, s>>>(p);
+    k_prep_gdn<D, TIO><<<dim3(p.NC, p.H), kPrepThreads, 0, s>>>(p);
   }
 };
 template <int D, typename TIO>
