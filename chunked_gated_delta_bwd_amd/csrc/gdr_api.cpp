@@ -110,11 +110,16 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   return L;
 }
 
+// Token tensors may be NULL only when there are no tokens (an empty tensor has
+// no storage); everything else the call reads or writes is required.
+bool no_tokens(const gdr_shape* s) { return int64_t(s->B) * s->T == 0; }
+
 gdr_status check_inputs(const gdr_shape* s, const gdr_inputs* in) {
   if (!in) return fail(GDR_EINVAL, "inputs is NULL");
   const void* req[] = {in->q, in->k, in->v, in->g, in->beta_logit};
   const char* names[] = {"q", "k", "v", "g", "beta_logit"};
   for (int i = 0; i < 5; ++i) {
+    if (!req[i] && no_tokens(s)) continue;
     if (!req[i]) return fail(GDR_EINVAL, "input %s is NULL", names[i]);
     if (!aligned16(req[i])) return fail(GDR_EINVAL, "input %s is not 16-byte aligned", names[i]);
   }
@@ -130,13 +135,14 @@ gdr_status check_inputs(const gdr_shape* s, const gdr_inputs* in) {
 }
 
 gdr_status check_grads(const gdr_shape* s, const void* dO, const float* dht, const gdr_grads* gr) {
-  if (!dO) return fail(GDR_EINVAL, "dO is NULL");
+  if (!dO && !no_tokens(s)) return fail(GDR_EINVAL, "dO is NULL");
   if (!aligned16(dO)) return fail(GDR_EINVAL, "dO is not 16-byte aligned");
   if (dht && !aligned16(dht)) return fail(GDR_EINVAL, "dht is not 16-byte aligned");
   if (!gr) return fail(GDR_EINVAL, "grads is NULL");
   const void* req[] = {gr->dq, gr->dk, gr->dv, gr->dg, gr->dbeta};
   const char* names[] = {"dq", "dk", "dv", "dg", "dbeta"};
   for (int i = 0; i < 5; ++i) {
+    if (!req[i] && no_tokens(s)) continue;
     if (!req[i]) return fail(GDR_EINVAL, "output %s is NULL", names[i]);
     if (!aligned16(req[i])) return fail(GDR_EINVAL, "output %s is not 16-byte aligned", names[i]);
   }
@@ -335,7 +341,7 @@ gdr_status gdr_fwd_recompute(const gdr_shape* shape, const gdr_inputs* in, void*
 
 gdr_status gdr_fwd(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes, void* o, float* ht,
                    void* stream) {
-  if (!o) return fail(GDR_EINVAL, "o is NULL");
+  if (!o && !(shape && no_tokens(shape))) return fail(GDR_EINVAL, "o is NULL");
   return run(kFwd, shape, in, nullptr, nullptr, ws, ws_bytes, nullptr, ht, stream, -1, o);
 }
 

@@ -80,7 +80,8 @@ typedef struct {
 /* Below, CHANNEL stands for either per-channel gate (GDR_GATE_CHANNEL or
  * GDR_GATE_CHANNEL_SIGMOID): both take the raw gate g, A_log and dt_bias and return
  * dg, dA_log and ddt_bias in the same shapes. */
-typedef struct {                    /* device pointers */
+typedef struct {                    /* device pointers; the token tensors (q, k, v, g, beta_logit) may be
+                                       NULL when B * T == 0 */
   const void *q, *k;                /* [B,T,Hk,Dk] dtype (Hk = H unless grouped) */
   const void *v;                    /* [B,T,H,Dv] dtype */
   const void *g;                    /* SCALAR: [B,T,H] log decay; CHANNEL: [B,T,H,Dk] raw gate; dtype */
@@ -90,7 +91,8 @@ typedef struct {                    /* device pointers */
   const float *h0;                  /* [N,H,Dv,Dk] or NULL (zero initial state) */
 } gdr_inputs;
 
-typedef struct {                    /* device pointers, all overwritten */
+typedef struct {                    /* device pointers, all overwritten; the token gradients (dq, dk, dv,
+                                       dg, dbeta) may be NULL when B * T == 0 */
   void *dq, *dk;                    /* [B,T,Hk,Dk] dtype (Hk = H unless grouped) */
   void *dv;                         /* [B,T,H,Dv] dtype */
   void *dg;                         /* SCALAR: [B,T,H]; CHANNEL: [B,T,H,Dk] (w.r.t. the raw gate); dtype */

@@ -86,3 +86,11 @@ def test_forward_then_backward_equals_fused(gate):
     for key, x in out.items():
         if x is not None:
             assert np.array_equal(x.double().cpu().numpy(), fused[key]), key
+
+
+def test_forward_no_tokens():
+    """T = 0: o has no storage (a NULL pointer), ht = h0 exactly."""
+    inp = synth.generate(synth.Spec("z", 1, "bf16", H=2, K=64, V=64, lengths=[0, 0], h0_std=0.3, seed=92))
+    got, _ = gpu_fwd(inp)
+    assert got["o"].size == 0
+    assert np.array_equal(got["ht"], inp["h0"].double().numpy())

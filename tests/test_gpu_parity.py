@@ -258,3 +258,18 @@ def test_grouped_heads_workload_sampled_group():
     inp = synth.generate(synth.workload("gdn_gqa4_bf16_t32768_h32_d128"))
     got = gpu_run(inp)
     _check(inp, got, "gdn_gqa4_t32768_h32", heads=[20, 21, 22, 23])
+
+
+@pytest.mark.parametrize("gate", [0, 1, 2])
+def test_no_tokens(gate):
+    """Every sequence empty (T = 0): the token tensors have no storage (NULL
+    pointers), ht = h0 and dh0 = dht exactly, the parameter gradients are zero."""
+    log(f"case no tokens, gate {gate}")
+    inp = synth.generate(synth.Spec("z", gate, "bf16", H=2, K=64, V=64, lengths=[0, 0], h0_std=0.3,
+                                    dht_std=0.3, seed=91))
+    assert inp["T"] == 0
+    got = gpu_run(inp)
+    ref = oracle.run(inp)
+    assert np.array_equal(got["dh0"], ref["dh0"]) and np.array_equal(got["ht"], ref["ht"])
+    if gate:
+        assert not got["dA_log"].any() and not got["ddt_bias"].any()
