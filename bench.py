@@ -37,15 +37,15 @@ CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 # valid only for the kernel sources they were taken on:
 # (workload, stage, sha256 prefix) -> bytes.
 MEASURED_TRAFFIC = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "5e698d1e8066"): 0.717e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "5e698d1e8066"): 1.690e9,
-    ("gdn_bf16_t32768_h16_d128", "grads", "5e698d1e8066"): 1.855e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "5e698d1e8066"): 0.747e9,
-    ("gdn_bf16_t32768_h16_d128", "output", "5e698d1e8066"): 0.745e9,
-    ("kda_bf16_t32768_h16_d128", "prep", "5e698d1e8066"): 1.846e9,
-    ("kda_bf16_t32768_h16_d128", "chain_both", "5e698d1e8066"): 2.947e9,
-    ("kda_bf16_t32768_h16_d128", "grads", "5e698d1e8066"): 3.139e9,
-    ("kda_bf16_t32768_h16_d128", "finish", "5e698d1e8066"): 0.004e9,
+    ("gdn_bf16_t32768_h16_d128", "prep", "0f2298a18f1b"): 0.717e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "0f2298a18f1b"): 1.690e9,
+    ("gdn_bf16_t32768_h16_d128", "grads", "0f2298a18f1b"): 1.855e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "0f2298a18f1b"): 0.747e9,
+    ("gdn_bf16_t32768_h16_d128", "output", "0f2298a18f1b"): 0.745e9,
+    ("kda_bf16_t32768_h16_d128", "prep", "0f2298a18f1b"): 1.846e9,
+    ("kda_bf16_t32768_h16_d128", "chain_both", "0f2298a18f1b"): 2.947e9,
+    ("kda_bf16_t32768_h16_d128", "grads", "0f2298a18f1b"): 3.139e9,
+    ("kda_bf16_t32768_h16_d128", "finish", "0f2298a18f1b"): 0.004e9,
 }
 
 
