@@ -273,3 +273,41 @@ def test_no_tokens(gate):
     assert np.array_equal(got["dh0"], ref["dh0"]) and np.array_equal(got["ht"], ref["ht"])
     if gate:
         assert not got["dA_log"].any() and not got["ddt_bias"].any()
+
+
+# ---------------------------------------------------------------------------
+# mixed small configurations: every gate with both dtypes and head dims, grouped
+# heads, dense batches and ragged varlen packs together (one seeded draw each)
+# ---------------------------------------------------------------------------
+def _mixed_specs():
+    rng = np.random.default_rng(2024)
+    specs = []
+    for i in range(8):
+        gate = i % 3
+        dtype = "f32" if i % 4 == 3 else "bf16"
+        D = 64 if i % 2 else 128
+        Hk = int(rng.choice([1, 2]))
+        H = Hk * int(rng.choice([1, 2, 3]))
+        if i % 2:
+            lengths = [int(x) for x in rng.integers(0, 150, size=int(rng.integers(1, 4)))]
+            kw = dict(lengths=lengths)
+        else:
+            kw = dict(B=int(rng.integers(1, 3)), T=int(rng.integers(1, 200)))
+        specs.append((f"mix{i}_g{gate}_{dtype}_d{D}_h{H}_hk{Hk}",
+                      synth.Spec(f"m{i}", gate, dtype, H=H, Hk=Hk, K=D, V=D, h0_std=0.2, dht_std=0.2,
+                                 seed=300 + i, **kw)))
+    return specs
+
+
+MIXED = _mixed_specs()
+
+
+@pytest.mark.parametrize("name,spec", MIXED, ids=[s[0] for s in MIXED])
+def test_mixed_small_against_oracle(name, spec):
+    log(f"case {name}")
+    inp = synth.generate(spec)
+    got = gpu_run(inp)
+    if spec.gate == 2:
+        _check_kdas(inp, got, name)
+    else:
+        _check(inp, got, name)
