@@ -267,6 +267,36 @@ __device__ __forceinline__ int64_t tok(int t, int H, int h) { return int64_t(t) 
 template <typename P>
 __device__ __forceinline__ int64_t qk_tok(const P& p, int t, int h) { return int64_t(t) * p.Hk + h / p.G; }
 
+// (chunk, value head) of a per-(chunk, head) workgroup on an NC x H grid.  With
+// grouped heads the G value heads of a key head read the same q, k rows, so their
+// workgroups for one chunk are dealt to one XCD back to back (workgroups go
+// round-robin over the 8 XCDs: ids j 8G + 8 i + x, i < G, all land on XCD x), where
+// that XCD's L2 serves the rows after the first read.  A bijection of the grid:
+// the (chunk, key head) pairs past the last whole set of eight keep their members
+// consecutive.
+template <typename P>
+__device__ __forceinline__ void chunk_head(const P& p, int& c, int& h) {
+  if (p.G == 1) {
+    c = blockIdx.x;
+    h = blockIdx.y;
+    return;
+  }
+  const int G = p.G, L = blockIdx.x + p.NC * blockIdx.y;
+  const int npair = p.NC * p.Hk, p8 = npair / 8 * 8;
+  int pair, gi;
+  if (L < p8 * G) {
+    const int j = L / (8 * G), r = L % (8 * G);
+    pair = 8 * j + r % 8;
+    gi = r / 8;
+  } else {
+    const int rem = L - p8 * G;
+    pair = p8 + rem / G;
+    gi = rem % G;
+  }
+  c = pair / p.Hk;
+  h = (pair % p.Hk) * G + gi;
+}
+
 __device__ __forceinline__ void st_bf16x4(bf16* dst, float a, float b, float c, float d) {
   *reinterpret_cast<uint2*>(dst) = pack4_bf16(a, b, c, d);
 }

@@ -108,7 +108,8 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
   __shared__ __attribute__((aligned(16))) bf16 Vsl[C * PD];
   __shared__ float beta_s[C], tot_s[NPART][D];
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  int c, h;
+  chunk_head(p, c, h);
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
@@ -515,7 +516,8 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
   constexpr bool kTailInY = Sm::y_tail >= kTailFloats * 4;
   __shared__ __attribute__((aligned(16))) float TX[kTailInY ? 4 : kTailFloats];
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  int c, h;
+  chunk_head(p, c, h);
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();

@@ -64,7 +64,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   // into bf16 high and low parts); bf16 inputs use the raw rows and row factors
   constexpr bool kMat = std::is_same<TIO, float>::value;
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  int c, h;
+  chunk_head(p, c, h);
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
   const int tid = threadIdx.x, l = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
@@ -383,7 +384,8 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
   const float* const rk_s = sc_s[2];
   const float* const beta_s = sc_s[3];
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  int c, h;
+  chunk_head(p, c, h);
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
   const int tid = threadIdx.x, l = lane_id();

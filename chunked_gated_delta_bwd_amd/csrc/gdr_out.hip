@@ -41,7 +41,8 @@ __global__ __launch_bounds__(kOutThreads) void k_output(const Params p) {
   __shared__ __attribute__((aligned(1024))) char Us[D * C * 2];   // U^T [v][s]
   __shared__ __attribute__((aligned(256))) float fq_s[C];
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  int c, h;
+  chunk_head(p, c, h);
   const ChunkEntry ce = p.ctab[c];
   const int t0 = ce.t_start, len = ce.len;
   const int l = lane_id();
