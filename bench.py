@@ -33,19 +33,23 @@ GATE_NAMES = {0: "scalar", 1: "channel", 2: "channel_sigmoid"}
 METRIC = "gated-delta-rule bwd tokens/s + ms/bwd at T=32k,H=16,D=128 bf16; MFMA %"
 CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 # HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by a
-# 1 GiB copy; profiles/gdn_t32768_h16_d128.md, profiles/kda_t32768_h16_d128.md),
+# 1 GiB copy; the kernel profiles under profiles/),
 # valid only for the kernel sources they were taken on:
 # (workload, stage, sha256 prefix) -> bytes.
 MEASURED_TRAFFIC = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "0f2298a18f1b"): 0.717e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "0f2298a18f1b"): 1.690e9,
-    ("gdn_bf16_t32768_h16_d128", "grads", "0f2298a18f1b"): 1.855e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "0f2298a18f1b"): 0.747e9,
-    ("gdn_bf16_t32768_h16_d128", "output", "0f2298a18f1b"): 0.745e9,
-    ("kda_bf16_t32768_h16_d128", "prep", "0f2298a18f1b"): 1.846e9,
-    ("kda_bf16_t32768_h16_d128", "chain_both", "0f2298a18f1b"): 2.947e9,
-    ("kda_bf16_t32768_h16_d128", "grads", "0f2298a18f1b"): 3.139e9,
-    ("kda_bf16_t32768_h16_d128", "finish", "0f2298a18f1b"): 0.004e9,
+    ("gdn_bf16_t32768_h16_d128", "prep", "32d9f090b8bf"): 0.717e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "32d9f090b8bf"): 1.690e9,
+    ("gdn_bf16_t32768_h16_d128", "grads", "32d9f090b8bf"): 1.855e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "32d9f090b8bf"): 0.747e9,
+    ("gdn_bf16_t32768_h16_d128", "output", "32d9f090b8bf"): 0.745e9,
+    ("kda_bf16_t32768_h16_d128", "prep", "32d9f090b8bf"): 1.846e9,
+    ("kda_bf16_t32768_h16_d128", "chain_both", "32d9f090b8bf"): 2.949e9,
+    ("kda_bf16_t32768_h16_d128", "grads", "32d9f090b8bf"): 3.138e9,
+    ("kda_bf16_t32768_h16_d128", "finish", "32d9f090b8bf"): 0.004e9,
+    ("gdn_gqa4_bf16_t32768_h32_d128", "prep", "32d9f090b8bf"): 1.003e9,
+    ("gdn_gqa4_bf16_t32768_h32_d128", "chain_both", "32d9f090b8bf"): 3.390e9,
+    ("gdn_gqa4_bf16_t32768_h32_d128", "grads", "32d9f090b8bf"): 3.256e9,
+    ("gdn_gqa4_bf16_t32768_h32_d128", "finish", "32d9f090b8bf"): 0.672e9,
 }
 
 
