@@ -898,8 +898,28 @@ __global__ __launch_bounds__(kChainThreads) void k_chain(const Params p, int mod
   }
   constexpr int ns = D / 16;
   const int xcd = b % 8, y = b / 8;
-  const int sl = y % ns;
-  const int gidx = (y / ns) * 8 + xcd;
+  const int sl = y % ns, t = y / ns;
+  // (sequence, head) of slot t on this XCD.  With grouped heads the G value heads
+  // of a key head read the same q, k rows, so they take consecutive slots of one
+  // XCD (its L2 then serves the rows they share); the (sequence, key head) pairs
+  // past the last whole set of eight keep the plain order.
+  int gidx;
+  if (p.G == 1) {
+    gidx = t * 8 + xcd;
+  } else {
+    const int npair = p.N * p.Hk, p8 = npair / 8 * 8;
+    const int L = t * 8 + xcd;
+    int pair, gi;
+    if (L < p8 * p.G) {
+      pair = (t / p.G) * 8 + xcd;
+      gi = t % p.G;
+    } else {
+      const int rem = L - p8 * p.G;
+      pair = p8 + rem / p.G;
+      gi = rem % p.G;
+    }
+    gidx = (pair / p.Hk) * p.H + (pair % p.Hk) * p.G + gi;
+  }
   if (gidx >= p.N * p.H) return;
   const int si = gidx / p.H, h = gidx % p.H;
   if (role == 0)
