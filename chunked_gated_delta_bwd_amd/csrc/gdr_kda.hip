@@ -435,7 +435,13 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
   __syncthreads();
 
   // --- W^T and U'^T tiles: lane owns W[r][j .. j+3]; U' = A_h V_h + A_h V_l + A_l V_h,
-  // stored as bf16 high + low parts ---
+  // stored as bf16 high + low parts.  The three tiles are staged in LDS no longer
+  // read (W over Qn / X, U' high over Gamma, U' low over L) and leave in 16-byte
+  // row pieces ---
+  bf16* const Wst = reinterpret_cast<bf16*>(QX);
+  bf16* const Uhst = reinterpret_cast<bf16*>(Gs);
+  bf16* const Ulst = reinterpret_cast<bf16*>(Lf);
+  static_assert(C * PD * 2 <= kQX && C * PD * 2 <= C * PG * 4 && C * PD * 2 <= C * PL * 4, "staging fits");
   {
     const int r = 16 * rb + jj;
 #pragma unroll
@@ -453,16 +459,25 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
         aU = mma(vh, bl, aU);
       }
       const int j0 = 16 * jb + 4 * g;
-      st_bf16x4(p.W + (ch * C + r) * D + j0, aW[0], aW[1], aW[2], aW[3]);
+      st_bf16x4(Wst + r * PD + j0, aW[0], aW[1], aW[2], aW[3]);
       float hi[4], lo[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         hi[i] = float(to_bf16(aU[i]));
         lo[i] = aU[i] - hi[i];
       }
-      st_bf16x4(p.Up + (ch * C + r) * D + j0, hi[0], hi[1], hi[2], hi[3]);
-      st_bf16x4(p.Uplo + (ch * C + r) * D + j0, lo[0], lo[1], lo[2], lo[3]);
+      st_bf16x4(Uhst + r * PD + j0, hi[0], hi[1], hi[2], hi[3]);
+      st_bf16x4(Ulst + r * PD + j0, lo[0], lo[1], lo[2], lo[3]);
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < C * D / 8 / kT; ++it) {
+    const int idx = tid + kT * it, row = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+    const int64_t o = (ch * C + row) * D + c8;
+    *reinterpret_cast<u32x4*>(p.W + o) = *reinterpret_cast<const u32x4*>(Wst + row * PD + c8);
+    *reinterpret_cast<u32x4*>(p.Up + o) = *reinterpret_cast<const u32x4*>(Uhst + row * PD + c8);
+    *reinterpret_cast<u32x4*>(p.Uplo + o) = *reinterpret_cast<const u32x4*>(Ulst + row * PD + c8);
   }
 }
 
