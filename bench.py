@@ -37,19 +37,19 @@ CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 # valid only for the kernel sources they were taken on:
 # (workload, stage, sha256 prefix) -> bytes.
 MEASURED_TRAFFIC = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "b3f5de1626df"): 0.717e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "b3f5de1626df"): 1.690e9,
-    ("gdn_bf16_t32768_h16_d128", "grads", "b3f5de1626df"): 1.855e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "b3f5de1626df"): 0.747e9,
-    ("gdn_bf16_t32768_h16_d128", "output", "b3f5de1626df"): 0.745e9,
-    ("kda_bf16_t32768_h16_d128", "prep", "b3f5de1626df"): 1.845e9,
-    ("kda_bf16_t32768_h16_d128", "chain_both", "b3f5de1626df"): 2.956e9,
-    ("kda_bf16_t32768_h16_d128", "grads", "b3f5de1626df"): 3.138e9,
-    ("kda_bf16_t32768_h16_d128", "finish", "b3f5de1626df"): 0.004e9,
-    ("gdn_gqa4_bf16_t32768_h32_d128", "prep", "b3f5de1626df"): 1.003e9,
-    ("gdn_gqa4_bf16_t32768_h32_d128", "chain_both", "b3f5de1626df"): 2.784e9,
-    ("gdn_gqa4_bf16_t32768_h32_d128", "grads", "b3f5de1626df"): 3.256e9,
-    ("gdn_gqa4_bf16_t32768_h32_d128", "finish", "b3f5de1626df"): 0.672e9,
+    ("gdn_bf16_t32768_h16_d128", "prep", "2df3a0f67d78"): 0.717e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "2df3a0f67d78"): 1.690e9,
+    ("gdn_bf16_t32768_h16_d128", "grads", "2df3a0f67d78"): 1.855e9,
+    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "2df3a0f67d78"): 0.747e9,
+    ("gdn_bf16_t32768_h16_d128", "output", "2df3a0f67d78"): 0.745e9,
+    ("kda_bf16_t32768_h16_d128", "prep", "2df3a0f67d78"): 1.841e9,
+    ("kda_bf16_t32768_h16_d128", "chain_both", "2df3a0f67d78"): 2.955e9,
+    ("kda_bf16_t32768_h16_d128", "grads", "2df3a0f67d78"): 3.138e9,
+    ("kda_bf16_t32768_h16_d128", "finish", "2df3a0f67d78"): 0.004e9,
+    ("gdn_gqa4_bf16_t32768_h32_d128", "prep", "2df3a0f67d78"): 1.003e9,
+    ("gdn_gqa4_bf16_t32768_h32_d128", "chain_both", "2df3a0f67d78"): 2.784e9,
+    ("gdn_gqa4_bf16_t32768_h32_d128", "grads", "2df3a0f67d78"): 3.256e9,
+    ("gdn_gqa4_bf16_t32768_h32_d128", "finish", "2df3a0f67d78"): 0.672e9,
 }
 
 
