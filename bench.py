@@ -6,10 +6,17 @@ fused entry point gdr_fwd_bwd) over the headline workload: GDN scalar gate,
 B=1, T=32768, H=16, Dk=Dv=128, bf16 inputs, h0/dht ~ N(0, 0.1), synthetic
 seeded inputs already resident in HBM.  Prints one JSON line.
 
-Besides the whole-step time it times every kernel alone (HIP events on the
-stream the library launches on), reports the roofline fraction of the dominant
-kernel from its algorithmic FLOPs or bytes, and times the float64 CPU oracle on
-a bounded sample of the same workload (the first --cpu-tokens tokens, all heads).
+ms_per_step is the median of the per-step times (a HIP event recorded after
+every step on the stream the library launches on).  Every kernel is then timed
+alone the same way (median over --stage-iters launches).  The roofline record
+is the dominant kernel's bf16 MFMA fraction (algorithmic FLOPs of the chunked
+method over its event-timed duration, against the 2.5 PFLOP/s dense peak),
+with its HBM fraction beside it and, where rocprofv3 counter runs on the same
+kernel sources exist, the counter-measured MFMA FLOPs and HBM bytes.  The path
+record is the roofline fraction of the whole step: the larger of its MFMA and
+HBM floors (476.5 kFLOP and 1,800 B per token-head) over the measured time.
+The float64 CPU oracle is timed on a bounded sample of the same workload (the
+first --cpu-tokens tokens, all heads).
 """
 
 from __future__ import annotations
@@ -19,6 +26,7 @@ import json
 import os
 import sys
 import time
+from typing import Dict
 
 import torch
 
@@ -32,24 +40,12 @@ from chunked_gated_delta_bwd_amd import synth  # noqa: E402
 GATE_NAMES = {0: "scalar", 1: "channel", 2: "channel_sigmoid"}
 METRIC = "gated-delta-rule bwd tokens/s + ms/bwd at T=32k,H=16,D=128 bf16; MFMA %"
 CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
-# HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by a
-# 1 GiB copy; the kernel profiles under profiles/),
-# valid only for the kernel sources they were taken on:
-# (workload, stage, sha256 prefix) -> bytes.
-MEASURED_TRAFFIC = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "2df3a0f67d78"): 0.717e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "2df3a0f67d78"): 1.690e9,
-    ("gdn_bf16_t32768_h16_d128", "grads", "2df3a0f67d78"): 1.855e9,
-    ("gdn_bf16_t32768_h16_d128", "chain_fwd", "2df3a0f67d78"): 0.747e9,
-    ("gdn_bf16_t32768_h16_d128", "output", "2df3a0f67d78"): 0.745e9,
-    ("kda_bf16_t32768_h16_d128", "prep", "2df3a0f67d78"): 1.841e9,
-    ("kda_bf16_t32768_h16_d128", "chain_both", "2df3a0f67d78"): 2.955e9,
-    ("kda_bf16_t32768_h16_d128", "grads", "2df3a0f67d78"): 3.138e9,
-    ("kda_bf16_t32768_h16_d128", "finish", "2df3a0f67d78"): 0.004e9,
-    ("gdn_gqa4_bf16_t32768_h32_d128", "prep", "2df3a0f67d78"): 1.003e9,
-    ("gdn_gqa4_bf16_t32768_h32_d128", "chain_both", "2df3a0f67d78"): 2.784e9,
-    ("gdn_gqa4_bf16_t32768_h32_d128", "grads", "2df3a0f67d78"): 3.256e9,
-    ("gdn_gqa4_bf16_t32768_h32_d128", "finish", "2df3a0f67d78"): 0.672e9,
+# Per-launch rocprofv3 counter readings (the summaries under profiles/), valid
+# only for the kernel sources they were taken on:
+# (workload, stage, sha256 prefix of the kernel sources) -> readings.
+#   traffic:   HBM bytes, FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB device copy
+#   mfma_flop: SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (bf16 MFMA FLOPs)
+MEASURED = {
 }
 
 
@@ -133,17 +129,43 @@ def algorithmic_work(inp, stage: str):
     raise KeyError(stage)
 
 
-def time_it(fn, iters: int) -> float:
-    """Average milliseconds per call, HIP events on the current stream."""
+def time_calls(fn, iters: int):
+    """Milliseconds of each of `iters` back-to-back calls: HIP events recorded
+    between the calls on the current stream (the stream the library launches
+    on), bracketed by device synchronisations."""
     stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(iters):
+    ev[0].record(stream)
+    for i in range(iters):
         fn()
-    end.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / iters
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def host_cpu():
+    """The host's logical CPU count, the CPUs this process may run on, and the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return os.cpu_count() or 1, usable, model
 
 
 def cpu_baseline(inp, tokens: int, backward: bool = True):
@@ -166,33 +188,71 @@ def cpu_baseline(inp, tokens: int, backward: bool = True):
     t0 = time.perf_counter()
     oracle.run(sub, nthreads=threads, backward=backward)
     dt = time.perf_counter() - t0
+    nproc, usable, model = host_cpu()
     what = "token recurrence + adjoint" if backward else "token recurrence (forward only)"
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
+            "seconds": round(dt, 3), "nproc": nproc, "cpus_usable": usable, "cpu_model": model,
             "sample": f"first {tokens} of {inp['T']} tokens, all {inp['H']} heads of the same workload; "
                       f"float64 {what}, {threads} threads over (sequence, head)"}
 
 
 def roofline(inp, workload: str, name: str, ms: float) -> Dict:
-    """The roofline record of one kernel: below the ridge point (peak FLOP/s over
-    peak bytes/s) its attainable rate is set by HBM, above it by the matrix cores."""
+    """The roofline record of one kernel of the chunked method (prologue,
+    recursions, gradients: dense 64 x 64 and 64 x D contractions, so the bound
+    is the bf16 matrix cores): algorithmic FLOPs per launch over the measured
+    duration against the dense bf16 peak.  The HBM fraction of its algorithmic
+    bytes and, where a counter run on the same kernel sources exists, the
+    counter-measured HBM bytes and MFMA FLOPs are reported beside it."""
     flops, nbytes = algorithmic_work(inp, name)
     secs = ms * 1e-3
-    if flops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        achieved = nbytes / secs / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        achieved = flops / secs / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = MEASURED_TRAFFIC.get((workload, name, kernel_source_hash()))
-    roof["source_hash"] = kernel_source_hash()
+    achieved = flops / secs / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    h = kernel_source_hash()
+    m = MEASURED.get((workload, name, h), {})
+    roof["traffic"] = m.get("traffic")
     roof["kernel"] = name
-    roof["algorithmic_bytes"] = nbytes
+    roof["ms"] = round(ms, 4)
+    roof["source_hash"] = h
     roof["algorithmic_flops"] = flops
-    roof["mfma_frac"] = round(flops / secs / 1e12 / PEAK_BF16_TFLOPS, 4)
+    roof["algorithmic_bytes"] = nbytes
+    roof["hbm_frac"] = round(nbytes / secs / 1e9 / PEAK_HBM_GBS, 4)
+    if m.get("mfma_flop") is not None:
+        roof["mfma_counter_flops"] = m["mfma_flop"]
+        roof["mfma_counter_frac"] = round(m["mfma_flop"] / secs / 1e12 / PEAK_BF16_TFLOPS, 4)
     return roof
+
+
+# The method's own work per token-head (chunk 64, K = V = 128): 476.5 kFLOP
+# (forward recompute 6CK + 4KV + C^2/3, backward 18CK + 12KV + 4C^2 per token)
+# and 1,800 B (q, k, v, dO, g, b read, dq, dk, dv, dg, db written, bf16).
+def path_floors(inp):
+    K, V = inp["K"], inp["V"]
+    th = inp["B"] * inp["T"] * inp["H"]
+    io = 2 if inp["dtype"] == "bf16" else 4
+    flop = th * (6 * C * K + 4 * K * V + C * C / 3 + 18 * C * K + 12 * K * V + 4 * C * C)
+    gk = K if inp["gate"] != 0 else 1
+    Hk = inp.get("Hk") or inp["H"]
+    tok = inp["B"] * inp["T"]
+    # per key head: q, k read, dq, dk written (4 K); per value head: v, dO read and
+    # dv written (3 V), the gate read and dg written (2 gk), the beta logit read and
+    # db written (2)
+    nbytes = tok * io * (2 * 2 * Hk * K + inp["H"] * (3 * V + 2 * gk + 2))
+    return flop, nbytes
+
+
+def path_record(inp, ms: float, kernels, workload: str) -> Dict:
+    flop, nbytes = path_floors(inp)
+    t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9) * 1e3
+    rec = {"frac": round(max(t_mfma, t_hbm) / ms, 4), "mfma_floor_ms": round(t_mfma, 4),
+           "hbm_floor_ms": round(t_hbm, 4), "algorithmic_flops": int(flop), "algorithmic_bytes": int(nbytes)}
+    h = kernel_source_hash()
+    traffic = [MEASURED.get((workload, n, h), {}).get("traffic") for n in kernels]
+    if kernels and all(t is not None for t in traffic):
+        rec["traffic"] = sum(traffic)
+        rec["traffic_ratio"] = round(sum(traffic) / nbytes, 2)
+    return rec
 
 
 def kernel_record(inp, name: str, t: float) -> Dict:
@@ -207,12 +267,12 @@ def kernel_record(inp, name: str, t: float) -> Dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=synth.HEADLINE, choices=synth.WORKLOADS)
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--stage-iters", type=int, default=10)
+    ap.add_argument("--stage-iters", type=int, default=20)
     ap.add_argument("--all-stages", action="store_true",
                     help="also time the forward and reverse recursions alone (two more chain launches)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -255,7 +315,8 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ms = time_it(step, args.steps)
+    times = time_calls(step, args.steps)
+    ms = median(times)
     tokens = inp["B"] * inp["T"]
 
     # every kernel alone (the workspace already holds what earlier stages leave)
@@ -273,7 +334,7 @@ def main() -> int:
         name = B.STAGE_NAMES[stage]
         fn = lambda s=stage: B.gdr_run_stage(prob, dev, dev["dO"], dev["dht"], ws, out, s, ht=ht)  # noqa: E731
         fn()
-        kernels[name] = kernel_record(inp, name, time_it(fn, args.stage_iters))
+        kernels[name] = kernel_record(inp, name, median(time_calls(fn, args.stage_iters)))
     dom = max(path, key=lambda n: kernels[n]["ms"])
     roof = roofline(inp, args.workload, dom, kernels[dom]["ms"])
 
@@ -285,6 +346,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_mean": round(sum(times) / len(times), 4),
+        "timed_region_ms": round(sum(times), 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -293,6 +356,7 @@ def main() -> int:
         "config": {"workload": args.workload, "B": inp["B"], "T": inp["T"], "H": H, "Hk": inp.get("Hk") or H, "D": K,
                    "gate": GATE_NAMES[inp["gate"]], "chunk": C},
         "roofline": roof,
+        "path": path_record(inp, ms, path, args.workload),
         "kernels": kernels,
     }
     if not args.no_cpu:
@@ -314,16 +378,18 @@ def bench_forward(args, inp, dev, prob, ws, out, ht) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ms = time_it(step, args.steps)
+    times = time_calls(step, args.steps)
+    ms = median(times)
     tokens = inp["B"] * inp["T"]
     kernels = {}
     for stage in (B.GDR_STAGE_PREP, B.GDR_STAGE_CHAIN_FWD):
         name = B.STAGE_NAMES[stage]
         fn = lambda s=stage: B.gdr_run_stage(prob, dev, dev["dO"], dev["dht"], ws, out, s, ht=ht)  # noqa: E731
         fn()
-        kernels[name] = kernel_record(inp, name, time_it(fn, args.stage_iters))
+        kernels[name] = kernel_record(inp, name, median(time_calls(fn, args.stage_iters)))
     step()
-    t_out = max(time_it(step, args.stage_iters) - kernels["prep"]["ms"] - kernels["chain_fwd"]["ms"], 1e-4)
+    t_out = max(median(time_calls(step, args.stage_iters)) - kernels["prep"]["ms"] - kernels["chain_fwd"]["ms"],
+                1e-4)
     kernels["output"] = kernel_record(inp, "output", t_out)
     kernels["output"]["derived"] = True
     dom = max(("prep", "chain_fwd"), key=lambda n: kernels[n]["ms"])
@@ -335,6 +401,7 @@ def bench_forward(args, inp, dev, prob, ws, out, ht) -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_mean": round(sum(times) / len(times), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -72,7 +72,7 @@ def load_library():
     P = ctypes.POINTER
     lib.gdr_workspace_bytes.argtypes = [P(Shape), P(ctypes.c_size_t)]
     lib.gdr_fwd_recompute.argtypes = [P(Shape), P(Inputs), ctypes.c_void_p, ctypes.c_size_t,
-                                      ctypes.c_void_p, ctypes.c_void_p]
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.gdr_fwd.argtypes = [P(Shape), P(Inputs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                             ctypes.c_void_p]
     lib.gdr_bwd.argtypes = [P(Shape), P(Inputs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -161,10 +161,10 @@ def _grads(o: Dict) -> Grads:
 
 
 def gdr_fwd_recompute(prob: Problem, t: Dict, ws: torch.Tensor, ht: Optional[torch.Tensor] = None,
-                      stream=None) -> None:
+                      o: Optional[torch.Tensor] = None, stream=None) -> None:
     inp = _inputs(t)
     _check(load_library().gdr_fwd_recompute(ctypes.byref(prob.shape), ctypes.byref(inp), _ptr(ws),
-                                            ws.numel() * ws.element_size(), _ptr(ht), _stream(stream)))
+                                            ws.numel() * ws.element_size(), _ptr(o), _ptr(ht), _stream(stream)))
 
 
 def gdr_fwd(prob: Problem, t: Dict, ws: torch.Tensor, o: torch.Tensor, ht: Optional[torch.Tensor] = None,

@@ -164,31 +164,47 @@ gdr_status check_ws(const gdr::WsLayout& L, const void* ws, size_t ws_bytes) {
   return GDR_OK;
 }
 
-// Builds the chunk and sequence tables on the host and enqueues their upload.
-// Both live back to back at the start of the workspace (one copy).
-gdr_status upload_tables(const gdr_shape* s, const gdr::WsLayout& L, void* ws, hipStream_t stream) {
+gdr_status hip_status(int err, const char* what) {
+  if (err == 0) return GDR_OK;
+  return fail(GDR_EHIP, "%s: %s", what, gdr::hip_error_string(err));
+}
+
+// Enqueues the writes of the chunk and sequence tables (k_tables).  Dense
+// problems take one launch that derives every entry from (B, T); varlen problems
+// order their sequences here, longest first, and pass the entries by value in
+// batches.  No host memory is read after this returns.
+gdr_status enqueue_tables(const gdr_shape* s, const gdr::WsLayout& L, void* ws, hipStream_t stream) {
   const int N = s->N;
-  std::vector<unsigned char> host(L.stab + size_t(N) * sizeof(gdr::SeqEntry));
-  auto* ct = reinterpret_cast<gdr::ChunkEntry*>(host.data() + L.ctab);
-  auto* st = reinterpret_cast<gdr::SeqEntry*>(host.data() + L.stab);
+  if (N == 0) return GDR_OK;
+  char* w = static_cast<char*>(ws);
+  auto* ctab = reinterpret_cast<const gdr::ChunkEntry*>(w + L.ctab);
+  auto* stab = reinterpret_cast<const gdr::SeqEntry*>(w + L.stab);
+  gdr::TableBatch tb;
+  std::memset(&tb, 0, sizeof(tb));
+  if (!s->cu_seqlens_host) {
+    tb.n = N;
+    tb.first = 0;
+    tb.dense_T = s->T;
+    return hip_status(gdr::launch_tables(ctab, stab, tb, stream), "table kernel");
+  }
+  std::vector<gdr::SeqEntry> st(N);
   int64_t c = 0;
   for (int n = 0; n < N; ++n) {
-    const int64_t b = s->cu_seqlens_host ? s->cu_seqlens_host[n] : int64_t(n) * s->T;
-    const int64_t e = s->cu_seqlens_host ? s->cu_seqlens_host[n + 1] : int64_t(n + 1) * s->T;
+    const int64_t b = s->cu_seqlens_host[n], e = s->cu_seqlens_host[n + 1];
     const int len = int(e - b);
     const int nck = (len + gdr::kChunk - 1) / gdr::kChunk;
     st[n] = gdr::SeqEntry{n, len, int32_t(c), nck, int32_t(b), {0, 0, 0}};
-    for (int i = 0; i < nck; ++i, ++c) {
-      const int rows = std::min(gdr::kChunk, len - i * gdr::kChunk);
-      ct[c] = gdr::ChunkEntry{int32_t(b + int64_t(i) * gdr::kChunk), rows, n, i};
-    }
+    c += nck;
   }
-  std::stable_sort(st, st + N, [](const gdr::SeqEntry& x, const gdr::SeqEntry& y) { return x.len > y.len; });
-  if (host.empty()) return GDR_OK;
-  // Pageable source: the runtime stages it before returning, so `host` may die afterwards.
-  hipError_t e = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice,
-                                reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(GDR_EHIP, "hipMemcpyAsync(tables): %s", hipGetErrorString(e));
+  std::stable_sort(st.begin(), st.end(), [](const gdr::SeqEntry& x, const gdr::SeqEntry& y) { return x.len > y.len; });
+  for (int first = 0; first < N; first += gdr::kTableBatch) {
+    tb.n = std::min(gdr::kTableBatch, N - first);
+    tb.first = first;
+    tb.dense_T = -1;
+    for (int i = 0; i < tb.n; ++i) tb.seqs[i] = st[first + i];
+    gdr_status r = hip_status(gdr::launch_tables(ctab, stab, tb, stream), "table kernel");
+    if (r != GDR_OK) return r;
+  }
   return GDR_OK;
 }
 
@@ -234,11 +250,6 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   return p;
 }
 
-gdr_status hip_status(int err, const char* what) {
-  if (err == 0) return GDR_OK;
-  return fail(GDR_EHIP, "%s: %s", what, gdr::hip_error_string(err));
-}
-
 // With grouped heads the kernels write dq, dk per value head into the workspace;
 // group_sum then reduces them into the caller's [tokens][Hk][K] outputs.
 void set_grads(gdr::Params& p, const gdr::WsLayout& L, void* ws, const void* dO, const float* dht,
@@ -269,7 +280,8 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
   if ((st = check_ws(L, ws, ws_bytes)) != GDR_OK) return st;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if ((st = upload_tables(s, L, ws, hs)) != GDR_OK) return st;
+  // a single stage reuses the tables the full call before it wrote
+  if (only < 0 && (st = enqueue_tables(s, L, ws, hs)) != GDR_OK) return st;
   gdr::Params p = make_params(s, L, in, ws);
   p.ht = ht;
   p.o = o;
@@ -334,9 +346,9 @@ gdr_status gdr_workspace_bytes(const gdr_shape* shape, size_t* bytes) {
   return GDR_OK;
 }
 
-gdr_status gdr_fwd_recompute(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes, float* ht,
-                             void* stream) {
-  return run(kFwd, shape, in, nullptr, nullptr, ws, ws_bytes, nullptr, ht, stream);
+gdr_status gdr_fwd_recompute(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes, void* o,
+                             float* ht, void* stream) {
+  return run(kFwd, shape, in, nullptr, nullptr, ws, ws_bytes, nullptr, ht, stream, -1, o);
 }
 
 gdr_status gdr_fwd(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes, void* o, float* ht,

@@ -32,6 +32,19 @@ struct SeqEntry {
   int32_t pad[3];
 };
 
+// Sequence entries handed to k_tables by value (one launch per batch).  With
+// dense_T >= 0 the batch is `n` dense sequences of dense_T tokens numbered from
+// `first`, and `seqs` is not read.
+constexpr int kTableBatch = 56;
+struct TableBatch {
+  int32_t n;         // sequences in this launch
+  int32_t first;     // sequence-table row of the first of them
+  int32_t dense_T;   // dense tokens per sequence, or -1
+  int32_t pad;
+  SeqEntry seqs[kTableBatch];
+};
+static_assert(sizeof(TableBatch) <= 2048, "kernel argument size");
+
 // Byte offsets of every workspace region (all 256-byte aligned).
 struct WsLayout {
   int64_t NC = 0;    // total chunks
@@ -101,6 +114,8 @@ struct Params {
 // Chain-kernel roles.
 enum ChainMode { kChainFwd = 1, kChainBwd = 2, kChainBoth = 3 };
 
+// Chunk and sequence tables from one batch of sequence entries (gdr_tables.hip).
+int launch_tables(const ChunkEntry* ctab, const SeqEntry* stab, const TableBatch& tb, void* stream);
 // Kernel launchers (gdr_kernels.hip).  Return a hipError_t as int.
 int launch_prep(const Params& p, void* stream);
 int launch_chain(const Params& p, int mode, void* stream);

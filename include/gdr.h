@@ -28,10 +28,13 @@
  * row-major [B, T, H, D] (dense) or [1, T_total, H, D] (varlen, B == 1 and
  * T == T_total); per-token scalars are [B, T, H]; states are [N, H, Dv, Dk]
  * fp32.  Device pointers must be 16-byte aligned.  The library never allocates,
- * frees or synchronises: all work is enqueued on `stream` (a hipStream_t; NULL
- * = the null stream).  The workspace carries state from gdr_fwd_recompute to
- * gdr_bwd; its layout is internal (gdr_workspace_region exposes it for tests).
- * Outputs are overwritten, never accumulated.
+ * frees or synchronises, and reads no host memory after a call returns: all
+ * work is enqueued on `stream` (a hipStream_t; NULL = the null stream) as kernel
+ * launches -- the chunk and sequence tables are written into the workspace by a
+ * kernel that receives the sequence lengths as launch arguments -- so a call
+ * can be recorded into a HIP graph.  The workspace carries state from
+ * gdr_fwd_recompute to gdr_bwd; its layout is internal (gdr_workspace_region
+ * exposes it for tests).  Outputs are overwritten, never accumulated.
  *
  * Errors.  All argument checks run before anything is enqueued; a non-OK status
  * means nothing was launched, except GDR_EHIP (a HIP call failed while
@@ -101,39 +104,67 @@ typedef struct {                    /* device pointers, all overwritten; the tok
   float *dA_log, *ddt_bias;         /* CHANNEL: [H], [H,Dk] required; SCALAR: must be NULL */
 } gdr_grads;
 
-/* Bytes of workspace the compute calls need for this shape. */
+/* Bytes of workspace the compute calls need for this shape (host only; no
+ * device work).  The workspace holds the per-chunk intermediates of the chunked
+ * form: the states at chunk starts and the state gradients at chunk ends (the
+ * quantities the FlashQLA overview's sections 2-3 carry between its forward
+ * and backward passes), the in-chunk UT/WY inverse, the gate cumsum and the
+ * chunk/sequence tables.  Returns GDR_EINVAL / GDR_EUNSUPPORTED for a bad shape. */
 gdr_status gdr_workspace_bytes(const gdr_shape* shape, size_t* bytes);
 
-/* Forward recompute: per-chunk prologue (normalisation, beta, in-chunk gate
- * cumsum, the UT/WY inverse A = (I + StrictLower(diag(beta) (K K^T o decay)))^-1
- * and W = A diag(beta) K e^Gamma, U' = A diag(beta) V), then the serial state
- * pass storing the state at the start of every chunk and v_new = U' - W S^T.
- * Optional outputs: ht = final state per sequence ([N,H,Dv,Dk] fp32, NULL to
- * skip).  Leaves what gdr_bwd needs in `ws`; every stage only reads inputs and
- * what earlier stages wrote, so any call may be repeated. */
-gdr_status gdr_fwd_recompute(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes,
+/* Forward recompute: the preprocessing that precedes the backward's main
+ * kernels (FlashQLA GDN backward overview, section 1: a backward call is a
+ * preprocessing stage plus two main kernels, fed the in-chunk cumsum of the
+ * gate; section 3: the UT/WY product X = A_beta K).  Per chunk: normalisation,
+ * beta, the in-chunk gate cumsum, the UT/WY inverse
+ * A = (I + StrictLower(diag(beta) (K K^T o decay)))^-1, U' = A diag(beta) V and
+ * W = A diag(beta) K e^Gamma; then the serial state pass storing the state at
+ * the start of every chunk and v_new = U' - W S^T.
+ * Arguments: shape and inputs as above; ws / ws_bytes a device workspace of at
+ * least gdr_workspace_bytes(shape) bytes, 256-byte aligned; o the forward output
+ * [B,T,H,Dv] in the input dtype (o_t = scale S_t qn_t, formed chunk-parallel as
+ * Qbar S_n^T + P U) or NULL to skip it; ht the final state per sequence
+ * [N,H,Dv,Dk] fp32 or NULL.  Leaves what gdr_bwd needs in `ws`; every stage
+ * only reads inputs and what earlier stages wrote, so the call may be repeated.
+ * Errors: GDR_EINVAL (null required / misaligned pointer, bad shape, gate and
+ * parameter mismatch), GDR_EUNSUPPORTED, GDR_EWORKSPACE; nothing is enqueued
+ * then.  GDR_EHIP if a launch fails. */
+gdr_status gdr_fwd_recompute(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes, void* o,
                              float* ht, void* stream);
 
-/* Forward pass with its output, for training use: gdr_fwd_recompute followed by
- * the chunk-parallel output O = Qbar S_n^T + P U per chunk (Qbar = scale qn e^Gamma,
- * P = scale (Qn Kn^T o decay) on and below the diagonal, U = v_new), the chunked
- * form of o_t = scale S_t qn_t (FlashQLA GDN overview, section 3).  o: [B,T,H,Dv]
- * in the input dtype, 16-byte aligned, required (GDR_EINVAL if NULL); ht as for
- * gdr_fwd_recompute.  Leaves the same workspace, so gdr_bwd may follow. */
+/* The forward pass for training use: gdr_fwd_recompute with the output o
+ * required (GDR_EINVAL if NULL while there are tokens).  o = scale S_t qn_t per
+ * token, formed per chunk as Qbar S_n^T + P U (Qbar = scale qn e^Gamma,
+ * P = scale (Qn Kn^T o decay) on and below the diagonal, U = v_new): the chunked
+ * form of the read-out (FlashQLA GDN overview, section 3).  Leaves the same
+ * workspace, so gdr_bwd may follow. */
 gdr_status gdr_fwd(const gdr_shape* shape, const gdr_inputs* in, void* ws, size_t ws_bytes, void* o, float* ht,
                    void* stream);
 
 /* Backward, after gdr_fwd_recompute on the same shape, inputs and workspace:
- * reverse-chunk state-gradient recursion (dh0), chunk-parallel gradients, and
- * the prepare-backward stage.  dO: [B,T,H,Dv] dtype; dht: [N,H,Dv,Dk] fp32 or
- * NULL (zero). */
+ *  - the reverse-chunk state-gradient recursion, run strictly from the last
+ *    chunk to the first (FlashQLA overview, section 2; its section 3 gives the
+ *    recursion dh <- g_last dh + R^T dO + X^T Y with X = A_beta K), starting
+ *    from dht (NULL = zero, section 1) and returning dh0 in fp32 (section 1);
+ *  - the chunk-parallel gradients of q, k, v, beta and the gate (section 2: the
+ *    compute-bound main backward);
+ *  - the prepare-backward of the FlashKDA K1 page: L2-norm backward (section
+ *    3.3), reverse cumsum of the gate gradient plus the chunk-total term
+ *    (section 5), gate-function backward and the per-head sums dA_log, ddt_bias
+ *    (section 5.2), beta-logit backward (section 6), tail rows masked (section 8).
+ * dO: [B,T,H,Dv] dtype, required unless there are no tokens; dht: [N,H,Dv,Dk]
+ * fp32 or NULL; grads: every token gradient required (dq, dk [B,T,Hk,Dk], dv,
+ * dg, dbeta in the input dtype), dh0 optional, dA_log / ddt_bias required for
+ * the per-channel gates and NULL for the scalar gate.  Errors as for
+ * gdr_fwd_recompute. */
 gdr_status gdr_bwd(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht,
                    void* ws, size_t ws_bytes, gdr_grads* grads, void* stream);
 
 /* The whole backward in one call: the same kernels as gdr_fwd_recompute
  * followed by gdr_bwd, except that the forward state pass and the reverse
  * state-gradient recursion (which do not depend on each other) run side by
- * side in one launch.  Same results; ht may be NULL. */
+ * side in one launch.  Same results, bit for bit; ht may be NULL.  Arguments
+ * and errors as gdr_fwd_recompute and gdr_bwd together. */
 gdr_status gdr_fwd_bwd(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht,
                        void* ws, size_t ws_bytes, gdr_grads* grads, float* ht, void* stream);
 

@@ -4,7 +4,7 @@ compare with the float64 oracle on the same input bytes."""
 from __future__ import annotations
 
 import sys
-from typing import Dict, Iterable, Optional
+from typing import Dict, Optional
 
 import numpy as np
 import torch
@@ -25,6 +25,35 @@ def nerr(x: np.ndarray, ref: np.ndarray) -> float:
     den = np.linalg.norm(ref)
     num = np.linalg.norm(x - ref)
     return float(num / den) if den > 0 else float(num)
+
+
+# A per-row check beside the per-tensor one: a fault confined to a few rows (one
+# tail chunk of one sequence in a 32k-token pack) is diluted below the per-tensor
+# bar, but not below this one.  A row is one (token, head) vector of a token
+# tensor, one per-token scalar, one state row (sequence, head, v) of dh0 / ht, or
+# one head of the parameter gradients; its error is |row - ref_row| divided by
+# the larger of |ref_row| and the root-mean-square row norm of ref (so that rows
+# with a near-zero reference are held in absolute terms).
+ROW_FACTOR = 5.0
+
+
+def _rows(a: np.ndarray, key: str) -> np.ndarray:
+    a = np.asarray(a, dtype=np.float64)
+    if a.ndim <= 1 or (a.ndim == 3 and key in ("dg", "db")):
+        return a.reshape(-1, 1)
+    return a.reshape(-1, a.shape[-1])
+
+
+def row_err(x: np.ndarray, ref: np.ndarray, key: str) -> float:
+    xr, rr = _rows(x, key), _rows(ref, key)
+    if rr.size == 0:
+        return 0.0
+    dn = np.linalg.norm(xr - rr, axis=1)
+    rn = np.linalg.norm(rr, axis=1)
+    rms = float(np.sqrt(np.mean(rn * rn)))
+    if rms == 0.0:
+        return float(dn.max())
+    return float((dn / np.maximum(rn, rms)).max())
 
 
 def log(msg: str) -> None:
@@ -59,53 +88,21 @@ def gpu_run(inp: Dict, mode: str = "fused", exports: bool = False) -> Dict[str, 
     return res
 
 
-def key_heads(inp: Dict, heads: Iterable[int]) -> list:
-    """The q, k heads that value heads `heads` read (grouped heads: h // (H / Hk))."""
-    G = inp["H"] // (inp.get("Hk") or inp["H"])
-    return sorted({h // G for h in heads})
-
-
-def subset_heads(inp: Dict, heads: Iterable[int]) -> Dict:
-    """The same problem restricted to some heads (heads never interact; with
-    grouped heads the value heads must form whole groups, since dq and dk sum
-    over a group)."""
-    heads = list(heads)
-    G = inp["H"] // (inp.get("Hk") or inp["H"])
-    kh = key_heads(inp, heads)
-    assert sorted(heads) == heads and heads == [j * G + i for j in kh for i in range(G)], "whole groups"
-    idx = torch.tensor(heads, dtype=torch.long)
-    kidx = torch.tensor(kh, dtype=torch.long)
-    out = dict(inp)
-    for key in ("q", "k"):
-        out[key] = inp[key].index_select(2, kidx).contiguous()
-    for key in ("v", "dO", "g", "b"):
-        out[key] = inp[key].index_select(2, idx).contiguous()
-    for key in ("h0", "dht"):
-        if inp.get(key) is not None:
-            out[key] = inp[key].index_select(1, idx).contiguous()
-    for key in ("A_log", "dt_bias"):
-        if inp.get(key) is not None:
-            out[key] = inp[key].index_select(0, idx).contiguous()
-    out["H"] = len(heads)
-    out["Hk"] = len(kh)
-    return out
-
-
-def compare(got: Dict, ref: Dict, keys, tol: float, label: str, head_index: Optional[list] = None,
-            key_index: Optional[list] = None) -> Dict:
-    """Normalised error per output; `head_index` picks the value heads the oracle
-    ran, `key_index` the q, k heads (dq, dk) where they differ."""
-    errs = {}
+def compare(got: Dict, ref: Dict, keys, tol: float, label: str, row_tol: Optional[float] = None) -> Dict:
+    """Normalised error per output (|X - ref|_F / |ref|_F <= tol) and the worst
+    row error (<= row_tol, default ROW_FACTOR * tol), over every head."""
+    row_tol = ROW_FACTOR * tol if row_tol is None else row_tol
+    errs, rows = {}, {}
     for key in keys:
         if key not in ref:
             continue
         x = got[key]
-        if head_index is not None:
-            axis = 0 if key in ("dA_log", "ddt_bias") else (1 if key in ("dh0", "ht") else 2)
-            idx = key_index if key in ("dq", "dk") and key_index is not None else head_index
-            x = np.take(x, idx, axis=axis)
+        assert np.shape(x) == np.shape(ref[key]), (label, key, np.shape(x), np.shape(ref[key]))
         errs[key] = nerr(x, ref[key])
-    log(f"[{label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        rows[key] = row_err(x, ref[key], key)
+    log(f"[{label}] " + " ".join(f"{k}={v:.2e}/row {rows[k]:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"{label}: {bad} above {tol}"
+    bad_rows = {k: v for k, v in rows.items() if not v <= row_tol}
+    assert not bad_rows, f"{label}: worst row errors {bad_rows} above {row_tol}"
     return errs

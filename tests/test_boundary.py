@@ -1,7 +1,8 @@
 """C-ABI boundary checks that need no GPU: the library loads, exports every
 symbol declared in include/gdr.h, sizes workspaces, and rejects bad arguments
 before anything is enqueued (every case here fails validation, so no HIP call
-is made)."""
+is made).  If libgdr.so has not been built yet, it is built here (hipcc
+cross-compiles for gfx950 without a GPU); a failed build fails these tests."""
 
 import ctypes
 import os
@@ -14,7 +15,14 @@ from chunked_gated_delta_bwd_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-pytestmark = pytest.mark.skipif(not os.path.exists(B.library_path()), reason="libgdr.so not built")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library():
+    if not os.path.exists(B.library_path()):
+        from chunked_gated_delta_bwd_amd import build
+        build.build()
+    B.load_library()
 
 
 def _declared_symbols():
@@ -159,6 +167,23 @@ def test_fwd_recompute_rejects(case, status):
     with pytest.raises(B.GdrError) as e:
         B.gdr_fwd_recompute(p, t, ws, stream=0)
     assert e.value.status == status
+    # the same with the optional output o given: the same status
+    with pytest.raises(B.GdrError) as e:
+        B.gdr_fwd_recompute(p, t, ws, o=_Fake(0x30000000), stream=0)
+    assert e.value.status == status
+
+
+def test_fwd_recompute_checks_the_optional_output():
+    """o is optional in gdr_fwd_recompute: NULL passes its check (the call then
+    fails on the next bad argument, not on o), a misaligned o is rejected."""
+    p = _prob(gate=0)
+    ws = _Fake(0x40000000, B.gdr_workspace_bytes(p))
+    with pytest.raises(B.GdrError) as e:
+        B.gdr_fwd_recompute(p, _tensors(0), ws, o=_Fake(0x30000008), stream=0)
+    assert e.value.status == B.GDR_EINVAL and "o is not 16-byte aligned" in str(e.value)
+    with pytest.raises(B.GdrError) as e:
+        B.gdr_fwd_recompute(p, _tensors(0, q=None), ws, o=None, stream=0)
+    assert e.value.status == B.GDR_EINVAL and "input q" in str(e.value)
 
 
 @pytest.mark.parametrize("case", ["null_dO", "null_dg", "kda_missing_dA_log", "gdn_with_ddt_bias",

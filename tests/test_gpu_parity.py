@@ -1,9 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the float64 oracle on the
 same seeded input bytes.  Normalised errors |X - ref| / |ref| must stay within
 2e-2 for the per-token gradients (stored in bf16) and 1e-3 for dh0, dA_log and
-ddt_bias (fp32).  Small problems are compared in full; full-size workloads are
-compared on sampled heads (heads are independent, so the oracle runs the exact
-same computation for them)."""
+ddt_bias (fp32), and the worst (token, head) row within five times those bars.
+Every workload is compared in full: all heads, all tokens.""" 
 
 import numpy as np
 import pytest
@@ -11,20 +10,17 @@ import torch
 
 import oracle
 from chunked_gated_delta_bwd_amd import synth
-from gpu_common import (FP32_GRADS, TOKEN_GRADS, TOL_BF16, TOL_FP32, compare, gpu_run, key_heads, log,
-                        subset_heads)
+from gpu_common import FP32_GRADS, TOKEN_GRADS, TOL_BF16, TOL_FP32, compare, gpu_run, log
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def _check(inp, got, label, heads=None, tol_fp32=TOL_FP32):
-    sub = inp if heads is None else subset_heads(inp, heads)
-    kh = None if heads is None else key_heads(inp, heads)
-    ref = oracle.run(sub)
-    compare(got, ref, TOKEN_GRADS, TOL_BF16, label + " grads", heads, kh)
-    compare(got, ref, FP32_GRADS, tol_fp32, label + " fp32", heads, kh)
-    compare(got, ref, ("ht",), TOL_FP32 * 5, label + " ht", heads, kh)
+def _check(inp, got, label, tol_fp32=TOL_FP32):
+    ref = oracle.run(inp)
+    compare(got, ref, TOKEN_GRADS, TOL_BF16, label + " grads")
+    compare(got, ref, FP32_GRADS, tol_fp32, label + " fp32")
+    compare(got, ref, ("ht",), TOL_FP32 * 5, label + " ht")
 
 
 SMALL = [
@@ -80,18 +76,18 @@ def test_workload_b2_t4096_h16():
     _check(inp, got, "gdn_bf16_b2_t4096_h16_d128")
 
 
-def test_workload_varlen12_h32_sampled_heads():
+def test_workload_varlen12_h32():
     inp = synth.generate(synth.workload("gdn_varlen12_bf16_t32768_h32_d128"))
     assert any(L % 64 for L in inp["lengths"])
     got = gpu_run(inp)
-    _check(inp, got, "gdn_varlen12_h32", heads=[0, 17, 31])
+    _check(inp, got, "gdn_varlen12_h32")
 
 
 @pytest.mark.parametrize("H", [16, 32])
-def test_workload_t32768_sampled_heads(H):
+def test_workload_t32768(H):
     inp = synth.generate(synth.workload(f"gdn_bf16_t32768_h{H}_d128"))
     got = gpu_run(inp)
-    _check(inp, got, f"gdn_t32768_h{H}", heads=[0, H - 1])
+    _check(inp, got, f"gdn_t32768_h{H}")
 
 
 # ---------------------------------------------------------------------------
@@ -165,10 +161,10 @@ def test_kda_workload_t8192_h16():
 
 
 @pytest.mark.parametrize("H", [16, 32])
-def test_kda_workload_t32768_sampled_heads(H):
+def test_kda_workload_t32768(H):
     inp = synth.generate(synth.workload(f"kda_bf16_t32768_h{H}_d128"))
     got = gpu_run(inp)
-    _check(inp, got, f"kda_t32768_h{H}", heads=[0, H - 1])
+    _check(inp, got, f"kda_t32768_h{H}")
 
 
 # ---------------------------------------------------------------------------
@@ -252,12 +248,11 @@ def test_grouped_heads_sigmoid_gate():
     _check_kdas(inp, gpu_run(inp), "gqa2_kdas_f32_t200_d64")
 
 
-def test_grouped_heads_workload_sampled_group():
-    """H = 32 value heads over Hk = 8 key heads at T = 32768; one whole group
-    (key head 5, value heads 20..23) against the oracle."""
+def test_grouped_heads_workload():
+    """H = 32 value heads over Hk = 8 key heads at T = 32768, every group."""
     inp = synth.generate(synth.workload("gdn_gqa4_bf16_t32768_h32_d128"))
     got = gpu_run(inp)
-    _check(inp, got, "gdn_gqa4_t32768_h32", heads=[20, 21, 22, 23])
+    _check(inp, got, "gdn_gqa4_t32768_h32")
 
 
 @pytest.mark.parametrize("gate", [0, 1, 2])
