@@ -28,7 +28,9 @@ STAGE_NAMES = {GDR_STAGE_PREP: "prep", GDR_STAGE_CHAIN_FWD: "chain_fwd", GDR_STA
                GDR_STAGE_CHAIN_BOTH: "chain_both", GDR_STAGE_GRADS: "grads", GDR_STAGE_FINISH: "finish"}
 
 SYMBOLS = ("gdr_workspace_bytes", "gdr_fwd_recompute", "gdr_fwd", "gdr_bwd", "gdr_fwd_bwd",
-           "gdr_workspace_region", "gdr_run_stage", "gdr_last_error")
+           "gdr_workspace_region", "gdr_run_stage", "gdr_fwd_bwd_noalloc", "gdr_last_error")
+# the device array gdr_fwd_bwd_noalloc uses as its workspace (128 MiB per GPU)
+NOALLOC_WORKSPACE_BYTES = 128 << 20
 
 
 class GdrError(RuntimeError):
@@ -82,6 +84,8 @@ def load_library():
     lib.gdr_workspace_region.argtypes = [P(Shape), ctypes.c_int32, P(ctypes.c_size_t), P(ctypes.c_size_t)]
     lib.gdr_run_stage.argtypes = [P(Shape), P(Inputs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_size_t, P(Grads), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.gdr_fwd_bwd_noalloc.argtypes = [P(Shape), P(Inputs), ctypes.c_void_p, ctypes.c_void_p, P(Grads),
+                                        ctypes.c_void_p, ctypes.c_void_p]
     lib.gdr_last_error.argtypes = []
     lib.gdr_last_error.restype = ctypes.c_char_p
     for name in SYMBOLS[:-1]:
@@ -187,6 +191,13 @@ def gdr_fwd_bwd(prob: Problem, t: Dict, dO: torch.Tensor, dht: Optional[torch.Te
     _check(load_library().gdr_fwd_bwd(ctypes.byref(prob.shape), ctypes.byref(inp), _ptr(dO), _ptr(dht),
                                       _ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(gr), _ptr(ht),
                                       _stream(stream)))
+
+
+def gdr_fwd_bwd_noalloc(prob: Problem, t: Dict, dO: torch.Tensor, dht: Optional[torch.Tensor], out: Dict,
+                        ht: Optional[torch.Tensor] = None, stream=None) -> None:
+    inp, gr = _inputs(t), _grads(out)
+    _check(load_library().gdr_fwd_bwd_noalloc(ctypes.byref(prob.shape), ctypes.byref(inp), _ptr(dO), _ptr(dht),
+                                              ctypes.byref(gr), _ptr(ht), _stream(stream)))
 
 
 def gdr_run_stage(prob: Problem, t: Dict, dO: torch.Tensor, dht: Optional[torch.Tensor], ws: torch.Tensor,

@@ -9,7 +9,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgdr.so")
-SOURCES = [os.path.join(PKG, "csrc", n) for n in ("gdr_api.cpp", "gdr_kernels.hip", "gdr_chain.hip", "gdr_kda.hip", "gdr_out.hip", "gdr_group.hip", "gdr_tables.hip")]
+SOURCES = [os.path.join(PKG, "csrc", n) for n in ("gdr_api.cpp", "gdr_kernels.hip", "gdr_chain.hip", "gdr_kda.hip", "gdr_out.hip", "gdr_group.hip", "gdr_tables.hip", "gdr_noalloc.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

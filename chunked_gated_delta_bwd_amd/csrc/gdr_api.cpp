@@ -335,6 +335,18 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
 
 }  // namespace
 
+namespace gdr {
+gdr_status set_error(gdr_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+}  // namespace gdr
+
 extern "C" {
 
 gdr_status gdr_workspace_bytes(const gdr_shape* shape, size_t* bytes) {

@@ -130,5 +130,8 @@ int launch_group_sum(const Params& p, const void* src, void* dst, void* stream);
 // prepare-backward, 2 dA_log / ddt_bias reduction.
 int launch_kda(const Params& p, int stage, void* stream);
 const char* hip_error_string(int err);
+// Records the message gdr_last_error() returns to this thread and returns `st`
+// (gdr_api.cpp).
+gdr_status set_error(gdr_status st, const char* fmt, ...);
 
 }  // namespace gdr

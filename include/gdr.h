@@ -197,6 +197,20 @@ enum { GDR_STAGE_PREP = 0, GDR_STAGE_CHAIN_FWD = 1, GDR_STAGE_CHAIN_BWD = 2, GDR
 gdr_status gdr_run_stage(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht,
                          void* ws, size_t ws_bytes, gdr_grads* grads, float* ht, int32_t stage, void* stream);
 
+/* gdr_fwd_bwd without a caller-supplied workspace, for callers that cannot
+ * allocate device memory (code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is a device array of
+ * 128 MiB (134217728 bytes) that the library holds on every GPU it runs on until
+ * the process ends; the call itself allocates and
+ * frees nothing.  Shapes whose gdr_workspace_bytes() exceed it are rejected with
+ * GDR_EWORKSPACE before anything is enqueued.  Every call on one GPU uses that
+ * GPU's single array, so calls that overlap in time on one GPU (different
+ * streams, threads or processes sharing the array) race; calls in order on one
+ * stream are safe.  Inputs, outputs and errors as gdr_fwd_bwd.  The first call
+ * on a device looks up that device's copy of the array (hipGetSymbolAddress). */
+gdr_status gdr_fwd_bwd_noalloc(const gdr_shape* shape, const gdr_inputs* in, const void* dO, const float* dht,
+                               gdr_grads* grads, float* ht, void* stream);
+
 /* Thread-local text for the last non-OK status returned to this thread. */
 const char* gdr_last_error(void);
 
