@@ -277,6 +277,8 @@ def main() -> int:
                     help="also time the forward and reverse recursions alone (two more chain launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy, the reference for HBM byte counters")
+    ap.add_argument("--seq-split", type=int, default=0,
+                    help="segments per sequence for the two recursions: 0 the library's choice, 1 never split")
     ap.add_argument("--path", choices=("bwd", "fwd"), default="bwd",
                     help="bwd: the backward (gdr_fwd_bwd, the headline); fwd: the forward with its output (gdr_fwd)")
     args = ap.parse_args()
@@ -301,7 +303,7 @@ def main() -> int:
     spec = synth.workload(args.workload)
     inp = synth.generate(spec)
     dev = B.to_device(inp)
-    prob = B.Problem.from_inputs(inp)
+    prob = B.Problem.from_inputs(inp, seq_split=args.seq_split)
     ws = B.alloc_workspace(prob)
     out = B.alloc_outputs(inp, dev)
     N, H, K, V = inp["N"], inp["H"], inp["K"], inp["V"]
@@ -354,7 +356,7 @@ def main() -> int:
         "dtype": "bf16" if inp["dtype"] == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": inp["B"], "T": inp["T"], "H": H, "Hk": inp.get("Hk") or H, "D": K,
-                   "gate": GATE_NAMES[inp["gate"]], "chunk": C},
+                   "gate": GATE_NAMES[inp["gate"]], "chunk": C, "seq_split": args.seq_split},
         "roofline": roof,
         "path": path_record(inp, ms, path, args.workload),
         "kernels": kernels,

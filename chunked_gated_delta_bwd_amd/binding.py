@@ -44,7 +44,7 @@ class Shape(ctypes.Structure):
                 ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int64)),
                 ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("gate_scale", ctypes.c_float), ("Hk", ctypes.c_int32)]
+                ("gate_scale", ctypes.c_float), ("Hk", ctypes.c_int32), ("seq_split", ctypes.c_int32)]
 
 
 class Inputs(ctypes.Structure):
@@ -118,17 +118,17 @@ class Problem:
     """
 
     def __init__(self, B: int, T: int, H: int, D: int, N: int, gate: int, dtype: int, scale: float,
-                 cu_seqlens=None, gate_scale: float = 0.0, Hk: int = 0):
+                 cu_seqlens=None, gate_scale: float = 0.0, Hk: int = 0, seq_split: int = 0):
         self.cu = None
         if cu_seqlens is not None:
             cu = torch.as_tensor(cu_seqlens, dtype=torch.int64).contiguous().cpu()
             self.cu = cu
         self.shape = Shape(B, T, H, D, D, N,
                            None if self.cu is None else ctypes.cast(self.cu.data_ptr(), ctypes.POINTER(ctypes.c_int64)),
-                           gate, dtype, scale, gate_scale, Hk)
+                           gate, dtype, scale, gate_scale, Hk, seq_split)
 
     @staticmethod
-    def from_inputs(inp: Dict, varlen: Optional[bool] = None) -> "Problem":
+    def from_inputs(inp: Dict, varlen: Optional[bool] = None, seq_split: int = 0) -> "Problem":
         lengths = inp["lengths"]
         if varlen is None:
             varlen = inp["B"] == 1 and (len(lengths) > 1 or lengths[0] != inp["T"])
@@ -137,9 +137,9 @@ class Problem:
         hk = int(inp.get("Hk") or 0)
         if varlen:
             return Problem(1, inp["T"], inp["H"], inp["K"], inp["N"], inp["gate"], dtype, inp["scale"],
-                           cu_seqlens=inp["cu_seqlens"], gate_scale=gs, Hk=hk)
+                           cu_seqlens=inp["cu_seqlens"], gate_scale=gs, Hk=hk, seq_split=seq_split)
         return Problem(inp["B"], inp["T"], inp["H"], inp["K"], inp["N"], inp["gate"], dtype, inp["scale"],
-                       gate_scale=gs, Hk=hk)
+                       gate_scale=gs, Hk=hk, seq_split=seq_split)
 
 
 def gdr_workspace_bytes(prob: Problem) -> int:

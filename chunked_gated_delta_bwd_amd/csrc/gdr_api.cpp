@@ -44,6 +44,7 @@ gdr_status check_shape(const gdr_shape* s, int64_t* NC_out) {
   if (s->H < 1 || s->B < 1 || s->T < 0 || s->N < 0) return fail(GDR_EINVAL, "bad B/T/H/N");
   if (s->Hk < 0 || s->Hk > s->H || (s->Hk > 0 && s->H % s->Hk != 0))
     return fail(GDR_EINVAL, "Hk (%d) must be 0 or divide H (%d)", s->Hk, s->H);
+  if (s->seq_split < 0) return fail(GDR_EINVAL, "seq_split %d must be >= 0", s->seq_split);
   int64_t NC = 0;
   if (s->cu_seqlens_host == nullptr) {
     if (s->N != s->B) return fail(GDR_EINVAL, "dense shape needs N == B (N=%d, B=%d)", s->N, s->B);
@@ -67,15 +68,103 @@ gdr_status check_shape(const gdr_shape* s, int64_t* NC_out) {
   return GDR_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Sequence split of the recursions (exact: both recursions are affine in the
+// carried state, so a segment run from zero plus the transfer product of its
+// chunks gives its end state for any starting state).
+// ---------------------------------------------------------------------------
+constexpr int kCUs = 256;           // MI355X compute units; one recursion workgroup fits per CU
+constexpr int kMinSegChunks = 8;    // automatic splits keep at least this many chunks per segment
+
+int64_t seq_chunks(const gdr_shape* s, int n) {
+  const int64_t len = s->cu_seqlens_host ? s->cu_seqlens_host[n + 1] - s->cu_seqlens_host[n] : s->T;
+  return (len + gdr::kChunk - 1) / gdr::kChunk;
+}
+
+// Segments of a sequence of nck chunks when P per sequence are asked for.
+int segments_for(int64_t nck, int P, int min_chunks) {
+  if (P <= 1 || nck < 2) return 1;
+  return int(std::max<int64_t>(1, std::min<int64_t>(P, nck / min_chunks)));
+}
+
+struct SplitPlan {
+  int P = 1;           // segments asked per sequence
+  int min_chunks = 1;  // per segment
+  int64_t NS = 0;      // total segments
+  bool split = false;  // some sequence has more than one
+};
+
+// Chain steps (chunk steps of the recursion kernel, one workgroup per CU) a
+// plan takes: the final pass over the longest segment, and for a split the
+// local pass and the boundary composition in front of it.
+int64_t plan_steps(const gdr_shape* s, int P, int min_chunks, SplitPlan* out) {
+  const int64_t ns = s->Dk / 16, H = s->H;
+  int64_t w_final = 0, w_local = 0, longest = 0, nseg = 0;
+  bool split = false;
+  for (int n = 0; n < s->N; ++n) {
+    const int64_t nck = seq_chunks(s, n);
+    const int Pn = segments_for(nck, P, min_chunks);
+    nseg += Pn;
+    w_final += 2 * H * ns * Pn;
+    longest = std::max<int64_t>(longest, (nck + Pn - 1) / Pn);
+    if (Pn > 1) {
+      split = true;
+      w_local += 2 * H * ns * (2 * Pn - 3);   // P - 1 state runs and P - 2 transfer runs per role
+    }
+    if (!s->cu_seqlens_host) {                // dense: every sequence alike
+      nseg *= s->N;
+      w_final *= s->N;
+      w_local *= s->N;
+      break;
+    }
+  }
+  auto rounds = [](int64_t w) { return (w + kCUs - 1) / kCUs; };
+  int64_t steps = rounds(w_final) * longest;
+  if (split) steps += rounds(w_local) * longest + 10 + 3 * P;
+  if (out) {
+    out->P = P;
+    out->min_chunks = min_chunks;
+    out->NS = nseg;
+    out->split = split;
+  }
+  return steps;
+}
+
+SplitPlan plan_split(const gdr_shape* s) {
+  SplitPlan best;
+  // the unsplit recursions already give every compute unit a workgroup: a split
+  // would only add work
+  const bool full = int64_t(2) * s->H * (s->Dk / 16) * s->N >= kCUs;
+  if (s->seq_split == 1 || (s->seq_split == 0 && full)) {
+    plan_steps(s, 1, 1, &best);
+  } else if (s->seq_split >= 2) {
+    plan_steps(s, std::min(s->seq_split, gdr::kMaxSegments), 1, &best);
+  } else {
+    int64_t best_steps = plan_steps(s, 1, 1, &best);
+    for (int P = 2; P <= gdr::kMaxSegments; ++P) {
+      SplitPlan cand;
+      const int64_t st = plan_steps(s, P, kMinSegChunks, &cand);
+      if (st < best_steps) {
+        best_steps = st;
+        best = cand;
+      }
+    }
+  }
+  return best;
+}
+
 gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   gdr::WsLayout L;
   L.NC = NC;
-  const size_t H = s->H, K = s->Dk, V = s->Dv, C = gdr::kChunk, N = s->N;
+  const SplitPlan sp = plan_split(s);
+  L.NS = sp.NS;
+  L.split = sp.split ? 1 : 0;
+  const size_t H = s->H, K = s->Dk, V = s->Dv, C = gdr::kChunk, NS = size_t(sp.NS);
   const size_t gk = s->gate != GDR_GATE_SCALAR ? K : 1;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   L.ctab = take(NC * sizeof(gdr::ChunkEntry));
-  L.stab = take(N * sizeof(gdr::SeqEntry));
+  L.stab = take(NS * sizeof(gdr::SeqEntry));
   L.gam = take(H * NC * C * gk * 4);
   L.rho = take(H * NC * 3 * C * 4);
   L.fac = take(H * NC * 3 * C * 4);
@@ -102,6 +191,8 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.Ulo = take(kda * H * NC * C * V * 2);
   L.Slo = take(kda * H * NC * V * K * 2);
   L.dSlo = take(kda * H * NC * V * K * 2);
+  L.xf = take(L.split * 2 * NS * H * 2 * K * K * 4);
+  L.sb = take(L.split * 2 * NS * H * K * K * 4);
   const size_t grouped = s->Hk > 0 && s->Hk < s->H ? 1 : 0;
   const size_t esz = s->dtype == GDR_BF16 ? 2 : 4;
   L.dqv = take(grouped * size_t(s->B) * size_t(s->T) * H * K * esz);
@@ -169,41 +260,60 @@ gdr_status hip_status(int err, const char* what) {
   return fail(GDR_EHIP, "%s: %s", what, gdr::hip_error_string(err));
 }
 
-// Enqueues the writes of the chunk and sequence tables (k_tables).  Dense
-// problems take one launch that derives every entry from (B, T); varlen problems
-// order their sequences here, longest first, and pass the entries by value in
-// batches.  No host memory is read after this returns.
+// Enqueues the writes of the chunk and segment tables (k_tables).  Dense
+// problems take one launch that derives every entry from (B, T) and the number
+// of segments per sequence; varlen problems split and order their segments here
+// (longest first) and pass the entries by value in batches.  No host memory is
+// read after this returns.
 gdr_status enqueue_tables(const gdr_shape* s, const gdr::WsLayout& L, void* ws, hipStream_t stream) {
   const int N = s->N;
   if (N == 0) return GDR_OK;
   char* w = static_cast<char*>(ws);
   auto* ctab = reinterpret_cast<const gdr::ChunkEntry*>(w + L.ctab);
   auto* stab = reinterpret_cast<const gdr::SeqEntry*>(w + L.stab);
+  const SplitPlan sp = plan_split(s);
   gdr::TableBatch tb;
   std::memset(&tb, 0, sizeof(tb));
   if (!s->cu_seqlens_host) {
     tb.n = N;
     tb.first = 0;
+    tb.kind = 0;
     tb.dense_T = s->T;
+    tb.nseg = segments_for(seq_chunks(s, 0), sp.P, sp.min_chunks);
     return hip_status(gdr::launch_tables(ctab, stab, tb, stream), "table kernel");
   }
-  std::vector<gdr::SeqEntry> st(N);
+  std::vector<gdr::SeqEntry> seqs(N), segs;
+  segs.reserve(size_t(L.NS));
   int64_t c = 0;
   for (int n = 0; n < N; ++n) {
     const int64_t b = s->cu_seqlens_host[n], e = s->cu_seqlens_host[n + 1];
     const int len = int(e - b);
-    const int nck = (len + gdr::kChunk - 1) / gdr::kChunk;
-    st[n] = gdr::SeqEntry{n, len, int32_t(c), nck, int32_t(b), {0, 0, 0}};
+    const int nck = int((len + gdr::kChunk - 1) / gdr::kChunk);
+    seqs[n] = gdr::SeqEntry{n, len, int32_t(c), nck, int32_t(b), 0, 1, 0};
+    const int P = segments_for(nck, sp.P, sp.min_chunks);
+    const int slot0 = int(segs.size());
+    for (int j = 0; j < P; ++j) {
+      const int a0 = j * nck / P, a1 = (j + 1) * nck / P;
+      const int slen = std::min(len, a1 * gdr::kChunk) - a0 * gdr::kChunk;
+      segs.push_back(gdr::SeqEntry{n, slen, int32_t(c + a0), a1 - a0, int32_t(b + int64_t(a0) * gdr::kChunk), j, P,
+                                   slot0 + j});
+    }
     c += nck;
   }
-  std::stable_sort(st.begin(), st.end(), [](const gdr::SeqEntry& x, const gdr::SeqEntry& y) { return x.len > y.len; });
-  for (int first = 0; first < N; first += gdr::kTableBatch) {
-    tb.n = std::min(gdr::kTableBatch, N - first);
-    tb.first = first;
-    tb.dense_T = -1;
-    for (int i = 0; i < tb.n; ++i) tb.seqs[i] = st[first + i];
-    gdr_status r = hip_status(gdr::launch_tables(ctab, stab, tb, stream), "table kernel");
-    if (r != GDR_OK) return r;
+  std::stable_sort(segs.begin(), segs.end(),
+                   [](const gdr::SeqEntry& x, const gdr::SeqEntry& y) { return x.len > y.len; });
+  for (int kind = 1; kind <= 2; ++kind) {
+    const std::vector<gdr::SeqEntry>& v = kind == 1 ? seqs : segs;
+    const int n_all = int(v.size());
+    for (int first = 0; first < n_all; first += gdr::kTableBatch) {
+      tb.n = std::min(gdr::kTableBatch, n_all - first);
+      tb.first = first;
+      tb.kind = kind;
+      tb.dense_T = -1;
+      for (int i = 0; i < tb.n; ++i) tb.e[i] = v[first + i];
+      gdr_status r = hip_status(gdr::launch_tables(ctab, stab, tb, stream), "table kernel");
+      if (r != GDR_OK) return r;
+    }
   }
   return GDR_OK;
 }
@@ -212,6 +322,7 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   gdr::Params p;
   std::memset(&p, 0, sizeof(p));
   p.H = s->H; p.K = s->Dk; p.V = s->Dv; p.N = s->N; p.NC = int32_t(L.NC); p.T = s->B * s->T;
+  p.NS = int32_t(L.NS);
   p.Hk = s->Hk > 0 ? s->Hk : s->H;
   p.G = s->H / p.Hk;
   // the kernels tell the scalar gate from the per-channel one; the per-channel
@@ -247,6 +358,8 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   p.Ulo = reinterpret_cast<uint16_t*>(w + L.Ulo);
   p.Slo = reinterpret_cast<uint16_t*>(w + L.Slo);
   p.dSlo = reinterpret_cast<uint16_t*>(w + L.dSlo);
+  p.xf = L.split ? reinterpret_cast<float*>(w + L.xf) : nullptr;
+  p.sb = L.split ? reinterpret_cast<float*>(w + L.sb) : nullptr;
   return p;
 }
 
@@ -300,12 +413,23 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
     if (p.G > 1 && !e) e = gdr::launch_group_sum(p, p.dk, gr->dk, stream);
     return e;
   };
+  // the recursions: for split sequences the local pass and the boundary
+  // composition first, then the final pass over every segment
+  auto chain = [&](int mode) {
+    int e = 0;
+    if (L.split) {
+      e = gdr::launch_chain(p, mode, gdr::kPassLocal, stream);
+      if (!e) e = gdr::launch_chain_fix(p, mode, stream);
+    }
+    if (!e) e = gdr::launch_chain(p, mode, gdr::kPassFinal, stream);
+    return e;
+  };
   if (only >= 0) {
     switch (only) {
       case GDR_STAGE_PREP: return NC > 0 ? hip_status(prep(), "prep kernel") : GDR_OK;
-      case GDR_STAGE_CHAIN_FWD: return hip_status(gdr::launch_chain(p, gdr::kChainFwd, stream), "chain kernel");
-      case GDR_STAGE_CHAIN_BWD: return hip_status(gdr::launch_chain(p, gdr::kChainBwd, stream), "chain kernel");
-      case GDR_STAGE_CHAIN_BOTH: return hip_status(gdr::launch_chain(p, gdr::kChainBoth, stream), "chain kernel");
+      case GDR_STAGE_CHAIN_FWD: return hip_status(chain(gdr::kChainFwd), "chain kernel");
+      case GDR_STAGE_CHAIN_BWD: return hip_status(chain(gdr::kChainBwd), "chain kernel");
+      case GDR_STAGE_CHAIN_BOTH: return hip_status(chain(gdr::kChainBoth), "chain kernel");
       case GDR_STAGE_GRADS: return NC > 0 ? hip_status(grads(), "gradient kernel") : GDR_OK;
       case GDR_STAGE_FINISH:
         if (NC > 0) return hip_status(finish(), "parameter reduction kernel");
@@ -317,7 +441,7 @@ gdr_status run(int stage, const gdr_shape* s, const gdr_inputs* in, const void* 
     if ((st = hip_status(prep(), "prep kernel")) != GDR_OK) return st;
   }
   const int mode = stage == kFwd ? gdr::kChainFwd : stage == kBwd ? gdr::kChainBwd : gdr::kChainBoth;
-  if ((st = hip_status(gdr::launch_chain(p, mode, stream), "chain kernel")) != GDR_OK) return st;
+  if ((st = hip_status(chain(mode), "chain kernel")) != GDR_OK) return st;
   if (o && NC > 0) {
     if ((st = hip_status(gdr::launch_output(p, stream), "output kernel")) != GDR_OK) return st;
   }

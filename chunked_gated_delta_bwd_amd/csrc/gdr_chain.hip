@@ -31,6 +31,18 @@
 // next chunk (one step to land).  The movers wait for their own loads with
 // vmcnt before the barrier that publishes them.
 //
+// Sequences may be split into segments (runs of whole chunks; one segment per
+// sequence unless the host splits them): both recursions are affine in the
+// carried state, S_{n+1} = S_n F_n + U'^T Khat with F_n = Diag(e^GamC) - W^T Khat,
+// and dS_n = dS_{n+1} F_n^T + (Qbar^T dO - (P^T dO)^T W).  A local pass runs each
+// segment from a zero state (the first one of a role from h0 / dht) and carries
+// the transfer product of its chunks as D more rows of the state, started at the
+// identity with the U' and dO terms left out; k_chain_fix composes the true
+// boundary states in order, and the final pass runs every segment from its true
+// state and stores the per-chunk outputs.  (The FlashQLA overview, section 3,
+// shards the state-gradient recursion over devices with warm-up chunks instead;
+// here the composition is exact.)
+//
 // Tiles are stored unpadded with an XOR swizzle of their 16-byte pieces (one
 // direct-to-LDS load writes 1 KB contiguously, so the swizzle is applied by
 // choosing which global piece each lane fetches).
@@ -481,10 +493,52 @@ __device__ __forceinline__ f32x4 decay4(const float* dec, int jb, int g) {
 }
 
 // ---------------------------------------------------------------------------
+// what one workgroup's recursion starts from, where its end state goes, and
+// whether it stores the per-chunk outputs
+// ---------------------------------------------------------------------------
+struct ChainJob {
+  const float* init;   // the 16 x D slice it starts from (row stride D), or NULL: zero / identity
+  float* fin;          // where the 16 x D end slice goes (row stride D), or NULL
+  bool store;          // per-chunk outputs (S, U / dS, dU) to the workspace
+  bool xfer;           // transfer rows: start at identity rows i0 .. i0 + 15, no U' / dO terms
+  int i0;
+  int v0l;             // V offset of the slice for loads of U' and dO (a state slice's own)
+};
+
+template <int D>
+__device__ __forceinline__ void job_init(const ChainJob& job, f32x4 (&acc)[Dims<D>::NJW], int w, int g, int jj) {
+  constexpr int NJW = Dims<D>::NJW;
+#pragma unroll
+  for (int x = 0; x < NJW; ++x) {
+    const int j = 16 * (w * NJW + x) + 4 * g;
+    if (job.init) {
+      const float4 t = *reinterpret_cast<const float4*>(job.init + jj * D + j);
+      acc[x] = f32x4{t.x, t.y, t.z, t.w};
+    } else if (job.xfer) {
+      const int r = job.i0 + jj;
+      acc[x] = f32x4{r == j ? 1.f : 0.f, r == j + 1 ? 1.f : 0.f, r == j + 2 ? 1.f : 0.f, r == j + 3 ? 1.f : 0.f};
+    } else {
+      acc[x] = zero4();
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void job_fin(const ChainJob& job, const f32x4 (&acc)[Dims<D>::NJW], int w, int g, int jj) {
+  constexpr int NJW = Dims<D>::NJW;
+  if (!job.fin) return;
+#pragma unroll
+  for (int x = 0; x < NJW; ++x) {
+    const int j = 16 * (w * NJW + x) + 4 * g;
+    *reinterpret_cast<float4*>(job.fin + jj * D + j) = make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // the two roles
 // ---------------------------------------------------------------------------
 template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, int h, int sl) {
+__device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, int h, int sl, const ChainJob& job) {
   using Dm = Dims<D>;
   using Cf = ChainCfg<D, TIO, GATE>;
   constexpr int NJW = Dm::NJW;
@@ -492,7 +546,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
   const int l = lane_id();
   const int g = l >> 4, jj = l & 15;
   const SeqEntry se = p.stab[si];
-  const int v0 = 16 * sl;
+  const int v0 = 16 * sl, v0l = job.v0l;
   const int nck = se.nchunks;
   char* Ss = smem + Cf::fS;
   char* Ut = smem + Cf::fU;
@@ -503,16 +557,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
   if (wv < 4) {
     const int w = wv;
     f32x4 acc[NJW];
-#pragma unroll
-    for (int x = 0; x < NJW; ++x) acc[x] = zero4();
-    if (p.h0) {
-#pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        const int j = 16 * (w * NJW + x) + 4 * g;
-        const float4 t = *reinterpret_cast<const float4*>(p.h0 + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j);
-        acc[x] = f32x4{t.x, t.y, t.z, t.w};
-      }
-    }
+    job_init<D>(job, acc, w, g, jj);
     if (nck > 0) chain_barrier();   // B0
     for (int k = 0; k < nck; ++k) {
       const char* Fb = smem + (k & 1) * Cf::bufF;
@@ -561,12 +606,14 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       }
       const uint16_t* Up = reinterpret_cast<const uint16_t*>(Fb + Cf::fUp);
       float u[4];
+      // transfer rows: U' = 0
+      const float um = job.xfer ? 0.f : 1.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]) - au[i];
+      for (int i = 0; i < 4; ++i) u[i] = um * bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]) - au[i];
       if constexpr (Cf::SPLIT) {
         const uint16_t* Upl = reinterpret_cast<const uint16_t*>(Fb + Cf::fUpl);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] += bf16_bits_to_f32(Upl[(16 * w + 4 * g + i) * 16 + jj]);
+        for (int i = 0; i < 4; ++i) u[i] += um * bf16_bits_to_f32(Upl[(16 * w + 4 * g + i) * 16 + jj]);
         st4_s<C, 1>(smem + Cf::fUl, jj, 16 * w + 4 * g, lo_part(u[0]), lo_part(u[1]), lo_part(u[2]), lo_part(u[3]));
       }
       if constexpr (Cf::RAW) {
@@ -591,34 +638,31 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
         acc[x] = a;
       }
     }
-    if (p.ht) {
-#pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        const int j = 16 * (w * NJW + x) + 4 * g;
-        *reinterpret_cast<float4*>(p.ht + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j) =
-            make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-      }
-    }
+    job_fin<D>(job, acc, w, g, jj);
   } else if (wv == kConvWave) {
     if (nck == 0) return;
     LoRegs<D, TIO, GATE> R;
     if constexpr (Cf::LO) {
-      R.load(p, se, h, chunk(0), v0, false);
+      R.load(p, se, h, chunk(0), v0l, false);
       R.store_dec(reinterpret_cast<float*>(slot(0) + Cf::sDec));
-      R.load(p, se, h, chunk(1), v0, false);
+      R.load(p, se, h, chunk(1), v0l, false);
     }
     chain_barrier();   // B0
     for (int k = 0; k < nck; ++k) {
       const int64_t ch = int64_t(h) * p.NC + chunk(k);
       chain_barrier();   // B1
-      store_slice<D>(Ss, p.S + (ch * D + v0) * D);
-      if constexpr (Cf::SPLIT) store_slice<D>(smem + Cf::fSl, p.Slo + (ch * D + v0) * D);
+      if (job.store) {
+        store_slice<D>(Ss, p.S + (ch * D + v0) * D);
+        if constexpr (Cf::SPLIT) store_slice<D>(smem + Cf::fSl, p.Slo + (ch * D + v0) * D);
+      }
       chain_barrier();   // B2
-      store_slice<C, 1>(Uo, p.U + (ch * D + v0) * C);
-      if constexpr (Cf::SPLIT) store_slice<C, 1>(smem + Cf::fUl, p.Ulo + (ch * D + v0) * C);
+      if (job.store) {
+        store_slice<C, 1>(Uo, p.U + (ch * D + v0) * C);
+        if constexpr (Cf::SPLIT) store_slice<C, 1>(smem + Cf::fUl, p.Ulo + (ch * D + v0) * C);
+      }
       if constexpr (Cf::LO) {
         R.store_dec(reinterpret_cast<float*>(slot(k + 1) + Cf::sDec));
-        R.load(p, se, h, chunk(k + 2), v0, false);
+        R.load(p, se, h, chunk(k + 2), v0l, false);
       }
     }
     wait_vm<0>();
@@ -628,12 +672,13 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     const bool hs = small_loads<D, TIO, GATE>(mw, false);
     MoverLane<D> ml;
     ml.init(mw, l);
-    move_small<D, TIO, GATE>(p, se, h, chunk(0), v0, slot(0), mw, false);
-    move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), v0, smem, mw);
+    const int sll = v0l / 16;   // the state slice whose rows this workgroup's loads take
+    move_small<D, TIO, GATE>(p, se, h, chunk(0), v0l, slot(0), mw, false);
+    move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), v0l, smem, mw);
     move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
-    move_small<D, TIO, GATE>(p, se, h, chunk(1), v0, slot(1), mw, false);
-    move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), v0, smem + Cf::bufF, mw);
-    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(c), sl, mw, smem + Cf::fPF);
+    move_small<D, TIO, GATE>(p, se, h, chunk(1), v0l, slot(1), mw, false);
+    move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), v0l, smem + Cf::bufF, mw);
+    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(c), sll, mw, smem + Cf::fPF);
     wait_mover<Cf::fwdA + Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
     chain_barrier();   // B0
     // raw mode reads set B (k) in the first window too: both sets of chunk 0 land
@@ -643,11 +688,11 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
-      move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0, slot(k + 2), mw, false);
+      move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, false);
       wait_mover<Cf::fwdA + 1 + Cf::fwdB>(hs);
       chain_barrier();   // B2
-      move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0, smem + (k & 1) * Cf::bufF, mw);
-      prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(k + Cf::PFD), sl, mw, smem + Cf::fPF);
+      move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0l, smem + (k & 1) * Cf::bufF, mw);
+      prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(k + Cf::PFD), sll, mw, smem + Cf::fPF);
       if constexpr (Cf::RAW) wait_mover<Cf::fwdA + 2>(hs);   // set B of chunk k + 1 before the next B1
       else wait_mover<Cf::fwdB + Cf::fwdA + 2>(hs);
     }
@@ -656,7 +701,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
 }
 
 template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, int h, int sl) {
+__device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, int h, int sl, const ChainJob& job) {
   using Dm = Dims<D>;
   using Cf = ChainCfg<D, TIO, GATE>;
   constexpr int NJW = Dm::NJW;
@@ -664,7 +709,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
   const int l = lane_id();
   const int g = l >> 4, jj = l & 15;
   const SeqEntry se = p.stab[si];
-  const int v0 = 16 * sl;
+  const int v0 = 16 * sl, v0l = job.v0l;
   const int nck = se.nchunks;
   char* dSl = smem + Cf::bdS;
   // dU^T of step k (buffer k & 1 when there are two)
@@ -676,16 +721,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
   if (wv < 4) {
     const int w = wv;
     f32x4 acc[NJW];
-#pragma unroll
-    for (int x = 0; x < NJW; ++x) acc[x] = zero4();
-    if (p.dht) {
-#pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        const int j = 16 * (w * NJW + x) + 4 * g;
-        const float4 t = *reinterpret_cast<const float4*>(p.dht + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j);
-        acc[x] = f32x4{t.x, t.y, t.z, t.w};
-      }
-    }
+    job_init<D>(job, acc, w, g, jj);
     if (nck > 0) chain_barrier();   // B0
     // raw mode: the compute waves form fq dO (high, low) of each chunk's dO slice
     // one step ahead, a quarter each (chunk 0 here, chunk k + 1 in the first
@@ -704,7 +740,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
         st4_s<D>(dSl, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-        if constexpr (Cf::SPLIT)   // no LDS left for a low tile: stored directly
+        if (Cf::SPLIT && job.store)   // no LDS left for a low tile: stored directly
           st_bf16x4(p.dSlo + (int64_t(h) * p.NC + chunk(k)) * D * D + (v0 + jj) * D + j, lo_part(acc[x][0]),
                     lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
       }
@@ -715,11 +751,13 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         convert_raw_rows<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
       // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice
       f32x4 ad = zero4(), ak = zero4();
+      if (!job.xfer) {   // transfer rows: dO = 0
 #pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 32) {
-        const bf16x8 pa = frag_kc_s<C>(Bb + Cf::bP, 16 * w, k0);
-        ad = mma(pa, frag_kc_s<16>(X1, 0, k0), ad);
-        if constexpr (Cf::LO) ad = mma(pa, frag_kc_s<16>(X2, 0, k0), ad);
+        for (int k0 = 0; k0 < C; k0 += 32) {
+          const bf16x8 pa = frag_kc_s<C>(Bb + Cf::bP, 16 * w, k0);
+          ad = mma(pa, frag_kc_s<16>(X1, 0, k0), ad);
+          if constexpr (Cf::LO) ad = mma(pa, frag_kc_s<16>(X2, 0, k0), ad);
+        }
       }
 #pragma unroll
       for (int k0 = 0; k0 < D; k0 += 32) ak = mma(frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0), frag_rk_s<D>(dSl, 0, k0), ak);
@@ -739,17 +777,19 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       for (int x = 0; x < NJW; ++x) {
         const int jb = w * NJW + x;
         f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
+        if (!job.xfer) {   // transfer rows: dO = 0
 #pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) {
-          const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, k0);
-          if constexpr (Cf::RAW) {
-            a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
-            a = mma(qa, frag_kc_s<16>(X3, 0, k0), a);
-          } else {
-            const bf16x8 bh = frag_kc_s<16>(X1, 0, k0);
-            a = mma(qa, bh, a);
-            a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, k0), bh, a);
-            if constexpr (Cf::LO) a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
+          for (int k0 = 0; k0 < C; k0 += 32) {
+            const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, k0);
+            if constexpr (Cf::RAW) {
+              a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
+              a = mma(qa, frag_kc_s<16>(X3, 0, k0), a);
+            } else {
+              const bf16x8 bh = frag_kc_s<16>(X1, 0, k0);
+              a = mma(qa, bh, a);
+              a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, k0), bh, a);
+              if constexpr (Cf::LO) a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
+            }
           }
         }
         an[x] = a;
@@ -812,42 +852,38 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         }
       }
     }
-    if (p.dh0) {
-#pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        const int j = 16 * (w * NJW + x) + 4 * g;
-        *reinterpret_cast<float4*>(p.dh0 + ((int64_t(se.seq) * p.H + h) * D + v0 + jj) * D + j) =
-            make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-      }
-    }
+    job_fin<D>(job, acc, w, g, jj);
   } else if (wv == kConvWave) {
     if (nck == 0) return;
     LoRegs<D, TIO, GATE> R;
     if constexpr (Cf::LO) {
-      R.load(p, se, h, chunk(0), v0, true);
+      R.load(p, se, h, chunk(0), v0l, true);
       R.store_dO(smem + Cf::bX1, smem + Cf::bX2);
       R.store_dec(reinterpret_cast<float*>(slot(0) + Cf::sDec));
-      R.load(p, se, h, chunk(1), v0, true);
+      R.load(p, se, h, chunk(1), v0l, true);
     }
     chain_barrier();   // B0
     for (int k = 0; k < nck; ++k) {
       const int64_t ch = int64_t(h) * p.NC + chunk(k);
       const int nb = (k + 1) & 1;
       chain_barrier();   // B1
-      store_slice<D>(dSl, p.dS + (ch * D + v0) * D);
-      // two dU buffers: dU of the previous step (its buffer is not written again
-      // before the next B2); one buffer: this step's, after B2
-      if (Cf::NDU == 2 && k > 0)
-        store_slice<C, 1>(dUbuf(k - 1), p.dU + ((int64_t(h) * p.NC + chunk(k - 1)) * D + v0) * C);
+      if (job.store) {
+        store_slice<D>(dSl, p.dS + (ch * D + v0) * D);
+        // two dU buffers: dU of the previous step (its buffer is not written again
+        // before the next B2); one buffer: this step's, after B2
+        if (Cf::NDU == 2 && k > 0)
+          store_slice<C, 1>(dUbuf(k - 1), p.dU + ((int64_t(h) * p.NC + chunk(k - 1)) * D + v0) * C);
+      }
       chain_barrier();   // B2
-      if (Cf::NDU == 1) store_slice<C, 1>(dUbuf(k), p.dU + (ch * D + v0) * C);
+      if (Cf::NDU == 1 && job.store) store_slice<C, 1>(dUbuf(k), p.dU + (ch * D + v0) * C);
       if constexpr (Cf::LO) {
         R.store_dO(smem + Cf::bX1 + nb * Cf::XB, smem + Cf::bX2 + nb * Cf::XB);
         R.store_dec(reinterpret_cast<float*>(slot(k + 1) + Cf::sDec));
-        R.load(p, se, h, chunk(k + 2), v0, true);
+        R.load(p, se, h, chunk(k + 2), v0l, true);
       }
     }
-    if (Cf::NDU == 2) store_slice<C, 1>(dUbuf(nck - 1), p.dU + ((int64_t(h) * p.NC + chunk(nck - 1)) * D + v0) * C);
+    if (Cf::NDU == 2 && job.store)
+      store_slice<C, 1>(dUbuf(nck - 1), p.dU + ((int64_t(h) * p.NC + chunk(nck - 1)) * D + v0) * C);
     wait_vm<0>();
   } else {
     if (nck == 0) return;
@@ -855,12 +891,13 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     const bool hs = small_loads<D, TIO, GATE>(mw, true);
     MoverLane<D> ml;
     ml.init(mw, l);
-    move_small<D, TIO, GATE>(p, se, h, chunk(0), v0, slot(0), mw, true);
+    const int sll = v0l / 16;   // the state slice whose rows this workgroup's loads take
+    move_small<D, TIO, GATE>(p, se, h, chunk(0), v0l, slot(0), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
     move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
-    move_small<D, TIO, GATE>(p, se, h, chunk(1), v0, slot(1), mw, true);
+    move_small<D, TIO, GATE>(p, se, h, chunk(1), v0l, slot(1), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), smem + Cf::bufB, mw);
-    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(c), sl, mw, smem + Cf::bPF);
+    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(c), sll, mw, smem + Cf::bPF);
     wait_mover<Cf::bwdA + Cf::bwdB + Cf::bwdA + Cf::PFD - 2>(hs);
     chain_barrier();   // B0
     // both sets of chunk 0 and the small data of chunk 1 land before B1 (set B is
@@ -869,11 +906,11 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
-      move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0, slot(k + 2), mw, true);
+      move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, true);
       wait_mover<Cf::bwdA + 1 + Cf::bwdB>(hs);
       chain_barrier();   // B2
       move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
-      prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(k + Cf::PFD), sl, mw, smem + Cf::bPF);
+      prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(k + Cf::PFD), sll, mw, smem + Cf::bPF);
       // set B of chunk k + 1 and the small data of chunk k + 2 land before the
       // next B1: only set A of chunk k + 2 and the prefetch stay in flight
       wait_vm<Cf::bwdA + 1>();
@@ -882,11 +919,13 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
   }
 }
 
-// blockIdx -> (one (sequence, head), V slice): the slices of one (sequence, head)
+// blockIdx -> (one (segment, head), slice): the slices of one (segment, head)
 // share its chunk tiles, so they are placed on the same XCD (workgroups are
-// dealt round-robin over the 8 XCDs).
+// dealt round-robin over the 8 XCDs).  The final pass has D / 16 slices per
+// (segment, head), the state rows; the local pass twice that many, the state
+// rows and then the transfer-product rows.
 template <int D, typename TIO, int GATE>
-__global__ __launch_bounds__(kChainThreads) void k_chain(const Params p, int mode, int nb_role) {
+__global__ __launch_bounds__(kChainThreads) void k_chain(const Params p, int mode, int nb_role, int pass) {
   __shared__ __attribute__((aligned(1024))) char smem[ChainCfg<D, TIO, GATE>::bytes];
   int b = blockIdx.x;
   int role;
@@ -897,17 +936,18 @@ __global__ __launch_bounds__(kChainThreads) void k_chain(const Params p, int mod
     role = mode == kChainFwd ? 0 : 1;
   }
   constexpr int ns = D / 16;
+  const int nsl = pass == kPassLocal ? 2 * ns : ns;
   const int xcd = b % 8, y = b / 8;
-  const int sl = y % ns, t = y / ns;
-  // (sequence, head) of slot t on this XCD.  With grouped heads the G value heads
+  const int sl = y % nsl, t = y / nsl;
+  // (segment, head) of slot t on this XCD.  With grouped heads the G value heads
   // of a key head read the same q, k rows, so they take consecutive slots of one
-  // XCD (its L2 then serves the rows they share); the (sequence, key head) pairs
+  // XCD (its L2 then serves the rows they share); the (segment, key head) pairs
   // past the last whole set of eight keep the plain order.
   int gidx;
   if (p.G == 1) {
     gidx = t * 8 + xcd;
   } else {
-    const int npair = p.N * p.Hk, p8 = npair / 8 * 8;
+    const int npair = p.NS * p.Hk, p8 = npair / 8 * 8;
     const int L = t * 8 + xcd;
     int pair, gi;
     if (L < p8 * p.G) {
@@ -920,37 +960,135 @@ __global__ __launch_bounds__(kChainThreads) void k_chain(const Params p, int mod
     }
     gidx = (pair / p.Hk) * p.H + (pair % p.Hk) * p.G + gi;
   }
-  if (gidx >= p.N * p.H) return;
+  if (gidx >= p.NS * p.H) return;
   const int si = gidx / p.H, h = gidx % p.H;
+  const SeqEntry se = p.stab[si];
+  const bool first = role == 0 ? se.seg == 0 : se.seg == se.nseg - 1;   // the role's first segment
+  const bool last = role == 0 ? se.seg == se.nseg - 1 : se.seg == 0;    // the role's last segment
+  const int64_t sh = int64_t(se.seq) * p.H + h;                           // (sequence, head)
+  const int64_t gh = (int64_t(role) * p.NS + se.slot) * p.H + h;           // (role, segment slot, head)
+  const float* start = role == 0 ? p.h0 : p.dht;
+  float* end = role == 0 ? p.ht : p.dh0;
+  ChainJob job;
+  job.xfer = sl >= ns;
+  job.i0 = 16 * (sl - ns);
+  job.v0l = 16 * (sl % ns);
+  if (pass == kPassLocal) {
+    // only segments that a later one (in the role's order) starts from, and the
+    // transfer product only where the segment does not start from h0 / dht
+    if (last || (job.xfer && first)) return;
+    job.init = first && !job.xfer && start ? start + (sh * D + 16 * sl) * D : nullptr;
+    job.fin = p.xf + (gh * 2 * D + 16 * sl) * D;
+    job.store = false;
+  } else {
+    job.init = first ? (start ? start + (sh * D + 16 * sl) * D : nullptr) : p.sb + (gh * D + 16 * sl) * D;
+    job.fin = last && end ? end + (sh * D + 16 * sl) * D : nullptr;
+    job.store = true;
+  }
   if (role == 0)
-    chain_fwd<D, TIO, GATE>(p, smem, si, h, sl);
+    chain_fwd<D, TIO, GATE>(p, smem, si, h, sl, job);
   else
-    chain_bwd<D, TIO, GATE>(p, smem, si, h, sl);
+    chain_bwd<D, TIO, GATE>(p, smem, si, h, sl, job);
+}
+
+// The boundary states of split sequences, in order: one workgroup per (first
+// segment of a split sequence, head, 16 state rows, role).  Forward: segment 1
+// starts from the local pass's end state of segment 0 (run from h0), and
+// segment j + 1 from S_j T_j + E_j (T_j the transfer product of segment j, E_j its
+// end state from zero); reverse likewise from the last segment down.  fp32
+// throughout; the 16 x D rows in LDS, T_j staged in LDS per boundary.
+template <int D>
+__global__ __launch_bounds__(256) void k_chain_fix(const Params p, int mode) {
+  __shared__ float cur[16][D];
+  __shared__ float Tt[D][D];
+  constexpr int ns = D / 16, CPT = D / 16;   // columns per thread
+  int b = blockIdx.x;
+  const int per_role = p.NS * p.H * ns;
+  int role = mode == kChainBwd ? 1 : 0;
+  if (mode == kChainBoth && b >= per_role) {
+    role = 1;
+    b -= per_role;
+  }
+  const int sl = b % ns, gidx = b / ns;
+  const int si = gidx / p.H, h = gidx % p.H;
+  const SeqEntry se = p.stab[si];
+  if (se.seg != 0 || se.nseg < 2) return;
+  const int tid = threadIdx.x, r = tid >> 4, c0 = (tid & 15) * CPT;
+  auto xf = [&](int slot) { return p.xf + ((int64_t(role) * p.NS + slot) * p.H + h) * 2 * D * D; };
+  auto sbuf = [&](int slot) { return p.sb + (((int64_t(role) * p.NS + slot) * p.H + h) * D + 16 * sl) * D; };
+  const int P = se.nseg, s0 = se.slot;
+  // the role's first segment ran from h0 / dht: its end state is already true
+  const int j0 = role == 0 ? 0 : P - 1;
+  const int step = role == 0 ? 1 : -1;
+  float v[CPT];
+  const float* e0 = xf(s0 + j0) + (16 * sl + r) * D + c0;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) v[i] = e0[i];
+  for (int j = j0 + step; j != j0 + step * (P - 1); j += step) {
+    // v: the state the segment s0 + j starts from
+    float* dst = sbuf(s0 + j) + r * D + c0;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      dst[i] = v[i];
+      cur[r][c0 + i] = v[i];
+    }
+    const float* T = xf(s0 + j) + D * D;   // rows D .. 2D - 1: the transfer product
+    for (int i = tid; i < D * D; i += 256) Tt[i / D][i % D] = T[i];
+    __syncthreads();
+    const float* E = xf(s0 + j) + (16 * sl + r) * D + c0;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) v[i] = E[i];
+    for (int k = 0; k < D; ++k) {
+      const float a = cur[r][k];
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) v[i] = fmaf(a, Tt[k][c0 + i], v[i]);
+    }
+    __syncthreads();
+  }
+  // the state of the role's last segment
+  float* dst = sbuf(s0 + j0 + step * (P - 1)) + r * D + c0;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) dst[i] = v[i];
 }
 
 namespace {
 template <int D, typename TIO, int GATE>
-void run_chain(const Params& p, int mode, hipStream_t s) {
+void run_chain(const Params& p, int mode, int pass, hipStream_t s) {
   constexpr int ns = D / 16;
-  const int groups = p.N * p.H;
-  const int nb = ((groups + 7) / 8) * 8 * ns;
+  const int nsl = pass == kPassLocal ? 2 * ns : ns;
+  const int groups = p.NS * p.H;
+  const int nb = ((groups + 7) / 8) * 8 * nsl;
   const int nroles = mode == kChainBoth ? 2 : 1;
-  k_chain<D, TIO, GATE><<<dim3(nb * nroles), kChainThreads, 0, s>>>(p, mode, nb);
+  k_chain<D, TIO, GATE><<<dim3(nb * nroles), kChainThreads, 0, s>>>(p, mode, nb, pass);
 }
 }  // namespace
 
-int launch_chain(const Params& p, int mode, void* stream) {
+int launch_chain(const Params& p, int mode, int pass, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  if (pass == kPassLocal && (!p.xf || !p.sb)) return static_cast<int>(hipErrorInvalidValue);
   const bool bf = p.dtype == GDR_BF16;
-  if (p.K == 128 && bf && p.gate == 0) run_chain<128, bf16, 0>(p, mode, s);
-  else if (p.K == 128 && bf && p.gate == 1) run_chain<128, bf16, 1>(p, mode, s);
-  else if (p.K == 128 && !bf && p.gate == 0) run_chain<128, float, 0>(p, mode, s);
-  else if (p.K == 128 && !bf && p.gate == 1) run_chain<128, float, 1>(p, mode, s);
-  else if (p.K == 64 && bf && p.gate == 0) run_chain<64, bf16, 0>(p, mode, s);
-  else if (p.K == 64 && bf && p.gate == 1) run_chain<64, bf16, 1>(p, mode, s);
-  else if (p.K == 64 && !bf && p.gate == 0) run_chain<64, float, 0>(p, mode, s);
-  else if (p.K == 64 && !bf && p.gate == 1) run_chain<64, float, 1>(p, mode, s);
+  if (p.K == 128 && bf && p.gate == 0) run_chain<128, bf16, 0>(p, mode, pass, s);
+  else if (p.K == 128 && bf && p.gate == 1) run_chain<128, bf16, 1>(p, mode, pass, s);
+  else if (p.K == 128 && !bf && p.gate == 0) run_chain<128, float, 0>(p, mode, pass, s);
+  else if (p.K == 128 && !bf && p.gate == 1) run_chain<128, float, 1>(p, mode, pass, s);
+  else if (p.K == 64 && bf && p.gate == 0) run_chain<64, bf16, 0>(p, mode, pass, s);
+  else if (p.K == 64 && bf && p.gate == 1) run_chain<64, bf16, 1>(p, mode, pass, s);
+  else if (p.K == 64 && !bf && p.gate == 0) run_chain<64, float, 0>(p, mode, pass, s);
+  else if (p.K == 64 && !bf && p.gate == 1) run_chain<64, float, 1>(p, mode, pass, s);
+  else return static_cast<int>(hipErrorInvalidValue);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_chain_fix(const Params& p, int mode, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (!p.xf || !p.sb) return static_cast<int>(hipErrorInvalidValue);
+  const int nroles = mode == kChainBoth ? 2 : 1;
+  const int per_role = p.NS * p.H * (p.K / 16);
+  if (per_role == 0) return 0;
+  if (p.K == 128) k_chain_fix<128><<<dim3(per_role * nroles), 256, 0, s>>>(p, mode);
+  else if (p.K == 64) k_chain_fix<64><<<dim3(per_role * nroles), 256, 0, s>>>(p, mode);
   else return static_cast<int>(hipErrorInvalidValue);
   return static_cast<int>(hipGetLastError());
 }

@@ -21,33 +21,48 @@ struct ChunkEntry {
   int32_t idx;       // chunk index inside its sequence
 };
 
-// One row per sequence, ordered longest first so the serial kernels start the
-// longest chains first.
+// One row per segment of a sequence: the recursions run over segments, each a
+// run of whole chunks of one sequence (a sequence that is not split is one
+// segment).  The recursion kernel's table is ordered longest first so that the
+// longest chains start first.
 struct SeqEntry {
   int32_t seq;       // sequence index (addresses h0/dht/dh0/ht)
   int32_t len;       // tokens
   int32_t c0;        // global index of its first chunk
   int32_t nchunks;   // ceil(len / 64)
   int32_t t_start;   // first token (packed token axis)
-  int32_t pad[3];
+  int32_t seg;       // segment index inside the sequence, 0 .. nseg - 1
+  int32_t nseg;      // segments of the sequence
+  int32_t slot;      // boundary-state slot: the sequence's segments take nseg consecutive slots
 };
 
-// Sequence entries handed to k_tables by value (one launch per batch).  With
-// dense_T >= 0 the batch is `n` dense sequences of dense_T tokens numbered from
-// `first`, and `seqs` is not read.
+// Table entries handed to k_tables by value, kTableBatch per launch.
+//   kind 0 (dense): `n` dense sequences of dense_T tokens numbered from `first`,
+//                   each split into nseg equal runs of chunks; writes chunk and
+//                   segment rows; `e` is not read
+//   kind 1:         `n` whole sequences in e[]: writes their chunk rows
+//   kind 2:         `n` segments in e[]: writes segment-table rows first .. first + n - 1
 constexpr int kTableBatch = 56;
 struct TableBatch {
-  int32_t n;         // sequences in this launch
-  int32_t first;     // sequence-table row of the first of them
-  int32_t dense_T;   // dense tokens per sequence, or -1
-  int32_t pad;
-  SeqEntry seqs[kTableBatch];
+  int32_t n;
+  int32_t first;
+  int32_t kind;
+  int32_t dense_T;
+  int32_t nseg;
+  int32_t pad[3];
+  SeqEntry e[kTableBatch];
 };
 static_assert(sizeof(TableBatch) <= 2048, "kernel argument size");
+
+// Segments per sequence chosen by the host for a shape (the same choice sizes
+// the workspace and builds the tables).
+constexpr int kMaxSegments = 16;
 
 // Byte offsets of every workspace region (all 256-byte aligned).
 struct WsLayout {
   int64_t NC = 0;    // total chunks
+  int64_t NS = 0;    // segments (rows of the segment table)
+  int32_t split = 0; // 1 when some sequence is split into several segments
   size_t ctab = 0, stab = 0;
   size_t gam = 0;    // fp32 [H][NC][64] or [H][NC][64][K]: in-chunk cumsum of the log decay
   size_t rho = 0;    // fp32 [H][NC][3][64]: 1/|q|, 1/|k|, beta per row (beta 0 past the end)
@@ -78,6 +93,11 @@ struct WsLayout {
   size_t Ulo = 0;    // bf16 [H][NC][V][64]
   size_t Slo = 0;    // bf16 [H][NC][V][K]
   size_t dSlo = 0;   // bf16 [H][NC][V][K]
+  // split sequences only: the first recursion pass's segment-end states and
+  // transfer products, and the composed segment boundary states
+  size_t xf = 0;     // fp32 [2 roles][NS][H][2 D][D]: rows 0..D-1 end state from zero (or from
+                     //   h0 / dht for the first segment of a role), rows D..2D-1 transfer product
+  size_t sb = 0;     // fp32 [2 roles][NS][H][D][D]: the state a segment's recursion starts from
   // grouped heads only (Hk < H): dq, dk per value head before the group sum
   size_t dqv = 0;    // dtype [tokens][H][K]
   size_t dkv = 0;    // dtype [tokens][H][K]
@@ -86,6 +106,7 @@ struct WsLayout {
 
 struct Params {
   int32_t H, K, V, N, NC, T;     // T = total tokens
+  int32_t NS;                     // rows of the segment table
   int32_t Hk, G;                  // q, k heads and value heads per key head (H = Hk G)
   int32_t gate, dtype;            // gate: 0 scalar, 1 per-channel (either gate function)
   float scale;
@@ -109,16 +130,27 @@ struct Params {
   uint16_t* Mk;                                  // per-channel gate only
   float *pdA, *pddt;
   uint16_t *Uplo, *Ulo, *Slo, *dSlo;             // per-channel gate only: low parts
+  float *xf, *sb;                                // split sequences only
 };
 
 // Chain-kernel roles.
 enum ChainMode { kChainFwd = 1, kChainBwd = 2, kChainBoth = 3 };
+// Passes of the recursions over segments.  kPassFinal runs every segment from
+// its true starting state (h0 / dht, or the composed boundary state) and stores
+// the per-chunk outputs; a problem with no split sequence runs only this pass.
+// kPassLocal runs every segment that some later (forward) or earlier (reverse)
+// segment depends on, from zero (or h0 / dht), with the transfer product as D
+// more state rows, and stores only the segment-end rows.
+enum ChainPass { kPassFinal = 0, kPassLocal = 1 };
 
 // Chunk and sequence tables from one batch of sequence entries (gdr_tables.hip).
 int launch_tables(const ChunkEntry* ctab, const SeqEntry* stab, const TableBatch& tb, void* stream);
 // Kernel launchers (gdr_kernels.hip).  Return a hipError_t as int.
 int launch_prep(const Params& p, void* stream);
-int launch_chain(const Params& p, int mode, void* stream);
+int launch_chain(const Params& p, int mode, int pass, void* stream);
+// The serial composition of the segment boundary states from the local pass's
+// segment-end states and transfer products (split sequences only).
+int launch_chain_fix(const Params& p, int mode, void* stream);
 int launch_grads(const Params& p, void* stream);
 int launch_zero_params(const Params& p, void* stream);
 // Forward output from the forward recompute's workspace (gdr_out.hip).

@@ -167,8 +167,9 @@ def workload(name: str) -> Spec:
     if name == "gdn_varlen12_bf16_t32768_h32_d128":
         return Spec(name, GATE_SCALAR, "bf16", H=32, K=128, V=128, varlen_n=12, varlen_max=8192,
                     varlen_total=32768, h0_std=0.1, dht_std=0.1, seed=1003)
+    # H = 2 and 4: one GPU's share of the H = 16 and H = 32 problems under 8-way head sharding
     for gate_name, gate in (("gdn", GATE_SCALAR), ("kda", GATE_CHANNEL), ("kdas", GATE_CHANNEL_SIGMOID)):
-        for H in (16, 32):
+        for H in (2, 4, 16, 32):
             if name == f"{gate_name}_bf16_t32768_h{H}_d128":
                 return Spec(name, gate, "bf16", H=H, K=128, V=128, B=1, T=32768,
                             h0_std=0.1, dht_std=0.1, seed=1004)
@@ -187,6 +188,9 @@ WORKLOADS = (
     "kdas_bf16_t8192_h16_d128",
     "kdas_bf16_t32768_h16_d128",
     "gdn_gqa4_bf16_t32768_h32_d128",
+    "gdn_bf16_t32768_h2_d128",
+    "gdn_bf16_t32768_h4_d128",
+    "kda_bf16_t32768_h2_d128",
 )
 
 HEADLINE = "gdn_bf16_t32768_h16_d128"

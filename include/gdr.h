@@ -76,8 +76,19 @@ typedef struct {
   int32_t Hk;                       /* heads of q and k (grouped heads): 0 means H; else H % Hk == 0 and
                                        value head h reads key head h / (H / Hk), and dq, dk sum over the
                                        H / Hk value heads of each key head (FlashQLA GDN overview,
-                                       section 4: hk and hv head counts, GQA tests).  Hk < H needs workspace for the per-value-head
-                                       dq, dk before that sum. */
+                                       section 4: hk and hv head counts, GQA tests).  Hk < H needs
+                                       workspace for the per-value-head dq, dk before that sum. */
+  int32_t seq_split;                /* segments per sequence for the two chunk recursions: 0 = chosen
+                                       by the library (a split pays only when few (sequence, head)
+                                       pairs leave compute units idle), 1 = never split, n >= 2 = split
+                                       every sequence of two or more chunks into min(n, 16, its chunks)
+                                       runs of whole chunks.  The split is exact (the chunk recursions
+                                       are affine in the carried state; the FlashQLA overview's section
+                                       3 splits them across devices with a warm-up approximation
+                                       instead): each segment runs from a zero state with its transfer
+                                       product, the true boundary states are composed in order, and
+                                       every segment then runs again from its true state.  Results
+                                       agree with the unsplit recursion up to rounding. */
 } gdr_shape;
 
 /* Below, CHANNEL stands for either per-channel gate (GDR_GATE_CHANNEL or

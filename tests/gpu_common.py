@@ -61,10 +61,12 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def gpu_run(inp: Dict, mode: str = "fused", exports: bool = False) -> Dict[str, np.ndarray]:
-    """Runs the backward on cuda:0 through the C ABI; float64 host copies."""
+def gpu_run(inp: Dict, mode: str = "fused", exports: bool = False, seq_split: int = 0) -> Dict[str, np.ndarray]:
+    """Runs the backward on cuda:0 through the C ABI; float64 host copies.
+    seq_split: segments per sequence for the recursions (0: the library's choice,
+    1: never split)."""
     dev = B.to_device(inp)
-    prob = B.Problem.from_inputs(inp)
+    prob = B.Problem.from_inputs(inp, seq_split=seq_split)
     ws = B.alloc_workspace(prob)
     out = B.alloc_outputs(inp, dev)
     N, H, K, V = inp["N"], inp["H"], inp["K"], inp["V"]

@@ -238,3 +238,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     with pytest.raises(ImportError):
         B.load_library()
     assert torch is not None
+
+
+def test_sequence_split_workspace_and_validation():
+    """A split adds the boundary-state buffers (2 roles x segments x H x (2D + D) x D
+    fp32); the library's own choice splits a long sequence with few heads and
+    leaves the full-width shapes alone; a negative seq_split is rejected."""
+    long_few = dict(B=1, T=32768, H=2, D=128, N=1)
+    plain = B.gdr_workspace_bytes(_prob(seq_split=1, **long_few))
+    auto = B.gdr_workspace_bytes(_prob(seq_split=0, **long_few))
+    forced = B.gdr_workspace_bytes(_prob(seq_split=4, **long_few))
+    seg_bytes = 2 * 2 * 3 * 128 * 128 * 4      # per segment: 2 roles, H = 2, (2D + D) x D fp32
+    assert forced - plain >= 4 * seg_bytes
+    assert auto > plain                          # split by the library's choice
+    wide = dict(B=1, T=32768, H=16, D=128, N=1)
+    assert B.gdr_workspace_bytes(_prob(seq_split=0, **wide)) == B.gdr_workspace_bytes(_prob(seq_split=1, **wide))
+    # a one-chunk sequence is never split
+    one = dict(B=1, T=64, H=2, D=64, N=1)
+    assert B.gdr_workspace_bytes(_prob(seq_split=8, **one)) == B.gdr_workspace_bytes(_prob(seq_split=1, **one))
+    with pytest.raises(B.GdrError) as e:
+        B.gdr_workspace_bytes(_prob(seq_split=-1))
+    assert e.value.status == B.GDR_EINVAL
