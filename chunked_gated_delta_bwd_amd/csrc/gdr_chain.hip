@@ -1032,8 +1032,17 @@ __global__ __launch_bounds__(256) void k_chain_fix(const Params p, int mode) {
       dst[i] = v[i];
       cur[r][c0 + i] = v[i];
     }
-    const float* T = xf(s0 + j) + D * D;   // rows D .. 2D - 1: the transfer product
-    for (int i = tid; i < D * D; i += 256) Tt[i / D][i % D] = T[i];
+    // rows D .. 2D - 1 of the segment's block: the transfer product, staged with
+    // all of a thread's 16-byte loads in flight at once
+    const float4* T4 = reinterpret_cast<const float4*>(xf(s0 + j) + D * D);
+    float4 tv[D * D / 4 / 256];
+#pragma unroll
+    for (int i = 0; i < D * D / 4 / 256; ++i) tv[i] = T4[tid + 256 * i];
+#pragma unroll
+    for (int i = 0; i < D * D / 4 / 256; ++i) {
+      const int e = 4 * (tid + 256 * i);
+      *reinterpret_cast<float4*>(&Tt[e / D][e % D]) = tv[i];
+    }
     __syncthreads();
     const float* E = xf(s0 + j) + (16 * sl + r) * D + c0;
 #pragma unroll
