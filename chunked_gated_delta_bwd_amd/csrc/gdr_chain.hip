@@ -51,6 +51,10 @@
 // row factors of Qbar = q (scale e^Gam / |q|) and Khat = k (e^(GamC - Gam) / |k|)
 // to the small operands instead (dO rows, U rows, dU rows); the per-channel
 // gate and fp32 inputs take the Khat / Qbar tiles the prologue kernel formed.
+// Both take the W tile the prologue formed: W S^T and W^T dU straight from it
+// (forming them from A and k instead costs every compute wave A, k and row
+// factor reads of all 64 rows each step, and the recursions are bound by their
+// LDS traffic).
 // Qbar^T dO carries the dominant part of dh0, so that product is taken in two
 // bf16 parts (Qbar high + low, or the scaled dO high + low).
 #include <hip/hip_runtime.h>
@@ -83,19 +87,19 @@ struct ChainCfg {
   static constexpr int XB = C * 16 * 2;            // a 64 x 16 bf16 slice
   static constexpr int NJ = TB / 4096;             // 1 KB loads per mover wave per 64 x D tile
   // small per-chunk data, three rotating slots: the raw dO slice (bf16 inputs),
-  // the row factors fq, fk, fw (raw mode) and the decay
-  static constexpr int NFAC = 3;
+  // the row factors fq, fk (raw mode) and the decay
+  static constexpr int NFAC = 2;
   static constexpr int sDO = 0;
   static constexpr int sFac = sDO + (LO ? 0 : XB);
   static constexpr int sDec = sFac + (RAW ? NFAC * C * 4 : 0);
   static constexpr int SLOT = sDec + DG * 4;
   // reverse role, byte offsets; the tile buffers first.  Materialised tiles:
-  // Khat, Qbar high, low, W, P.  Raw mode: q, P (set A), k, A (set B), where
-  // W^T dU is formed as k^T (Diag(fw) A^T dU) from the raw k rows already there
-  static constexpr int bK = 0, bQh = TB, bQl = 2 * TB, bW = 3 * TB;
+  // Khat, Qbar high, low, W, P.  Raw mode: k, q, P, W.  Set A (Khat or q, and P)
+  // is read in the first window, set B (Qbar and W, or k and W) in both
+  static constexpr int bK = 0, bQh = TB, bQl = 2 * TB;
+  static constexpr int bW = MAT ? 3 * TB : 2 * TB + PB;
   static constexpr int bP = MAT ? 4 * TB : 2 * TB;
-  static constexpr int bA = 2 * TB + PB;                           // raw mode
-  static constexpr int bufB = MAT ? 4 * TB + PB : 2 * TB + 2 * PB;
+  static constexpr int bufB = MAT ? 4 * TB + PB : 3 * TB + PB;
   static constexpr int bX1 = 2 * bufB;                             // LO: dO high part
   static constexpr int bX2 = bX1 + (LO ? 2 * XB : 0);              // RAW: fq dO high; LO: dO low
   static constexpr int bX3 = bX2 + ((RAW || LO) ? 2 * XB : 0);     // RAW: fq dO low
@@ -108,10 +112,8 @@ struct ChainCfg {
   static constexpr int NDU = bdU + 2 * dUB + 256 <= 160 * 1024 ? 2 : 1;
   static constexpr int bPF = bdU + NDU * dUB;                      // 256 B sink of the L2 prefetches
   static constexpr int bEnd = bPF + 256;
-  // forward role
-  // forward role: materialised tiles W, Khat; raw mode A (in W's place) and k,
-  // with W S^T formed as A (Diag(fw) k S^T)
-  static constexpr int fW = 0, fA = 0, fK = MAT ? TB : PB, fUp = fK + TB, fUpl = fUp + XB;
+  // forward role: W, Khat (raw mode: k), the U' slice (and its low part)
+  static constexpr int fW = 0, fK = TB, fUp = 2 * TB, fUpl = fUp + XB;
   static constexpr int bufF = fUpl + (SPLIT ? XB : 0);
   static constexpr int fSlot = 2 * bufF;
   static constexpr int fS = fSlot + 3 * SLOT;                      // 16 x D state slice
@@ -128,10 +130,10 @@ struct ChainCfg {
   // none wait for one fewer: wait_mover)
   static constexpr int nSb = 1;
   static constexpr int nSf = 1;
-  static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 * NJ : NJ + 2) + nSb;
+  static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 * NJ : 2 * NJ) + nSb;
   // L2 prefetch distance in chunk steps (one prefetch load per mover wave per step)
   static constexpr int PFD = 5;
-  static constexpr int fwdA = (MAT ? NJ : 2) + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
+  static constexpr int fwdA = NJ + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(2 * bwdA + bwdB + PFD - 2 < 64 && 2 * fwdA + fwdB + PFD - 2 < 64, "vmcnt range");
 };
@@ -150,15 +152,29 @@ __device__ __forceinline__ ChunkGeo geo(const Params& p, const SeqEntry& se, int
 }
 
 // ---------------------------------------------------------------------------
-// movers (waves 5-8): mover wave mw fills bytes [mw T/4, (mw+1) T/4) of a tile T
+// movers: mover wave mw fills bytes [mw T/4, (mw+1) T/4) of a tile T
 // ---------------------------------------------------------------------------
+// Every address is a per-chunk scalar base plus a lane offset.  The lane offsets
+// (the swizzle, the lane's row and piece) are computed once and hidden from the
+// compiler (keep()), which would otherwise recompute them, with a division and
+// 64-bit arithmetic, for every load of every chunk step on the SIMDs the compute
+// waves run on; only the last, partial chunk of a sequence takes clamped offsets.
+__device__ __forceinline__ void keep(int& x) { asm volatile("" : "+v"(x)); }
+
 template <int D>
 struct MoverLane {
   int rD[4], pD[4], tD[4];   // 64 x D tile, load j: row, swizzled piece byte offset, in-tile offset
+  int rowoff[4];             // q / k token rows of a whole chunk, load j: byte offset from its first row
   int tP[2];                 // P tile, load j: in-tile offset
   int up;                    // 64 x 16 slice of a 64 x D tile (lanes 0-31): row * 2D + piece * 16
-  __device__ __forceinline__ void init(int mw, int l) {
+  int drow, doff;            // dO halves (movers 0, 1): logical row; byte offset, whole chunk
+  int rs, ds;                // byte strides of q / k rows and of dO rows (scalars)
+  int hk;                    // the key head of value head h (scalar)
+  __device__ __forceinline__ void init(const Params& p, int h, int mw, int l, int dsz) {
     constexpr int RB = 2 * D, TB = C * RB, NJ = TB / 4096;
+    rs = __builtin_amdgcn_readfirstlane(p.Hk * D * 2);
+    ds = __builtin_amdgcn_readfirstlane(p.H * D * dsz);
+    hk = __builtin_amdgcn_readfirstlane(h / p.G);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int pos = mw * (TB / 4) + (j < NJ ? j : 0) * 1024 + 16 * l;
@@ -166,15 +182,26 @@ struct MoverLane {
       rD[j] = row;
       pD[j] = lp << 4;
       tD[j] = row * RB + (lp << 4);
+      rowoff[j] = row * rs + (lp << 4);
+      keep(rD[j]);
+      keep(pD[j]);
+      keep(tD[j]);
+      keep(rowoff[j]);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int pos = mw * 2048 + j * 1024 + 16 * l;
       const int row = pos >> 7, lp = ((pos & 127) >> 4) ^ swz<64, 0>(row);
       tP[j] = row * 128 + (lp << 4);
+      keep(tP[j]);
     }
     const int pos = mw * 512 + 16 * (l & 31);
     up = (pos >> 5) * RB + (((pos & 31) >> 4) << 4);
+    drow = prow<16>(32 * (mw & 1) + (l >> 1));   // logical row landing at physical row 32 mw + l/2
+    doff = drow * ds + (l & 1) * 16;
+    keep(up);
+    keep(drow);
+    keep(doff);
   }
 };
 
@@ -184,20 +211,23 @@ __device__ __forceinline__ void move_tile(const MoverLane<D>& ml, const void* sr
   constexpr int TB = C * D * 2, NJ = TB / 4096;
   const char* s = static_cast<const char*>(src);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) dma16(s + ml.tD[j], dst + mw * (TB / 4) + j * 1024);
+  for (int j = 0; j < NJ; ++j) dma16(s + uint32_t(ml.tD[j]), dst + mw * (TB / 4) + j * 1024);
 }
 
 // a 64 x D tile of raw token rows (q or k of the key head that value head h reads),
 // rows past the end clamped
 template <int D>
-__device__ __forceinline__ void move_rows(const MoverLane<D>& ml, const void* base, const Params& p, const ChunkGeo& cg,
-                                          int h, char* dst, int mw) {
+__device__ __forceinline__ void move_rows(const MoverLane<D>& ml, const void* base, const ChunkGeo& cg, char* dst,
+                                          int mw) {
   constexpr int TB = C * D * 2, NJ = TB / 4096;
-  const char* s = static_cast<const char*>(base) + int64_t(h / p.G) * D * 2;
+  const char* s = static_cast<const char*>(base) + (int64_t(cg.t0) * (ml.rs / (D * 2)) + ml.hk) * (D * 2);
+  if (cg.len == C) {
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int64_t t = cg.t0 + min(ml.rD[j], cg.len - 1);
-    dma16(s + t * (int64_t(p.Hk) * D * 2) + ml.pD[j], dst + mw * (TB / 4) + j * 1024);
+    for (int j = 0; j < NJ; ++j) dma16(s + uint32_t(ml.rowoff[j]), dst + mw * (TB / 4) + j * 1024);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      dma16(s + uint32_t(min(ml.rD[j], cg.len - 1) * ml.rs + ml.pD[j]), dst + mw * (TB / 4) + j * 1024);
   }
 }
 
@@ -205,10 +235,10 @@ template <int D>
 __device__ __forceinline__ void move_p(const MoverLane<D>& ml, const void* src, char* dst, int mw) {
   const char* s = static_cast<const char*>(src);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) dma16(s + ml.tP[j], dst + mw * 2048 + j * 1024);
+  for (int j = 0; j < 2; ++j) dma16(s + uint32_t(ml.tP[j]), dst + mw * 2048 + j * 1024);
 }
 
-// small data of chunk c into a slot: the dO slice (reverse role), fq / fk / fw, decay,
+// small data of chunk c into a slot: the dO slice (reverse role), fq / fk, decay,
 // in as few whole-wave loads as possible (a load costs about the same however few
 // bytes it carries): reverse role, movers 0 and 1 one half of the dO slice each
 // (rows 32 mw .. 32 mw + 31, two pieces a row), mover 2 the row factors and the
@@ -222,20 +252,19 @@ __device__ __forceinline__ bool small_loads(int mw, bool with_dO) {
 }
 
 template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void move_small(const Params& p, const SeqEntry& se, int h, int c, int v0, char* slot,
-                                           int mw, bool with_dO) {
+__device__ __forceinline__ void move_small(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
+                                           int v0, char* slot, int mw, bool with_dO) {
   using Cf = ChainCfg<D, TIO, GATE>;
   if constexpr (!Cf::LO) {
     const ChunkGeo cg = geo(p, se, h, c);
     const int l = lane_id();
     if (with_dO && mw < 2) {
-      const int row = prow<16>(32 * mw + (l >> 1));   // logical row landing at physical row 32 mw + l/2
-      const char* src = reinterpret_cast<const char*>(p.dO) +
-                        (tok(cg.t0 + min(row, cg.len - 1), p.H, h) * D + v0) * 2 + (l & 1) * 16;
-      dma16(src, slot + Cf::sDO + mw * 1024);
+      const char* s = reinterpret_cast<const char*>(p.dO) + ((int64_t(cg.t0) * p.H + h) * D + v0) * 2;
+      const int o = cg.len == C ? ml.doff : min(ml.drow, cg.len - 1) * ml.ds + (l & 1) * 16;
+      dma16(s + uint32_t(o), slot + Cf::sDO + mw * 1024);
     } else if (mw == (with_dO ? 2 : 0)) {
       if constexpr (Cf::RAW) {
-        // fq, fk, fw (768 bytes, lanes 0-47), then the decay (lane 48) right behind them
+        // fq, fk (512 bytes, lanes 0-31), then the decay (lane 32) right behind them
         constexpr int NL = Cf::NFAC * C * 4 / 16;
         static_assert(Cf::sDec == Cf::sFac + NL * 16, "decay follows the row factors");
         if (l < NL) dma16(reinterpret_cast<const char*>(p.fac + cg.ch * Cf::NFAC * C) + l * 16, slot + Cf::sFac);
@@ -257,14 +286,14 @@ __device__ __forceinline__ void wait_mover(bool has_small) {
 }
 
 // reverse role: set A (Khat, P; raw mode q, P), set B (Qbar high + low, W; raw
-// mode k, A)
+// mode k, W)
 template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void move_bwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            char* buf, int mw) {
   using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
   if constexpr (Cf::RAW)
-    move_rows<D>(ml, p.q, p, cg, h, buf + Cf::bQh, mw);
+    move_rows<D>(ml, p.q, cg, buf + Cf::bQh, mw);
   else
     move_tile<D>(ml, p.Kh + cg.ch * C * D, buf + Cf::bK, mw);
   move_p<D>(ml, p.P + cg.ch * C * C, buf + Cf::bP, mw);
@@ -276,25 +305,21 @@ __device__ __forceinline__ void move_bwd_b(const MoverLane<D>& ml, const Params&
   using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
   if constexpr (Cf::RAW) {
-    move_rows<D>(ml, p.k, p, cg, h, buf + Cf::bK, mw);
-    move_p<D>(ml, p.A + cg.ch * C * C, buf + Cf::bA, mw);
+    move_rows<D>(ml, p.k, cg, buf + Cf::bK, mw);
   } else {
     move_tile<D>(ml, p.Qh + cg.ch * C * D, buf + Cf::bQh, mw);
     move_tile<D>(ml, p.Ql + cg.ch * C * D, buf + Cf::bQl, mw);
-    move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::bW, mw);
   }
+  move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::bW, mw);
 }
 
-// forward role: set A (W or, raw mode, A; the U' slice), set B (Khat or k)
+// forward role: set A (W, the U' slice), set B (Khat or k)
 template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void move_fwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            int v0, char* buf, int mw) {
   using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
-  if constexpr (Cf::MAT)
-    move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::fW, mw);
-  else
-    move_p<D>(ml, p.A + cg.ch * C * C, buf + Cf::fA, mw);
+  move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::fW, mw);
   if (lane_id() < 32) dma16(reinterpret_cast<const char*>(p.Up + cg.ch * C * D + v0) + ml.up, buf + Cf::fUp + mw * 512);
   if constexpr (Cf::SPLIT) {
     if (lane_id() < 32)
@@ -308,7 +333,7 @@ __device__ __forceinline__ void move_fwd_b(const MoverLane<D>& ml, const Params&
   using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
   if constexpr (Cf::RAW)
-    move_rows<D>(ml, p.k, p, cg, h, buf + Cf::fK, mw);
+    move_rows<D>(ml, p.k, cg, buf + Cf::fK, mw);
   else
     move_tile<D>(ml, p.Kh + cg.ch * C * D, buf + Cf::fK, mw);
 }
@@ -316,69 +341,115 @@ __device__ __forceinline__ void move_fwd_b(const MoverLane<D>& ml, const Params&
 // L2 prefetch of chunk c, three steps beyond the direct-to-LDS loads: the V
 // slices of one (sequence, head) read the same tiles, so slice sl touches only
 // rows [sl R, (sl+1) R) of them (R = 64 / slices), mover wave mw a quarter of
-// those, one 4-byte load per 64-byte sector into a sink that is never read.
+// those, one 4-byte load per 64-byte sector into a sink that is never read.  The
+// lane plan (which rows a lane touches, its row and byte offset) is computed once;
+// a step adds the chunk's scalar base of the lane's kind of rows.
 template <int D, typename TIO, int GATE, bool BWD>
-__device__ __forceinline__ void prefetch_chunk(const Params& p, const SeqEntry& se, int h, int c, int sl, int mw,
-                                               char* sink) {
+struct PfLane {
   using Cf = ChainCfg<D, TIO, GATE>;
-  constexpr int ns = D / 16, R = C / ns, RW = R / 4;
-  constexpr int LB = 64;                                   // bytes per prefetch load
-  constexpr int LPR = (2 * D) / LB;                        // loads per row of a 64 x D bf16 tile
-  constexpr int DOL = int(D * sizeof(TIO)) / LB;           // loads per dO row of one head
-  constexpr int NP = 128 / LB;                             // loads per row of a 64 x 64 tile
-  constexpr int NT = BWD ? (Cf::MAT ? 4 : 2) : (Cf::MAT ? 2 : 1);   // tiles with D-wide rows
-  constexpr int NT64 = BWD ? (Cf::MAT ? 1 : 2) : (Cf::MAT ? 0 : 1);  // 64 x 64 tiles (P, A)
-  constexpr int NTAIL = (Cf::RAW ? Cf::NFAC * C * 4 : 512) / LB;   // row factors or the decay
-  constexpr int N1 = NT * RW * LPR, N2 = N1 + NT64 * RW * NP, N3 = N2 + (BWD ? RW * DOL : RW * LPR);
+  static constexpr int ns = D / 16, R = C / ns, RW = R / 4;
+  static constexpr int LB = 64;                                   // bytes per prefetch load
+  static constexpr int LPR = (2 * D) / LB;                        // loads per row of a 64 x D bf16 tile
+  static constexpr int DOL = int(D * sizeof(TIO)) / LB;           // loads per dO row of one head
+  static constexpr int NP = 128 / LB;                             // loads per row of a 64 x 64 tile
+  static constexpr int NT = BWD ? (Cf::MAT ? 4 : 3) : 2;          // tiles with D-wide rows
+  static constexpr int NT64 = BWD ? 1 : 0;                        // 64 x 64 tiles (P)
+  static constexpr int NTAIL = (Cf::RAW ? Cf::NFAC * C * 4 : 512) / LB;   // row factors or the decay
+  static constexpr int N1 = NT * RW * LPR, N2 = N1 + NT64 * RW * NP, N3 = N2 + (BWD ? RW * DOL : RW * LPR);
   static_assert(N3 + NTAIL <= 64, "one prefetch load per wave");
-  const ChunkGeo cg = geo(p, se, h, c);
-  const int l = lane_id(), r0 = sl * R + mw * RW;
-  const char* a = nullptr;
-  auto tok_row = [&](const void* base, int row, int bytes_per_elem) {
-    return static_cast<const char*>(base) +
-           (tok(cg.t0 + min(row, cg.len - 1), p.H, h) * D) * bytes_per_elem;
-  };
-  auto qk_row = [&](const void* base, int row) {   // q, k: the key head of value head h
-    return static_cast<const char*>(base) + qk_tok(p, cg.t0 + min(row, cg.len - 1), h) * D * 2;
-  };
-  auto tile_row = [&](const uint16_t* base, int row) {
-    return reinterpret_cast<const char*>(base + (cg.ch * C + row) * D);
-  };
-  if (l < N1) {
-    const int t = l / (RW * LPR), rem = l % (RW * LPR), row = r0 + rem / LPR, line = rem % LPR;
-    const char* rb;
-    if constexpr (BWD) {
-      if constexpr (Cf::RAW)
-        rb = t == 0 ? qk_row(p.k, row) : qk_row(p.q, row);
-      else
-        rb = t == 0 ? tile_row(p.Kh, row) : t == 1 ? tile_row(p.Qh, row) : t == 2 ? tile_row(p.Ql, row) : tile_row(p.W, row);
-    } else {
-      if constexpr (Cf::RAW)
-        rb = qk_row(p.k, row);
-      else
-        rb = t == 0 ? tile_row(p.W, row) : tile_row(p.Kh, row);
-    }
-    a = rb + line * LB;
-  } else if (l < N2) {
-    const int i = l - N1, t = i / (RW * NP), rem = i % (RW * NP);
-    const uint16_t* base = BWD && t == 0 ? p.P : p.A;
-    a = reinterpret_cast<const char*>(base + (cg.ch * C + r0 + rem / NP) * C) + (rem % NP) * LB;
-  } else if (l < N3) {
-    if constexpr (BWD) {
+  // kinds: 0 .. NT - 1 the D-wide tiles (reverse: Khat, Qbar high, low, W; raw
+  // mode k, q, W; forward: W, Khat or k), NT the P tile, NT + 1 the dO rows
+  // (reverse) or U' rows (forward), NT + 2 the row factors or decay; -1 idle
+  static constexpr int NK = NT + 3;
+  int kind, row, col, stride, off;
+  bool tok;   // token rows (clamped at the end of a sequence)
+
+  __device__ __forceinline__ void init(const Params& p, int sl, int mw, int l) {
+    const int r0 = sl * R + mw * RW;
+    kind = -1;
+    row = 0;
+    col = 0;
+    stride = 0;
+    tok = false;
+    if (l < N1) {
+      const int t = l / (RW * LPR), rem = l % (RW * LPR);
+      kind = t;
+      row = r0 + rem / LPR;
+      col = (rem % LPR) * LB;
+      tok = Cf::RAW && (BWD ? t < 2 : t == 1);
+      stride = tok ? p.Hk * D * 2 : D * 2;
+    } else if (l < N2) {
+      const int i = l - N1;
+      kind = NT;
+      row = r0 + i / NP;
+      col = (i % NP) * LB;
+      stride = C * 2;
+    } else if (l < N3) {
       const int i = l - N2;
-      a = tok_row(p.dO, r0 + i / DOL, int(sizeof(TIO))) + (i % DOL) * LB;
-    } else {
-      const int i = l - N2;
-      a = tile_row(p.Up, r0 + i / LPR) + (i % LPR) * LB;
+      kind = NT + 1;
+      if constexpr (BWD) {
+        row = r0 + i / DOL;
+        col = (i % DOL) * LB;
+        tok = true;
+        stride = p.H * D * int(sizeof(TIO));
+      } else {
+        row = r0 + i / LPR;
+        col = (i % LPR) * LB;
+        stride = D * 2;
+      }
+    } else if (sl == 0 && mw == 0 && l < N3 + NTAIL) {
+      const int i = l - N3;
+      kind = NT + 2;
+      col = Cf::RAW ? i * LB : (i * LB) % (GATE == 1 ? D * 4 : 16);
     }
-  } else if (sl == 0 && mw == 0 && l < N3 + NTAIL) {
-    const int i = l - N3;
-    if constexpr (Cf::RAW)
-      a = reinterpret_cast<const char*>(p.fac + cg.ch * Cf::NFAC * C) + i * LB;
-    else
-      a = reinterpret_cast<const char*>(p.edec + cg.ch * (GATE == 1 ? D : 4)) + (i * LB) % (GATE == 1 ? D * 4 : 16);
+    off = row * stride + col;
+    keep(kind);
+    keep(row);
+    keep(col);
+    keep(stride);
+    keep(off);
   }
-  if (a) dma4(a, sink);
+};
+
+template <int D, typename TIO, int GATE, bool BWD>
+__device__ __forceinline__ void prefetch_chunk(const PfLane<D, TIO, GATE, BWD>& pf, const MoverLane<D>& ml,
+                                               const Params& p, const SeqEntry& se, int h, int c, char* sink) {
+  using Cf = ChainCfg<D, TIO, GATE>;
+  using Pl = PfLane<D, TIO, GATE, BWD>;
+  const ChunkGeo cg = geo(p, se, h, c);
+  const int64_t tb = cg.ch * C * D * 2;                                    // a workspace 64 x D tile
+  const int64_t qk = (int64_t(cg.t0) * p.Hk + ml.hk) * D * 2;             // q, k rows of the key head
+  auto base = [&](int kd) -> const char* {
+    if (kd < Pl::NT) {
+      if constexpr (BWD) {
+        if constexpr (Cf::RAW)
+          return kd == 0 ? reinterpret_cast<const char*>(p.k) + qk
+                 : kd == 1 ? reinterpret_cast<const char*>(p.q) + qk
+                           : reinterpret_cast<const char*>(p.W) + tb;
+        else
+          return reinterpret_cast<const char*>(kd == 0 ? p.Kh : kd == 1 ? p.Qh : kd == 2 ? p.Ql : p.W) + tb;
+      } else {
+        if constexpr (Cf::RAW)
+          return kd == 0 ? reinterpret_cast<const char*>(p.W) + tb : reinterpret_cast<const char*>(p.k) + qk;
+        else
+          return reinterpret_cast<const char*>(kd == 0 ? p.W : p.Kh) + tb;
+      }
+    }
+    if (kd == Pl::NT) return reinterpret_cast<const char*>(p.P) + cg.ch * C * C * 2;
+    if (kd == Pl::NT + 1) {
+      if constexpr (BWD)
+        return reinterpret_cast<const char*>(p.dO) + (int64_t(cg.t0) * p.H + h) * D * int64_t(sizeof(TIO));
+      else
+        return reinterpret_cast<const char*>(p.Up) + tb;
+    }
+    if constexpr (Cf::RAW) return reinterpret_cast<const char*>(p.fac + cg.ch * Cf::NFAC * C);
+    else return reinterpret_cast<const char*>(p.edec + cg.ch * (GATE == 1 ? D : 4));
+  };
+  const char* a = base(0);
+#pragma unroll
+  for (int kd = 1; kd < Pl::NK; ++kd) a = pf.kind == kd ? base(kd) : a;
+  const int o = pf.tok && cg.len < C ? min(pf.row, cg.len - 1) * pf.stride + pf.col : pf.off;
+  if (pf.kind >= 0) dma4(a + uint32_t(o), sink);
 }
 
 // ---------------------------------------------------------------------------
@@ -459,20 +530,33 @@ struct LoRegs {
 
 // scalar gate, bf16 inputs: fq dO of the chunk's dO slice in bf16 high + low
 // parts (X2, X3), rows 16w .. 16w+15 by compute wave w (lane: row 16w + l/4,
-// columns 4(l%4) .. +3)
+// columns 4(l%4) .. +3); the reads (raw_rows_in) and the rest (raw_rows_out)
+// apart, so that the reads can join the other reads of a window
+struct RawRows {
+  uint2 r;    // four raw dO values
+  float fq;   // their row's factor
+};
+
 template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void convert_raw_rows(const char* slot, char* x2, char* x3, int w) {
+__device__ __forceinline__ RawRows raw_rows_in(const char* slot, int w) {
   using Cf = ChainCfg<D, TIO, GATE>;
   const int l = lane_id();
   const int row = 16 * w + (l >> 2), o = prow<16>(row) * 32 + (l & 3) * 8;
-  const uint2 r = *reinterpret_cast<const uint2*>(slot + Cf::sDO + o);
-  const float fq = reinterpret_cast<const float*>(slot + Cf::sFac)[row];
-  const float a[4] = {bf16_bits_to_f32(r.x & 0xffffu), bf16_bits_to_f32(r.x >> 16), bf16_bits_to_f32(r.y & 0xffffu),
-                      bf16_bits_to_f32(r.y >> 16)};
+  RawRows v;
+  v.r = *reinterpret_cast<const uint2*>(slot + Cf::sDO + o);
+  v.fq = reinterpret_cast<const float*>(slot + Cf::sFac)[row];
+  return v;
+}
+
+__device__ __forceinline__ void raw_rows_out(const RawRows& v, char* x2, char* x3, int w) {
+  const int l = lane_id();
+  const int o = prow<16>(16 * w + (l >> 2)) * 32 + (l & 3) * 8;
+  const float a[4] = {bf16_bits_to_f32(v.r.x & 0xffffu), bf16_bits_to_f32(v.r.x >> 16),
+                      bf16_bits_to_f32(v.r.y & 0xffffu), bf16_bits_to_f32(v.r.y >> 16)};
   float hv[4], lv[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float y = fq * a[e];
+    const float y = v.fq * a[e];
     hv[e] = float(to_bf16(y));
     lv[e] = y - hv[e];
   }
@@ -571,70 +655,66 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
                    lo_part(acc[x][3]));
       }
       chain_barrier();   // B1
-      // U = U' - W S^T, rows 16w.., columns of this slice
-      f32x4 au = zero4();
-      if constexpr (Cf::RAW) {
-        // W S^T = A Y with Y = Diag(fw) k S^T (W = A Diag(fw) k): every wave forms all
-        // 64 rows of Y (straight-line code schedules better than skipping the blocks
-        // that A's zero upper blocks do not need) and feeds its accumulators, rounded
-        // to bf16, straight back as the B operand, K-step kk pairing the row blocks
-        // 2kk and 2kk+1 (frag_rk_split_s reads the rows of A in that column order)
-        const float* fw = reinterpret_cast<const float*>(sl_k + Cf::sFac) + 2 * C;
-        f32x4 y[4];
+      // U = U' - W S^T, rows 16w.., columns of this slice.  Every LDS read of a
+      // window is issued before its arithmetic (waiting for each fragment right
+      // before its MFMA costs one LDS round trip after another)
+      bf16x8 wf[D / 32], sf[D / 32];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          y[rb] = zero4();
-#pragma unroll
-          for (int k0 = 0; k0 < D; k0 += 32)
-            y[rb] = mma(frag_rk_s<D>(Fb + Cf::fK, 16 * rb, k0), frag_rk_s<D>(Ss, 0, k0), y[rb]);
-          const float4 f = *reinterpret_cast<const float4*>(fw + 16 * rb + 4 * g);
-          y[rb] *= f32x4{f.x, f.y, f.z, f.w};
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          bf16x8 yb;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            yb[i] = to_bf16(y[2 * kk][i]);
-            yb[4 + i] = to_bf16(y[2 * kk + 1][i]);
-          }
-          au = mma(frag_rk_split_s<C>(Fb + Cf::fA, 16 * w, 32 * kk), yb, au);
-        }
-      } else {
-#pragma unroll
-        for (int k0 = 0; k0 < D; k0 += 32) au = mma(frag_rk_s<D>(Fb + Cf::fW, 16 * w, k0), frag_rk_s<D>(Ss, 0, k0), au);
+      for (int i = 0; i < D / 32; ++i) {
+        wf[i] = frag_rk_s<D>(Fb + Cf::fW, 16 * w, 32 * i);
+        sf[i] = frag_rk_s<D>(Ss, 0, 32 * i);
       }
       const uint16_t* Up = reinterpret_cast<const uint16_t*>(Fb + Cf::fUp);
-      float u[4];
+      const uint16_t* Upl = reinterpret_cast<const uint16_t*>(Fb + Cf::fUpl);
+      float u[4], ul[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u[i] = bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]);
+        if constexpr (Cf::SPLIT) ul[i] = bf16_bits_to_f32(Upl[(16 * w + 4 * g + i) * 16 + jj]);
+      }
+      float4 fk = make_float4(1.f, 1.f, 1.f, 1.f);
+      if constexpr (Cf::RAW)
+        fk = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C + 16 * w + 4 * g);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 au = zero4();
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) au = mma(wf[i], sf[i], au);
       // transfer rows: U' = 0
       const float um = job.xfer ? 0.f : 1.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = um * bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]) - au[i];
+      for (int i = 0; i < 4; ++i) u[i] = um * u[i] - au[i];
       if constexpr (Cf::SPLIT) {
-        const uint16_t* Upl = reinterpret_cast<const uint16_t*>(Fb + Cf::fUpl);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] += um * bf16_bits_to_f32(Upl[(16 * w + 4 * g + i) * 16 + jj]);
+        for (int i = 0; i < 4; ++i) u[i] += um * ul[i];
         st4_s<C, 1>(smem + Cf::fUl, jj, 16 * w + 4 * g, lo_part(u[0]), lo_part(u[1]), lo_part(u[2]), lo_part(u[3]));
       }
       if constexpr (Cf::RAW) {
         st4_s<C, 1>(Uo, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
-        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C +
-                                                          16 * w + 4 * g);
-        u[0] *= f.x;
-        u[1] *= f.y;
-        u[2] *= f.z;
-        u[3] *= f.w;
+        u[0] *= fk.x;
+        u[1] *= fk.y;
+        u[2] *= fk.z;
+        u[3] *= fk.w;
       }
       st4_s<C, 1>(Ut, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
       chain_barrier();   // B2
       // S_{k+1}^T = Diag(e^GamC) S_k^T + Khat^T U
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
+      bf16x8 kt[NJW][C / 32], ut[C / 32];
+      f32x4 dv[NJW];
+#pragma unroll
+      for (int kk = 0; kk < C / 32; ++kk) {
+        ut[kk] = frag_rk_s<C, 1>(Ut, 0, 32 * kk);
+#pragma unroll
+        for (int x = 0; x < NJW; ++x) kt[x][kk] = frag_kc_s<D>(Fb + Cf::fK, 16 * (w * NJW + x), 32 * kk);
+      }
+#pragma unroll
+      for (int x = 0; x < NJW; ++x) dv[x] = decay4<D, GATE>(dec, w * NJW + x, g);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
-        const int jb = w * NJW + x;
-        f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
+        f32x4 a = acc[x] * dv[x];
 #pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc_s<D>(Fb + Cf::fK, 16 * jb, k0), frag_rk_s<C, 1>(Ut, 0, k0), a);
+        for (int kk = 0; kk < C / 32; ++kk) a = mma(kt[x][kk], ut[kk], a);
         acc[x] = a;
       }
     }
@@ -671,30 +751,28 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     const int mw = wv - kMoveWave0;
     const bool hs = small_loads<D, TIO, GATE>(mw, false);
     MoverLane<D> ml;
-    ml.init(mw, l);
-    const int sll = v0l / 16;   // the state slice whose rows this workgroup's loads take
-    move_small<D, TIO, GATE>(p, se, h, chunk(0), v0l, slot(0), mw, false);
+    ml.init(p, h, mw, l, int(sizeof(TIO)));
+    PfLane<D, TIO, GATE, false> pf;
+    pf.init(p, v0l / 16, mw, l);   // the rows of the state slice whose U' / dO this workgroup loads
+    move_small<D, TIO, GATE>(ml, p, se, h, chunk(0), v0l, slot(0), mw, false);
     move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), v0l, smem, mw);
     move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
-    move_small<D, TIO, GATE>(p, se, h, chunk(1), v0l, slot(1), mw, false);
+    move_small<D, TIO, GATE>(ml, p, se, h, chunk(1), v0l, slot(1), mw, false);
     move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), v0l, smem + Cf::bufF, mw);
-    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(c), sll, mw, smem + Cf::fPF);
+    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, false>(pf, ml, p, se, h, chunk(c), smem + Cf::fPF);
     wait_mover<Cf::fwdA + Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
     chain_barrier();   // B0
-    // raw mode reads set B (k) in the first window too: both sets of chunk 0 land
-    // before B1; otherwise set B may land by B2
-    if constexpr (Cf::RAW) wait_mover<Cf::fwdA + Cf::PFD - 1>(hs);
-    else wait_mover<Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
+    // set B of chunk 0 may land by B2
+    wait_mover<Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
-      move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, false);
+      move_small<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, false);
       wait_mover<Cf::fwdA + 1 + Cf::fwdB>(hs);
       chain_barrier();   // B2
       move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0l, smem + (k & 1) * Cf::bufF, mw);
-      prefetch_chunk<D, TIO, GATE, false>(p, se, h, chunk(k + Cf::PFD), sll, mw, smem + Cf::fPF);
-      if constexpr (Cf::RAW) wait_mover<Cf::fwdA + 2>(hs);   // set B of chunk k + 1 before the next B1
-      else wait_mover<Cf::fwdB + Cf::fwdA + 2>(hs);
+      prefetch_chunk<D, TIO, GATE, false>(pf, ml, p, se, h, chunk(k + Cf::PFD), smem + Cf::fPF);
+      wait_mover<Cf::fwdB + Cf::fwdA + 2>(hs);
     }
     wait_vm<0>();
   }
@@ -727,7 +805,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     // one step ahead, a quarter each (chunk 0 here, chunk k + 1 in the first
     // window of step k; published by the next barrier)
     if constexpr (Cf::RAW)
-      if (nck > 0) convert_raw_rows<D, TIO, GATE>(slot(0), smem + Cf::bX2, smem + Cf::bX3, w);
+      if (nck > 0) raw_rows_out(raw_rows_in<D, TIO, GATE>(slot(0), w), smem + Cf::bX2, smem + Cf::bX3, w);
     for (int k = 0; k < nck; ++k) {
       const int buf = k & 1;
       const char* Bb = smem + buf * Cf::bufB;
@@ -745,111 +823,105 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
                     lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
       }
       chain_barrier();   // B1
-      // raw mode: fq dO (high, low) of the next chunk first, so that its LDS round
-      // trip overlaps the fragment reads below
-      if constexpr (Cf::RAW)
-        convert_raw_rows<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
-      // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice
-      f32x4 ad = zero4(), ak = zero4();
-      if (!job.xfer) {   // transfer rows: dO = 0
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) {
-          const bf16x8 pa = frag_kc_s<C>(Bb + Cf::bP, 16 * w, k0);
-          ad = mma(pa, frag_kc_s<16>(X1, 0, k0), ad);
-          if constexpr (Cf::LO) ad = mma(pa, frag_kc_s<16>(X2, 0, k0), ad);
-        }
-      }
-#pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) ak = mma(frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0), frag_rk_s<D>(dSl, 0, k0), ak);
-      if constexpr (Cf::RAW) {
-        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C +
-                                                          16 * w + 4 * g);
-        ad += ak * f32x4{f.x, f.y, f.z, f.w};
-      } else {
-        ad += ak;
-      }
-      st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
-      // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU: the first two terms do
-      // not depend on dU and are issued before the barrier
+      // dU = P^T dO + Khat dS^T (rows 16w.., columns of this slice), then the terms
+      // of dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU that do not depend
+      // on dU, before the barrier
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
       f32x4 an[NJW];
+      if constexpr (Cf::RAW) {
+        // every LDS read of the window first, in the order of use (waiting for each
+        // fragment right before its MFMA costs one LDS round trip after another):
+        // the next chunk's dO quarter, dS and k, P and dO, q and fq dO (high, low)
+        const RawRows nxt = raw_rows_in<D, TIO, GATE>(slot(k + 1), w);
+        bf16x8 dsf[D / 32], kf[D / 32], pf[2], x1f[2], x2f[2], x3f[2], qf[NJW][2];
 #pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        const int jb = w * NJW + x;
-        f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
+        for (int i = 0; i < D / 32; ++i) {
+          dsf[i] = frag_rk_s<D>(dSl, 0, 32 * i);
+          kf[i] = frag_rk_s<D>(Bb + Cf::bK, 16 * w, 32 * i);
+        }
+        const float4 fk =
+            *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C + 16 * w + 4 * g);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          pf[kk] = frag_kc_s<C>(Bb + Cf::bP, 16 * w, 32 * kk);
+          x1f[kk] = frag_kc_s<16>(X1, 0, 32 * kk);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          x2f[kk] = frag_kc_s<16>(X2, 0, 32 * kk);
+          x3f[kk] = frag_kc_s<16>(X3, 0, 32 * kk);
+#pragma unroll
+          for (int x = 0; x < NJW; ++x) qf[x][kk] = frag_kc_s<D>(Bb + Cf::bQh, 16 * (w * NJW + x), 32 * kk);
+        }
+        const f32x4 dv = decay4<D, GATE>(dec, 0, g);
+        __builtin_amdgcn_sched_barrier(0);
+        // fq dO (high, low) of the next chunk, published by the next barrier
+        raw_rows_out(nxt, smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
+        f32x4 ad = zero4(), ak = zero4();
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) ak = mma(kf[i], dsf[i], ak);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) ad = mma(pf[kk], x1f[kk], ad);
+        const float m = job.xfer ? 0.f : 1.f;   // transfer rows: dO = 0
+        ad = m * ad + ak * f32x4{fk.x, fk.y, fk.z, fk.w};
+        st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
+#pragma unroll
+        for (int x = 0; x < NJW; ++x) {
+          f32x4 a = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            a = mma(qf[x][kk], x2f[kk], a);
+            a = mma(qf[x][kk], x3f[kk], a);
+          }
+          an[x] = acc[x] * dv + m * a;
+        }
+      } else {
+        // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice
+        f32x4 ad = zero4(), ak = zero4();
         if (!job.xfer) {   // transfer rows: dO = 0
 #pragma unroll
           for (int k0 = 0; k0 < C; k0 += 32) {
-            const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, k0);
-            if constexpr (Cf::RAW) {
-              a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
-              a = mma(qa, frag_kc_s<16>(X3, 0, k0), a);
-            } else {
+            const bf16x8 pa = frag_kc_s<C>(Bb + Cf::bP, 16 * w, k0);
+            ad = mma(pa, frag_kc_s<16>(X1, 0, k0), ad);
+            if constexpr (Cf::LO) ad = mma(pa, frag_kc_s<16>(X2, 0, k0), ad);
+          }
+        }
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 32) ak = mma(frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0), frag_rk_s<D>(dSl, 0, k0), ak);
+        ad += ak;
+        st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
+#pragma unroll
+        for (int x = 0; x < NJW; ++x) {
+          const int jb = w * NJW + x;
+          f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
+          if (!job.xfer) {   // transfer rows: dO = 0
+#pragma unroll
+            for (int k0 = 0; k0 < C; k0 += 32) {
+              const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, k0);
               const bf16x8 bh = frag_kc_s<16>(X1, 0, k0);
               a = mma(qa, bh, a);
               a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, k0), bh, a);
               if constexpr (Cf::LO) a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
             }
           }
+          an[x] = a;
         }
-        an[x] = a;
       }
       chain_barrier();   // B2
-      if constexpr (Cf::RAW) {
-        // W^T dU = k^T Y with Y = Diag(fw) A^T dU (W = A Diag(fw) k).  Every wave
-        // forms all 64 rows of Y (A is block lower triangular: row block rb takes
-        // dU rows from 16 rb on) and feeds its accumulators, rounded to bf16,
-        // straight back as the B operand of k^T Y, K-step kk pairing the row
-        // blocks 2kk and 2kk+1 (frag_kc_split_s reads k^T in that row order)
-        const bf16x8 du0 = frag_rk_s<C, 1>(dUt, 0, 0), du1 = frag_rk_s<C, 1>(dUt, 0, 32);
-        // fw of this lane's Y rows 16 rb + 4g .. +3 and the k^T fragments, read in
-        // the same round trip as dU
-        const float* fw = reinterpret_cast<const float*>(sl_k + Cf::sFac) + 2 * C;
-        f32x4 fwv[4];
+      bf16x8 wt[NJW][C / 32], duf[C / 32];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const float4 f = *reinterpret_cast<const float4*>(fw + 16 * rb + 4 * g);
-          fwv[rb] = f32x4{f.x, f.y, f.z, f.w};
-        }
-        bf16x8 kfr[NJW][2];
+      for (int kk = 0; kk < C / 32; ++kk) {
+        duf[kk] = frag_rk_s<C, 1>(dUt, 0, 32 * kk);
 #pragma unroll
-        for (int x = 0; x < NJW; ++x)
+        for (int x = 0; x < NJW; ++x) wt[x][kk] = frag_kc_s<D>(Bb + Cf::bW, 16 * (w * NJW + x), 32 * kk);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) kfr[x][kk] = frag_kc_split_s<D>(Bb + Cf::bK, 16 * (w * NJW + x), 32 * kk);
-        f32x4 y[4];
+      for (int x = 0; x < NJW; ++x) {
+        f32x4 aw = zero4();
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          y[rb] = zero4();
-          if (rb < 2) y[rb] = mma(frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 0), du0, y[rb]);
-          y[rb] = mma(frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 32), du1, y[rb]);
-          y[rb] *= fwv[rb];
-        }
-        bf16x8 yb[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            yb[kk][i] = to_bf16(y[2 * kk][i]);
-            yb[kk][4 + i] = to_bf16(y[2 * kk + 1][i]);
-          }
-#pragma unroll
-        for (int x = 0; x < NJW; ++x) {
-          const int jb = w * NJW + x;
-          f32x4 aw = zero4();
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) aw = mma(kfr[x][kk], yb[kk], aw);
-          acc[x] = an[x] - aw;
-        }
-      } else {
-#pragma unroll
-        for (int x = 0; x < NJW; ++x) {
-          const int jb = w * NJW + x;
-          f32x4 aw = zero4();
-#pragma unroll
-          for (int k0 = 0; k0 < C; k0 += 32)
-            aw = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C, 1>(dUt, 0, k0), aw);
-          acc[x] = an[x] - aw;
-        }
+        for (int kk = 0; kk < C / 32; ++kk) aw = mma(wt[x][kk], duf[kk], aw);
+        acc[x] = an[x] - aw;
       }
     }
     job_fin<D>(job, acc, w, g, jj);
@@ -890,14 +962,15 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     const int mw = wv - kMoveWave0;
     const bool hs = small_loads<D, TIO, GATE>(mw, true);
     MoverLane<D> ml;
-    ml.init(mw, l);
-    const int sll = v0l / 16;   // the state slice whose rows this workgroup's loads take
-    move_small<D, TIO, GATE>(p, se, h, chunk(0), v0l, slot(0), mw, true);
+    ml.init(p, h, mw, l, int(sizeof(TIO)));
+    PfLane<D, TIO, GATE, true> pf;
+    pf.init(p, v0l / 16, mw, l);   // the rows of the state slice whose U' / dO this workgroup loads
+    move_small<D, TIO, GATE>(ml, p, se, h, chunk(0), v0l, slot(0), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
     move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
-    move_small<D, TIO, GATE>(p, se, h, chunk(1), v0l, slot(1), mw, true);
+    move_small<D, TIO, GATE>(ml, p, se, h, chunk(1), v0l, slot(1), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), smem + Cf::bufB, mw);
-    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(c), sll, mw, smem + Cf::bPF);
+    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, true>(pf, ml, p, se, h, chunk(c), smem + Cf::bPF);
     wait_mover<Cf::bwdA + Cf::bwdB + Cf::bwdA + Cf::PFD - 2>(hs);
     chain_barrier();   // B0
     // both sets of chunk 0 and the small data of chunk 1 land before B1 (set B is
@@ -906,11 +979,11 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
-      move_small<D, TIO, GATE>(p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, true);
+      move_small<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, true);
       wait_mover<Cf::bwdA + 1 + Cf::bwdB>(hs);
       chain_barrier();   // B2
       move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
-      prefetch_chunk<D, TIO, GATE, true>(p, se, h, chunk(k + Cf::PFD), sll, mw, smem + Cf::bPF);
+      prefetch_chunk<D, TIO, GATE, true>(pf, ml, p, se, h, chunk(k + Cf::PFD), smem + Cf::bPF);
       // set B of chunk k + 1 and the small data of chunk k + 2 land before the
       // next B1: only set A of chunk k + 2 and the prefetch stay in flight
       wait_vm<Cf::bwdA + 1>();

@@ -66,11 +66,15 @@ __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (bf16)x); }
 
-// Four fp32 -> four bf16 packed into 8 bytes.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Four fp32 -> four bf16 (round to nearest even) packed into 8 bytes, one packed
+// conversion per pair.
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
   uint2 r;
-  r.x = uint32_t(f32_to_bf16_bits(a)) | (uint32_t(f32_to_bf16_bits(b)) << 16);
-  r.y = uint32_t(f32_to_bf16_bits(c)) | (uint32_t(f32_to_bf16_bits(d)) << 16);
+  r.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{c, d}, bf16x2));
   return r;
 }
 

@@ -159,9 +159,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   // inputs the Khat and Qbar (high + low) tiles ---
   if (tid < C) {
     const float m = tid < len ? 1.f : 0.f, gC = gam_s[C - 1], gr = gam_s[tid];
-    p.fac[ch * 3 * C + tid] = m * p.scale * rq_s[tid] * fast_exp(gr);
-    p.fac[ch * 3 * C + C + tid] = m * rk_s[tid] * fast_exp(gC - gr);
-    p.fac[ch * 3 * C + 2 * C + tid] = beta_s[tid] * rk_s[tid] * fast_exp(gr);   // W = A Diag(this) k
+    p.fac[ch * 2 * C + tid] = m * p.scale * rq_s[tid] * fast_exp(gr);
+    p.fac[ch * 2 * C + C + tid] = m * rk_s[tid] * fast_exp(gC - gr);
     if (tid == 0) p.edec[ch * 4] = fast_exp(gC);
   }
   if constexpr (kMat) {
@@ -222,8 +221,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
     *reinterpret_cast<u32x4*>(p.P + (ch * C + row) * C + c8) = *reinterpret_cast<const u32x4*>(As + row * PC + c8);
   }
 
-  // --- beta * Kbar (for W; fp32 inputs only, bf16 inputs leave W to the
-  // recursions as A Diag(fw) k) and beta * V overwrite the operand tiles ---
+  // --- beta * Kbar (for W) and beta * V overwrite the operand tiles ---
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
@@ -234,7 +232,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
       kb[e] = to_bf16(kn_r[ps][e] * fk);
       vb[e] = to_bf16(v_r[ps][e] * fv);
     }
-    if constexpr (kMat) *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
+    *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
     *reinterpret_cast<bf16x8*>(Vs + r * PD + c0) = vb;
   }
 
@@ -293,7 +291,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   }
   __syncthreads();
 
-  // --- W (fp32 inputs) and U' tiles: lane owns W[r][j .. j+3] ---
+  // --- W and U' tiles: lane owns W[r][j .. j+3] ---
   {
     const int r = 16 * rb + (l & 15);
 #pragma unroll
@@ -303,11 +301,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
 #pragma unroll
       for (int k0 = 0; k0 < C; k0 += 32) {
         const bf16x8 b = frag_rk(As, PC, 16 * rb, k0);  // B[s][r] = A[r][s]
-        if constexpr (kMat) aW = mma(frag_kc(Ks, PD, 16 * jb, k0), b, aW);
+        aW = mma(frag_kc(Ks, PD, 16 * jb, k0), b, aW);
         aU = mma(frag_kc(Vs, PD, 16 * jb, k0), b, aU);
       }
       const int j0 = 16 * jb + 4 * (l >> 4);
-      if constexpr (kMat) st_bf16x4(p.W + (ch * C + r) * D + j0, aW[0], aW[1], aW[2], aW[3]);
+      st_bf16x4(p.W + (ch * C + r) * D + j0, aW[0], aW[1], aW[2], aW[3]);
       st_bf16x4(p.Up + (ch * C + r) * D + j0, aU[0], aU[1], aU[2], aU[3]);
     }
   }
