@@ -291,7 +291,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   }
   __syncthreads();
 
-  // --- W and U' tiles: lane owns W[r][j .. j+3] ---
+  // --- W and U' tiles: lane owns W[r][j .. j+3]; staged in the inverse's
+  // scratch (free by now) and stored as 16-byte row pieces ---
+  static_assert(C * PD * 2 <= kQX && C * PD * 2 <= C * PL * 4, "staging tiles fit");
+  bf16* const Wst = reinterpret_cast<bf16*>(QX);
+  bf16* const Ust = reinterpret_cast<bf16*>(Lf);
   {
     const int r = 16 * rb + (l & 15);
 #pragma unroll
@@ -305,9 +309,16 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
         aU = mma(frag_kc(Vs, PD, 16 * jb, k0), b, aU);
       }
       const int j0 = 16 * jb + 4 * (l >> 4);
-      st_bf16x4(p.W + (ch * C + r) * D + j0, aW[0], aW[1], aW[2], aW[3]);
-      st_bf16x4(p.Up + (ch * C + r) * D + j0, aU[0], aU[1], aU[2], aU[3]);
+      st_bf16x4(Wst + r * PD + j0, aW[0], aW[1], aW[2], aW[3]);
+      st_bf16x4(Ust + r * PD + j0, aU[0], aU[1], aU[2], aU[3]);
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < C * D / 8 / kT; ++it) {
+    const int idx = tid + kT * it, row = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+    *reinterpret_cast<u32x4*>(p.W + (ch * C + row) * D + c8) = *reinterpret_cast<const u32x4*>(Wst + row * PD + c8);
+    *reinterpret_cast<u32x4*>(p.Up + (ch * C + row) * D + c8) = *reinterpret_cast<const u32x4*>(Ust + row * PD + c8);
   }
 }
 
