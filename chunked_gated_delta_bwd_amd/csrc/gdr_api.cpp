@@ -167,14 +167,14 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.stab = take(NS * sizeof(gdr::SeqEntry));
   L.gam = take(H * NC * C * gk * 4);
   L.rho = take(H * NC * 3 * C * 4);
-  L.fac = take(H * NC * 2 * C * 4);
+  L.fac = take(H * NC * 3 * C * 4);
   L.edec = take(H * NC * (gk == 1 ? 4 : gk) * 4);
-  // materialised Khat / Qbar tiles: the per-channel gate and fp32 inputs (the
-  // scalar gate with bf16 inputs works from the raw q, k rows and row factors)
+  // materialised Khat / Qbar / W tiles: the per-channel gate and fp32 inputs (the
+  // scalar gate with bf16 inputs works from the raw rows, row factors and A)
   const size_t mat = (s->gate != GDR_GATE_SCALAR || s->dtype == GDR_F32) ? 1 : 0;
   L.A = take(H * NC * C * C * 2);
   L.P = take(H * NC * C * C * 2);
-  L.W = take(H * NC * C * K * 2);
+  L.W = take(mat * H * NC * C * K * 2);
   L.Up = take(H * NC * C * V * 2);
   L.U = take(H * NC * C * V * 2);
   L.S = take(H * NC * V * K * 2);

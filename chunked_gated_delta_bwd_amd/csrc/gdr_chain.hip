@@ -51,10 +51,6 @@
 // row factors of Qbar = q (scale e^Gam / |q|) and Khat = k (e^(GamC - Gam) / |k|)
 // to the small operands instead (dO rows, U rows, dU rows); the per-channel
 // gate and fp32 inputs take the Khat / Qbar tiles the prologue kernel formed.
-// Both take the W tile the prologue formed: W S^T and W^T dU straight from it
-// (forming them from A and k instead costs every compute wave A, k and row
-// factor reads of all 64 rows each step, and the recursions are bound by their
-// LDS traffic).
 // Qbar^T dO carries the dominant part of dh0, so that product is taken in two
 // bf16 parts (Qbar high + low, or the scaled dO high + low).
 #include <hip/hip_runtime.h>
@@ -87,19 +83,19 @@ struct ChainCfg {
   static constexpr int XB = C * 16 * 2;            // a 64 x 16 bf16 slice
   static constexpr int NJ = TB / 4096;             // 1 KB loads per mover wave per 64 x D tile
   // small per-chunk data, three rotating slots: the raw dO slice (bf16 inputs),
-  // the row factors fq, fk (raw mode) and the decay
-  static constexpr int NFAC = 2;
+  // the row factors fq, fk, fw (raw mode) and the decay
+  static constexpr int NFAC = 3;
   static constexpr int sDO = 0;
   static constexpr int sFac = sDO + (LO ? 0 : XB);
   static constexpr int sDec = sFac + (RAW ? NFAC * C * 4 : 0);
   static constexpr int SLOT = sDec + DG * 4;
   // reverse role, byte offsets; the tile buffers first.  Materialised tiles:
-  // Khat, Qbar high, low, W, P.  Raw mode: k, q, P, W.  Set A (Khat or q, and P)
-  // is read in the first window, set B (Qbar and W, or k and W) in both
-  static constexpr int bK = 0, bQh = TB, bQl = 2 * TB;
-  static constexpr int bW = MAT ? 3 * TB : 2 * TB + PB;
+  // Khat, Qbar high, low, W, P.  Raw mode: q, P (set A), k, A (set B), where
+  // W^T dU is formed as k^T (Diag(fw) A^T dU) from the raw k rows already there
+  static constexpr int bK = 0, bQh = TB, bQl = 2 * TB, bW = 3 * TB;
   static constexpr int bP = MAT ? 4 * TB : 2 * TB;
-  static constexpr int bufB = MAT ? 4 * TB + PB : 3 * TB + PB;
+  static constexpr int bA = 2 * TB + PB;                           // raw mode
+  static constexpr int bufB = MAT ? 4 * TB + PB : 2 * TB + 2 * PB;
   static constexpr int bX1 = 2 * bufB;                             // LO: dO high part
   static constexpr int bX2 = bX1 + (LO ? 2 * XB : 0);              // RAW: fq dO high; LO: dO low
   static constexpr int bX3 = bX2 + ((RAW || LO) ? 2 * XB : 0);     // RAW: fq dO low
@@ -112,8 +108,10 @@ struct ChainCfg {
   static constexpr int NDU = bdU + 2 * dUB + 256 <= 160 * 1024 ? 2 : 1;
   static constexpr int bPF = bdU + NDU * dUB;                      // 256 B sink of the L2 prefetches
   static constexpr int bEnd = bPF + 256;
-  // forward role: W, Khat (raw mode: k), the U' slice (and its low part)
-  static constexpr int fW = 0, fK = TB, fUp = 2 * TB, fUpl = fUp + XB;
+  // forward role
+  // forward role: materialised tiles W, Khat; raw mode A (in W's place) and k,
+  // with W S^T formed as A (Diag(fw) k S^T)
+  static constexpr int fW = 0, fA = 0, fK = MAT ? TB : PB, fUp = fK + TB, fUpl = fUp + XB;
   static constexpr int bufF = fUpl + (SPLIT ? XB : 0);
   static constexpr int fSlot = 2 * bufF;
   static constexpr int fS = fSlot + 3 * SLOT;                      // 16 x D state slice
@@ -130,13 +128,30 @@ struct ChainCfg {
   // none wait for one fewer: wait_mover)
   static constexpr int nSb = 1;
   static constexpr int nSf = 1;
-  static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 * NJ : 2 * NJ) + nSb;
+  static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 * NJ : NJ + 2) + nSb;
   // L2 prefetch distance in chunk steps (one prefetch load per mover wave per step)
   static constexpr int PFD = 5;
-  static constexpr int fwdA = NJ + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
+  static constexpr int fwdA = (MAT ? NJ : 2) + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(2 * bwdA + bwdB + PFD - 2 < 64 && 2 * fwdA + fwdB + PFD - 2 < 64, "vmcnt range");
 };
+
+// The segment entry of a workgroup, read once into scalar registers (left in
+// memory, the compiler may reload it with a vector load inside a chunk loop, and
+// a mover's wait for that load drains all of its tile loads in flight)
+__device__ __forceinline__ SeqEntry seq_entry(const Params& p, int si) {
+  const SeqEntry e = p.stab[si];
+  SeqEntry r;
+  r.seq = __builtin_amdgcn_readfirstlane(e.seq);
+  r.len = __builtin_amdgcn_readfirstlane(e.len);
+  r.c0 = __builtin_amdgcn_readfirstlane(e.c0);
+  r.nchunks = __builtin_amdgcn_readfirstlane(e.nchunks);
+  r.t_start = __builtin_amdgcn_readfirstlane(e.t_start);
+  r.seg = __builtin_amdgcn_readfirstlane(e.seg);
+  r.nseg = __builtin_amdgcn_readfirstlane(e.nseg);
+  r.slot = __builtin_amdgcn_readfirstlane(e.slot);
+  return r;
+}
 
 struct ChunkGeo {
   int64_t ch;   // chunk-head index
@@ -264,7 +279,7 @@ __device__ __forceinline__ void move_small(const MoverLane<D>& ml, const Params&
       dma16(s + uint32_t(o), slot + Cf::sDO + mw * 1024);
     } else if (mw == (with_dO ? 2 : 0)) {
       if constexpr (Cf::RAW) {
-        // fq, fk (512 bytes, lanes 0-31), then the decay (lane 32) right behind them
+        // fq, fk, fw (768 bytes, lanes 0-47), then the decay (lane 48) right behind them
         constexpr int NL = Cf::NFAC * C * 4 / 16;
         static_assert(Cf::sDec == Cf::sFac + NL * 16, "decay follows the row factors");
         if (l < NL) dma16(reinterpret_cast<const char*>(p.fac + cg.ch * Cf::NFAC * C) + l * 16, slot + Cf::sFac);
@@ -286,7 +301,7 @@ __device__ __forceinline__ void wait_mover(bool has_small) {
 }
 
 // reverse role: set A (Khat, P; raw mode q, P), set B (Qbar high + low, W; raw
-// mode k, W)
+// mode k, A)
 template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void move_bwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            char* buf, int mw) {
@@ -306,20 +321,24 @@ __device__ __forceinline__ void move_bwd_b(const MoverLane<D>& ml, const Params&
   const ChunkGeo cg = geo(p, se, h, c);
   if constexpr (Cf::RAW) {
     move_rows<D>(ml, p.k, cg, buf + Cf::bK, mw);
+    move_p<D>(ml, p.A + cg.ch * C * C, buf + Cf::bA, mw);
   } else {
     move_tile<D>(ml, p.Qh + cg.ch * C * D, buf + Cf::bQh, mw);
     move_tile<D>(ml, p.Ql + cg.ch * C * D, buf + Cf::bQl, mw);
+    move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::bW, mw);
   }
-  move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::bW, mw);
 }
 
-// forward role: set A (W, the U' slice), set B (Khat or k)
+// forward role: set A (W or, raw mode, A; the U' slice), set B (Khat or k)
 template <int D, typename TIO, int GATE>
 __device__ __forceinline__ void move_fwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            int v0, char* buf, int mw) {
   using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
-  move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::fW, mw);
+  if constexpr (Cf::MAT)
+    move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::fW, mw);
+  else
+    move_p<D>(ml, p.A + cg.ch * C * C, buf + Cf::fA, mw);
   if (lane_id() < 32) dma16(reinterpret_cast<const char*>(p.Up + cg.ch * C * D + v0) + ml.up, buf + Cf::fUp + mw * 512);
   if constexpr (Cf::SPLIT) {
     if (lane_id() < 32)
@@ -352,15 +371,16 @@ struct PfLane {
   static constexpr int LPR = (2 * D) / LB;                        // loads per row of a 64 x D bf16 tile
   static constexpr int DOL = int(D * sizeof(TIO)) / LB;           // loads per dO row of one head
   static constexpr int NP = 128 / LB;                             // loads per row of a 64 x 64 tile
-  static constexpr int NT = BWD ? (Cf::MAT ? 4 : 3) : 2;          // tiles with D-wide rows
-  static constexpr int NT64 = BWD ? 1 : 0;                        // 64 x 64 tiles (P)
+  static constexpr int NT = BWD ? (Cf::MAT ? 4 : 2) : (Cf::MAT ? 2 : 1);   // tiles with D-wide rows
+  static constexpr int NT64 = BWD ? (Cf::MAT ? 1 : 2) : (Cf::MAT ? 0 : 1);  // 64 x 64 tiles (P, A)
   static constexpr int NTAIL = (Cf::RAW ? Cf::NFAC * C * 4 : 512) / LB;   // row factors or the decay
   static constexpr int N1 = NT * RW * LPR, N2 = N1 + NT64 * RW * NP, N3 = N2 + (BWD ? RW * DOL : RW * LPR);
   static_assert(N3 + NTAIL <= 64, "one prefetch load per wave");
   // kinds: 0 .. NT - 1 the D-wide tiles (reverse: Khat, Qbar high, low, W; raw
-  // mode k, q, W; forward: W, Khat or k), NT the P tile, NT + 1 the dO rows
-  // (reverse) or U' rows (forward), NT + 2 the row factors or decay; -1 idle
-  static constexpr int NK = NT + 3;
+  // mode k, q; forward: W, Khat; raw mode k), then the 64 x 64 tiles (reverse: P,
+  // raw mode A too; forward, raw mode: A), then the dO rows (reverse) or U' rows
+  // (forward), then the row factors or decay; -1 idle
+  static constexpr int KR = NT + NT64, KT = KR + 1, NK = KR + 2;
   int kind, row, col, stride, off;
   bool tok;   // token rows (clamped at the end of a sequence)
 
@@ -376,17 +396,17 @@ struct PfLane {
       kind = t;
       row = r0 + rem / LPR;
       col = (rem % LPR) * LB;
-      tok = Cf::RAW && (BWD ? t < 2 : t == 1);
+      tok = Cf::RAW;
       stride = tok ? p.Hk * D * 2 : D * 2;
     } else if (l < N2) {
-      const int i = l - N1;
-      kind = NT;
-      row = r0 + i / NP;
-      col = (i % NP) * LB;
+      const int i = l - N1, t = i / (RW * NP), rem = i % (RW * NP);
+      kind = NT + t;
+      row = r0 + rem / NP;
+      col = (rem % NP) * LB;
       stride = C * 2;
     } else if (l < N3) {
       const int i = l - N2;
-      kind = NT + 1;
+      kind = KR;
       if constexpr (BWD) {
         row = r0 + i / DOL;
         col = (i % DOL) * LB;
@@ -399,7 +419,7 @@ struct PfLane {
       }
     } else if (sl == 0 && mw == 0 && l < N3 + NTAIL) {
       const int i = l - N3;
-      kind = NT + 2;
+      kind = KT;
       col = Cf::RAW ? i * LB : (i * LB) % (GATE == 1 ? D * 4 : 16);
     }
     off = row * stride + col;
@@ -410,6 +430,16 @@ struct PfLane {
     keep(off);
   }
 };
+
+// a pointer the whole wave holds, pinned in scalar registers (a choice between
+// such pointers per lane is then register moves; chosen among Params fields
+// directly, the compiler turns it into a per-lane load from the kernel arguments,
+// and the wait for that load drains every load in flight)
+__device__ __forceinline__ const char* wave_ptr(const void* q) {
+  const uint64_t u = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u)), hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
+  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+}
 
 template <int D, typename TIO, int GATE, bool BWD>
 __device__ __forceinline__ void prefetch_chunk(const PfLane<D, TIO, GATE, BWD>& pf, const MoverLane<D>& ml,
@@ -423,20 +453,18 @@ __device__ __forceinline__ void prefetch_chunk(const PfLane<D, TIO, GATE, BWD>& 
     if (kd < Pl::NT) {
       if constexpr (BWD) {
         if constexpr (Cf::RAW)
-          return kd == 0 ? reinterpret_cast<const char*>(p.k) + qk
-                 : kd == 1 ? reinterpret_cast<const char*>(p.q) + qk
-                           : reinterpret_cast<const char*>(p.W) + tb;
+          return reinterpret_cast<const char*>(kd == 0 ? p.k : p.q) + qk;
         else
           return reinterpret_cast<const char*>(kd == 0 ? p.Kh : kd == 1 ? p.Qh : kd == 2 ? p.Ql : p.W) + tb;
       } else {
         if constexpr (Cf::RAW)
-          return kd == 0 ? reinterpret_cast<const char*>(p.W) + tb : reinterpret_cast<const char*>(p.k) + qk;
+          return reinterpret_cast<const char*>(p.k) + qk;
         else
           return reinterpret_cast<const char*>(kd == 0 ? p.W : p.Kh) + tb;
       }
     }
-    if (kd == Pl::NT) return reinterpret_cast<const char*>(p.P) + cg.ch * C * C * 2;
-    if (kd == Pl::NT + 1) {
+    if (kd < Pl::KR) return reinterpret_cast<const char*>(BWD && kd == Pl::NT ? p.P : p.A) + cg.ch * C * C * 2;
+    if (kd == Pl::KR) {
       if constexpr (BWD)
         return reinterpret_cast<const char*>(p.dO) + (int64_t(cg.t0) * p.H + h) * D * int64_t(sizeof(TIO));
       else
@@ -445,9 +473,12 @@ __device__ __forceinline__ void prefetch_chunk(const PfLane<D, TIO, GATE, BWD>& 
     if constexpr (Cf::RAW) return reinterpret_cast<const char*>(p.fac + cg.ch * Cf::NFAC * C);
     else return reinterpret_cast<const char*>(p.edec + cg.ch * (GATE == 1 ? D : 4));
   };
-  const char* a = base(0);
+  const char* a = wave_ptr(base(0));
 #pragma unroll
-  for (int kd = 1; kd < Pl::NK; ++kd) a = pf.kind == kd ? base(kd) : a;
+  for (int kd = 1; kd < Pl::NK; ++kd) {
+    const char* b = wave_ptr(base(kd));
+    a = pf.kind == kd ? b : a;
+  }
   const int o = pf.tok && cg.len < C ? min(pf.row, cg.len - 1) * pf.stride + pf.col : pf.off;
   if (pf.kind >= 0) dma4(a + uint32_t(o), sink);
 }
@@ -530,33 +561,20 @@ struct LoRegs {
 
 // scalar gate, bf16 inputs: fq dO of the chunk's dO slice in bf16 high + low
 // parts (X2, X3), rows 16w .. 16w+15 by compute wave w (lane: row 16w + l/4,
-// columns 4(l%4) .. +3); the reads (raw_rows_in) and the rest (raw_rows_out)
-// apart, so that the reads can join the other reads of a window
-struct RawRows {
-  uint2 r;    // four raw dO values
-  float fq;   // their row's factor
-};
-
+// columns 4(l%4) .. +3)
 template <int D, typename TIO, int GATE>
-__device__ __forceinline__ RawRows raw_rows_in(const char* slot, int w) {
+__device__ __forceinline__ void convert_raw_rows(const char* slot, char* x2, char* x3, int w) {
   using Cf = ChainCfg<D, TIO, GATE>;
   const int l = lane_id();
   const int row = 16 * w + (l >> 2), o = prow<16>(row) * 32 + (l & 3) * 8;
-  RawRows v;
-  v.r = *reinterpret_cast<const uint2*>(slot + Cf::sDO + o);
-  v.fq = reinterpret_cast<const float*>(slot + Cf::sFac)[row];
-  return v;
-}
-
-__device__ __forceinline__ void raw_rows_out(const RawRows& v, char* x2, char* x3, int w) {
-  const int l = lane_id();
-  const int o = prow<16>(16 * w + (l >> 2)) * 32 + (l & 3) * 8;
-  const float a[4] = {bf16_bits_to_f32(v.r.x & 0xffffu), bf16_bits_to_f32(v.r.x >> 16),
-                      bf16_bits_to_f32(v.r.y & 0xffffu), bf16_bits_to_f32(v.r.y >> 16)};
+  const uint2 r = *reinterpret_cast<const uint2*>(slot + Cf::sDO + o);
+  const float fq = reinterpret_cast<const float*>(slot + Cf::sFac)[row];
+  const float a[4] = {bf16_bits_to_f32(r.x & 0xffffu), bf16_bits_to_f32(r.x >> 16), bf16_bits_to_f32(r.y & 0xffffu),
+                      bf16_bits_to_f32(r.y >> 16)};
   float hv[4], lv[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float y = v.fq * a[e];
+    const float y = fq * a[e];
     hv[e] = float(to_bf16(y));
     lv[e] = y - hv[e];
   }
@@ -629,7 +647,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id();
   const int g = l >> 4, jj = l & 15;
-  const SeqEntry se = p.stab[si];
+  const SeqEntry se = seq_entry(p, si);
   const int v0 = 16 * sl, v0l = job.v0l;
   const int nck = se.nchunks;
   char* Ss = smem + Cf::fS;
@@ -655,66 +673,70 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
                    lo_part(acc[x][3]));
       }
       chain_barrier();   // B1
-      // U = U' - W S^T, rows 16w.., columns of this slice.  Every LDS read of a
-      // window is issued before its arithmetic (waiting for each fragment right
-      // before its MFMA costs one LDS round trip after another)
-      bf16x8 wf[D / 32], sf[D / 32];
+      // U = U' - W S^T, rows 16w.., columns of this slice
+      f32x4 au = zero4();
+      if constexpr (Cf::RAW) {
+        // W S^T = A Y with Y = Diag(fw) k S^T (W = A Diag(fw) k): every wave forms all
+        // 64 rows of Y (straight-line code schedules better than skipping the blocks
+        // that A's zero upper blocks do not need) and feeds its accumulators, rounded
+        // to bf16, straight back as the B operand, K-step kk pairing the row blocks
+        // 2kk and 2kk+1 (frag_rk_split_s reads the rows of A in that column order)
+        const float* fw = reinterpret_cast<const float*>(sl_k + Cf::sFac) + 2 * C;
+        f32x4 y[4];
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        wf[i] = frag_rk_s<D>(Fb + Cf::fW, 16 * w, 32 * i);
-        sf[i] = frag_rk_s<D>(Ss, 0, 32 * i);
+        for (int rb = 0; rb < 4; ++rb) {
+          y[rb] = zero4();
+#pragma unroll
+          for (int k0 = 0; k0 < D; k0 += 32)
+            y[rb] = mma(frag_rk_s<D>(Fb + Cf::fK, 16 * rb, k0), frag_rk_s<D>(Ss, 0, k0), y[rb]);
+          const float4 f = *reinterpret_cast<const float4*>(fw + 16 * rb + 4 * g);
+          y[rb] *= f32x4{f.x, f.y, f.z, f.w};
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bf16x8 yb;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            yb[i] = to_bf16(y[2 * kk][i]);
+            yb[4 + i] = to_bf16(y[2 * kk + 1][i]);
+          }
+          au = mma(frag_rk_split_s<C>(Fb + Cf::fA, 16 * w, 32 * kk), yb, au);
+        }
+      } else {
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 32) au = mma(frag_rk_s<D>(Fb + Cf::fW, 16 * w, k0), frag_rk_s<D>(Ss, 0, k0), au);
       }
       const uint16_t* Up = reinterpret_cast<const uint16_t*>(Fb + Cf::fUp);
-      const uint16_t* Upl = reinterpret_cast<const uint16_t*>(Fb + Cf::fUpl);
-      float u[4], ul[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u[i] = bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]);
-        if constexpr (Cf::SPLIT) ul[i] = bf16_bits_to_f32(Upl[(16 * w + 4 * g + i) * 16 + jj]);
-      }
-      float4 fk = make_float4(1.f, 1.f, 1.f, 1.f);
-      if constexpr (Cf::RAW)
-        fk = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C + 16 * w + 4 * g);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 au = zero4();
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) au = mma(wf[i], sf[i], au);
+      float u[4];
       // transfer rows: U' = 0
       const float um = job.xfer ? 0.f : 1.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = um * u[i] - au[i];
+      for (int i = 0; i < 4; ++i) u[i] = um * bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]) - au[i];
       if constexpr (Cf::SPLIT) {
+        const uint16_t* Upl = reinterpret_cast<const uint16_t*>(Fb + Cf::fUpl);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] += um * ul[i];
+        for (int i = 0; i < 4; ++i) u[i] += um * bf16_bits_to_f32(Upl[(16 * w + 4 * g + i) * 16 + jj]);
         st4_s<C, 1>(smem + Cf::fUl, jj, 16 * w + 4 * g, lo_part(u[0]), lo_part(u[1]), lo_part(u[2]), lo_part(u[3]));
       }
       if constexpr (Cf::RAW) {
         st4_s<C, 1>(Uo, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
-        u[0] *= fk.x;
-        u[1] *= fk.y;
-        u[2] *= fk.z;
-        u[3] *= fk.w;
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C +
+                                                          16 * w + 4 * g);
+        u[0] *= f.x;
+        u[1] *= f.y;
+        u[2] *= f.z;
+        u[3] *= f.w;
       }
       st4_s<C, 1>(Ut, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
       chain_barrier();   // B2
       // S_{k+1}^T = Diag(e^GamC) S_k^T + Khat^T U
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
-      bf16x8 kt[NJW][C / 32], ut[C / 32];
-      f32x4 dv[NJW];
-#pragma unroll
-      for (int kk = 0; kk < C / 32; ++kk) {
-        ut[kk] = frag_rk_s<C, 1>(Ut, 0, 32 * kk);
-#pragma unroll
-        for (int x = 0; x < NJW; ++x) kt[x][kk] = frag_kc_s<D>(Fb + Cf::fK, 16 * (w * NJW + x), 32 * kk);
-      }
-#pragma unroll
-      for (int x = 0; x < NJW; ++x) dv[x] = decay4<D, GATE>(dec, w * NJW + x, g);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
-        f32x4 a = acc[x] * dv[x];
+        const int jb = w * NJW + x;
+        f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
 #pragma unroll
-        for (int kk = 0; kk < C / 32; ++kk) a = mma(kt[x][kk], ut[kk], a);
+        for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc_s<D>(Fb + Cf::fK, 16 * jb, k0), frag_rk_s<C, 1>(Ut, 0, k0), a);
         acc[x] = a;
       }
     }
@@ -762,8 +784,10 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, false>(pf, ml, p, se, h, chunk(c), smem + Cf::fPF);
     wait_mover<Cf::fwdA + Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
     chain_barrier();   // B0
-    // set B of chunk 0 may land by B2
-    wait_mover<Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
+    // raw mode reads set B (k) in the first window too: both sets of chunk 0 land
+    // before B1; otherwise set B may land by B2
+    if constexpr (Cf::RAW) wait_mover<Cf::fwdA + Cf::PFD - 1>(hs);
+    else wait_mover<Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
@@ -772,7 +796,8 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       chain_barrier();   // B2
       move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0l, smem + (k & 1) * Cf::bufF, mw);
       prefetch_chunk<D, TIO, GATE, false>(pf, ml, p, se, h, chunk(k + Cf::PFD), smem + Cf::fPF);
-      wait_mover<Cf::fwdB + Cf::fwdA + 2>(hs);
+      if constexpr (Cf::RAW) wait_mover<Cf::fwdA + 2>(hs);   // set B of chunk k + 1 before the next B1
+      else wait_mover<Cf::fwdB + Cf::fwdA + 2>(hs);
     }
     wait_vm<0>();
   }
@@ -786,7 +811,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id();
   const int g = l >> 4, jj = l & 15;
-  const SeqEntry se = p.stab[si];
+  const SeqEntry se = seq_entry(p, si);
   const int v0 = 16 * sl, v0l = job.v0l;
   const int nck = se.nchunks;
   char* dSl = smem + Cf::bdS;
@@ -805,7 +830,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     // one step ahead, a quarter each (chunk 0 here, chunk k + 1 in the first
     // window of step k; published by the next barrier)
     if constexpr (Cf::RAW)
-      if (nck > 0) raw_rows_out(raw_rows_in<D, TIO, GATE>(slot(0), w), smem + Cf::bX2, smem + Cf::bX3, w);
+      if (nck > 0) convert_raw_rows<D, TIO, GATE>(slot(0), smem + Cf::bX2, smem + Cf::bX3, w);
     for (int k = 0; k < nck; ++k) {
       const int buf = k & 1;
       const char* Bb = smem + buf * Cf::bufB;
@@ -823,105 +848,111 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
                     lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
       }
       chain_barrier();   // B1
-      // dU = P^T dO + Khat dS^T (rows 16w.., columns of this slice), then the terms
-      // of dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU that do not depend
-      // on dU, before the barrier
+      // raw mode: fq dO (high, low) of the next chunk first, so that its LDS round
+      // trip overlaps the fragment reads below
+      if constexpr (Cf::RAW)
+        convert_raw_rows<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
+      // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice
+      f32x4 ad = zero4(), ak = zero4();
+      if (!job.xfer) {   // transfer rows: dO = 0
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32) {
+          const bf16x8 pa = frag_kc_s<C>(Bb + Cf::bP, 16 * w, k0);
+          ad = mma(pa, frag_kc_s<16>(X1, 0, k0), ad);
+          if constexpr (Cf::LO) ad = mma(pa, frag_kc_s<16>(X2, 0, k0), ad);
+        }
+      }
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 32) ak = mma(frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0), frag_rk_s<D>(dSl, 0, k0), ak);
+      if constexpr (Cf::RAW) {
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C +
+                                                          16 * w + 4 * g);
+        ad += ak * f32x4{f.x, f.y, f.z, f.w};
+      } else {
+        ad += ak;
+      }
+      st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
+      // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU: the first two terms do
+      // not depend on dU and are issued before the barrier
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
       f32x4 an[NJW];
-      if constexpr (Cf::RAW) {
-        // every LDS read of the window first, in the order of use (waiting for each
-        // fragment right before its MFMA costs one LDS round trip after another):
-        // the next chunk's dO quarter, dS and k, P and dO, q and fq dO (high, low)
-        const RawRows nxt = raw_rows_in<D, TIO, GATE>(slot(k + 1), w);
-        bf16x8 dsf[D / 32], kf[D / 32], pf[2], x1f[2], x2f[2], x3f[2], qf[NJW][2];
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) {
-          dsf[i] = frag_rk_s<D>(dSl, 0, 32 * i);
-          kf[i] = frag_rk_s<D>(Bb + Cf::bK, 16 * w, 32 * i);
-        }
-        const float4 fk =
-            *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C + 16 * w + 4 * g);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          pf[kk] = frag_kc_s<C>(Bb + Cf::bP, 16 * w, 32 * kk);
-          x1f[kk] = frag_kc_s<16>(X1, 0, 32 * kk);
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          x2f[kk] = frag_kc_s<16>(X2, 0, 32 * kk);
-          x3f[kk] = frag_kc_s<16>(X3, 0, 32 * kk);
-#pragma unroll
-          for (int x = 0; x < NJW; ++x) qf[x][kk] = frag_kc_s<D>(Bb + Cf::bQh, 16 * (w * NJW + x), 32 * kk);
-        }
-        const f32x4 dv = decay4<D, GATE>(dec, 0, g);
-        __builtin_amdgcn_sched_barrier(0);
-        // fq dO (high, low) of the next chunk, published by the next barrier
-        raw_rows_out(nxt, smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
-        f32x4 ad = zero4(), ak = zero4();
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) ak = mma(kf[i], dsf[i], ak);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) ad = mma(pf[kk], x1f[kk], ad);
-        const float m = job.xfer ? 0.f : 1.f;   // transfer rows: dO = 0
-        ad = m * ad + ak * f32x4{fk.x, fk.y, fk.z, fk.w};
-        st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
-#pragma unroll
-        for (int x = 0; x < NJW; ++x) {
-          f32x4 a = zero4();
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            a = mma(qf[x][kk], x2f[kk], a);
-            a = mma(qf[x][kk], x3f[kk], a);
-          }
-          an[x] = acc[x] * dv + m * a;
-        }
-      } else {
-        // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice
-        f32x4 ad = zero4(), ak = zero4();
+      for (int x = 0; x < NJW; ++x) {
+        const int jb = w * NJW + x;
+        f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
         if (!job.xfer) {   // transfer rows: dO = 0
 #pragma unroll
           for (int k0 = 0; k0 < C; k0 += 32) {
-            const bf16x8 pa = frag_kc_s<C>(Bb + Cf::bP, 16 * w, k0);
-            ad = mma(pa, frag_kc_s<16>(X1, 0, k0), ad);
-            if constexpr (Cf::LO) ad = mma(pa, frag_kc_s<16>(X2, 0, k0), ad);
-          }
-        }
-#pragma unroll
-        for (int k0 = 0; k0 < D; k0 += 32) ak = mma(frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0), frag_rk_s<D>(dSl, 0, k0), ak);
-        ad += ak;
-        st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
-#pragma unroll
-        for (int x = 0; x < NJW; ++x) {
-          const int jb = w * NJW + x;
-          f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
-          if (!job.xfer) {   // transfer rows: dO = 0
-#pragma unroll
-            for (int k0 = 0; k0 < C; k0 += 32) {
-              const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, k0);
+            const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, k0);
+            if constexpr (Cf::RAW) {
+              a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
+              a = mma(qa, frag_kc_s<16>(X3, 0, k0), a);
+            } else {
               const bf16x8 bh = frag_kc_s<16>(X1, 0, k0);
               a = mma(qa, bh, a);
               a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, k0), bh, a);
               if constexpr (Cf::LO) a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
             }
           }
-          an[x] = a;
         }
+        an[x] = a;
       }
       chain_barrier();   // B2
-      bf16x8 wt[NJW][C / 32], duf[C / 32];
+      if constexpr (Cf::RAW) {
+        // W^T dU = k^T Y with Y = Diag(fw) A^T dU (W = A Diag(fw) k).  Every wave
+        // forms all 64 rows of Y (A is block lower triangular: row block rb takes
+        // dU rows from 16 rb on) and feeds its accumulators, rounded to bf16,
+        // straight back as the B operand of k^T Y, K-step kk pairing the row
+        // blocks 2kk and 2kk+1 (frag_kc_split_s reads k^T in that row order)
+        const bf16x8 du0 = frag_rk_s<C, 1>(dUt, 0, 0), du1 = frag_rk_s<C, 1>(dUt, 0, 32);
+        // fw of this lane's Y rows 16 rb + 4g .. +3 and the k^T fragments, read in
+        // the same round trip as dU
+        const float* fw = reinterpret_cast<const float*>(sl_k + Cf::sFac) + 2 * C;
+        f32x4 fwv[4];
 #pragma unroll
-      for (int kk = 0; kk < C / 32; ++kk) {
-        duf[kk] = frag_rk_s<C, 1>(dUt, 0, 32 * kk);
+        for (int rb = 0; rb < 4; ++rb) {
+          const float4 f = *reinterpret_cast<const float4*>(fw + 16 * rb + 4 * g);
+          fwv[rb] = f32x4{f.x, f.y, f.z, f.w};
+        }
+        bf16x8 kfr[NJW][2];
 #pragma unroll
-        for (int x = 0; x < NJW; ++x) wt[x][kk] = frag_kc_s<D>(Bb + Cf::bW, 16 * (w * NJW + x), 32 * kk);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+        for (int x = 0; x < NJW; ++x)
 #pragma unroll
-      for (int x = 0; x < NJW; ++x) {
-        f32x4 aw = zero4();
+          for (int kk = 0; kk < 2; ++kk) kfr[x][kk] = frag_kc_split_s<D>(Bb + Cf::bK, 16 * (w * NJW + x), 32 * kk);
+        f32x4 y[4];
 #pragma unroll
-        for (int kk = 0; kk < C / 32; ++kk) aw = mma(wt[x][kk], duf[kk], aw);
-        acc[x] = an[x] - aw;
+        for (int rb = 0; rb < 4; ++rb) {
+          y[rb] = zero4();
+          if (rb < 2) y[rb] = mma(frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 0), du0, y[rb]);
+          y[rb] = mma(frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 32), du1, y[rb]);
+          y[rb] *= fwv[rb];
+        }
+        bf16x8 yb[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            yb[kk][i] = to_bf16(y[2 * kk][i]);
+            yb[kk][4 + i] = to_bf16(y[2 * kk + 1][i]);
+          }
+#pragma unroll
+        for (int x = 0; x < NJW; ++x) {
+          const int jb = w * NJW + x;
+          f32x4 aw = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) aw = mma(kfr[x][kk], yb[kk], aw);
+          acc[x] = an[x] - aw;
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < NJW; ++x) {
+          const int jb = w * NJW + x;
+          f32x4 aw = zero4();
+#pragma unroll
+          for (int k0 = 0; k0 < C; k0 += 32)
+            aw = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C, 1>(dUt, 0, k0), aw);
+          acc[x] = an[x] - aw;
+        }
       }
     }
     job_fin<D>(job, acc, w, g, jj);
@@ -1035,7 +1066,7 @@ __global__ __launch_bounds__(kChainThreads) void k_chain(const Params p, int mod
   }
   if (gidx >= p.NS * p.H) return;
   const int si = gidx / p.H, h = gidx % p.H;
-  const SeqEntry se = p.stab[si];
+  const SeqEntry se = seq_entry(p, si);
   const bool first = role == 0 ? se.seg == 0 : se.seg == se.nseg - 1;   // the role's first segment
   const bool last = role == 0 ? se.seg == se.nseg - 1 : se.seg == 0;    // the role's last segment
   const int64_t sh = int64_t(se.seq) * p.H + h;                           // (sequence, head)
@@ -1084,7 +1115,7 @@ __global__ __launch_bounds__(256) void k_chain_fix(const Params p, int mode) {
   }
   const int sl = b % ns, gidx = b / ns;
   const int si = gidx / p.H, h = gidx % p.H;
-  const SeqEntry se = p.stab[si];
+  const SeqEntry se = seq_entry(p, si);
   if (se.seg != 0 || se.nseg < 2) return;
   const int tid = threadIdx.x, r = tid >> 4, c0 = (tid & 15) * CPT;
   auto xf = [&](int slot) { return p.xf + ((int64_t(role) * p.NS + slot) * p.H + h) * 2 * D * D; };

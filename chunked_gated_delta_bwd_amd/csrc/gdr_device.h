@@ -278,14 +278,15 @@ __device__ __forceinline__ int64_t qk_tok(const P& p, int t, int h) { return int
 // that XCD's L2 serves the rows after the first read.  A bijection of the grid:
 // the (chunk, key head) pairs past the last whole set of eight keep their members
 // consecutive.
+// chunk_head_at: the same for the workgroup with linear id L (x fastest).
 template <typename P>
-__device__ __forceinline__ void chunk_head(const P& p, int& c, int& h) {
+__device__ __forceinline__ void chunk_head_at(const P& p, int L, int& c, int& h) {
   if (p.G == 1) {
-    c = blockIdx.x;
-    h = blockIdx.y;
+    c = L % p.NC;
+    h = L / p.NC;
     return;
   }
-  const int G = p.G, L = blockIdx.x + p.NC * blockIdx.y;
+  const int G = p.G;
   const int npair = p.NC * p.Hk, p8 = npair / 8 * 8;
   int pair, gi;
   if (L < p8 * G) {
@@ -299,6 +300,16 @@ __device__ __forceinline__ void chunk_head(const P& p, int& c, int& h) {
   }
   c = pair / p.Hk;
   h = (pair % p.Hk) * G + gi;
+}
+
+template <typename P>
+__device__ __forceinline__ void chunk_head(const P& p, int& c, int& h) {
+  if (p.G == 1) {
+    c = blockIdx.x;
+    h = blockIdx.y;
+    return;
+  }
+  chunk_head_at(p, int(blockIdx.x + p.NC * blockIdx.y), c, h);
 }
 
 __device__ __forceinline__ void st_bf16x4(bf16* dst, float a, float b, float c, float d) {

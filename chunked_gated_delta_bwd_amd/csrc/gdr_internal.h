@@ -66,12 +66,13 @@ struct WsLayout {
   size_t ctab = 0, stab = 0;
   size_t gam = 0;    // fp32 [H][NC][64] or [H][NC][64][K]: in-chunk cumsum of the log decay
   size_t rho = 0;    // fp32 [H][NC][3][64]: 1/|q|, 1/|k|, beta per row (beta 0 past the end)
-  size_t fac = 0;    // fp32 [H][NC][2][64]: scalar gate row factors of the recursions,
-                     //   fq = scale e^Gam / |q|, fk = e^(GamC - Gam) / |k| (zero past the end)
+  size_t fac = 0;    // fp32 [H][NC][3][64]: scalar gate row factors of the recursions,
+                     //   fq = scale e^Gam / |q|, fk = e^(GamC - Gam) / |k|,
+                     //   fw = beta e^Gam / |k| (W = A Diag(fw) k; all zero past the end)
   size_t edec = 0;   // fp32 [H][NC][4] (value, 3 pad) or [H][NC][K]: chunk decay e^GamC
   size_t A = 0;      // bf16 [H][NC][64][64]: UT/WY inverse
   size_t P = 0;      // bf16 [H][NC][64][64]: scale * (Qn Kn^T o E), lower incl. diagonal
-  size_t W = 0;      // bf16 [H][NC][64][K]:  A diag(beta) Kbar
+  size_t W = 0;      // bf16 [H][NC][64][K]:  A diag(beta) Kbar (materialised tiles only)
   size_t Up = 0;     // bf16 [H][NC][64][V]:  U' = A diag(beta) V
   size_t U = 0;      // bf16 [H][NC][V][64]:  v_new = U' - W S^T (forward state pass), transposed
   size_t S = 0;      // bf16 [H][NC][V][K]:   state at chunk start

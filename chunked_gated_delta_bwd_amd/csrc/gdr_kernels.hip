@@ -159,8 +159,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   // inputs the Khat and Qbar (high + low) tiles ---
   if (tid < C) {
     const float m = tid < len ? 1.f : 0.f, gC = gam_s[C - 1], gr = gam_s[tid];
-    p.fac[ch * 2 * C + tid] = m * p.scale * rq_s[tid] * fast_exp(gr);
-    p.fac[ch * 2 * C + C + tid] = m * rk_s[tid] * fast_exp(gC - gr);
+    p.fac[ch * 3 * C + tid] = m * p.scale * rq_s[tid] * fast_exp(gr);
+    p.fac[ch * 3 * C + C + tid] = m * rk_s[tid] * fast_exp(gC - gr);
+    p.fac[ch * 3 * C + 2 * C + tid] = beta_s[tid] * rk_s[tid] * fast_exp(gr);   // W = A Diag(this) k
     if (tid == 0) p.edec[ch * 4] = fast_exp(gC);
   }
   if constexpr (kMat) {
@@ -221,7 +222,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
     *reinterpret_cast<u32x4*>(p.P + (ch * C + row) * C + c8) = *reinterpret_cast<const u32x4*>(As + row * PC + c8);
   }
 
-  // --- beta * Kbar (for W) and beta * V overwrite the operand tiles ---
+  // --- beta * Kbar (for W; fp32 inputs only, bf16 inputs leave W to the
+  // recursions as A Diag(fw) k) and beta * V overwrite the operand tiles ---
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
       kb[e] = to_bf16(kn_r[ps][e] * fk);
       vb[e] = to_bf16(v_r[ps][e] * fv);
     }
-    *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
+    if constexpr (kMat) *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
     *reinterpret_cast<bf16x8*>(Vs + r * PD + c0) = vb;
   }
 
@@ -291,8 +293,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   }
   __syncthreads();
 
-  // --- W and U' tiles: lane owns W[r][j .. j+3]; staged in the inverse's
-  // scratch (free by now) and stored as 16-byte row pieces ---
+  // --- W (fp32 inputs) and U' tiles: lane owns W[r][j .. j+3]; staged in the
+  // inverse's scratch (free by now) and stored as 16-byte row pieces ---
   static_assert(C * PD * 2 <= kQX && C * PD * 2 <= C * PL * 4, "staging tiles fit");
   bf16* const Wst = reinterpret_cast<bf16*>(QX);
   bf16* const Ust = reinterpret_cast<bf16*>(Lf);
@@ -305,11 +307,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
 #pragma unroll
       for (int k0 = 0; k0 < C; k0 += 32) {
         const bf16x8 b = frag_rk(As, PC, 16 * rb, k0);  // B[s][r] = A[r][s]
-        aW = mma(frag_kc(Ks, PD, 16 * jb, k0), b, aW);
+        if constexpr (kMat) aW = mma(frag_kc(Ks, PD, 16 * jb, k0), b, aW);
         aU = mma(frag_kc(Vs, PD, 16 * jb, k0), b, aU);
       }
       const int j0 = 16 * jb + 4 * (l >> 4);
-      st_bf16x4(Wst + r * PD + j0, aW[0], aW[1], aW[2], aW[3]);
+      if constexpr (kMat) st_bf16x4(Wst + r * PD + j0, aW[0], aW[1], aW[2], aW[3]);
       st_bf16x4(Ust + r * PD + j0, aU[0], aU[1], aU[2], aU[3]);
     }
   }
@@ -317,7 +319,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
 #pragma unroll
   for (int it = 0; it < C * D / 8 / kT; ++it) {
     const int idx = tid + kT * it, row = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-    *reinterpret_cast<u32x4*>(p.W + (ch * C + row) * D + c8) = *reinterpret_cast<const u32x4*>(Wst + row * PD + c8);
+    if constexpr (kMat)
+      *reinterpret_cast<u32x4*>(p.W + (ch * C + row) * D + c8) = *reinterpret_cast<const u32x4*>(Wst + row * PD + c8);
     *reinterpret_cast<u32x4*>(p.Up + (ch * C + row) * D + c8) = *reinterpret_cast<const u32x4*>(Ust + row * PD + c8);
   }
 }
@@ -355,6 +358,41 @@ struct GradLds {
 // half hf = w / 4 of every D-wide result; waves w and w + 4 share a SIMD.
 constexpr int kGradWaves = 8;
 constexpr int kGradThreads = 64 * kGradWaves;
+
+// how many workgroups ahead a gradient workgroup prefetches (one per CU run at once)
+constexpr int kGradAhead = 256;
+
+// L2 prefetch of the first tile group of the gradient workgroup with linear id L:
+// dU^T, A, U^T and (bf16 inputs) the dO and v rows; rows past the end clamped
+template <int D, typename TIO>
+__device__ __forceinline__ void grads_prefetch(const Params& p, int L, char* sink) {
+  constexpr bool kRows = !std::is_same<TIO, float>::value;
+  constexpr int SR = D * 2 / 64;                                  // sectors per token row
+  constexpr int NU = D * C * 2 / 64, NA = C * C * 2 / 64, NR = C * SR;
+  constexpr int NTOT = 2 * NU + NA + (kRows ? 2 * NR : 0);
+  int c, h;
+  chunk_head_at(p, L, c, h);
+  const ChunkEntry ce = p.ctab[c];
+  const int64_t ch = int64_t(h) * p.NC + c;
+  const char* dU = reinterpret_cast<const char*>(p.dU + ch * D * C);
+  const char* A = reinterpret_cast<const char*>(p.A + ch * C * C);
+  const char* U = reinterpret_cast<const char*>(p.U + ch * D * C);
+  for (int u = threadIdx.x; u < NTOT; u += blockDim.x) {
+    const char* a;
+    if (u < NU) {
+      a = dU + 64 * u;
+    } else if (u < NU + NA) {
+      a = A + 64 * (u - NU);
+    } else if (u < 2 * NU + NA) {
+      a = U + 64 * (u - NU - NA);
+    } else {
+      const int i = u - 2 * NU - NA, k = i % NR, row = min(k / SR, ce.len - 1);
+      const void* base = i < NR ? p.dO : p.v;
+      a = reinterpret_cast<const char*>(base) + tok(ce.t_start + row, p.H, h) * D * 2 + 64 * (k % SR);
+    }
+    dma4(a, sink);
+  }
+}
 
 // phase-3 tiles (rb, sb), sb <= rb: slot 0 of every wave, slot 1 of waves 0 and 1
 // (so that each SIMD gets two or three of the ten tiles)
@@ -533,6 +571,17 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
   }
   wait_vm<0>();
   chain_barrier();   // B_c: S and dS are no longer read; raw q, k in LDS
+
+  // The workgroup dealt kGradAhead places later runs on this XCD (workgroups go
+  // round-robin over the 8 XCDs) at about the time this one ends: pull its first
+  // tile group into this XCD's L2 now, so that its start does not wait for HBM
+  // (4-byte direct-to-LDS loads, one per 64-byte sector, into the A tile, which is
+  // not read again; waited for at the end).  bf16 inputs only: with fp32 inputs
+  // ordinary register loads follow, and their waits would take the prefetch along
+  if constexpr (kDma) {
+    if (const int L = blockIdx.x + p.NC * blockIdx.y + kGradAhead; L < p.NC * p.H)
+      grads_prefetch<D, TIO>(p, L, At);
+  }
 
   // ---- Kn, Qn (over S) ----
 #pragma unroll
@@ -794,6 +843,7 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
       }
     }
   }
+  wait_vm<0>();   // the prefetch's direct-to-LDS loads land before the workgroup's LDS is released
 }
 
 __global__ void k_zero(float* a, int n) {

@@ -68,6 +68,33 @@ __device__ __forceinline__ bf16x8 frag_kc_s(const char* T, int c0, int k0) {
   return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// T[m_e][c0 + j] with rows m_e = k0 + 4g + e (e < 4) and k0 + 16 + 4g + e - 4
+// (e >= 4): the K order of an MFMA operand is free as long as both operands
+// share it, and this one matches a B operand assembled from the accumulators
+// of two 16-row MFMA tiles (lane group g holds rows 4g .. 4g+3 of each)
+template <int W, int KIND = 0>
+__device__ __forceinline__ bf16x8 frag_kc_split_s(const char* T, int c0, int k0) {
+  const int l = lane_id();
+  const int g = l >> 4, q = l & 15;
+  const int r = k0 + 4 * g + (q >> 2), c = c0 + 4 * (q & 3);
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(T + soff<W, KIND>(r, c))));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(T + soff<W, KIND>(r + 16, c))));
+  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+  const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+  return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// T[r0 + j][m_e], m_e as in frag_kc_split_s: the row-fragment form of the same
+// K order (two 8-byte reads)
+template <int W, int KIND = 0>
+__device__ __forceinline__ bf16x8 frag_rk_split_s(const char* T, int r0, int k0) {
+  const int l = lane_id();
+  const int r = r0 + (l & 15), c = k0 + 4 * (l >> 4);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(T + soff<W, KIND>(r, c));
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(T + soff<W, KIND>(r, c + 16));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 template <int W, int KIND = 0>
 __device__ __forceinline__ void st4_s(char* T, int r, int c, float a, float b, float d, float e) {
   *reinterpret_cast<uint2*>(T + soff<W, KIND>(r, c)) = pack4_bf16(a, b, d, e);

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kOutThreads) void k_output(const Params p) {
     dma_tile<D, 0, C, kOutWaves>(Qs, [&](int r) {
       return reinterpret_cast<const char*>(p.q) + qk_tok(p, t0 + min(r, len - 1), h) * D * 2;
     }, w);
-    if (w == 0) dma4(p.fac + ch * 2 * C + l, reinterpret_cast<char*>(fq_s));   // fq: row factor 0
+    if (w == 0) dma4(p.fac + ch * 3 * C + l, reinterpret_cast<char*>(fq_s));   // fq: row factor 0
   } else {
     dma_tile<D, 0, C, kOutWaves>(Qs, [&](int r) { return u16(p.Qh + (ch * C + r) * D); }, w);
   }
