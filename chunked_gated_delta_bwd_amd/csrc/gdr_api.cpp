@@ -73,7 +73,7 @@ gdr_status check_shape(const gdr_shape* s, int64_t* NC_out) {
 // carried state, so a segment run from zero plus the transfer product of its
 // chunks gives its end state for any starting state).
 // ---------------------------------------------------------------------------
-constexpr int kCUs = 256;           // MI355X compute units; one recursion workgroup fits per CU
+constexpr int kCUs = gdr::kGpuCUs;
 constexpr int kMinSegChunks = 8;    // automatic splits keep at least this many chunks per segment
 
 int64_t seq_chunks(const gdr_shape* s, int n) {

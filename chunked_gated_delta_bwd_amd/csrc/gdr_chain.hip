@@ -63,30 +63,33 @@
 
 namespace gdr {
 
-constexpr int kChainWaves = 9;
-constexpr int kChainThreads = 64 * kChainWaves;
-constexpr int kConvWave = 4;
-constexpr int kMoveWave0 = 5;
 
 // ---------------------------------------------------------------------------
 // LDS plan
 // ---------------------------------------------------------------------------
-template <int D, typename TIO, int GATE>
+// NSL: V slices per workgroup (two share the chunk tiles: raw mode only, where
+// LDS allows; waves 0-3 compute for the first slice, 4-7 for the second)
+template <int D, typename TIO, int GATE, int NSL = 1>
 struct ChainCfg {
   static constexpr bool LO = std::is_same<TIO, float>::value;  // fp32 inputs: dO split in two parts
   static constexpr bool MAT = GATE == 1 || LO;                 // materialised Khat / Qbar tiles
   static constexpr bool RAW = !MAT;                            // raw q, k rows and row factors
   static constexpr bool SPLIT = GATE == 1;   // U', U, S, dS also carried as bf16 high + low parts
+  static_assert(NSL == 1 || (NSL == 2 && RAW), "two slices a workgroup in raw mode only");
+  static constexpr int NCW = 4 * NSL;                      // compute waves
+  static constexpr int CONV = NCW, MOVE0 = NCW + 1;        // converter, first of four movers
+  static constexpr int WAVES = NCW + 5, THREADS = 64 * WAVES;
+  static constexpr int NPF = NSL;                          // L2 prefetch loads per mover wave and step
   static constexpr int DG = GATE == 1 ? D : 16;    // decay floats per slot (scalar: one value, 64-byte slot part)
   static constexpr int TB = C * D * 2;             // one 64 x D bf16 tile
   static constexpr int PB = C * C * 2;             // the 64 x 64 P tile
   static constexpr int XB = C * 16 * 2;            // a 64 x 16 bf16 slice
   static constexpr int NJ = TB / 4096;             // 1 KB loads per mover wave per 64 x D tile
-  // small per-chunk data, three rotating slots: the raw dO slice (bf16 inputs),
-  // the row factors fq, fk, fw (raw mode) and the decay
+  // small per-chunk data, three rotating slots: the raw dO slices (bf16 inputs, one
+  // per V slice), the row factors fq, fk, fw (raw mode) and the decay
   static constexpr int NFAC = 3;
   static constexpr int sDO = 0;
-  static constexpr int sFac = sDO + (LO ? 0 : XB);
+  static constexpr int sFac = sDO + (LO ? 0 : NSL * XB);
   static constexpr int sDec = sFac + (RAW ? NFAC * C * 4 : 0);
   static constexpr int SLOT = sDec + DG * 4;
   // reverse role, byte offsets; the tile buffers first.  Materialised tiles:
@@ -96,28 +99,31 @@ struct ChainCfg {
   static constexpr int bP = MAT ? 4 * TB : 2 * TB;
   static constexpr int bA = 2 * TB + PB;                           // raw mode
   static constexpr int bufB = MAT ? 4 * TB + PB : 2 * TB + 2 * PB;
+  // per-slice parts: slice s, buffer b at X + (2 s + b) XB
   static constexpr int bX1 = 2 * bufB;                             // LO: dO high part
   static constexpr int bX2 = bX1 + (LO ? 2 * XB : 0);              // RAW: fq dO high; LO: dO low
-  static constexpr int bX3 = bX2 + ((RAW || LO) ? 2 * XB : 0);     // RAW: fq dO low
-  static constexpr int bSlot = bX3 + (RAW ? 2 * XB : 0);
-  static constexpr int bdS = bSlot + 3 * SLOT;                     // 16 x D state-gradient slice
-  static constexpr int bdU = bdS + 16 * D * 2;                     // 16 x 64: dU^T
+  static constexpr int bX3 = bX2 + ((RAW || LO) ? 2 * NSL * XB : 0);   // RAW: fq dO low
+  static constexpr int bSlot = bX3 + (RAW ? 2 * NSL * XB : 0);
+  static constexpr int bdS = bSlot + 3 * SLOT;                     // 16 x D state-gradient slice, each slice
+  static constexpr int bdU = bdS + NSL * 16 * D * 2;               // 16 x 64: dU^T, each slice
   static constexpr int dUB = 16 * C * 2;
   // dU^T in two buffers (step parity) where LDS allows: the converter then stores
   // it during the next step instead of holding up the first barrier
-  static constexpr int NDU = bdU + 2 * dUB + 256 <= 160 * 1024 ? 2 : 1;
-  static constexpr int bPF = bdU + NDU * dUB;                      // 256 B sink of the L2 prefetches
+  static constexpr int NDU = bdU + 2 * NSL * dUB + 256 <= 160 * 1024 ? 2 : 1;
+  static constexpr int bPF = bdU + NSL * NDU * dUB;                // 256 B sink of the L2 prefetches
   static constexpr int bEnd = bPF + 256;
   // forward role
   // forward role: materialised tiles W, Khat; raw mode A (in W's place) and k,
   // with W S^T formed as A (Diag(fw) k S^T)
-  static constexpr int fW = 0, fA = 0, fK = MAT ? TB : PB, fUp = fK + TB, fUpl = fUp + XB;
+  // (the U' slices of the NSL slices in one region: element (s, r, c) at
+  // ((r / 16) NSL + s) 512 + (r % 16) 32 + 2c bytes, one mover load covering 16 rows of all)
+  static constexpr int fW = 0, fA = 0, fK = MAT ? TB : PB, fUp = fK + TB, fUpl = fUp + NSL * XB;
   static constexpr int bufF = fUpl + (SPLIT ? XB : 0);
   static constexpr int fSlot = 2 * bufF;
-  static constexpr int fS = fSlot + 3 * SLOT;                      // 16 x D state slice
-  static constexpr int fU = fS + 16 * D * 2;                       // 16 x 64: U^T as the MFMA takes it
-  static constexpr int fUo = fU + 16 * C * 2;                      // RAW: unscaled U^T, to be stored
-  static constexpr int fUl = fUo + (RAW ? 16 * C * 2 : 0);         // SPLIT: low part of U^T
+  static constexpr int fS = fSlot + 3 * SLOT;                      // 16 x D state slice, each slice
+  static constexpr int fU = fS + NSL * 16 * D * 2;                 // 16 x 64: U^T as the MFMA takes it, each slice
+  static constexpr int fUo = fU + NSL * 16 * C * 2;                // RAW: unscaled U^T, to be stored, each slice
+  static constexpr int fUl = fUo + (RAW ? NSL * 16 * C * 2 : 0);   // SPLIT: low part of U^T
   static constexpr int fSl = fUl + (SPLIT ? 16 * C * 2 : 0);       // SPLIT: low part of the state slice
   static constexpr int fPF = fSl + (SPLIT ? 16 * D * 2 : 0);
   static constexpr int fEnd = fPF + 256;
@@ -133,7 +139,7 @@ struct ChainCfg {
   static constexpr int PFD = 5;
   static constexpr int fwdA = (MAT ? NJ : 2) + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
   static_assert(bytes <= 160 * 1024, "LDS budget");
-  static_assert(2 * bwdA + bwdB + PFD - 2 < 64 && 2 * fwdA + fwdB + PFD - 2 < 64, "vmcnt range");
+  static_assert(2 * bwdA + bwdB + (PFD - 2) * NPF < 64 && 2 * fwdA + fwdB + (PFD - 2) * NPF < 64, "vmcnt range");
 };
 
 // The segment entry of a workgroup, read once into scalar registers (left in
@@ -181,10 +187,11 @@ struct MoverLane {
   int rD[4], pD[4], tD[4];   // 64 x D tile, load j: row, swizzled piece byte offset, in-tile offset
   int rowoff[4];             // q / k token rows of a whole chunk, load j: byte offset from its first row
   int tP[2];                 // P tile, load j: in-tile offset
-  int up;                    // 64 x 16 slice of a 64 x D tile (lanes 0-31): row * 2D + piece * 16
+  int up;                    // the U' slices' part of a 64 x D tile: row * 2D + byte offset
   int drow, doff;            // dO halves (movers 0, 1): logical row; byte offset, whole chunk
   int rs, ds;                // byte strides of q / k rows and of dO rows (scalars)
   int hk;                    // the key head of value head h (scalar)
+  template <int NSL>
   __device__ __forceinline__ void init(const Params& p, int h, int mw, int l, int dsz) {
     constexpr int RB = 2 * D, TB = C * RB, NJ = TB / 4096;
     rs = __builtin_amdgcn_readfirstlane(p.Hk * D * 2);
@@ -210,8 +217,10 @@ struct MoverLane {
       tP[j] = row * 128 + (lp << 4);
       keep(tP[j]);
     }
-    const int pos = mw * 512 + 16 * (l & 31);
-    up = (pos >> 5) * RB + (((pos & 31) >> 4) << 4);
+    // U' slices: one slice, lanes 0-31, 16 rows x 32 bytes; two slices, lane l
+    // 16 rows x 64 bytes (slice l / 32 in the upper half of the lanes)
+    up = NSL == 1 ? (16 * mw + ((l & 31) >> 1)) * RB + ((l & 1) << 4)
+                  : (16 * mw + ((l & 31) >> 1)) * RB + (l >> 5) * 32 + ((l & 1) << 4);
     drow = prow<16>(32 * (mw & 1) + (l >> 1));   // logical row landing at physical row 32 mw + l/2
     doff = drow * ds + (l & 1) * 16;
     keep(up);
@@ -259,25 +268,29 @@ __device__ __forceinline__ void move_p(const MoverLane<D>& ml, const void* src, 
 // (rows 32 mw .. 32 mw + 31, two pieces a row), mover 2 the row factors and the
 // decay together (contiguous in the slot); forward role, mover 0 the latter.
 // small_loads() is the number of loads a mover issues here (0 or 1).
-template <int D, typename TIO, int GATE>
+template <int D, typename TIO, int GATE, int NSL>
 __device__ __forceinline__ bool small_loads(int mw, bool with_dO) {
-  using Cf = ChainCfg<D, TIO, GATE>;
+  using Cf = ChainCfg<D, TIO, GATE, NSL>;
   if constexpr (Cf::LO) return false;
-  return with_dO ? mw < 3 : mw == 0;
+  return with_dO ? mw < 2 * NSL + 1 : mw == 0;
 }
 
-template <int D, typename TIO, int GATE>
+// (two slices: movers 0, 1 the halves of the first dO slice, 2, 3 of the second,
+// mover 0 the row factors and decay as well)
+template <int D, typename TIO, int GATE, int NSL>
 __device__ __forceinline__ void move_small(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            int v0, char* slot, int mw, bool with_dO) {
-  using Cf = ChainCfg<D, TIO, GATE>;
+  using Cf = ChainCfg<D, TIO, GATE, NSL>;
   if constexpr (!Cf::LO) {
     const ChunkGeo cg = geo(p, se, h, c);
     const int l = lane_id();
-    if (with_dO && mw < 2) {
-      const char* s = reinterpret_cast<const char*>(p.dO) + ((int64_t(cg.t0) * p.H + h) * D + v0) * 2;
+    if (with_dO && mw < 2 * NSL) {
+      const int sv = mw >> 1;   // the slice
+      const char* s = reinterpret_cast<const char*>(p.dO) + ((int64_t(cg.t0) * p.H + h) * D + v0 + 16 * sv) * 2;
       const int o = cg.len == C ? ml.doff : min(ml.drow, cg.len - 1) * ml.ds + (l & 1) * 16;
-      dma16(s + uint32_t(o), slot + Cf::sDO + mw * 1024);
-    } else if (mw == (with_dO ? 2 : 0)) {
+      dma16(s + uint32_t(o), slot + Cf::sDO + sv * Cf::XB + (mw & 1) * 1024);
+    }
+    if (mw == (with_dO && NSL == 1 ? 2 : 0)) {
       if constexpr (Cf::RAW) {
         // fq, fk, fw (768 bytes, lanes 0-47), then the decay (lane 48) right behind them
         constexpr int NL = Cf::NFAC * C * 4 / 16;
@@ -330,16 +343,17 @@ __device__ __forceinline__ void move_bwd_b(const MoverLane<D>& ml, const Params&
 }
 
 // forward role: set A (W or, raw mode, A; the U' slice), set B (Khat or k)
-template <int D, typename TIO, int GATE>
+template <int D, typename TIO, int GATE, int NSL>
 __device__ __forceinline__ void move_fwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            int v0, char* buf, int mw) {
-  using Cf = ChainCfg<D, TIO, GATE>;
+  using Cf = ChainCfg<D, TIO, GATE, NSL>;
   const ChunkGeo cg = geo(p, se, h, c);
   if constexpr (Cf::MAT)
     move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::fW, mw);
   else
     move_p<D>(ml, p.A + cg.ch * C * C, buf + Cf::fA, mw);
-  if (lane_id() < 32) dma16(reinterpret_cast<const char*>(p.Up + cg.ch * C * D + v0) + ml.up, buf + Cf::fUp + mw * 512);
+  if (NSL == 2 || lane_id() < 32)
+    dma16(reinterpret_cast<const char*>(p.Up + cg.ch * C * D + v0) + ml.up, buf + Cf::fUp + mw * 512 * NSL);
   if constexpr (Cf::SPLIT) {
     if (lane_id() < 32)
       dma16(reinterpret_cast<const char*>(p.Uplo + cg.ch * C * D + v0) + ml.up, buf + Cf::fUpl + mw * 512);
@@ -562,12 +576,12 @@ struct LoRegs {
 // scalar gate, bf16 inputs: fq dO of the chunk's dO slice in bf16 high + low
 // parts (X2, X3), rows 16w .. 16w+15 by compute wave w (lane: row 16w + l/4,
 // columns 4(l%4) .. +3)
-template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void convert_raw_rows(const char* slot, char* x2, char* x3, int w) {
-  using Cf = ChainCfg<D, TIO, GATE>;
+template <int D, typename TIO, int GATE, int NSL>
+__device__ __forceinline__ void convert_raw_rows(const char* slot, int sv, char* x2, char* x3, int w) {
+  using Cf = ChainCfg<D, TIO, GATE, NSL>;
   const int l = lane_id();
   const int row = 16 * w + (l >> 2), o = prow<16>(row) * 32 + (l & 3) * 8;
-  const uint2 r = *reinterpret_cast<const uint2*>(slot + Cf::sDO + o);
+  const uint2 r = *reinterpret_cast<const uint2*>(slot + Cf::sDO + sv * Cf::XB + o);
   const float fq = reinterpret_cast<const float*>(slot + Cf::sFac)[row];
   const float a[4] = {bf16_bits_to_f32(r.x & 0xffffu), bf16_bits_to_f32(r.x >> 16), bf16_bits_to_f32(r.y & 0xffffu),
                       bf16_bits_to_f32(r.y >> 16)};
@@ -639,25 +653,50 @@ __device__ __forceinline__ void job_fin(const ChainJob& job, const f32x4 (&acc)[
 // ---------------------------------------------------------------------------
 // the two roles
 // ---------------------------------------------------------------------------
-template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, int h, int sl, const ChainJob& job) {
+// the job of slice sv (0 .. NSL - 1), chosen by selects (a dynamic index into
+// the array would put it in scratch memory)
+template <int NSL>
+__device__ __forceinline__ ChainJob job_of(const ChainJob (&jobs)[NSL], int sv) {
+  if constexpr (NSL == 1) {
+    return jobs[0];
+  } else {
+    const bool b = sv != 0;
+    ChainJob j;
+    j.init = b ? jobs[1].init : jobs[0].init;
+    j.fin = b ? jobs[1].fin : jobs[0].fin;
+    j.store = jobs[0].store;
+    j.xfer = jobs[0].xfer;
+    j.i0 = b ? jobs[1].i0 : jobs[0].i0;
+    j.v0l = b ? jobs[1].v0l : jobs[0].v0l;
+    return j;
+  }
+}
+
+template <int D, typename TIO, int GATE, int NSL>
+__device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, int h, int sl,
+                                          const ChainJob (&jobs)[NSL]) {
   using Dm = Dims<D>;
-  using Cf = ChainCfg<D, TIO, GATE>;
+  using Cf = ChainCfg<D, TIO, GATE, NSL>;
   constexpr int NJW = Dm::NJW;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id();
   const int g = l >> 4, jj = l & 15;
   const SeqEntry se = seq_entry(p, si);
-  const int v0 = 16 * sl, v0l = job.v0l;
+  const int v0 = 16 * sl, v0l = jobs[0].v0l;   // the first slice's (the others follow, 16 apart)
   const int nck = se.nchunks;
-  char* Ss = smem + Cf::fS;
-  char* Ut = smem + Cf::fU;
-  char* Uo = smem + (Cf::RAW ? Cf::fUo : Cf::fU);
+  // slice sv's state, U^T and unscaled U^T tiles
+  auto Ss_of = [&](int sv) { return smem + Cf::fS + sv * (16 * D * 2); };
+  auto Ut_of = [&](int sv) { return smem + Cf::fU + sv * (16 * C * 2); };
+  auto Uo_of = [&](int sv) { return smem + (Cf::RAW ? Cf::fUo : Cf::fU) + sv * (16 * C * 2); };
   auto chunk = [&](int k) { return se.c0 + min(k, nck - 1); };
   auto slot = [&](int k) { return smem + Cf::fSlot + (k % 3) * Cf::SLOT; };
 
-  if (wv < 4) {
-    const int w = wv;
+  if (wv < Cf::NCW) {
+    const int sv = wv >> 2, w = wv & 3;
+    const ChainJob job = job_of<NSL>(jobs, sv);
+    char* Ss = Ss_of(sv);
+    char* Ut = Ut_of(sv);
+    char* Uo = Uo_of(sv);
     f32x4 acc[NJW];
     job_init<D>(job, acc, w, g, jj);
     if (nck > 0) chain_barrier();   // B0
@@ -711,7 +750,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       // transfer rows: U' = 0
       const float um = job.xfer ? 0.f : 1.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = um * bf16_bits_to_f32(Up[(16 * w + 4 * g + i) * 16 + jj]) - au[i];
+      for (int i = 0; i < 4; ++i) u[i] = um * bf16_bits_to_f32(Up[(w * NSL + sv) * 256 + (4 * g + i) * 16 + jj]) - au[i];
       if constexpr (Cf::SPLIT) {
         const uint16_t* Upl = reinterpret_cast<const uint16_t*>(Fb + Cf::fUpl);
 #pragma unroll
@@ -741,7 +780,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       }
     }
     job_fin<D>(job, acc, w, g, jj);
-  } else if (wv == kConvWave) {
+  } else if (wv == Cf::CONV) {
     if (nck == 0) return;
     LoRegs<D, TIO, GATE> R;
     if constexpr (Cf::LO) {
@@ -749,17 +788,20 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       R.store_dec(reinterpret_cast<float*>(slot(0) + Cf::sDec));
       R.load(p, se, h, chunk(1), v0l, false);
     }
+    const bool store = jobs[0].store;
     chain_barrier();   // B0
     for (int k = 0; k < nck; ++k) {
       const int64_t ch = int64_t(h) * p.NC + chunk(k);
       chain_barrier();   // B1
-      if (job.store) {
-        store_slice<D>(Ss, p.S + (ch * D + v0) * D);
+      if (store) {
+#pragma unroll
+        for (int sv = 0; sv < NSL; ++sv) store_slice<D>(Ss_of(sv), p.S + (ch * D + v0 + 16 * sv) * D);
         if constexpr (Cf::SPLIT) store_slice<D>(smem + Cf::fSl, p.Slo + (ch * D + v0) * D);
       }
       chain_barrier();   // B2
-      if (job.store) {
-        store_slice<C, 1>(Uo, p.U + (ch * D + v0) * C);
+      if (store) {
+#pragma unroll
+        for (int sv = 0; sv < NSL; ++sv) store_slice<C, 1>(Uo_of(sv), p.U + (ch * D + v0 + 16 * sv) * C);
         if constexpr (Cf::SPLIT) store_slice<C, 1>(smem + Cf::fUl, p.Ulo + (ch * D + v0) * C);
       }
       if constexpr (Cf::LO) {
@@ -770,59 +812,74 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     wait_vm<0>();
   } else {
     if (nck == 0) return;
-    const int mw = wv - kMoveWave0;
-    const bool hs = small_loads<D, TIO, GATE>(mw, false);
+    constexpr int NPF = Cf::NPF;
+    const int mw = wv - Cf::MOVE0;
+    const bool hs = small_loads<D, TIO, GATE, NSL>(mw, false);
     MoverLane<D> ml;
-    ml.init(p, h, mw, l, int(sizeof(TIO)));
-    PfLane<D, TIO, GATE, false> pf;
-    pf.init(p, v0l / 16, mw, l);   // the rows of the state slice whose U' / dO this workgroup loads
-    move_small<D, TIO, GATE>(ml, p, se, h, chunk(0), v0l, slot(0), mw, false);
-    move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), v0l, smem, mw);
+    ml.template init<NSL>(p, h, mw, l, int(sizeof(TIO)));
+    // the rows of the state slices whose U' this workgroup loads, one prefetch a slice
+    PfLane<D, TIO, GATE, false> pf[NSL];
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) pf[i].init(p, v0l / 16 + i, mw, l);
+    auto prefetch = [&](int c) {
+#pragma unroll
+      for (int i = 0; i < NSL; ++i) prefetch_chunk<D, TIO, GATE, false>(pf[i], ml, p, se, h, c, smem + Cf::fPF);
+    };
+    move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(0), v0l, slot(0), mw, false);
+    move_fwd_a<D, TIO, GATE, NSL>(ml, p, se, h, chunk(0), v0l, smem, mw);
     move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
-    move_small<D, TIO, GATE>(ml, p, se, h, chunk(1), v0l, slot(1), mw, false);
-    move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), v0l, smem + Cf::bufF, mw);
-    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, false>(pf, ml, p, se, h, chunk(c), smem + Cf::fPF);
-    wait_mover<Cf::fwdA + Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
+    move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(1), v0l, slot(1), mw, false);
+    move_fwd_a<D, TIO, GATE, NSL>(ml, p, se, h, chunk(1), v0l, smem + Cf::bufF, mw);
+    for (int c = 2; c < Cf::PFD; ++c) prefetch(chunk(c));
+    wait_mover<Cf::fwdA + Cf::fwdB + Cf::fwdA + (Cf::PFD - 2) * NPF>(hs);
     chain_barrier();   // B0
     // raw mode reads set B (k) in the first window too: both sets of chunk 0 land
     // before B1; otherwise set B may land by B2
-    if constexpr (Cf::RAW) wait_mover<Cf::fwdA + Cf::PFD - 1>(hs);
-    else wait_mover<Cf::fwdB + Cf::fwdA + Cf::PFD - 2>(hs);
+    if constexpr (Cf::RAW) wait_mover<Cf::fwdA + 1 + (Cf::PFD - 2) * NPF>(hs);
+    else wait_mover<Cf::fwdB + Cf::fwdA + (Cf::PFD - 2) * NPF>(hs);
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
-      move_small<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, false);
-      wait_mover<Cf::fwdA + 1 + Cf::fwdB>(hs);
+      move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, false);
+      wait_mover<Cf::fwdA + NPF + Cf::fwdB>(hs);
       chain_barrier();   // B2
-      move_fwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0l, smem + (k & 1) * Cf::bufF, mw);
-      prefetch_chunk<D, TIO, GATE, false>(pf, ml, p, se, h, chunk(k + Cf::PFD), smem + Cf::fPF);
-      if constexpr (Cf::RAW) wait_mover<Cf::fwdA + 2>(hs);   // set B of chunk k + 1 before the next B1
-      else wait_mover<Cf::fwdB + Cf::fwdA + 2>(hs);
+      move_fwd_a<D, TIO, GATE, NSL>(ml, p, se, h, chunk(k + 2), v0l, smem + (k & 1) * Cf::bufF, mw);
+      prefetch(chunk(k + Cf::PFD));
+      if constexpr (Cf::RAW) wait_mover<Cf::fwdA + NPF + 1>(hs);   // set B of chunk k + 1 before the next B1
+      else wait_mover<Cf::fwdB + Cf::fwdA + 2 * NPF>(hs);
     }
     wait_vm<0>();
   }
 }
 
-template <int D, typename TIO, int GATE>
-__device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, int h, int sl, const ChainJob& job) {
+template <int D, typename TIO, int GATE, int NSL>
+__device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, int h, int sl,
+                                          const ChainJob (&jobs)[NSL]) {
   using Dm = Dims<D>;
-  using Cf = ChainCfg<D, TIO, GATE>;
+  using Cf = ChainCfg<D, TIO, GATE, NSL>;
   constexpr int NJW = Dm::NJW;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id();
   const int g = l >> 4, jj = l & 15;
   const SeqEntry se = seq_entry(p, si);
-  const int v0 = 16 * sl, v0l = job.v0l;
+  const int v0 = 16 * sl, v0l = jobs[0].v0l;   // the first slice's (the others follow, 16 apart)
   const int nck = se.nchunks;
-  char* dSl = smem + Cf::bdS;
-  // dU^T of step k (buffer k & 1 when there are two)
-  auto dUbuf = [&](int k) { return smem + Cf::bdU + (Cf::NDU == 2 ? (k & 1) : 0) * Cf::dUB; };
+  auto dS_of = [&](int sv) { return smem + Cf::bdS + sv * (16 * D * 2); };
+  // slice sv's dU^T of step k (buffer k & 1 when there are two)
+  auto dUbuf = [&](int sv, int k) {
+    return smem + Cf::bdU + (sv * Cf::NDU + (Cf::NDU == 2 ? (k & 1) : 0)) * Cf::dUB;
+  };
   // step k walks chunk c0 + nck - 1 - k (last to first), clamped past the end
   auto chunk = [&](int k) { return se.c0 + nck - 1 - min(k, nck - 1); };
   auto slot = [&](int k) { return smem + Cf::bSlot + (k % 3) * Cf::SLOT; };
 
-  if (wv < 4) {
-    const int w = wv;
+  if (wv < Cf::NCW) {
+    const int sv = wv >> 2, w = wv & 3;
+    const ChainJob job = job_of<NSL>(jobs, sv);
+    char* dSl = dS_of(sv);
+    // slice sv's fq dO high / low parts, buffer b
+    auto X2_of = [&](int b) { return smem + Cf::bX2 + (2 * sv + b) * Cf::XB; };
+    auto X3_of = [&](int b) { return smem + Cf::bX3 + (2 * sv + b) * Cf::XB; };
     f32x4 acc[NJW];
     job_init<D>(job, acc, w, g, jj);
     if (nck > 0) chain_barrier();   // B0
@@ -830,28 +887,28 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     // one step ahead, a quarter each (chunk 0 here, chunk k + 1 in the first
     // window of step k; published by the next barrier)
     if constexpr (Cf::RAW)
-      if (nck > 0) convert_raw_rows<D, TIO, GATE>(slot(0), smem + Cf::bX2, smem + Cf::bX3, w);
+      if (nck > 0) convert_raw_rows<D, TIO, GATE, NSL>(slot(0), sv, X2_of(0), X3_of(0), w);
     for (int k = 0; k < nck; ++k) {
       const int buf = k & 1;
       const char* Bb = smem + buf * Cf::bufB;
       const char* sl_k = slot(k);
-      const char* X1 = Cf::LO ? smem + Cf::bX1 + buf * Cf::XB : sl_k + Cf::sDO;
-      const char* X2 = smem + Cf::bX2 + buf * Cf::XB;
-      const char* X3 = smem + Cf::bX3 + buf * Cf::XB;
-      char* dUt = dUbuf(k);
+      const char* X1 = Cf::LO ? smem + Cf::bX1 + buf * Cf::XB : sl_k + Cf::sDO + sv * Cf::XB;
+      const char* X2 = X2_of(buf);
+      const char* X3 = X3_of(buf);
+      char* dUt = dUbuf(sv, k);
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
         st4_s<D>(dSl, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
         if (Cf::SPLIT && job.store)   // no LDS left for a low tile: stored directly
-          st_bf16x4(p.dSlo + (int64_t(h) * p.NC + chunk(k)) * D * D + (v0 + jj) * D + j, lo_part(acc[x][0]),
+          st_bf16x4(p.dSlo + (int64_t(h) * p.NC + chunk(k)) * D * D + (v0 + 16 * sv + jj) * D + j, lo_part(acc[x][0]),
                     lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
       }
       chain_barrier();   // B1
       // raw mode: fq dO (high, low) of the next chunk first, so that its LDS round
       // trip overlaps the fragment reads below
       if constexpr (Cf::RAW)
-        convert_raw_rows<D, TIO, GATE>(slot(k + 1), smem + Cf::bX2 + (buf ^ 1) * Cf::XB, smem + Cf::bX3 + (buf ^ 1) * Cf::XB, w);
+        convert_raw_rows<D, TIO, GATE, NSL>(slot(k + 1), sv, X2_of(buf ^ 1), X3_of(buf ^ 1), w);
       // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice
       f32x4 ad = zero4(), ak = zero4();
       if (!job.xfer) {   // transfer rows: dO = 0
@@ -956,9 +1013,10 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       }
     }
     job_fin<D>(job, acc, w, g, jj);
-  } else if (wv == kConvWave) {
+  } else if (wv == Cf::CONV) {
     if (nck == 0) return;
     LoRegs<D, TIO, GATE> R;
+    const bool store = jobs[0].store;
     if constexpr (Cf::LO) {
       R.load(p, se, h, chunk(0), v0l, true);
       R.store_dO(smem + Cf::bX1, smem + Cf::bX2);
@@ -970,54 +1028,70 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       const int64_t ch = int64_t(h) * p.NC + chunk(k);
       const int nb = (k + 1) & 1;
       chain_barrier();   // B1
-      if (job.store) {
-        store_slice<D>(dSl, p.dS + (ch * D + v0) * D);
-        // two dU buffers: dU of the previous step (its buffer is not written again
-        // before the next B2); one buffer: this step's, after B2
-        if (Cf::NDU == 2 && k > 0)
-          store_slice<C, 1>(dUbuf(k - 1), p.dU + ((int64_t(h) * p.NC + chunk(k - 1)) * D + v0) * C);
+      if (store) {
+#pragma unroll
+        for (int sv = 0; sv < NSL; ++sv) {
+          store_slice<D>(dS_of(sv), p.dS + (ch * D + v0 + 16 * sv) * D);
+          // two dU buffers: dU of the previous step (its buffer is not written again
+          // before the next B2); one buffer: this step's, after B2
+          if (Cf::NDU == 2 && k > 0)
+            store_slice<C, 1>(dUbuf(sv, k - 1), p.dU + ((int64_t(h) * p.NC + chunk(k - 1)) * D + v0 + 16 * sv) * C);
+        }
       }
       chain_barrier();   // B2
-      if (Cf::NDU == 1 && job.store) store_slice<C, 1>(dUbuf(k), p.dU + (ch * D + v0) * C);
+      if (Cf::NDU == 1 && store) {
+#pragma unroll
+        for (int sv = 0; sv < NSL; ++sv) store_slice<C, 1>(dUbuf(sv, k), p.dU + (ch * D + v0 + 16 * sv) * C);
+      }
       if constexpr (Cf::LO) {
         R.store_dO(smem + Cf::bX1 + nb * Cf::XB, smem + Cf::bX2 + nb * Cf::XB);
         R.store_dec(reinterpret_cast<float*>(slot(k + 1) + Cf::sDec));
         R.load(p, se, h, chunk(k + 2), v0l, true);
       }
     }
-    if (Cf::NDU == 2 && job.store)
-      store_slice<C, 1>(dUbuf(nck - 1), p.dU + ((int64_t(h) * p.NC + chunk(nck - 1)) * D + v0) * C);
+    if (Cf::NDU == 2 && store) {
+#pragma unroll
+      for (int sv = 0; sv < NSL; ++sv)
+        store_slice<C, 1>(dUbuf(sv, nck - 1), p.dU + ((int64_t(h) * p.NC + chunk(nck - 1)) * D + v0 + 16 * sv) * C);
+    }
     wait_vm<0>();
   } else {
     if (nck == 0) return;
-    const int mw = wv - kMoveWave0;
-    const bool hs = small_loads<D, TIO, GATE>(mw, true);
+    constexpr int NPF = Cf::NPF;
+    const int mw = wv - Cf::MOVE0;
+    const bool hs = small_loads<D, TIO, GATE, NSL>(mw, true);
     MoverLane<D> ml;
-    ml.init(p, h, mw, l, int(sizeof(TIO)));
-    PfLane<D, TIO, GATE, true> pf;
-    pf.init(p, v0l / 16, mw, l);   // the rows of the state slice whose U' / dO this workgroup loads
-    move_small<D, TIO, GATE>(ml, p, se, h, chunk(0), v0l, slot(0), mw, true);
+    ml.template init<NSL>(p, h, mw, l, int(sizeof(TIO)));
+    // the rows of the state slices whose dO this workgroup loads, one prefetch a slice
+    PfLane<D, TIO, GATE, true> pf[NSL];
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) pf[i].init(p, v0l / 16 + i, mw, l);
+    auto prefetch = [&](int c) {
+#pragma unroll
+      for (int i = 0; i < NSL; ++i) prefetch_chunk<D, TIO, GATE, true>(pf[i], ml, p, se, h, c, smem + Cf::bPF);
+    };
+    move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(0), v0l, slot(0), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
     move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
-    move_small<D, TIO, GATE>(ml, p, se, h, chunk(1), v0l, slot(1), mw, true);
+    move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(1), v0l, slot(1), mw, true);
     move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), smem + Cf::bufB, mw);
-    for (int c = 2; c < Cf::PFD; ++c) prefetch_chunk<D, TIO, GATE, true>(pf, ml, p, se, h, chunk(c), smem + Cf::bPF);
-    wait_mover<Cf::bwdA + Cf::bwdB + Cf::bwdA + Cf::PFD - 2>(hs);
+    for (int c = 2; c < Cf::PFD; ++c) prefetch(chunk(c));
+    wait_mover<Cf::bwdA + Cf::bwdB + Cf::bwdA + (Cf::PFD - 2) * NPF>(hs);
     chain_barrier();   // B0
     // both sets of chunk 0 and the small data of chunk 1 land before B1 (set B is
     // read in the first window too, and so is the next chunk's small data)
-    wait_vm<Cf::bwdA + Cf::PFD - 2>();
+    wait_vm<Cf::bwdA + (Cf::PFD - 2) * NPF>();
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
       move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
-      move_small<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, true);
-      wait_mover<Cf::bwdA + 1 + Cf::bwdB>(hs);
+      move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, true);
+      wait_mover<Cf::bwdA + NPF + Cf::bwdB>(hs);
       chain_barrier();   // B2
       move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
-      prefetch_chunk<D, TIO, GATE, true>(pf, ml, p, se, h, chunk(k + Cf::PFD), smem + Cf::bPF);
+      prefetch(chunk(k + Cf::PFD));
       // set B of chunk k + 1 and the small data of chunk k + 2 land before the
       // next B1: only set A of chunk k + 2 and the prefetch stay in flight
-      wait_vm<Cf::bwdA + 1>();
+      wait_vm<Cf::bwdA + NPF>();
     }
     wait_vm<0>();
   }
@@ -1027,10 +1101,11 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
 // share its chunk tiles, so they are placed on the same XCD (workgroups are
 // dealt round-robin over the 8 XCDs).  The final pass has D / 16 slices per
 // (segment, head), the state rows; the local pass twice that many, the state
-// rows and then the transfer-product rows.
-template <int D, typename TIO, int GATE>
-__global__ __launch_bounds__(kChainThreads) void k_chain(const Params p, int mode, int nb_role, int pass) {
-  __shared__ __attribute__((aligned(1024))) char smem[ChainCfg<D, TIO, GATE>::bytes];
+// rows and then the transfer-product rows; a workgroup takes NSL consecutive slices.
+template <int D, typename TIO, int GATE, int NSL>
+__global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chain(const Params p, int mode, int nb_role,
+                                                                                  int pass) {
+  __shared__ __attribute__((aligned(1024))) char smem[ChainCfg<D, TIO, GATE, NSL>::bytes];
   int b = blockIdx.x;
   int role;
   if (mode == kChainBoth) {
@@ -1041,8 +1116,9 @@ __global__ __launch_bounds__(kChainThreads) void k_chain(const Params p, int mod
   }
   constexpr int ns = D / 16;
   const int nsl = pass == kPassLocal ? 2 * ns : ns;
+  const int nsg = nsl / NSL;   // slice groups per (segment, head)
   const int xcd = b % 8, y = b / 8;
-  const int sl = y % nsl, t = y / nsl;
+  const int sl = (y % nsg) * NSL, t = y / nsg;   // sl: the group's first slice
   // (segment, head) of slot t on this XCD.  With grouped heads the G value heads
   // of a key head read the same q, k rows, so they take consecutive slots of one
   // XCD (its L2 then serves the rows they share); the (segment, key head) pairs
@@ -1073,26 +1149,34 @@ __global__ __launch_bounds__(kChainThreads) void k_chain(const Params p, int mod
   const int64_t gh = (int64_t(role) * p.NS + se.slot) * p.H + h;           // (role, segment slot, head)
   const float* start = role == 0 ? p.h0 : p.dht;
   float* end = role == 0 ? p.ht : p.dh0;
-  ChainJob job;
-  job.xfer = sl >= ns;
-  job.i0 = 16 * (sl - ns);
-  job.v0l = 16 * (sl % ns);
-  if (pass == kPassLocal) {
-    // only segments that a later one (in the role's order) starts from, and the
-    // transfer product only where the segment does not start from h0 / dht
-    if (last || (job.xfer && first)) return;
-    job.init = first && !job.xfer && start ? start + (sh * D + 16 * sl) * D : nullptr;
-    job.fin = p.xf + (gh * 2 * D + 16 * sl) * D;
-    job.store = false;
-  } else {
-    job.init = first ? (start ? start + (sh * D + 16 * sl) * D : nullptr) : p.sb + (gh * D + 16 * sl) * D;
-    job.fin = last && end ? end + (sh * D + 16 * sl) * D : nullptr;
-    job.store = true;
+  // the slices of a group lie on one side of ns (ns is even): all state rows or
+  // all transfer rows
+  const bool xfer = sl >= ns;
+  // only segments that a later one (in the role's order) starts from, and the
+  // transfer product only where the segment does not start from h0 / dht
+  if (pass == kPassLocal && (last || (xfer && first))) return;
+  ChainJob jobs[NSL];
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) {
+    const int sx = sl + i;
+    ChainJob& job = jobs[i];
+    job.xfer = xfer;
+    job.i0 = 16 * (sx - ns);
+    job.v0l = 16 * (sx % ns);
+    if (pass == kPassLocal) {
+      job.init = first && !xfer && start ? start + (sh * D + 16 * sx) * D : nullptr;
+      job.fin = p.xf + (gh * 2 * D + 16 * sx) * D;
+      job.store = false;
+    } else {
+      job.init = first ? (start ? start + (sh * D + 16 * sx) * D : nullptr) : p.sb + (gh * D + 16 * sx) * D;
+      job.fin = last && end ? end + (sh * D + 16 * sx) * D : nullptr;
+      job.store = true;
+    }
   }
   if (role == 0)
-    chain_fwd<D, TIO, GATE>(p, smem, si, h, sl, job);
+    chain_fwd<D, TIO, GATE, NSL>(p, smem, si, h, sl, jobs);
   else
-    chain_bwd<D, TIO, GATE>(p, smem, si, h, sl, job);
+    chain_bwd<D, TIO, GATE, NSL>(p, smem, si, h, sl, jobs);
 }
 
 // The boundary states of split sequences, in order: one workgroup per (first
@@ -1165,14 +1249,32 @@ __global__ __launch_bounds__(256) void k_chain_fix(const Params p, int mode) {
 }
 
 namespace {
+template <int D, typename TIO, int GATE, int NSL>
+void launch_nsl(const Params& p, int mode, int pass, hipStream_t s) {
+  constexpr int ns = D / 16;
+  const int nsl = pass == kPassLocal ? 2 * ns : ns;
+  const int groups = p.NS * p.H;
+  const int nb = ((groups + 7) / 8) * 8 * (nsl / NSL);
+  const int nroles = mode == kChainBoth ? 2 : 1;
+  k_chain<D, TIO, GATE, NSL><<<dim3(nb * nroles), ChainCfg<D, TIO, GATE, NSL>::THREADS, 0, s>>>(p, mode, nb, pass);
+}
+
+// One slice a workgroup while every workgroup gets a CU of its own (one fits per
+// CU); beyond that, in raw mode, two slices a workgroup: they share the chunk
+// tiles (one set of loads for two slices), so the grid stays in one round
+// instead of two.
 template <int D, typename TIO, int GATE>
 void run_chain(const Params& p, int mode, int pass, hipStream_t s) {
   constexpr int ns = D / 16;
   const int nsl = pass == kPassLocal ? 2 * ns : ns;
-  const int groups = p.NS * p.H;
-  const int nb = ((groups + 7) / 8) * 8 * nsl;
-  const int nroles = mode == kChainBoth ? 2 : 1;
-  k_chain<D, TIO, GATE><<<dim3(nb * nroles), kChainThreads, 0, s>>>(p, mode, nb, pass);
+  const int64_t nb1 = int64_t((p.NS * p.H + 7) / 8) * 8 * nsl * (mode == kChainBoth ? 2 : 1);
+  if constexpr (ChainCfg<D, TIO, GATE>::RAW) {
+    if (nb1 > kGpuCUs) {
+      launch_nsl<D, TIO, GATE, 2>(p, mode, pass, s);
+      return;
+    }
+  }
+  launch_nsl<D, TIO, GATE, 1>(p, mode, pass, s);
 }
 }  // namespace
 

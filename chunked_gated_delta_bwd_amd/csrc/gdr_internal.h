@@ -25,6 +25,9 @@ struct ChunkEntry {
 // run of whole chunks of one sequence (a sequence that is not split is one
 // segment).  The recursion kernel's table is ordered longest first so that the
 // longest chains start first.
+// MI355X compute units; one recursion workgroup fits per CU
+constexpr int kGpuCUs = 256;
+
 struct SeqEntry {
   int32_t seq;       // sequence index (addresses h0/dht/dh0/ht)
   int32_t len;       // tokens
