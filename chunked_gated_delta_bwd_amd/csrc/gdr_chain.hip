@@ -105,12 +105,17 @@ struct ChainCfg {
   static constexpr int bX3 = bX2 + ((RAW || LO) ? 2 * NSL * XB : 0);   // RAW: fq dO low
   static constexpr int bSlot = bX3 + (RAW ? 2 * NSL * XB : 0);
   static constexpr int bdS = bSlot + 3 * SLOT;                     // 16 x D state-gradient slice, each slice
-  static constexpr int bdU = bdS + NSL * 16 * D * 2;               // 16 x 64: dU^T, each slice
+  // raw mode: low parts of the dS slices and of the dU^T buffers for the steps of
+  // weakly decaying chunks (two-part operands), each a fixed distance above its
+  // high part (one lane address serves both)
+  static constexpr int bdSl = bdS + NSL * 16 * D * 2;
   static constexpr int dUB = 16 * C * 2;
+  static constexpr int bdU = bdSl + (RAW ? NSL * 16 * D * 2 : 0);  // 16 x 64: dU^T, each slice
   // dU^T in two buffers (step parity) where LDS allows: the converter then stores
   // it during the next step instead of holding up the first barrier
-  static constexpr int NDU = bdU + 2 * NSL * dUB + 256 <= 160 * 1024 ? 2 : 1;
-  static constexpr int bPF = bdU + NSL * NDU * dUB;                // 256 B sink of the L2 prefetches
+  static constexpr int NDU = bdU + (RAW ? 4 : 2) * NSL * dUB + 256 <= 160 * 1024 ? 2 : 1;
+  static constexpr int bdUl = bdU + NSL * NDU * dUB;
+  static constexpr int bPF = bdUl + (RAW ? NSL * NDU * dUB : 0);   // 256 B sink of the L2 prefetches
   static constexpr int bEnd = bPF + 256;
   // forward role
   // forward role: materialised tiles W, Khat; raw mode A (in W's place) and k,
@@ -852,7 +857,18 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
   }
 }
 
-template <int D, typename TIO, int GATE, int NSL>
+// Raw mode: reverse steps of chunks whose decay e^GamC is at least this take the
+// operands dS (in Khat dS^T), dU (in A^T dU) and Y (in k^T Y) in two bf16 parts.
+// A step's rounding error is proportional to e^GamC (Khat^T W is), and the next
+// steps damp it by their own decay; with little decay it accumulates over the
+// whole sequence (float64 model of the state-gradient recursion with each
+// rounding switched on alone: at e^GamC = 1 each of the three gives 8e-4 relative
+// error in dh0 over four chunks, 1.5e-3 together; at 1/16 all of them 5e-4).
+constexpr float kTwoPartDecay = 1.f / 16;
+
+// TWO: the kernel that runs the segments with weakly decaying chunks (their steps
+// take two-part operands; the other steps the common ones)
+template <int D, typename TIO, int GATE, int NSL, bool TWO>
 __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, int h, int sl,
                                           const ChainJob (&jobs)[NSL]) {
   using Dm = Dims<D>;
@@ -877,6 +893,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     const int sv = wv >> 2, w = wv & 3;
     const ChainJob job = job_of<NSL>(jobs, sv);
     char* dSl = dS_of(sv);
+    char* dSlo = dSl + (Cf::bdSl - Cf::bdS);
     // slice sv's fq dO high / low parts, buffer b
     auto X2_of = [&](int b) { return smem + Cf::bX2 + (2 * sv + b) * Cf::XB; };
     auto X3_of = [&](int b) { return smem + Cf::bX3 + (2 * sv + b) * Cf::XB; };
@@ -896,10 +913,15 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       const char* X2 = X2_of(buf);
       const char* X3 = X3_of(buf);
       char* dUt = dUbuf(sv, k);
+      char* dUlo = dUt + (Cf::bdUl - Cf::bdU);
+      // a weakly decaying chunk: two-part operands (uniform over the workgroup)
+      const bool two = TWO && uniform_f(reinterpret_cast<const float*>(sl_k + Cf::sDec)[0]) >= kTwoPartDecay;
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
         st4_s<D>(dSl, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+        if (TWO && two)
+          st4_s<D>(dSlo, jj, j, lo_part(acc[x][0]), lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
         if (Cf::SPLIT && job.store)   // no LDS left for a low tile: stored directly
           st_bf16x4(p.dSlo + (int64_t(h) * p.NC + chunk(k)) * D * D + (v0 + 16 * sv + jj) * D + j, lo_part(acc[x][0]),
                     lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
@@ -919,8 +941,18 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
           if constexpr (Cf::LO) ad = mma(pa, frag_kc_s<16>(X2, 0, k0), ad);
         }
       }
+      if (TWO && two) {
 #pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) ak = mma(frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0), frag_rk_s<D>(dSl, 0, k0), ak);
+        for (int k0 = 0; k0 < D; k0 += 32) {
+          const bf16x8 kf = frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0);
+          ak = mma(kf, frag_rk_s<D>(dSl, 0, k0), ak);
+          ak = mma(kf, frag_rk_s<D>(dSlo, 0, k0), ak);
+        }
+      } else {
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 32)
+          ak = mma(frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0), frag_rk_s<D>(dSl, 0, k0), ak);
+      }
       if constexpr (Cf::RAW) {
         const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C +
                                                           16 * w + 4 * g);
@@ -929,6 +961,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
         ad += ak;
       }
       st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
+      if (TWO && two) st4_s<C, 1>(dUlo, jj, 16 * w + 4 * g, lo_part(ad[0]), lo_part(ad[1]), lo_part(ad[2]), lo_part(ad[3]));
       // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU: the first two terms do
       // not depend on dU and are issued before the barrier
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
@@ -971,34 +1004,73 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
           const float4 f = *reinterpret_cast<const float4*>(fw + 16 * rb + 4 * g);
           fwv[rb] = f32x4{f.x, f.y, f.z, f.w};
         }
-        bf16x8 kfr[NJW][2];
-#pragma unroll
-        for (int x = 0; x < NJW; ++x)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) kfr[x][kk] = frag_kc_split_s<D>(Bb + Cf::bK, 16 * (w * NJW + x), 32 * kk);
         f32x4 y[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          y[rb] = zero4();
-          if (rb < 2) y[rb] = mma(frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 0), du0, y[rb]);
-          y[rb] = mma(frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 32), du1, y[rb]);
-          y[rb] *= fwv[rb];
-        }
         bf16x8 yb[2];
+        if (TWO && two) {
+          // (the rare path: fragments read where they are used, to keep the
+          // registers of the common path's schedule free)
+          const bf16x8 dl0 = frag_rk_s<C, 1>(dUlo, 0, 0), dl1 = frag_rk_s<C, 1>(dUlo, 0, 32);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+          for (int rb = 0; rb < 4; ++rb) {
+            y[rb] = zero4();
+            if (rb < 2) {
+              const bf16x8 a0 = frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 0);
+              y[rb] = mma(a0, du0, y[rb]);
+              y[rb] = mma(a0, dl0, y[rb]);
+            }
+            const bf16x8 a1 = frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 32);
+            y[rb] = mma(a1, du1, y[rb]);
+            y[rb] = mma(a1, dl1, y[rb]);
+            y[rb] *= fwv[rb];
+          }
+          bf16x8 yl[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            yb[kk][i] = to_bf16(y[2 * kk][i]);
-            yb[kk][4 + i] = to_bf16(y[2 * kk + 1][i]);
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              yb[kk][i] = to_bf16(y[2 * kk][i]);
+              yb[kk][4 + i] = to_bf16(y[2 * kk + 1][i]);
+              yl[kk][i] = to_bf16(lo_part(y[2 * kk][i]));
+              yl[kk][4 + i] = to_bf16(lo_part(y[2 * kk + 1][i]));
+            }
+#pragma unroll
+          for (int x = 0; x < NJW; ++x) {
+            f32x4 aw = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              const bf16x8 kf = frag_kc_split_s<D>(Bb + Cf::bK, 16 * (w * NJW + x), 32 * kk);
+              aw = mma(kf, yb[kk], aw);
+              aw = mma(kf, yl[kk], aw);
+            }
+            acc[x] = an[x] - aw;
+          }
+        } else {
+          bf16x8 kfr[NJW][2];
+#pragma unroll
+          for (int x = 0; x < NJW; ++x)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) kfr[x][kk] = frag_kc_split_s<D>(Bb + Cf::bK, 16 * (w * NJW + x), 32 * kk);
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            y[rb] = zero4();
+            if (rb < 2) y[rb] = mma(frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 0), du0, y[rb]);
+            y[rb] = mma(frag_kc_s<C>(Bb + Cf::bA, 16 * rb, 32), du1, y[rb]);
+            y[rb] *= fwv[rb];
           }
 #pragma unroll
-        for (int x = 0; x < NJW; ++x) {
-          const int jb = w * NJW + x;
-          f32x4 aw = zero4();
+          for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) aw = mma(kfr[x][kk], yb[kk], aw);
-          acc[x] = an[x] - aw;
+            for (int i = 0; i < 4; ++i) {
+              yb[kk][i] = to_bf16(y[2 * kk][i]);
+              yb[kk][4 + i] = to_bf16(y[2 * kk + 1][i]);
+            }
+#pragma unroll
+          for (int x = 0; x < NJW; ++x) {
+            f32x4 aw = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) aw = mma(kfr[x][kk], yb[kk], aw);
+            acc[x] = an[x] - aw;
+          }
         }
       } else {
 #pragma unroll
@@ -1102,9 +1174,21 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
 // dealt round-robin over the 8 XCDs).  The final pass has D / 16 slices per
 // (segment, head), the state rows; the local pass twice that many, the state
 // rows and then the transfer-product rows; a workgroup takes NSL consecutive slices.
-template <int D, typename TIO, int GATE, int NSL>
+// Raw mode: whether any chunk of segment se decays weakly enough for two-part
+// reverse steps (every wave reads the chunk decays itself: a uniform answer with
+// no barrier)
+__device__ __forceinline__ bool weak_segment(const Params& p, const SeqEntry& se, int h) {
+  int f = 0;
+  for (int i = lane_id(); i < se.nchunks; i += 64) f |= p.edec[(int64_t(h) * p.NC + se.c0 + i) * 4] >= kTwoPartDecay;
+  return __any(f);
+}
+
+// TWO: the reverse role of the segments weak_segment() picks (the common kernel
+// leaves them out); raw mode only
+template <int D, typename TIO, int GATE, int NSL, bool TWO = false>
 __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chain(const Params p, int mode, int nb_role,
                                                                                   int pass) {
+  static_assert(!TWO || ChainCfg<D, TIO, GATE, NSL>::RAW, "two-part steps in raw mode only");
   __shared__ __attribute__((aligned(1024))) char smem[ChainCfg<D, TIO, GATE, NSL>::bytes];
   int b = blockIdx.x;
   int role;
@@ -1155,6 +1239,8 @@ __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chai
   // only segments that a later one (in the role's order) starts from, and the
   // transfer product only where the segment does not start from h0 / dht
   if (pass == kPassLocal && (last || (xfer && first))) return;
+  if constexpr (ChainCfg<D, TIO, GATE, NSL>::RAW)
+    if (role == 1 && weak_segment(p, se, h) != TWO) return;
   ChainJob jobs[NSL];
 #pragma unroll
   for (int i = 0; i < NSL; ++i) {
@@ -1173,10 +1259,14 @@ __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chai
       job.store = true;
     }
   }
-  if (role == 0)
-    chain_fwd<D, TIO, GATE, NSL>(p, smem, si, h, sl, jobs);
-  else
-    chain_bwd<D, TIO, GATE, NSL>(p, smem, si, h, sl, jobs);
+  if constexpr (TWO) {
+    chain_bwd<D, TIO, GATE, NSL, true>(p, smem, si, h, sl, jobs);
+  } else {
+    if (role == 0)
+      chain_fwd<D, TIO, GATE, NSL>(p, smem, si, h, sl, jobs);
+    else
+      chain_bwd<D, TIO, GATE, NSL, false>(p, smem, si, h, sl, jobs);
+  }
 }
 
 // The boundary states of split sequences, in order: one workgroup per (first
@@ -1249,14 +1339,14 @@ __global__ __launch_bounds__(256) void k_chain_fix(const Params p, int mode) {
 }
 
 namespace {
-template <int D, typename TIO, int GATE, int NSL>
+template <int D, typename TIO, int GATE, int NSL, bool TWO = false>
 void launch_nsl(const Params& p, int mode, int pass, hipStream_t s) {
   constexpr int ns = D / 16;
   const int nsl = pass == kPassLocal ? 2 * ns : ns;
   const int groups = p.NS * p.H;
   const int nb = ((groups + 7) / 8) * 8 * (nsl / NSL);
   const int nroles = mode == kChainBoth ? 2 : 1;
-  k_chain<D, TIO, GATE, NSL><<<dim3(nb * nroles), ChainCfg<D, TIO, GATE, NSL>::THREADS, 0, s>>>(p, mode, nb, pass);
+  k_chain<D, TIO, GATE, NSL, TWO><<<dim3(nb * nroles), ChainCfg<D, TIO, GATE, NSL>::THREADS, 0, s>>>(p, mode, nb, pass);
 }
 
 // One slice a workgroup while every workgroup gets a CU of its own (one fits per
@@ -1269,10 +1359,14 @@ void run_chain(const Params& p, int mode, int pass, hipStream_t s) {
   const int nsl = pass == kPassLocal ? 2 * ns : ns;
   const int64_t nb1 = int64_t((p.NS * p.H + 7) / 8) * 8 * nsl * (mode == kChainBoth ? 2 : 1);
   if constexpr (ChainCfg<D, TIO, GATE>::RAW) {
-    if (nb1 > kGpuCUs) {
+    if (nb1 > kGpuCUs)
       launch_nsl<D, TIO, GATE, 2>(p, mode, pass, s);
-      return;
-    }
+    else
+      launch_nsl<D, TIO, GATE, 1>(p, mode, pass, s);
+    // the reverse role of the segments with weakly decaying chunks (their
+    // workgroups in the launch above return at once, as do the others here)
+    if (mode != kChainFwd) launch_nsl<D, TIO, GATE, 1, true>(p, kChainBwd, pass, s);
+    return;
   }
   launch_nsl<D, TIO, GATE, 1>(p, mode, pass, s);
 }
