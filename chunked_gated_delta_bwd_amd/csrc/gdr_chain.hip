@@ -773,14 +773,20 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       }
       st4_s<C, 1>(Ut, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
       chain_barrier();   // B2
-      // S_{k+1}^T = Diag(e^GamC) S_k^T + Khat^T U
+      // S_{k+1}^T = Diag(e^GamC) S_k^T + Khat^T U (per-channel gate: U in two parts,
+      // the low one also stored for the gradient kernel; U's bf16 rounding here is
+      // the largest single term of the gate-parameter gradients' error)
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int jb = w * NJW + x;
         f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
 #pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_kc_s<D>(Fb + Cf::fK, 16 * jb, k0), frag_rk_s<C, 1>(Ut, 0, k0), a);
+        for (int k0 = 0; k0 < C; k0 += 32) {
+          const bf16x8 kh = frag_kc_s<D>(Fb + Cf::fK, 16 * jb, k0);
+          a = mma(kh, frag_rk_s<C, 1>(Ut, 0, k0), a);
+          if constexpr (Cf::SPLIT) a = mma(kh, frag_rk_s<C, 1>(smem + Cf::fUl, 0, k0), a);
+        }
         acc[x] = a;
       }
     }
