@@ -191,6 +191,8 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.Ulo = take(kda * H * NC * C * V * 2);
   L.Slo = take(kda * H * NC * V * K * 2);
   L.dSlo = take(kda * H * NC * V * K * 2);
+  L.Khl = take(kda * H * NC * C * K * 2);
+  L.weak = take(kda * H * NC * 4);
   L.xf = take(L.split * 2 * NS * H * 2 * K * K * 4);
   L.sb = take(L.split * 2 * NS * H * K * K * 4);
   const size_t grouped = s->Hk > 0 && s->Hk < s->H ? 1 : 0;
@@ -358,6 +360,8 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   p.Ulo = reinterpret_cast<uint16_t*>(w + L.Ulo);
   p.Slo = reinterpret_cast<uint16_t*>(w + L.Slo);
   p.dSlo = reinterpret_cast<uint16_t*>(w + L.dSlo);
+  p.Khl = reinterpret_cast<uint16_t*>(w + L.Khl);
+  p.weak = reinterpret_cast<int32_t*>(w + L.weak);
   p.xf = L.split ? reinterpret_cast<float*>(w + L.xf) : nullptr;
   p.sb = L.split ? reinterpret_cast<float*>(w + L.sb) : nullptr;
   return p;

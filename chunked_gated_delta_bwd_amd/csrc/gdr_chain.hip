@@ -122,8 +122,10 @@ struct ChainCfg {
   // with W S^T formed as A (Diag(fw) k S^T)
   // (the U' slices of the NSL slices in one region: element (s, r, c) at
   // ((r / 16) NSL + s) 512 + (r % 16) 32 + 2c bytes, one mover load covering 16 rows of all)
+  // (per-channel gate: Khat's low part for the weak-chunk kernel, fKl)
   static constexpr int fW = 0, fA = 0, fK = MAT ? TB : PB, fUp = fK + TB, fUpl = fUp + NSL * XB;
-  static constexpr int bufF = fUpl + (SPLIT ? XB : 0);
+  static constexpr int fKl = fUpl + (SPLIT ? XB : 0);
+  static constexpr int bufF = fKl + (SPLIT ? TB : 0);
   static constexpr int fSlot = 2 * bufF;
   static constexpr int fS = fSlot + 3 * SLOT;                      // 16 x D state slice, each slice
   static constexpr int fU = fS + NSL * 16 * D * 2;                 // 16 x 64: U^T as the MFMA takes it, each slice
@@ -365,15 +367,19 @@ __device__ __forceinline__ void move_fwd_a(const MoverLane<D>& ml, const Params&
   }
 }
 
-template <int D, typename TIO, int GATE>
+// (TWO, per-channel gate: Khat's low part too, written by the prologue for weak
+// chunks only; the tile of another chunk is loaded but not read)
+template <int D, typename TIO, int GATE, bool TWO = false>
 __device__ __forceinline__ void move_fwd_b(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            char* buf, int mw) {
   using Cf = ChainCfg<D, TIO, GATE>;
   const ChunkGeo cg = geo(p, se, h, c);
-  if constexpr (Cf::RAW)
+  if constexpr (Cf::RAW) {
     move_rows<D>(ml, p.k, cg, buf + Cf::fK, mw);
-  else
+  } else {
     move_tile<D>(ml, p.Kh + cg.ch * C * D, buf + Cf::fK, mw);
+    if constexpr (TWO) move_tile<D>(ml, p.Khl + cg.ch * C * D, buf + Cf::fKl, mw);
+  }
 }
 
 // L2 prefetch of chunk c, three steps beyond the direct-to-LDS loads: the V
@@ -677,11 +683,17 @@ __device__ __forceinline__ ChainJob job_of(const ChainJob (&jobs)[NSL], int sv) 
   }
 }
 
-template <int D, typename TIO, int GATE, int NSL>
+// TWO (per-channel gate): the kernel that runs the segments with weak chunks,
+// whose steps take Khat in two parts in the state update
+template <int D, typename TIO, int GATE, int NSL, bool TWO = false>
 __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, int h, int sl,
                                           const ChainJob (&jobs)[NSL]) {
   using Dm = Dims<D>;
   using Cf = ChainCfg<D, TIO, GATE, NSL>;
+  static_assert(!TWO || Cf::SPLIT, "two-part forward steps for the per-channel gate only");
+  // mover loads per wave in a chunk's second set (TWO: Khat's low part as well)
+  constexpr int FB = Cf::fwdB + (TWO ? Cf::NJ : 0);
+  static_assert(2 * Cf::fwdA + FB + (Cf::PFD - 2) * Cf::NPF < 64, "vmcnt range");
   constexpr int NJW = Dm::NJW;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id();
@@ -708,6 +720,8 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     for (int k = 0; k < nck; ++k) {
       const char* Fb = smem + (k & 1) * Cf::bufF;
       const char* sl_k = slot(k);
+      // a weak chunk (TWO): read ahead of its use after the second barrier
+      const bool wk = TWO && p.weak[int64_t(h) * p.NC + chunk(k)] != 0;
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
@@ -775,7 +789,8 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       chain_barrier();   // B2
       // S_{k+1}^T = Diag(e^GamC) S_k^T + Khat^T U (per-channel gate: U in two parts,
       // the low one also stored for the gradient kernel; U's bf16 rounding here is
-      // the largest single term of the gate-parameter gradients' error)
+      // the largest single term of the gate-parameter gradients' error, Khat's the
+      // next one, which only weak chunks pay for)
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
@@ -784,8 +799,10 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += 32) {
           const bf16x8 kh = frag_kc_s<D>(Fb + Cf::fK, 16 * jb, k0);
-          a = mma(kh, frag_rk_s<C, 1>(Ut, 0, k0), a);
+          const bf16x8 ut = frag_rk_s<C, 1>(Ut, 0, k0);
+          a = mma(kh, ut, a);
           if constexpr (Cf::SPLIT) a = mma(kh, frag_rk_s<C, 1>(smem + Cf::fUl, 0, k0), a);
+          if (TWO && wk) a = mma(frag_kc_s<D>(Fb + Cf::fKl, 16 * jb, k0), ut, a);
         }
         acc[x] = a;
       }
@@ -838,39 +855,38 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
     };
     move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(0), v0l, slot(0), mw, false);
     move_fwd_a<D, TIO, GATE, NSL>(ml, p, se, h, chunk(0), v0l, smem, mw);
-    move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
+    move_fwd_b<D, TIO, GATE, TWO>(ml, p, se, h, chunk(0), smem, mw);
     move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(1), v0l, slot(1), mw, false);
     move_fwd_a<D, TIO, GATE, NSL>(ml, p, se, h, chunk(1), v0l, smem + Cf::bufF, mw);
     for (int c = 2; c < Cf::PFD; ++c) prefetch(chunk(c));
-    wait_mover<Cf::fwdA + Cf::fwdB + Cf::fwdA + (Cf::PFD - 2) * NPF>(hs);
+    wait_mover<Cf::fwdA + FB + Cf::fwdA + (Cf::PFD - 2) * NPF>(hs);
     chain_barrier();   // B0
     // raw mode reads set B (k) in the first window too: both sets of chunk 0 land
     // before B1; otherwise set B may land by B2
     if constexpr (Cf::RAW) wait_mover<Cf::fwdA + 1 + (Cf::PFD - 2) * NPF>(hs);
-    else wait_mover<Cf::fwdB + Cf::fwdA + (Cf::PFD - 2) * NPF>(hs);
+    else wait_mover<FB + Cf::fwdA + (Cf::PFD - 2) * NPF>(hs);
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
-      move_fwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
+      move_fwd_b<D, TIO, GATE, TWO>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufF, mw);
       move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, false);
-      wait_mover<Cf::fwdA + NPF + Cf::fwdB>(hs);
+      wait_mover<Cf::fwdA + NPF + FB>(hs);
       chain_barrier();   // B2
       move_fwd_a<D, TIO, GATE, NSL>(ml, p, se, h, chunk(k + 2), v0l, smem + (k & 1) * Cf::bufF, mw);
       prefetch(chunk(k + Cf::PFD));
       if constexpr (Cf::RAW) wait_mover<Cf::fwdA + NPF + 1>(hs);   // set B of chunk k + 1 before the next B1
-      else wait_mover<Cf::fwdB + Cf::fwdA + 2 * NPF>(hs);
+      else wait_mover<FB + Cf::fwdA + 2 * NPF>(hs);
     }
     wait_vm<0>();
   }
 }
 
-// Raw mode: reverse steps of chunks whose decay e^GamC is at least this take the
-// operands dS (in Khat dS^T), dU (in A^T dU) and Y (in k^T Y) in two bf16 parts.
-// A step's rounding error is proportional to e^GamC (Khat^T W is), and the next
-// steps damp it by their own decay; with little decay it accumulates over the
-// whole sequence (float64 model of the state-gradient recursion with each
-// rounding switched on alone: at e^GamC = 1 each of the three gives 8e-4 relative
-// error in dh0 over four chunks, 1.5e-3 together; at 1/16 all of them 5e-4).
-constexpr float kTwoPartDecay = 1.f / 16;
+// Raw mode: reverse steps of weak chunks (kTwoPartDecay) take the operands dS (in
+// Khat dS^T), dU (in A^T dU) and Y (in k^T Y) in two bf16 parts.  A step's
+// rounding error is proportional to e^GamC (Khat^T W is), and the next steps damp
+// it by their own decay; with little decay it accumulates over the whole sequence
+// (float64 model of the state-gradient recursion with each rounding switched on
+// alone: at e^GamC = 1 each of the three gives 8e-4 relative error in dh0 over
+// four chunks, 1.5e-3 together; at 1/16 all of them 5e-4).
 
 // TWO: the kernel that runs the segments with weakly decaying chunks (their steps
 // take two-part operands; the other steps the common ones)
@@ -1180,21 +1196,28 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
 // dealt round-robin over the 8 XCDs).  The final pass has D / 16 slices per
 // (segment, head), the state rows; the local pass twice that many, the state
 // rows and then the transfer-product rows; a workgroup takes NSL consecutive slices.
-// Raw mode: whether any chunk of segment se decays weakly enough for two-part
-// reverse steps (every wave reads the chunk decays itself: a uniform answer with
-// no barrier)
+// Whether segment se has a weak chunk (kTwoPartDecay); every wave reads the chunk
+// decays (scalar gate) or flags (per-channel gate) itself: a uniform answer with
+// no barrier
+template <int GATE>
 __device__ __forceinline__ bool weak_segment(const Params& p, const SeqEntry& se, int h) {
   int f = 0;
-  for (int i = lane_id(); i < se.nchunks; i += 64) f |= p.edec[(int64_t(h) * p.NC + se.c0 + i) * 4] >= kTwoPartDecay;
+  for (int i = lane_id(); i < se.nchunks; i += 64) {
+    const int64_t ch = int64_t(h) * p.NC + se.c0 + i;
+    if constexpr (GATE == 0) f |= p.edec[ch * 4] >= kTwoPartDecay;
+    else f |= p.weak[ch];
+  }
   return __any(f);
 }
 
-// TWO: the reverse role of the segments weak_segment() picks (the common kernel
-// leaves them out); raw mode only
+// TWO: the segments weak_segment() picks, in the role whose steps take two-part
+// operands for them (raw mode: the reverse role; per-channel gate: the forward
+// role); the common kernel leaves them out of that role
 template <int D, typename TIO, int GATE, int NSL, bool TWO = false>
 __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chain(const Params p, int mode, int nb_role,
                                                                                   int pass) {
-  static_assert(!TWO || ChainCfg<D, TIO, GATE, NSL>::RAW, "two-part steps in raw mode only");
+  using Cf = ChainCfg<D, TIO, GATE, NSL>;
+  static_assert(!TWO || Cf::RAW || Cf::SPLIT, "two-part steps: raw mode or the per-channel gate");
   __shared__ __attribute__((aligned(1024))) char smem[ChainCfg<D, TIO, GATE, NSL>::bytes];
   int b = blockIdx.x;
   int role;
@@ -1245,8 +1268,8 @@ __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chai
   // only segments that a later one (in the role's order) starts from, and the
   // transfer product only where the segment does not start from h0 / dht
   if (pass == kPassLocal && (last || (xfer && first))) return;
-  if constexpr (ChainCfg<D, TIO, GATE, NSL>::RAW)
-    if (role == 1 && weak_segment(p, se, h) != TWO) return;
+  if constexpr (Cf::RAW || Cf::SPLIT)
+    if (role == (Cf::RAW ? 1 : 0) && weak_segment<GATE>(p, se, h) != TWO) return;
   ChainJob jobs[NSL];
 #pragma unroll
   for (int i = 0; i < NSL; ++i) {
@@ -1266,7 +1289,10 @@ __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chai
     }
   }
   if constexpr (TWO) {
-    chain_bwd<D, TIO, GATE, NSL, true>(p, smem, si, h, sl, jobs);
+    if constexpr (Cf::RAW)
+      chain_bwd<D, TIO, GATE, NSL, true>(p, smem, si, h, sl, jobs);
+    else
+      chain_fwd<D, TIO, GATE, NSL, true>(p, smem, si, h, sl, jobs);
   } else {
     if (role == 0)
       chain_fwd<D, TIO, GATE, NSL>(p, smem, si, h, sl, jobs);
@@ -1375,6 +1401,9 @@ void run_chain(const Params& p, int mode, int pass, hipStream_t s) {
     return;
   }
   launch_nsl<D, TIO, GATE, 1>(p, mode, pass, s);
+  // per-channel gate: the forward role of the segments with weak chunks
+  if constexpr (ChainCfg<D, TIO, GATE>::SPLIT)
+    if (mode != kChainBwd) launch_nsl<D, TIO, GATE, 1, true>(p, kChainFwd, pass, s);
 }
 }  // namespace
 

@@ -11,6 +11,13 @@
 namespace gdr {
 
 constexpr int kChunk = 64;     // tokens per chunk
+// Chunks whose decay e^GamC (the scalar gate's, or the per-channel gate's largest
+// over the channels) is at least this are "weak": a recursion step's bf16 rounding
+// error is proportional to that decay, and with little decay the following steps
+// do not damp it.  Their steps take some operands in two bf16 parts (x = hi + lo):
+// the scalar gate's reverse steps dS, dU and Y, the per-channel gate's forward
+// steps Khat.
+constexpr float kTwoPartDecay = 1.f / 16;
 constexpr int kThreads = 256;  // threads per workgroup in every kernel (4 wave64s)
 
 // One row per chunk (global chunk index c).
@@ -96,6 +103,8 @@ struct WsLayout {
   size_t Ulo = 0;    // bf16 [H][NC][V][64]
   size_t Slo = 0;    // bf16 [H][NC][V][K]
   size_t dSlo = 0;   // bf16 [H][NC][V][K]
+  size_t Khl = 0;    // bf16 [H][NC][64][K]: Khat's low part, written for weak chunks only
+  size_t weak = 0;   // int32 [H][NC]: 1 for a weak chunk (see kTwoPartDecay)
   // split sequences only: the first recursion pass's segment-end states and
   // transfer products, and the composed segment boundary states
   size_t xf = 0;     // fp32 [2 roles][NS][H][2 D][D]: rows 0..D-1 end state from zero (or from
@@ -133,6 +142,8 @@ struct Params {
   uint16_t* Mk;                                  // per-channel gate only
   float *pdA, *pddt;
   uint16_t *Uplo, *Ulo, *Slo, *dSlo;             // per-channel gate only: low parts
+  uint16_t* Khl;                                 // per-channel gate only, weak chunks only
+  int32_t* weak;                                 // per-channel gate only
   float *xf, *sb;                                // split sequences only
 };
 

@@ -345,12 +345,17 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
   __syncthreads();
 
   // --- beta Kbar (Kbar = kn e^Gam) and beta V overwrite the operand tiles; the
-  // recursions' Khat / Qbar tiles and the chunk decay go to the workspace ---
+  // recursions' Khat / Qbar tiles and the chunk decay go to the workspace; a weak
+  // chunk (some channel decays by less than kTwoPartDecay) also Khat's low part ---
+  int wf = 0;
+  for (int j = l; j < D; j += 64) wf |= fast_exp(Gs[(C - 1) * PG + j]) >= kTwoPartDecay;
+  const bool weak = __any(wf);
+  if (tid == 0) p.weak[ch] = weak ? 1 : 0;
 #pragma unroll
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     const float fb = beta_s[r];
-    bf16x8 kb, vb, vl, kh, qh, ql;
+    bf16x8 kb, vb, vl, kh, khl, qh, ql;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float gr = Gs[r * PG + c0 + e], gC = Gs[(C - 1) * PG + c0 + e];
@@ -359,7 +364,9 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
       const float bv = fb * v_r[ps][e];
       vb[e] = to_bf16(bv);
       vl[e] = to_bf16(bv - float(vb[e]));
-      kh[e] = to_bf16(kn_r[ps][e] * eh);
+      const float kx = kn_r[ps][e] * eh;
+      kh[e] = to_bf16(kx);
+      khl[e] = to_bf16(kx - float(kh[e]));
       const float x = scale * qn_r[ps][e] * eg;
       qh[e] = to_bf16(x);
       ql[e] = to_bf16(x - float(qh[e]));
@@ -369,6 +376,7 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
     *reinterpret_cast<bf16x8*>(Vsl + r * PD + c0) = vl;
     const int64_t o = (ch * C + r) * D + c0;
     *reinterpret_cast<bf16x8*>(p.Kh + o) = kh;
+    if (weak) *reinterpret_cast<bf16x8*>(p.Khl + o) = khl;
     *reinterpret_cast<bf16x8*>(p.Qh + o) = qh;
     *reinterpret_cast<bf16x8*>(p.Ql + o) = ql;
   }

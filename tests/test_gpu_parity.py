@@ -121,20 +121,20 @@ def test_kda_small_against_oracle(name, spec, mode):
 # far above 60) sends every channel down the exact per-element path; in between
 # (e^A_log = 9, half-spans of 60 and more in about half of the channels of every
 # block) the prologue splits each diagonal block between the two paths by channel
-# and the gradient kernel by 16-channel tile.  With almost no forgetting the fp32
-# parameter gradients lose precision to the bf16 chunk states accumulated over the
-# whole sequence (measured 1.7e-3 on dA_log, the same before the factored paths
-# existed), so the weak regime is held to 3e-3 there; everything else keeps the
-# standard bars.
-@pytest.mark.parametrize("a_log,tol_fp32", [(-3.0, 3e-3), (2.2, TOL_FP32), (3.0, TOL_FP32)],
-                         ids=["weak_decay", "mixed_decay", "strong_decay"])
-def test_kda_decay_regimes(a_log, tol_fp32):
-    log(f"case kda decay regime A_log={a_log}")
-    inp = synth.generate(synth.Spec("kd", 1, "bf16", H=2, K=128, V=128, lengths=[200, 77], h0_std=0.1,
+# and the gradient kernel by 16-channel tile.  With almost no forgetting the chunk
+# states' bf16 rounding is not damped between chunks: the forward state update
+# then takes U and Khat in two parts (weak chunks), and all three regimes keep the
+# standard bars (one part each: dA_log 1.7e-3, ddt_bias 1.2e-3 in the weak regime).
+# The H = 17 case runs the same in a grid of more than one workgroup per CU.
+@pytest.mark.parametrize("a_log,H", [(-3.0, 2), (-3.0, 17), (2.2, 2), (3.0, 2)],
+                         ids=["weak_decay", "weak_decay_h17", "mixed_decay", "strong_decay"])
+def test_kda_decay_regimes(a_log, H):
+    log(f"case kda decay regime A_log={a_log} H={H}")
+    inp = synth.generate(synth.Spec("kd", 1, "bf16", H=H, K=128, V=128, lengths=[200, 77], h0_std=0.1,
                                     dht_std=0.1, seed=47))
     inp["A_log"] = torch.full_like(inp["A_log"], a_log)
     got = gpu_run(inp)
-    _check(inp, got, f"kda_decay_{a_log}", tol_fp32=tol_fp32)
+    _check(inp, got, f"kda_decay_{a_log}_h{H}")
 
 
 def test_kda_chunk_boundary_states():
