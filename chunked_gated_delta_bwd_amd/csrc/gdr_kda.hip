@@ -107,6 +107,14 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
   __shared__ __attribute__((aligned(16))) bf16 Asl[C * PC];
   __shared__ __attribute__((aligned(16))) bf16 Vsl[C * PD];
   __shared__ float beta_s[C], tot_s[NPART][D];
+  // bf16 inputs: Ks, Qs hold the raw k, q rows (exact in bf16) until the M, P
+  // blocks are formed, and these the row norms 1/|k|, 1/|q| (kn = k / |k| in fp32);
+  // fp32 inputs: kn, qn in bf16 and factors 1.  They share space with Asl, which
+  // is written only later.
+  constexpr bool kRawRows = !std::is_same<TIO, float>::value;
+  float* const rk_s = reinterpret_cast<float*>(Asl);
+  float* const rq_s = rk_s + C;
+  static_assert(2 * C * 4 <= C * PC * 2, "row norms fit in Asl");
 
   int c, h;
   chunk_head(p, c, h);
@@ -172,12 +180,14 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
     for (int e = 0; e < 8; ++e) {
       kn_r[ps][e] = kv[e] * rk;
       qn_r[ps][e] = qv[e] * rq;
-      qb[e] = to_bf16(qn_r[ps][e]);
-      kb[e] = to_bf16(kn_r[ps][e]);
+      qb[e] = to_bf16(kRawRows ? qv[e] : qn_r[ps][e]);
+      kb[e] = to_bf16(kRawRows ? kv[e] : kn_r[ps][e]);
     }
     *reinterpret_cast<bf16x8*>(Qs + r * PD + c0) = qb;
     *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
     if (tid % TPR == 0) {
+      rk_s[r] = kRawRows ? rk : 1.f;
+      rq_s[r] = kRawRows ? rq : 1.f;
       p.rho[ch * 3 * C + r] = rq;
       p.rho[ch * 3 * C + C + r] = rk;
     }
@@ -212,64 +222,87 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
   }
   __syncthreads();
 
-  // --- M and P between blocks (the second wave of each row block): rows 16R..,
-  // blocks sb < R, reference row 16R (so both factors are <= 1); lane owns
-  // M[r][s .. s+3] ---
+  // --- M and P between blocks (the second waves of the row blocks): block (R, sb),
+  // sb < R, rows 16R.., reference row 16R (so both factors are <= 1); lane owns
+  // M[r][s .. s+3].  The operands kn e^(Gam - Gam_ref) and qn e^(Gam - Gam_ref)
+  // are formed in fp32 and taken in two bf16 parts (products hi hi + lo hi + hi
+  // lo): the gate-parameter gradients sum terms that cancel strongly, and these
+  // blocks' bf16 roundings are among the largest terms of their error.  The six
+  // blocks are dealt two, two, one and one to the four waves, the pairs sharing
+  // their row operands: (3,0) (3,1) | (2,0) (2,1) | (3,2) | (1,0) ---
   if (hf == 1) {
-    const int R = rb, r = 16 * R + jj;
-    f32x4 aM[3], aP[3];
+    const int R = rb == 0 || rb == 2 ? 3 : rb == 1 ? 2 : 1;
+    const int sb0 = rb == 2 ? 2 : 0, nsb = rb < 2 ? 2 : 1;
+    const int r = 16 * R + jj;
+    f32x4 aM[2], aP[2];
 #pragma unroll
-    for (int x = 0; x < 3; ++x) aM[x] = aP[x] = zero4();
-    if (R > 0) {
+    for (int x = 0; x < 2; ++x) aM[x] = aP[x] = zero4();
+    const float rkr = rk_s[r], rqr = rq_s[r];
 #pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) {
-        const int c0 = k0 + 8 * g;
-        const float4 gr0 = ld4(Gs + r * PG + c0), gr1 = ld4(Gs + r * PG + c0 + 4);
-        const float4 gf0 = ld4(Gs + 16 * R * PG + c0), gf1 = ld4(Gs + 16 * R * PG + c0 + 4);
-        const bf16x8 kr = *reinterpret_cast<const bf16x8*>(Ks + r * PD + c0);
-        const bf16x8 qr = *reinterpret_cast<const bf16x8*>(Qs + r * PD + c0);
-        bf16x8 bk, bq;
+    for (int k0 = 0; k0 < D; k0 += 32) {
+      const int c0 = k0 + 8 * g;
+      const float4 gr0 = ld4(Gs + r * PG + c0), gr1 = ld4(Gs + r * PG + c0 + 4);
+      const float4 gf0 = ld4(Gs + 16 * R * PG + c0), gf1 = ld4(Gs + 16 * R * PG + c0 + 4);
+      const bf16x8 kr = *reinterpret_cast<const bf16x8*>(Ks + r * PD + c0);
+      const bf16x8 qr = *reinterpret_cast<const bf16x8*>(Qs + r * PD + c0);
+      bf16x8 bk, bq, bkl, bql;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float d = fast_exp(e < 4 ? el(gr0, e) - el(gf0, e) : el(gr1, e - 4) - el(gf1, e - 4));
-          bk[e] = to_bf16(float(kr[e]) * d);
-          bq[e] = to_bf16(float(qr[e]) * d);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float d = fast_exp(e < 4 ? el(gr0, e) - el(gf0, e) : el(gr1, e - 4) - el(gf1, e - 4));
+        const float xk = float(kr[e]) * (rkr * d), xq = float(qr[e]) * (rqr * d);
+        bk[e] = to_bf16(xk);
+        bq[e] = to_bf16(xq);
+        bkl[e] = to_bf16(xk - float(bk[e]));
+        bql[e] = to_bf16(xq - float(bq[e]));
+      }
 #pragma unroll
-        for (int sb = 0; sb < 3; ++sb) {
-          if (sb < R) {
-            const int s = 16 * sb + jj;
-            const float4 gs0 = ld4(Gs + s * PG + c0), gs1 = ld4(Gs + s * PG + c0 + 4);
-            const bf16x8 ks = *reinterpret_cast<const bf16x8*>(Ks + s * PD + c0);
-            bf16x8 ak;
+      for (int x = 0; x < 2; ++x) {
+        if (x < nsb) {
+          const int s = 16 * (sb0 + x) + jj;
+          const float4 gs0 = ld4(Gs + s * PG + c0), gs1 = ld4(Gs + s * PG + c0 + 4);
+          const bf16x8 ks = *reinterpret_cast<const bf16x8*>(Ks + s * PD + c0);
+          const float rks = rk_s[s];
+          bf16x8 ak, akl;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float d = fast_exp(e < 4 ? el(gf0, e) - el(gs0, e) : el(gf1, e - 4) - el(gs1, e - 4));
-              ak[e] = to_bf16(float(ks[e]) * d);
-            }
-            aM[sb] = mma(ak, bk, aM[sb]);
-            aP[sb] = mma(ak, bq, aP[sb]);
+          for (int e = 0; e < 8; ++e) {
+            const float d = fast_exp(e < 4 ? el(gf0, e) - el(gs0, e) : el(gf1, e - 4) - el(gs1, e - 4));
+            const float xs = float(ks[e]) * (rks * d);
+            ak[e] = to_bf16(xs);
+            akl[e] = to_bf16(xs - float(ak[e]));
           }
+          aM[x] = mma(ak, bk, aM[x]);
+          aM[x] = mma(akl, bk, aM[x]);
+          aM[x] = mma(ak, bkl, aM[x]);
+          aP[x] = mma(ak, bq, aP[x]);
+          aP[x] = mma(akl, bq, aP[x]);
+          aP[x] = mma(ak, bql, aP[x]);
         }
       }
     }
     const float br = beta_s[r];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      if (sb == R) continue;   // diagonal blocks below
-      const int s0 = 16 * sb + 4 * g;
-      float Lv[4] = {0.f, 0.f, 0.f, 0.f}, Pv[4] = {0.f, 0.f, 0.f, 0.f}, Mv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (sb < R) {
+    for (int x = 0; x < 2; ++x) {
+      if (x < nsb) {
+        const int s0 = 16 * (sb0 + x) + 4 * g;
+        float Lv[4], Pv[4], Mv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          Mv[i] = aM[sb < 3 ? sb : 0][i];
-          Pv[i] = scale * aP[sb < 3 ? sb : 0][i];
+          Mv[i] = aM[x][i];
+          Pv[i] = scale * aP[x][i];
           Lv[i] = br * Mv[i];
         }
+        *reinterpret_cast<float4*>(Lf + r * PL + s0) = make_float4(Lv[0], Lv[1], Lv[2], Lv[3]);
+        st_bf16x4(p.P + (ch * C + r) * C + s0, Pv[0], Pv[1], Pv[2], Pv[3]);
+        st_bf16x4(p.Mk + (ch * C + r) * C + s0, Mv[0], Mv[1], Mv[2], Mv[3]);
       }
-      *reinterpret_cast<float4*>(Lf + r * PL + s0) = make_float4(Lv[0], Lv[1], Lv[2], Lv[3]);
-      st_bf16x4(p.P + (ch * C + r) * C + s0, Pv[0], Pv[1], Pv[2], Pv[3]);
-      st_bf16x4(p.Mk + (ch * C + r) * C + s0, Mv[0], Mv[1], Mv[2], Mv[3]);
+    }
+    // the zero blocks above the diagonal of row block rb
+    const int rz = 16 * rb + jj;
+    for (int sb = rb + 1; sb < 4; ++sb) {
+      const int s0 = 16 * sb + 4 * g;
+      *reinterpret_cast<float4*>(Lf + rz * PL + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
+      st_bf16x4(p.P + (ch * C + rz) * C + s0, 0.f, 0.f, 0.f, 0.f);
+      st_bf16x4(p.Mk + (ch * C + rz) * C + s0, 0.f, 0.f, 0.f, 0.f);
     }
   }
   // --- diagonal blocks: wave R's block factored at its middle row m = f + 8,
@@ -291,6 +324,7 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
     uint64_t wide1 = 0;
     if constexpr (D > 64) wide1 = __builtin_amdgcn_ballot_w64(wide_ch(64 + l));
     f32x4 aM = zero4(), aP = zero4();
+    const float rkr = rk_s[rr], rqr = rq_s[rr];
 #pragma unroll
     for (int kq = 0; kq < D / 16; ++kq) {
       const int c4 = (D / 4) * g + 4 * kq;
@@ -303,9 +337,9 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
         const bool wd = ((cc < 64 ? wide0 >> cc : wide1 >> (cc & 63)) & 1) != 0;
         const float ea = wd ? 0.f : fast_exp(el(gr4, e) - el(gm4, e));   // row as r
         const float eb = wd ? 0.f : fast_exp(el(gm4, e) - el(gr4, e));   // row as s
-        const float kn = float(k4[e]);
+        const float kn = float(k4[e]) * rkr;
         aM = mma_f32(kn * eb, kn * ea, aM);
-        aP = mma_f32(kn * eb, float(q4[e]) * ea, aP);
+        aP = mma_f32(kn * eb, float(q4[e]) * rqr * ea, aP);
       }
     }
     const int s0 = f + 4 * g;
@@ -320,11 +354,11 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
         cc = 64 + __builtin_ctzll(rest1);
         rest1 &= rest1 - 1;
       }
-      const float gr = Gs[rr * PG + cc], kr = float(Ks[rr * PD + cc]), qr = float(Qs[rr * PD + cc]);
+      const float gr = Gs[rr * PG + cc], kr = float(Ks[rr * PD + cc]) * rkr, qr = float(Qs[rr * PD + cc]) * rqr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int sc = s0 + i;
-        const float kk = float(Ks[sc * PD + cc]) * fast_exp(-fabsf(gr - Gs[sc * PG + cc]));
+        const float kk = float(Ks[sc * PD + cc]) * rk_s[sc] * fast_exp(-fabsf(gr - Gs[sc * PG + cc]));
         aM[i] += kr * kk;
         aP[i] += qr * kk;
       }

@@ -7,10 +7,10 @@ runs again from its true state.  The result is the unsplit recursion's up to
 rounding, so it is held to the same bars against the float64 oracle: forced
 splits on small problems (every gate form, both dtypes, both head sizes,
 ragged varlen packs with empty and one-token sequences, segments of one chunk),
-the library's own choice at T = 32768 with H = 2 and H = 4 (one GPU's share of
-the H = 16 and H = 32 problems under 8-way head sharding, where the unsplit
-recursions would use 32 or 64 of 256 compute units), and agreement with the
-unsplit path."""
+the library's own choice at T = 32768 with H = 2 and H = 4, both gates (one GPU's
+share of the H = 16 and H = 32 problems under 8-way head sharding, where the
+unsplit recursions would use 32 or 64 of 256 compute units), and agreement with
+the unsplit path."""
 
 import numpy as np
 import pytest
@@ -113,7 +113,7 @@ def test_split_chunk_states_match_unsplit():
         assert err < 1e-2, (key, err)
 
 
-@pytest.mark.parametrize("wl", ["gdn_bf16_t32768_h2_d128", "gdn_bf16_t32768_h4_d128"])
+@pytest.mark.parametrize("wl", ["gdn_bf16_t32768_h2_d128", "gdn_bf16_t32768_h4_d128", "kda_bf16_t32768_h2_d128"])
 def test_long_sequence_few_heads(wl):
     """The library's own choice (it splits these) against the oracle, every head,
     every token, and against the unsplit path."""
