@@ -63,6 +63,14 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   // fp32 inputs: the recursions take materialised Khat / Qbar tiles (Qbar split
   // into bf16 high and low parts); bf16 inputs use the raw rows and row factors
   constexpr bool kMat = std::is_same<TIO, float>::value;
+  // fp32 inputs: low bf16 parts of qn, kn (then beta Kbar) and A, so that M, P and
+  // W are formed from two-part operands (hi hi + lo hi + hi lo); bf16 inputs' rows
+  // are exact in bf16 after the row norm only up to its rounding, which the
+  // recursions' row factors carry instead
+  constexpr int kLoT = kMat ? C * PD : 8, kLoA = kMat ? C * PC : 8;
+  __shared__ __attribute__((aligned(16))) bf16 Qsl[kLoT];
+  __shared__ __attribute__((aligned(16))) bf16 Ksl[kLoT];
+  __shared__ __attribute__((aligned(16))) bf16 Asl[kLoA];
 
   int c, h;
   chunk_head(p, c, h);
@@ -121,16 +129,24 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
     sq = group_sum_dpp<TPR>(sq);
     sk = group_sum_dpp<TPR>(sk);
     const float rq = 1.0f / sqrtf(sq + 1e-6f), rk = 1.0f / sqrtf(sk + 1e-6f);
-    bf16x8 qb, kb;
+    bf16x8 qb, kb, ql, kl;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       kn_r[ps][e] = kv[e] * rk;
       if constexpr (kMat) qn_r[ps][e] = qv[e] * rq;
       qb[e] = to_bf16(qv[e] * rq);
       kb[e] = to_bf16(kn_r[ps][e]);
+      if constexpr (kMat) {
+        ql[e] = to_bf16(qn_r[ps][e] - float(qb[e]));
+        kl[e] = to_bf16(kn_r[ps][e] - float(kb[e]));
+      }
     }
     *reinterpret_cast<bf16x8*>(Qs + r * PD + c0) = qb;
     *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
+    if constexpr (kMat) {
+      *reinterpret_cast<bf16x8*>(Qsl + r * PD + c0) = ql;
+      *reinterpret_cast<bf16x8*>(Ksl + r * PD + c0) = kl;
+    }
     if (tid % TPR == 0) {
       p.rho[ch * 3 * C + r] = rq;
       p.rho[ch * 3 * C + C + r] = rk;
@@ -195,8 +211,16 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += 32) {
       const bf16x8 a = frag_rk(Ks, PD, 16 * sb, k0);
-      aM = mma(a, frag_rk(Ks, PD, 16 * tb, k0), aM);
-      aP = mma(a, frag_rk(Qs, PD, 16 * tb, k0), aP);
+      const bf16x8 bk = frag_rk(Ks, PD, 16 * tb, k0), bq = frag_rk(Qs, PD, 16 * tb, k0);
+      aM = mma(a, bk, aM);
+      aP = mma(a, bq, aP);
+      if constexpr (kMat) {
+        const bf16x8 al = frag_rk(Ksl, PD, 16 * sb, k0);
+        aM = mma(al, bk, aM);
+        aM = mma(a, frag_rk(Ksl, PD, 16 * tb, k0), aM);
+        aP = mma(al, bq, aP);
+        aP = mma(a, frag_rk(Qsl, PD, 16 * tb, k0), aP);
+      }
     }
     const float gr = gam_s[r], br = beta_s[r];
     float Lv[4], Pv[4];
@@ -228,13 +252,18 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   for (int ps = 0; ps < NPASS; ++ps) {
     const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
     const float fk = beta_s[r] * fast_exp(gam_s[r]), fv = beta_s[r];
-    bf16x8 kb, vb;
+    bf16x8 kb, kl, vb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      kb[e] = to_bf16(kn_r[ps][e] * fk);
+      const float x = kn_r[ps][e] * fk;
+      kb[e] = to_bf16(x);
+      kl[e] = to_bf16(x - float(kb[e]));
       vb[e] = to_bf16(v_r[ps][e] * fv);
     }
-    if constexpr (kMat) *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
+    if constexpr (kMat) {
+      *reinterpret_cast<bf16x8*>(Ks + r * PD + c0) = kb;
+      *reinterpret_cast<bf16x8*>(Ksl + r * PD + c0) = kl;
+    }
     *reinterpret_cast<bf16x8*>(Vs + r * PD + c0) = vb;
   }
 
@@ -285,10 +314,15 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   for (int it = 0; it < C * C / 8 / kT; ++it) {
     const int idx = tid + kT * it, row = idx / 8, c8 = (idx % 8) * 8;
     const bool on = (c8 >> 4) <= (row >> 4);
-    bf16x8 v;
+    bf16x8 v, vl;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = to_bf16(on ? Xf[row * PL + c8 + e] : 0.f);
+    for (int e = 0; e < 8; ++e) {
+      const float x = on ? Xf[row * PL + c8 + e] : 0.f;
+      v[e] = to_bf16(x);
+      vl[e] = to_bf16(x - float(v[e]));
+    }
     *reinterpret_cast<bf16x8*>(As + row * PC + c8) = v;
+    if constexpr (kMat) *reinterpret_cast<bf16x8*>(Asl + row * PC + c8) = vl;
     *reinterpret_cast<bf16x8*>(p.A + (ch * C + row) * C + c8) = v;
   }
   __syncthreads();
@@ -307,7 +341,12 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
 #pragma unroll
       for (int k0 = 0; k0 < C; k0 += 32) {
         const bf16x8 b = frag_rk(As, PC, 16 * rb, k0);  // B[s][r] = A[r][s]
-        if constexpr (kMat) aW = mma(frag_kc(Ks, PD, 16 * jb, k0), b, aW);
+        if constexpr (kMat) {
+          const bf16x8 kf = frag_kc(Ks, PD, 16 * jb, k0);
+          aW = mma(kf, b, aW);
+          aW = mma(frag_kc(Ksl, PD, 16 * jb, k0), b, aW);
+          aW = mma(kf, frag_rk(Asl, PC, 16 * rb, k0), aW);
+        }
         aU = mma(frag_kc(Vs, PD, 16 * jb, k0), b, aU);
       }
       const int j0 = 16 * jb + 4 * (l >> 4);
