@@ -1174,8 +1174,12 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
       const float xg = x_r[i] + bias;
       float dx;
       if (p.gate_fn) {
-        const float sz = sigmoidf(ea * xg);
-        dx = acc * p.gate_scale * sz * (1.f - sz) * ea;
+        // sigma'(z) = sigma(z) sigma(-z) = t / (1 + t)^2 with t = e^-|z|: no
+        // cancellation where sigma saturates (1 - sigma(z) in fp32 loses the
+        // relative accuracy of sigma' there, and dA_log sums these terms with
+        // strong cancellation)
+        const float t = fast_exp(-fabsf(ea * xg));
+        dx = acc * p.gate_scale * (t / ((1.f + t) * (1.f + t))) * ea;
         pa += dx * xg;
       } else {
         dx = acc * (-ea * sigmoidf(xg));
