@@ -46,6 +46,23 @@ CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 #   traffic:   HBM bytes, FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB device copy
 #   mfma_flop: SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (bf16 MFMA FLOPs)
 MEASURED = {
+    ("gdn_bf16_t32768_h16_d128", "prep", "26b887273135"): {'traffic': 716000000, 'mfma_flop': 19330000000},
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "26b887273135"): {'traffic': 1690000000, 'mfma_flop': 197570000000},
+    ("gdn_bf16_t32768_h16_d128", "grads", "26b887273135"): {'traffic': 2131000000, 'mfma_flop': 120260000000},
+    ("kda_bf16_t32768_h16_d128", "prep", "26b887273135"): {'traffic': 1841000000, 'mfma_flop': 53690000000},
+    ("kda_bf16_t32768_h16_d128", "chain_both", "26b887273135"): {'traffic': 2963000000, 'mfma_flop': 128850000000},
+    ("kda_bf16_t32768_h16_d128", "grads", "26b887273135"): {'traffic': 3139000000, 'mfma_flop': 188980000000},
+    ("kda_bf16_t32768_h16_d128", "finish", "26b887273135"): {'traffic': 4000000},
+    ("gdn_bf16_t32768_h32_d128", "prep", "26b887273135"): {'traffic': 1446000000, 'mfma_flop': 38650000000},
+    ("gdn_bf16_t32768_h32_d128", "chain_both", "26b887273135"): {'traffic': 3818000000, 'mfma_flop': 395140000000},
+    ("gdn_bf16_t32768_h32_d128", "grads", "26b887273135"): {'traffic': 4540000000, 'mfma_flop': 240520000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "prep", "26b887273135"): {'traffic': 1003000000, 'mfma_flop': 38650000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "chain_both", "26b887273135"): {'traffic': 2831000000, 'mfma_flop': 395140000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "grads", "26b887273135"): {'traffic': 3964000000, 'mfma_flop': 240520000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "finish", "26b887273135"): {'traffic': 672000000},
+    ("gdn_bf16_t32768_h2_d128", "prep", "26b887273135"): {'traffic': 86000000, 'mfma_flop': 2420000000},
+    ("gdn_bf16_t32768_h2_d128", "chain_both", "26b887273135"): {'traffic': 321000000, 'mfma_flop': 60800000000},
+    ("gdn_bf16_t32768_h2_d128", "grads", "26b887273135"): {'traffic': 245000000, 'mfma_flop': 15030000000},
 }
 
 
@@ -189,11 +206,13 @@ def cpu_baseline(inp, tokens: int, backward: bool = True):
     oracle.run(sub, nthreads=threads, backward=backward)
     dt = time.perf_counter() - t0
     nproc, usable, model = host_cpu()
+    # the oracle's threads take one (sequence, head) each: no more of them work than there are pairs
+    used = min(threads, len(sub["lengths"]) * inp["H"])
     what = "token recurrence + adjoint" if backward else "token recurrence (forward only)"
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
             "seconds": round(dt, 3), "nproc": nproc, "cpus_usable": usable, "cpu_model": model,
             "sample": f"first {tokens} of {inp['T']} tokens, all {inp['H']} heads of the same workload; "
-                      f"float64 {what}, {threads} threads over (sequence, head)"}
+                      f"float64 {what}, {used} threads over (sequence, head)"}
 
 
 def roofline(inp, workload: str, name: str, ms: float) -> Dict:

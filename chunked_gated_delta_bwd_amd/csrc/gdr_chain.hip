@@ -683,8 +683,8 @@ __device__ __forceinline__ ChainJob job_of(const ChainJob (&jobs)[NSL], int sv) 
   }
 }
 
-// TWO (per-channel gate): the kernel that runs the segments with weak chunks,
-// whose steps take Khat in two parts in the state update
+// TWO (per-channel gate): the form for segments with weak chunks, whose steps take
+// Khat in two parts in the state update where the chunk is weak
 template <int D, typename TIO, int GATE, int NSL, bool TWO = false>
 __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, int h, int sl,
                                           const ChainJob (&jobs)[NSL]) {
@@ -880,19 +880,19 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
   }
 }
 
-// Raw mode: reverse steps of weak chunks (kTwoPartDecay) take the operands dS (in
-// Khat dS^T), dU (in A^T dU) and Y (in k^T Y) in two bf16 parts.  A step's
-// rounding error is proportional to e^GamC (Khat^T W is), and the next steps damp
-// it by their own decay; with little decay it accumulates over the whole sequence
-// (float64 model of the state-gradient recursion with each rounding switched on
-// alone: at e^GamC = 1 each of the three gives 8e-4 relative error in dh0 over
-// four chunks, 1.5e-3 together; at 1/16 all of them 5e-4).
+// Raw mode: the reverse steps two_part_last() picks take the operands dS (in Khat
+// dS^T), dU (in A^T dU) and Y (in k^T Y) in two bf16 parts.  A step's rounding
+// error is proportional to e^GamC (Khat^T W is), and the earlier chunks damp it by
+// their own decays on its way to dh0; with little decay it accumulates over the
+// whole sequence (float64 model of the state-gradient recursion with each
+// rounding switched on alone: at e^GamC = 1 each of the three gives 8e-4 relative
+// error in dh0 over four chunks, 1.5e-3 together; at 1/16 all of them 5e-4).
 
 // TWO: the kernel that runs the segments with weakly decaying chunks (their steps
 // take two-part operands; the other steps the common ones)
 template <int D, typename TIO, int GATE, int NSL, bool TWO>
 __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, int h, int sl,
-                                          const ChainJob (&jobs)[NSL]) {
+                                          const ChainJob (&jobs)[NSL], int two_last) {
   using Dm = Dims<D>;
   using Cf = ChainCfg<D, TIO, GATE, NSL>;
   constexpr int NJW = Dm::NJW;
@@ -937,7 +937,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       char* dUt = dUbuf(sv, k);
       char* dUlo = dUt + (Cf::bdUl - Cf::bdU);
       // a weakly decaying chunk: two-part operands (uniform over the workgroup)
-      const bool two = TWO && uniform_f(reinterpret_cast<const float*>(sl_k + Cf::sDec)[0]) >= kTwoPartDecay;
+      const bool two = TWO && chunk(k) <= two_last;
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int j = 16 * (w * NJW + x) + 4 * g;
@@ -1191,33 +1191,59 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
   }
 }
 
+// Scalar gate, reverse role: a step's rounding reaches the segment's end state
+// (dh0 for a sequence's first segment) damped by the decays of the chunks before
+// it, so the steps that take two-part operands are those of the chunks whose
+// decay from the segment's start, e^(sum of GamC up to and including the chunk),
+// is at least kTwoPartDecay: the segment's first chunks (GamC <= 0).  Returns the
+// global index of the last of them, or -1.  Every wave scans the chunk decays
+// itself (a wave-wide prefix sum of their logarithms): a uniform answer with no
+// barrier.
+__device__ __forceinline__ int two_part_last(const Params& p, const SeqEntry& se, int h) {
+  const int l = lane_id();
+  const float thr = logf(kTwoPartDecay);
+  float carry = 0.f;
+  int last = -1;
+  for (int b = 0; b < se.nchunks; b += 64) {
+    const int i = b + l;
+    const float e = i < se.nchunks ? p.edec[(int64_t(h) * p.NC + se.c0 + i) * 4] : 0.f;
+    float x = e > 0.f ? logf(e) : -INFINITY;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(x, o, 64);
+      if (l >= o) x += y;
+    }
+    x += carry;
+    const uint64_t m = __ballot(x >= thr);
+    if (m) last = se.c0 + b + 63 - __clzll(m);
+    carry = __shfl(x, 63, 64);
+    if (!(carry >= thr)) break;   // the sums only decrease from here
+  }
+  return __builtin_amdgcn_readfirstlane(last);
+}
+
+// Per-channel gate, forward role: whether segment se has a weak chunk before its
+// last one (the last step's rounding reaches only the end state, through one
+// step: it does not accumulate).  Every wave reads the prologue's flags itself.
+__device__ __forceinline__ bool weak_segment(const Params& p, const SeqEntry& se, int h) {
+  int f = 0;
+  for (int i = lane_id(); i < se.nchunks - 1; i += 64) f |= p.weak[int64_t(h) * p.NC + se.c0 + i];
+  return __any(f);
+}
+
 // blockIdx -> (one (segment, head), slice): the slices of one (segment, head)
 // share its chunk tiles, so they are placed on the same XCD (workgroups are
 // dealt round-robin over the 8 XCDs).  The final pass has D / 16 slices per
 // (segment, head), the state rows; the local pass twice that many, the state
 // rows and then the transfer-product rows; a workgroup takes NSL consecutive slices.
-// Whether segment se has a weak chunk (kTwoPartDecay); every wave reads the chunk
-// decays (scalar gate) or flags (per-channel gate) itself: a uniform answer with
-// no barrier
-template <int GATE>
-__device__ __forceinline__ bool weak_segment(const Params& p, const SeqEntry& se, int h) {
-  int f = 0;
-  for (int i = lane_id(); i < se.nchunks; i += 64) {
-    const int64_t ch = int64_t(h) * p.NC + se.c0 + i;
-    if constexpr (GATE == 0) f |= p.edec[ch * 4] >= kTwoPartDecay;
-    else f |= p.weak[ch];
-  }
-  return __any(f);
-}
-
-// TWO: the segments weak_segment() picks, in the role whose steps take two-part
-// operands for them (raw mode: the reverse role; per-channel gate: the forward
-// role); the common kernel leaves them out of that role
+// TWO (raw mode): the reverse role of the segments two_part_last() picks (the
+// common kernel leaves them out).  The per-channel gate's forward role takes its
+// two-part form in the common kernel, for the segments weak_segment() picks.
 template <int D, typename TIO, int GATE, int NSL, bool TWO = false>
 __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chain(const Params p, int mode, int nb_role,
                                                                                   int pass) {
   using Cf = ChainCfg<D, TIO, GATE, NSL>;
-  static_assert(!TWO || Cf::RAW || Cf::SPLIT, "two-part steps: raw mode or the per-channel gate");
+  static_assert(!TWO || Cf::RAW, "a kernel of two-part steps: raw mode");
   __shared__ __attribute__((aligned(1024))) char smem[ChainCfg<D, TIO, GATE, NSL>::bytes];
   int b = blockIdx.x;
   int role;
@@ -1268,8 +1294,13 @@ __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chai
   // only segments that a later one (in the role's order) starts from, and the
   // transfer product only where the segment does not start from h0 / dht
   if (pass == kPassLocal && (last || (xfer && first))) return;
-  if constexpr (Cf::RAW || Cf::SPLIT)
-    if (role == (Cf::RAW ? 1 : 0) && weak_segment<GATE>(p, se, h) != TWO) return;
+  int two_last = -1;   // raw mode, reverse role: the last chunk of two-part steps
+  if constexpr (Cf::RAW) {
+    if (role == 1) {
+      two_last = two_part_last(p, se, h);
+      if ((two_last >= 0) != TWO) return;
+    }
+  }
   ChainJob jobs[NSL];
 #pragma unroll
   for (int i = 0; i < NSL; ++i) {
@@ -1289,15 +1320,16 @@ __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chai
     }
   }
   if constexpr (TWO) {
-    if constexpr (Cf::RAW)
-      chain_bwd<D, TIO, GATE, NSL, true>(p, smem, si, h, sl, jobs);
-    else
-      chain_fwd<D, TIO, GATE, NSL, true>(p, smem, si, h, sl, jobs);
+    chain_bwd<D, TIO, GATE, NSL, true>(p, smem, si, h, sl, jobs, two_last);
   } else {
-    if (role == 0)
-      chain_fwd<D, TIO, GATE, NSL>(p, smem, si, h, sl, jobs);
-    else
-      chain_bwd<D, TIO, GATE, NSL, false>(p, smem, si, h, sl, jobs);
+    if (role == 0) {
+      if (Cf::SPLIT && weak_segment(p, se, h))
+        chain_fwd<D, TIO, GATE, NSL, Cf::SPLIT>(p, smem, si, h, sl, jobs);
+      else
+        chain_fwd<D, TIO, GATE, NSL>(p, smem, si, h, sl, jobs);
+    } else {
+      chain_bwd<D, TIO, GATE, NSL, false>(p, smem, si, h, sl, jobs, -1);
+    }
   }
 }
 
@@ -1401,9 +1433,6 @@ void run_chain(const Params& p, int mode, int pass, hipStream_t s) {
     return;
   }
   launch_nsl<D, TIO, GATE, 1>(p, mode, pass, s);
-  // per-channel gate: the forward role of the segments with weak chunks
-  if constexpr (ChainCfg<D, TIO, GATE>::SPLIT)
-    if (mode != kChainBwd) launch_nsl<D, TIO, GATE, 1, true>(p, kChainFwd, pass, s);
 }
 }  // namespace
 

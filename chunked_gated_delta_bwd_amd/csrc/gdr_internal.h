@@ -11,12 +11,12 @@
 namespace gdr {
 
 constexpr int kChunk = 64;     // tokens per chunk
-// Chunks whose decay e^GamC (the scalar gate's, or the per-channel gate's largest
-// over the channels) is at least this are "weak": a recursion step's bf16 rounding
-// error is proportional to that decay, and with little decay the following steps
-// do not damp it.  Their steps take some operands in two bf16 parts (x = hi + lo):
-// the scalar gate's reverse steps dS, dU and Y, the per-channel gate's forward
-// steps Khat.
+// A recursion step's bf16 rounding error is proportional to the chunk's decay
+// e^GamC, and with little decay the following steps do not damp it.  Steps whose
+// error is damped by less than this take some operands in two bf16 parts (x = hi
+// + lo): the scalar gate's reverse steps dS, dU and Y where the decay from the
+// segment's start to the chunk's end is at least this, the per-channel gate's
+// forward steps Khat where some channel's e^GamC is (a "weak" chunk).
 constexpr float kTwoPartDecay = 1.f / 16;
 constexpr int kThreads = 256;  // threads per workgroup in every kernel (4 wave64s)
 
