@@ -32,6 +32,7 @@
 
 #include "gdr_device.h"
 #include "gdr_internal.h"
+#include "gdr_lds.h"
 
 namespace gdr {
 
@@ -533,6 +534,40 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
 // and the operands of the pairwise products are split likewise.
 // the gradient kernel runs eight waves (two per SIMD: phases alternate between them)
 constexpr int kKdaGradThreads = 2 * kThreads;
+// one workgroup per CU: the workgroup dealt this many places later runs on the
+// same XCD (workgroups go round-robin over the 8 XCDs) at about the time this one
+// ends
+constexpr int kKdaGradAhead = 256;
+
+// L2 prefetch of the first loads of the gradient workgroup with linear id L (dU^T,
+// U^T high and low, A, and the dO and v rows; rows past the end clamped): one
+// 4-byte direct-to-LDS load per 64-byte sector into a sink that is never read
+template <int D>
+__device__ __forceinline__ void kda_grads_prefetch(const Params& p, int L, char* sink) {
+  constexpr int SR = D * 2 / 64;                     // sectors per bf16 token row
+  constexpr int NU = D * C * 2 / 64, NA = C * C * 2 / 64, NR = C * SR;
+  constexpr int NTOT = 3 * NU + NA + 2 * NR;
+  int c, h;
+  chunk_head_at(p, L, c, h);
+  const ChunkEntry ce = p.ctab[c];
+  const int64_t ch = int64_t(h) * p.NC + c;
+  const char* tiles[3] = {reinterpret_cast<const char*>(p.dU + ch * D * C), reinterpret_cast<const char*>(p.U + ch * D * C),
+                          reinterpret_cast<const char*>(p.Ulo + ch * D * C)};
+  const char* A = reinterpret_cast<const char*>(p.A + ch * C * C);
+  for (int u = threadIdx.x; u < NTOT; u += blockDim.x) {
+    const char* a;
+    if (u < 3 * NU) {
+      a = (u < NU ? tiles[0] : u < 2 * NU ? tiles[1] : tiles[2]) + 64 * (u % NU);
+    } else if (u < 3 * NU + NA) {
+      a = A + 64 * (u - 3 * NU);
+    } else {
+      const int i = u - 3 * NU - NA, k = i % NR, row = min(k / SR, ce.len - 1);
+      const void* base = i < NR ? p.dO : p.v;
+      a = reinterpret_cast<const char*>(base) + tok(ce.t_start + row, p.H, h) * D * 2 + 64 * (k % SR);
+    }
+    dma4(a, sink);
+  }
+}
 
 template <int D>
 struct KdaGradSmem {
@@ -572,6 +607,9 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
   constexpr int kTailFloats = 2 * NPART * D + kT / 64 + 4 * C + C + D;
   constexpr bool kTailInY = Sm::y_tail >= kTailFloats * 4;
   __shared__ __attribute__((aligned(16))) float TX[kTailInY ? 4 : kTailFloats];
+  // bf16 inputs: the sink of the successor's L2 prefetch
+  constexpr bool kPf = !kLo;
+  __shared__ __attribute__((aligned(256))) char pf_sink[kPf ? 256 : 4];
 
   int c, h;
   chunk_head(p, c, h);
@@ -875,6 +913,14 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
     *reinterpret_cast<float4*>(Gs + rr * PG + c4) = g_r[i];
   }
   __syncthreads();
+
+  // the successor's first loads into this XCD's L2 (waited for at the end); phase
+  // 4 is long enough for them to land before the tail's register loads are waited
+  // for (their waits would take the prefetch along)
+  if constexpr (kPf) {
+    if (const int L = blockIdx.x + p.NC * blockIdx.y + kKdaGradAhead; L < p.NC * p.H)
+      kda_grads_prefetch<D>(p, L, pf_sink);
+  }
 
   // ---- phase 4: pairwise terms ----
   //   X1_rc = sum_{s<r} dM_rs kn_sc E_rsc     -> dkn_r, dGamma_r (+ kn_r X1)
@@ -1205,6 +1251,7 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
     for (int x = 0; x < kT / 64; ++x) sa += pa_s[x];
     p.pdA[ch] = sa;
   }
+  if constexpr (kPf) wait_vm<0>();   // the prefetch's direct-to-LDS loads land before the LDS is released
 }
 
 // dA_log[h] and ddt_bias[h][:] from the per-chunk partials, in a fixed order:
