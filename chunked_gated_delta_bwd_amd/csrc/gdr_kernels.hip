@@ -134,8 +134,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
     for (int e = 0; e < 8; ++e) {
       kn_r[ps][e] = kv[e] * rk;
       if constexpr (kMat) qn_r[ps][e] = qv[e] * rq;
-      qb[e] = to_bf16(qv[e] * rq);
-      kb[e] = to_bf16(kn_r[ps][e]);
+      // bf16 inputs: the raw rows (exact in bf16) for M and P, whose products
+      // take the row norms in fp32 afterwards; fp32 inputs: qn, kn in two parts
+      qb[e] = to_bf16(kMat ? qv[e] * rq : qv[e]);
+      kb[e] = to_bf16(kMat ? kn_r[ps][e] : kv[e]);
       if constexpr (kMat) {
         ql[e] = to_bf16(qn_r[ps][e] - float(qb[e]));
         kl[e] = to_bf16(kn_r[ps][e] - float(kb[e]));
@@ -223,14 +225,17 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
       }
     }
     const float gr = gam_s[r], br = beta_s[r];
+    // bf16 inputs: the row norms of the raw-row products
+    const float fm = kMat ? 1.f : rk_s[r], fp = kMat ? 1.f : rq_s[r];
     float Lv[4], Pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = s0 + i;
       // Gamma is non-increasing, so the exponent is <= 0 wherever it is used
       const float E = fast_exp(fminf(gr - gam_s[s], 0.f));
-      Pv[i] = r >= s ? p.scale * aP[i] * E : 0.f;
-      Lv[i] = r > s ? br * aM[i] * E : 0.f;
+      const float fs = kMat ? 1.f : rk_s[s];
+      Pv[i] = r >= s ? p.scale * (aP[i] * (fp * fs)) * E : 0.f;
+      Lv[i] = r > s ? br * (aM[i] * (fm * fs)) * E : 0.f;
     }
     if (tile_valid(w, slot)) {
       *reinterpret_cast<float4*>(Lf + r * PL + s0) = make_float4(Lv[0], Lv[1], Lv[2], Lv[3]);
