@@ -11,7 +11,9 @@
 // runs both in one grid.  The fp32 state / state gradient of a slice lives in
 // registers for the whole sequence.
 //
-// Workgroups have nine waves with fixed jobs:
+// Workgroups have nine waves with fixed jobs (thirteen with two V slices a
+// workgroup: compute waves 4-7 for the second slice, the converter and movers
+// after them):
 //   waves 0-3  compute: the MFMA products of one chunk step, two barriers a step;
 //              their results for later kernels (S, U or dS, dU of the chunk) go
 //              to LDS only; for the scalar gate with bf16 inputs they also turn
@@ -53,6 +55,13 @@
 // gate and fp32 inputs take the Khat / Qbar tiles the prologue kernel formed.
 // Qbar^T dO carries the dominant part of dh0, so that product is taken in two
 // bf16 parts (Qbar high + low, or the scaled dO high + low).
+//
+// Where the gate barely decays, a step's bf16 roundings are not damped by the
+// following steps and accumulate over the sequence.  The scalar gate's reverse
+// steps whose error reaches dh0 with little damping then take dS, dU and Y in two
+// parts (a second launch, k_chain<..., TWO = true>, for the segments that have
+// such steps); the per-channel gate's forward steps on chunks with a barely
+// decaying channel take Khat in two parts (the same launch, chain_fwd<..., TWO>).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
