@@ -308,6 +308,20 @@ def test_mixed_small_against_oracle(name, spec):
         _check(inp, got, name)
 
 
+# Many sequences in one pack: the chunk and segment tables are written on the device
+# from batches of 56 sequence entries a launch, so 130 sequences take three batches
+# (and, split, three batches of segment rows); lengths 0 .. 149, every head compared.
+@pytest.mark.parametrize("gate,split", [(0, 1), (1, 1), (0, 3)], ids=["gdn", "kda", "gdn_split3"])
+def test_many_sequences(gate, split):
+    rng = np.random.default_rng(77)
+    lengths = [int(x) for x in rng.integers(0, 150, size=130)]
+    log(f"case many sequences gate {gate} split {split}: {len(lengths)} sequences, {sum(lengths)} tokens")
+    inp = synth.generate(synth.Spec("ms", gate, "bf16", H=3, K=64, V=64, lengths=lengths, h0_std=0.2, dht_std=0.2,
+                                    seed=78))
+    got = gpu_run(inp, seq_split=split)
+    _check(inp, got, f"many_sequences_g{gate}_s{split}")
+
+
 # Scalar gate outside the synthetic recipe (g = -0.1 softplus(N(0, 1))): no decay at all
 # (g = 0: the plain delta rule), weak decay (g = -0.01 a token: e^-0.64 a chunk) and very
 # strong decay (g = -30 per token: e^Gamma underflows to zero inside a chunk, so every
