@@ -12,7 +12,10 @@ alone the same way (median over --stage-iters launches).  The roofline record
 is the dominant kernel's bf16 MFMA fraction (algorithmic FLOPs of the chunked
 method over its event-timed duration, against the 2.5 PFLOP/s dense peak),
 with its HBM fraction beside it and, where rocprofv3 counter runs on the same
-kernel sources exist, the counter-measured MFMA FLOPs and HBM bytes.  The path
+kernel sources exist, the counter-measured MFMA FLOPs and HBM bytes (and every
+kernel's counter-measured MFMA fraction, with the combined fraction of the
+recursions and the gradient kernel), plus the recursions' grid against the CUs
+(the share of the device the reverse role can use).  The path
 record is the roofline fraction of the whole step: the larger of its MFMA and
 HBM floors (476.5 kFLOP and 1,800 B per token-head) over the measured time.
 The float64 CPU oracle is timed on a bounded sample of the same workload (the
@@ -274,6 +277,46 @@ def path_record(inp, ms: float, kernels, workload: str) -> Dict:
     return rec
 
 
+GPU_CUS = 256
+
+
+def counters_per_kernel(workload: str, kernels: Dict, roof: Dict) -> None:
+    """Where counter runs on these kernel sources exist: each kernel's counter-measured
+    bf16 MFMA fraction (MFMA FLOPs issued per launch / its time / bf16 peak), and the
+    combined fraction of the recursions and the gradient kernel."""
+    h = kernel_source_hash()
+    for name, rec in kernels.items():
+        m = MEASURED.get((workload, name, h), {})
+        if m.get("mfma_flop") is not None:
+            rec["mfma_counter_frac"] = round(m["mfma_flop"] / (rec["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    pair = [(MEASURED.get((workload, n, h), {}).get("mfma_flop"), kernels.get(n, {}).get("ms"))
+            for n in ("chain_both", "grads")]
+    if all(f is not None and t for f, t in pair):
+        roof["combined_mfma_counter_frac"] = round(
+            sum(f for f, _ in pair) / (sum(t for _, t in pair) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+
+
+def recursion_grid(inp, seq_split: int) -> Dict:
+    """The recursions' grid against the CUs (one recursion workgroup fits a CU): the
+    reverse role alone can use at most this share of the device (a ceiling on its
+    MFMA fraction, whatever its per-CU efficiency).  Unsplit sequences only."""
+    H, D = inp["H"], inp["K"]
+    segs = len([L for L in inp["lengths"] if L > 0]) if inp["N"] != inp["B"] else inp["B"]
+    raw = inp["gate"] == 0 and inp["dtype"] == "bf16"
+    # (the launch pads the (sequence, head) pairs to a multiple of 8, one per XCD;
+    # two slices a workgroup when the padded grid of both roles exceeds the CUs)
+    per_role = ((segs * H + 7) // 8) * 8 * (D // 16)
+    nsl = 2 if raw and 2 * per_role > GPU_CUS else 1
+    wgs = segs * H * (D // 16) // nsl   # workgroups with work
+    rec = {"workgroups_per_role": wgs, "slices_per_workgroup": nsl,
+           "reverse_role_cu_share": round(min(1.0, wgs / GPU_CUS), 4)}
+    # the library splits sequences (its own choice) only when both roles together
+    # leave compute units idle; the figures above are for the unsplit grid
+    if seq_split >= 2 or (seq_split == 0 and 2 * H * (D // 16) * segs < GPU_CUS):
+        rec["split"] = True
+    return rec
+
+
 def kernel_record(inp, name: str, t: float) -> Dict:
     flops, nbytes = algorithmic_work(inp, name)
     return {"ms": round(t, 4),
@@ -358,6 +401,8 @@ def main() -> int:
         kernels[name] = kernel_record(inp, name, median(time_calls(fn, args.stage_iters)))
     dom = max(path, key=lambda n: kernels[n]["ms"])
     roof = roofline(inp, args.workload, dom, kernels[dom]["ms"])
+    counters_per_kernel(args.workload, kernels, roof)
+    roof["recursion_grid"] = recursion_grid(inp, args.seq_split)
 
     line = {
         "metric": METRIC,
