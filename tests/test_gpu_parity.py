@@ -53,13 +53,23 @@ def test_chunk_boundary_states():
     compare(got, ref, ("S_chunk", "dS_chunk"), 1e-2, "chunk states")
 
 
-def test_fused_and_split_agree():
-    inp = synth.generate(synth.Spec("a", 0, "bf16", H=4, K=128, V=128, B=1, T=512, h0_std=0.1,
+# gdr_fwd_bwd against gdr_fwd_recompute + gdr_bwd, bit for bit: the recipe, and the
+# two-part steps (the scalar gate without decay: reverse steps in the second launch;
+# the per-channel gate with weak decay: forward steps in the common launch)
+@pytest.mark.parametrize("case", ["recipe", "gdn_no_decay", "kda_weak_decay"])
+def test_fused_and_split_agree(case):
+    gate = 1 if case.startswith("kda") else 0
+    inp = synth.generate(synth.Spec("a", gate, "bf16", H=4, K=128, V=128, B=1, T=512, h0_std=0.1,
                                     dht_std=0.1, seed=35))
+    if case == "gdn_no_decay":
+        inp["g"] = torch.zeros_like(inp["g"])
+    elif case == "kda_weak_decay":
+        inp["A_log"] = torch.full_like(inp["A_log"], -3.0)
     a = gpu_run(inp, mode="fused")
     b = gpu_run(inp, mode="split")
-    for key in TOKEN_GRADS + ("dh0", "ht"):
-        assert (a[key] == b[key]).all(), key
+    for key in TOKEN_GRADS + FP32_GRADS + ("ht",):
+        if key in a:
+            assert (a[key] == b[key]).all(), key
 
 
 def test_repeat_is_deterministic():
