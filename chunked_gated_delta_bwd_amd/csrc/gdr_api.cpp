@@ -191,7 +191,10 @@ gdr::WsLayout layout(const gdr_shape* s, int64_t NC) {
   L.Ulo = take(kda * H * NC * C * V * 2);
   L.Slo = take(kda * H * NC * V * K * 2);
   L.dSlo = take(kda * H * NC * V * K * 2);
-  L.Khl = take(kda * H * NC * C * K * 2);
+  // fp32 inputs, scalar gate, K = kMatTwoPartK: the low tiles of Khat and W
+  const size_t mat2 = (s->gate == GDR_GATE_SCALAR && s->dtype == GDR_F32 && K == size_t(gdr::kMatTwoPartK)) ? 1 : 0;
+  L.Khl = take((kda | mat2) * H * NC * C * K * 2);
+  L.Wl = take(mat2 * H * NC * C * K * 2);
   L.weak = take(kda * H * NC * 4);
   L.xf = take(L.split * 2 * NS * H * 2 * K * K * 4);
   L.sb = take(L.split * 2 * NS * H * K * K * 4);
@@ -361,6 +364,7 @@ gdr::Params make_params(const gdr_shape* s, const gdr::WsLayout& L, const gdr_in
   p.Slo = reinterpret_cast<uint16_t*>(w + L.Slo);
   p.dSlo = reinterpret_cast<uint16_t*>(w + L.dSlo);
   p.Khl = reinterpret_cast<uint16_t*>(w + L.Khl);
+  p.Wl = reinterpret_cast<uint16_t*>(w + L.Wl);
   p.weak = reinterpret_cast<int32_t*>(w + L.weak);
   p.xf = L.split ? reinterpret_cast<float*>(w + L.xf) : nullptr;
   p.sb = L.split ? reinterpret_cast<float*>(w + L.sb) : nullptr;

@@ -58,9 +58,10 @@
 //
 // Where the gate barely decays, a step's bf16 roundings are not damped by the
 // following steps and accumulate over the sequence.  The scalar gate's reverse
-// steps whose error reaches dh0 with little damping then take dS, dU and Y in two
-// parts (a second launch, k_chain<..., TWO = true>, for the segments that have
-// such steps); the per-channel gate's forward steps on chunks with a barely
+// steps whose error reaches dh0 with little damping then take dS, dU and (raw
+// mode) Y in two parts (a second launch, k_chain<..., TWO = true>, for the
+// segments that have such steps; with fp32 inputs where the LDS holds the low
+// parts, D = 64); the per-channel gate's forward steps on chunks with a barely
 // decaying channel take Khat in two parts (the same launch, chain_fwd<..., TWO>).
 #include <hip/hip_runtime.h>
 
@@ -107,24 +108,30 @@ struct ChainCfg {
   static constexpr int bK = 0, bQh = TB, bQl = 2 * TB, bW = 3 * TB;
   static constexpr int bP = MAT ? 4 * TB : 2 * TB;
   static constexpr int bA = 2 * TB + PB;                           // raw mode
-  static constexpr int bufB = MAT ? 4 * TB + PB : 2 * TB + 2 * PB;
+  // The reverse steps of weakly decaying chunks take dS and dU^T in two bf16
+  // parts: in raw mode always; with materialised tiles (fp32 inputs, scalar gate)
+  // at kMatTwoPartK-wide heads, where Khat and W come in two parts as well (their
+  // low tiles, set A and set B, loaded by the two-part kernel only)
+  static constexpr bool TWOM = LO && GATE == 0 && D == kMatTwoPartK;
+  static constexpr bool LOWB = RAW || TWOM;
+  static constexpr int bKl = 4 * TB + PB, bWl = 5 * TB + PB;       // TWOM
+  static constexpr int bufB = MAT ? 4 * TB + PB + (TWOM ? 2 * TB : 0) : 2 * TB + 2 * PB;
   // per-slice parts: slice s, buffer b at X + (2 s + b) XB
   static constexpr int bX1 = 2 * bufB;                             // LO: dO high part
   static constexpr int bX2 = bX1 + (LO ? 2 * XB : 0);              // RAW: fq dO high; LO: dO low
   static constexpr int bX3 = bX2 + ((RAW || LO) ? 2 * NSL * XB : 0);   // RAW: fq dO low
   static constexpr int bSlot = bX3 + (RAW ? 2 * NSL * XB : 0);
   static constexpr int bdS = bSlot + 3 * SLOT;                     // 16 x D state-gradient slice, each slice
-  // raw mode: low parts of the dS slices and of the dU^T buffers for the steps of
-  // weakly decaying chunks (two-part operands), each a fixed distance above its
-  // high part (one lane address serves both)
-  static constexpr int bdSl = bdS + NSL * 16 * D * 2;
   static constexpr int dUB = 16 * C * 2;
-  static constexpr int bdU = bdSl + (RAW ? NSL * 16 * D * 2 : 0);  // 16 x 64: dU^T, each slice
+  // the low parts of the dS slices and of the dU^T buffers, each a fixed distance
+  // above its high part (one lane address serves both)
+  static constexpr int bdSl = bdS + NSL * 16 * D * 2;
+  static constexpr int bdU = bdSl + (LOWB ? NSL * 16 * D * 2 : 0);  // 16 x 64: dU^T, each slice
   // dU^T in two buffers (step parity) where LDS allows: the converter then stores
   // it during the next step instead of holding up the first barrier
-  static constexpr int NDU = bdU + (RAW ? 4 : 2) * NSL * dUB + 256 <= 160 * 1024 ? 2 : 1;
+  static constexpr int NDU = bdU + (LOWB ? 4 : 2) * NSL * dUB + 256 <= 160 * 1024 ? 2 : 1;
   static constexpr int bdUl = bdU + NSL * NDU * dUB;
-  static constexpr int bPF = bdUl + (RAW ? NSL * NDU * dUB : 0);   // 256 B sink of the L2 prefetches
+  static constexpr int bPF = bdUl + (LOWB ? NSL * NDU * dUB : 0);  // 256 B sink of the L2 prefetches
   static constexpr int bEnd = bPF + 256;
   // forward role
   // forward role: materialised tiles W, Khat; raw mode A (in W's place) and k,
@@ -151,11 +158,13 @@ struct ChainCfg {
   static constexpr int nSb = 1;
   static constexpr int nSf = 1;
   static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 * NJ : NJ + 2) + nSb;
+  // the two-part kernel's counts (TWOM: the low tiles of Khat and W too)
+  static constexpr int bwdA2 = bwdA + (TWOM ? NJ : 0), bwdB2 = bwdB + (TWOM ? NJ : 0);
   // L2 prefetch distance in chunk steps (one prefetch load per mover wave per step)
   static constexpr int PFD = 5;
   static constexpr int fwdA = (MAT ? NJ : 2) + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
   static_assert(bytes <= 160 * 1024, "LDS budget");
-  static_assert(2 * bwdA + bwdB + (PFD - 2) * NPF < 64 && 2 * fwdA + fwdB + (PFD - 2) * NPF < 64, "vmcnt range");
+  static_assert(2 * bwdA2 + bwdB2 + (PFD - 2) * NPF < 64 && 2 * fwdA + fwdB + (PFD - 2) * NPF < 64, "vmcnt range");
 };
 
 // The segment entry of a workgroup, read once into scalar registers (left in
@@ -330,8 +339,9 @@ __device__ __forceinline__ void wait_mover(bool has_small) {
 }
 
 // reverse role: set A (Khat, P; raw mode q, P), set B (Qbar high + low, W; raw
-// mode k, A)
-template <int D, typename TIO, int GATE>
+// mode k, A); TWO with materialised tiles: the low tiles of Khat (set A) and W
+// (set B) as well
+template <int D, typename TIO, int GATE, bool TWO = false>
 __device__ __forceinline__ void move_bwd_a(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            char* buf, int mw) {
   using Cf = ChainCfg<D, TIO, GATE>;
@@ -341,9 +351,10 @@ __device__ __forceinline__ void move_bwd_a(const MoverLane<D>& ml, const Params&
   else
     move_tile<D>(ml, p.Kh + cg.ch * C * D, buf + Cf::bK, mw);
   move_p<D>(ml, p.P + cg.ch * C * C, buf + Cf::bP, mw);
+  if constexpr (TWO && Cf::TWOM) move_tile<D>(ml, p.Khl + cg.ch * C * D, buf + Cf::bKl, mw);
 }
 
-template <int D, typename TIO, int GATE>
+template <int D, typename TIO, int GATE, bool TWO = false>
 __device__ __forceinline__ void move_bwd_b(const MoverLane<D>& ml, const Params& p, const SeqEntry& se, int h, int c,
                                            char* buf, int mw) {
   using Cf = ChainCfg<D, TIO, GATE>;
@@ -355,6 +366,7 @@ __device__ __forceinline__ void move_bwd_b(const MoverLane<D>& ml, const Params&
     move_tile<D>(ml, p.Qh + cg.ch * C * D, buf + Cf::bQh, mw);
     move_tile<D>(ml, p.Ql + cg.ch * C * D, buf + Cf::bQl, mw);
     move_tile<D>(ml, p.W + cg.ch * C * D, buf + Cf::bW, mw);
+    if constexpr (TWO && Cf::TWOM) move_tile<D>(ml, p.Wl + cg.ch * C * D, buf + Cf::bWl, mw);
   }
 }
 
@@ -896,6 +908,8 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
 // whole sequence (float64 model of the state-gradient recursion with each
 // rounding switched on alone: at e^GamC = 1 each of the three gives 8e-4 relative
 // error in dh0 over four chunks, 1.5e-3 together; at 1/16 all of them 5e-4).
+// With materialised tiles (fp32 inputs, D = 64) the same steps take dS (in Khat
+// dS^T) and dU (in W^T dU) in two parts.
 
 // TWO: the kernel that runs the segments with weakly decaying chunks (their steps
 // take two-part operands; the other steps the common ones)
@@ -976,8 +990,10 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += 32) {
           const bf16x8 kf = frag_rk_s<D>(Bb + Cf::bK, 16 * w, k0);
-          ak = mma(kf, frag_rk_s<D>(dSl, 0, k0), ak);
+          const bf16x8 sh = frag_rk_s<D>(dSl, 0, k0);
+          ak = mma(kf, sh, ak);
           ak = mma(kf, frag_rk_s<D>(dSlo, 0, k0), ak);
+          if constexpr (Cf::TWOM) ak = mma(frag_rk_s<D>(Bb + Cf::bKl, 16 * w, k0), sh, ak);
         }
       } else {
 #pragma unroll
@@ -997,22 +1013,36 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       // not depend on dU and are issued before the barrier
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
       f32x4 an[NJW];
+      // the dO fragments (B operands: raw mode fq dO high, low; else dO high and,
+      // for fp32 inputs, low) serve every x: with one slice a workgroup they are
+      // read once (with two, the registers are not there: re-read per x)
+      constexpr int NK = C / 32;
+      constexpr bool HOIST = NSL == 1;
+      const char* XH = Cf::RAW ? X2 : X1;
+      const char* XL = Cf::RAW ? X3 : X2;
+      bf16x8 xh[NK], xl[NK];
+      if (HOIST && !job.xfer) {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          xh[kk] = frag_kc_s<16>(XH, 0, 32 * kk);
+          if constexpr (Cf::RAW || Cf::LO) xl[kk] = frag_kc_s<16>(XL, 0, 32 * kk);
+        }
+      }
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
         const int jb = w * NJW + x;
         f32x4 a = acc[x] * decay4<D, GATE>(dec, jb, g);
         if (!job.xfer) {   // transfer rows: dO = 0
 #pragma unroll
-          for (int k0 = 0; k0 < C; k0 += 32) {
-            const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, k0);
+          for (int kk = 0; kk < NK; ++kk) {
+            const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, 32 * kk);
+            const bf16x8 bh = HOIST ? xh[kk] : frag_kc_s<16>(XH, 0, 32 * kk);
+            a = mma(qa, bh, a);
             if constexpr (Cf::RAW) {
-              a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
-              a = mma(qa, frag_kc_s<16>(X3, 0, k0), a);
+              a = mma(qa, HOIST ? xl[kk] : frag_kc_s<16>(XL, 0, 32 * kk), a);
             } else {
-              const bf16x8 bh = frag_kc_s<16>(X1, 0, k0);
-              a = mma(qa, bh, a);
-              a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, k0), bh, a);
-              if constexpr (Cf::LO) a = mma(qa, frag_kc_s<16>(X2, 0, k0), a);
+              a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, 32 * kk), bh, a);
+              if constexpr (Cf::LO) a = mma(qa, HOIST ? xl[kk] : frag_kc_s<16>(XL, 0, 32 * kk), a);
             }
           }
         }
@@ -1109,8 +1139,15 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
           const int jb = w * NJW + x;
           f32x4 aw = zero4();
 #pragma unroll
-          for (int k0 = 0; k0 < C; k0 += 32)
-            aw = mma(frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0), frag_rk_s<C, 1>(dUt, 0, k0), aw);
+          for (int k0 = 0; k0 < C; k0 += 32) {
+            const bf16x8 wf = frag_kc_s<D>(Bb + Cf::bW, 16 * jb, k0);
+            const bf16x8 uh = frag_rk_s<C, 1>(dUt, 0, k0);
+            aw = mma(wf, uh, aw);
+            if (TWO && two) {
+              aw = mma(wf, frag_rk_s<C, 1>(dUlo, 0, k0), aw);
+              if constexpr (Cf::TWOM) aw = mma(frag_kc_s<D>(Bb + Cf::bWl, 16 * jb, k0), uh, aw);
+            }
+          }
           acc[x] = an[x] - aw;
         }
       }
@@ -1161,6 +1198,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
   } else {
     if (nck == 0) return;
     constexpr int NPF = Cf::NPF;
+    constexpr int BA = TWO ? Cf::bwdA2 : Cf::bwdA, BB = TWO ? Cf::bwdB2 : Cf::bwdB;
     const int mw = wv - Cf::MOVE0;
     const bool hs = small_loads<D, TIO, GATE, NSL>(mw, true);
     MoverLane<D> ml;
@@ -1174,27 +1212,27 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       for (int i = 0; i < NSL; ++i) prefetch_chunk<D, TIO, GATE, true>(pf[i], ml, p, se, h, c, smem + Cf::bPF);
     };
     move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(0), v0l, slot(0), mw, true);
-    move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
-    move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(0), smem, mw);
+    move_bwd_a<D, TIO, GATE, TWO>(ml, p, se, h, chunk(0), smem, mw);
+    move_bwd_b<D, TIO, GATE, TWO>(ml, p, se, h, chunk(0), smem, mw);
     move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(1), v0l, slot(1), mw, true);
-    move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(1), smem + Cf::bufB, mw);
+    move_bwd_a<D, TIO, GATE, TWO>(ml, p, se, h, chunk(1), smem + Cf::bufB, mw);
     for (int c = 2; c < Cf::PFD; ++c) prefetch(chunk(c));
-    wait_mover<Cf::bwdA + Cf::bwdB + Cf::bwdA + (Cf::PFD - 2) * NPF>(hs);
+    wait_mover<BA + BB + BA + (Cf::PFD - 2) * NPF>(hs);
     chain_barrier();   // B0
     // both sets of chunk 0 and the small data of chunk 1 land before B1 (set B is
     // read in the first window too, and so is the next chunk's small data)
-    wait_vm<Cf::bwdA + (Cf::PFD - 2) * NPF>();
+    wait_vm<BA + (Cf::PFD - 2) * NPF>();
     for (int k = 0; k < nck; ++k) {
       chain_barrier();   // B1
-      move_bwd_b<D, TIO, GATE>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
+      move_bwd_b<D, TIO, GATE, TWO>(ml, p, se, h, chunk(k + 1), smem + ((k + 1) & 1) * Cf::bufB, mw);
       move_small<D, TIO, GATE, NSL>(ml, p, se, h, chunk(k + 2), v0l, slot(k + 2), mw, true);
-      wait_mover<Cf::bwdA + NPF + Cf::bwdB>(hs);
+      wait_mover<BA + NPF + BB>(hs);
       chain_barrier();   // B2
-      move_bwd_a<D, TIO, GATE>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
+      move_bwd_a<D, TIO, GATE, TWO>(ml, p, se, h, chunk(k + 2), smem + (k & 1) * Cf::bufB, mw);
       prefetch(chunk(k + Cf::PFD));
       // set B of chunk k + 1 and the small data of chunk k + 2 land before the
       // next B1: only set A of chunk k + 2 and the prefetch stay in flight
-      wait_vm<Cf::bwdA + NPF>();
+      wait_vm<BA + NPF>();
     }
     wait_vm<0>();
   }
@@ -1245,14 +1283,14 @@ __device__ __forceinline__ bool weak_segment(const Params& p, const SeqEntry& se
 // dealt round-robin over the 8 XCDs).  The final pass has D / 16 slices per
 // (segment, head), the state rows; the local pass twice that many, the state
 // rows and then the transfer-product rows; a workgroup takes NSL consecutive slices.
-// TWO (raw mode): the reverse role of the segments two_part_last() picks (the
+// TWO (Cf::LOWB): the reverse role of the segments two_part_last() picks (the
 // common kernel leaves them out).  The per-channel gate's forward role takes its
 // two-part form in the common kernel, for the segments weak_segment() picks.
 template <int D, typename TIO, int GATE, int NSL, bool TWO = false>
 __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chain(const Params p, int mode, int nb_role,
                                                                                   int pass) {
   using Cf = ChainCfg<D, TIO, GATE, NSL>;
-  static_assert(!TWO || Cf::RAW, "a kernel of two-part steps: raw mode");
+  static_assert(!TWO || Cf::LOWB, "a kernel of two-part steps: where the LDS holds the low parts");
   __shared__ __attribute__((aligned(1024))) char smem[ChainCfg<D, TIO, GATE, NSL>::bytes];
   int b = blockIdx.x;
   int role;
@@ -1303,8 +1341,8 @@ __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chai
   // only segments that a later one (in the role's order) starts from, and the
   // transfer product only where the segment does not start from h0 / dht
   if (pass == kPassLocal && (last || (xfer && first))) return;
-  int two_last = -1;   // raw mode, reverse role: the last chunk of two-part steps
-  if constexpr (Cf::RAW) {
+  int two_last = -1;   // reverse role: the last chunk of two-part steps
+  if constexpr (Cf::LOWB) {
     if (role == 1) {
       two_last = two_part_last(p, se, h);
       if ((two_last >= 0) != TWO) return;
@@ -1442,6 +1480,8 @@ void run_chain(const Params& p, int mode, int pass, hipStream_t s) {
     return;
   }
   launch_nsl<D, TIO, GATE, 1>(p, mode, pass, s);
+  if constexpr (ChainCfg<D, TIO, GATE>::TWOM)
+    if (mode != kChainFwd) launch_nsl<D, TIO, GATE, 1, true>(p, kChainBwd, pass, s);
 }
 }  // namespace
 

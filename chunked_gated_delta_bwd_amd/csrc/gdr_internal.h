@@ -18,6 +18,12 @@ constexpr int kChunk = 64;     // tokens per chunk
 // segment's start to the chunk's end is at least this, the per-channel gate's
 // forward steps Khat where some channel's e^GamC is (a "weak" chunk).
 constexpr float kTwoPartDecay = 1.f / 16;
+// With fp32 inputs the scalar gate's recursions take Khat and W as materialised
+// bf16 tiles, whose rounding weighs as much as that of dS and dU there.  At this
+// head size the reverse recursion's two-part steps take them in two parts too,
+// from low tiles the prologue writes (at 128-wide heads the recursion's LDS has
+// no room for them).
+constexpr int kMatTwoPartK = 64;
 constexpr int kThreads = 256;  // threads per workgroup in every kernel (4 wave64s)
 
 // One row per chunk (global chunk index c).
@@ -103,7 +109,9 @@ struct WsLayout {
   size_t Ulo = 0;    // bf16 [H][NC][V][64]
   size_t Slo = 0;    // bf16 [H][NC][V][K]
   size_t dSlo = 0;   // bf16 [H][NC][V][K]
-  size_t Khl = 0;    // bf16 [H][NC][64][K]: Khat's low part, written for weak chunks only
+  size_t Khl = 0;    // bf16 [H][NC][64][K]: Khat's low part (per-channel gate: weak chunks only;
+                     //   fp32 inputs, scalar gate, K = kMatTwoPartK: every chunk)
+  size_t Wl = 0;     // bf16 [H][NC][64][K]: W's low part (fp32 inputs, scalar gate, K = kMatTwoPartK)
   size_t weak = 0;   // int32 [H][NC]: 1 for a weak chunk (see kTwoPartDecay)
   // split sequences only: the first recursion pass's segment-end states and
   // transfer products, and the composed segment boundary states
@@ -142,7 +150,7 @@ struct Params {
   uint16_t* Mk;                                  // per-channel gate only
   float *pdA, *pddt;
   uint16_t *Uplo, *Ulo, *Slo, *dSlo;             // per-channel gate only: low parts
-  uint16_t* Khl;                                 // per-channel gate only, weak chunks only
+  uint16_t *Khl, *Wl;                            // low tiles of Khat and W (see WsLayout)
   int32_t* weak;                                 // per-channel gate only
   float *xf, *sb;                                // split sequences only
 };

@@ -63,6 +63,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
   // fp32 inputs: the recursions take materialised Khat / Qbar tiles (Qbar split
   // into bf16 high and low parts); bf16 inputs use the raw rows and row factors
   constexpr bool kMat = std::is_same<TIO, float>::value;
+  // and at kMatTwoPartK-wide heads the low tiles of Khat and W as well, for the
+  // reverse recursion's two-part steps
+  constexpr bool kMat2 = kMat && D == kMatTwoPartK;
   // fp32 inputs: low bf16 parts of qn, kn (then beta Kbar) and A, so that M, P and
   // W are formed from two-part operands (hi hi + lo hi + hi lo); bf16 inputs' rows
   // are exact in bf16 after the row norm only up to its rounding, which the
@@ -187,16 +190,18 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
     for (int ps = 0; ps < NPASS; ++ps) {
       const int r = ps * RPP + tid / TPR, c0 = (tid % TPR) * 8;
       const float fk = fast_exp(gam_s[C - 1] - gam_s[r]), fq = p.scale * fast_exp(gam_s[r]);
-      bf16x8 kh, qh, ql;
+      bf16x8 kh, kl, qh, ql;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = qn_r[ps][e] * fq;
-        kh[e] = to_bf16(kn_r[ps][e] * fk);
+        const float x = qn_r[ps][e] * fq, y = kn_r[ps][e] * fk;
+        kh[e] = to_bf16(y);
+        kl[e] = to_bf16(y - float(kh[e]));
         qh[e] = to_bf16(x);
         ql[e] = to_bf16(x - float(qh[e]));
       }
       const int64_t o = (ch * C + r) * D + c0;
       *reinterpret_cast<bf16x8*>(p.Kh + o) = kh;
+      if constexpr (kMat2) *reinterpret_cast<bf16x8*>(p.Khl + o) = kl;
       *reinterpret_cast<bf16x8*>(p.Qh + o) = qh;
       *reinterpret_cast<bf16x8*>(p.Ql + o) = ql;
     }
@@ -356,6 +361,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_gdn(const Params p) {
       }
       const int j0 = 16 * jb + 4 * (l >> 4);
       if constexpr (kMat) st_bf16x4(Wst + r * PD + j0, aW[0], aW[1], aW[2], aW[3]);
+      if constexpr (kMat2)   // (fp32 inputs only: stored from the lane, 8 bytes a row)
+        st_bf16x4(p.Wl + (ch * C + r) * D + j0, lo_part(aW[0]), lo_part(aW[1]), lo_part(aW[2]), lo_part(aW[3]));
       st_bf16x4(Ust + r * PD + j0, aU[0], aU[1], aU[2], aU[3]);
     }
   }

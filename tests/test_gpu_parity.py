@@ -136,15 +136,17 @@ def test_kda_small_against_oracle(name, spec, mode):
 # then takes U and Khat in two parts (weak chunks), and all three regimes keep the
 # standard bars (one part each: dA_log 1.7e-3, ddt_bias 1.2e-3 in the weak regime).
 # The H = 17 case runs the same in a grid of more than one workgroup per CU.
-@pytest.mark.parametrize("a_log,H,D", [(-3.0, 2, 128), (-3.0, 17, 128), (-3.0, 3, 64), (2.2, 2, 128), (3.0, 2, 128)],
-                         ids=["weak_decay", "weak_decay_h17", "weak_decay_d64", "mixed_decay", "strong_decay"])
-def test_kda_decay_regimes(a_log, H, D):
-    log(f"case kda decay regime A_log={a_log} H={H} D={D}")
-    inp = synth.generate(synth.Spec("kd", 1, "bf16", H=H, K=D, V=D, lengths=[200, 77], h0_std=0.1,
+@pytest.mark.parametrize("a_log,H,D,dtype", [(-3.0, 2, 128, "bf16"), (-3.0, 17, 128, "bf16"), (-3.0, 3, 64, "bf16"),
+                                              (-3.0, 2, 128, "f32"), (2.2, 2, 128, "bf16"), (3.0, 2, 128, "bf16")],
+                         ids=["weak_decay", "weak_decay_h17", "weak_decay_d64", "weak_decay_f32", "mixed_decay",
+                              "strong_decay"])
+def test_kda_decay_regimes(a_log, H, D, dtype):
+    log(f"case kda decay regime A_log={a_log} H={H} D={D} {dtype}")
+    inp = synth.generate(synth.Spec("kd", 1, dtype, H=H, K=D, V=D, lengths=[200, 77], h0_std=0.1,
                                     dht_std=0.1, seed=47))
     inp["A_log"] = torch.full_like(inp["A_log"], a_log)
     got = gpu_run(inp)
-    _check(inp, got, f"kda_decay_{a_log}_h{H}_d{D}")
+    _check(inp, got, f"kda_decay_{a_log}_h{H}_d{D}_{dtype}")
 
 
 def test_kda_chunk_boundary_states():
@@ -341,16 +343,17 @@ def test_many_sequences(gate, split):
 # run two V slices a workgroup.  With strong decay dg and dh0 are ~1e-13 in the oracle
 # (every path to them carries e^-30 or less), so a relative bar is meaningless there:
 # they are held to an absolute 1e-6 instead; every other output keeps the standard bars.
-@pytest.mark.parametrize("gval,H,D", [(0.0, 2, 128), (-0.01, 2, 128), (0.0, 17, 128), (0.0, 3, 64), (-30.0, 2, 128)],
-                         ids=["no_decay", "weak_decay", "no_decay_h17", "no_decay_d64", "strong_decay"])
-def test_gdn_decay_extremes(gval, H, D):
-    log(f"case gdn decay g={gval} H={H} D={D}")
-    inp = synth.generate(synth.Spec("ge", 0, "bf16", H=H, K=D, V=D, lengths=[200, 77], h0_std=0.1,
+@pytest.mark.parametrize("gval,H,D,dtype", [(0.0, 2, 128, "bf16"), (-0.01, 2, 128, "bf16"), (0.0, 17, 128, "bf16"),
+                                             (0.0, 3, 64, "bf16"), (0.0, 2, 64, "f32"), (-30.0, 2, 128, "bf16")],
+                         ids=["no_decay", "weak_decay", "no_decay_h17", "no_decay_d64", "no_decay_f32", "strong_decay"])
+def test_gdn_decay_extremes(gval, H, D, dtype):
+    log(f"case gdn decay g={gval} H={H} D={D} {dtype}")
+    inp = synth.generate(synth.Spec("ge", 0, dtype, H=H, K=D, V=D, lengths=[200, 77], h0_std=0.1,
                                     dht_std=0.1, seed=48))
     inp["g"] = torch.full_like(inp["g"], gval)
     got = gpu_run(inp)
     if gval > -1.0:
-        _check(inp, got, f"gdn_decay_{gval}_h{H}_d{D}")
+        _check(inp, got, f"gdn_decay_{gval}_h{H}_d{D}_{dtype}")
         return
     ref = oracle.run(inp)
     compare(got, ref, ("dq", "dk", "dv", "db"), TOL_BF16, f"gdn_decay_{gval} grads")
