@@ -49,23 +49,23 @@ CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 #   traffic:   HBM bytes, FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB device copy
 #   mfma_flop: SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (bf16 MFMA FLOPs)
 MEASURED = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "77c09009919e"): {'traffic': 716000000, 'mfma_flop': 19330000000},
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "77c09009919e"): {'traffic': 1690000000, 'mfma_flop': 197570000000},
-    ("gdn_bf16_t32768_h16_d128", "grads", "77c09009919e"): {'traffic': 2124000000, 'mfma_flop': 120260000000},
-    ("kda_bf16_t32768_h16_d128", "prep", "77c09009919e"): {'traffic': 1841000000, 'mfma_flop': 53690000000},
-    ("kda_bf16_t32768_h16_d128", "chain_both", "77c09009919e"): {'traffic': 2968000000, 'mfma_flop': 128850000000},
-    ("kda_bf16_t32768_h16_d128", "grads", "77c09009919e"): {'traffic': 3797000000, 'mfma_flop': 188980000000},
-    ("kda_bf16_t32768_h16_d128", "finish", "77c09009919e"): {'traffic': 4000000},
-    ("gdn_bf16_t32768_h32_d128", "prep", "77c09009919e"): {'traffic': 1447000000, 'mfma_flop': 38650000000},
-    ("gdn_bf16_t32768_h32_d128", "chain_both", "77c09009919e"): {'traffic': 3807000000, 'mfma_flop': 395140000000},
-    ("gdn_bf16_t32768_h32_d128", "grads", "77c09009919e"): {'traffic': 4534000000, 'mfma_flop': 240520000000},
-    ("gdn_gqa4_bf16_t32768_h32_d128", "prep", "77c09009919e"): {'traffic': 1003000000, 'mfma_flop': 38650000000},
-    ("gdn_gqa4_bf16_t32768_h32_d128", "chain_both", "77c09009919e"): {'traffic': 2823000000, 'mfma_flop': 395140000000},
-    ("gdn_gqa4_bf16_t32768_h32_d128", "grads", "77c09009919e"): {'traffic': 3948000000, 'mfma_flop': 240520000000},
-    ("gdn_gqa4_bf16_t32768_h32_d128", "finish", "77c09009919e"): {'traffic': 672000000},
-    ("gdn_bf16_t32768_h2_d128", "prep", "77c09009919e"): {'traffic': 86000000, 'mfma_flop': 2420000000},
-    ("gdn_bf16_t32768_h2_d128", "chain_both", "77c09009919e"): {'traffic': 323000000, 'mfma_flop': 60800000000},
-    ("gdn_bf16_t32768_h2_d128", "grads", "77c09009919e"): {'traffic': 245000000, 'mfma_flop': 15030000000},
+    ("gdn_bf16_t32768_h16_d128", "prep", "2e7e632bfee7"): {'traffic': 716000000, 'mfma_flop': 19330000000},
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "2e7e632bfee7"): {'traffic': 1690000000, 'mfma_flop': 197570000000},
+    ("gdn_bf16_t32768_h16_d128", "grads", "2e7e632bfee7"): {'traffic': 2126000000, 'mfma_flop': 120260000000},
+    ("kda_bf16_t32768_h16_d128", "prep", "2e7e632bfee7"): {'traffic': 1841000000, 'mfma_flop': 53690000000},
+    ("kda_bf16_t32768_h16_d128", "chain_both", "2e7e632bfee7"): {'traffic': 2964000000, 'mfma_flop': 128850000000},
+    ("kda_bf16_t32768_h16_d128", "grads", "2e7e632bfee7"): {'traffic': 3802000000, 'mfma_flop': 188980000000},
+    ("kda_bf16_t32768_h16_d128", "finish", "2e7e632bfee7"): {'traffic': 4000000},
+    ("gdn_bf16_t32768_h32_d128", "prep", "2e7e632bfee7"): {'traffic': 1447000000, 'mfma_flop': 38650000000},
+    ("gdn_bf16_t32768_h32_d128", "chain_both", "2e7e632bfee7"): {'traffic': 3805000000, 'mfma_flop': 395140000000},
+    ("gdn_bf16_t32768_h32_d128", "grads", "2e7e632bfee7"): {'traffic': 4527000000, 'mfma_flop': 240520000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "prep", "2e7e632bfee7"): {'traffic': 1003000000, 'mfma_flop': 38650000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "chain_both", "2e7e632bfee7"): {'traffic': 2824000000, 'mfma_flop': 395140000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "grads", "2e7e632bfee7"): {'traffic': 3954000000, 'mfma_flop': 240520000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "finish", "2e7e632bfee7"): {'traffic': 672000000},
+    ("gdn_bf16_t32768_h2_d128", "prep", "2e7e632bfee7"): {'traffic': 86000000, 'mfma_flop': 2420000000},
+    ("gdn_bf16_t32768_h2_d128", "chain_both", "2e7e632bfee7"): {'traffic': 323000000, 'mfma_flop': 60800000000},
+    ("gdn_bf16_t32768_h2_d128", "grads", "2e7e632bfee7"): {'traffic': 244000000, 'mfma_flop': 15030000000},
 }
 
 
