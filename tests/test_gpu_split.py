@@ -74,10 +74,14 @@ def test_forced_split_against_oracle(name, P, spec, mode):
 # composed boundary state hardly matters.  With weak decay the transfer products
 # carry the boundary state through whole segments: these cases check the
 # composition itself.
-@pytest.mark.parametrize("gate,P", [(0, 4), (0, 16), (1, 5)], ids=["gdn_s4", "gdn_s16", "kda_s5"])
-def test_forced_split_weak_decay(gate, P):
-    log(f"case weak decay gate {gate} split {P}")
-    inp = synth.generate(synth.Spec("sw", gate, "bf16", H=2, K=128, V=128, lengths=[1200, 333, 64], h0_std=0.3,
+# (fp32 inputs at D = 64: the materialised-tile steps with Khat and W in two parts,
+# in both passes)
+@pytest.mark.parametrize("gate,P,dtype,D", [(0, 4, "bf16", 128), (0, 16, "bf16", 128), (1, 5, "bf16", 128),
+                                            (0, 4, "f32", 64)],
+                         ids=["gdn_s4", "gdn_s16", "kda_s5", "gdn_f32_d64_s4"])
+def test_forced_split_weak_decay(gate, P, dtype, D):
+    log(f"case weak decay gate {gate} split {P} {dtype} D={D}")
+    inp = synth.generate(synth.Spec("sw", gate, dtype, H=2, K=D, V=D, lengths=[1200, 333, 64], h0_std=0.3,
                                     dht_std=0.3, seed=411))
     if gate == 0:
         inp["g"] = torch.full_like(inp["g"], -0.002)
