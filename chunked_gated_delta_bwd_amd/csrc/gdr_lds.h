@@ -46,21 +46,38 @@ __device__ __forceinline__ int soff(int r, int c) {
   return prow<W>(r) * (2 * W) + (((c >> 3) ^ swz<W, KIND>(r)) << 4) + ((c & 7) << 1);
 }
 
+// Fragment addresses.  Every fragment read below takes tile-aligned arguments: its
+// first row r0 or column c0 is a multiple of 16, its K offset k0 a multiple of 32.
+// Then the swizzle of each row a lane touches depends on the lane alone (every
+// swz depends on r mod 16 only), and the aligned offsets either add whole rows or
+// flip bits that the lane's own part leaves clear, so (q = lane % 16, g = lane / 16)
+//   soff(r0 + q, k0 + 8g)                    = r0 2W + (rk_lane ^ 2 k0)
+//   soff(k0 + 8g + q/4 (+4), c0 + 4 (q % 4)) = k0 2W + (kc_lane(0 or 4) ^ 2 c0)
+// and likewise for the split K orders.  A read then costs one XOR with a
+// compile-time or wave-uniform value (shared by the reads with the same one)
+// instead of the swizzle arithmetic per read.  The identities hold for every tile
+// width and swizzle kind here (checked exhaustively against soff on the host).
+template <int W, int KIND>
+__device__ __forceinline__ int rk_lane() {
+  const int l = lane_id(), q = l & 15, g = l >> 4;
+  return prow<W>(q) * (2 * W) + ((g ^ swz<W, KIND>(q)) << 4);
+}
+
+// transposed reads: rows 8g + q/4 + d (d = 0, 4), column piece of 4 (q % 4)
+template <int W, int KIND>
+__device__ __forceinline__ int kc_lane(int d) {
+  const int l = lane_id(), q = l & 15, g = l >> 4;
+  const int rl = 8 * g + (q >> 2) + d;
+  return prow<W>(rl) * (2 * W) + 8 * (q & 1) + ((((q >> 1) & 1) ^ swz<W, KIND>(rl)) << 4);
+}
+
 // T[r0 + j][k0 + 8g .. 8g+7] (see frag_rk)
 template <int W, int KIND = 0>
 __device__ __forceinline__ bf16x8 frag_rk_s(const char* T, int r0, int k0) {
-  const int l = lane_id();
-  return *reinterpret_cast<const bf16x8*>(T + soff<W, KIND>(r0 + (l & 15), k0 + 8 * (l >> 4)));
+  return *reinterpret_cast<const bf16x8*>(T + r0 * (2 * W) + (rk_lane<W, KIND>() ^ (2 * k0)));
 }
 
-// T[k0 + 8g .. 8g+7][c0 + j] by transposed reads (see frag_kc)
-template <int W, int KIND = 0>
-__device__ __forceinline__ bf16x8 frag_kc_s(const char* T, int c0, int k0) {
-  const int l = lane_id();
-  const int g = l >> 4, q = l & 15;
-  const int r = k0 + 8 * g + (q >> 2), c = c0 + 4 * (q & 3);
-  const char* p0 = T + soff<W, KIND>(r, c);
-  const char* p1 = T + soff<W, KIND>(r + 4, c);
+__device__ __forceinline__ bf16x8 tr_pair(const char* p0, const char* p1) {
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(p0)));
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(p1)));
   const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
@@ -68,30 +85,44 @@ __device__ __forceinline__ bf16x8 frag_kc_s(const char* T, int c0, int k0) {
   return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// T[k0 + 8g .. 8g+7][c0 + j] by transposed reads (see frag_kc)
+template <int W, int KIND = 0>
+__device__ __forceinline__ bf16x8 frag_kc_s(const char* T, int c0, int k0) {
+  const char* base = T + k0 * (2 * W);
+  return tr_pair(base + (kc_lane<W, KIND>(0) ^ (2 * c0)), base + (kc_lane<W, KIND>(4) ^ (2 * c0)));
+}
+
 // T[m_e][c0 + j] with rows m_e = k0 + 4g + e (e < 4) and k0 + 16 + 4g + e - 4
 // (e >= 4): the K order of an MFMA operand is free as long as both operands
 // share it, and this one matches a B operand assembled from the accumulators
 // of two 16-row MFMA tiles (lane group g holds rows 4g .. 4g+3 of each)
+template <int W, int KIND>
+__device__ __forceinline__ int kcs_lane() {
+  const int l = lane_id(), q = l & 15, g = l >> 4;
+  const int rl = 4 * g + (q >> 2);
+  return prow<W>(rl) * (2 * W) + 8 * (q & 1) + ((((q >> 1) & 1) ^ swz<W, KIND>(rl)) << 4);
+}
+
 template <int W, int KIND = 0>
 __device__ __forceinline__ bf16x8 frag_kc_split_s(const char* T, int c0, int k0) {
-  const int l = lane_id();
-  const int g = l >> 4, q = l & 15;
-  const int r = k0 + 4 * g + (q >> 2), c = c0 + 4 * (q & 3);
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(T + soff<W, KIND>(r, c))));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_short*)(T + soff<W, KIND>(r + 16, c))));
-  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
-  const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
-  return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+  const int o = kcs_lane<W, KIND>() ^ (2 * c0);
+  return tr_pair(T + k0 * (2 * W) + o, T + (k0 + 16) * (2 * W) + o);
 }
 
 // T[r0 + j][m_e], m_e as in frag_kc_split_s: the row-fragment form of the same
-// K order (two 8-byte reads)
+// K order (two 8-byte reads: columns k0 + 4g and k0 + 16 + 4g)
+template <int W, int KIND>
+__device__ __forceinline__ int rks_lane() {
+  const int l = lane_id(), q = l & 15, g = l >> 4;
+  return prow<W>(q) * (2 * W) + 8 * (g & 1) + (((g >> 1) ^ swz<W, KIND>(q)) << 4);
+}
+
 template <int W, int KIND = 0>
 __device__ __forceinline__ bf16x8 frag_rk_split_s(const char* T, int r0, int k0) {
-  const int l = lane_id();
-  const int r = r0 + (l & 15), c = k0 + 4 * (l >> 4);
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(T + soff<W, KIND>(r, c));
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(T + soff<W, KIND>(r, c + 16));
+  const char* base = T + r0 * (2 * W);
+  const int o = rks_lane<W, KIND>();
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(base + (o ^ (2 * k0)));
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + (o ^ (2 * k0 + 32)));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
