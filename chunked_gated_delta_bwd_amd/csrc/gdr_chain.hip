@@ -1014,14 +1014,12 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);
       f32x4 an[NJW];
       // the dO fragments (B operands: raw mode fq dO high, low; else dO high and,
-      // for fp32 inputs, low) serve every x: with one slice a workgroup they are
-      // read once (with two, the registers are not there: re-read per x)
+      // for fp32 inputs, low) serve every x: read once
       constexpr int NK = C / 32;
-      constexpr bool HOIST = NSL == 1;
       const char* XH = Cf::RAW ? X2 : X1;
       const char* XL = Cf::RAW ? X3 : X2;
       bf16x8 xh[NK], xl[NK];
-      if (HOIST && !job.xfer) {
+      if (!job.xfer) {
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
           xh[kk] = frag_kc_s<16>(XH, 0, 32 * kk);
@@ -1036,13 +1034,12 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
 #pragma unroll
           for (int kk = 0; kk < NK; ++kk) {
             const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, 32 * kk);
-            const bf16x8 bh = HOIST ? xh[kk] : frag_kc_s<16>(XH, 0, 32 * kk);
-            a = mma(qa, bh, a);
+            a = mma(qa, xh[kk], a);
             if constexpr (Cf::RAW) {
-              a = mma(qa, HOIST ? xl[kk] : frag_kc_s<16>(XL, 0, 32 * kk), a);
+              a = mma(qa, xl[kk], a);
             } else {
-              a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, 32 * kk), bh, a);
-              if constexpr (Cf::LO) a = mma(qa, HOIST ? xl[kk] : frag_kc_s<16>(XL, 0, 32 * kk), a);
+              a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, 32 * kk), xh[kk], a);
+              if constexpr (Cf::LO) a = mma(qa, xl[kk], a);
             }
           }
         }
