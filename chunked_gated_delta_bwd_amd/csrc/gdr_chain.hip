@@ -745,10 +745,10 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
       const bool wk = TWO && p.weak[int64_t(h) * p.NC + chunk(k)] != 0;
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
-        const int j = 16 * (w * NJW + x) + 4 * g;
-        st4_s<D>(Ss, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+        const int jc = 16 * (w * NJW + x);
+        st4_q<D>(Ss, 0, jc, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
         if constexpr (Cf::SPLIT)
-          st4_s<D>(smem + Cf::fSl, jj, j, lo_part(acc[x][0]), lo_part(acc[x][1]), lo_part(acc[x][2]),
+          st4_q<D>(smem + Cf::fSl, 0, jc, lo_part(acc[x][0]), lo_part(acc[x][1]), lo_part(acc[x][2]),
                    lo_part(acc[x][3]));
       }
       chain_barrier();   // B1
@@ -795,10 +795,10 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
         const uint16_t* Upl = reinterpret_cast<const uint16_t*>(Fb + Cf::fUpl);
 #pragma unroll
         for (int i = 0; i < 4; ++i) u[i] += um * bf16_bits_to_f32(Upl[(16 * w + 4 * g + i) * 16 + jj]);
-        st4_s<C, 1>(smem + Cf::fUl, jj, 16 * w + 4 * g, lo_part(u[0]), lo_part(u[1]), lo_part(u[2]), lo_part(u[3]));
+        st4_q<C, 1>(smem + Cf::fUl, 0, 16 * w, lo_part(u[0]), lo_part(u[1]), lo_part(u[2]), lo_part(u[3]));
       }
       if constexpr (Cf::RAW) {
-        st4_s<C, 1>(Uo, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
+        st4_q<C, 1>(Uo, 0, 16 * w, u[0], u[1], u[2], u[3]);
         const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl_k + Cf::sFac) + C +
                                                           16 * w + 4 * g);
         u[0] *= f.x;
@@ -806,7 +806,7 @@ __device__ __forceinline__ void chain_fwd(const Params& p, char* smem, int si, i
         u[2] *= f.z;
         u[3] *= f.w;
       }
-      st4_s<C, 1>(Ut, jj, 16 * w + 4 * g, u[0], u[1], u[2], u[3]);
+      st4_q<C, 1>(Ut, 0, 16 * w, u[0], u[1], u[2], u[3]);
       chain_barrier();   // B2
       // S_{k+1}^T = Diag(e^GamC) S_k^T + Khat^T U (per-channel gate: U in two parts,
       // the low one also stored for the gradient kernel; U's bf16 rounding here is
@@ -963,10 +963,10 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       const bool two = TWO && chunk(k) <= two_last;
 #pragma unroll
       for (int x = 0; x < NJW; ++x) {
-        const int j = 16 * (w * NJW + x) + 4 * g;
-        st4_s<D>(dSl, jj, j, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+        const int jc = 16 * (w * NJW + x), j = jc + 4 * g;
+        st4_q<D>(dSl, 0, jc, acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
         if (TWO && two)
-          st4_s<D>(dSlo, jj, j, lo_part(acc[x][0]), lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
+          st4_q<D>(dSlo, 0, jc, lo_part(acc[x][0]), lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
         if (Cf::SPLIT && job.store)   // no LDS left for a low tile: stored directly
           st_bf16x4(p.dSlo + (int64_t(h) * p.NC + chunk(k)) * D * D + (v0 + 16 * sv + jj) * D + j, lo_part(acc[x][0]),
                     lo_part(acc[x][1]), lo_part(acc[x][2]), lo_part(acc[x][3]));
@@ -1007,8 +1007,8 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       } else {
         ad += ak;
       }
-      st4_s<C, 1>(dUt, jj, 16 * w + 4 * g, ad[0], ad[1], ad[2], ad[3]);
-      if (TWO && two) st4_s<C, 1>(dUlo, jj, 16 * w + 4 * g, lo_part(ad[0]), lo_part(ad[1]), lo_part(ad[2]), lo_part(ad[3]));
+      st4_q<C, 1>(dUt, 0, 16 * w, ad[0], ad[1], ad[2], ad[3]);
+      if (TWO && two) st4_q<C, 1>(dUlo, 0, 16 * w, lo_part(ad[0]), lo_part(ad[1]), lo_part(ad[2]), lo_part(ad[3]));
       // dS_n^T = Diag(e^GamC) dS_{n+1}^T + Qbar^T dO - W^T dU: the first two terms do
       // not depend on dU and are issued before the barrier
       const float* dec = reinterpret_cast<const float*>(sl_k + Cf::sDec);

@@ -565,11 +565,11 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
 #pragma unroll
     for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_rk_s<C, 1>(dUT, 16 * vb, k0), frag_kc_s<C, 0>(At, 16 * rb, k0), a);
     const int v = 16 * vb + 4 * g;
-    st4_s<D>(dYt, r, v, a[0], a[1], a[2], a[3]);
+    st4_q<D>(dYt, 16 * rb, 16 * vb, a[0], a[1], a[2], a[3]);
     // rows past the end: dY is exactly zero there, so the clamped v row adds nothing
     float vv[4];
     if constexpr (kDma) {
-      const bf16x4 vb4 = *reinterpret_cast<const bf16x4*>(Vt + soff<D>(r, v));
+      const bf16x4 vb4 = ld4_q<D>(Vt, 16 * rb, 16 * vb);
 #pragma unroll
       for (int i = 0; i < 4; ++i) vv[i] = float(vb4[i]);
     } else {
@@ -675,9 +675,9 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
   f32x4 dkn[NJH], dqn[NJH];
 #pragma unroll
   for (int q = 0; q < NJH; ++q) {
-    const int j = 16 * (hf * NJH + q) + 4 * g;
-    const bf16x4 kb = *reinterpret_cast<const bf16x4*>(Kn + soff<D>(r, j));
-    const bf16x4 qb = *reinterpret_cast<const bf16x4*>(Qn + soff<D>(r, j));
+    const int jc = 16 * (hf * NJH + q);
+    const bf16x4 kb = ld4_q<D>(Kn, 16 * rb, jc);
+    const bf16x4 qb = ld4_q<D>(Qn, 16 * rb, jc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float kn = float(kb[i]), qn = float(qb[i]);
@@ -745,9 +745,9 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
 #pragma unroll
   for (int slot = 0; slot < 2; ++slot) {
     if (slot == 0 || w < 2) {
-      const int rr = 16 * g3_rb(w, slot) + jj, s0 = 16 * g3_sb(w, slot) + 4 * g;
-      st4_s<C, 0>(dME, rr, s0, dme[slot][0], dme[slot][1], dme[slot][2], dme[slot][3]);
-      st4_s<C, 0>(dPE, rr, s0, dpe[slot][0], dpe[slot][1], dpe[slot][2], dpe[slot][3]);
+      const int r0 = 16 * g3_rb(w, slot), c0 = 16 * g3_sb(w, slot);
+      st4_q<C, 0>(dME, r0, c0, dme[slot][0], dme[slot][1], dme[slot][2], dme[slot][3]);
+      st4_q<C, 0>(dPE, r0, c0, dpe[slot][0], dpe[slot][1], dpe[slot][2], dpe[slot][3]);
     }
   }
   // raw q, k of this lane's outputs, for the L2-norm backward at the end
@@ -784,10 +784,9 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
     float pq = 0.f, pk = 0.f;
 #pragma unroll
     for (int q = 0; q < NJH; ++q) {
-      const int j = 16 * (hf * NJH + q) + 4 * g;
       if constexpr (kDma) {
-        const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(dUT + soff<D>(r, j));
-        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Vt + soff<D>(r, j));
+        const bf16x4 q4 = ld4_q<D>(dUT, 16 * rb, 16 * (hf * NJH + q));
+        const bf16x4 k4 = ld4_q<D>(Vt, 16 * rb, 16 * (hf * NJH + q));
 #pragma unroll
         for (int i = 0; i < 4; ++i) { qn[q][i] = float(q4[i]); kn[q][i] = float(k4[i]); }
       } else {
@@ -829,10 +828,10 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
       // bf16 rows go out through LDS (the dO and dY tiles are free now), below
 #pragma unroll
       for (int q = 0; q < NJH; ++q) {
-        const int j = 16 * (hf * NJH + q) + 4 * g;
-        st4_s<D>(dOt, r, j, rq * (dqn[q][0] - qn[q][0] * pq), rq * (dqn[q][1] - qn[q][1] * pq),
+        const int jc = 16 * (hf * NJH + q);
+        st4_q<D>(dOt, 16 * rb, jc, rq * (dqn[q][0] - qn[q][0] * pq), rq * (dqn[q][1] - qn[q][1] * pq),
                  rq * (dqn[q][2] - qn[q][2] * pq), rq * (dqn[q][3] - qn[q][3] * pq));
-        st4_s<D>(dYt, r, j, rk * (dkn[q][0] - kn[q][0] * pk), rk * (dkn[q][1] - kn[q][1] * pk),
+        st4_q<D>(dYt, 16 * rb, jc, rk * (dkn[q][0] - kn[q][0] * pk), rk * (dkn[q][1] - kn[q][1] * pk),
                  rk * (dkn[q][2] - kn[q][2] * pk), rk * (dkn[q][3] - kn[q][3] * pk));
       }
     } else if (r < len) {

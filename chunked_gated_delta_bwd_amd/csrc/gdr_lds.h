@@ -126,9 +126,22 @@ __device__ __forceinline__ bf16x8 frag_rk_split_s(const char* T, int r0, int k0)
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Lane (q, g)'s four consecutive elements of row r0 + q, columns c0 + 4g .. +3
+// (r0, c0 multiples of 16: an accumulator tile's layout), as bytes from the tile:
+// the 8-byte pieces frag_rk_split_s reads, so the same per-lane part serves
 template <int W, int KIND = 0>
-__device__ __forceinline__ void st4_s(char* T, int r, int c, float a, float b, float d, float e) {
-  *reinterpret_cast<uint2*>(T + soff<W, KIND>(r, c)) = pack4_bf16(a, b, d, e);
+__device__ __forceinline__ int quad_off(int r0, int c0) {
+  return r0 * (2 * W) + (rks_lane<W, KIND>() ^ (2 * c0));
+}
+
+template <int W, int KIND = 0>
+__device__ __forceinline__ void st4_q(char* T, int r0, int c0, float a, float b, float d, float e) {
+  *reinterpret_cast<uint2*>(T + quad_off<W, KIND>(r0, c0)) = pack4_bf16(a, b, d, e);
+}
+
+template <int W, int KIND = 0>
+__device__ __forceinline__ bf16x4 ld4_q(const char* T, int r0, int c0) {
+  return *reinterpret_cast<const bf16x4*>(T + quad_off<W, KIND>(r0, c0));
 }
 
 // x - bf16(x): the low part of a two-part bf16 value
