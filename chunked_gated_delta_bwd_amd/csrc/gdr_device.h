@@ -320,6 +320,10 @@ __device__ __forceinline__ void st_bf16x4(uint16_t* dst, float a, float b, float
 }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+// 2^x on the hardware exponential alone (fast_exp(x) is this of x log2(e)): for
+// exponents kept in base-2 units, which saves the multiply per factor
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
 // softplus(x) = max(x, 0) + log(1 + exp(-|x|)), stable for every x.  The
 // argument of the log lies in (1, 2], where the hardware log is accurate; rounding

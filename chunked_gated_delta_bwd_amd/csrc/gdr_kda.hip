@@ -217,7 +217,9 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
       const float v = x[i] + before;
-      Gs[(part * RP + i) * PG + cc] = v;
+      // kept in base-2 units (log2(e) Gamma) from here on: every use below is an
+      // exponent of 2; the workspace copy is Gamma itself
+      Gs[(part * RP + i) * PG + cc] = kLog2e * v;
       p.gam[(ch * C + part * RP + i) * D + cc] = v;
     }
   }
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
       bf16x8 bk, bq, bkl, bql;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float d = fast_exp(e < 4 ? el(gr0, e) - el(gf0, e) : el(gr1, e - 4) - el(gf1, e - 4));
+        const float d = fast_exp2(e < 4 ? el(gr0, e) - el(gf0, e) : el(gr1, e - 4) - el(gf1, e - 4));
         const float xk = float(kr[e]) * (rkr * d), xq = float(qr[e]) * (rqr * d);
         bk[e] = to_bf16(xk);
         bq[e] = to_bf16(xq);
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
           bf16x8 ak, akl;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float d = fast_exp(e < 4 ? el(gf0, e) - el(gs0, e) : el(gf1, e - 4) - el(gs1, e - 4));
+            const float d = fast_exp2(e < 4 ? el(gf0, e) - el(gs0, e) : el(gf1, e - 4) - el(gs1, e - 4));
             const float xs = float(ks[e]) * (rks * d);
             ak[e] = to_bf16(xs);
             akl[e] = to_bf16(xs - float(ak[e]));
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
     const int f = 16 * rb, m = f + 8, rr = f + jj;
     auto wide_ch = [&](int cc) {
       const float gm = Gs[m * PG + cc];
-      return fmaxf(Gs[f * PG + cc] - gm, gm - Gs[(f + 15) * PG + cc]) >= kSpanMax;
+      return fmaxf(Gs[f * PG + cc] - gm, gm - Gs[(f + 15) * PG + cc]) >= kLog2e * kSpanMax;
     };
     // wave-uniform masks of the wide channels: lane l tests channels l and 64 + l
     const uint64_t wide0 = __builtin_amdgcn_ballot_w64(wide_ch(l));
@@ -336,8 +338,8 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
       for (int e = 0; e < 4; ++e) {
         const int cc = c4 + e;
         const bool wd = ((cc < 64 ? wide0 >> cc : wide1 >> (cc & 63)) & 1) != 0;
-        const float ea = wd ? 0.f : fast_exp(el(gr4, e) - el(gm4, e));   // row as r
-        const float eb = wd ? 0.f : fast_exp(el(gm4, e) - el(gr4, e));   // row as s
+        const float ea = wd ? 0.f : fast_exp2(el(gr4, e) - el(gm4, e));   // row as r
+        const float eb = wd ? 0.f : fast_exp2(el(gm4, e) - el(gr4, e));   // row as s
         const float kn = float(k4[e]) * rkr;
         aM = mma_f32(kn * eb, kn * ea, aM);
         aP = mma_f32(kn * eb, float(q4[e]) * rqr * ea, aP);
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int sc = s0 + i;
-        const float kk = float(Ks[sc * PD + cc]) * rk_s[sc] * fast_exp(-fabsf(gr - Gs[sc * PG + cc]));
+        const float kk = float(Ks[sc * PD + cc]) * rk_s[sc] * fast_exp2(-fabsf(gr - Gs[sc * PG + cc]));
         aM[i] += kr * kk;
         aP[i] += qr * kk;
       }
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
   // recursions' Khat / Qbar tiles and the chunk decay go to the workspace; a weak
   // chunk (some channel decays by less than kTwoPartDecay) also Khat's low part ---
   int wf = 0;
-  for (int j = l; j < D; j += 64) wf |= fast_exp(Gs[(C - 1) * PG + j]) >= kTwoPartDecay;
+  for (int j = l; j < D; j += 64) wf |= fast_exp2(Gs[(C - 1) * PG + j]) >= kTwoPartDecay;
   const bool weak = __any(wf);
   if (tid == 0) p.weak[ch] = weak ? 1 : 0;
 #pragma unroll
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float gr = Gs[r * PG + c0 + e], gC = Gs[(C - 1) * PG + c0 + e];
-      const float eg = fast_exp(gr), eh = fast_exp(gC - gr);
+      const float eg = fast_exp2(gr), eh = fast_exp2(gC - gr);
       kb[e] = to_bf16(fb * kn_r[ps][e] * eg);
       const float bv = fb * v_r[ps][e];
       vb[e] = to_bf16(bv);
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(kKdaPrepThreads) void k_prep_kda(const Params p) {
     *reinterpret_cast<bf16x8*>(p.Qh + o) = qh;
     *reinterpret_cast<bf16x8*>(p.Ql + o) = ql;
   }
-  if (tid < D) p.edec[ch * D + tid] = fast_exp(Gs[(C - 1) * PG + tid]);
+  if (tid < D) p.edec[ch * D + tid] = fast_exp2(Gs[(C - 1) * PG + tid]);
 
   // --- A = (I + L)^-1 in 16x16 blocks X_ij (fp32): wave i inverts the diagonal
   // block I + L_ii by forward substitution (lane = column) ... ---
@@ -910,7 +912,9 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
 #pragma unroll
   for (int i = 0; i < NGL; ++i) {
     const int pc = tid + i * kT, rr = pc / (D / 4), c4 = (pc % (D / 4)) * 4;
-    *reinterpret_cast<float4*>(Gs + rr * PG + c4) = g_r[i];
+    // in base-2 units (log2(e) Gamma): every use below is an exponent of 2
+    *reinterpret_cast<float4*>(Gs + rr * PG + c4) =
+        make_float4(kLog2e * g_r[i].x, kLog2e * g_r[i].y, kLog2e * g_r[i].z, kLog2e * g_r[i].w);
   }
   __syncthreads();
 
@@ -997,7 +1001,7 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float kn = el(kr, i), qn = el(qr, i);
-        const float eg = fast_exp(el(gr, i)), eh = fast_exp(el(gC, i) - el(gr, i));
+        const float eg = fast_exp2(el(gr, i)), eh = fast_exp2(el(gC, i) - el(gr, i));
         const float z = aZ[q][i], dkh = aK[q][i], dqb = aQ[q][i];
         dgm[i] = -br * z * kn * eg - dkh * kn * eh + dqb * scale * qn * eg;
         dbeta_row -= kn * eg * z;
@@ -1022,7 +1026,7 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 16 * sb + 4 * g + i;
-        av[i] = Knf[s * PG + cm] * fast_exp(ge - Gs[s * PG + cm]);
+        av[i] = Knf[s * PG + cm] * fast_exp2(ge - Gs[s * PG + cm]);
       }
       bf16x4 ah, al;
       split4(av, ah, al);
@@ -1032,7 +1036,7 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
       const float4 gend = ld4(Gs + se * PG + j);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float mlt = fast_exp(Gr[i] - el(gend, i));
+        const float mlt = fast_exp2(Gr[i] - el(gend, i));
         const float x1 = t1[i] * mlt, x3 = scale * t3[i] * mlt;
         dkn[i] += x1;
         dqn[i] += x3;
@@ -1049,7 +1053,7 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = rs + 4 * g + i;
-        const float d = fast_exp(Gs[rr * PG + cm] - gst);
+        const float d = fast_exp2(Gs[rr * PG + cm] - gst);
         kv[i] = Knf[rr * PG + cm] * d;
         qv[i] = Qnf[rr * PG + cm] * d;
       }
@@ -1062,7 +1066,7 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
       const float4 gsv = ld4(Gs + rs * PG + j);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float mlt = fast_exp(el(gsv, i) - Gr[i]);
+        const float mlt = fast_exp2(el(gsv, i) - Gr[i]);
         const float x = (t2[i] + scale * t4[i]) * mlt;
         dkn[i] += x;
         dgm[i] -= el(kr, i) * x;
@@ -1079,7 +1083,7 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
     {
       const int f = 16 * rb, m = f + 8;
       const float gm = Gs[m * PG + cm];
-      const bool wide = fmaxf(Gs[f * PG + cm] - gm, gm - Gs[(f + 15) * PG + cm]) >= kSpanMax;
+      const bool wide = fmaxf(Gs[f * PG + cm] - gm, gm - Gs[(f + 15) * PG + cm]) >= kLog2e * kSpanMax;
       fact_ok = __builtin_amdgcn_ballot_w64(wide) == 0;
       if (fact_ok) {
         f32x4 t1 = zero4(), t2 = zero4(), t3 = zero4(), t4 = zero4();
@@ -1087,8 +1091,8 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
         for (int kk = 0; kk < 4; ++kk) {
           const int s = f + 4 * kk + g;   // A: m = channel cm, k = s - f
           const float gs = Gs[s * PG + cm];
-          const float kb = Knf[s * PG + cm] * fast_exp(gm - gs);   // kn_s b_s
-          const float d = fast_exp(gs - gm);                        // a_s
+          const float kb = Knf[s * PG + cm] * fast_exp2(gm - gs);   // kn_s b_s
+          const float d = fast_exp2(gs - gm);                        // a_s
           t1 = mma_f32(kb, dm_row[kk], t1);
           t3 = mma_f32(kb, dp_row[kk], t3);
           t2 = mma_f32(Knf[s * PG + cm] * d, dm_col[kk], t2);
@@ -1097,8 +1101,8 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
         const float4 gmv = ld4(Gs + m * PG + j);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float arow = fast_exp(Gr[i] - el(gmv, i));   // a_r
-          const float bcol = fast_exp(el(gmv, i) - Gr[i]);   // b_r
+          const float arow = fast_exp2(Gr[i] - el(gmv, i));   // a_r
+          const float bcol = fast_exp2(el(gmv, i) - Gr[i]);   // b_r
           const float x1 = t1[i] * arow, x3 = scale * t3[i] * arow;
           const float x24 = (t2[i] + scale * t4[i]) * bcol;
           dkn[i] += x1 + x24;
@@ -1119,7 +1123,7 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
         const float4 kt = ld4(Knf + t * PG + j), qt = ld4(Qnf + t * PG + j);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float E = fast_exp(-fabsf(Gr[i] - el(gt, i)));
+          const float E = fast_exp2(-fabsf(Gr[i] - el(gt, i)));
           const float ke = el(kt, i) * E, qe = el(qt, i) * E;
           const float x1 = mrt * ke, x3 = prt * ke, x24 = mtr * ke + ptr * qe;
           dkn[i] += x1 + x24;
@@ -1166,7 +1170,7 @@ __global__ __launch_bounds__(kKdaGradThreads) void k_grads_kda(const Params p) {
   if (tid < D) {
     const float st = (ssum_s[0][tid] + ssum_s[1][tid]) + (ssum_s[2][tid] + ssum_s[3][tid]);
     const float a = (csum_s[0][tid] + csum_s[1][tid]) + (csum_s[2][tid] + csum_s[3][tid]);
-    dgc_s[tid] = a + st * fast_exp(Gs[(C - 1) * PG + tid]);
+    dgc_s[tid] = a + st * fast_exp2(Gs[(C - 1) * PG + tid]);
   }
   __syncthreads();
   // L2-norm backward (K1 page, 3.3): dq = rq (dqn - qn <qn, dqn>), dk likewise
