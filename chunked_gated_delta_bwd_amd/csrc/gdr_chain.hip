@@ -609,7 +609,7 @@ struct LoRegs {
 // parts (X2, X3), rows 16w .. 16w+15 by compute wave w (lane: row 16w + l/4,
 // columns 4(l%4) .. +3)
 template <int D, typename TIO, int GATE, int NSL>
-__device__ __forceinline__ void convert_raw_rows(const char* slot, int sv, char* x2, char* x3, int w) {
+__device__ __forceinline__ void convert_raw_rows(const char* slot, int sv, char* x2, char* x3, int w, bool lo) {
   using Cf = ChainCfg<D, TIO, GATE, NSL>;
   const int l = lane_id();
   const int row = 16 * w + (l >> 2), o = prow<16>(row) * 32 + (l & 3) * 8;
@@ -625,7 +625,7 @@ __device__ __forceinline__ void convert_raw_rows(const char* slot, int sv, char*
     lv[e] = y - hv[e];
   }
   *reinterpret_cast<uint2*>(x2 + o) = pack4_bf16(hv[0], hv[1], hv[2], hv[3]);
-  *reinterpret_cast<uint2*>(x3 + o) = pack4_bf16(lv[0], lv[1], lv[2], lv[3]);
+  if (lo) *reinterpret_cast<uint2*>(x3 + o) = pack4_bf16(lv[0], lv[1], lv[2], lv[3]);
 }
 
 // the decay of this lane's four accumulator rows j = 16 jb + 4 g .. +3
@@ -948,8 +948,15 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     // raw mode: the compute waves form fq dO (high, low) of each chunk's dO slice
     // one step ahead, a quarter each (chunk 0 here, chunk k + 1 in the first
     // window of step k; published by the next barrier)
+    // Qbar^T dO's low part (raw mode the fq dO low slice, else the Qbar low tile).
+    // Scalar gate: a chunk's term reaches the segment's end state damped by the
+    // decays of the chunks before it, so the common kernel takes it for the
+    // segment's first chunk (its last step) only, the two-part kernel on every
+    // step.  Per-channel gate: every step, since its dS also leaves in two parts
+    // for the gate-parameter gradients, whose sums cancel strongly.
+    auto qlo_step = [&](int k) { return TWO || Cf::SPLIT || k == nck - 1; };
     if constexpr (Cf::RAW)
-      if (nck > 0) convert_raw_rows<D, TIO, GATE, NSL>(slot(0), sv, X2_of(0), X3_of(0), w);
+      if (nck > 0) convert_raw_rows<D, TIO, GATE, NSL>(slot(0), sv, X2_of(0), X3_of(0), w, qlo_step(0));
     for (int k = 0; k < nck; ++k) {
       const int buf = k & 1;
       const char* Bb = smem + buf * Cf::bufB;
@@ -975,7 +982,7 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       // raw mode: fq dO (high, low) of the next chunk first, so that its LDS round
       // trip overlaps the fragment reads below
       if constexpr (Cf::RAW)
-        convert_raw_rows<D, TIO, GATE, NSL>(slot(k + 1), sv, X2_of(buf ^ 1), X3_of(buf ^ 1), w);
+        convert_raw_rows<D, TIO, GATE, NSL>(slot(k + 1), sv, X2_of(buf ^ 1), X3_of(buf ^ 1), w, qlo_step(k + 1));
       // dU = P^T dO + Khat dS^T, rows 16w.., columns of this slice
       f32x4 ad = zero4(), ak = zero4();
       if (!job.xfer) {   // transfer rows: dO = 0
@@ -1018,12 +1025,15 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
       constexpr int NK = C / 32;
       const char* XH = Cf::RAW ? X2 : X1;
       const char* XL = Cf::RAW ? X3 : X2;
+      const bool qlo = qlo_step(k);
       bf16x8 xh[NK], xl[NK];
       if (!job.xfer) {
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
           xh[kk] = frag_kc_s<16>(XH, 0, 32 * kk);
-          if constexpr (Cf::RAW || Cf::LO) xl[kk] = frag_kc_s<16>(XL, 0, 32 * kk);
+          if constexpr (Cf::LO) xl[kk] = frag_kc_s<16>(XL, 0, 32 * kk);
+          if constexpr (Cf::RAW)
+            if (qlo) xl[kk] = frag_kc_s<16>(XL, 0, 32 * kk);
         }
       }
 #pragma unroll
@@ -1036,9 +1046,9 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
             const bf16x8 qa = frag_kc_s<D>(Bb + Cf::bQh, 16 * jb, 32 * kk);
             a = mma(qa, xh[kk], a);
             if constexpr (Cf::RAW) {
-              a = mma(qa, xl[kk], a);
+              if (qlo) a = mma(qa, xl[kk], a);
             } else {
-              a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, 32 * kk), xh[kk], a);
+              if (qlo) a = mma(frag_kc_s<D>(Bb + Cf::bQl, 16 * jb, 32 * kk), xh[kk], a);
               if constexpr (Cf::LO) a = mma(qa, xl[kk], a);
             }
           }
