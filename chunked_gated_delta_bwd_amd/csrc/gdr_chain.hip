@@ -945,9 +945,6 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     f32x4 acc[NJW];
     job_init<D>(job, acc, w, g, jj);
     if (nck > 0) chain_barrier();   // B0
-    // raw mode: the compute waves form fq dO (high, low) of each chunk's dO slice
-    // one step ahead, a quarter each (chunk 0 here, chunk k + 1 in the first
-    // window of step k; published by the next barrier)
     // Qbar^T dO's low part (raw mode the fq dO low slice, else the Qbar low tile).
     // Scalar gate: a chunk's term reaches the segment's end state damped by the
     // decays of the chunks before it, so the common kernel takes it for the
@@ -955,6 +952,9 @@ __device__ __forceinline__ void chain_bwd(const Params& p, char* smem, int si, i
     // step.  Per-channel gate: every step, since its dS also leaves in two parts
     // for the gate-parameter gradients, whose sums cancel strongly.
     auto qlo_step = [&](int k) { return TWO || Cf::SPLIT || k == nck - 1; };
+    // raw mode: the compute waves form fq dO (high and, where it is taken, low) of
+    // each chunk's dO slice one step ahead, a quarter each (chunk 0 here, chunk
+    // k + 1 in the first window of step k; published by the next barrier)
     if constexpr (Cf::RAW)
       if (nck > 0) convert_raw_rows<D, TIO, GATE, NSL>(slot(0), sv, X2_of(0), X3_of(0), w, qlo_step(0));
     for (int k = 0; k < nck; ++k) {
