@@ -564,7 +564,6 @@ __global__ __launch_bounds__(kGradThreads) void k_grads_gdn(const Params p) {
     f32x4 a = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < C; k0 += 32) a = mma(frag_rk_s<C, 1>(dUT, 16 * vb, k0), frag_kc_s<C, 0>(At, 16 * rb, k0), a);
-    const int v = 16 * vb + 4 * g;
     st4_q<D>(dYt, 16 * rb, 16 * vb, a[0], a[1], a[2], a[3]);
     // rows past the end: dY is exactly zero there, so the clamped v row adds nothing
     float vv[4];
