@@ -160,8 +160,10 @@ struct ChainCfg {
   static constexpr int bwdA = NJ + 2, bwdB = (MAT ? 3 * NJ : NJ + 2) + nSb;
   // the two-part kernel's counts (TWOM: the low tiles of Khat and W too)
   static constexpr int bwdA2 = bwdA + (TWOM ? NJ : 0), bwdB2 = bwdB + (TWOM ? NJ : 0);
-  // L2 prefetch distance in chunk steps (one prefetch load per mover wave per step)
-  static constexpr int PFD = 5;
+  // L2 prefetch distance in chunk steps (one prefetch load per mover wave per
+  // step), the best of 2 .. 6 measured for each form: raw rows with one slice a
+  // workgroup 5, two slices 3 (each step twice as long), materialised tiles 4
+  static constexpr int PFD = MAT ? 4 : NSL == 2 ? 3 : 5;
   static constexpr int fwdA = (MAT ? NJ : 2) + 1 + (SPLIT ? 1 : 0), fwdB = NJ + nSf;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(2 * bwdA2 + bwdB2 + (PFD - 2) * NPF < 64 && 2 * fwdA + fwdB + (PFD - 2) * NPF < 64, "vmcnt range");
