@@ -94,38 +94,51 @@ struct SplitPlan {
   bool split = false;  // some sequence has more than one
 };
 
-// Chain steps (chunk steps of the recursion kernel, one workgroup per CU) a
-// plan takes: the final pass over the longest segment, and for a split the
-// local pass and the boundary composition in front of it.
-int64_t plan_steps(const gdr_shape* s, int P, int min_chunks, SplitPlan* out) {
-  const int64_t ns = s->Dk / 16, H = s->H;
-  int64_t w_final = 0, w_local = 0, longest = 0, nseg = 0;
-  bool split = false;
+// Time of a plan in chunk steps of a one-slice recursion workgroup (about a
+// microsecond each on the headline shape). Each pass (for a split, the local
+// pass and then the final one) takes the longest segment's chunks once per round
+// of workgroups over the CUs; the launch pads the (segment, head) groups to a
+// multiple of 8. Raw-row recursions with more slices than CUs run two slices a
+// workgroup, whose step takes about 1.6 times as long. Partial rounds count as
+// fractions: workgroups of unequal length leave room for the extra ones. The
+// boundary composition walks a sequence's segments in order, about 4.4 steps
+// each. The constants are fitted to timings of 2 .. 16 segments on sequences of
+// 512 chunks with 2 and 4 heads.
+constexpr double kTwoSliceStep = 1.6;
+constexpr double kFixStepsPerSegment = 4.4;
+
+double plan_steps(const gdr_shape* s, int P, int min_chunks, SplitPlan* out) {
+  const int64_t ns = s->Dk / 16;
+  const bool raw = s->gate == GDR_GATE_SCALAR && s->dtype == GDR_BF16;
+  int64_t longest = 0, nseg = 0;
+  int pmax = 1;
   for (int n = 0; n < s->N; ++n) {
     const int64_t nck = seq_chunks(s, n);
     const int Pn = segments_for(nck, P, min_chunks);
     nseg += Pn;
-    w_final += 2 * H * ns * Pn;
+    pmax = std::max(pmax, Pn);
     longest = std::max<int64_t>(longest, (nck + Pn - 1) / Pn);
-    if (Pn > 1) {
-      split = true;
-      w_local += 2 * H * ns * (2 * Pn - 3);   // P - 1 state runs and P - 2 transfer runs per role
-    }
     if (!s->cu_seqlens_host) {                // dense: every sequence alike
       nseg *= s->N;
-      w_final *= s->N;
-      w_local *= s->N;
       break;
     }
   }
-  auto rounds = [](int64_t w) { return (w + kCUs - 1) / kCUs; };
-  int64_t steps = rounds(w_final) * longest;
-  if (split) steps += rounds(w_local) * longest + 10 + 3 * P;
+  const int64_t groups = (nseg * s->H + 7) / 8 * 8;
+  auto pass = [&](int64_t slices) {           // slices of both roles
+    double wg = double(slices), step = 1.0;
+    if (raw && slices > kCUs) {
+      wg = 0.5 * double(slices);
+      step = kTwoSliceStep;
+    }
+    return std::max(1.0, wg / kCUs) * step * double(longest);
+  };
+  double steps = pass(groups * ns * 2);
+  if (pmax > 1) steps += pass(groups * 2 * ns * 2) + kFixStepsPerSegment * pmax;
   if (out) {
     out->P = P;
     out->min_chunks = min_chunks;
     out->NS = nseg;
-    out->split = split;
+    out->split = pmax > 1;
   }
   return steps;
 }
@@ -140,10 +153,10 @@ SplitPlan plan_split(const gdr_shape* s) {
   } else if (s->seq_split >= 2) {
     plan_steps(s, std::min(s->seq_split, gdr::kMaxSegments), 1, &best);
   } else {
-    int64_t best_steps = plan_steps(s, 1, 1, &best);
+    double best_steps = plan_steps(s, 1, 1, &best);
     for (int P = 2; P <= gdr::kMaxSegments; ++P) {
       SplitPlan cand;
-      const int64_t st = plan_steps(s, P, kMinSegChunks, &cand);
+      const double st = plan_steps(s, P, kMinSegChunks, &cand);
       if (st < best_steps) {
         best_steps = st;
         best = cand;
