@@ -101,11 +101,11 @@ struct SplitPlan {
 // multiple of 8. Raw-row recursions with more slices than CUs run two slices a
 // workgroup, whose step takes about 1.6 times as long. Partial rounds count as
 // fractions: workgroups of unequal length leave room for the extra ones. The
-// boundary composition walks a sequence's segments in order, about 4.4 steps
+// boundary composition walks a sequence's segments in order, about 1.8 steps
 // each. The constants are fitted to timings of 2 .. 16 segments on sequences of
 // 512 chunks with 2 and 4 heads.
 constexpr double kTwoSliceStep = 1.6;
-constexpr double kFixStepsPerSegment = 4.4;
+constexpr double kFixStepsPerSegment = 1.8;
 
 double plan_steps(const gdr_shape* s, int P, int min_chunks, SplitPlan* out) {
   const int64_t ns = s->Dk / 16;

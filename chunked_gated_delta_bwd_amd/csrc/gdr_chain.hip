@@ -1393,13 +1393,21 @@ __global__ __launch_bounds__((ChainCfg<D, TIO, GATE, NSL>::THREADS)) void k_chai
 // segment of a split sequence, head, 16 state rows, role).  Forward: segment 1
 // starts from the local pass's end state of segment 0 (run from h0), and
 // segment j + 1 from S_j T_j + E_j (T_j the transfer product of segment j, E_j its
-// end state from zero); reverse likewise from the last segment down.  fp32
-// throughout; the 16 x D rows in LDS, T_j staged in LDS per boundary.
+// end state from zero); reverse likewise from the last segment down.  Each row of
+// the state composes on its own, so a workgroup carries its 16 rows through all
+// the boundaries.  The products run on 16x16x4 fp32 MFMA: wave w owns columns
+// [w D/4, (w + 1) D/4), the state rows (the A operand) come from LDS, and T_j
+// (the B operand) goes straight from global memory into registers, the next
+// boundary's while this one computes.  Over the MFMA's four k lanes the sum
+// index is taken as k = g (D/4) + kk at step kk, so each lane reads a contiguous
+// run of its state row.
 template <int D>
 __global__ __launch_bounds__(256) void k_chain_fix(const Params p, int mode) {
-  __shared__ float cur[16][D];
-  __shared__ float Tt[D][D];
-  constexpr int ns = D / 16, CPT = D / 16;   // columns per thread
+  constexpr int KK = D / 4;        // MFMA steps over the sum index
+  constexpr int NT = D / 64;       // 16-column tiles per wave
+  constexpr int PIT = D + 4;       // LDS row pitch (floats)
+  constexpr int ns = D / 16, CPT = D / 16;
+  __shared__ __align__(16) float cur[16 * PIT];
   int b = blockIdx.x;
   const int per_role = p.NS * p.H * ns;
   int role = mode == kChainBwd ? 1 : 0;
@@ -1412,50 +1420,78 @@ __global__ __launch_bounds__(256) void k_chain_fix(const Params p, int mode) {
   const SeqEntry se = seq_entry(p, si);
   if (se.seg != 0 || se.nseg < 2) return;
   const int tid = threadIdx.x, r = tid >> 4, c0 = (tid & 15) * CPT;
+  const int l = lane_id(), q = l & 15, g = l >> 4, n0 = wave_id() * (D / 4);
   auto xf = [&](int slot) { return p.xf + ((int64_t(role) * p.NS + slot) * p.H + h) * 2 * D * D; };
   auto sbuf = [&](int slot) { return p.sb + (((int64_t(role) * p.NS + slot) * p.H + h) * D + 16 * sl) * D; };
   const int P = se.nseg, s0 = se.slot;
   // the role's first segment ran from h0 / dht: its end state is already true
   const int j0 = role == 0 ? 0 : P - 1;
   const int step = role == 0 ? 1 : -1;
-  float v[CPT];
-  const float* e0 = xf(s0 + j0) + (16 * sl + r) * D + c0;
+  const int jlast = j0 + step * (P - 1);
+  {
+    const float* e0 = xf(s0 + j0) + (16 * sl + r) * D + c0;
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) v[i] = e0[i];
-  for (int j = j0 + step; j != j0 + step * (P - 1); j += step) {
-    // v: the state the segment s0 + j starts from
+    for (int i = 0; i < CPT; ++i) cur[r * PIT + c0 + i] = e0[i];
+  }
+  // B operand of boundary j: T_j[g KK + kk][n0 + 16 n + q]; the accumulators
+  // start from E_j at the MFMA output positions (rows 4 g + v, column n0 + 16 n + q)
+  auto load_t = [&](float (&bt)[NT][KK], float (&e)[NT][4], int j) {
+    const float* T = xf(s0 + j) + D * D + (g * KK) * D + n0 + q;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) bt[n][kk] = T[kk * D + 16 * n];
+    const float* E = xf(s0 + j) + (16 * sl + 4 * g) * D + n0 + q;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) e[n][v] = E[v * D + 16 * n];
+  };
+  // one boundary: cur holds the state segment s0 + j starts from
+  auto compose = [&](const float (&bt)[NT][KK], const float (&e)[NT][4], int j) {
     float* dst = sbuf(s0 + j) + r * D + c0;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      dst[i] = v[i];
-      cur[r][c0 + i] = v[i];
+    for (int i = 0; i < CPT; ++i) dst[i] = cur[r * PIT + c0 + i];
+    float a[KK];
+#pragma unroll
+    for (int i = 0; i < KK; i += 4) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(&cur[q * PIT + g * KK + i]);
+      a[i] = t[0];
+      a[i + 1] = t[1];
+      a[i + 2] = t[2];
+      a[i + 3] = t[3];
     }
-    // rows D .. 2D - 1 of the segment's block: the transfer product, staged with
-    // all of a thread's 16-byte loads in flight at once
-    const float4* T4 = reinterpret_cast<const float4*>(xf(s0 + j) + D * D);
-    float4 tv[D * D / 4 / 256];
+    f32x4 acc[NT];
 #pragma unroll
-    for (int i = 0; i < D * D / 4 / 256; ++i) tv[i] = T4[tid + 256 * i];
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4{e[n][0], e[n][1], e[n][2], e[n][3]};
 #pragma unroll
-    for (int i = 0; i < D * D / 4 / 256; ++i) {
-      const int e = 4 * (tid + 256 * i);
-      *reinterpret_cast<float4*>(&Tt[e / D][e % D]) = tv[i];
-    }
-    __syncthreads();
-    const float* E = xf(s0 + j) + (16 * sl + r) * D + c0;
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) v[i] = E[i];
-    for (int k = 0; k < D; ++k) {
-      const float a = cur[r][k];
+      for (int n = 0; n < NT; ++n) acc[n] = mma_f32(a[kk], bt[n][kk], acc[n]);
+    chain_barrier();   // every read of cur is done (the next T_j stays in flight)
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) v[i] = fmaf(a, Tt[k][c0 + i], v[i]);
-    }
-    __syncthreads();
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) cur[(4 * g + v) * PIT + n0 + 16 * n + q] = acc[n][v];
+    chain_barrier();
+  };
+  float bt0[NT][KK], bt1[NT][KK], e0[NT][4], e1[NT][4];
+  int j = j0 + step;
+  if (j != jlast) load_t(bt0, e0, j);
+  __syncthreads();
+  while (j != jlast) {
+    if (j + step != jlast) load_t(bt1, e1, j + step);
+    compose(bt0, e0, j);
+    j += step;
+    if (j == jlast) break;
+    if (j + step != jlast) load_t(bt0, e0, j + step);
+    compose(bt1, e1, j);
+    j += step;
   }
   // the state of the role's last segment
-  float* dst = sbuf(s0 + j0 + step * (P - 1)) + r * D + c0;
+  float* dst = sbuf(s0 + jlast) + r * D + c0;
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) dst[i] = v[i];
+  for (int i = 0; i < CPT; ++i) dst[i] = cur[r * PIT + c0 + i];
 }
 
 namespace {
