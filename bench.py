@@ -49,23 +49,23 @@ CSRC = os.path.join(ROOT, "chunked_gated_delta_bwd_amd", "csrc")
 #   traffic:   HBM bytes, FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB device copy
 #   mfma_flop: SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (bf16 MFMA FLOPs)
 MEASURED = {
-    ("gdn_bf16_t32768_h16_d128", "prep", "241d8191a28d"): {'traffic': 716000000, 'mfma_flop': 19330000000},
-    ("gdn_bf16_t32768_h16_d128", "chain_both", "241d8191a28d"): {'traffic': 1690000000, 'mfma_flop': 180420000000},
-    ("gdn_bf16_t32768_h16_d128", "grads", "241d8191a28d"): {'traffic': 2120000000, 'mfma_flop': 120260000000},
-    ("kda_bf16_t32768_h16_d128", "prep", "241d8191a28d"): {'traffic': 1841000000, 'mfma_flop': 53690000000},
-    ("kda_bf16_t32768_h16_d128", "chain_both", "241d8191a28d"): {'traffic': 2794000000, 'mfma_flop': 128850000000},
-    ("kda_bf16_t32768_h16_d128", "grads", "241d8191a28d"): {'traffic': 3794000000, 'mfma_flop': 188980000000},
-    ("kda_bf16_t32768_h16_d128", "finish", "241d8191a28d"): {'traffic': 4000000},
-    ("gdn_bf16_t32768_h32_d128", "prep", "241d8191a28d"): {'traffic': 1447000000, 'mfma_flop': 38650000000},
-    ("gdn_bf16_t32768_h32_d128", "chain_both", "241d8191a28d"): {'traffic': 3385000000, 'mfma_flop': 360840000000},
-    ("gdn_bf16_t32768_h32_d128", "grads", "241d8191a28d"): {'traffic': 4546000000, 'mfma_flop': 240520000000},
-    ("gdn_gqa4_bf16_t32768_h32_d128", "prep", "241d8191a28d"): {'traffic': 1003000000, 'mfma_flop': 38650000000},
-    ("gdn_gqa4_bf16_t32768_h32_d128", "chain_both", "241d8191a28d"): {'traffic': 2783000000, 'mfma_flop': 360840000000},
-    ("gdn_gqa4_bf16_t32768_h32_d128", "grads", "241d8191a28d"): {'traffic': 3997000000, 'mfma_flop': 240520000000},
-    ("gdn_gqa4_bf16_t32768_h32_d128", "finish", "241d8191a28d"): {'traffic': 672000000},
-    ("gdn_bf16_t32768_h2_d128", "prep", "241d8191a28d"): {'traffic': 86000000, 'mfma_flop': 2420000000},
-    ("gdn_bf16_t32768_h2_d128", "chain_both", "241d8191a28d"): {'traffic': 317000000, 'mfma_flop': 56830000000},
-    ("gdn_bf16_t32768_h2_d128", "grads", "241d8191a28d"): {'traffic': 245000000, 'mfma_flop': 15030000000},
+    ("gdn_bf16_t32768_h16_d128", "prep", "3d8743f98324"): {'traffic': 716000000, 'mfma_flop': 19330000000},
+    ("gdn_bf16_t32768_h16_d128", "chain_both", "3d8743f98324"): {'traffic': 1690000000, 'mfma_flop': 180420000000},
+    ("gdn_bf16_t32768_h16_d128", "grads", "3d8743f98324"): {'traffic': 2125000000, 'mfma_flop': 120260000000},
+    ("kda_bf16_t32768_h16_d128", "prep", "3d8743f98324"): {'traffic': 1841000000, 'mfma_flop': 53690000000},
+    ("kda_bf16_t32768_h16_d128", "chain_both", "3d8743f98324"): {'traffic': 2795000000, 'mfma_flop': 128850000000},
+    ("kda_bf16_t32768_h16_d128", "grads", "3d8743f98324"): {'traffic': 3794000000, 'mfma_flop': 188980000000},
+    ("kda_bf16_t32768_h16_d128", "finish", "3d8743f98324"): {'traffic': 4000000},
+    ("gdn_bf16_t32768_h32_d128", "prep", "3d8743f98324"): {'traffic': 1447000000, 'mfma_flop': 38650000000},
+    ("gdn_bf16_t32768_h32_d128", "chain_both", "3d8743f98324"): {'traffic': 3385000000, 'mfma_flop': 360840000000},
+    ("gdn_bf16_t32768_h32_d128", "grads", "3d8743f98324"): {'traffic': 4548000000, 'mfma_flop': 240520000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "prep", "3d8743f98324"): {'traffic': 1003000000, 'mfma_flop': 38650000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "chain_both", "3d8743f98324"): {'traffic': 2783000000, 'mfma_flop': 360840000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "grads", "3d8743f98324"): {'traffic': 4025000000, 'mfma_flop': 240520000000},
+    ("gdn_gqa4_bf16_t32768_h32_d128", "finish", "3d8743f98324"): {'traffic': 672000000},
+    ("gdn_bf16_t32768_h2_d128", "prep", "3d8743f98324"): {'traffic': 86000000, 'mfma_flop': 2420000000},
+    ("gdn_bf16_t32768_h2_d128", "chain_both", "3d8743f98324"): {'traffic': 317000000, 'mfma_flop': 56830000000},
+    ("gdn_bf16_t32768_h2_d128", "grads", "3d8743f98324"): {'traffic': 246000000, 'mfma_flop': 15030000000},
 }
 
 
