@@ -259,3 +259,23 @@ def test_sequence_split_workspace_and_validation():
     with pytest.raises(B.GdrError) as e:
         B.gdr_workspace_bytes(_prob(seq_split=-1))
     assert e.value.status == B.GDR_EINVAL
+
+
+def _ws_split(H, seq_split, gate=0):
+    prob = B.Problem(B=1, T=32768, H=H, D=128, N=1, gate=gate, dtype=0, scale=128 ** -0.5, cu_seqlens=None,
+                     seq_split=seq_split)
+    return B.gdr_workspace_bytes(prob)
+
+
+@pytest.mark.parametrize("H,gate,segments", [(2, 0, 8), (4, 0, 8), (2, 1, 8), (8, 0, 1), (16, 0, 1)])
+def test_automatic_sequence_split_choice(H, gate, segments):
+    """The workspace holds the split's segment-end rows per segment, so its size
+    shows the segment count the library chose.  At T = 32768, D = 128 the
+    planner's time model (fitted to timings of 2 .. 16 segments) picks 8
+    segments for 2 and 4 heads and no split once the unsplit recursions give
+    every compute unit a workgroup (8 heads and more)."""
+    auto = _ws_split(H, 0, gate)
+    assert auto == _ws_split(H, segments, gate)
+    for other in (1, 4, 16):
+        if other != segments:
+            assert auto != _ws_split(H, other, gate), other
